@@ -1,0 +1,400 @@
+/*
+ * dust_oracle.c -- TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow, fp64 CPU oracle for Dust's per-token zeroth-order weight
+ * gradient estimator of one linear layer y_t = W x_t.  Only tests/, the
+ * package's smoke() entry and bench.py's cpu_baseline leg may load this
+ * library.  It shares no code, header, table or constant generator with the
+ * HIP path under token_activation_perturbation_amd/csrc, and it includes
+ * nothing from there.
+ *
+ * What it computes, step by step, in the order the method is written:
+ *   1. y_t = W x_t, delta_t = y_t - target_t and the clean per-token loss
+ *      L_t = 1/2 ||delta_t||^2  (layer-local squared error stands in for the
+ *      network; "Dust: every token is a member of the population", section
+ *      "Perturb the activations, not the weights": dL/dW = sum_t delta_t x_t^T).
+ *   2. For every draw i and token t the literal perturbed loss
+ *      L_t^(i) = 1/2 ||y_t + s_i sigma a_t^(n(i)) - target_t||^2 and the loss
+ *      reduction rho_t^(i) = L_t - L_t^(i)  (same page, section "What the
+ *      released code actually does", step 2: reward = clean minus perturbed).
+ *   3. Centring across the K draws of one call, which share one forward:
+ *      c_t^(i) = rho_t^(i) - (1/K) sum_j rho_t^(j)  (same section, step 2,
+ *      and the definition of c_s under the estimator equations).
+ *   4. Discounted credit, reset at every sequence end:
+ *      r_t^(i) = sum_{s >= t, s in seq(t)} gamma^(s-t) c_s^(i), computed as
+ *      the reverse recursion r_t = c_t + gamma r_{t+1}  (estimator equation
+ *      for r_t, section "Perturb the activations, not the weights").
+ *   5. g_t = -1/(K sigma) sum_i r_t^(i) s_i a_t^(n(i))  (estimator equation
+ *      for g_t, same section; the antithetic sign s_i is part of the jitter
+ *      of draw i, section "What a zeroth-order gradient is").
+ *   6. G_W = sum_t g_t x_t^T  (estimator equation for G_W, same section;
+ *      the einsum 'btd,bti->di' of "What the released code actually does",
+ *      step 7).  Not divided by the token count.
+ *
+ * Noise (the pages fix no generator; they name Philox as a counter-based
+ * generator whose n-th output is a pure function of (seed, n): "Scaling To
+ * Unfathomable Depth", section "MeZO", last paragraphs).  Reading used here:
+ *   draw i uses noise index n(i) = i, or floor(i/2) with antithetic pairs,
+ *   and sign s_i = +1, or (-1)^i with antithetic pairs;
+ *   channel quad q = floor(c/4) of token t under noise index n takes the four
+ *   words of Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11) with counter
+ *   (q, t, n, 0) and key (seed mod 2^32, floor(seed / 2^32));
+ *   words (w0,w1) give channels 4q, 4q+1 and (w2,w3) channels 4q+2, 4q+3 by
+ *   Box-Muller: u = ((w_even >> 8) + 1) 2^-24 in (0,1],
+ *   v = (w_odd >> 8) 2^-24 in [0,1), R = sqrt(-2 ln u),
+ *   a_even = R cos(2 pi v), a_odd = R sin(2 pi v).
+ *
+ * Parity is pinned (see tests/): Philox words against an independent library
+ * implementation, the Gaussians by distribution tests, each estimator step
+ * by closed forms, brute-force sums and statistical laws.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_TWO_PI 6.283185307179586476925286766559
+
+/* Philox4x32 round constants (Salmon et al., SC'11, section on Philox). */
+#define PHILOX_M0 0xD2511F53u
+#define PHILOX_M1 0xCD9E8D57u
+#define PHILOX_W0 0x9E3779B9u
+#define PHILOX_W1 0xBB67AE85u
+
+/* Philox4x32-10: ten rounds of two 32x32->64 multiplies and xors, the key
+ * bumped by the Weyl constants between rounds. */
+void dust_oracle_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2],
+                               uint32_t out[4]) {
+  uint32_t x0 = ctr[0], x1 = ctr[1], x2 = ctr[2], x3 = ctr[3];
+  uint32_t k0 = key[0], k1 = key[1];
+  for (int round = 0; round < 10; ++round) {
+    if (round > 0) {
+      k0 += PHILOX_W0;
+      k1 += PHILOX_W1;
+    }
+    uint64_t prod0 = (uint64_t)PHILOX_M0 * (uint64_t)x0;
+    uint64_t prod1 = (uint64_t)PHILOX_M1 * (uint64_t)x2;
+    uint32_t y0 = (uint32_t)(prod1 >> 32) ^ x1 ^ k0;
+    uint32_t y1 = (uint32_t)prod1;
+    uint32_t y2 = (uint32_t)(prod0 >> 32) ^ x3 ^ k1;
+    uint32_t y3 = (uint32_t)prod0;
+    x0 = y0;
+    x1 = y1;
+    x2 = y2;
+    x3 = y3;
+  }
+  out[0] = x0;
+  out[1] = x1;
+  out[2] = x2;
+  out[3] = x3;
+}
+
+/* The four words of quad q of token t under noise index n. */
+static void quad_words(uint64_t seed, uint32_t n, uint32_t t, uint32_t q,
+                       uint32_t w[4]) {
+  uint32_t ctr[4] = {q, t, n, 0u};
+  uint32_t key[2] = {(uint32_t)(seed & 0xFFFFFFFFu), (uint32_t)(seed >> 32)};
+  dust_oracle_philox4x32_10(ctr, key, w);
+}
+
+/* Box-Muller on one pair of words, in fp64. */
+static void box_muller(uint32_t w_even, uint32_t w_odd, double *a_even,
+                       double *a_odd) {
+  double u = ((double)(w_even >> 8) + 1.0) * (1.0 / 16777216.0);
+  double v = (double)(w_odd >> 8) * (1.0 / 16777216.0);
+  double radius = sqrt(-2.0 * log(u));
+  *a_even = radius * cos(ORACLE_TWO_PI * v);
+  *a_odd = radius * sin(ORACLE_TWO_PI * v);
+}
+
+/* The noise vector a_t^(n) over all d_out channels, in fp64. */
+static void noise_vector(uint64_t seed, uint32_t n, uint32_t t, int64_t d_out,
+                         double *a) {
+  int64_t n_quads = (d_out + 3) / 4;
+  for (int64_t q = 0; q < n_quads; ++q) {
+    uint32_t w[4];
+    double g[4];
+    quad_words(seed, n, t, (uint32_t)q, w);
+    box_muller(w[0], w[1], &g[0], &g[1]);
+    box_muller(w[2], w[3], &g[2], &g[3]);
+    for (int j = 0; j < 4; ++j) {
+      int64_t c = 4 * q + j;
+      if (c < d_out) a[c] = g[j];
+    }
+  }
+}
+
+/* Test hook: words[n][t][4*ceil(d_out/4)] and gauss[n][t][d_out] for the
+ * noise indices n0..n0+n_cnt-1 and tokens t0..t0+t_cnt-1.  Either output may
+ * be NULL. */
+void dust_oracle_noise_fill(uint64_t seed, int64_t n0, int64_t n_cnt,
+                            int64_t t0, int64_t t_cnt, int64_t d_out,
+                            uint32_t *words, double *gauss) {
+  int64_t n_quads = (d_out + 3) / 4;
+  for (int64_t ni = 0; ni < n_cnt; ++ni) {
+    for (int64_t ti = 0; ti < t_cnt; ++ti) {
+      uint32_t n = (uint32_t)(n0 + ni), t = (uint32_t)(t0 + ti);
+      if (words) {
+        uint32_t *dst = words + (ni * t_cnt + ti) * 4 * n_quads;
+        for (int64_t q = 0; q < n_quads; ++q)
+          quad_words(seed, n, t, (uint32_t)q, dst + 4 * q);
+      }
+      if (gauss) noise_vector(seed, n, t, d_out, gauss + (ni * t_cnt + ti) * d_out);
+    }
+  }
+}
+
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+  const float *X, *W, *target;
+  int64_t T, d_in, d_out, seq_len;
+  int32_t K;
+  double sigma, gamma;
+  uint64_t seed;
+  int32_t antithetic;
+  int64_t t_begin, t_end; /* token range handled by this call */
+  double *delta;          /* [t_end - t_begin][d_out]  (scratch) */
+  double *loss;           /* [t range] */
+  double *rho;            /* [t range][K] */
+  double *reward;         /* [t range][K] */
+  double *g;              /* [t range][d_out] */
+  double *G;              /* [d_out][d_in] */
+  int n_threads;
+} oracle_job;
+
+typedef struct {
+  oracle_job *job;
+  int tid;
+} worker_arg;
+
+static int32_t noise_index(const oracle_job *j, int32_t i) {
+  return j->antithetic ? i / 2 : i;
+}
+static double draw_sign(const oracle_job *j, int32_t i) {
+  return (j->antithetic && (i % 2 == 1)) ? -1.0 : 1.0;
+}
+
+/* Step 1: y_t = W x_t, delta_t, L_t.  Tokens split across threads. */
+static void *phase_forward(void *p) {
+  worker_arg *wa = (worker_arg *)p;
+  oracle_job *j = wa->job;
+  int64_t n_tok = j->t_end - j->t_begin;
+  for (int64_t lt = wa->tid; lt < n_tok; lt += j->n_threads) {
+    int64_t t = j->t_begin + lt;
+    double loss = 0.0;
+    for (int64_t c = 0; c < j->d_out; ++c) {
+      double y = 0.0;
+      for (int64_t k = 0; k < j->d_in; ++k)
+        y += (double)j->W[c * j->d_in + k] * (double)j->X[t * j->d_in + k];
+      double d = y - (double)j->target[t * j->d_out + c];
+      j->delta[lt * j->d_out + c] = d;
+      loss += 0.5 * d * d;
+    }
+    j->loss[lt] = loss;
+  }
+  return NULL;
+}
+
+/* Step 2: literal perturbed losses and rho.  Each distinct noise vector is
+ * generated once per token and used by every draw that shares it. */
+static void *phase_rho(void *p) {
+  worker_arg *wa = (worker_arg *)p;
+  oracle_job *j = wa->job;
+  int64_t n_tok = j->t_end - j->t_begin;
+  double *a = (double *)malloc(sizeof(double) * (size_t)j->d_out);
+  for (int64_t lt = wa->tid; lt < n_tok; lt += j->n_threads) {
+    int64_t t = j->t_begin + lt;
+    const double *delta = j->delta + lt * j->d_out;
+    int32_t last_n = -1;
+    for (int32_t i = 0; i < j->K; ++i) {
+      int32_t n = noise_index(j, i);
+      if (n != last_n) {
+        noise_vector(j->seed, (uint32_t)n, (uint32_t)t, j->d_out, a);
+        last_n = n;
+      }
+      double s = draw_sign(j, i);
+      double perturbed = 0.0;
+      for (int64_t c = 0; c < j->d_out; ++c) {
+        /* y + s sigma a - target = delta + s sigma a */
+        double e = delta[c] + s * j->sigma * a[c];
+        perturbed += 0.5 * e * e;
+      }
+      j->rho[lt * j->K + i] = j->loss[lt] - perturbed;
+    }
+  }
+  free(a);
+  return NULL;
+}
+
+/* Steps 3 and 4: centring over draws, then the reverse discounted scan that
+ * restarts at every sequence end.  Sequences split across threads. */
+static void *phase_credit(void *p) {
+  worker_arg *wa = (worker_arg *)p;
+  oracle_job *j = wa->job;
+  int64_t seq0 = j->t_begin / j->seq_len, seq1 = j->t_end / j->seq_len;
+  double *centred = (double *)malloc(sizeof(double) * (size_t)j->K);
+  for (int64_t sq = seq0 + wa->tid; sq < seq1; sq += j->n_threads) {
+    int64_t first = sq * j->seq_len, last = first + j->seq_len - 1;
+    for (int64_t t = last; t >= first; --t) {
+      int64_t lt = t - j->t_begin;
+      double mean = 0.0;
+      for (int32_t i = 0; i < j->K; ++i) mean += j->rho[lt * j->K + i];
+      mean /= (double)j->K;
+      for (int32_t i = 0; i < j->K; ++i)
+        centred[i] = j->rho[lt * j->K + i] - mean;
+      for (int32_t i = 0; i < j->K; ++i) {
+        double later = (t == last) ? 0.0 : j->reward[(lt + 1) * j->K + i];
+        j->reward[lt * j->K + i] = centred[i] + j->gamma * later;
+      }
+    }
+  }
+  free(centred);
+  return NULL;
+}
+
+/* Step 5: g_t = -1/(K sigma) sum_i r_t^(i) s_i a_t^(n(i)). */
+static void *phase_error(void *p) {
+  worker_arg *wa = (worker_arg *)p;
+  oracle_job *j = wa->job;
+  int64_t n_tok = j->t_end - j->t_begin;
+  double *a = (double *)malloc(sizeof(double) * (size_t)j->d_out);
+  double scale = -1.0 / ((double)j->K * j->sigma);
+  for (int64_t lt = wa->tid; lt < n_tok; lt += j->n_threads) {
+    int64_t t = j->t_begin + lt;
+    double *g = j->g + lt * j->d_out;
+    for (int64_t c = 0; c < j->d_out; ++c) g[c] = 0.0;
+    int32_t last_n = -1;
+    for (int32_t i = 0; i < j->K; ++i) {
+      int32_t n = noise_index(j, i);
+      if (n != last_n) {
+        noise_vector(j->seed, (uint32_t)n, (uint32_t)t, j->d_out, a);
+        last_n = n;
+      }
+      double coef = j->reward[lt * j->K + i] * draw_sign(j, i);
+      for (int64_t c = 0; c < j->d_out; ++c) g[c] += coef * a[c];
+    }
+    for (int64_t c = 0; c < j->d_out; ++c) g[c] *= scale;
+  }
+  free(a);
+  return NULL;
+}
+
+/* Step 6: G_W[c][k] = sum_t g_t[c] x_t[k], tokens summed in order.  Rows of
+ * G split across threads. */
+static void *phase_outer(void *p) {
+  worker_arg *wa = (worker_arg *)p;
+  oracle_job *j = wa->job;
+  int64_t n_tok = j->t_end - j->t_begin;
+  for (int64_t c = wa->tid; c < j->d_out; c += j->n_threads) {
+    double *row = j->G + c * j->d_in;
+    for (int64_t k = 0; k < j->d_in; ++k) row[k] = 0.0;
+    for (int64_t lt = 0; lt < n_tok; ++lt) {
+      double gc = j->g[lt * j->d_out + c];
+      const float *x = j->X + (j->t_begin + lt) * j->d_in;
+      for (int64_t k = 0; k < j->d_in; ++k) row[k] += gc * (double)x[k];
+    }
+  }
+  return NULL;
+}
+
+static void run_phase(oracle_job *j, void *(*fn)(void *)) {
+  int nt = j->n_threads;
+  pthread_t *th = (pthread_t *)malloc(sizeof(pthread_t) * (size_t)nt);
+  worker_arg *args = (worker_arg *)malloc(sizeof(worker_arg) * (size_t)nt);
+  for (int i = 0; i < nt; ++i) {
+    args[i].job = j;
+    args[i].tid = i;
+    pthread_create(&th[i], NULL, fn, &args[i]);
+  }
+  for (int i = 0; i < nt; ++i) pthread_join(th[i], NULL);
+  free(th);
+  free(args);
+}
+
+/*
+ * The whole estimator over the sequences seq_begin..seq_end-1 (all of them
+ * when seq_end <= seq_begin is passed as 0,0 -> use every sequence).
+ * Inputs are fp32 host arrays holding the exact values the GPU receives
+ * (bf16 inputs are widened exactly); sigma and gamma are the fp32 values the
+ * GPU receives, widened.  Outputs are fp64 host arrays sized for the token
+ * range handled: loss[n_tok], rho[n_tok][K], reward[n_tok][K],
+ * g[n_tok][d_out], G[d_out][d_in] (the contribution of that token range).
+ * Returns 0, or -1 on an argument error.
+ */
+int dust_oracle_estimate(const float *X, const float *W, const float *target,
+                         int64_t T, int64_t d_in, int64_t d_out,
+                         int64_t seq_len, int32_t K, float sigma, float gamma,
+                         uint64_t seed, int32_t antithetic, int64_t seq_begin,
+                         int64_t seq_end, int32_t n_threads, double *G,
+                         double *loss, double *rho, double *reward, double *g) {
+  if (!X || !W || !target || !G || !loss || !rho || !reward || !g) return -1;
+  if (T <= 0 || d_in <= 0 || d_out <= 0 || seq_len <= 0 || T % seq_len != 0)
+    return -1;
+  if (K < 2 || (antithetic && K % 2 != 0)) return -1;
+  int64_t n_seq = T / seq_len;
+  if (seq_end <= seq_begin) {
+    seq_begin = 0;
+    seq_end = n_seq;
+  }
+  if (seq_begin < 0 || seq_end > n_seq) return -1;
+  if (n_threads < 1) n_threads = 1;
+
+  oracle_job j;
+  memset(&j, 0, sizeof(j));
+  j.X = X;
+  j.W = W;
+  j.target = target;
+  j.T = T;
+  j.d_in = d_in;
+  j.d_out = d_out;
+  j.seq_len = seq_len;
+  j.K = K;
+  j.sigma = (double)sigma;
+  j.gamma = (double)gamma;
+  j.seed = seed;
+  j.antithetic = antithetic;
+  j.t_begin = seq_begin * seq_len;
+  j.t_end = seq_end * seq_len;
+  j.n_threads = n_threads;
+  int64_t n_tok = j.t_end - j.t_begin;
+  j.delta = (double *)malloc(sizeof(double) * (size_t)(n_tok * d_out));
+  if (!j.delta) return -1;
+  j.loss = loss;
+  j.rho = rho;
+  j.reward = reward;
+  j.g = g;
+  j.G = G;
+
+  run_phase(&j, phase_forward);
+  run_phase(&j, phase_rho);
+  run_phase(&j, phase_credit);
+  run_phase(&j, phase_error);
+  run_phase(&j, phase_outer);
+  free(j.delta);
+  return 0;
+}
+
+/* The backprop gradient of the layer-local loss, sum_t delta_t x_t^T, and
+ * delta itself ("Perturb the activations, not the weights": the weight
+ * gradient of a linear layer is the outer product of output error and
+ * input).  Used by the statistical pins (expectation and cosine laws). */
+void dust_oracle_true_gradient(const float *X, const float *W,
+                               const float *target, int64_t T, int64_t d_in,
+                               int64_t d_out, double *delta, double *G_true) {
+  for (int64_t t = 0; t < T; ++t)
+    for (int64_t c = 0; c < d_out; ++c) {
+      double y = 0.0;
+      for (int64_t k = 0; k < d_in; ++k)
+        y += (double)W[c * d_in + k] * (double)X[t * d_in + k];
+      delta[t * d_out + c] = y - (double)target[t * d_out + c];
+    }
+  for (int64_t c = 0; c < d_out; ++c)
+    for (int64_t k = 0; k < d_in; ++k) {
+      double s = 0.0;
+      for (int64_t t = 0; t < T; ++t)
+        s += delta[t * d_out + c] * (double)X[t * d_in + k];
+      G_true[c * d_in + k] = s;
+    }
+}

@@ -1,0 +1,148 @@
+"""TEST INFRASTRUCTURE ONLY: Python front end of the fp64 CPU oracle.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s cpu_baseline
+leg may import this module.  It loads ``oracle/libdust_oracle.so`` (plain C,
+built with gcc by :func:`build`) and shares nothing with the HIP path.
+
+Every function mirrors one in ``dust_oracle.c``; the method it follows is
+stated there, step by step, with the passage of "Dust: every token is a member
+of the population" each step comes from.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "dust_oracle.c")
+_LIB = os.path.join(_HERE, "libdust_oracle.so")
+_lib = None
+
+
+def build() -> str:
+    """Compile the oracle with gcc (no fast-math; plain fp64)."""
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-Wall", "-Wextra",
+           "-o", _LIB + ".tmp", _SRC, "-lm", "-lpthread"]
+    subprocess.run(cmd, check=True)
+    os.replace(_LIB + ".tmp", _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        build()
+    lib = ctypes.CDLL(_LIB)
+    u32p = ctypes.POINTER(ctypes.c_uint32)
+    f32p = ctypes.POINTER(ctypes.c_float)
+    f64p = ctypes.POINTER(ctypes.c_double)
+    i64 = ctypes.c_int64
+    lib.dust_oracle_philox4x32_10.argtypes = [u32p, u32p, u32p]
+    lib.dust_oracle_philox4x32_10.restype = None
+    lib.dust_oracle_noise_fill.argtypes = [ctypes.c_uint64, i64, i64, i64, i64, i64, u32p, f64p]
+    lib.dust_oracle_noise_fill.restype = None
+    lib.dust_oracle_estimate.argtypes = [
+        f32p, f32p, f32p, i64, i64, i64, i64, ctypes.c_int32, ctypes.c_float,
+        ctypes.c_float, ctypes.c_uint64, ctypes.c_int32, i64, i64, ctypes.c_int32,
+        f64p, f64p, f64p, f64p, f64p]
+    lib.dust_oracle_estimate.restype = ctypes.c_int
+    lib.dust_oracle_true_gradient.argtypes = [f32p, f32p, f32p, i64, i64, i64, f64p, f64p]
+    lib.dust_oracle_true_gradient.restype = None
+    _lib = lib
+    return lib
+
+
+def _ptr(a: np.ndarray, ctype):
+    return a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+def philox4x32_10(ctr, key) -> np.ndarray:
+    """Philox4x32-10 of one 4-word counter under one 2-word key."""
+    lib = _load()
+    c = np.ascontiguousarray(ctr, dtype=np.uint32)
+    k = np.ascontiguousarray(key, dtype=np.uint32)
+    out = np.zeros(4, dtype=np.uint32)
+    lib.dust_oracle_philox4x32_10(_ptr(c, ctypes.c_uint32), _ptr(k, ctypes.c_uint32),
+                                  _ptr(out, ctypes.c_uint32))
+    return out
+
+
+def noise_fill(seed: int, n0: int, n_cnt: int, t0: int, t_cnt: int, d_out: int,
+               words: bool = True, gauss: bool = True):
+    """Hashed words [n][t][4*ceil(d_out/4)] (uint32) and Gaussians [n][t][d_out] (fp64)."""
+    lib = _load()
+    nq = (d_out + 3) // 4
+    w = np.zeros((n_cnt, t_cnt, 4 * nq), dtype=np.uint32) if words else None
+    g = np.zeros((n_cnt, t_cnt, d_out), dtype=np.float64) if gauss else None
+    lib.dust_oracle_noise_fill(
+        ctypes.c_uint64(seed), n0, n_cnt, t0, t_cnt, d_out,
+        _ptr(w, ctypes.c_uint32) if w is not None else None,
+        _ptr(g, ctypes.c_double) if g is not None else None)
+    return w, g
+
+
+def default_threads() -> int:
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:  # pragma: no cover
+        return max(1, os.cpu_count() or 1)
+
+
+def estimate(X, W, target, *, K: int, sigma: float, gamma: float, seed: int,
+             antithetic: bool, seq_len: int, seq_range=None, threads: int | None = None):
+    """Run the fp64 oracle.
+
+    X [T,d_in], W [d_out,d_in], target [T,d_out] hold the exact input values
+    (bf16 inputs widened to fp32).  ``seq_range=(s0, s1)`` restricts the work
+    to sequences s0..s1-1: every output then covers those tokens only and G
+    is their contribution.  Returns a dict of fp64 arrays:
+    G [d_out,d_in], loss [n], rho [n,K], reward [n,K], g [n,d_out].
+    """
+    lib = _load()
+    X = np.ascontiguousarray(X, dtype=np.float32)
+    W = np.ascontiguousarray(W, dtype=np.float32)
+    target = np.ascontiguousarray(target, dtype=np.float32)
+    T, d_in = X.shape
+    d_out = W.shape[0]
+    assert W.shape == (d_out, d_in) and target.shape == (T, d_out)
+    assert T % seq_len == 0
+    n_seq = T // seq_len
+    s0, s1 = (0, n_seq) if seq_range is None else seq_range
+    n_tok = (s1 - s0) * seq_len
+    G = np.zeros((d_out, d_in), dtype=np.float64)
+    loss = np.zeros(n_tok, dtype=np.float64)
+    rho = np.zeros((n_tok, K), dtype=np.float64)
+    reward = np.zeros((n_tok, K), dtype=np.float64)
+    g = np.zeros((n_tok, d_out), dtype=np.float64)
+    th = default_threads() if threads is None else threads
+    rc = lib.dust_oracle_estimate(
+        _ptr(X, ctypes.c_float), _ptr(W, ctypes.c_float), _ptr(target, ctypes.c_float),
+        T, d_in, d_out, seq_len, K, ctypes.c_float(sigma), ctypes.c_float(gamma),
+        ctypes.c_uint64(seed), int(bool(antithetic)), s0, s1, th,
+        _ptr(G, ctypes.c_double), _ptr(loss, ctypes.c_double), _ptr(rho, ctypes.c_double),
+        _ptr(reward, ctypes.c_double), _ptr(g, ctypes.c_double))
+    if rc != 0:
+        raise ValueError("oracle rejected its arguments")
+    return {"G": G, "loss": loss, "rho": rho, "reward": reward, "g": g,
+            "threads": th}
+
+
+def true_gradient(X, W, target):
+    """delta [T,d_out] and the backprop gradient sum_t delta_t x_t^T [d_out,d_in]."""
+    lib = _load()
+    X = np.ascontiguousarray(X, dtype=np.float32)
+    W = np.ascontiguousarray(W, dtype=np.float32)
+    target = np.ascontiguousarray(target, dtype=np.float32)
+    T, d_in = X.shape
+    d_out = W.shape[0]
+    delta = np.zeros((T, d_out), dtype=np.float64)
+    G = np.zeros((d_out, d_in), dtype=np.float64)
+    lib.dust_oracle_true_gradient(_ptr(X, ctypes.c_float), _ptr(W, ctypes.c_float),
+                                  _ptr(target, ctypes.c_float), T, d_in, d_out,
+                                  _ptr(delta, ctypes.c_double), _ptr(G, ctypes.c_double))
+    return delta, G

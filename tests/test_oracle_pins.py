@@ -1,0 +1,327 @@
+"""Pins of the fp64 CPU oracle to what the pages and the mathematics fix.
+
+Each test compares the oracle with something other than itself: an
+independent library implementation (PyTorch's Philox engine), distribution
+laws, closed forms derived from the layer-local quadratic loss, brute-force
+sums, finite differences, and the statistical laws and worked toy numbers of
+"Dust: every token is a member of the population".
+"""
+import json
+import os
+import subprocess
+
+import numpy as np
+import pytest
+from scipy import stats
+
+from token_activation_perturbation_amd import synth
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+# --------------------------------------------------------------------------
+# Noise: Philox words and the Gaussian transform
+
+
+@pytest.fixture(scope="module")
+def aten_philox(tmp_path_factory):
+    import torch
+    inc = os.path.join(os.path.dirname(torch.__file__), "include")
+    exe = str(tmp_path_factory.mktemp("aten") / "aten_philox")
+    subprocess.run(["g++", "-O1", "-std=c++17", "-I", inc, "-o", exe,
+                    os.path.join(HERE, "helpers", "aten_philox_words.cpp")], check=True)
+    return exe
+
+
+def test_philox_words_match_pytorch_engine(oracle_mod, aten_philox):
+    """Philox4x32-10 (Salmon et al., SC'11; named as a counter-based generator
+    in "Scaling To Unfathomable Depth", section "MeZO") against PyTorch's own
+    header-only engine, on edge and random counters and keys."""
+    rng = np.random.default_rng(7)
+    cases = [[0, 0, 0, 0, 0, 0], [2**32 - 1] * 6, [1, 0, 0, 0, 0, 0],
+             [0, 0, 0, 0, 1, 0], [0, 0, 0, 0, 0, 1], [5, 17, 3, 0, 0, 0]]
+    cases += rng.integers(0, 2**32, size=(500, 6), dtype=np.uint64).tolist()
+    # the counter layout the estimator uses: (quad, token, noise index, 0)
+    cases += [[q, t, n, 0, s & 0xFFFFFFFF, s >> 32]
+              for q, t, n, s in rng.integers(0, 5000, size=(300, 4)).tolist()]
+    text = "\n".join(" ".join(str(int(v)) for v in c) for c in cases) + "\n"
+    out = subprocess.run([aten_philox], input=text, capture_output=True, text=True,
+                         check=True).stdout.split("\n")
+    for c, line in zip(cases, out):
+        ref = [int(v) for v in line.split()]
+        got = oracle_mod.philox4x32_10(c[:4], c[4:]).tolist()
+        assert got == ref, (c, got, ref)
+
+
+def test_noise_words_follow_counter_layout(oracle_mod):
+    """The words of quad q, token t, noise index n are Philox((q,t,n,0), key)."""
+    seed = (123 << 32) | 456
+    w, _ = oracle_mod.noise_fill(seed, 3, 2, 10, 3, 13, words=True, gauss=False)
+    for ni in range(2):
+        for ti in range(3):
+            for q in range(4):
+                ref = oracle_mod.philox4x32_10([q, 10 + ti, 3 + ni, 0], [456, 123])
+                assert w[ni, ti, 4 * q:4 * q + 4].tolist() == ref.tolist()
+
+
+def test_gaussians_are_standard_normal(oracle_mod):
+    """a_t ~ N(0, I) ("Perturb the activations, not the weights"): moments,
+    Kolmogorov-Smirnov, independence of neighbours, and the Box-Muller bound
+    |a| <= sqrt(-2 ln 2^-24)."""
+    _, g = oracle_mod.noise_fill(0, 0, 64, 0, 256, 64, words=False, gauss=True)
+    a = g.ravel()
+    n = a.size
+    assert abs(a.mean()) < 5 / np.sqrt(n)
+    assert abs(a.var() - 1) < 5 * np.sqrt(2 / n)
+    assert abs(stats.kurtosis(a, fisher=False) - 3) < 5 * np.sqrt(24 / n)
+    assert stats.kstest(a[:200000], "norm").pvalue > 1e-4
+    assert np.abs(a).max() <= np.sqrt(48 * np.log(2)) + 1e-12
+    # neighbours: channel pairs of one Box-Muller call, adjacent quads,
+    # adjacent tokens and adjacent noise indices are uncorrelated
+    thr = 5 / np.sqrt(g[..., ::2].size)
+    assert abs(np.mean(g[..., 0::2] * g[..., 1::2])) < thr
+    assert abs(np.mean(g[..., 0:60] * g[..., 4:64])) < thr
+    assert abs(np.mean(g[:, :-1, :] * g[:, 1:, :])) < thr
+    assert abs(np.mean(g[:-1] * g[1:])) < thr
+    # the squared radius of a pair is exponential with mean 2
+    r2 = g[..., 0::2] ** 2 + g[..., 1::2] ** 2
+    assert stats.kstest(r2.ravel()[:100000], "expon", args=(0, 2)).pvalue > 1e-4
+
+
+def test_ragged_channels_share_quads(oracle_mod):
+    """d_out not a multiple of 4: channel c keeps the value it has for any
+    wider layer (the key does not depend on d_out)."""
+    _, g13 = oracle_mod.noise_fill(9, 0, 2, 0, 3, 13, words=False, gauss=True)
+    _, g16 = oracle_mod.noise_fill(9, 0, 2, 0, 3, 16, words=False, gauss=True)
+    assert np.array_equal(g13, g16[..., :13])
+
+
+# --------------------------------------------------------------------------
+# Estimator steps
+
+
+def _tiny(T=12, d_in=5, d_out=7, seed=3):
+    return synth.random_inputs(T, d_in, d_out, "f32", seed)
+
+
+def _noise(oracle_mod, seed, K_n, T, d_out):
+    _, g = oracle_mod.noise_fill(seed, 0, K_n, 0, T, d_out, words=False, gauss=True)
+    return g  # [n][t][c]
+
+
+def test_true_gradient_matches_finite_differences(oracle_mod):
+    """The layer-local loss sum_t 1/2||W x_t - target_t||^2 has gradient
+    sum_t delta_t x_t^T ("Perturb the activations, not the weights").
+    Central differences of the oracle's clean loss are exact for a quadratic
+    (up to rounding), so they pin delta, its sign and the loss."""
+    inp = synth.random_inputs(6, 4, 3, "bf16", 11)
+    X, W, tg = inp["X"], inp["W"], inp["target"]
+    delta, G_true = oracle_mod.true_gradient(X, W, tg)
+    h = 2.0 ** -6
+    kw = dict(K=2, sigma=1e-2, gamma=0.0, seed=0, antithetic=False, seq_len=6)
+    for c in range(3):
+        for k in range(4):
+            Wp, Wm = W.copy(), W.copy()
+            Wp[c, k] += h
+            Wm[c, k] -= h
+            assert Wp[c, k] - W[c, k] == h and W[c, k] - Wm[c, k] == h
+            Lp = oracle_mod.estimate(X, Wp, tg, **kw)["loss"].sum()
+            Lm = oracle_mod.estimate(X, Wm, tg, **kw)["loss"].sum()
+            fd = (Lp - Lm) / (2 * h)
+            assert abs(fd - G_true[c, k]) <= 1e-9 * max(1.0, abs(G_true[c, k]))
+    out = oracle_mod.estimate(X, W, tg, **kw)
+    assert np.allclose(out["loss"], 0.5 * (delta ** 2).sum(1), rtol=1e-13)
+
+
+@pytest.mark.parametrize("antithetic", [False, True])
+def test_rho_closed_form(oracle_mod, antithetic):
+    """reward = clean_loss - perturbed_loss ("What the released code actually
+    does", step 2).  For the quadratic loss this is exactly
+    rho = -s sigma <delta, a> - 1/2 sigma^2 ||a||^2."""
+    inp = _tiny()
+    K, sigma, seed = 6, 0.03, 77
+    out = oracle_mod.estimate(inp["X"], inp["W"], inp["target"], K=K, sigma=sigma,
+                              gamma=0.0, seed=seed, antithetic=antithetic, seq_len=4)
+    delta, _ = oracle_mod.true_gradient(inp["X"], inp["W"], inp["target"])
+    K_n = K // 2 if antithetic else K
+    a = _noise(oracle_mod, seed, K_n, 12, 7)
+    s32 = float(np.float32(sigma))
+    for i in range(K):
+        n = i // 2 if antithetic else i
+        s = -1.0 if (antithetic and i % 2) else 1.0
+        P = np.einsum("tc,tc->t", delta, a[n])
+        Q = np.einsum("tc,tc->t", a[n], a[n])
+        ref = -s * s32 * P - 0.5 * s32 ** 2 * Q
+        assert np.allclose(out["rho"][:, i], ref, rtol=1e-10, atol=1e-13)
+
+
+@pytest.mark.parametrize("gamma", [0.0, 0.5, 0.9, 1.0])
+def test_centring_and_credit_brute_force(oracle_mod, gamma):
+    """c_t = rho_t - mean over draws; r_t = sum_{s>=t, same sequence}
+    gamma^(s-t) c_s (estimator equation for r_t, "Perturb the activations,
+    not the weights").  The O(T^2) double sum, restarted per sequence, against
+    the oracle's reverse recursion."""
+    inp = _tiny(T=12)
+    seq_len, K = 4, 5
+    out = oracle_mod.estimate(inp["X"], inp["W"], inp["target"], K=K, sigma=0.02,
+                              gamma=gamma, seed=5, antithetic=False, seq_len=seq_len)
+    rho = out["rho"]
+    c = rho - rho.mean(axis=1, keepdims=True)
+    assert np.allclose(c.sum(1), 0, atol=1e-12)
+    g32 = float(np.float32(gamma))
+    r = np.zeros_like(c)
+    for t in range(12):
+        end = (t // seq_len + 1) * seq_len
+        for s in range(t, end):
+            r[t] += g32 ** (s - t) * c[s]
+    assert np.allclose(out["reward"], r, rtol=1e-12, atol=1e-14)
+    if gamma == 0.0:
+        assert np.array_equal(out["reward"], c)
+
+
+def test_one_token_sequences_have_no_credit_from_neighbours(oracle_mod):
+    """With seq_len = 1 every token is its own sequence, so r = c for any gamma."""
+    inp = _tiny(T=6)
+    out = oracle_mod.estimate(inp["X"], inp["W"], inp["target"], K=4, sigma=0.02,
+                              gamma=0.9, seed=1, antithetic=False, seq_len=1)
+    c = out["rho"] - out["rho"].mean(1, keepdims=True)
+    assert np.array_equal(out["reward"], c)
+
+
+@pytest.mark.parametrize("gamma,sigma", [(0.0, 1e-2), (0.0, 0.5), (0.7, 1e-2), (1.0, 0.3)])
+def test_antithetic_exact_identity(oracle_mod, gamma, sigma):
+    """Antithetic pairs cancel the even-order terms ("What a zeroth-order
+    gradient is"), and centring is a no-op because the pair's noises sum to
+    zero.  For the quadratic loss this gives, for any sigma, exactly
+    g_t = (2/K) sum_p a_t^p sum_{s>=t} gamma^(s-t) <delta_s, a_s^p>."""
+    T, seq_len, d_out, K = 12, 6, 7, 8
+    inp = _tiny(T=T, d_out=d_out)
+    out = oracle_mod.estimate(inp["X"], inp["W"], inp["target"], K=K, sigma=sigma,
+                              gamma=gamma, seed=21, antithetic=True, seq_len=seq_len)
+    delta, _ = oracle_mod.true_gradient(inp["X"], inp["W"], inp["target"])
+    a = _noise(oracle_mod, 21, K // 2, T, d_out)
+    P = np.einsum("tc,ntc->nt", delta, a)  # [n][t]
+    g32 = float(np.float32(gamma))
+    g_ref = np.zeros((T, d_out))
+    for t in range(T):
+        end = (t // seq_len + 1) * seq_len
+        for p in range(K // 2):
+            pi = sum(g32 ** (s - t) * P[p, s] for s in range(t, end))
+            g_ref[t] += (2.0 / K) * pi * a[p, t]
+    assert np.allclose(out["g"], g_ref, rtol=1e-10, atol=1e-12)
+
+
+def test_weight_gradient_is_outer_product(oracle_mod):
+    """G_W = sum_t g_t x_t^T with G in W's [d_out, d_in] layout (estimator
+    equation for G_W; the einsum 'btd,bti->di').  Non-square to catch a
+    transposition."""
+    inp = _tiny(T=8, d_in=3, d_out=5)
+    out = oracle_mod.estimate(inp["X"], inp["W"], inp["target"], K=4, sigma=0.02,
+                              gamma=0.3, seed=2, antithetic=False, seq_len=4)
+    assert out["G"].shape == (5, 3)
+    ref = out["g"].T @ inp["X"].astype(np.float64)
+    assert np.allclose(out["G"], ref, rtol=1e-12, atol=1e-14)
+
+
+def test_sequence_range_matches_full_run(oracle_mod):
+    inp = _tiny(T=12)
+    kw = dict(K=4, sigma=0.02, gamma=0.6, seed=8, antithetic=True, seq_len=4)
+    full = oracle_mod.estimate(inp["X"], inp["W"], inp["target"], **kw)
+    part = oracle_mod.estimate(inp["X"], inp["W"], inp["target"], seq_range=(1, 3), **kw)
+    for k in ("loss", "rho", "reward", "g"):
+        assert np.array_equal(part[k], full[k][4:12])
+    ref_G = part["g"].T @ inp["X"][4:12].astype(np.float64)
+    assert np.allclose(part["G"], ref_G, rtol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# Statistical laws
+
+
+@pytest.mark.parametrize("antithetic,K", [(True, 4), (False, 4)])
+def test_expectation_of_error_estimate(oracle_mod, antithetic, K):
+    """E[g_t] = delta_t for antithetic pairs; with plain draws the centring
+    over the K draws of one call shrinks it to (K-1)/K delta_t, which tends to
+    delta_t as K grows.  Averaged over many noise seeds, projected on delta."""
+    T, d_out = 4, 6
+    inp = _tiny(T=T, d_in=3, d_out=d_out, seed=4)
+    delta, G_true = oracle_mod.true_gradient(inp["X"], inp["W"], inp["target"])
+    S = 3000
+    acc = np.zeros((T, d_out))
+    accG = np.zeros_like(G_true)
+    for s in range(S):
+        out = oracle_mod.estimate(inp["X"], inp["W"], inp["target"], K=K, sigma=0.05,
+                                  gamma=0.0, seed=1000 + s, antithetic=antithetic,
+                                  seq_len=T, threads=1)
+        acc += out["g"]
+        accG += out["G"]
+    mean_g = acc / S
+    expect = 1.0 if antithetic else (K - 1) / K
+    ratio = (mean_g * delta).sum() / (delta * delta).sum()
+    assert abs(ratio - expect) < 0.03, ratio
+    ratioG = (accG / S * G_true).sum() / (G_true * G_true).sum()
+    assert abs(ratioG - expect) < 0.04, ratioG
+
+
+def test_per_token_cosine_law(oracle_mod):
+    """The ES variance law ("What a zeroth-order gradient is"): the error of
+    an isotropic-Gaussian estimate has squared norm about (D+1)||grad||^2/K,
+    so cos is about sqrt(K/(K+D+1)).  Per token, D = d_out; antithetic pairs
+    count K/2 independent directions."""
+    T, d = 256, 32
+    inp = synth.random_inputs(T, d, d, "f32", 31)
+    delta, _ = oracle_mod.true_gradient(inp["X"], inp["W"], inp["target"])
+    for K, anti in [(64, True), (32, False)]:
+        out = oracle_mod.estimate(inp["X"], inp["W"], inp["target"], K=K, sigma=1e-2,
+                                  gamma=0.0, seed=3, antithetic=anti, seq_len=T)
+        g = out["g"]
+        cos = (g * delta).sum(1) / np.linalg.norm(g, axis=1) / np.linalg.norm(delta, axis=1)
+        Ke = K // 2 if anti else K
+        if not anti:
+            Ke = K - 1  # the centring removes one direction's worth of signal
+        pred = np.sqrt(Ke / (Ke + d + 1))
+        assert abs(cos.mean() - pred) < 0.02, (K, anti, cos.mean(), pred)
+
+
+def test_toy_cosines_printed_on_the_page(oracle_mod):
+    """The page's toy (section "Try it: three estimators, same forward
+    passes"): one d x d layer, 32 tokens, a quadratic loss per token; with
+    per-token rewards the estimate reaches a cosine of 0.968 (d=16, K=256)
+    and 0.984 (d=64, K=2048).  Reading: those printed values are the
+    per-token cosine between g_t and delta_t (they equal the law
+    sqrt(K/(K+d+1)) to three decimals); the cosine of the rebuilt weight
+    gradient depends on the toy's input distribution, which the page does
+    not give.  One seeded run each on the page with unstated noise settings,
+    and the law is first order, so the match is to 0.01."""
+    with open(os.path.join(HERE, "golden", "toy_cosines.json")) as f:
+        fixture = json.load(f)
+    T = fixture["tokens"]
+    for case in fixture["cases"]:
+        d, K = case["d"], case["K"]
+        cosines = []
+        for rep in range(3):
+            inp = synth.random_inputs(T, d, d, "f32", 500 + rep)
+            delta, _ = oracle_mod.true_gradient(inp["X"], inp["W"], inp["target"])
+            out = oracle_mod.estimate(inp["X"], inp["W"], inp["target"], K=K, sigma=1e-2,
+                                      gamma=0.0, seed=40 + rep, antithetic=False, seq_len=T)
+            g = out["g"]
+            cos = (g * delta).sum(1) / np.linalg.norm(g, axis=1) / np.linalg.norm(delta, axis=1)
+            cosines.append(cos.mean())
+        assert abs(np.mean(cosines) - case["per_token_reward_cosine"]) < 0.01, (case, cosines)
+
+
+def test_gamma_adds_variance_not_bias(oracle_mod):
+    """gamma only adds later tokens' independent rewards (estimator equation
+    for r_t): E[g_t] stays delta_t for gamma > 0 under antithetic pairs."""
+    T, d_out = 4, 5
+    inp = _tiny(T=T, d_in=3, d_out=d_out, seed=6)
+    delta, _ = oracle_mod.true_gradient(inp["X"], inp["W"], inp["target"])
+    S = 3000
+    acc = np.zeros((T, d_out))
+    for s in range(S):
+        out = oracle_mod.estimate(inp["X"], inp["W"], inp["target"], K=4, sigma=0.05,
+                                  gamma=0.8, seed=90000 + s, antithetic=True,
+                                  seq_len=T, threads=1)
+        acc += out["g"]
+    ratio = (acc / S * delta).sum() / (delta * delta).sum()
+    assert abs(ratio - 1.0) < 0.05, ratio

@@ -1,0 +1,117 @@
+"""Seeded synthetic inputs for the Dust estimator of one linear layer.
+
+This module holds no arithmetic of the estimator: it only draws X, W and
+target with the shapes and distributions of the five workloads below, and
+rounds them to the input dtype.  The pages train on FineWeb with a 37.7M
+parameter GPT whose layers are 512 wide ("Dust: every token is a member of the
+population", sections "What the released code actually does" and "The results,
+checked against the tables"); neither the data nor the weights are available,
+so these draws stand in for that layer's inputs, and the layer-local squared
+error stands in for the network.
+
+Recipe: numpy ``default_rng(data_seed)`` (PCG64) standard normals in fp64,
+scaled, cast to fp32 (round to nearest even) and, for bf16 workloads, rounded
+once more from fp32 to bf16 (round to nearest even).  Both the HIP path and
+the oracle consume exactly these values.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    T: int
+    seq_len: int
+    d_in: int
+    d_out: int
+    K: int
+    sigma: float
+    gamma: float
+    antithetic: bool
+    dtype: str          # "f32" or "bf16"
+    data_seed: int
+    noise_seed: int
+    target_kind: str    # "iid" (target ~ N(0,1)) or "teacher" (bf16(X W'^T))
+
+    @property
+    def n_seq(self) -> int:
+        return self.T // self.seq_len
+
+    @property
+    def rows(self) -> int:
+        """Draw-token rows K*T of one estimate."""
+        return self.K * self.T
+
+    def describe(self) -> dict:
+        return {"workload": self.name, "T": self.T, "seq_len": self.seq_len,
+                "d_in": self.d_in, "d_out": self.d_out, "K": self.K,
+                "sigma": self.sigma, "gamma": self.gamma,
+                "antithetic": self.antithetic, "dtype": self.dtype}
+
+
+WORKLOADS = {
+    w.name: w for w in [
+        Workload("tiny_f32", 64, 64, 64, 64, 16, 1e-2, 0.0, False, "f32", 1001, 0, "iid"),
+        Workload("bf16_layer", 4096, 512, 512, 512, 64, 1e-2, 0.0, True, "bf16", 1002, 0, "iid"),
+        Workload("mlp_up_bf16", 16384, 512, 768, 3072, 256, 5e-3, 0.0, True, "bf16", 1003, 0, "teacher"),
+        Workload("qkv_credit_bf16", 8192, 1024, 1024, 3072, 128, 1e-2, 0.9, False, "bf16", 1004, 0, "iid"),
+        Workload("large_population_bf16", 2048, 1024, 1024, 1024, 4096, 1e-2, 0.5, True, "bf16", 1005, 0, "iid"),
+    ]
+}
+WORKLOAD_ORDER = ["tiny_f32", "bf16_layer", "mlp_up_bf16", "qkv_credit_bf16",
+                  "large_population_bf16"]
+
+
+def bf16_round(x: np.ndarray) -> np.ndarray:
+    """Round fp32 values to the nearest bf16 (ties to even); returns fp32."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    bits = x.view(np.uint32).astype(np.uint64)
+    lsb = (bits >> 16) & 1
+    rounded = ((bits + 0x7FFF + lsb) >> 16) << 16
+    return rounded.astype(np.uint32).view(np.float32).reshape(x.shape)
+
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """The upper 16 bits of fp32 values that are already bf16-representable."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    b = x.view(np.uint32)
+    assert np.all((b & 0xFFFF) == 0), "value not representable in bf16"
+    return (b >> 16).astype(np.uint16)
+
+
+def _round(x64: np.ndarray, dtype: str) -> np.ndarray:
+    x32 = x64.astype(np.float32)
+    return bf16_round(x32) if dtype == "bf16" else x32
+
+
+def make_inputs(w: Workload, T: int | None = None, d_in: int | None = None,
+                d_out: int | None = None, data_seed: int | None = None) -> dict:
+    """X [T,d_in], W [d_out,d_in], target [T,d_out] as fp32 arrays holding the
+    exact input values.  Sizes and seed default to the workload's."""
+    T = w.T if T is None else T
+    d_in = w.d_in if d_in is None else d_in
+    d_out = w.d_out if d_out is None else d_out
+    rng = np.random.default_rng(w.data_seed if data_seed is None else data_seed)
+    X = _round(rng.standard_normal((T, d_in)), w.dtype)
+    W = _round(rng.standard_normal((d_out, d_in)) / np.sqrt(d_in), w.dtype)
+    if w.target_kind == "teacher":
+        # W' = W + E with E ~ N(0, 0.01) read as variance 0.01 (std 0.1).
+        W_teacher = W.astype(np.float64) + 0.1 * rng.standard_normal((d_out, d_in))
+        target = _round(X.astype(np.float64) @ W_teacher.T, w.dtype)
+    else:
+        target = _round(rng.standard_normal((T, d_out)), w.dtype)
+    return {"X": X, "W": W, "target": target}
+
+
+def random_inputs(T: int, d_in: int, d_out: int, dtype: str, seed: int) -> dict:
+    """Inputs of any shape with the iid recipe (X, target ~ N(0,1),
+    W ~ N(0, 1/d_in)), for edge-case and ragged-shape tests."""
+    rng = np.random.default_rng(seed)
+    X = _round(rng.standard_normal((T, d_in)), dtype)
+    W = _round(rng.standard_normal((d_out, d_in)) / np.sqrt(max(d_in, 1)), dtype)
+    target = _round(rng.standard_normal((T, d_out)), dtype)
+    return {"X": X, "W": W, "target": target}
