@@ -1,0 +1,182 @@
+"""Benchmark of dust_estimate on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one whole dust_estimate call (every stage: base GEMM, noise +
+loss change, centring and credit, reweighting, outer product) over one batch
+of synthetic inputs already resident in HBM.  The default workload is the
+"bf16 layer" (T = 4096 tokens in 8 sequences of 512, d_in = d_out = 512,
+K = 64 antithetic draws, sigma = 1e-2, gamma = 0).  Prints one JSON line:
+draw-token-rows per second (K*T per step), the ALU roofline of the dominant
+kernel timed with HIP events inside the timed region, and the fp64 CPU
+oracle timed on a bounded sample on this machine's host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = ["token_activation_perturbation_amd/csrc/dust_kernels.hip",
+                  "token_activation_perturbation_amd/csrc/dust_noise.hpp"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload: str, kernel: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when it is missing or was taken on different kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = data.get(workload)
+    if not entry or entry.get("kernel") != kernel:
+        return None
+    if entry.get("source_hash") != kernel_source_hash():
+        return None
+    return entry.get("bytes_per_launch")
+
+
+def cpu_baseline(w, inp, budget_s: float):
+    """The fp64 oracle, as it stands, on a bounded sample: whole sequences of
+    the same workload, as many as fit the time budget (at least one)."""
+    from oracle import oracle
+    threads = min(16, oracle.default_threads())
+    kw = dict(K=w.K, sigma=w.sigma, gamma=w.gamma, seed=w.noise_seed,
+              antithetic=w.antithetic, seq_len=w.seq_len, threads=threads)
+    t0 = time.perf_counter()
+    oracle.estimate(inp["X"], inp["W"], inp["target"], seq_range=(0, 1), **kw)
+    one = time.perf_counter() - t0
+    n_seq = max(1, min(w.n_seq, int(budget_s / max(one, 1e-6))))
+    if n_seq > 1:
+        t0 = time.perf_counter()
+        oracle.estimate(inp["X"], inp["W"], inp["target"], seq_range=(0, n_seq), **kw)
+        elapsed = time.perf_counter() - t0
+    else:
+        elapsed = one
+    rows = w.K * w.seq_len * n_seq
+    return {"value": rows / elapsed, "unit": "draw-token-rows/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{n_seq} of {w.n_seq} sequences ({n_seq * w.seq_len} tokens x {w.K} draws) "
+                      f"of the benchmarked workload, fp64, {elapsed:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="bf16_layer")
+    ap.add_argument("--cpu-budget", type=float, default=15.0,
+                    help="seconds of oracle work for the CPU baseline (0 to skip)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        sys.exit(f"bench.py: this estimator is measured on one GPU; --gpus {args.gpus} is not "
+                 "supported (sharding over sequences is a design note, not built)")
+
+    import torch
+
+    import token_activation_perturbation_amd as dust
+    from token_activation_perturbation_amd import roofline, synth
+
+    w = synth.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    inp = synth.make_inputs(w)
+    tdt = torch.float32 if w.dtype == "f32" else torch.bfloat16
+    X, W, tg = (torch.from_numpy(inp[k]).to(dev).to(tdt).contiguous()
+                for k in ("X", "W", "target"))
+    dt_code = dust.DUST_F32 if w.dtype == "f32" else dust.DUST_BF16
+    ws = torch.empty(dust.dust_workspace_bytes(w.T, w.d_in, w.d_out, w.K, w.antithetic, dt_code),
+                     dtype=torch.uint8, device=dev)
+    kw = dict(K=w.K, sigma=w.sigma, gamma=w.gamma, seed=w.noise_seed, antithetic=w.antithetic,
+              seq_len=w.seq_len)
+    out = {}
+    for _ in range(args.warmup):
+        out = dust.dust_estimate(X, W, tg, out=out, workspace=ws, **kw)
+    torch.cuda.synchronize(dev)
+    if not bool(torch.isfinite(out["G_W"]).all()):
+        sys.exit("bench.py: non-finite G_W")
+
+    # events around the dominant kernel of every timed step
+    fused = (w.gamma == 0.0 or w.seq_len == 1)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    stops = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    for e in starts + stops:
+        e.record()  # creates the underlying hipEvent
+    torch.cuda.synchronize(dev)
+    dust.dust_set_timing_events(starts, stops)
+
+    t_begin = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize(dev)
+    wall0 = time.perf_counter()
+    t_begin.record()
+    for _ in range(args.steps):
+        dust.dust_estimate(X, W, tg, out=out, workspace=ws, **kw)
+    t_end.record()
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - wall0
+    dust.dust_set_timing_events([], [])
+    ms_per_step = t_begin.elapsed_time(t_end) / args.steps
+    kernel_ms = sum(s.elapsed_time(e) for s, e in zip(starts, stops)) / args.steps
+
+    value = w.rows / (ms_per_step * 1e-3)
+    if fused:
+        kernel = "fused_g0_kernel"
+        slots = roofline.fused_kernel_slots(w.T, w.d_out, w.K, w.antithetic)
+    else:
+        kernel = "jitter_loss_kernel"
+        slots = roofline.jitter_kernel_slots(w.T, w.d_out, w.K, w.antithetic)
+    achieved = slots / (kernel_ms * 1e-3) / 1e12
+    peak = roofline.PEAK_SLOTS_PER_S / 1e12
+    result = {
+        "metric": "draw-token-rows/sec (K*T) for dust_estimate",
+        "value": value,
+        "unit": "draw-token-rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "wall_ms_per_step": wall * 1e3 / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded normal X, W, target; no dataset or trained weights)",
+        "config": {**w.describe(), "input_dtype": w.dtype, "parallelism": "none (1 GPU)"},
+        "roofline": {
+            "bound": "alu",
+            "kernel": kernel,
+            "kernel_ms": kernel_ms,
+            "achieved": achieved,
+            "peak": peak,
+            "unit": "T lane-slot/s",
+            "frac": achieved / peak,
+            "traffic": read_traffic(w.name, kernel),
+            "end_to_end_frac": roofline.estimate_min_seconds(
+                w.T, w.d_out, w.K, w.antithetic) / (ms_per_step * 1e-3),
+        },
+    }
+    if args.cpu_budget > 0:
+        result["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,138 @@
+/*
+ * dust.h -- C ABI of the MI355X (gfx950) Dust estimator library, libdust.so.
+ *
+ * Dust estimates the weight gradient of one linear layer y_t = W x_t from
+ * loss values alone: it jitters every token's output by sigma a_t over K
+ * draws, scores each token by its own centred loss reduction c_t, discounts
+ * the credit along the sequence r_t = sum_{s>=t} gamma^(s-t) c_s, averages the
+ * reward-weighted noise into g_t = -1/(K sigma) sum_i r_t^(i) a_t^(i), and
+ * contracts G_W = sum_t g_t x_t^T ("Dust: every token is a member of the
+ * population", section "Perturb the activations, not the weights", the three
+ * estimator equations; reward = clean minus perturbed loss and the centring
+ * across draws of one forward: section "What the released code actually
+ * does", step 2).  Here the layer-local loss L_t = 1/2 ||y_t - target_t||^2
+ * stands in for the network downstream of the layer.
+ *
+ * Conventions for every entry point:
+ *  - Tensor pointers are DEVICE pointers owned by the caller; tensors are
+ *    row-major and contiguous.  The library never allocates, frees or
+ *    synchronizes; all work is enqueued on `stream` (a hipStream_t passed as
+ *    void*; NULL is the default stream) and returns before it runs.
+ *  - Status codes are returned; on a non-OK status dust_last_error() gives a
+ *    message (thread-local, valid until the next call on the thread).
+ *    Argument errors are found on the host before anything is enqueued.
+ *    Faults while kernels run surface at the caller's next synchronization.
+ *  - Non-finite input values are not checked; they propagate.
+ *  - Results are deterministic: the same arguments give bitwise-equal
+ *    outputs (every reduction has a fixed order; no float atomics).
+ */
+#ifndef DUST_H
+#define DUST_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { DUST_F32 = 0, DUST_BF16 = 1 } dust_dtype_t;
+
+typedef enum {
+  DUST_OK = 0,
+  DUST_ERR_INVALID_ARG = 1, /* a size, scalar or required pointer is invalid */
+  DUST_ERR_UNSUPPORTED = 2, /* dtype or size outside what the kernels take  */
+  DUST_ERR_WORKSPACE = 3,   /* workspace NULL or smaller than required      */
+  DUST_ERR_HIP = 4          /* a HIP launch or runtime call failed          */
+} dust_status_t;
+
+/*
+ * Bytes of device workspace dust_estimate needs for these sizes (0 when the
+ * sizes are invalid).  Pure host function.
+ */
+size_t dust_workspace_bytes(int64_t T, int64_t d_in, int64_t d_out, int32_t K,
+                            int32_t antithetic, int32_t dtype);
+
+/*
+ * Host-side check of dust_estimate's arguments, the same check dust_estimate
+ * runs first.  Touches no device memory and makes no HIP call.  Rejects: a
+ * NULL X, W, target or G_W; T, d_in, d_out <= 0; seq_len <= 0 or T not a
+ * multiple of seq_len; T >= 2^31 or d_out >= 2^31 (the noise counter words
+ * are 32-bit); K < 2 (centring over one draw leaves nothing); odd K with
+ * antithetic pairs; sigma <= 0 or non-finite; gamma outside [0,1] or
+ * non-finite; an unknown dtype or T >= 2^24 tokens in one call
+ * (DUST_ERR_UNSUPPORTED); a NULL or too small workspace (DUST_ERR_WORKSPACE).
+ */
+dust_status_t dust_validate(const void* X, const void* W, const void* target,
+                            int64_t T, int64_t d_in, int64_t d_out,
+                            int64_t seq_len, int32_t dtype, int32_t K,
+                            float sigma, float gamma, int32_t antithetic,
+                            const float* G_W, const void* workspace,
+                            size_t workspace_bytes);
+
+/*
+ * The estimator, all stages, enqueued on `stream`.
+ *
+ * Inputs (dtype `dtype`, all three the same):
+ *   X      [T, d_in]      layer inputs, token t = b*seq_len + pos
+ *   W      [d_out, d_in]  weights (nn.Linear layout)
+ *   target [T, d_out]     target of the layer-local squared-error loss
+ * Scalars:
+ *   seq_len  tokens per sequence; the credit scan restarts at each end
+ *   K        draws; with antithetic != 0 draws 2p and 2p+1 share noise
+ *            vector p with signs +1 and -1 (K must be even)
+ *   sigma    jitter scale (fp32); gamma credit decay in [0,1] (fp32)
+ *   seed     64-bit noise key.  Noise value a_t^(n)[c] is Box-Muller of
+ *            Philox4x32-10 words, counter (c/4, t, n, 0), key (seed low,
+ *            seed high); it is regenerated where needed, never stored.
+ * Outputs (fp32, overwritten, not accumulated):
+ *   G_W        [d_out, d_in]  sum_t g_t x_t^T (NOT divided by T); required
+ *   loss_clean [T]            L_t = 1/2 ||W x_t - target_t||^2; optional
+ *   rho        [T, K]         loss reductions L_t - L_t^(i); optional
+ *   reward     [T, K]         discounted centred credit r_t^(i); optional
+ *   g          [T, d_out]     per-token error estimate g_t; optional
+ *   (optional outputs may be NULL)
+ * Workspace: device memory of at least dust_workspace_bytes(...) bytes,
+ * owned by the caller, contents undefined on return.
+ */
+dust_status_t dust_estimate(const void* X, const void* W, const void* target,
+                            int64_t T, int64_t d_in, int64_t d_out,
+                            int64_t seq_len, int32_t dtype, int32_t K,
+                            float sigma, float gamma, uint64_t seed,
+                            int32_t antithetic, float* G_W, float* loss_clean,
+                            float* rho, float* reward, float* g,
+                            void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+/*
+ * Test hook: the noise the estimator uses, written out.  For noise indices
+ * n0..n0+n_cnt-1 and tokens t0..t0+t_cnt-1:
+ *   words [n_cnt, t_cnt, 4*ceil(d_out/4)] uint32  Philox words (optional)
+ *   gauss [n_cnt, t_cnt, d_out]           fp32    Gaussians    (optional)
+ * Sizes must be positive and n0+n_cnt, t0+t_cnt, d_out below 2^31.
+ */
+dust_status_t dust_noise_fill(uint64_t seed, int64_t n0, int64_t n_cnt,
+                              int64_t t0, int64_t t_cnt, int64_t d_out,
+                              uint32_t* words, float* gauss, void* stream);
+
+/*
+ * Measurement hook (used by the benchmark to time the dominant kernel with
+ * HIP events inside its timed region).  After this call, dust_estimate call
+ * number i records start[i % n_pairs] and stop[i % n_pairs] (hipEvent_t
+ * values passed as void*, created and owned by the caller) on its stream
+ * right before and right after its noise kernel: the single-generation
+ * kernel when gamma = 0, else the jitter-loss kernel.  n_pairs = 0 turns the
+ * hook off.  The pointer arrays are copied; the events must outlive their
+ * use.  Process-wide state: not thread-safe.
+ */
+dust_status_t dust_set_timing_events(void* const* start, void* const* stop,
+                                     int32_t n_pairs);
+
+/* Message for the last non-OK status on this thread ("" if none). */
+const char* dust_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DUST_H */

@@ -1,0 +1,215 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 CPU oracle.
+
+Tolerances.  The estimate's own bar: G_W within relative Frobenius error
+2e-3 for bf16 inputs with fp32 accumulation and 1e-5 for the fp32 path.  The
+intermediate stages (per-token loss L_t, loss reductions rho, credit r,
+error estimate g) are held to the same relative level.  Noise words are
+compared bit for bit; Gaussians within GAUSS_ABS_TOL (derivation in the
+comment there).
+"""
+import numpy as np
+import pytest
+
+from token_activation_perturbation_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+# fp32 Box-Muller from the hardware transcendentals: v_log_f32, v_sqrt_f32,
+# v_sin_f32 and v_cos_f32 are each accurate to a few ulp over the ranges used
+# (u in [2^-24, 1], v in [0, 1) revolutions); with |a| <= 5.77 a few ulp of
+# the largest values is about 2e-6, so 1e-5 absolute leaves a 5x margin.
+GAUSS_ABS_TOL = 1e-5
+TOL = {"f32": 1e-5, "bf16": 2e-3}
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import token_activation_perturbation_amd as dust
+    dust._load()
+    return torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module")
+def threads(oracle_mod):
+    return min(16, oracle_mod.default_threads())
+
+
+def rel(a, b):
+    nb = np.linalg.norm(b)
+    return np.linalg.norm(a - b) / (nb if nb > 0 else 1.0)
+
+
+def to_dev(inp, dtype, dev):
+    import torch
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    return [torch.from_numpy(inp[k]).to(dev).to(tdt).contiguous() for k in ("X", "W", "target")]
+
+
+def gpu_estimate(inp, dtype, dev, **kw):
+    import torch
+    import token_activation_perturbation_amd as dust
+    Xd, Wd, td = to_dev(inp, dtype, dev)
+    out = dust.dust_estimate(Xd, Wd, td, want_loss=True, want_rho=True, want_reward=True,
+                             want_g=True, **kw)
+    torch.cuda.synchronize(dev)
+    return {k: v.cpu().numpy().astype(np.float64) for k, v in out.items()}
+
+
+def report(name, errs):
+    print(name, " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
+
+
+# --------------------------------------------------------------------------
+# Noise
+
+
+NOISE_CASES = [
+    # seed, n0, n_cnt, t0, t_cnt, d_out
+    (0, 0, 4, 0, 64, 64),
+    ((7 << 32) | 99, 3, 5, 1000, 17, 13),
+    (2**64 - 1, 2**31 - 8, 4, 2**31 - 20, 10, 38),
+    (12345, 100, 2, 4000, 3, 3072),
+]
+
+
+@pytest.mark.parametrize("case", NOISE_CASES)
+def test_noise_words_bit_exact_and_gaussians(dev, oracle_mod, case):
+    import torch
+    import token_activation_perturbation_amd as dust
+    seed, n0, n_cnt, t0, t_cnt, d_out = case
+    print(f"noise case {case}", flush=True)
+    w_gpu, g_gpu = dust.dust_noise_fill(seed, n0, n_cnt, t0, t_cnt, d_out, device=dev)
+    torch.cuda.synchronize(dev)
+    w_ref, g_ref = oracle_mod.noise_fill(seed, n0, n_cnt, t0, t_cnt, d_out)
+    assert np.array_equal(w_gpu.cpu().numpy().view(np.uint32), w_ref)
+    err = np.abs(g_gpu.cpu().numpy().astype(np.float64) - g_ref)
+    print(f"  gauss max abs err {err.max():.3e}, rms {np.sqrt((err**2).mean()):.3e}", flush=True)
+    assert err.max() <= GAUSS_ABS_TOL
+
+
+def test_gaussian_error_over_many_values(dev, oracle_mod):
+    """4M Gaussians: the worst case of the fp32 transform, including the
+    extremes of u (tails) and v (angles near 0 and 1)."""
+    import torch
+    import token_activation_perturbation_amd as dust
+    _, g_gpu = dust.dust_noise_fill(3, 0, 16, 0, 1024, 256, words=False, device=dev)
+    torch.cuda.synchronize(dev)
+    _, g_ref = oracle_mod.noise_fill(3, 0, 16, 0, 1024, 256, words=False)
+    err = np.abs(g_gpu.cpu().numpy().astype(np.float64) - g_ref)
+    relerr = err / np.maximum(np.abs(g_ref), 1e-3)
+    print(f"gauss 4M: max abs {err.max():.3e} rms {np.sqrt((err**2).mean()):.3e} "
+          f"max rel(|a|>1e-3) {relerr.max():.3e}", flush=True)
+    assert err.max() <= GAUSS_ABS_TOL
+
+
+# --------------------------------------------------------------------------
+# Stage parity on small shapes (several tiles, ragged tails, every option)
+
+SMALL = [
+    # T, seq_len, d_in, d_out, K, sigma, gamma, antithetic, dtype
+    (64, 64, 64, 64, 16, 1e-2, 0.0, False, "f32"),
+    (192, 64, 96, 160, 32, 1e-2, 0.0, True, "bf16"),
+    (130, 26, 45, 37, 10, 2e-2, 0.5, False, "bf16"),     # ragged everything
+    (96, 32, 72, 300, 34, 5e-3, 0.9, True, "bf16"),      # K_n = 17: ragged batches
+    (64, 16, 33, 19, 6, 1e-2, 1.0, False, "f32"),        # gamma = 1: suffix sums
+    (40, 1, 24, 8, 2, 1e-1, 0.7, True, "bf16"),          # one-token sequences, K = 2
+    (1, 1, 1, 1, 2, 1e-2, 0.0, False, "f32"),            # the smallest problem
+    (256, 128, 128, 1024, 64, 1e-2, 0.5, True, "bf16"),  # d_out spans 4 quad rounds
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[f"T{c[0]}_dout{c[3]}_K{c[4]}_g{c[6]}_{c[8]}" for c in SMALL])
+def test_stage_parity_small(dev, oracle_mod, threads, case):
+    T, seq_len, d_in, d_out, K, sigma, gamma, anti, dtype = case
+    print(f"stage parity case {case}", flush=True)
+    inp = synth.random_inputs(T, d_in, d_out, dtype, seed=T * 7 + d_out)
+    kw = dict(K=K, sigma=sigma, gamma=gamma, seed=T + 11, antithetic=anti, seq_len=seq_len)
+    got = gpu_estimate(inp, dtype, dev, **kw)
+    ref = oracle_mod.estimate(inp["X"], inp["W"], inp["target"], threads=threads, **kw)
+    errs = {"loss": rel(got["loss"], ref["loss"]), "rho": rel(got["rho"], ref["rho"]),
+            "reward": rel(got["reward"], ref["reward"]), "g": rel(got["g"], ref["g"]),
+            "G_W": rel(got["G_W"], ref["G"])}
+    report("  rel err", errs)
+    tol = TOL[dtype]
+    for k, v in errs.items():
+        assert v <= tol, (k, v, tol)
+
+
+# --------------------------------------------------------------------------
+# The five workloads at full size
+
+
+@pytest.mark.parametrize("name", ["tiny_f32", "bf16_layer"])
+def test_workload_full_parity(dev, oracle_mod, threads, name):
+    w = synth.WORKLOADS[name]
+    print(f"full parity {name}", flush=True)
+    inp = synth.make_inputs(w)
+    kw = dict(K=w.K, sigma=w.sigma, gamma=w.gamma, seed=w.noise_seed, antithetic=w.antithetic,
+              seq_len=w.seq_len)
+    got = gpu_estimate(inp, w.dtype, dev, **kw)
+    ref = oracle_mod.estimate(inp["X"], inp["W"], inp["target"], threads=threads, **kw)
+    errs = {"loss": rel(got["loss"], ref["loss"]), "rho": rel(got["rho"], ref["rho"]),
+            "reward": rel(got["reward"], ref["reward"]), "g": rel(got["g"], ref["g"]),
+            "G_W": rel(got["G_W"], ref["G"])}
+    report(f"  {name}", errs)
+    for k, v in errs.items():
+        assert v <= TOL[w.dtype], (k, v)
+
+
+@pytest.mark.parametrize("name", ["mlp_up_bf16", "qkv_credit_bf16", "large_population_bf16"])
+def test_workload_full_size_sampled(dev, oracle_mod, threads, name):
+    """Full-size run in the benchmarked launch configuration.  The oracle
+    recomputes one whole sequence (every output of its tokens: loss, rho,
+    credit, g); G_W is checked at full size against the property
+    G_W = sum_t g_t x_t^T evaluated in fp64 from the GPU's own g."""
+    w = synth.WORKLOADS[name]
+    print(f"full-size sampled parity {name}", flush=True)
+    inp = synth.make_inputs(w)
+    kw = dict(K=w.K, sigma=w.sigma, gamma=w.gamma, seed=w.noise_seed, antithetic=w.antithetic,
+              seq_len=w.seq_len)
+    got = gpu_estimate(inp, w.dtype, dev, **kw)
+    s = w.n_seq - 1
+    ref = oracle_mod.estimate(inp["X"], inp["W"], inp["target"], seq_range=(s, s + 1),
+                              threads=threads, **kw)
+    sl = slice(s * w.seq_len, (s + 1) * w.seq_len)
+    errs = {"loss": rel(got["loss"][sl], ref["loss"]), "rho": rel(got["rho"][sl], ref["rho"]),
+            "reward": rel(got["reward"][sl], ref["reward"]), "g": rel(got["g"][sl], ref["g"])}
+    G_from_g = got["g"].T @ inp["X"].astype(np.float64)
+    errs["G_W_vs_gTX"] = rel(got["G_W"], G_from_g)
+    report(f"  {name} (sequence {s})", errs)
+    for k, v in errs.items():
+        assert v <= TOL[w.dtype], (k, v)
+
+
+# --------------------------------------------------------------------------
+# Determinism and the statistical law on GPU outputs
+
+
+def test_bitwise_deterministic(dev):
+    w = synth.WORKLOADS["bf16_layer"]
+    inp = synth.make_inputs(w, T=1024)
+    kw = dict(K=w.K, sigma=w.sigma, gamma=0.5, seed=5, antithetic=w.antithetic,
+              seq_len=w.seq_len)
+    a = gpu_estimate(inp, w.dtype, dev, **kw)
+    b = gpu_estimate(inp, w.dtype, dev, **kw)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
+
+
+def test_gpu_cosine_law(dev, oracle_mod):
+    """Per-token cosine of g_t to delta_t about sqrt(K_e/(K_e+D+1)) ("What a
+    zeroth-order gradient is"), on the bf16 layer workload (K_e = 32 pairs,
+    D = 512): 0.242."""
+    w = synth.WORKLOADS["bf16_layer"]
+    inp = synth.make_inputs(w)
+    got = gpu_estimate(inp, w.dtype, dev, K=w.K, sigma=w.sigma, gamma=w.gamma,
+                       seed=w.noise_seed, antithetic=w.antithetic, seq_len=w.seq_len)
+    delta, _ = oracle_mod.true_gradient(inp["X"], inp["W"], inp["target"])
+    g = got["g"]
+    cos = (g * delta).sum(1) / np.linalg.norm(g, axis=1) / np.linalg.norm(delta, axis=1)
+    pred = np.sqrt(32 / (32 + 512 + 1))
+    print(f"cosine mean {cos.mean():.4f} predicted {pred:.4f}", flush=True)
+    assert abs(cos.mean() - pred) < 0.01

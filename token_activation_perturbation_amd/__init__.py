@@ -1,1 +1,193 @@
-"""Dust per-token zeroth-order estimator on MI355X (placeholder; binding follows)."""
+"""Dust per-token zeroth-order weight-gradient estimator on MI355X (gfx950).
+
+A thin ctypes binding over libdust.so: every function here only checks and
+marshals arguments (torch device tensors -> device pointers, the current HIP
+stream, a workspace tensor) and calls the C entry point of the same name
+declared in include/dust.h.  All arithmetic runs in the library's kernels.
+If libdust.so is missing the calls raise; nothing falls back to the CPU.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = ["DustError", "dust_workspace_bytes", "dust_validate", "dust_estimate",
+           "dust_noise_fill", "dust_set_timing_events", "dust_last_error", "library_path",
+           "DUST_F32", "DUST_BF16"]
+
+DUST_F32 = 0
+DUST_BF16 = 1
+_STATUS = {0: "DUST_OK", 1: "DUST_ERR_INVALID_ARG", 2: "DUST_ERR_UNSUPPORTED",
+           3: "DUST_ERR_WORKSPACE", 4: "DUST_ERR_HIP"}
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libdust.so")
+_lib = None
+
+
+class DustError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is missing: build it with "
+                           "`python -m token_activation_perturbation_amd.build`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i64, i32, f32, sz = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                             ctypes.c_float, ctypes.c_size_t)
+    lib.dust_workspace_bytes.argtypes = [i64, i64, i64, i32, i32, i32]
+    lib.dust_workspace_bytes.restype = sz
+    lib.dust_validate.argtypes = [vp, vp, vp, i64, i64, i64, i64, i32, i32, f32, f32, i32,
+                                  vp, vp, sz]
+    lib.dust_validate.restype = ctypes.c_int
+    lib.dust_estimate.argtypes = [vp, vp, vp, i64, i64, i64, i64, i32, i32, f32, f32,
+                                  ctypes.c_uint64, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.dust_estimate.restype = ctypes.c_int
+    lib.dust_noise_fill.argtypes = [ctypes.c_uint64, i64, i64, i64, i64, i64, vp, vp, vp]
+    lib.dust_noise_fill.restype = ctypes.c_int
+    vpp = ctypes.POINTER(ctypes.c_void_p)
+    lib.dust_set_timing_events.argtypes = [vpp, vpp, i32]
+    lib.dust_set_timing_events.restype = ctypes.c_int
+    lib.dust_last_error.argtypes = []
+    lib.dust_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def dust_last_error() -> str:
+    return _load().dust_last_error().decode()
+
+
+def _check(status: int):
+    if status != 0:
+        raise DustError(status, dust_last_error())
+
+
+def dust_workspace_bytes(T: int, d_in: int, d_out: int, K: int, antithetic: bool,
+                         dtype: int) -> int:
+    return int(_load().dust_workspace_bytes(T, d_in, d_out, K, int(bool(antithetic)), dtype))
+
+
+def dust_validate(X_ptr, W_ptr, target_ptr, T, d_in, d_out, seq_len, dtype, K, sigma, gamma,
+                  antithetic, G_ptr, workspace_ptr, workspace_bytes) -> int:
+    """Raw host-side validation (no device memory touched); returns the status."""
+    return int(_load().dust_validate(X_ptr, W_ptr, target_ptr, T, d_in, d_out, seq_len, dtype,
+                                     K, sigma, gamma, int(bool(antithetic)), G_ptr,
+                                     workspace_ptr, workspace_bytes))
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return DUST_BF16
+    if t.dtype == torch.float32:
+        return DUST_F32
+    raise TypeError(f"unsupported dtype {t.dtype}: bfloat16 or float32")
+
+
+def _stream_ptr(device):
+    import torch
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def dust_estimate(X, W, target, *, K: int, sigma: float, gamma: float, seed: int,
+                  antithetic: bool, seq_len: int, want_loss: bool = False,
+                  want_rho: bool = False, want_reward: bool = False, want_g: bool = False,
+                  out: dict | None = None, workspace=None):
+    """Enqueue dust_estimate on the current stream of X's device.
+
+    X [T,d_in], W [d_out,d_in], target [T,d_out]: contiguous device tensors,
+    all bfloat16 or all float32.  Returns a dict of fp32 device tensors: "G_W"
+    [d_out,d_in] and the requested optional outputs "loss" [T], "rho" [T,K],
+    "reward" [T,K], "g" [T,d_out].  ``out`` may supply preallocated output
+    tensors and ``workspace`` a uint8 device tensor of dust_workspace_bytes.
+    """
+    import torch
+    for name, t in (("X", X), ("W", W), ("target", target)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    if not (X.dtype == W.dtype == target.dtype):
+        raise TypeError("X, W and target must share one dtype")
+    if X.dim() != 2 or W.dim() != 2 or target.dim() != 2:
+        raise ValueError("X, W and target must be 2-D")
+    T, d_in = X.shape
+    d_out = W.shape[0]
+    if W.shape[1] != d_in or tuple(target.shape) != (T, d_out):
+        raise ValueError(f"shape mismatch: X {tuple(X.shape)}, W {tuple(W.shape)}, "
+                         f"target {tuple(target.shape)}")
+    dt = _dtype_code(X)
+    dev = X.device
+    res = dict(out or {})
+
+    def _get(name, shape):
+        t = res.get(name)
+        if t is None:
+            t = torch.empty(shape, dtype=torch.float32, device=dev)
+            res[name] = t
+        elif (tuple(t.shape) != tuple(shape) or t.dtype != torch.float32 or not t.is_contiguous()
+              or t.device != dev):
+            raise ValueError(f"out[{name!r}] must be a contiguous float32 {tuple(shape)} "
+                             f"tensor on {dev}")
+        return t
+
+    G = _get("G_W", (d_out, d_in))
+    loss = _get("loss", (T,)) if want_loss else None
+    rho = _get("rho", (T, K)) if want_rho else None
+    reward = _get("reward", (T, K)) if want_reward else None
+    g = _get("g", (T, d_out)) if want_g else None
+    need = dust_workspace_bytes(T, d_in, d_out, K, antithetic, dt)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    ptr = lambda t: None if t is None else t.data_ptr()  # noqa: E731
+    status = _load().dust_estimate(
+        X.data_ptr(), W.data_ptr(), target.data_ptr(), T, d_in, d_out, seq_len, dt, K,
+        sigma, gamma, ctypes.c_uint64(seed & 0xFFFFFFFFFFFFFFFF), int(bool(antithetic)),
+        G.data_ptr(), ptr(loss), ptr(rho), ptr(reward), ptr(g), workspace.data_ptr(),
+        workspace.numel(), _stream_ptr(dev))
+    _check(status)
+    return res
+
+
+def dust_noise_fill(seed: int, n0: int, n_cnt: int, t0: int, t_cnt: int, d_out: int, *,
+                    words: bool = True, gauss: bool = True, device="cuda"):
+    """The estimator's noise written out: words [n_cnt,t_cnt,4*ceil(d_out/4)]
+    (int32 tensor holding the uint32 bits) and Gaussians [n_cnt,t_cnt,d_out]
+    (float32), on the current stream of `device`."""
+    import torch
+    nq = (d_out + 3) // 4
+    w = torch.empty((n_cnt, t_cnt, 4 * nq), dtype=torch.int32, device=device) if words else None
+    g = torch.empty((n_cnt, t_cnt, d_out), dtype=torch.float32, device=device) if gauss else None
+    status = _load().dust_noise_fill(
+        ctypes.c_uint64(seed & 0xFFFFFFFFFFFFFFFF), n0, n_cnt, t0, t_cnt, d_out,
+        None if w is None else w.data_ptr(), None if g is None else g.data_ptr(),
+        _stream_ptr(torch.device(device)))
+    _check(status)
+    return w, g
+
+
+def dust_set_timing_events(starts, stops) -> None:
+    """Register event pairs (torch.cuda.Event with enable_timing=True, already
+    recorded once so their HIP events exist) that the next dust_estimate calls
+    record around their noise kernel, pair i on call i.  Pass empty lists to
+    turn the hook off."""
+    n = len(starts)
+    if len(stops) != n:
+        raise ValueError("starts and stops must have the same length")
+    if n == 0:
+        _check(_load().dust_set_timing_events(None, None, 0))
+        return
+    arr = ctypes.c_void_p * n
+    handles_s = [e.cuda_event for e in starts]
+    handles_e = [e.cuda_event for e in stops]
+    if not all(handles_s) or not all(handles_e):
+        raise ValueError("record every event once before registering it")
+    _check(_load().dust_set_timing_events(arr(*handles_s), arr(*handles_e), n))

@@ -1,0 +1,83 @@
+// dust_host.cpp -- host-only entry points of libdust.so: argument validation,
+// workspace sizing and the thread-local error text.  No HIP calls here, so
+// these work (and are tested) on machines without a GPU.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+
+#include "dust.h"
+#include "dust_internal.hpp"
+#include "dust_plan.hpp"
+
+namespace {
+thread_local char g_last_error[512] = "";
+}
+
+namespace dust {
+
+dust_status_t fail(dust_status_t status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+dust_status_t ok() {
+  g_last_error[0] = '\0';
+  return DUST_OK;
+}
+
+}  // namespace dust
+
+extern "C" {
+
+size_t dust_workspace_bytes(int64_t T, int64_t d_in, int64_t d_out, int32_t K,
+                            int32_t antithetic, int32_t dtype) {
+  if (dtype != DUST_F32 && dtype != DUST_BF16) return 0;
+  dust::Plan p;
+  if (!dust::make_plan(T, d_in, d_out, K, antithetic, dtype, &p)) return 0;
+  return p.total;
+}
+
+dust_status_t dust_validate(const void* X, const void* W, const void* target,
+                            int64_t T, int64_t d_in, int64_t d_out,
+                            int64_t seq_len, int32_t dtype, int32_t K,
+                            float sigma, float gamma, int32_t antithetic,
+                            const float* G_W, const void* workspace,
+                            size_t workspace_bytes) {
+  using dust::fail;
+  if (!X || !W || !target || !G_W)
+    return fail(DUST_ERR_INVALID_ARG, "X, W, target and G_W must not be NULL");
+  if (T <= 0 || d_in <= 0 || d_out <= 0)
+    return fail(DUST_ERR_INVALID_ARG, "T=%lld, d_in=%lld, d_out=%lld must be positive",
+                (long long)T, (long long)d_in, (long long)d_out);
+  if (T >= (int64_t(1) << 31) || d_out >= (int64_t(1) << 31) || d_in >= (int64_t(1) << 31))
+    return fail(DUST_ERR_INVALID_ARG, "T, d_in and d_out must be below 2^31");
+  if (T >= (int64_t(1) << 24))
+    return fail(DUST_ERR_UNSUPPORTED, "T=%lld: at most 2^24 - 1 tokens per call", (long long)T);
+  if (seq_len <= 0 || T % seq_len != 0)
+    return fail(DUST_ERR_INVALID_ARG, "seq_len=%lld must be positive and divide T=%lld",
+                (long long)seq_len, (long long)T);
+  if (K < 2)
+    return fail(DUST_ERR_INVALID_ARG, "K=%d: at least 2 draws are needed for centring", K);
+  if (antithetic && (K % 2) != 0)
+    return fail(DUST_ERR_INVALID_ARG, "K=%d must be even with antithetic pairs", K);
+  if (!(std::isfinite(sigma) && sigma > 0.0f))
+    return fail(DUST_ERR_INVALID_ARG, "sigma=%g must be finite and positive", (double)sigma);
+  if (!(std::isfinite(gamma) && gamma >= 0.0f && gamma <= 1.0f))
+    return fail(DUST_ERR_INVALID_ARG, "gamma=%g must lie in [0, 1]", (double)gamma);
+  if (dtype != DUST_F32 && dtype != DUST_BF16)
+    return fail(DUST_ERR_UNSUPPORTED, "dtype=%d: only DUST_F32 (0) and DUST_BF16 (1)", dtype);
+  dust::Plan p;
+  if (!dust::make_plan(T, d_in, d_out, K, antithetic, dtype, &p))
+    return fail(DUST_ERR_UNSUPPORTED, "sizes exceed the kernels' index range");
+  if (!workspace || workspace_bytes < p.total)
+    return fail(DUST_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed",
+                workspace ? workspace_bytes : (size_t)0, p.total);
+  return dust::ok();
+}
+
+const char* dust_last_error(void) { return g_last_error; }
+
+}  // extern "C"

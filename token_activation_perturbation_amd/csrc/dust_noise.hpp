@@ -1,0 +1,82 @@
+// dust_noise.hpp -- the estimator's noise, evaluated inline on gfx950.
+//
+// The pages fix no generator; they ask for noise that is a pure function of
+// a seed and an index so it never has to be stored ("Scaling To Unfathomable
+// Depth", section "MeZO": counter-based generators such as Philox).  Value
+// a_t^(n)[c] is:
+//   words (w0,w1,w2,w3) = Philox4x32-10(counter (c/4, t, n, 0),
+//                                        key (seed low, seed high))
+//   (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as easy as 1, 2,
+//   3", SC'11), then Box-Muller on (w0,w1) for channels 4q, 4q+1 and on
+//   (w2,w3) for 4q+2, 4q+3 with 24-bit uniforms
+//   u = ((w_even >> 8) + 1) 2^-24 in (0,1], v = (w_odd >> 8) 2^-24 in [0,1),
+//   a_even = sqrt(-2 ln u) cos(2 pi v), a_odd = sqrt(-2 ln u) sin(2 pi v).
+//
+// gfx950 notes.  The counter is laid out so that one lane's quad index is the
+// only per-lane word: token and noise index are wave-uniform, so the first
+// two rounds largely run on the scalar unit or are loop-invariant, and the
+// key schedule is scalar.  The 32x32->64 products map to v_mad_u64_u32.  The
+// transform uses the hardware transcendental unit directly: v_log_f32 is
+// log2, and v_sin_f32 / v_cos_f32 take their argument in revolutions, so
+// 2 pi v needs no range reduction (v is already in [0,1)).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dust {
+
+constexpr uint32_t kPhiloxM0 = 0xD2511F53u;
+constexpr uint32_t kPhiloxM1 = 0xCD9E8D57u;
+constexpr uint32_t kPhiloxW0 = 0x9E3779B9u;
+constexpr uint32_t kPhiloxW1 = 0xBB67AE85u;
+
+struct NoiseKey {
+  uint32_t k0, k1;
+};
+
+__device__ __forceinline__ void mul_wide(uint32_t m, uint32_t x, uint32_t& hi, uint32_t& lo) {
+  const uint64_t prod = (uint64_t)m * (uint64_t)x;
+  hi = (uint32_t)(prod >> 32);
+  lo = (uint32_t)prod;
+}
+
+__device__ __forceinline__ uint4 philox4x32_10(uint32_t x0, uint32_t x1, uint32_t x2,
+                                               uint32_t x3, NoiseKey key) {
+  uint32_t k0 = key.k0, k1 = key.k1;
+#pragma unroll
+  for (int round = 0; round < 10; ++round) {
+    uint32_t hi0, lo0, hi1, lo1;
+    mul_wide(kPhiloxM0, x0, hi0, lo0);
+    mul_wide(kPhiloxM1, x2, hi1, lo1);
+    const uint32_t y0 = hi1 ^ x1 ^ k0;
+    const uint32_t y2 = hi0 ^ x3 ^ k1;
+    x0 = y0;
+    x1 = lo1;
+    x2 = y2;
+    x3 = lo0;
+    k0 += kPhiloxW0;
+    k1 += kPhiloxW1;
+  }
+  return make_uint4(x0, x1, x2, x3);
+}
+
+// -2 ln 2, so that -2 ln u = kMinusTwoLn2 * log2 u.
+constexpr float kMinusTwoLn2 = -1.38629436111989061883f;
+
+__device__ __forceinline__ float2 box_muller(uint32_t w_even, uint32_t w_odd) {
+  const float u = __builtin_fmaf((float)(w_even >> 8), 0x1p-24f, 0x1p-24f);  // exact
+  const float v = (float)(w_odd >> 8) * 0x1p-24f;                            // exact
+  const float radius = __builtin_amdgcn_sqrtf(kMinusTwoLn2 * __builtin_amdgcn_logf(u));
+  return make_float2(radius * __builtin_amdgcn_cosf(v), radius * __builtin_amdgcn_sinf(v));
+}
+
+// The four Gaussians of channel quad q of token t under noise index n.
+__device__ __forceinline__ float4 noise_quad(uint32_t q, uint32_t t, uint32_t n, NoiseKey key) {
+  const uint4 w = philox4x32_10(q, t, n, 0u, key);
+  const float2 a = box_muller(w.x, w.y);
+  const float2 b = box_muller(w.z, w.w);
+  return make_float4(a.x, a.y, b.x, b.y);
+}
+
+}  // namespace dust

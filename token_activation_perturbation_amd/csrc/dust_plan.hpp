@@ -1,0 +1,119 @@
+// dust_plan.hpp -- host-only launch plan and workspace layout of dust_estimate.
+//
+// Pure C++ (no HIP types, no HIP calls): dust_workspace_bytes and
+// dust_validate use it on machines without a GPU, and dust_estimate uses the
+// very same plan to carve the workspace and size its launches.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+namespace dust {
+
+// Noise vectors handled per unrolled batch inside the noise kernels.
+constexpr int kNoiseBatch = 16;
+// Waves the noise kernels aim to keep resident (256 CUs x 4 SIMDs x 8).
+constexpr int64_t kTargetWaves = 8192;
+
+struct Plan {
+  int64_t T = 0, d_in = 0, d_out = 0;
+  int32_t K = 0, K_n = 0, antithetic = 0, dtype = 0;
+  int32_t nq = 0;  // channel quads per token, ceil(d_out / 4)
+
+  // jitter-loss kernel: one wave per (token, chunk of noise indices)
+  int32_t jl_chunks = 1, jl_per_chunk = 0;
+  // reweight kernel: one workgroup of rw_waves waves per token, the noise
+  // indices split into rw_waves contiguous ranges of rw_per_wave
+  int32_t rw_waves = 1, rw_per_wave = 0;
+  // fused single-generation kernel (gamma = 0): one workgroup of fz_waves
+  // waves per token, the noise indices split into ranges of fz_per_wave
+  int32_t fz_waves = 1, fz_per_wave = 0;
+  // outer product: split of the token (contraction) axis
+  int32_t outer_split = 1;
+  int64_t outer_tokens = 0;  // tokens per split (multiple of 32)
+
+  // workspace byte offsets (each 256-byte aligned) and total
+  size_t off_delta = 0, off_P = 0, off_Q = 0, off_rho = 0, off_mean = 0,
+         off_wgt = 0, off_g = 0, off_gpart = 0, total = 0;
+};
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Returns false when the sizes cannot be planned (non-positive sizes, K < 2,
+// odd K with antithetic pairs, or sizes past the kernels' 32-bit indices).
+inline bool make_plan(int64_t T, int64_t d_in, int64_t d_out, int32_t K,
+                      int32_t antithetic, int32_t dtype, Plan* p) {
+  if (T <= 0 || d_in <= 0 || d_out <= 0 || K < 2) return false;
+  if (antithetic && (K % 2) != 0) return false;
+  // T below 2^24 keeps every grid (up to 256 threads per token) under 2^32
+  // threads; the noise counter words themselves would allow 2^32.
+  if (T >= (int64_t(1) << 24) || d_out >= (int64_t(1) << 31) ||
+      d_in >= (int64_t(1) << 31))
+    return false;
+  Plan q;
+  q.T = T;
+  q.d_in = d_in;
+  q.d_out = d_out;
+  q.K = K;
+  q.antithetic = antithetic ? 1 : 0;
+  q.K_n = antithetic ? K / 2 : K;
+  q.dtype = dtype;
+  q.nq = (int32_t)ceil_div(d_out, 4);
+  if ((int64_t)T * q.K_n >= (int64_t(1) << 40)) return false;
+
+  const int64_t batches = ceil_div(q.K_n, kNoiseBatch);
+  // jitter-loss: enough (token, chunk) waves to fill the chip
+  int64_t chunks = ceil_div(kTargetWaves, T);
+  if (chunks > batches) chunks = batches;
+  if (chunks < 1) chunks = 1;
+  q.jl_per_chunk = (int32_t)(ceil_div(batches, chunks) * kNoiseBatch);
+  q.jl_chunks = (int32_t)ceil_div(q.K_n, q.jl_per_chunk);
+  // reweight: 1, 2 or 4 waves per token
+  int64_t waves = ceil_div(kTargetWaves, T);
+  if (waves > 4) waves = 4;
+  if (waves > batches) waves = batches;
+  if (waves == 3) waves = 2;
+  if (waves < 1) waves = 1;
+  q.rw_per_wave = (int32_t)(ceil_div(batches, waves) * kNoiseBatch);
+  q.rw_waves = (int32_t)ceil_div(q.K_n, q.rw_per_wave);
+  // fused: same wave budget; ranges are whole multiples of 4 noise indices
+  int64_t fw = ceil_div(kTargetWaves, T);
+  if (fw > 4) fw = 4;
+  if (fw > ceil_div(q.K_n, 4)) fw = ceil_div(q.K_n, 4);
+  if (fw == 3) fw = 2;
+  if (fw < 1) fw = 1;
+  q.fz_per_wave = (int32_t)(ceil_div(ceil_div(q.K_n, fw), 4) * 4);
+  q.fz_waves = (int32_t)ceil_div(q.K_n, q.fz_per_wave);
+  // outer product: 64x64 output tiles; split the tokens until ~1024 tiles
+  const int64_t tiles = ceil_div(d_out, 64) * ceil_div(d_in, 64);
+  int64_t split = ceil_div(1024, tiles);
+  const int64_t max_split = ceil_div(T, 256);  // keep >= 256 tokens a split
+  if (split > max_split) split = max_split;
+  if (split > 64) split = 64;
+  if (split < 1) split = 1;
+  q.outer_tokens = ceil_div(ceil_div(T, split), 32) * 32;
+  q.outer_split = (int32_t)ceil_div(T, q.outer_tokens);
+
+  size_t off = 0;
+  auto take = [&off](size_t bytes) {
+    size_t at = off;
+    off = align256(off + bytes);
+    return at;
+  };
+  q.off_delta = take(sizeof(float) * size_t(T) * size_t(d_out));
+  q.off_P = take(sizeof(float) * size_t(T) * size_t(q.K_n));
+  q.off_Q = take(sizeof(float) * size_t(T) * size_t(q.K_n));
+  q.off_rho = take(sizeof(float) * size_t(T) * size_t(K));
+  q.off_mean = take(sizeof(float) * size_t(T));
+  q.off_wgt = take(sizeof(float) * size_t(T) * size_t(q.K_n));
+  q.off_g = take(sizeof(float) * size_t(T) * size_t(d_out));
+  q.off_gpart = take(q.outer_split > 1 ? sizeof(float) * size_t(q.outer_split) *
+                                             size_t(d_out) * size_t(d_in)
+                                       : 0);
+  q.total = off;
+  *p = q;
+  return true;
+}
+
+}  // namespace dust

@@ -1,0 +1,96 @@
+"""Summaries of rocprofv3 output (its SQLite results database) as short text.
+
+    python -m token_activation_perturbation_amd.profiling trace <results.db> <title> <command>
+    python -m token_activation_perturbation_amd.profiling pmc <fetch.db> <write.db> <kernel> <copy_bytes>
+
+`trace` prints a markdown table of per-kernel calls and durations from a
+`--kernel-trace --stats` run.  `pmc` turns two counter runs (FETCH_SIZE,
+then WRITE_SIZE, in KiB per dispatch) into HBM bytes per launch of `kernel`,
+scaled by what the same counters read for the largest plain copy kernel in
+the run (whose true traffic is copy_bytes read + copy_bytes written).
+"""
+from __future__ import annotations
+
+import json
+import re
+import sqlite3
+import sys
+
+
+def short_name(name: str) -> str:
+    name = name.replace("(anonymous namespace)::", "").replace("void ", "")
+    depth, out = 0, []
+    for ch in name:  # drop the argument list, keep template arguments
+        if ch == "(" and depth == 0:
+            break
+        depth += ch == "<"
+        depth -= ch == ">"
+        out.append(ch)
+    s = "".join(out)
+    return s if len(s) < 90 else s[:87] + "..."
+
+
+def trace_rows(db: str):
+    con = sqlite3.connect(db)
+    return list(con.execute(
+        "select name, total_calls, total_duration, average, percentage from top_kernels"))
+
+
+def trace_markdown(db: str, title: str, command: str) -> str:
+    lines = [f"# {title}", "", "Command (repository root, MI355X box):", "", "```", command,
+             "```", "", "| kernel | calls | total us | avg us | % |", "|---|---|---|---|---|"]
+    for name, calls, tot, avg, pct in trace_rows(db):
+        lines.append(f"| `{short_name(name)}` | {calls} | {tot:.1f} | {avg:.2f} | {pct:.1f} |")
+    return "\n".join(lines) + "\n"
+
+
+def _pmc_per_dispatch(db: str, counter: str):
+    """{kernel name: [value per dispatch]} for one counter."""
+    con = sqlite3.connect(db)
+    cols = [r[1] for r in con.execute("pragma table_info(counters_collection)")]
+    name_col = "kernel_name" if "kernel_name" in cols else "name"
+    value_col = "value" if "value" in cols else "counter_value"
+    cname_col = "counter_name" if "counter_name" in cols else "counter"
+    out = {}
+    q = (f"select {name_col}, dispatch_id, sum({value_col}) from counters_collection "
+         f"where {cname_col} = ? group by dispatch_id")
+    for name, _did, val in con.execute(q, (counter,)):
+        out.setdefault(name, []).append(float(val))
+    return out
+
+
+def pmc_traffic(fetch_db: str, write_db: str, kernel: str, copy_bytes: int) -> dict:
+    fetch = _pmc_per_dispatch(fetch_db, "FETCH_SIZE")
+    write = _pmc_per_dispatch(write_db, "WRITE_SIZE")
+
+    def pick(d, pattern):
+        keys = [k for k in d if re.search(pattern, k)]
+        if not keys:
+            raise KeyError(pattern)
+        return keys[0]
+
+    copy_key_f = pick(fetch, r"copy|Copy")
+    copy_key_w = pick(write, r"copy|Copy")
+    # the copy dispatch with the most traffic is the calibration copy
+    copy_f = max(fetch[copy_key_f])
+    copy_w = max(write[copy_key_w])
+    f_scale = copy_bytes / (copy_f * 1024.0)
+    w_scale = copy_bytes / (copy_w * 1024.0)
+    kf = pick(fetch, re.escape(kernel))
+    kw = pick(write, re.escape(kernel))
+    fetch_kib = sum(fetch[kf]) / len(fetch[kf])
+    write_kib = sum(write[kw]) / len(write[kw])
+    return {"kernel": kernel, "fetch_kib_per_dispatch": fetch_kib,
+            "write_kib_per_dispatch": write_kib, "copy_fetch_kib": copy_f,
+            "copy_write_kib": copy_w, "fetch_scale": f_scale, "write_scale": w_scale,
+            "bytes_per_launch": fetch_kib * 1024.0 * f_scale + write_kib * 1024.0 * w_scale}
+
+
+if __name__ == "__main__":
+    if len(sys.argv) >= 5 and sys.argv[1] == "trace":
+        print(trace_markdown(sys.argv[2], sys.argv[3], sys.argv[4]), end="")
+    elif len(sys.argv) >= 6 and sys.argv[1] == "pmc":
+        print(json.dumps(pmc_traffic(sys.argv[2], sys.argv[3], sys.argv[4], int(sys.argv[5])),
+                         indent=1))
+    else:
+        sys.exit(__doc__)

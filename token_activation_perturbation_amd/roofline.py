@@ -1,0 +1,56 @@
+"""The ALU roofline of the estimator's noise kernels on MI355X (gfx950).
+
+The noise kernels move almost no memory: each noise value is a pure function
+of (seed, noise index, token, channel), generated in registers and consumed
+at once.  Their bound is the vector ALU issue rate, counted in lane-slots:
+
+* Peak.  MI355X: 256 compute units at 2.4 GHz; its fp32 vector peak of
+  157.3 TFLOP/s is 2 flops x 128 lanes per clock per CU, so a full-rate
+  32-bit VALU operation occupies one of 256 x 128 x 2.4e9 = 7.864e13
+  lane-slots per second.  Quarter-rate operations (32x32->64 integer
+  multiply, and the transcendentals log2, sqrt, sin, cos) occupy 4 slots.
+
+* Work per distinct noise value (the minimum the method needs: each of the
+  K_n * T * d_out values generated once, where K_n = K/2 with antithetic
+  pairs, else K).  Per quad of four values:
+    Philox4x32-10   10 rounds x (2 multiplies x 4 + 4 xor)      = 120 slots
+    Box-Muller      8 transcendentals x 4 + 18 simple ops        =  50 slots
+  i.e. 42.5 slots per value, plus the consumers: 2 FMA for P and Q (loss
+  change), 1 FMA for the reweighted sum g, and 1 add for the plain-draw
+  noise sum used by the centring.
+
+Counted this way a two-pass pipeline (generate for the loss change, then
+regenerate for g) is capped at about half of the roofline; a single
+generation can reach all of it.
+"""
+from __future__ import annotations
+
+CUS = 256
+CLOCK_HZ = 2.4e9
+LANES_PER_CU_CLOCK = 128
+PEAK_SLOTS_PER_S = CUS * LANES_PER_CU_CLOCK * CLOCK_HZ  # 7.864e13
+
+PHILOX_SLOTS_PER_QUAD = 10 * (2 * 4 + 4)           # 120
+BOX_MULLER_SLOTS_PER_QUAD = 8 * 4 + 18             # 50
+GEN_SLOTS_PER_VALUE = (PHILOX_SLOTS_PER_QUAD + BOX_MULLER_SLOTS_PER_QUAD) / 4.0  # 42.5
+
+
+def distinct_noise_values(T: int, d_out: int, K: int, antithetic: bool) -> int:
+    K_n = K // 2 if antithetic else K
+    return K_n * T * d_out
+
+
+def fused_kernel_slots(T: int, d_out: int, K: int, antithetic: bool) -> float:
+    """Algorithmic lane-slots of the single-generation kernel (gamma = 0)."""
+    per_value = GEN_SLOTS_PER_VALUE + 3.0 + (0.0 if antithetic else 1.0)
+    return distinct_noise_values(T, d_out, K, antithetic) * per_value
+
+
+def jitter_kernel_slots(T: int, d_out: int, K: int, antithetic: bool) -> float:
+    """Algorithmic lane-slots of the jitter-loss kernel of the two-pass path."""
+    return distinct_noise_values(T, d_out, K, antithetic) * (GEN_SLOTS_PER_VALUE + 2.0)
+
+
+def estimate_min_seconds(T: int, d_out: int, K: int, antithetic: bool) -> float:
+    """Lower bound on one estimate: one generation of every noise value."""
+    return fused_kernel_slots(T, d_out, K, antithetic) / PEAK_SLOTS_PER_S
