@@ -25,6 +25,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+CAL_COPY_BYTES = 256 << 20
 KERNEL_SOURCES = ["token_activation_perturbation_amd/csrc/dust_kernels.hip",
                   "token_activation_perturbation_amd/csrc/dust_noise.hpp"]
 
@@ -106,6 +107,13 @@ def main():
                      dtype=torch.uint8, device=dev)
     kw = dict(K=w.K, sigma=w.sigma, gamma=w.gamma, seed=w.noise_seed, antithetic=w.antithetic,
               seq_len=w.seq_len)
+    # an untimed plain copy of known size: rocprofv3's FETCH_SIZE / WRITE_SIZE
+    # counters read on it calibrate the HBM bytes reported for our kernels
+    cal_src = torch.ones(CAL_COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    cal_dst = torch.empty_like(cal_src)
+    cal_dst.copy_(cal_src)
+    torch.cuda.synchronize(dev)
+    del cal_src, cal_dst
     out = {}
     for _ in range(args.warmup):
         out = dust.dust_estimate(X, W, tg, out=out, workspace=ws, **kw)

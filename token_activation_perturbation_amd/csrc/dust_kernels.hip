@@ -21,6 +21,7 @@
 
 #include "dust.h"
 #include "dust_internal.hpp"
+#include "dust_gemm.hpp"
 #include "dust_noise.hpp"
 #include "dust_plan.hpp"
 
@@ -39,6 +40,14 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   const uint32_t u = __float_as_uint(f);
   return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+// The wave's index in its workgroup, as a wave-uniform (scalar) value: the
+// compiler cannot prove threadIdx.x / 64 uniform, and everything derived
+// from it (token, noise range) would otherwise live in vector registers and
+// turn uniform loop tests into divergent branches.
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
 }
 
 __device__ __forceinline__ f32x4_t mfma_bf16(u16x8_t a, u16x8_t b, f32x4_t c) {
@@ -84,73 +93,17 @@ __global__ void noise_fill_kernel(NoiseKey key, int32_t n0, int32_t n_cnt, int32
 }
 
 // ---------------------------------------------------------------------------
-// Base GEMM: delta[t][c] = sum_k X[t][k] W[c][k] - target[t][c].
-// 64x64 output tile per 256-thread workgroup; each wave a 32x32 sub-tile as
-// 2x2 MFMA 16x16 blocks.  MFMA 16x16: lane l supplies row (l % 16) of A and
-// column (l % 16) of B for its group (l / 16) of the contraction, and holds
-// D rows 4 (l / 16) + 0..3 of column (l % 16).
-
-__device__ __forceinline__ u16x8_t load8_bf16(const uint16_t* __restrict__ base, int64_t rows,
-                                              int64_t ld, int64_t row, int64_t k, int64_t kmax,
-                                              bool vec) {
-  u16x8_t v = {0, 0, 0, 0, 0, 0, 0, 0};
-  if (row < rows) {
-    const uint16_t* p = base + row * ld + k;
-    if (vec && k + 8 <= kmax) {
-      v = *(const u16x8_t*)p;
-    } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        if (k + j < kmax) v[j] = p[j];
-    }
-  }
-  return v;
-}
-
-__global__ __launch_bounds__(256) void base_gemm_bf16_kernel(
-    const uint16_t* __restrict__ X, const uint16_t* __restrict__ W,
-    const uint16_t* __restrict__ target, int32_t T, int32_t d_in, int32_t d_out,
-    int32_t tiles_n, float* __restrict__ delta) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int tile_m = blockIdx.x / tiles_n, tile_n = blockIdx.x % tiles_n;
-  const int m0 = tile_m * 64 + (wave >> 1) * 32;
-  const int n0 = tile_n * 64 + (wave & 1) * 32;
-  const int r = lane & 15, kg = (lane >> 4) * 8;
-  const bool vec = (d_in % 8) == 0;
-  f32x4_t acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  for (int k = 0; k < d_in; k += 32) {
-    const u16x8_t a0 = load8_bf16(X, T, d_in, m0 + r, k + kg, d_in, vec);
-    const u16x8_t a1 = load8_bf16(X, T, d_in, m0 + 16 + r, k + kg, d_in, vec);
-    const u16x8_t b0 = load8_bf16(W, d_out, d_in, n0 + r, k + kg, d_in, vec);
-    const u16x8_t b1 = load8_bf16(W, d_out, d_in, n0 + 16 + r, k + kg, d_in, vec);
-    acc[0][0] = mfma_bf16(a0, b0, acc[0][0]);
-    acc[0][1] = mfma_bf16(a0, b1, acc[0][1]);
-    acc[1][0] = mfma_bf16(a1, b0, acc[1][0]);
-    acc[1][1] = mfma_bf16(a1, b1, acc[1][1]);
-  }
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int row = m0 + 16 * i + 4 * (lane >> 4) + e;
-        const int col = n0 + 16 * j + (lane & 15);
-        if (row < T && col < d_out) {
-          const int64_t o = (int64_t)row * d_out + col;
-          delta[o] = acc[i][j][e] - bf16_to_f32(target[o]);
-        }
-      }
-}
+// fp32 GEMMs (the fp32-input path): delta = X W^T - target and the outer
+// product, on v_mfma_f32_16x16x4_f32.  64x64 output tile per 256-thread
+// workgroup, a 32x32 block of 2x2 MFMA tiles per wave; lane l supplies row
+// l % 16 of A and column l % 16 of B at contraction index l / 16, and holds D
+// rows 4 (l / 16) + 0..3 of column l % 16.  (The bf16 GEMMs are in
+// dust_gemm.hpp.)
 
 __global__ __launch_bounds__(256) void base_gemm_f32_kernel(
     const float* __restrict__ X, const float* __restrict__ W, const float* __restrict__ target,
     int32_t T, int32_t d_in, int32_t d_out, int32_t tiles_n, float* __restrict__ delta) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = wave_id(), lane = threadIdx.x & 63;
   const int tile_m = blockIdx.x / tiles_n, tile_n = blockIdx.x % tiles_n;
   const int m0 = tile_m * 64 + (wave >> 1) * 32;
   const int n0 = tile_n * 64 + (wave & 1) * 32;
@@ -249,7 +202,7 @@ __global__ __launch_bounds__(256) void jitter_loss_kernel(
     int32_t chunks, int32_t per_chunk, NoiseKey key, float* __restrict__ P,
     float* __restrict__ Q, float* __restrict__ loss_clean) {
   const int lane = threadIdx.x & 63;
-  const int64_t task = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t task = (int64_t)blockIdx.x * 4 + wave_id();
   if (task >= (int64_t)T * chunks) return;
   const int32_t t = (int32_t)(task / chunks);
   const int32_t chunk = (int32_t)(task % chunks);
@@ -331,7 +284,7 @@ __global__ __launch_bounds__(256) void token_stats_kernel(
     const float* __restrict__ P, const float* __restrict__ Q, int32_t T, int32_t K, int32_t K_n,
     int32_t antithetic, float sigma, float* __restrict__ rho, float* __restrict__ mean) {
   const int lane = threadIdx.x & 63;
-  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t t = (int64_t)blockIdx.x * 4 + wave_id();
   if (t >= T) return;
   const float half_s2 = 0.5f * sigma * sigma;
   float sum = 0.f;
@@ -404,7 +357,7 @@ __global__ __launch_bounds__(256) void reweight_kernel(
     const float* __restrict__ wgt, int32_t T, int32_t d_out, int32_t nq, int32_t K_n,
     int32_t per_wave, NoiseKey key, float* __restrict__ g) {
   __shared__ float4 part[4][64];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = wave_id();
   const int waves = blockDim.x >> 6;
   const int32_t t = blockIdx.x;
   const int32_t n_begin = wave * per_wave;
@@ -463,66 +416,10 @@ __global__ __launch_bounds__(256) void reweight_kernel(
 // written to out + s * d_out * d_in.  64x64 tile per workgroup, 32x32 per wave.
 // bf16: g = hi + lo with hi = bf16(g), lo = bf16(g - hi); two MFMAs per block.
 
-__global__ __launch_bounds__(256) void outer_bf16_kernel(
-    const float* __restrict__ g, const uint16_t* __restrict__ X, int32_t T, int32_t d_in,
-    int32_t d_out, int32_t tiles_n, int32_t tokens_per_split, float* __restrict__ out) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int tiles = ((d_out + 63) / 64) * tiles_n;
-  const int split = blockIdx.x / tiles;
-  const int tile = blockIdx.x % tiles;
-  const int tile_m = tile / tiles_n, tile_n = tile % tiles_n;
-  const int m0 = tile_m * 64 + (wave >> 1) * 32;  // channels c
-  const int n0 = tile_n * 64 + (wave & 1) * 32;   // inputs i
-  const int r = lane & 15, kg = (lane >> 4) * 8;
-  const int t_begin = split * tokens_per_split;
-  const int t_end = min(T, t_begin + tokens_per_split);
-  f32x4_t acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  for (int t0 = t_begin; t0 < t_end; t0 += 32) {
-    u16x8_t ahi[2], alo[2], b[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = m0 + 16 * i + r;
-      const int col = n0 + 16 * i + r;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int t = t0 + kg + e;
-        const bool tin = t < t_end;
-        const float gv = (tin && c < d_out) ? g[(int64_t)t * d_out + c] : 0.f;
-        const uint16_t h = f32_to_bf16(gv);
-        ahi[i][e] = h;
-        alo[i][e] = f32_to_bf16(gv - bf16_to_f32(h));
-        b[i][e] = (tin && col < d_in) ? X[(int64_t)t * d_in + col] : (uint16_t)0;
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        acc[i][j] = mfma_bf16(ahi[i], b[j], acc[i][j]);
-        acc[i][j] = mfma_bf16(alo[i], b[j], acc[i][j]);
-      }
-  }
-  float* dst = out + (int64_t)split * d_out * d_in;
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int row = m0 + 16 * i + 4 * (lane >> 4) + e;
-        const int col = n0 + 16 * j + (lane & 15);
-        if (row < d_out && col < d_in) dst[(int64_t)row * d_in + col] = acc[i][j][e];
-      }
-}
-
 __global__ __launch_bounds__(256) void outer_f32_kernel(
     const float* __restrict__ g, const float* __restrict__ X, int32_t T, int32_t d_in,
     int32_t d_out, int32_t tiles_n, int32_t tokens_per_split, float* __restrict__ out) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = wave_id(), lane = threadIdx.x & 63;
   const int tiles = ((d_out + 63) / 64) * tiles_n;
   const int split = blockIdx.x / tiles;
   const int tile = blockIdx.x % tiles;
@@ -564,15 +461,30 @@ __global__ __launch_bounds__(256) void outer_f32_kernel(
       }
 }
 
-// Fixed-order sum of the split partial products.
+// Fixed-order sum of the split partial products; four values per thread
+// (n is padded to nothing: the tail is handled element-wise).
 __global__ __launch_bounds__(256) void split_sum_kernel(const float* __restrict__ part,
                                                         int32_t splits, int64_t n,
                                                         float* __restrict__ out) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t i = 4 * ((int64_t)blockIdx.x * blockDim.x + threadIdx.x);
   if (i >= n) return;
-  float s = part[i];
-  for (int k = 1; k < splits; ++k) s += part[(int64_t)k * n + i];
-  out[i] = s;
+  if (i + 4 <= n && (n % 4) == 0) {
+    float4 s = *(const float4*)(part + i);
+    for (int k = 1; k < splits; ++k) {
+      const float4 o = *(const float4*)(part + (int64_t)k * n + i);
+      s.x += o.x;
+      s.y += o.y;
+      s.z += o.z;
+      s.w += o.w;
+    }
+    *(float4*)(out + i) = s;
+  } else {
+    for (int64_t e = i; e < n && e < i + 4; ++e) {
+      float s = part[e];
+      for (int k = 1; k < splits; ++k) s += part[(int64_t)k * n + e];
+      out[e] = s;
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -591,31 +503,74 @@ __global__ __launch_bounds__(256) void split_sum_kernel(const float* __restrict_
 // Wave reduction of M values per lane: halving steps leave lane l with the
 // total of value (l / (64/M)); each total is then read into a scalar register.
 
+// DPP moves inside a row of 16 lanes (control codes of the DPP "quad_perm"
+// and "row_ror" forms): lane i reads lane i^1, i^2 or i^8 of its row.
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1;   // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;   // quad_perm [2,3,0,1]
+constexpr int kDppRor8 = 0x128;  // row_ror:8, i.e. lane i^8 within the row
+constexpr int kDppHalfMirror = 0x141;  // lane 7-i within each group of 8
+
+// One halving step of the transpose-reduce: lanes whose bit `MASK` is set
+// keep the upper H values, the others the lower H, and each adds its
+// partner's (lane ^ MASK) copy of the half it keeps.
+template <int H, int MASK>
+__device__ __forceinline__ void halve(float* v, int lane) {
+  const bool hi = (lane & MASK) != 0;
+#pragma unroll
+  for (int j = 0; j < H; ++j) {
+    const float send = hi ? v[j] : v[j + H];
+    const float keep = hi ? v[j + H] : v[j];
+    float recv;
+    if (MASK == 8)
+      recv = dpp_move<kDppRor8>(send);
+    else
+      recv = __shfl_xor(send, MASK);
+    v[j] = keep + recv;
+  }
+}
+
+// Sum of v over the lanes of each group of 2^b consecutive lanes that the
+// halving steps left holding the same value index (quads, then groups of 8).
+__device__ __forceinline__ float sum_quad(float x) {
+  x += dpp_move<kDppXor1>(x);
+  x += dpp_move<kDppXor2>(x);
+  return x;
+}
+
+// Wave reduction of M values per lane, fixed order; the M totals are
+// returned in scalar registers.  After the halving steps (masks 32, 16, 8 as
+// needed) lane l holds the partial total of value l / (64 / M); the rest is
+// summed inside rows with DPP.
 template <int M>
 __device__ __forceinline__ void wave_reduce_to_scalars(float (&v)[M], int lane, float (&tot)[M]) {
   static_assert(M == 2 || M == 4 || M == 8, "M");
-  int width = M;
-#pragma unroll
-  for (int mask = 32; mask >= 1; mask >>= 1) {
-    if (width > 1) {
-      const bool hi = (lane & mask) != 0;
-      const int h = width / 2;
-#pragma unroll
-      for (int j = 0; j < M / 2; ++j) {
-        if (j < h) {
-          const float send = hi ? v[j] : v[j + h];
-          const float keep = hi ? v[j + h] : v[j];
-          v[j] = keep + __shfl_xor(send, mask);
-        }
-      }
-      width = h;
-    } else {
-      v[0] += __shfl_xor(v[0], mask);
-    }
+  float x;
+  if constexpr (M == 8) {
+    halve<4, 32>(v, lane);
+    halve<2, 16>(v, lane);
+    halve<1, 8>(v, lane);
+    x = sum_quad(v[0]);
+    x += dpp_move<kDppHalfMirror>(x);  // groups of 8
+  } else if constexpr (M == 4) {
+    halve<2, 32>(v, lane);
+    halve<1, 16>(v, lane);
+    x = sum_quad(v[0]);
+    x += dpp_move<kDppHalfMirror>(x);
+    x += dpp_move<kDppRor8>(x);  // groups of 16
+  } else {
+    halve<1, 32>(v, lane);
+    x = sum_quad(v[0]);
+    x += dpp_move<kDppHalfMirror>(x);
+    x += dpp_move<kDppRor8>(x);
+    x += __shfl_xor(x, 16);  // groups of 32
   }
 #pragma unroll
   for (int k = 0; k < M; ++k)
-    tot[k] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v[0]), k * (64 / M)));
+    tot[k] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), k * (64 / M)));
 }
 
 template <int QPL, bool ANTI, bool FULL>
@@ -627,7 +582,7 @@ __global__ __launch_bounds__(256) void fused_g0_kernel(
   constexpr int M = 2 * NB;
   __shared__ float4 xch[4][64];
   __shared__ float rsum_x[4];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = wave_id();
   const int waves = blockDim.x >> 6;
   const int32_t t = blockIdx.x;
   const int32_t n_begin = wave * per_wave;
@@ -909,17 +864,30 @@ dust_status_t dust_estimate(const void* X, const void* W, const void* target, in
   const NoiseKey key = make_key(seed);
   const int32_t Ti = (int32_t)T, di = (int32_t)d_in, dout = (int32_t)d_out;
 
-  // 1. base GEMM -> delta
-  {
+  // 1. base GEMM -> delta (and X transposed, for the outer product)
+  uint16_t* xt_out = (uint16_t*)(ws + p.off_xt);
+  if (dtype == DUST_BF16) {
+    const bool vec = (d_in % 8 == 0) && ((uintptr_t)X % 16 == 0) && ((uintptr_t)W % 16 == 0);
+    const int bt = p.base_tile;
+    const int tiles_m = (int)ceil_div(T, bt), tiles_n = (int)ceil_div(d_out, bt);
+    const int per_xcd = (int)ceil_div((int64_t)tiles_m * tiles_n, 8);
+#define DUST_BASE_GEMM(BT, S, V)                                                                \
+  hipLaunchKernelGGL((gemm::nt_gemm_kernel<BT, BT, false, true, S, V>),                        \
+                     dim3((unsigned)(8 * per_xcd)), dim3(256), 0, s, (const uint16_t*)X,        \
+                     (const uint16_t*)nullptr, (const uint16_t*)W, (int64_t)d_in, (int64_t)d_in, \
+                     Ti, dout, (int64_t)d_in, tiles_m, tiles_n, 1, per_xcd, (int64_t)d_in,      \
+                     (const uint16_t*)target, delta, xt_out, p.T_pad)
+    if (bt == 128) {
+      if (vec) DUST_BASE_GEMM(128, 3, true); else DUST_BASE_GEMM(128, 3, false);
+    } else {
+      if (vec) DUST_BASE_GEMM(64, 4, true); else DUST_BASE_GEMM(64, 4, false);
+    }
+#undef DUST_BASE_GEMM
+  } else {
     const int tiles_n = (int)ceil_div(d_out, 64);
     const unsigned blocks = (unsigned)(ceil_div(T, 64) * tiles_n);
-    if (dtype == DUST_BF16)
-      hipLaunchKernelGGL(base_gemm_bf16_kernel, dim3(blocks), dim3(256), 0, s,
-                         (const uint16_t*)X, (const uint16_t*)W, (const uint16_t*)target, Ti, di,
-                         dout, tiles_n, delta);
-    else
-      hipLaunchKernelGGL(base_gemm_f32_kernel, dim3(blocks), dim3(256), 0, s, (const float*)X,
-                         (const float*)W, (const float*)target, Ti, di, dout, tiles_n, delta);
+    hipLaunchKernelGGL(base_gemm_f32_kernel, dim3(blocks), dim3(256), 0, s, (const float*)X,
+                       (const float*)W, (const float*)target, Ti, di, dout, tiles_n, delta);
   }
   const int qpl = fused_qpl(p.nq);
   const bool independent = (gamma == 0.0f || seq_len == 1);
@@ -966,19 +934,49 @@ dust_status_t dust_estimate(const void* X, const void* W, const void* target, in
   }
   // 6. outer product -> G_W
   {
-    const int tiles_n = (int)ceil_div(d_in, 64);
-    const int64_t tiles = ceil_div(d_out, 64) * tiles_n;
     float* dst = p.outer_split > 1 ? gpart : G_W;
-    const unsigned blocks = (unsigned)(tiles * p.outer_split);
-    if (dtype == DUST_BF16)
-      hipLaunchKernelGGL(outer_bf16_kernel, dim3(blocks), dim3(256), 0, s, (const float*)g_buf,
-                         (const uint16_t*)X, Ti, di, dout, tiles_n, (int32_t)p.outer_tokens, dst);
-    else
-      hipLaunchKernelGGL(outer_f32_kernel, dim3(blocks), dim3(256), 0, s, (const float*)g_buf,
-                         (const float*)X, Ti, di, dout, tiles_n, (int32_t)p.outer_tokens, dst);
+    if (dtype == DUST_BF16) {
+      // transposed operands with the token axis contiguous: g -> hi + lo, X
+      uint16_t* gth = (uint16_t*)(ws + p.off_gth);
+      uint16_t* gtl = (uint16_t*)(ws + p.off_gtl);
+      uint16_t* xt = (uint16_t*)(ws + p.off_xt);
+      const int64_t tp = p.T_pad;
+      {
+        const int tc = (int)ceil_div(d_out, 64);
+        const dim3 grid((unsigned)(ceil_div(tp, 64) * tc));
+        if (d_out % 8 == 0 && (uintptr_t)g_buf % 16 == 0)
+          hipLaunchKernelGGL((gemm::transpose_kernel<true, true>), grid, dim3(256), 0, s,
+                             (const void*)g_buf, Ti, dout, tp, tc, gth, gtl);
+        else
+          hipLaunchKernelGGL((gemm::transpose_kernel<true, false>), grid, dim3(256), 0, s,
+                             (const void*)g_buf, Ti, dout, tp, tc, gth, gtl);
+      }
+      const int bt = p.outer_tile;
+      const int tiles_m = (int)ceil_div(d_out, bt), tiles_n = (int)ceil_div(d_in, bt);
+      const int per_xcd = (int)ceil_div((int64_t)tiles_m * tiles_n * p.outer_split, 8);
+      const dim3 grid((unsigned)(8 * per_xcd));
+      if (bt == 128)
+        hipLaunchKernelGGL((gemm::nt_gemm_kernel<128, 128, true, false, 3, true>), grid,
+                           dim3(256), 0, s, (const uint16_t*)gth, (const uint16_t*)gtl,
+                           (const uint16_t*)xt, tp, tp, dout, di, tp, tiles_m, tiles_n,
+                           p.outer_split, per_xcd, (int64_t)p.outer_tokens,
+                           (const uint16_t*)nullptr, dst, (uint16_t*)nullptr, (int64_t)0);
+      else
+        hipLaunchKernelGGL((gemm::nt_gemm_kernel<64, 64, true, false, 4, true>), grid,
+                           dim3(256), 0, s, (const uint16_t*)gth, (const uint16_t*)gtl,
+                           (const uint16_t*)xt, tp, tp, dout, di, tp, tiles_m, tiles_n,
+                           p.outer_split, per_xcd, (int64_t)p.outer_tokens,
+                           (const uint16_t*)nullptr, dst, (uint16_t*)nullptr, (int64_t)0);
+    } else {
+      const int tiles_n = (int)ceil_div(d_in, 64);
+      const int64_t tiles = ceil_div(d_out, 64) * tiles_n;
+      hipLaunchKernelGGL(outer_f32_kernel, dim3((unsigned)(tiles * p.outer_split)), dim3(256), 0,
+                         s, (const float*)g_buf, (const float*)X, Ti, di, dout, tiles_n,
+                         (int32_t)p.outer_tokens, dst);
+    }
     if (p.outer_split > 1) {
       const int64_t n = d_out * d_in;
-      hipLaunchKernelGGL(split_sum_kernel, dim3(grid_for(n, 256)), dim3(256), 0, s,
+      hipLaunchKernelGGL(split_sum_kernel, dim3(grid_for(ceil_div(n, 4), 256)), dim3(256), 0, s,
                          (const float*)gpart, p.outer_split, n, G_W);
     }
   }
