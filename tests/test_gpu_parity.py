@@ -213,3 +213,98 @@ def test_gpu_cosine_law(dev, oracle_mod):
     pred = np.sqrt(32 / (32 + 512 + 1))
     print(f"cosine mean {cos.mean():.4f} predicted {pred:.4f}", flush=True)
     assert abs(cos.mean() - pred) < 0.01
+
+
+# --------------------------------------------------------------------------
+# Paths, options and the boundary's behaviour on the device
+
+
+def test_two_pass_fallback_at_gamma_zero(dev, oracle_mod, threads):
+    """d_out above the single-generation kernel's register budget (4096
+    channels) takes the two-pass path even for gamma = 0."""
+    T, d_in, d_out = 32, 16, 4100
+    inp = synth.random_inputs(T, d_in, d_out, "bf16", seed=77)
+    kw = dict(K=4, sigma=1e-2, gamma=0.0, seed=3, antithetic=True, seq_len=16)
+    got = gpu_estimate(inp, "bf16", dev, **kw)
+    ref = oracle_mod.estimate(inp["X"], inp["W"], inp["target"], threads=threads, **kw)
+    errs = {"g": rel(got["g"], ref["g"]), "G_W": rel(got["G_W"], ref["G"]),
+            "reward": rel(got["reward"], ref["reward"])}
+    report("  two-pass at gamma 0", errs)
+    for k, v in errs.items():
+        assert v <= TOL["bf16"], (k, v)
+
+
+@pytest.mark.parametrize("gamma", [0.0, 0.5])
+def test_optional_outputs_do_not_change_G(dev, gamma):
+    import torch
+    import token_activation_perturbation_amd as dust
+    w = synth.WORKLOADS["bf16_layer"]
+    inp = synth.make_inputs(w, T=1024)
+    Xd, Wd, td = to_dev(inp, "bf16", dev)
+    kw = dict(K=w.K, sigma=w.sigma, gamma=gamma, seed=9, antithetic=True, seq_len=w.seq_len)
+    bare = dust.dust_estimate(Xd, Wd, td, **kw)["G_W"].clone()
+    full = dust.dust_estimate(Xd, Wd, td, want_loss=True, want_rho=True, want_reward=True,
+                              want_g=True, **kw)
+    torch.cuda.synchronize(dev)
+    assert torch.equal(bare, full["G_W"])
+
+
+def test_runs_on_the_callers_stream(dev):
+    import torch
+    import token_activation_perturbation_amd as dust
+    w = synth.WORKLOADS["bf16_layer"]
+    inp = synth.make_inputs(w, T=512)
+    Xd, Wd, td = to_dev(inp, "bf16", dev)
+    kw = dict(K=w.K, sigma=w.sigma, gamma=0.3, seed=2, antithetic=True, seq_len=w.seq_len)
+    ref = dust.dust_estimate(Xd, Wd, td, **kw)["G_W"]
+    torch.cuda.synchronize(dev)
+    side = torch.cuda.Stream(device=dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        out = dust.dust_estimate(Xd, Wd, td, **kw)["G_W"]
+    side.synchronize()
+    assert torch.equal(ref, out)
+
+
+def test_misaligned_inputs_take_the_guarded_loads(dev, oracle_mod, threads):
+    """X and W as views starting one element into their storage: no 16-byte
+    alignment, so the GEMMs fall back to element-wise loads."""
+    import torch
+    import token_activation_perturbation_amd as dust
+    T, d_in, d_out = 96, 64, 48
+    inp = synth.random_inputs(T, d_in, d_out, "bf16", seed=5)
+    kw = dict(K=8, sigma=1e-2, gamma=0.0, seed=4, antithetic=False, seq_len=32)
+
+    def shifted(a):
+        flat = torch.zeros(a.size + 1, dtype=torch.bfloat16, device=dev)
+        flat[1:] = torch.from_numpy(a.ravel()).to(dev).to(torch.bfloat16)
+        return flat[1:].view(a.shape)
+
+    Xd, Wd = shifted(inp["X"]), shifted(inp["W"])
+    td = torch.from_numpy(inp["target"]).to(dev).to(torch.bfloat16)
+    assert Xd.data_ptr() % 16 != 0
+    out = dust.dust_estimate(Xd, Wd, td, **kw)
+    torch.cuda.synchronize(dev)
+    ref = oracle_mod.estimate(inp["X"], inp["W"], inp["target"], threads=threads, **kw)
+    assert rel(out["G_W"].cpu().numpy().astype(np.float64), ref["G"]) <= TOL["bf16"]
+
+
+def test_small_workspace_is_an_error(dev):
+    import torch
+    import token_activation_perturbation_amd as dust
+    X = torch.zeros(64, 16, dtype=torch.bfloat16, device=dev)
+    W = torch.zeros(8, 16, dtype=torch.bfloat16, device=dev)
+    t = torch.zeros(64, 8, dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(16, dtype=torch.uint8, device=dev)
+    with pytest.raises(dust.DustError) as e:
+        dust.dust_estimate(X, W, t, K=4, sigma=0.1, gamma=0.0, seed=0, antithetic=True,
+                           seq_len=64, workspace=ws)
+    assert e.value.status == 3
+
+
+def test_noise_fill_rejects_bad_ranges(dev):
+    import token_activation_perturbation_amd as dust
+    with pytest.raises(dust.DustError):
+        dust.dust_noise_fill(0, -1, 2, 0, 2, 8, device=dev)
+    with pytest.raises(dust.DustError):
+        dust.dust_noise_fill(0, 2**31 - 1, 2, 0, 2, 8, device=dev)

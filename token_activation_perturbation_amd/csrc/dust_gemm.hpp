@@ -26,8 +26,6 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef unsigned short u16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int BK = 32;       // contraction depth per LDS tile
-constexpr int LDK = BK + 8;  // padded LDS row, in bf16 elements (80 bytes)
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
   return __uint_as_float((uint32_t)b << 16);
@@ -45,8 +43,9 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 // branch; the out-of-range chunks are zeroed when written to LDS, so nothing
 // waits for a load before the store that needs it.  Otherwise element-wise
 // guarded loads.
-template <int ROWS, bool VEC>
+template <int ROWS, int BK, bool VEC>
 struct KMajorTile {
+  static constexpr int LDK = BK + 8;  // padded LDS row, in bf16 elements
   static constexpr int kChunks = ROWS * BK / 8 / 256;
   u16x8_t reg[kChunks];
   bool in_range[kChunks];
@@ -120,13 +119,14 @@ __device__ __forceinline__ TileWork map_tile(int tiles_m, int tiles_n, int split
 // out[split][m][n] = C.  When at != nullptr, the workgroups of n-tile 0 also
 // write A transposed, at[k][m] for m < ld_at (ld_at a multiple of 8; rows of
 // A past M are zeros), from the A tiles they already hold in LDS.
+// The split partials are summed by a separate fixed-order kernel.
 //
 // Software pipeline: S register stages hold the next S k-tiles in flight
 // from HBM.  Step kt multiplies tile kt from LDS buffer kt & 1, writes tile
 // kt+1 from its register stage into the other LDS buffer, refills that stage
 // with tile kt+1+S, and ends with one barrier.  The k loop is unrolled by S so
 // every stage index is a compile-time constant.
-template <int BM, int BN, bool DUAL, bool EPI_DELTA, int S, bool VEC>
+template <int BM, int BN, int BK, bool DUAL, bool EPI_DELTA, int S, bool VEC>
 __global__ __launch_bounds__(256) void nt_gemm_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ A2,
     const uint16_t* __restrict__ B, int64_t lda, int64_t ldb, int32_t M, int32_t N,
@@ -134,6 +134,7 @@ __global__ __launch_bounds__(256) void nt_gemm_kernel(
     int64_t k_per_split, const uint16_t* __restrict__ target, float* __restrict__ out,
     uint16_t* __restrict__ at, int64_t ld_at) {
   constexpr int WM = BM / 2, WN = BN / 2, TM = WM / 16, TN = WN / 16;
+  constexpr int LDK = BK + 8;
   constexpr int A_SZ = BM * LDK, B_SZ = BN * LDK;
   __shared__ __attribute__((aligned(16))) uint16_t lds_a[2][A_SZ];
   __shared__ __attribute__((aligned(16))) uint16_t lds_a2[DUAL ? 2 : 1][DUAL ? A_SZ : 8];
@@ -150,8 +151,8 @@ __global__ __launch_bounds__(256) void nt_gemm_kernel(
   const int64_t k_end = min(K, k_begin + k_per_split);
   const int nk = (int)((k_end - k_begin + BK - 1) / BK);
 
-  KMajorTile<BM, VEC> ta[S], ta2[DUAL ? S : 1];
-  KMajorTile<BN, VEC> tb[S];
+  KMajorTile<BM, BK, VEC> ta[S], ta2[DUAL ? S : 1];
+  KMajorTile<BN, BK, VEC> tb[S];
   auto load_stage = [&](int st, int kt) {
     const int64_t k0 = k_begin + (int64_t)kt * BK;
     ta[st].load(A, lda, M, k_end, tid, m0, k0);
@@ -170,6 +171,23 @@ __global__ __launch_bounds__(256) void nt_gemm_kernel(
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
+  // Small tiles: fetch the epilogue's target values now, so their latency
+  // hides behind the k loop (a few registers per lane).
+  constexpr bool kPrefetchTarget = EPI_DELTA && TM * TN <= 4;
+  uint16_t tgt[kPrefetchTarget ? TM : 1][kPrefetchTarget ? TN : 1][4];
+  if constexpr (kPrefetchTarget) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int64_t row = m0 + wm * WM + i * 16 + 4 * (lane >> 4) + e;
+          const int64_t col = n0 + wn * WN + j * 16 + (lane & 15);
+          tgt[i][j][e] = (row < M && col < N) ? target[row * N + col] : (uint16_t)0;
+        }
+  }
+
   // prologue: tiles 0..S-1 in flight; tile 0 to LDS; its stage refilled
 #pragma unroll
   for (int st = 0; st < S; ++st)
@@ -187,23 +205,27 @@ __global__ __launch_bounds__(256) void nt_gemm_kernel(
       const int kt = kt0 + s;
       if (kt < nk) {
         const int cur = kt & 1;
-        u16x8_t af[TM], af2[TM], bfr[TN];
 #pragma unroll
-        for (int i = 0; i < TM; ++i) {
-          af[i] = *(const u16x8_t*)(&lds_a[cur][(wm * WM + i * 16 + fr) * LDK + fk]);
-          if (DUAL)
-            af2[i] = *(const u16x8_t*)(&lds_a2[DUAL ? cur : 0][(wm * WM + i * 16 + fr) * LDK + fk]);
-        }
+        for (int ks = 0; ks < BK; ks += 32) {
+          u16x8_t af[TM], af2[TM], bfr[TN];
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
-          bfr[j] = *(const u16x8_t*)(&lds_b[cur][(wn * WN + j * 16 + fr) * LDK + fk]);
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-          for (int j = 0; j < TN; ++j) {
-            acc[i][j] = mfma16(af[i], bfr[j], acc[i][j]);
-            if (DUAL) acc[i][j] = mfma16(af2[i], bfr[j], acc[i][j]);
+          for (int i = 0; i < TM; ++i) {
+            af[i] = *(const u16x8_t*)(&lds_a[cur][(wm * WM + i * 16 + fr) * LDK + ks + fk]);
+            if (DUAL)
+              af2[i] = *(const u16x8_t*)(
+                  &lds_a2[DUAL ? cur : 0][(wm * WM + i * 16 + fr) * LDK + ks + fk]);
           }
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+            bfr[j] = *(const u16x8_t*)(&lds_b[cur][(wn * WN + j * 16 + fr) * LDK + ks + fk]);
+#pragma unroll
+          for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+              acc[i][j] = mfma16(af[i], bfr[j], acc[i][j]);
+              if (DUAL) acc[i][j] = mfma16(af2[i], bfr[j], acc[i][j]);
+            }
+        }
         if (at != nullptr && work.n_tile == 0) {
           // A tile [BM][BK] of buffer cur -> at rows k0..k0+BK-1, 8 m per chunk
           const int64_t k0 = k_begin + (int64_t)kt * BK;
@@ -240,7 +262,9 @@ __global__ __launch_bounds__(256) void nt_gemm_kernel(
         const int64_t col = n0 + wn * WN + j * 16 + (lane & 15);
         if (row < M && col < N) {
           const int64_t o = row * N + col;
-          if (EPI_DELTA)
+          if constexpr (kPrefetchTarget)
+            dst[o] = acc[i][j][e] - bf16_bits_to_f32(tgt[kPrefetchTarget ? i : 0][kPrefetchTarget ? j : 0][e]);
+          else if (EPI_DELTA)
             dst[o] = acc[i][j][e] - bf16_bits_to_f32(target[o]);
           else
             dst[o] = acc[i][j][e];

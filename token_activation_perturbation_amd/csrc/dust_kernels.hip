@@ -573,12 +573,18 @@ __device__ __forceinline__ void wave_reduce_to_scalars(float (&v)[M], int lane, 
     tot[k] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), k * (64 / M)));
 }
 
+// Noise vectors per register batch when a lane owns at most two quads
+// (-DDUST_FUSED_NB_SMALL=2, 4 or 8 at build time; 4 by default).
+#ifndef DUST_FUSED_NB_SMALL
+#define DUST_FUSED_NB_SMALL 4
+#endif
+
 template <int QPL, bool ANTI, bool FULL>
 __global__ __launch_bounds__(256) void fused_g0_kernel(
     const float* __restrict__ delta, int32_t T, int32_t d_out, int32_t nq, int32_t K,
     int32_t K_n, int32_t per_wave, float sigma, NoiseKey key, float* __restrict__ Pout,
     float* __restrict__ Qout, float* __restrict__ loss_clean, float* __restrict__ g) {
-  constexpr int NB = QPL <= 2 ? 4 : (QPL <= 4 ? 2 : 1);
+  constexpr int NB = QPL <= 2 ? DUST_FUSED_NB_SMALL : (QPL <= 4 ? 2 : 1);
   constexpr int M = 2 * NB;
   __shared__ float4 xch[4][64];
   __shared__ float rsum_x[4];
@@ -871,16 +877,16 @@ dust_status_t dust_estimate(const void* X, const void* W, const void* target, in
     const int bt = p.base_tile;
     const int tiles_m = (int)ceil_div(T, bt), tiles_n = (int)ceil_div(d_out, bt);
     const int per_xcd = (int)ceil_div((int64_t)tiles_m * tiles_n, 8);
-#define DUST_BASE_GEMM(BT, S, V)                                                                \
-  hipLaunchKernelGGL((gemm::nt_gemm_kernel<BT, BT, false, true, S, V>),                        \
+#define DUST_BASE_GEMM(BT, BKK, S, V)                                                              \
+  hipLaunchKernelGGL((gemm::nt_gemm_kernel<BT, BT, BKK, false, true, S, V>),                        \
                      dim3((unsigned)(8 * per_xcd)), dim3(256), 0, s, (const uint16_t*)X,        \
                      (const uint16_t*)nullptr, (const uint16_t*)W, (int64_t)d_in, (int64_t)d_in, \
                      Ti, dout, (int64_t)d_in, tiles_m, tiles_n, 1, per_xcd, (int64_t)d_in,      \
                      (const uint16_t*)target, delta, xt_out, p.T_pad)
     if (bt == 128) {
-      if (vec) DUST_BASE_GEMM(128, 3, true); else DUST_BASE_GEMM(128, 3, false);
+      if (vec) DUST_BASE_GEMM(128, 32, 3, true); else DUST_BASE_GEMM(128, 32, 3, false);
     } else {
-      if (vec) DUST_BASE_GEMM(64, 4, true); else DUST_BASE_GEMM(64, 4, false);
+      if (vec) DUST_BASE_GEMM(64, 64, 3, true); else DUST_BASE_GEMM(64, 64, 3, false);
     }
 #undef DUST_BASE_GEMM
   } else {
@@ -956,13 +962,13 @@ dust_status_t dust_estimate(const void* X, const void* W, const void* target, in
       const int per_xcd = (int)ceil_div((int64_t)tiles_m * tiles_n * p.outer_split, 8);
       const dim3 grid((unsigned)(8 * per_xcd));
       if (bt == 128)
-        hipLaunchKernelGGL((gemm::nt_gemm_kernel<128, 128, true, false, 3, true>), grid,
+        hipLaunchKernelGGL((gemm::nt_gemm_kernel<128, 128, 32, true, false, 3, true>), grid,
                            dim3(256), 0, s, (const uint16_t*)gth, (const uint16_t*)gtl,
                            (const uint16_t*)xt, tp, tp, dout, di, tp, tiles_m, tiles_n,
                            p.outer_split, per_xcd, (int64_t)p.outer_tokens,
                            (const uint16_t*)nullptr, dst, (uint16_t*)nullptr, (int64_t)0);
       else
-        hipLaunchKernelGGL((gemm::nt_gemm_kernel<64, 64, true, false, 4, true>), grid,
+        hipLaunchKernelGGL((gemm::nt_gemm_kernel<64, 64, 64, true, false, 3, true>), grid,
                            dim3(256), 0, s, (const uint16_t*)gth, (const uint16_t*)gtl,
                            (const uint16_t*)xt, tp, tp, dout, di, tp, tiles_m, tiles_n,
                            p.outer_split, per_xcd, (int64_t)p.outer_tokens,

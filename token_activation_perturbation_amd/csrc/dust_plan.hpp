@@ -12,10 +12,10 @@ namespace dust {
 
 // Noise vectors handled per unrolled batch inside the noise kernels.
 constexpr int kNoiseBatch = 16;
-// Waves the noise kernels are split into (256 CUs x 4 SIMDs x 8); a build
+// Waves the noise kernels are split into (256 CUs x 4 SIMDs x 16); a build
 // may override it with -DDUST_TARGET_WAVES=n.
 #ifndef DUST_TARGET_WAVES
-#define DUST_TARGET_WAVES 8192
+#define DUST_TARGET_WAVES 16384
 #endif
 constexpr int64_t kTargetWaves = DUST_TARGET_WAVES;
 // Workgroups the outer product's token split aims for (-DDUST_OUTER_WORKGROUPS).
@@ -42,7 +42,7 @@ struct Plan {
   // split of the token (contraction) axis
   int32_t outer_tile = 64;
   int32_t outer_split = 1;
-  int64_t outer_tokens = 0;  // tokens per split (multiple of 32)
+  int64_t outer_tokens = 0;  // tokens per split (multiple of 64)
 
   // bf16 path: tokens padded to a multiple of 8 for the transposed operands
   // of the outer product (gT_hi, gT_lo [d_out][T_pad], XT [d_in][T_pad])
@@ -114,7 +114,7 @@ inline bool make_plan(int64_t T, int64_t d_in, int64_t d_out, int32_t K,
   if (split > 64) split = 64;
   if (split < 1) split = 1;
   q.T_pad = ceil_div(T, 8) * 8;
-  q.outer_tokens = ceil_div(ceil_div(q.T_pad, split), 32) * 32;
+  q.outer_tokens = ceil_div(ceil_div(q.T_pad, split), 64) * 64;
   q.outer_split = (int32_t)ceil_div(q.T_pad, q.outer_tokens);
 
   size_t off = 0;
@@ -137,6 +137,7 @@ inline bool make_plan(int64_t T, int64_t d_in, int64_t d_out, int32_t K,
   q.off_gth = take(bf16 ? sizeof(uint16_t) * size_t(d_out) * size_t(q.T_pad) : 0);
   q.off_gtl = take(bf16 ? sizeof(uint16_t) * size_t(d_out) * size_t(q.T_pad) : 0);
   q.off_xt = take(bf16 ? sizeof(uint16_t) * size_t(d_in) * size_t(q.T_pad) : 0);
+
   q.total = off;
   *p = q;
   return true;
