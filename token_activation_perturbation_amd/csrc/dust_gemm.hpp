@@ -43,9 +43,14 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 // branch; the out-of-range chunks are zeroed when written to LDS, so nothing
 // waits for a load before the store that needs it.  Otherwise element-wise
 // guarded loads.
+// LDS row padding in bf16 elements (-DDUST_LDS_PAD=n at build time).
+#ifndef DUST_LDS_PAD
+#define DUST_LDS_PAD 16
+#endif
+
 template <int ROWS, int BK, bool VEC>
 struct KMajorTile {
-  static constexpr int LDK = BK + 8;  // padded LDS row, in bf16 elements
+  static constexpr int LDK = BK + DUST_LDS_PAD;  // padded LDS row, in bf16 elements
   static constexpr int kChunks = ROWS * BK / 8 / 256;
   u16x8_t reg[kChunks];
   bool in_range[kChunks];
@@ -134,7 +139,7 @@ __global__ __launch_bounds__(256) void nt_gemm_kernel(
     int64_t k_per_split, const uint16_t* __restrict__ target, float* __restrict__ out,
     uint16_t* __restrict__ at, int64_t ld_at) {
   constexpr int WM = BM / 2, WN = BN / 2, TM = WM / 16, TN = WN / 16;
-  constexpr int LDK = BK + 8;
+  constexpr int LDK = BK + DUST_LDS_PAD;
   constexpr int A_SZ = BM * LDK, B_SZ = BN * LDK;
   __shared__ __attribute__((aligned(16))) uint16_t lds_a[2][A_SZ];
   __shared__ __attribute__((aligned(16))) uint16_t lds_a2[DUAL ? 2 : 1][DUAL ? A_SZ : 8];
@@ -150,6 +155,7 @@ __global__ __launch_bounds__(256) void nt_gemm_kernel(
   const int64_t k_begin = (int64_t)split * k_per_split;
   const int64_t k_end = min(K, k_begin + k_per_split);
   const int nk = (int)((k_end - k_begin + BK - 1) / BK);
+  static_assert(S % 2 == 0, "the LDS double buffer is indexed by the stage parity");
 
   KMajorTile<BM, BK, VEC> ta[S], ta2[DUAL ? S : 1];
   KMajorTile<BN, BK, VEC> tb[S];
@@ -184,71 +190,71 @@ __global__ __launch_bounds__(256) void nt_gemm_kernel(
         for (int e = 0; e < 4; ++e) {
           const int64_t row = m0 + wm * WM + i * 16 + 4 * (lane >> 4) + e;
           const int64_t col = n0 + wn * WN + j * 16 + (lane & 15);
-          tgt[i][j][e] = (row < M && col < N) ? target[row * N + col] : (uint16_t)0;
+          // unconditional load from a clamped address (no branch, no wait);
+          // entries outside the matrix are never stored
+          const int64_t rr = row < M ? row : M - 1, cc = col < N ? col : N - 1;
+          tgt[i][j][e] = target[rr * N + cc];
         }
   }
 
-  // prologue: tiles 0..S-1 in flight; tile 0 to LDS; its stage refilled
+  // Branch-free pipeline: the tile count is padded to a multiple of S (the
+  // padding tiles lie past k_end, so they load from a clamped address and
+  // store zeros), so the compiler sees one straight-line body per S steps
+  // and keeps S tiles of loads in flight instead of waiting at branches.
+  const int nk_pad = ((nk + S - 1) / S) * S;
 #pragma unroll
-  for (int st = 0; st < S; ++st)
-    if (st < nk) load_stage(st, st);
-  if (nk > 0) {
-    store_stage(0, 0);
-    if (S < nk) load_stage(0, S);
-  }
+  for (int st = 0; st < S; ++st) load_stage(st, st);
+  store_stage(0, 0);
+  load_stage(0, S);
   __syncthreads();
 
   const int fr = lane & 15, fk = (lane >> 4) * 8;
-  for (int kt0 = 0; kt0 < nk; kt0 += S) {
+  for (int kt0 = 0; kt0 < nk_pad; kt0 += S) {
 #pragma unroll
     for (int s = 0; s < S; ++s) {
       const int kt = kt0 + s;
-      if (kt < nk) {
-        const int cur = kt & 1;
+      const int cur = s & 1;  // S is even, so kt & 1 == s & 1
 #pragma unroll
-        for (int ks = 0; ks < BK; ks += 32) {
-          u16x8_t af[TM], af2[TM], bfr[TN];
+      for (int ks = 0; ks < BK; ks += 32) {
+        u16x8_t af[TM], af2[TM], bfr[TN];
 #pragma unroll
-          for (int i = 0; i < TM; ++i) {
-            af[i] = *(const u16x8_t*)(&lds_a[cur][(wm * WM + i * 16 + fr) * LDK + ks + fk]);
-            if (DUAL)
-              af2[i] = *(const u16x8_t*)(
-                  &lds_a2[DUAL ? cur : 0][(wm * WM + i * 16 + fr) * LDK + ks + fk]);
+        for (int i = 0; i < TM; ++i) {
+          af[i] = *(const u16x8_t*)(&lds_a[cur][(wm * WM + i * 16 + fr) * LDK + ks + fk]);
+          if (DUAL)
+            af2[i] = *(const u16x8_t*)(
+                &lds_a2[DUAL ? cur : 0][(wm * WM + i * 16 + fr) * LDK + ks + fk]);
+        }
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          bfr[j] = *(const u16x8_t*)(&lds_b[cur][(wn * WN + j * 16 + fr) * LDK + ks + fk]);
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j) {
+            acc[i][j] = mfma16(af[i], bfr[j], acc[i][j]);
+            if (DUAL) acc[i][j] = mfma16(af2[i], bfr[j], acc[i][j]);
           }
-#pragma unroll
-          for (int j = 0; j < TN; ++j)
-            bfr[j] = *(const u16x8_t*)(&lds_b[cur][(wn * WN + j * 16 + fr) * LDK + ks + fk]);
-#pragma unroll
-          for (int i = 0; i < TM; ++i)
-#pragma unroll
-            for (int j = 0; j < TN; ++j) {
-              acc[i][j] = mfma16(af[i], bfr[j], acc[i][j]);
-              if (DUAL) acc[i][j] = mfma16(af2[i], bfr[j], acc[i][j]);
-            }
-        }
-        if (at != nullptr && work.n_tile == 0) {
-          // A tile [BM][BK] of buffer cur -> at rows k0..k0+BK-1, 8 m per chunk
-          const int64_t k0 = k_begin + (int64_t)kt * BK;
-#pragma unroll
-          for (int rep = 0; rep < BM * BK / 8 / 256; ++rep) {
-            const int c = tid + 256 * rep;
-            const int kk = c % BK, mseg = (c / BK) * 8;
-            const int64_t m = m0 + mseg, k = k0 + kk;
-            if (k < k_end && m < ld_at) {
-              u16x8_t v;
-#pragma unroll
-              for (int e = 0; e < 8; ++e) v[e] = lds_a[cur][(mseg + e) * LDK + kk];
-              *(u16x8_t*)(at + k * ld_at + m) = v;
-            }
-          }
-        }
-        const int nxt = (s + 1) % S;
-        if (kt + 1 < nk) {
-          store_stage(nxt, cur ^ 1);
-          if (kt + 1 + S < nk) load_stage(nxt, kt + 1 + S);
-        }
-        __syncthreads();
       }
+      if (at != nullptr && work.n_tile == 0 && kt < nk) {
+        // A tile [BM][BK] of buffer cur -> at rows k0..k0+BK-1, 8 m per chunk
+        const int64_t k0 = k_begin + (int64_t)kt * BK;
+#pragma unroll
+        for (int rep = 0; rep < BM * BK / 8 / 256; ++rep) {
+          const int c = tid + 256 * rep;
+          const int kk = c % BK, mseg = (c / BK) * 8;
+          const int64_t m = m0 + mseg, k = k0 + kk;
+          if (k < k_end && m < ld_at) {
+            u16x8_t v;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = lds_a[cur][(mseg + e) * LDK + kk];
+            *(u16x8_t*)(at + k * ld_at + m) = v;
+          }
+        }
+      }
+      const int nxt = (s + 1) % S;
+      store_stage(nxt, cur ^ 1);
+      load_stage(nxt, kt + 1 + S);
+      __syncthreads();
     }
   }
   float* dst = EPI_DELTA ? out : out + (int64_t)split * M * N;

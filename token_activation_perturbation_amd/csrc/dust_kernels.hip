@@ -884,9 +884,9 @@ dust_status_t dust_estimate(const void* X, const void* W, const void* target, in
                      Ti, dout, (int64_t)d_in, tiles_m, tiles_n, 1, per_xcd, (int64_t)d_in,      \
                      (const uint16_t*)target, delta, xt_out, p.T_pad)
     if (bt == 128) {
-      if (vec) DUST_BASE_GEMM(128, 32, 3, true); else DUST_BASE_GEMM(128, 32, 3, false);
+      if (vec) DUST_BASE_GEMM(128, 32, 2, true); else DUST_BASE_GEMM(128, 32, 2, false);
     } else {
-      if (vec) DUST_BASE_GEMM(64, 64, 3, true); else DUST_BASE_GEMM(64, 64, 3, false);
+      if (vec) DUST_BASE_GEMM(64, 64, 4, true); else DUST_BASE_GEMM(64, 64, 4, false);
     }
 #undef DUST_BASE_GEMM
   } else {
@@ -962,13 +962,13 @@ dust_status_t dust_estimate(const void* X, const void* W, const void* target, in
       const int per_xcd = (int)ceil_div((int64_t)tiles_m * tiles_n * p.outer_split, 8);
       const dim3 grid((unsigned)(8 * per_xcd));
       if (bt == 128)
-        hipLaunchKernelGGL((gemm::nt_gemm_kernel<128, 128, 32, true, false, 3, true>), grid,
+        hipLaunchKernelGGL((gemm::nt_gemm_kernel<128, 128, 32, true, false, 4, true>), grid,
                            dim3(256), 0, s, (const uint16_t*)gth, (const uint16_t*)gtl,
                            (const uint16_t*)xt, tp, tp, dout, di, tp, tiles_m, tiles_n,
                            p.outer_split, per_xcd, (int64_t)p.outer_tokens,
                            (const uint16_t*)nullptr, dst, (uint16_t*)nullptr, (int64_t)0);
       else
-        hipLaunchKernelGGL((gemm::nt_gemm_kernel<64, 64, 64, true, false, 3, true>), grid,
+        hipLaunchKernelGGL((gemm::nt_gemm_kernel<64, 64, 64, true, false, 4, true>), grid,
                            dim3(256), 0, s, (const uint16_t*)gth, (const uint16_t*)gtl,
                            (const uint16_t*)xt, tp, tp, dout, di, tp, tiles_m, tiles_n,
                            p.outer_split, per_xcd, (int64_t)p.outer_tokens,

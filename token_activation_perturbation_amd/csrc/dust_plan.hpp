@@ -20,7 +20,7 @@ constexpr int kNoiseBatch = 16;
 constexpr int64_t kTargetWaves = DUST_TARGET_WAVES;
 // Workgroups the outer product's token split aims for (-DDUST_OUTER_WORKGROUPS).
 #ifndef DUST_OUTER_WORKGROUPS
-#define DUST_OUTER_WORKGROUPS 512
+#define DUST_OUTER_WORKGROUPS 2048
 #endif
 
 struct Plan {
@@ -104,12 +104,13 @@ inline bool make_plan(int64_t T, int64_t d_in, int64_t d_out, int32_t K,
   q.fz_waves = (int32_t)ceil_div(q.K_n, q.fz_per_wave);
   // base GEMM: 128x128 tiles when that still gives >= 512 workgroups
   q.base_tile = (dtype == 1 && ceil_div(T, 128) * ceil_div(d_out, 128) >= 512) ? 128 : 64;
-  // outer product: 128x128 tiles when there are >= 128 of them; split the
-  // tokens until ~1024 workgroups, keeping >= 256 tokens per split
-  q.outer_tile = (dtype == 1 && ceil_div(d_out, 128) * ceil_div(d_in, 128) >= 128) ? 128 : 64;
-  const int64_t tiles = ceil_div(d_out, q.outer_tile) * ceil_div(d_in, q.outer_tile);
+  // outer product: 64x64 tiles; split the tokens until ~DUST_OUTER_WORKGROUPS
+  // workgroups, keeping >= 512 tokens per split (measured best on MI355X for
+  // 512-wide and 3072 x 768 layers)
+  q.outer_tile = 64;
+  const int64_t tiles = ceil_div(d_out, 64) * ceil_div(d_in, 64);
   int64_t split = ceil_div(DUST_OUTER_WORKGROUPS, tiles);
-  const int64_t max_split = ceil_div(T, 256);
+  const int64_t max_split = ceil_div(T, 512);
   if (split > max_split) split = max_split;
   if (split > 64) split = 64;
   if (split < 1) split = 1;
