@@ -118,6 +118,8 @@ SMALL = [
     (40, 1, 24, 8, 2, 1e-1, 0.7, True, "bf16"),          # one-token sequences, K = 2
     (1, 1, 1, 1, 2, 1e-2, 0.0, False, "f32"),            # the smallest problem
     (256, 128, 128, 1024, 64, 1e-2, 0.5, True, "bf16"),  # d_out spans 4 quad rounds
+    (140, 70, 40, 52, 8, 1e-2, 0.95, True, "bf16"),      # credit chunks 32 + 32 + 6
+    (99, 33, 16, 24, 4, 1e-2, 1.0, False, "f32"),        # chunks 32 + 1, suffix sums
 ]
 
 

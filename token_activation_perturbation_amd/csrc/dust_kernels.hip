@@ -11,9 +11,10 @@
 //                  reduction of the quadratic loss, computed at its own
 //                  scale instead of as a difference of two large losses) and
 //                  its mean over the K draws of the token
-//   reward_scan    c = rho - mean, r_t = c_t + gamma r_{t+1} per sequence,
-//                  and the per-(t, n) weight -1/(K sigma) (r^(2n) - r^(2n+1))
-//                  (antithetic) or -1/(K sigma) r^(n)
+//   credit         c = rho - mean, r_t = c_t + gamma r_{t+1} per sequence
+//                  (a chunked scan for gamma > 0), and the per-(t, n) weight
+//                  -1/(K sigma) (r^(2n) - r^(2n+1)) (antithetic) or
+//                  -1/(K sigma) r^(n)
 //   reweight       g_t = sum_n weight_(t,n) a_t^n; the noise regenerated inline
 //   outer          G_W = sum_t g_t x_t^T on MFMA (bf16 hi/lo split of g)
 #include <hip/hip_runtime.h>
@@ -309,43 +310,141 @@ __global__ __launch_bounds__(256) void token_stats_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Centring and the discounted credit.  One thread per (sequence, column),
-// column = draw, or pair of draws with antithetic noise; reverse scan over
-// the sequence's tokens.  With gamma == 0 every token is independent and the
-// grid covers (token, column) instead.
+// Centring and the discounted credit, r_t = c_t + gamma r_(t+1) with
+// c = rho - mean over draws, restarting at each sequence's end; the per-(t, n)
+// weight is -r / (K sigma), or -(r_+ - r_-) / (K sigma) for an antithetic
+// pair, whose two draws share noise n.
+//
+// Every token on its own (gamma == 0 or one-token sequences): one thread per
+// (token, column), column = draw, or pair of draws with antithetic noise.
 
-__global__ __launch_bounds__(256) void reward_scan_kernel(
-    const float* __restrict__ rho, const float* __restrict__ mean, int32_t T, int32_t seq_len,
-    int32_t K, int32_t K_n, int32_t antithetic, float sigma, float gamma, int32_t independent,
-    float* __restrict__ reward, float* __restrict__ wgt) {
+__device__ __forceinline__ void write_credit(int64_t t, int32_t col, int32_t K, int32_t K_n,
+                                             int32_t antithetic, float scale, float r0,
+                                             float r1, float* reward, float* wgt) {
+  if (antithetic) {
+    if (reward) {
+      reward[t * K + 2 * col] = r0;
+      reward[t * K + 2 * col + 1] = r1;
+    }
+    wgt[t * K_n + col] = scale * (r0 - r1);
+  } else {
+    if (reward) reward[t * K + col] = r0;
+    wgt[t * K_n + col] = scale * r0;
+  }
+}
+
+__global__ __launch_bounds__(256) void credit_token_kernel(
+    const float* __restrict__ rho, const float* __restrict__ mean, int32_t T, int32_t K,
+    int32_t K_n, int32_t antithetic, float sigma, float* __restrict__ reward,
+    float* __restrict__ wgt) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int32_t col = (int32_t)(idx % K_n);
-  const int64_t row = idx / K_n;  // sequence, or token when independent
-  const int64_t n_rows = independent ? (int64_t)T : (int64_t)(T / seq_len);
-  if (row >= n_rows) return;
+  const int64_t t = idx / K_n;
+  if (t >= T) return;
   const float scale = -1.0f / ((float)K * sigma);
-  const int64_t t_first = independent ? row : row * seq_len;
-  const int64_t t_last = independent ? row : t_first + seq_len - 1;
-  float r0 = 0.f, r1 = 0.f;
-  for (int64_t t = t_last; t >= t_first; --t) {
-    const float m = mean[t];
-    if (antithetic) {
-      const float c0 = rho[t * K + 2 * col] - m;
-      const float c1 = rho[t * K + 2 * col + 1] - m;
-      r0 = __builtin_fmaf(gamma, r0, c0);
-      r1 = __builtin_fmaf(gamma, r1, c1);
-      if (reward) {
-        reward[t * K + 2 * col] = r0;
-        reward[t * K + 2 * col + 1] = r1;
-      }
-      wgt[t * K_n + col] = scale * (r0 - r1);
-    } else {
-      const float c0 = rho[t * K + col] - m;
-      r0 = __builtin_fmaf(gamma, r0, c0);
-      if (reward) reward[t * K + col] = r0;
-      wgt[t * K_n + col] = scale * r0;
+  const float m = mean[t];
+  const int64_t c0 = antithetic ? 2 * col : col;
+  const float r0 = rho[t * K + c0] - m;
+  const float r1 = antithetic ? rho[t * K + c0 + 1] - m : 0.f;
+  write_credit(t, col, K, K_n, antithetic, scale, r0, r1, reward, wgt);
+}
+
+// Sequences of several tokens with gamma > 0: a chunked reverse scan, so the
+// serial part is short.  Sequences are cut into chunks of kScanChunk tokens
+// (the last one may be shorter).
+//   scan_local_kernel  one thread per (sequence, chunk, draw): the chunk's
+//                      own reverse scan, with nothing entering from its
+//                      right, r_loc; and r_loc at the chunk's first token,
+//                      head.
+//   scan_carry_kernel  one thread per (sequence, draw), last chunk to first:
+//                      the credit at the first token of chunk ch + 1, which
+//                      is head(ch + 1) + gamma^32 carry(ch + 1), replaces
+//                      head(ch) in place (the last chunk's carry is 0).
+//   scan_apply_kernel  one thread per (token, column):
+//                      r_t = r_loc_t + gamma^e carry(ch), e the distance from
+//                      t to the next chunk's first token.
+// The scan is associative, so this equals the token-by-token recurrence up
+// to fp32 rounding order.
+constexpr int kScanChunk = 32;
+
+__global__ __launch_bounds__(256) void scan_local_kernel(
+    const float* __restrict__ rho, const float* __restrict__ mean, int32_t T, int32_t seq_len,
+    int32_t K, int32_t n_chunks, float gamma, float* __restrict__ r_loc,
+    float* __restrict__ head) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int32_t col = (int32_t)(idx % K);
+  const int64_t rest = idx / K;
+  const int32_t chunk = (int32_t)(rest % n_chunks);
+  const int64_t sq = rest / n_chunks;
+  if (sq * seq_len >= T) return;
+  const int64_t t_first = sq * seq_len + (int64_t)chunk * kScanChunk;
+  const int32_t len = min(kScanChunk, seq_len - chunk * kScanChunk);
+  float c[kScanChunk];
+#pragma unroll
+  for (int k = 0; k < kScanChunk; ++k) {
+    const int64_t t = t_first + min(k, len - 1);  // clamped: loads stay in the chunk
+    c[k] = rho[t * K + col] - mean[t];
+  }
+  float r = 0.f;
+#pragma unroll
+  for (int k = kScanChunk - 1; k >= 0; --k) {
+    if (k < len) {
+      r = __builtin_fmaf(gamma, r, c[k]);
+      r_loc[(t_first + k) * K + col] = r;
     }
   }
+  head[(sq * n_chunks + chunk) * K + col] = r;
+}
+
+__global__ __launch_bounds__(256) void scan_carry_kernel(float* head_carry, int32_t n_seq,
+                                                         int32_t n_chunks, int32_t K,
+                                                         float gamma_chunk) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int32_t col = (int32_t)(idx % K);
+  const int64_t sq = idx / K;
+  if (sq >= n_seq) return;
+  float* base = head_carry + sq * n_chunks * (int64_t)K + col;
+  float cin = 0.f;
+  constexpr int G = 8;  // heads loaded ahead of the serial chain
+  for (int32_t hi = n_chunks; hi > 0; hi -= G) {
+    float h[G];
+#pragma unroll
+    for (int k = 0; k < G; ++k) {
+      const int32_t ch = max(hi - 1 - k, 0);
+      h[k] = base[(int64_t)ch * K];
+    }
+#pragma unroll
+    for (int k = 0; k < G; ++k) {
+      const int32_t ch = hi - 1 - k;
+      if (ch >= 0) {
+        base[(int64_t)ch * K] = cin;
+        cin = __builtin_fmaf(gamma_chunk, cin, h[k]);
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void scan_apply_kernel(
+    const float* r_loc, const float* __restrict__ carry, int32_t T, int32_t seq_len, int32_t K,
+    int32_t K_n, int32_t n_chunks, int32_t antithetic, float sigma, float gamma, float* reward,
+    float* __restrict__ wgt) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int32_t col = (int32_t)(idx % K_n);
+  const int64_t t = idx / K_n;
+  if (t >= T) return;
+  const int64_t sq = t / seq_len;
+  const int32_t pos = (int32_t)(t - sq * seq_len);
+  const int32_t ch = pos / kScanChunk;
+  const int32_t e = min((ch + 1) * kScanChunk, seq_len) - pos;  // 1 .. kScanChunk
+  float factor = 1.f;
+  for (int k = 0; k < e; ++k) factor *= gamma;
+  const int64_t cb = (sq * n_chunks + ch) * K;
+  const float scale = -1.0f / ((float)K * sigma);
+  const int64_t c0 = antithetic ? 2 * col : col;
+  const float r0 = __builtin_fmaf(factor, carry[cb + c0], r_loc[t * K + c0]);
+  const float r1 =
+      antithetic ? __builtin_fmaf(factor, carry[cb + c0 + 1], r_loc[t * K + c0 + 1]) : 0.f;
+  write_credit(t, col, K, K_n, antithetic, scale, r0, r1, reward, wgt);
 }
 
 // ---------------------------------------------------------------------------
@@ -912,9 +1011,9 @@ dust_status_t dust_estimate(const void* X, const void* W, const void* target, in
       hipLaunchKernelGGL(token_stats_kernel, dim3(grid_for(T, 4)), dim3(256), 0, s,
                          (const float*)Pbuf, (const float*)Qbuf, Ti, K, p.K_n, p.antithetic,
                          sigma, rho_buf, mean);
-      hipLaunchKernelGGL(reward_scan_kernel, dim3(grid_for(T * p.K_n, 256)), dim3(256), 0, s,
-                         (const float*)rho_buf, (const float*)mean, Ti, (int32_t)seq_len, K,
-                         p.K_n, p.antithetic, sigma, gamma, 1, reward, wgt);
+      hipLaunchKernelGGL(credit_token_kernel, dim3(grid_for(T * p.K_n, 256)), dim3(256), 0, s,
+                         (const float*)rho_buf, (const float*)mean, Ti, K, p.K_n, p.antithetic,
+                         sigma, reward, wgt);
     }
   } else {
     // 2. jitter + loss change
@@ -928,11 +1027,25 @@ dust_status_t dust_estimate(const void* X, const void* W, const void* target, in
                        (const float*)Pbuf, (const float*)Qbuf, Ti, K, p.K_n, p.antithetic, sigma,
                        rho_buf, mean);
     // 4. centring + discounted credit -> per-(t, n) weights
-    {
-      const int64_t rows = independent ? T : T / seq_len;
-      hipLaunchKernelGGL(reward_scan_kernel, dim3(grid_for(rows * p.K_n, 256)), dim3(256), 0, s,
-                         (const float*)rho_buf, (const float*)mean, Ti, (int32_t)seq_len, K,
-                         p.K_n, p.antithetic, sigma, gamma, independent ? 1 : 0, reward, wgt);
+    if (independent) {
+      hipLaunchKernelGGL(credit_token_kernel, dim3(grid_for(T * p.K_n, 256)), dim3(256), 0, s,
+                         (const float*)rho_buf, (const float*)mean, Ti, K, p.K_n, p.antithetic,
+                         sigma, reward, wgt);
+    } else {
+      const int64_t n_seq = T / seq_len;
+      const int32_t n_chunks = (int32_t)ceil_div(seq_len, kScanChunk);
+      float* r_loc = reward ? reward : (float*)(ws + p.off_rloc);
+      float* carry = (float*)(ws + p.off_carry);
+      float gamma_chunk = 1.f;
+      for (int k = 0; k < kScanChunk; ++k) gamma_chunk *= gamma;
+      hipLaunchKernelGGL(scan_local_kernel, dim3(grid_for(n_seq * n_chunks * K, 256)), dim3(256),
+                         0, s, (const float*)rho_buf, (const float*)mean, Ti, (int32_t)seq_len,
+                         K, n_chunks, gamma, r_loc, carry);
+      hipLaunchKernelGGL(scan_carry_kernel, dim3(grid_for(n_seq * K, 256)), dim3(256), 0, s,
+                         carry, (int32_t)n_seq, n_chunks, K, gamma_chunk);
+      hipLaunchKernelGGL(scan_apply_kernel, dim3(grid_for(T * p.K_n, 256)), dim3(256), 0, s,
+                         (const float*)r_loc, (const float*)carry, Ti, (int32_t)seq_len, K,
+                         p.K_n, n_chunks, p.antithetic, sigma, gamma, reward, wgt);
     }
     // 5. reweight -> g
     hipLaunchKernelGGL(reweight_kernel, dim3((unsigned)T), dim3(64 * p.rw_waves), 0, s,

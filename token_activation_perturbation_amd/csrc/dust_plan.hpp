@@ -51,7 +51,7 @@ struct Plan {
   // workspace byte offsets (each 256-byte aligned) and total
   size_t off_delta = 0, off_P = 0, off_Q = 0, off_rho = 0, off_mean = 0,
          off_wgt = 0, off_g = 0, off_gpart = 0, off_gth = 0, off_gtl = 0, off_xt = 0,
-         total = 0;
+         off_rloc = 0, off_carry = 0, total = 0;
 };
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -139,6 +139,12 @@ inline bool make_plan(int64_t T, int64_t d_in, int64_t d_out, int32_t K,
   q.off_gtl = take(bf16 ? sizeof(uint16_t) * size_t(d_out) * size_t(q.T_pad) : 0);
   q.off_xt = take(bf16 ? sizeof(uint16_t) * size_t(d_in) * size_t(q.T_pad) : 0);
 
+  // chunked credit scan (gamma > 0, sequences of >= 2 tokens): the chunks'
+  // own scans [T][K], and one head/carry per (sequence, 32-token chunk,
+  // draw); (T / seq_len) * ceil(seq_len / 32) <= T / 2 chunks for any
+  // seq_len >= 2
+  q.off_rloc = take(sizeof(float) * size_t(T) * size_t(K));
+  q.off_carry = take(sizeof(float) * size_t(ceil_div(T, 2)) * size_t(K));
   q.total = off;
   *p = q;
   return true;
