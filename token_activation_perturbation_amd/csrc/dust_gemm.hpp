@@ -1,19 +1,22 @@
-// dust_gemm.hpp -- LDS-tiled bf16 MFMA GEMM for the two dense contractions
-// of the estimator on gfx950, both in "NT" form C[m][n] = sum_k A[m][k] B[n][k]
-// with the contraction axis k contiguous in HBM:
-//   base   delta[t][c] = sum_k X[t][k] W[c][k] - target[t][c]
-//   outer  G[c][i] = sum_t gT[c][t] XT[i][t], gT = gT_hi + gT_lo (bf16 split
-//          of fp32 g, written by transpose_kernel), XT = X transposed.
+// dust_gemm.hpp -- LDS-tiled bf16 MFMA GEMMs for the two dense contractions
+// of the estimator on gfx950:
+//   base   delta[t][c] = sum_k X[t][k] W[c][k] - target[t][c]  ("NT": both
+//          operands contiguous along the contraction axis k)
+//   outer  G[c][i] = sum_t g[t][c] X[t][i]  ("TN": both operands contiguous
+//          along the output axes, the token axis t strided), g fp32 split
+//          into bf16 hi + lo on the way into LDS.
 //
 // A workgroup of 256 threads (4 waves in a 2x2 grid) computes a BM x BN tile;
 // each wave a (BM/2) x (BN/2) block of 16x16 MFMA tiles
 // (v_mfma_f32_16x16x32_bf16: lane l supplies row l % 16 of A and column
 // l % 16 of B with the 8 contraction values of group l / 16, and holds D rows
-// 4 (l / 16) + 0..3 of column l % 16).  Operand tiles are staged in LDS with a
-// padded row of BK + 8 bf16, so every fragment is one ds_read_b128.  LDS is
-// double buffered and several k-tiles are in flight from HBM in registers
-// (see nt_gemm_kernel), so each step needs a single barrier and the load
-// latency is hidden behind the MFMAs of the tiles before it.
+// 4 (l / 16) + 0..3 of column l % 16).  Both kernels stage operand tiles in
+// LDS "k-major" (a padded row of contraction values per output row or
+// column), so every MFMA fragment is one ds_read_b128; the TN kernel
+// transposes in registers before its LDS stores.  LDS is double buffered and
+// several k-tiles are in flight from HBM in registers, so each step needs a
+// single barrier and the load latency is hidden behind the MFMAs of the tiles
+// before it.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -118,243 +121,338 @@ __device__ __forceinline__ TileWork map_tile(int tiles_m, int tiles_n, int split
   return w;
 }
 
-// C = A B^T over k in [k_begin, k_end).  DUAL: A is the sum of two bf16
-// matrices (hi + lo), multiplied separately into the same accumulator.
-// EPI_DELTA: out[m][n] = C - target[m][n] (bf16 target), else
-// out[split][m][n] = C.  When at != nullptr, the workgroups of n-tile 0 also
-// write A transposed, at[k][m] for m < ld_at (ld_at a multiple of 8; rows of
-// A past M are zeros), from the A tiles they already hold in LDS.
-// The split partials are summed by a separate fixed-order kernel.
+// The MFMAs of one k-tile held in LDS: wave (wm, wn) multiplies rows
+// wm * 32 + [0, 32) of A with rows wn * 32 + [0, 32) of B.
+template <int BK, int LDK>
+__device__ __forceinline__ void mma_tile(const uint16_t* la, const uint16_t* lb, int wm, int wn,
+                                         int lane, f32x4_t (&acc)[2][2]) {
+  const int fr = lane & 15, fk = (lane >> 4) * 8;
+#pragma unroll
+  for (int ks = 0; ks < BK; ks += 32) {
+    u16x8_t af[2], bfr[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      af[i] = *(const u16x8_t*)(&la[(wm * 32 + i * 16 + fr) * LDK + ks + fk]);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      bfr[j] = *(const u16x8_t*)(&lb[(wn * 32 + j * 16 + fr) * LDK + ks + fk]);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[i][j] = mfma16(af[i], bfr[j], acc[i][j]);
+  }
+}
+
+// The same for the TN kernel's swizzled tiles: chunk c of row r at chunk
+// position c ^ ((r >> 4) & 3).  A fragment's 16 rows share r >> 4, so the
+// swizzle is one XOR per fragment.  A is hi + lo (two MFMAs per product).
+template <int BK, int LDK>
+__device__ __forceinline__ void mma_tile_swz(const uint16_t* la, const uint16_t* la2,
+                                             const uint16_t* lb, int wm, int wn, int lane,
+                                             f32x4_t (&acc)[2][2]) {
+  const int fr = lane & 15, fc = lane >> 4;
+#pragma unroll
+  for (int ks = 0; ks < BK; ks += 32) {
+    u16x8_t af[2], af2[2], bfr[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int r = wm * 32 + i * 16 + fr;
+      const int c = ((ks / 8 + fc) ^ ((r >> 4) & 3)) * 8;
+      af[i] = *(const u16x8_t*)(&la[r * LDK + c]);
+      af2[i] = *(const u16x8_t*)(&la2[r * LDK + c]);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int r = wn * 32 + j * 16 + fr;
+      const int c = ((ks / 8 + fc) ^ ((r >> 4) & 3)) * 8;
+      bfr[j] = *(const u16x8_t*)(&lb[r * LDK + c]);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        acc[i][j] = mfma16(af[i], bfr[j], acc[i][j]);
+        acc[i][j] = mfma16(af2[i], bfr[j], acc[i][j]);
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Base GEMM: delta[m][n] = sum_k A[m][k] B[n][k] - target[m][n] (target bf16,
+// delta fp32), A = X [M = T][K = d_in], B = W [N = d_out][K].  64 x 64 tiles,
+// BK = 64.
 //
 // Software pipeline: S register stages hold the next S k-tiles in flight
 // from HBM.  Step kt multiplies tile kt from LDS buffer kt & 1, writes tile
 // kt+1 from its register stage into the other LDS buffer, refills that stage
 // with tile kt+1+S, and ends with one barrier.  The k loop is unrolled by S so
 // every stage index is a compile-time constant.
-template <int BM, int BN, int BK, bool DUAL, bool EPI_DELTA, int S, bool VEC>
+template <int S, bool VEC>
 __global__ __launch_bounds__(256) void nt_gemm_kernel(
-    const uint16_t* __restrict__ A, const uint16_t* __restrict__ A2,
-    const uint16_t* __restrict__ B, int64_t lda, int64_t ldb, int32_t M, int32_t N,
-    int64_t K, int32_t tiles_m, int32_t tiles_n, int32_t splits, int32_t per_xcd,
-    int64_t k_per_split, const uint16_t* __restrict__ target, float* __restrict__ out,
-    uint16_t* __restrict__ at, int64_t ld_at) {
-  constexpr int WM = BM / 2, WN = BN / 2, TM = WM / 16, TN = WN / 16;
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, int64_t lda, int64_t ldb,
+    int32_t M, int32_t N, int64_t K, int32_t tiles_m, int32_t tiles_n, int32_t per_xcd,
+    const uint16_t* __restrict__ target, float* __restrict__ out) {
+  constexpr int BM = 64, BN = 64, BK = 64, WM = 32, WN = 32;
   constexpr int LDK = BK + DUST_LDS_PAD;
-  constexpr int A_SZ = BM * LDK, B_SZ = BN * LDK;
-  __shared__ __attribute__((aligned(16))) uint16_t lds_a[2][A_SZ];
-  __shared__ __attribute__((aligned(16))) uint16_t lds_a2[DUAL ? 2 : 1][DUAL ? A_SZ : 8];
-  __shared__ __attribute__((aligned(16))) uint16_t lds_b[2][B_SZ];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_a[2][BM * LDK];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_b[2][BN * LDK];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  const TileWork work = map_tile(tiles_m, tiles_n, splits, per_xcd);
+  const TileWork work = map_tile(tiles_m, tiles_n, 1, per_xcd);
   if (!work.valid) return;
-  const int split = work.split;
   const int64_t m0 = (int64_t)work.m_tile * BM;
   const int64_t n0 = (int64_t)work.n_tile * BN;
-  const int64_t k_begin = (int64_t)split * k_per_split;
-  const int64_t k_end = min(K, k_begin + k_per_split);
-  const int nk = (int)((k_end - k_begin + BK - 1) / BK);
+  const int nk = (int)((K + BK - 1) / BK);
   static_assert(S % 2 == 0, "the LDS double buffer is indexed by the stage parity");
 
-  KMajorTile<BM, BK, VEC> ta[S], ta2[DUAL ? S : 1];
+  KMajorTile<BM, BK, VEC> ta[S];
   KMajorTile<BN, BK, VEC> tb[S];
   auto load_stage = [&](int st, int kt) {
-    const int64_t k0 = k_begin + (int64_t)kt * BK;
-    ta[st].load(A, lda, M, k_end, tid, m0, k0);
-    if (DUAL) ta2[DUAL ? st : 0].load(A2, lda, M, k_end, tid, m0, k0);
-    tb[st].load(B, ldb, N, k_end, tid, n0, k0);
+    const int64_t k0 = (int64_t)kt * BK;
+    ta[st].load(A, lda, M, K, tid, m0, k0);
+    tb[st].load(B, ldb, N, K, tid, n0, k0);
   };
   auto store_stage = [&](int st, int buf) {
     ta[st].store(lds_a[buf], tid);
-    if (DUAL) ta2[DUAL ? st : 0].store(lds_a2[DUAL ? buf : 0], tid);
     tb[st].store(lds_b[buf], tid);
   };
 
-  f32x4_t acc[TM][TN];
+  f32x4_t acc[2][2];
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // Small tiles: fetch the epilogue's target values now, so their latency
-  // hides behind the k loop (a few registers per lane).
-  constexpr bool kPrefetchTarget = EPI_DELTA && TM * TN <= 4;
-  uint16_t tgt[kPrefetchTarget ? TM : 1][kPrefetchTarget ? TN : 1][4];
-  if constexpr (kPrefetchTarget) {
+  // fetch the epilogue's target values now, so their latency hides behind
+  // the k loop: unconditional loads from a clamped address (no branch, no
+  // wait); entries outside the matrix are never stored
+  uint16_t tgt[2][2][4];
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int64_t row = m0 + wm * WM + i * 16 + 4 * (lane >> 4) + e;
-          const int64_t col = n0 + wn * WN + j * 16 + (lane & 15);
-          // unconditional load from a clamped address (no branch, no wait);
-          // entries outside the matrix are never stored
-          const int64_t rr = row < M ? row : M - 1, cc = col < N ? col : N - 1;
-          tgt[i][j][e] = target[rr * N + cc];
-        }
-  }
+      for (int e = 0; e < 4; ++e) {
+        const int64_t row = m0 + wm * WM + i * 16 + 4 * (lane >> 4) + e;
+        const int64_t col = n0 + wn * WN + j * 16 + (lane & 15);
+        const int64_t rr = row < M ? row : M - 1, cc = col < N ? col : N - 1;
+        tgt[i][j][e] = target[rr * N + cc];
+      }
 
   // Branch-free pipeline: the tile count is padded to a multiple of S (the
-  // padding tiles lie past k_end, so they load from a clamped address and
-  // store zeros), so the compiler sees one straight-line body per S steps
-  // and keeps S tiles of loads in flight instead of waiting at branches.
+  // padding tiles lie past K, so they load from a clamped address and store
+  // zeros), so the compiler sees one straight-line body per S steps and keeps
+  // S tiles of loads in flight instead of waiting at branches.
   const int nk_pad = ((nk + S - 1) / S) * S;
 #pragma unroll
   for (int st = 0; st < S; ++st) load_stage(st, st);
   store_stage(0, 0);
   load_stage(0, S);
   __syncthreads();
-
-  const int fr = lane & 15, fk = (lane >> 4) * 8;
   for (int kt0 = 0; kt0 < nk_pad; kt0 += S) {
 #pragma unroll
     for (int s = 0; s < S; ++s) {
       const int kt = kt0 + s;
       const int cur = s & 1;  // S is even, so kt & 1 == s & 1
-#pragma unroll
-      for (int ks = 0; ks < BK; ks += 32) {
-        u16x8_t af[TM], af2[TM], bfr[TN];
-#pragma unroll
-        for (int i = 0; i < TM; ++i) {
-          af[i] = *(const u16x8_t*)(&lds_a[cur][(wm * WM + i * 16 + fr) * LDK + ks + fk]);
-          if (DUAL)
-            af2[i] = *(const u16x8_t*)(
-                &lds_a2[DUAL ? cur : 0][(wm * WM + i * 16 + fr) * LDK + ks + fk]);
-        }
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          bfr[j] = *(const u16x8_t*)(&lds_b[cur][(wn * WN + j * 16 + fr) * LDK + ks + fk]);
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-          for (int j = 0; j < TN; ++j) {
-            acc[i][j] = mfma16(af[i], bfr[j], acc[i][j]);
-            if (DUAL) acc[i][j] = mfma16(af2[i], bfr[j], acc[i][j]);
-          }
-      }
-      if (at != nullptr && work.n_tile == 0 && kt < nk) {
-        // A tile [BM][BK] of buffer cur -> at rows k0..k0+BK-1, 8 m per chunk
-        const int64_t k0 = k_begin + (int64_t)kt * BK;
-#pragma unroll
-        for (int rep = 0; rep < BM * BK / 8 / 256; ++rep) {
-          const int c = tid + 256 * rep;
-          const int kk = c % BK, mseg = (c / BK) * 8;
-          const int64_t m = m0 + mseg, k = k0 + kk;
-          if (k < k_end && m < ld_at) {
-            u16x8_t v;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = lds_a[cur][(mseg + e) * LDK + kk];
-            *(u16x8_t*)(at + k * ld_at + m) = v;
-          }
-        }
-      }
+      mma_tile<BK, LDK>(lds_a[cur], lds_b[cur], wm, wn, lane, acc);
       const int nxt = (s + 1) % S;
       store_stage(nxt, cur ^ 1);
       load_stage(nxt, kt + 1 + S);
       __syncthreads();
+      // keep each step's register work in its step: the scheduler would
+      // otherwise hoist later stages' masking above their loads' arrival
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
-  float* dst = EPI_DELTA ? out : out + (int64_t)split * M * N;
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < TN; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int64_t row = m0 + wm * WM + i * 16 + 4 * (lane >> 4) + e;
         const int64_t col = n0 + wn * WN + j * 16 + (lane & 15);
-        if (row < M && col < N) {
-          const int64_t o = row * N + col;
-          if constexpr (kPrefetchTarget)
-            dst[o] = acc[i][j][e] - bf16_bits_to_f32(tgt[kPrefetchTarget ? i : 0][kPrefetchTarget ? j : 0][e]);
-          else if (EPI_DELTA)
-            dst[o] = acc[i][j][e] - bf16_bits_to_f32(target[o]);
-          else
-            dst[o] = acc[i][j][e];
-        }
+        if (row < M && col < N)
+          out[row * N + col] = acc[i][j][e] - bf16_bits_to_f32(tgt[i][j][e]);
       }
 }
 
 // ---------------------------------------------------------------------------
-// Transposes for the outer product, 64x64 tiles through LDS, 16-byte
-// accesses on both sides.  src [rows][cols] -> dst [cols][ld_dst] with
-// ld_dst >= rows (a multiple of 8); padding entries rows..ld_dst-1 are
-// written as zeros.
-//   SPLIT: src fp32, dst_hi = bf16(src), dst_lo = bf16(src - hi)
-//   else : src bf16, dst_hi = src
-// VEC: cols a multiple of 8 and src 16-byte aligned (vector loads).
-// grid = ceil(ld_dst / 64) * ceil(cols / 64).
+// Outer product over a token range: out[m][n] = sum_t g[t][m] X[t][n] for t in
+// split's range [split * t_per_split, min(T, (split + 1) * t_per_split)),
+// g fp32 [T][M] (M = d_out), X bf16 [T][N] (N = d_in); out is G itself with
+// one split, else the split's own [M][N] partial (summed afterwards by a
+// fixed-order kernel).  64 x 64 tiles, BK = 64 tokens.
+//
+// Both operands are contiguous along the output axes, so the loaders keep
+// lanes along a token row and transpose in registers: thread (cq, tq) =
+// (tid % 16, tid / 16) holds channels 4 cq .. 4 cq + 3 of tokens
+// 4 tq .. 4 tq + 3 of a tile, fetched as four 16-byte (g) and four 8-byte (X)
+// loads, one per token; it then writes, per channel, the 4 tokens as one
+// 8-byte piece of that channel's k-major LDS row (g split into bf16
+// hi = rn(v) and lo = rn(v - hi) on the way, by v_cvt_pk_bf16_f32).
+// LDS rows are 72 bf16 (144 bytes), and the 16-byte chunk c of row r sits at
+// chunk position c ^ ((r >> 4) & 3): the 16 lanes of a store then hit 16
+// distinct bank pairs, and the 16 rows of an MFMA fragment read (same
+// r >> 4) 16 distinct bank quads.
+//
+// Addressing: a uniform tile base (the tile's first token, clamped to T - 1)
+// plus a 32-bit lane offset, min(row offset, last valid row) + column offset,
+// so rows past T re-read row T - 1 and columns past the edge re-read the last
+// 4 columns; tokens outside the split are zeroed at the LDS store.  VEC: M and
+// N multiples of 4, g 16-byte and X 8-byte aligned (else element-wise loads
+// with the same clamping).  M, N < 2^22 keep the lane offsets in 32 bits.
+// Pipeline as in nt_gemm_kernel.
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
-template <bool SPLIT, bool VEC>
-__global__ __launch_bounds__(256) void transpose_kernel(const void* __restrict__ src,
-                                                        int32_t rows, int32_t cols,
-                                                        int64_t ld_dst, int32_t tiles_c,
-                                                        uint16_t* __restrict__ dst_hi,
-                                                        uint16_t* __restrict__ dst_lo) {
-  __shared__ float tile[64][65];
-  const int tid = threadIdx.x;
-  const int tr = blockIdx.x / tiles_c, tc = blockIdx.x % tiles_c;
-  const int64_t r0 = (int64_t)tr * 64, c0 = (int64_t)tc * 64;
-  // load: thread -> 8 consecutive columns of rows (tid / 8) + 32 j
-  {
-    const int cc = (tid % 8) * 8;
+__device__ __forceinline__ void split_pair(float a, float b, uint32_t& hi, uint32_t& lo) {
+  const f32x2_t v = {a, b};
+  hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+  const f32x2_t h = {__uint_as_float(hi << 16), __uint_as_float(hi & 0xFFFF0000u)};
+  lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(v - h, bf16x2_t));
+}
+
+template <int S, bool VEC>
+__global__ __launch_bounds__(256) void tn_outer_kernel(
+    const float* __restrict__ g, const uint16_t* __restrict__ X, int32_t T, int32_t M,
+    int32_t N, int32_t tiles_m, int32_t tiles_n, int32_t splits, int32_t per_xcd,
+    int64_t t_per_split, float* __restrict__ out) {
+  constexpr int BM = 64, BN = 64, BK = 64;
+  constexpr int LDK = BK + 8;
+  __shared__ __attribute__((aligned(16))) uint16_t lds_ah[2][BM * LDK];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_al[2][BM * LDK];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_b[2][BN * LDK];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const TileWork work = map_tile(tiles_m, tiles_n, splits, per_xcd);
+  if (!work.valid) return;
+  const int64_t m0 = (int64_t)work.m_tile * BM;
+  const int64_t n0 = (int64_t)work.n_tile * BN;
+  const int64_t t_begin = (int64_t)work.split * t_per_split;
+  const int64_t t_end = min((int64_t)T, t_begin + t_per_split);
+  const int nk = (int)((t_end - t_begin + BK - 1) / BK);
+  static_assert(S % 2 == 0, "the LDS double buffer is indexed by the stage parity");
+
+  const int cq = tid & 15, tq = tid >> 4;
+  // VEC lane offsets (bytes): columns clamped to the last 4, rows of the tile
+  const int64_t am = m0 + 4 * cq, bn = n0 + 4 * cq;
+  const uint32_t a_col = (uint32_t)((am < M ? am : M - 4) * 4);
+  const uint32_t b_col = (uint32_t)((bn < N ? bn : N - 4) * 2);
+  const uint32_t a_row = (uint32_t)(4 * tq) * (uint32_t)M * 4u;
+  const uint32_t b_row = (uint32_t)(4 * tq) * (uint32_t)N * 2u;
+
+  float4 ra[S][4];
+  uint2 rb[S][4];
+  auto load_stage = [&](int st, int kt) {
+    const int64_t tb = t_begin + (int64_t)kt * BK;
+    const int64_t tbc = tb < T ? tb : (int64_t)T - 1;   // uniform
+    const int64_t rows_left = (int64_t)T - 1 - tbc;      // valid rows after the first
+    const uint32_t last = (uint32_t)(rows_left < 63 ? rows_left : 63);
+    if (VEC) {
+      const char* abase = (const char*)(g + tbc * M);
+      const char* bbase = (const char*)(X + tbc * N);
+      const uint32_t a_lim = last * (uint32_t)M * 4u, b_lim = last * (uint32_t)N * 2u;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int rr = tid / 8 + 32 * j;
-      const int64_t r = r0 + rr, c = c0 + cc;
-      float v[8];
-      if (VEC && r < rows && c + 8 <= cols) {
-        if (SPLIT) {
-          const float4 a = *(const float4*)((const float*)src + r * cols + c);
-          const float4 b = *(const float4*)((const float*)src + r * cols + c + 4);
-          v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-          v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-        } else {
-          const u16x8_t a = *(const u16x8_t*)((const uint16_t*)src + r * cols + c);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] = bf16_bits_to_f32(a[e]);
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          v[e] = 0.f;
-          if (r < rows && c + e < cols)
-            v[e] = SPLIT ? ((const float*)src)[r * cols + c + e]
-                         : bf16_bits_to_f32(((const uint16_t*)src)[r * cols + c + e]);
-        }
+      for (int r = 0; r < 4; ++r) {
+        const uint32_t ao = a_row + (uint32_t)r * (uint32_t)M * 4u;
+        const uint32_t bo = b_row + (uint32_t)r * (uint32_t)N * 2u;
+        ra[st][r] = *(const float4*)(abase + ((ao < a_lim ? ao : a_lim) + a_col));
+        rb[st][r] = *(const uint2*)(bbase + ((bo < b_lim ? bo : b_lim) + b_col));
       }
+    } else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) tile[rr][cc + e] = v[e];
+      for (int r = 0; r < 4; ++r) {
+        int64_t t = tbc + 4 * tq + r;
+        t = t < T ? t : (int64_t)T - 1;
+        float av[4];
+        uint32_t bv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int64_t ca = am + e < M ? am + e : (int64_t)M - 1;
+          const int64_t cb = bn + e < N ? bn + e : (int64_t)N - 1;
+          av[e] = g[t * M + ca];
+          bv[e] = X[t * N + cb];
+        }
+        ra[st][r] = make_float4(av[0], av[1], av[2], av[3]);
+        rb[st][r] = make_uint2(bv[0] | (bv[1] << 16), bv[2] | (bv[3] << 16));
+      }
     }
-  }
+  };
+  auto store_stage = [&](int st, int buf, int kt) {
+    const int64_t tb = t_begin + (int64_t)kt * BK;
+    const int64_t left = t_end - tb;                     // uniform
+    const int n_ok = (int)(left < 0 ? 0 : (left > 64 ? 64 : left));
+    bool ok[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) ok[r] = 4 * tq + r < n_ok;
+    const int half = (tq & 1) * 4, chunk = tq >> 1;
+#pragma unroll
+    for (int ci = 0; ci < 4; ++ci) {
+      const int row = 4 * cq + ci;
+      const int off = row * LDK + ((chunk ^ ((row >> 4) & 3)) * 8) + half;
+      float v[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float4 q = ra[st][r];
+        const float x = ci == 0 ? q.x : ci == 1 ? q.y : ci == 2 ? q.z : q.w;
+        v[r] = ok[r] ? x : 0.f;
+      }
+      uint32_t h01, l01, h23, l23;
+      split_pair(v[0], v[1], h01, l01);
+      split_pair(v[2], v[3], h23, l23);
+      *(uint2*)(&lds_ah[buf][off]) = make_uint2(h01, h23);
+      *(uint2*)(&lds_al[buf][off]) = make_uint2(l01, l23);
+      uint32_t w[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const uint32_t d = (ci >> 1) ? rb[st][r].y : rb[st][r].x;
+        w[r] = ok[r] ? ((ci & 1) ? (d >> 16) : (d & 0xFFFFu)) : 0u;
+      }
+      *(uint2*)(&lds_b[buf][off]) = make_uint2(w[0] | (w[1] << 16), w[2] | (w[3] << 16));
+    }
+  };
+
+  f32x4_t acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int nk_pad = ((nk + S - 1) / S) * S;
+#pragma unroll
+  for (int st = 0; st < S; ++st) load_stage(st, st);
+  store_stage(0, 0, 0);
+  load_stage(0, S);
   __syncthreads();
-  // store: thread -> output row c = tid / 4 (a source column), 16 source
-  // rows starting at (tid % 4) * 16, as two 8-value chunks
-  {
-    const int cc = tid / 4, rseg = (tid % 4) * 16;
-    const int64_t c = c0 + cc;
-    if (c < cols) {
+  for (int kt0 = 0; kt0 < nk_pad; kt0 += S) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int64_t r = r0 + rseg + 8 * h;  // multiple of 8
-        if (r < ld_dst) {
-          u16x8_t hv, lv;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float v = tile[rseg + 8 * h + e][cc];  // zero where r >= rows
-            const uint16_t hb = f32_to_bf16_rne(v);
-            hv[e] = hb;
-            lv[e] = f32_to_bf16_rne(v - bf16_bits_to_f32(hb));
-          }
-          *(u16x8_t*)(dst_hi + c * ld_dst + r) = hv;
-          if (SPLIT) *(u16x8_t*)(dst_lo + c * ld_dst + r) = lv;
-        }
-      }
+    for (int s = 0; s < S; ++s) {
+      const int kt = kt0 + s;
+      const int cur = s & 1;
+      mma_tile_swz<BK, LDK>(lds_ah[cur], lds_al[cur], lds_b[cur], wm, wn, lane, acc);
+      const int nxt = (s + 1) % S;
+      store_stage(nxt, cur ^ 1, kt + 1);
+      load_stage(nxt, kt + 1 + S);
+      __syncthreads();
+      // keep each step's register work in its step: the scheduler would
+      // otherwise hoist later stages' unpacking above their loads' arrival
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
+  float* dst = splits > 1 ? out + (int64_t)work.split * M * N : out;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t row = m0 + wm * 32 + i * 16 + 4 * (lane >> 4) + e;
+        const int64_t col = n0 + wn * 32 + j * 16 + (lane & 15);
+        if (row < M && col < N) dst[row * N + col] = acc[i][j][e];
+      }
 }
 
 }  // namespace gemm

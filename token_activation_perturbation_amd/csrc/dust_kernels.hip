@@ -16,7 +16,8 @@
 //                  -1/(K sigma) (r^(2n) - r^(2n+1)) (antithetic) or
 //                  -1/(K sigma) r^(n)
 //   reweight       g_t = sum_n weight_(t,n) a_t^n; the noise regenerated inline
-//   outer          G_W = sum_t g_t x_t^T on MFMA (bf16 hi/lo split of g)
+//   outer          G_W = sum_t g_t x_t^T on MFMA (bf16 hi/lo split of g),
+//                  split over tokens, partials summed in a fixed order
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -969,25 +970,22 @@ dust_status_t dust_estimate(const void* X, const void* W, const void* target, in
   const NoiseKey key = make_key(seed);
   const int32_t Ti = (int32_t)T, di = (int32_t)d_in, dout = (int32_t)d_out;
 
-  // 1. base GEMM -> delta (and X transposed, for the outer product)
-  uint16_t* xt_out = (uint16_t*)(ws + p.off_xt);
+  // 1. base GEMM -> delta
   if (dtype == DUST_BF16) {
     const bool vec = (d_in % 8 == 0) && ((uintptr_t)X % 16 == 0) && ((uintptr_t)W % 16 == 0);
-    const int bt = p.base_tile;
-    const int tiles_m = (int)ceil_div(T, bt), tiles_n = (int)ceil_div(d_out, bt);
+    const int tiles_m = (int)ceil_div(T, 64), tiles_n = (int)ceil_div(d_out, 64);
     const int per_xcd = (int)ceil_div((int64_t)tiles_m * tiles_n, 8);
-#define DUST_BASE_GEMM(BT, BKK, S, V)                                                              \
-  hipLaunchKernelGGL((gemm::nt_gemm_kernel<BT, BT, BKK, false, true, S, V>),                        \
-                     dim3((unsigned)(8 * per_xcd)), dim3(256), 0, s, (const uint16_t*)X,        \
-                     (const uint16_t*)nullptr, (const uint16_t*)W, (int64_t)d_in, (int64_t)d_in, \
-                     Ti, dout, (int64_t)d_in, tiles_m, tiles_n, 1, per_xcd, (int64_t)d_in,      \
-                     (const uint16_t*)target, delta, xt_out, p.T_pad)
-    if (bt == 128) {
-      if (vec) DUST_BASE_GEMM(128, 32, 2, true); else DUST_BASE_GEMM(128, 32, 2, false);
-    } else {
-      if (vec) DUST_BASE_GEMM(64, 64, 4, true); else DUST_BASE_GEMM(64, 64, 4, false);
-    }
-#undef DUST_BASE_GEMM
+    const dim3 grid((unsigned)(8 * per_xcd));
+    if (vec)
+      hipLaunchKernelGGL((gemm::nt_gemm_kernel<4, true>), grid, dim3(256), 0, s,
+                         (const uint16_t*)X, (const uint16_t*)W, (int64_t)d_in, (int64_t)d_in,
+                         Ti, dout, (int64_t)d_in, tiles_m, tiles_n, per_xcd,
+                         (const uint16_t*)target, delta);
+    else
+      hipLaunchKernelGGL((gemm::nt_gemm_kernel<4, false>), grid, dim3(256), 0, s,
+                         (const uint16_t*)X, (const uint16_t*)W, (int64_t)d_in, (int64_t)d_in,
+                         Ti, dout, (int64_t)d_in, tiles_m, tiles_n, per_xcd,
+                         (const uint16_t*)target, delta);
   } else {
     const int tiles_n = (int)ceil_div(d_out, 64);
     const unsigned blocks = (unsigned)(ceil_div(T, 64) * tiles_n);
@@ -1055,37 +1053,19 @@ dust_status_t dust_estimate(const void* X, const void* W, const void* target, in
   {
     float* dst = p.outer_split > 1 ? gpart : G_W;
     if (dtype == DUST_BF16) {
-      // transposed operands with the token axis contiguous: g -> hi + lo, X
-      uint16_t* gth = (uint16_t*)(ws + p.off_gth);
-      uint16_t* gtl = (uint16_t*)(ws + p.off_gtl);
-      uint16_t* xt = (uint16_t*)(ws + p.off_xt);
-      const int64_t tp = p.T_pad;
-      {
-        const int tc = (int)ceil_div(d_out, 64);
-        const dim3 grid((unsigned)(ceil_div(tp, 64) * tc));
-        if (d_out % 8 == 0 && (uintptr_t)g_buf % 16 == 0)
-          hipLaunchKernelGGL((gemm::transpose_kernel<true, true>), grid, dim3(256), 0, s,
-                             (const void*)g_buf, Ti, dout, tp, tc, gth, gtl);
-        else
-          hipLaunchKernelGGL((gemm::transpose_kernel<true, false>), grid, dim3(256), 0, s,
-                             (const void*)g_buf, Ti, dout, tp, tc, gth, gtl);
-      }
-      const int bt = p.outer_tile;
-      const int tiles_m = (int)ceil_div(d_out, bt), tiles_n = (int)ceil_div(d_in, bt);
+      const bool vec = (d_in % 4 == 0) && (d_out % 4 == 0) && ((uintptr_t)X % 8 == 0) &&
+                       ((uintptr_t)g_buf % 16 == 0) && d_in < (1 << 22) && d_out < (1 << 22);
+      const int tiles_m = (int)ceil_div(d_out, 64), tiles_n = (int)ceil_div(d_in, 64);
       const int per_xcd = (int)ceil_div((int64_t)tiles_m * tiles_n * p.outer_split, 8);
       const dim3 grid((unsigned)(8 * per_xcd));
-      if (bt == 128)
-        hipLaunchKernelGGL((gemm::nt_gemm_kernel<128, 128, 32, true, false, 4, true>), grid,
-                           dim3(256), 0, s, (const uint16_t*)gth, (const uint16_t*)gtl,
-                           (const uint16_t*)xt, tp, tp, dout, di, tp, tiles_m, tiles_n,
-                           p.outer_split, per_xcd, (int64_t)p.outer_tokens,
-                           (const uint16_t*)nullptr, dst, (uint16_t*)nullptr, (int64_t)0);
+      if (vec)
+        hipLaunchKernelGGL((gemm::tn_outer_kernel<4, true>), grid, dim3(256), 0, s,
+                           (const float*)g_buf, (const uint16_t*)X, Ti, dout, di, tiles_m,
+                           tiles_n, p.outer_split, per_xcd, (int64_t)p.outer_tokens, dst);
       else
-        hipLaunchKernelGGL((gemm::nt_gemm_kernel<64, 64, 64, true, false, 4, true>), grid,
-                           dim3(256), 0, s, (const uint16_t*)gth, (const uint16_t*)gtl,
-                           (const uint16_t*)xt, tp, tp, dout, di, tp, tiles_m, tiles_n,
-                           p.outer_split, per_xcd, (int64_t)p.outer_tokens,
-                           (const uint16_t*)nullptr, dst, (uint16_t*)nullptr, (int64_t)0);
+        hipLaunchKernelGGL((gemm::tn_outer_kernel<4, false>), grid, dim3(256), 0, s,
+                           (const float*)g_buf, (const uint16_t*)X, Ti, dout, di, tiles_m,
+                           tiles_n, p.outer_split, per_xcd, (int64_t)p.outer_tokens, dst);
     } else {
       const int tiles_n = (int)ceil_div(d_in, 64);
       const int64_t tiles = ceil_div(d_out, 64) * tiles_n;

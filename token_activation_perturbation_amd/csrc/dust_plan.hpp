@@ -36,21 +36,14 @@ struct Plan {
   // fused single-generation kernel (gamma = 0): one workgroup of fz_waves
   // waves per token, the noise indices split into ranges of fz_per_wave
   int32_t fz_waves = 1, fz_per_wave = 0;
-  // base GEMM output tile edge (64 or 128)
-  int32_t base_tile = 64;
-  // outer product: output tile edge (64 or 128; 64 for the fp32 path) and
-  // split of the token (contraction) axis
-  int32_t outer_tile = 64;
+  // outer product (64 x 64 output tiles): split of the token (contraction)
+  // axis into outer_split ranges of outer_tokens
   int32_t outer_split = 1;
   int64_t outer_tokens = 0;  // tokens per split (multiple of 64)
 
-  // bf16 path: tokens padded to a multiple of 8 for the transposed operands
-  // of the outer product (gT_hi, gT_lo [d_out][T_pad], XT [d_in][T_pad])
-  int64_t T_pad = 0;
-
   // workspace byte offsets (each 256-byte aligned) and total
   size_t off_delta = 0, off_P = 0, off_Q = 0, off_rho = 0, off_mean = 0,
-         off_wgt = 0, off_g = 0, off_gpart = 0, off_gth = 0, off_gtl = 0, off_xt = 0,
+         off_wgt = 0, off_g = 0, off_gpart = 0,
          off_rloc = 0, off_carry = 0, total = 0;
 };
 
@@ -102,21 +95,17 @@ inline bool make_plan(int64_t T, int64_t d_in, int64_t d_out, int32_t K,
   if (fw < 1) fw = 1;
   q.fz_per_wave = (int32_t)(ceil_div(ceil_div(q.K_n, fw), 4) * 4);
   q.fz_waves = (int32_t)ceil_div(q.K_n, q.fz_per_wave);
-  // base GEMM: 128x128 tiles when that still gives >= 512 workgroups
-  q.base_tile = (dtype == 1 && ceil_div(T, 128) * ceil_div(d_out, 128) >= 512) ? 128 : 64;
   // outer product: 64x64 tiles; split the tokens until ~DUST_OUTER_WORKGROUPS
   // workgroups, keeping >= 512 tokens per split (measured best on MI355X for
   // 512-wide and 3072 x 768 layers)
-  q.outer_tile = 64;
   const int64_t tiles = ceil_div(d_out, 64) * ceil_div(d_in, 64);
   int64_t split = ceil_div(DUST_OUTER_WORKGROUPS, tiles);
   const int64_t max_split = ceil_div(T, 512);
   if (split > max_split) split = max_split;
   if (split > 64) split = 64;
   if (split < 1) split = 1;
-  q.T_pad = ceil_div(T, 8) * 8;
-  q.outer_tokens = ceil_div(ceil_div(q.T_pad, split), 64) * 64;
-  q.outer_split = (int32_t)ceil_div(q.T_pad, q.outer_tokens);
+  q.outer_tokens = ceil_div(ceil_div(T, split), 64) * 64;
+  q.outer_split = (int32_t)ceil_div(T, q.outer_tokens);
 
   size_t off = 0;
   auto take = [&off](size_t bytes) {
@@ -134,10 +123,6 @@ inline bool make_plan(int64_t T, int64_t d_in, int64_t d_out, int32_t K,
   q.off_gpart = take(q.outer_split > 1 ? sizeof(float) * size_t(q.outer_split) *
                                              size_t(d_out) * size_t(d_in)
                                        : 0);
-  const bool bf16 = dtype == 1;
-  q.off_gth = take(bf16 ? sizeof(uint16_t) * size_t(d_out) * size_t(q.T_pad) : 0);
-  q.off_gtl = take(bf16 ? sizeof(uint16_t) * size_t(d_out) * size_t(q.T_pad) : 0);
-  q.off_xt = take(bf16 ? sizeof(uint16_t) * size_t(d_in) * size_t(q.T_pad) : 0);
 
   // chunked credit scan (gamma > 0, sequences of >= 2 tokens): the chunks'
   // own scans [T][K], and one head/carry per (sequence, 32-token chunk,
