@@ -18,6 +18,7 @@
 //   reweight       g_t = sum_n weight_(t,n) a_t^n; the noise regenerated inline
 //   outer          G_W = sum_t g_t x_t^T on MFMA (bf16 hi/lo split of g),
 //                  split over tokens, partials summed in a fixed order
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -858,23 +859,48 @@ __global__ __launch_bounds__(256) void fused_g0_kernel(
   }
 }
 
+// Bench hook state: event pairs stamped by the dispatch of the noise kernel
+// of the next dust_estimate calls (hipExtLaunchKernelGGL's start and stop
+// events, so they time the kernel itself, not the gap before it), pair i on
+// call i (cycling).  Process-wide, not synchronized: set it from one thread
+// while no estimate is being enqueued.
+hipEvent_t* g_ev_start = nullptr;
+hipEvent_t* g_ev_stop = nullptr;
+int32_t g_ev_count = 0;
+int64_t g_ev_next = 0;
+
+struct TimedLaunch {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+// The event pair for this call (null events when no pairs are set), and
+// the cursor moved on to the next pair.
+inline TimedLaunch take_timing_events() {
+  TimedLaunch t;
+  if (g_ev_count <= 0) return t;
+  const int64_t i = g_ev_next++ % g_ev_count;
+  t.start = g_ev_start[i];
+  t.stop = g_ev_stop[i];
+  return t;
+}
+
 template <int QPL>
 void launch_fused_g0_qpl(bool anti, bool full, unsigned blocks, unsigned threads,
-                         hipStream_t s, const float* delta, int32_t T, int32_t d_out,
-                         int32_t nq, int32_t K, int32_t K_n, int32_t per_wave, float sigma,
-                         NoiseKey key, float* P, float* Q, float* loss, float* g) {
+                         hipStream_t s, TimedLaunch tl, const float* delta, int32_t T,
+                         int32_t d_out, int32_t nq, int32_t K, int32_t K_n, int32_t per_wave,
+                         float sigma, NoiseKey key, float* P, float* Q, float* loss, float* g) {
+#define DUST_FUSED_LAUNCH(A, F)                                                                \
+  hipExtLaunchKernelGGL((fused_g0_kernel<QPL, A, F>), dim3(blocks), dim3(threads), 0, s,       \
+                        tl.start, tl.stop, 0, delta, T, d_out, nq, K, K_n, per_wave, sigma, key, \
+                        P, Q, loss, g)
   if (anti && full)
-    hipLaunchKernelGGL((fused_g0_kernel<QPL, true, true>), dim3(blocks), dim3(threads), 0, s,
-                       delta, T, d_out, nq, K, K_n, per_wave, sigma, key, P, Q, loss, g);
+    DUST_FUSED_LAUNCH(true, true);
   else if (anti)
-    hipLaunchKernelGGL((fused_g0_kernel<QPL, true, false>), dim3(blocks), dim3(threads), 0, s,
-                       delta, T, d_out, nq, K, K_n, per_wave, sigma, key, P, Q, loss, g);
+    DUST_FUSED_LAUNCH(true, false);
   else if (full)
-    hipLaunchKernelGGL((fused_g0_kernel<QPL, false, true>), dim3(blocks), dim3(threads), 0, s,
-                       delta, T, d_out, nq, K, K_n, per_wave, sigma, key, P, Q, loss, g);
+    DUST_FUSED_LAUNCH(false, true);
   else
-    hipLaunchKernelGGL((fused_g0_kernel<QPL, false, false>), dim3(blocks), dim3(threads), 0, s,
-                       delta, T, d_out, nq, K, K_n, per_wave, sigma, key, P, Q, loss, g);
+    DUST_FUSED_LAUNCH(false, false);
+#undef DUST_FUSED_LAUNCH
 }
 
 // Quads per lane the fused kernel is instantiated for (covers d_out <= 4096).
@@ -887,12 +913,12 @@ inline int fused_qpl(int32_t nq) {
 }
 
 void launch_fused_g0(int qpl, bool anti, bool full, unsigned blocks, unsigned threads,
-                     hipStream_t s, const float* delta, int32_t T, int32_t d_out, int32_t nq,
-                     int32_t K, int32_t K_n, int32_t per_wave, float sigma, NoiseKey key,
-                     float* P, float* Q, float* loss, float* g) {
+                     hipStream_t s, TimedLaunch tl, const float* delta, int32_t T,
+                     int32_t d_out, int32_t nq, int32_t K, int32_t K_n, int32_t per_wave,
+                     float sigma, NoiseKey key, float* P, float* Q, float* loss, float* g) {
 #define DUST_FUSED_CASE(V)                                                                  \
   case V:                                                                                   \
-    launch_fused_g0_qpl<V>(anti, full, blocks, threads, s, delta, T, d_out, nq, K, K_n,     \
+    launch_fused_g0_qpl<V>(anti, full, blocks, threads, s, tl, delta, T, d_out, nq, K, K_n, \
                            per_wave, sigma, key, P, Q, loss, g);                            \
     break;
   switch (qpl) {
@@ -908,28 +934,6 @@ void launch_fused_g0(int qpl, bool anti, bool full, unsigned blocks, unsigned th
       break;
   }
 #undef DUST_FUSED_CASE
-}
-
-// Bench hook state: event pairs recorded around the noise kernel of the
-// next dust_estimate calls, pair i on call i (cycling).  Process-wide, not
-// synchronized: set it from one thread while no estimate is being enqueued.
-hipEvent_t* g_ev_start = nullptr;
-hipEvent_t* g_ev_stop = nullptr;
-int32_t g_ev_count = 0;
-int64_t g_ev_next = 0;
-
-inline void record_start(hipStream_t s, hipEvent_t* slot_stop) {
-  *slot_stop = nullptr;
-  if (g_ev_count <= 0) return;
-  const int64_t i = g_ev_next % g_ev_count;
-  if (g_ev_start[i]) hipEventRecord(g_ev_start[i], s);
-  *slot_stop = g_ev_stop[i];
-}
-
-inline void record_stop(hipStream_t s, hipEvent_t stop) {
-  if (g_ev_count <= 0) return;
-  if (stop) hipEventRecord(stop, s);
-  ++g_ev_next;
 }
 
 inline NoiseKey make_key(uint64_t seed) {
@@ -994,17 +998,15 @@ dust_status_t dust_estimate(const void* X, const void* W, const void* target, in
   }
   const int qpl = fused_qpl(p.nq);
   const bool independent = (gamma == 0.0f || seq_len == 1);
-  hipEvent_t ev_stop = nullptr;
+  const TimedLaunch tl = take_timing_events();
   if (independent && qpl > 0) {
     // 2'. single-generation estimator: g directly (and P, Q when the loss
     //     reductions or the credit are requested)
     const bool want_pq = rho != nullptr || reward != nullptr;
     const bool full = (p.nq == 64 * qpl) && (d_out % 4 == 0);
-    record_start(s, &ev_stop);
     launch_fused_g0(qpl, p.antithetic != 0, full, (unsigned)T, (unsigned)(64 * p.fz_waves), s,
-                    (const float*)delta, Ti, dout, p.nq, K, p.K_n, p.fz_per_wave, sigma, key,
+                    tl, (const float*)delta, Ti, dout, p.nq, K, p.K_n, p.fz_per_wave, sigma, key,
                     want_pq ? Pbuf : nullptr, want_pq ? Qbuf : nullptr, loss_clean, g_buf);
-    record_stop(s, ev_stop);
     if (want_pq) {
       hipLaunchKernelGGL(token_stats_kernel, dim3(grid_for(T, 4)), dim3(256), 0, s,
                          (const float*)Pbuf, (const float*)Qbuf, Ti, K, p.K_n, p.antithetic,
@@ -1015,11 +1017,9 @@ dust_status_t dust_estimate(const void* X, const void* W, const void* target, in
     }
   } else {
     // 2. jitter + loss change
-    record_start(s, &ev_stop);
-    hipLaunchKernelGGL(jitter_loss_kernel, dim3(grid_for(T * p.jl_chunks, 4)), dim3(256), 0, s,
-                       (const float*)delta, Ti, dout, p.nq, p.K_n, p.jl_chunks, p.jl_per_chunk,
-                       key, Pbuf, Qbuf, loss_clean);
-    record_stop(s, ev_stop);
+    hipExtLaunchKernelGGL(jitter_loss_kernel, dim3(grid_for(T * p.jl_chunks, 4)), dim3(256), 0, s,
+                          tl.start, tl.stop, 0, (const float*)delta, Ti, dout, p.nq, p.K_n,
+                          p.jl_chunks, p.jl_per_chunk, key, Pbuf, Qbuf, loss_clean);
     // 3. loss reductions and their mean over draws
     hipLaunchKernelGGL(token_stats_kernel, dim3(grid_for(T, 4)), dim3(256), 0, s,
                        (const float*)Pbuf, (const float*)Qbuf, Ti, K, p.K_n, p.antithetic, sigma,

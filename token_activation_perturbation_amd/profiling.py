@@ -69,11 +69,15 @@ def pmc_traffic(fetch_db: str, write_db: str, kernel: str, copy_bytes: int) -> d
             raise KeyError(pattern)
         return keys[0]
 
-    copy_key_f = pick(fetch, r"copy|Copy")
-    copy_key_w = pick(write, r"copy|Copy")
-    # the copy dispatch with the most traffic is the calibration copy
-    copy_f = max(fetch[copy_key_f])
-    copy_w = max(write[copy_key_w])
+    def largest_copy(d):
+        # the copy dispatch with the most traffic is the calibration copy
+        vals = [v for k, vs in d.items() if re.search(r"copy|Copy", k) for v in vs]
+        if not vals:
+            raise KeyError("no copy kernel in the counter run")
+        return max(vals)
+
+    copy_f = largest_copy(fetch)
+    copy_w = largest_copy(write)
     f_scale = copy_bytes / (copy_f * 1024.0)
     w_scale = copy_bytes / (copy_w * 1024.0)
     kf = pick(fetch, re.escape(kernel))
