@@ -28,6 +28,7 @@ namespace gemm {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef unsigned short u16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
@@ -143,38 +144,25 @@ __device__ __forceinline__ void mma_tile(const uint16_t* la, const uint16_t* lb,
   }
 }
 
-// The same for the TN kernel's swizzled tiles: chunk c of row r at chunk
-// position c ^ ((r >> 4) & 3).  A fragment's 16 rows share r >> 4, so the
-// swizzle is one XOR per fragment.  A is hi + lo (two MFMAs per product).
-template <int BK, int LDK>
-__device__ __forceinline__ void mma_tile_swz(const uint16_t* la, const uint16_t* la2,
-                                             const uint16_t* lb, int wm, int wn, int lane,
-                                             f32x4_t (&acc)[2][2]) {
-  const int fr = lane & 15, fc = lane >> 4;
-#pragma unroll
-  for (int ks = 0; ks < BK; ks += 32) {
-    u16x8_t af[2], af2[2], bfr[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int r = wm * 32 + i * 16 + fr;
-      const int c = ((ks / 8 + fc) ^ ((r >> 4) & 3)) * 8;
-      af[i] = *(const u16x8_t*)(&la[r * LDK + c]);
-      af2[i] = *(const u16x8_t*)(&la2[r * LDK + c]);
-    }
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int r = wn * 32 + j * 16 + fr;
-      const int c = ((ks / 8 + fc) ^ ((r >> 4) & 3)) * 8;
-      bfr[j] = *(const u16x8_t*)(&lb[r * LDK + c]);
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        acc[i][j] = mfma16(af[i], bfr[j], acc[i][j]);
-        acc[i][j] = mfma16(af2[i], bfr[j], acc[i][j]);
-      }
-  }
+// gfx950's transposing LDS read, ds_read_b64_tr_b16: within each group of 16
+// lanes, output lane i element e is element i % 4 of the 8 bytes that lane
+// 4 e + i / 4 addressed (measured on MI355X).  So when the 16 lanes of a
+// group address a block of 4 tokens x 16 channels of a token-major tile (lane
+// j: token j / 4, channels 4 (j % 4) .. + 3), lane i receives channel i of
+// the 4 tokens: half of an MFMA operand fragment, contraction-contiguous.
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+
+// MFMA operand fragment (16 rows = channels ch0 .. ch0 + 15, 8 contraction
+// values = tokens k0 + 8 (lane / 16) .. + 7) from a token-major bf16 tile with
+// row pitch LDT elements.
+template <int LDT>
+__device__ __forceinline__ u16x8_t frag_tr(const uint16_t* tile, int ch0, int k0, int lane) {
+  const int tok = k0 + 8 * (lane >> 4) + ((lane & 15) >> 2);
+  const uint16_t* p = tile + tok * LDT + ch0 + 4 * (lane & 3);
+  typedef __attribute__((address_space(3))) v4i16_t* lds_v4_ptr;
+  const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4_ptr)p);
+  const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4_ptr)(p + 4 * LDT));
+  return __builtin_bit_cast(u16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
 // ---------------------------------------------------------------------------
@@ -279,34 +267,32 @@ __global__ __launch_bounds__(256) void nt_gemm_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Outer product over a token range: out[m][n] = sum_t g[t][m] X[t][n] for t in
-// split's range [split * t_per_split, min(T, (split + 1) * t_per_split)),
-// g fp32 [T][M] (M = d_out), X bf16 [T][N] (N = d_in); out is G itself with
-// one split, else the split's own [M][N] partial (summed afterwards by a
-// fixed-order kernel).  64 x 64 tiles, BK = 64 tokens.
+// Outer product over token ranges: out[m][n] = sum_t g[t][m] X[t][n] for t in
+// split s's range [t_first + s * t_per_split, min(T, t_first + (s + 1) *
+// t_per_split)), s < splits; g as its bf16 split g = g_hi + g_lo (written so by
+// the kernels that produce g), both [T][M] (M = d_out), X bf16 [T][N]
+// (N = d_in).  partial == 0: one split, out is G itself; else split s writes
+// its own [M][N] partial at out + s M N (summed afterwards by a fixed-order
+// kernel).  64 x 64 tiles, BK = 64 tokens; two MFMAs (hi, lo) per product.
 //
-// Both operands are contiguous along the output axes, so the loaders keep
-// lanes along a token row and transpose in registers: thread (cq, tq) =
-// (tid % 16, tid / 16) holds channels 4 cq .. 4 cq + 3 of tokens
-// 4 tq .. 4 tq + 3 of a tile, fetched as four 16-byte (g) and four 8-byte (X)
-// loads, one per token; it then writes, per channel, the 4 tokens as one
-// 8-byte piece of that channel's k-major LDS row (g split into bf16
-// hi = rn(v) and lo = rn(v - hi) on the way, by v_cvt_pk_bf16_f32).
-// LDS rows are 72 bf16 (144 bytes), and the 16-byte chunk c of row r sits at
-// chunk position c ^ ((r >> 4) & 3): the 16 lanes of a store then hit 16
-// distinct bank pairs, and the 16 rows of an MFMA fragment read (same
-// r >> 4) 16 distinct bank quads.
-//
-// Addressing: a uniform tile base (the tile's first token, clamped to T - 1)
-// plus a 32-bit lane offset, min(row offset, last valid row) + column offset,
-// so rows past T re-read row T - 1 and columns past the edge re-read the last
-// 4 columns; tokens outside the split are zeroed at the LDS store.  VEC: M and
-// N multiples of 4, g 16-byte and X 8-byte aligned (else element-wise loads
-// with the same clamping).  M, N < 2^22 keep the lane offsets in 32 bits.
+// Both operands are contiguous along the output axes (token-major), so the
+// tiles are staged as they lie in HBM, 64 tokens x 64 channels with a row
+// pitch of 72 bf16 (144 bytes; nearly free of bank conflicts for the reads
+// below), and the transposition happens in the LDS read (frag_tr).  Loads:
+// thread t moves 16-byte chunks t and t + 256 of each tile (token c / 8,
+// channels 8 (c % 8) .. + 7), a token row per 8 lanes.  Rows past T re-read
+// row T - 1 and chunks past the channel edge re-read the last full chunk;
+// g rows of tokens outside the split are zeroed at the LDS store (X rows need
+// not be: their products with zero g vanish).  VEC: M and N multiples of 8,
+// g_hi, g_lo and X 16-byte aligned (else element-wise loads with the same
+// clamping).  M, N < 2^22 keep the lane offsets in 32 bits.
 // Pipeline as in nt_gemm_kernel.
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
+// bf16 split of two floats, hi = rn(v) and lo = rn(v - hi) (v_cvt_pk_bf16_f32,
+// round to nearest even), each pair packed in a dword with a in the low half.
+// hi + lo carries 16 significant bits of v.
 __device__ __forceinline__ void split_pair(float a, float b, uint32_t& hi, uint32_t& lo) {
   const f32x2_t v = {a, b};
   hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
@@ -316,14 +302,14 @@ __device__ __forceinline__ void split_pair(float a, float b, uint32_t& hi, uint3
 
 template <int S, bool VEC>
 __global__ __launch_bounds__(256) void tn_outer_kernel(
-    const float* __restrict__ g, const uint16_t* __restrict__ X, int32_t T, int32_t M,
-    int32_t N, int32_t tiles_m, int32_t tiles_n, int32_t splits, int32_t per_xcd,
-    int64_t t_per_split, float* __restrict__ out) {
-  constexpr int BM = 64, BN = 64, BK = 64;
-  constexpr int LDK = BK + 8;
-  __shared__ __attribute__((aligned(16))) uint16_t lds_ah[2][BM * LDK];
-  __shared__ __attribute__((aligned(16))) uint16_t lds_al[2][BM * LDK];
-  __shared__ __attribute__((aligned(16))) uint16_t lds_b[2][BN * LDK];
+    const uint16_t* __restrict__ g_hi, const uint16_t* __restrict__ g_lo,
+    const uint16_t* __restrict__ X, int32_t T, int32_t M, int32_t N, int32_t tiles_m,
+    int32_t tiles_n, int32_t splits, int32_t per_xcd, int64_t t_first, int64_t t_per_split,
+    int32_t partial, float* __restrict__ out) {
+  constexpr int BM = 64, BN = 64, BK = 64, LDT = 72;
+  __shared__ __attribute__((aligned(16))) uint16_t lds_ah[2][BK * LDT];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_al[2][BK * LDT];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_b[2][BK * LDT];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
@@ -331,53 +317,62 @@ __global__ __launch_bounds__(256) void tn_outer_kernel(
   if (!work.valid) return;
   const int64_t m0 = (int64_t)work.m_tile * BM;
   const int64_t n0 = (int64_t)work.n_tile * BN;
-  const int64_t t_begin = (int64_t)work.split * t_per_split;
+  const int64_t t_begin = t_first + (int64_t)work.split * t_per_split;
   const int64_t t_end = min((int64_t)T, t_begin + t_per_split);
   const int nk = (int)((t_end - t_begin + BK - 1) / BK);
   static_assert(S % 2 == 0, "the LDS double buffer is indexed by the stage parity");
 
-  const int cq = tid & 15, tq = tid >> 4;
-  // VEC lane offsets (bytes): columns clamped to the last 4, rows of the tile
-  const int64_t am = m0 + 4 * cq, bn = n0 + 4 * cq;
-  const uint32_t a_col = (uint32_t)((am < M ? am : M - 4) * 4);
-  const uint32_t b_col = (uint32_t)((bn < N ? bn : N - 4) * 2);
-  const uint32_t a_row = (uint32_t)(4 * tq) * (uint32_t)M * 4u;
-  const uint32_t b_row = (uint32_t)(4 * tq) * (uint32_t)N * 2u;
+  // this thread's two chunks: token rows tr[h], channel offsets cc (x8)
+  int trow[2], cc[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int c = tid + 256 * h;
+    trow[h] = c >> 3;
+    cc[h] = (c & 7) * 8;
+  }
+  // VEC lane offsets (bytes) of the chunks: columns clamped to the last full
+  // chunk, rows relative to the tile's first token
+  uint32_t a_col[2], b_col[2], a_row[2], b_row[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int64_t am = m0 + cc[h], bn = n0 + cc[h];
+    a_col[h] = (uint32_t)((am < M ? am : M - 8) * 2);
+    b_col[h] = (uint32_t)((bn < N ? bn : N - 8) * 2);
+    a_row[h] = (uint32_t)trow[h] * (uint32_t)M * 2u;
+    b_row[h] = (uint32_t)trow[h] * (uint32_t)N * 2u;
+  }
 
-  float4 ra[S][4];
-  uint2 rb[S][4];
+  u16x8_t rh[S][2], rl[S][2], rb[S][2];
   auto load_stage = [&](int st, int kt) {
     const int64_t tb = t_begin + (int64_t)kt * BK;
     const int64_t tbc = tb < T ? tb : (int64_t)T - 1;   // uniform
     const int64_t rows_left = (int64_t)T - 1 - tbc;      // valid rows after the first
     const uint32_t last = (uint32_t)(rows_left < 63 ? rows_left : 63);
     if (VEC) {
-      const char* abase = (const char*)(g + tbc * M);
+      const char* hbase = (const char*)(g_hi + tbc * M);
+      const char* lbase = (const char*)(g_lo + tbc * M);
       const char* bbase = (const char*)(X + tbc * N);
-      const uint32_t a_lim = last * (uint32_t)M * 4u, b_lim = last * (uint32_t)N * 2u;
+      const uint32_t a_lim = last * (uint32_t)M * 2u, b_lim = last * (uint32_t)N * 2u;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const uint32_t ao = a_row + (uint32_t)r * (uint32_t)M * 4u;
-        const uint32_t bo = b_row + (uint32_t)r * (uint32_t)N * 2u;
-        ra[st][r] = *(const float4*)(abase + ((ao < a_lim ? ao : a_lim) + a_col));
-        rb[st][r] = *(const uint2*)(bbase + ((bo < b_lim ? bo : b_lim) + b_col));
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t a_off = (a_row[h] < a_lim ? a_row[h] : a_lim) + a_col[h];
+        rh[st][h] = *(const u16x8_t*)(hbase + a_off);
+        rl[st][h] = *(const u16x8_t*)(lbase + a_off);
+        rb[st][h] = *(const u16x8_t*)(bbase + ((b_row[h] < b_lim ? b_row[h] : b_lim) + b_col[h]));
       }
     } else {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        int64_t t = tbc + 4 * tq + r;
+      for (int h = 0; h < 2; ++h) {
+        int64_t t = tbc + trow[h];
         t = t < T ? t : (int64_t)T - 1;
-        float av[4];
-        uint32_t bv[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int64_t ca = am + e < M ? am + e : (int64_t)M - 1;
-          const int64_t cb = bn + e < N ? bn + e : (int64_t)N - 1;
-          av[e] = g[t * M + ca];
-          bv[e] = X[t * N + cb];
+        for (int e = 0; e < 8; ++e) {
+          const int64_t ca = m0 + cc[h] + e < M ? m0 + cc[h] + e : (int64_t)M - 1;
+          const int64_t cb = n0 + cc[h] + e < N ? n0 + cc[h] + e : (int64_t)N - 1;
+          rh[st][h][e] = g_hi[t * M + ca];
+          rl[st][h][e] = g_lo[t * M + ca];
+          rb[st][h][e] = X[t * N + cb];
         }
-        ra[st][r] = make_float4(av[0], av[1], av[2], av[3]);
-        rb[st][r] = make_uint2(bv[0] | (bv[1] << 16), bv[2] | (bv[3] << 16));
       }
     }
   };
@@ -385,33 +380,34 @@ __global__ __launch_bounds__(256) void tn_outer_kernel(
     const int64_t tb = t_begin + (int64_t)kt * BK;
     const int64_t left = t_end - tb;                     // uniform
     const int n_ok = (int)(left < 0 ? 0 : (left > 64 ? 64 : left));
-    bool ok[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) ok[r] = 4 * tq + r < n_ok;
-    const int half = (tq & 1) * 4, chunk = tq >> 1;
+    for (int h = 0; h < 2; ++h) {
+      // all-ones or zero, applied with ANDs (a select here becomes a branch)
+      const uint32_t mk = 0u - (uint32_t)(trow[h] < n_ok);
+      const int off = trow[h] * LDT + cc[h];
+      *(u32x4_t*)(&lds_ah[buf][off]) = __builtin_bit_cast(u32x4_t, rh[st][h]) & mk;
+      *(u32x4_t*)(&lds_al[buf][off]) = __builtin_bit_cast(u32x4_t, rl[st][h]) & mk;
+      *(u16x8_t*)(&lds_b[buf][off]) = rb[st][h];
+    }
+  };
+  auto mma = [&](int buf, f32x4_t (&acc)[2][2]) {
 #pragma unroll
-    for (int ci = 0; ci < 4; ++ci) {
-      const int row = 4 * cq + ci;
-      const int off = row * LDK + ((chunk ^ ((row >> 4) & 3)) * 8) + half;
-      float v[4];
+    for (int ks = 0; ks < BK; ks += 32) {
+      u16x8_t ah[2], al[2], bf[2];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float4 q = ra[st][r];
-        const float x = ci == 0 ? q.x : ci == 1 ? q.y : ci == 2 ? q.z : q.w;
-        v[r] = ok[r] ? x : 0.f;
+      for (int i = 0; i < 2; ++i) {
+        ah[i] = frag_tr<LDT>(lds_ah[buf], wm * 32 + i * 16, ks, lane);
+        al[i] = frag_tr<LDT>(lds_al[buf], wm * 32 + i * 16, ks, lane);
       }
-      uint32_t h01, l01, h23, l23;
-      split_pair(v[0], v[1], h01, l01);
-      split_pair(v[2], v[3], h23, l23);
-      *(uint2*)(&lds_ah[buf][off]) = make_uint2(h01, h23);
-      *(uint2*)(&lds_al[buf][off]) = make_uint2(l01, l23);
-      uint32_t w[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const uint32_t d = (ci >> 1) ? rb[st][r].y : rb[st][r].x;
-        w[r] = ok[r] ? ((ci & 1) ? (d >> 16) : (d & 0xFFFFu)) : 0u;
-      }
-      *(uint2*)(&lds_b[buf][off]) = make_uint2(w[0] | (w[1] << 16), w[2] | (w[3] << 16));
+      for (int j = 0; j < 2; ++j) bf[j] = frag_tr<LDT>(lds_b[buf], wn * 32 + j * 16, ks, lane);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          acc[i][j] = mfma16(ah[i], bf[j], acc[i][j]);
+          acc[i][j] = mfma16(al[i], bf[j], acc[i][j]);
+        }
     }
   };
 
@@ -432,17 +428,17 @@ __global__ __launch_bounds__(256) void tn_outer_kernel(
     for (int s = 0; s < S; ++s) {
       const int kt = kt0 + s;
       const int cur = s & 1;
-      mma_tile_swz<BK, LDK>(lds_ah[cur], lds_al[cur], lds_b[cur], wm, wn, lane, acc);
+      mma(cur, acc);
       const int nxt = (s + 1) % S;
       store_stage(nxt, cur ^ 1, kt + 1);
       load_stage(nxt, kt + 1 + S);
       __syncthreads();
       // keep each step's register work in its step: the scheduler would
-      // otherwise hoist later stages' unpacking above their loads' arrival
+      // otherwise hoist later stages' masking above their loads' arrival
       __builtin_amdgcn_sched_barrier(0);
     }
   }
-  float* dst = splits > 1 ? out + (int64_t)work.split * M * N : out;
+  float* dst = partial ? out + (int64_t)work.split * M * N : out;
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll

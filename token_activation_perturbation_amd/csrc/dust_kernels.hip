@@ -450,21 +450,55 @@ __global__ __launch_bounds__(256) void scan_apply_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// g_t's channels c .. c + 3 (c = 4 q) at row offset `row` of a [T][d_out]
+// array: fp32 to g32 and / or the bf16 split hi = rn(v), lo = rn(v - hi) to
+// g_hi, g_lo (each optional; the bf16 outer product reads the split).
+// `full`: all 4 channels in range and d_out % 4 == 0 (vector stores).
+__device__ __forceinline__ void store_g_quad(float4 r, int64_t row, int c, int d_out, bool full,
+                                             float* g32, uint16_t* g_hi, uint16_t* g_lo) {
+  if (g32) {
+    if (full) {
+      *(float4*)(g32 + row + c) = r;
+    } else {
+      const float v[4] = {r.x, r.y, r.z, r.w};
+      for (int e = 0; e < 4; ++e)
+        if (c + e < d_out) g32[row + c + e] = v[e];
+    }
+  }
+  if (g_hi) {
+    uint32_t h01, l01, h23, l23;
+    gemm::split_pair(r.x, r.y, h01, l01);
+    gemm::split_pair(r.z, r.w, h23, l23);
+    if (full) {
+      *(uint2*)(g_hi + row + c) = make_uint2(h01, h23);
+      *(uint2*)(g_lo + row + c) = make_uint2(l01, l23);
+    } else {
+      const uint32_t hv[2] = {h01, h23}, lv[2] = {l01, l23};
+      for (int e = 0; e < 4; ++e)
+        if (c + e < d_out) {
+          g_hi[row + c + e] = (uint16_t)(hv[e >> 1] >> (16 * (e & 1)));
+          g_lo[row + c + e] = (uint16_t)(lv[e >> 1] >> (16 * (e & 1)));
+        }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Reweight: g_t = sum_n wgt[t][n] a_t^n.  One workgroup of `waves` waves per
 // token; wave w sums the noise indices of its contiguous range, lane l owns
 // quads l + 64 j, and the waves' partial sums are added in wave order.
 
 __global__ __launch_bounds__(256) void reweight_kernel(
-    const float* __restrict__ wgt, int32_t T, int32_t d_out, int32_t nq, int32_t K_n,
-    int32_t per_wave, NoiseKey key, float* __restrict__ g) {
+    const float* __restrict__ wgt, int32_t t0, int32_t T, int32_t d_out, int32_t nq,
+    int32_t K_n, int32_t per_wave, NoiseKey key, float* __restrict__ g32,
+    uint16_t* __restrict__ g_hi, uint16_t* __restrict__ g_lo) {
   __shared__ float4 part[4][64];
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int waves = blockDim.x >> 6;
-  const int32_t t = blockIdx.x;
+  const int32_t t = t0 + (int32_t)blockIdx.x;
   const int32_t n_begin = wave * per_wave;
   const int32_t n_end = min(K_n, n_begin + per_wave);
   const float* wrow = wgt + (int64_t)t * K_n;
-  float* grow = g + (int64_t)t * d_out;
   const int32_t q_rounds = (nq + 63) / 64;
   for (int32_t jr = 0; jr < q_rounds; ++jr) {
     const int32_t q = jr * 64 + lane;
@@ -501,13 +535,8 @@ __global__ __launch_bounds__(256) void reweight_kernel(
     }
     if (wave == 0 && q < nq) {
       const int c = 4 * q;
-      if (c + 3 < d_out && (d_out & 3) == 0) {
-        *(float4*)(grow + c) = acc;
-      } else {
-        const float v[4] = {acc.x, acc.y, acc.z, acc.w};
-        for (int e = 0; e < 4; ++e)
-          if (c + e < d_out) grow[c + e] = v[e];
-      }
+      store_g_quad(acc, (int64_t)t * d_out, c, d_out, c + 3 < d_out && (d_out & 3) == 0, g32,
+                   g_hi, g_lo);
     }
   }
 }
@@ -682,16 +711,17 @@ __device__ __forceinline__ void wave_reduce_to_scalars(float (&v)[M], int lane, 
 
 template <int QPL, bool ANTI, bool FULL>
 __global__ __launch_bounds__(256) void fused_g0_kernel(
-    const float* __restrict__ delta, int32_t T, int32_t d_out, int32_t nq, int32_t K,
-    int32_t K_n, int32_t per_wave, float sigma, NoiseKey key, float* __restrict__ Pout,
-    float* __restrict__ Qout, float* __restrict__ loss_clean, float* __restrict__ g) {
+    const float* __restrict__ delta, int32_t t0, int32_t T, int32_t d_out, int32_t nq,
+    int32_t K, int32_t K_n, int32_t per_wave, float sigma, NoiseKey key,
+    float* __restrict__ Pout, float* __restrict__ Qout, float* __restrict__ loss_clean,
+    float* __restrict__ g32, uint16_t* __restrict__ g_hi, uint16_t* __restrict__ g_lo) {
   constexpr int NB = QPL <= 2 ? DUST_FUSED_NB_SMALL : (QPL <= 4 ? 2 : 1);
   constexpr int M = 2 * NB;
   __shared__ float4 xch[4][64];
   __shared__ float rsum_x[4];
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int waves = blockDim.x >> 6;
-  const int32_t t = blockIdx.x;
+  const int32_t t = t0 + (int32_t)blockIdx.x;
   const int32_t n_begin = wave * per_wave;
   const int32_t n_end = min(K_n, n_begin + per_wave);
   const float* drow = delta + (int64_t)t * d_out;
@@ -834,7 +864,6 @@ __global__ __launch_bounds__(256) void fused_g0_kernel(
   if (wave != 0) return;
   const float mean_rho = rsum / (float)K;
   const float scale = ANTI ? 2.0f / (float)K : -1.0f / ((float)K * sigma);
-  float* grow = g + (int64_t)t * d_out;
 #pragma unroll
   for (int j = 0; j < QPL; ++j) {
     const int q = lane + 64 * j;
@@ -847,15 +876,7 @@ __global__ __launch_bounds__(256) void fused_g0_kernel(
                       scale * __builtin_fmaf(-mean_rho, S[j].z, A[j].z),
                       scale * __builtin_fmaf(-mean_rho, S[j].w, A[j].w));
     }
-    if (FULL) {
-      *(float4*)(grow + 4 * q) = r;
-    } else {
-      const int c = 4 * q;
-      if (c < d_out) grow[c] = r.x;
-      if (c + 1 < d_out) grow[c + 1] = r.y;
-      if (c + 2 < d_out) grow[c + 2] = r.z;
-      if (c + 3 < d_out) grow[c + 3] = r.w;
-    }
+    store_g_quad(r, (int64_t)t * d_out, 4 * q, d_out, FULL, g32, g_hi, g_lo);
   }
 }
 
@@ -885,13 +906,14 @@ inline TimedLaunch take_timing_events() {
 
 template <int QPL>
 void launch_fused_g0_qpl(bool anti, bool full, unsigned blocks, unsigned threads,
-                         hipStream_t s, TimedLaunch tl, const float* delta, int32_t T,
-                         int32_t d_out, int32_t nq, int32_t K, int32_t K_n, int32_t per_wave,
-                         float sigma, NoiseKey key, float* P, float* Q, float* loss, float* g) {
-#define DUST_FUSED_LAUNCH(A, F)                                                                \
-  hipExtLaunchKernelGGL((fused_g0_kernel<QPL, A, F>), dim3(blocks), dim3(threads), 0, s,       \
-                        tl.start, tl.stop, 0, delta, T, d_out, nq, K, K_n, per_wave, sigma, key, \
-                        P, Q, loss, g)
+                         hipStream_t s, TimedLaunch tl, const float* delta, int32_t t0,
+                         int32_t T, int32_t d_out, int32_t nq, int32_t K, int32_t K_n,
+                         int32_t per_wave, float sigma, NoiseKey key, float* P, float* Q,
+                         float* loss, float* g32, uint16_t* g_hi, uint16_t* g_lo) {
+#define DUST_FUSED_LAUNCH(A, F)                                                               \
+  hipExtLaunchKernelGGL((fused_g0_kernel<QPL, A, F>), dim3(blocks), dim3(threads), 0, s,      \
+                        tl.start, tl.stop, 0, delta, t0, T, d_out, nq, K, K_n, per_wave, sigma, \
+                        key, P, Q, loss, g32, g_hi, g_lo)
   if (anti && full)
     DUST_FUSED_LAUNCH(true, true);
   else if (anti)
@@ -913,13 +935,14 @@ inline int fused_qpl(int32_t nq) {
 }
 
 void launch_fused_g0(int qpl, bool anti, bool full, unsigned blocks, unsigned threads,
-                     hipStream_t s, TimedLaunch tl, const float* delta, int32_t T,
-                     int32_t d_out, int32_t nq, int32_t K, int32_t K_n, int32_t per_wave,
-                     float sigma, NoiseKey key, float* P, float* Q, float* loss, float* g) {
-#define DUST_FUSED_CASE(V)                                                                  \
-  case V:                                                                                   \
-    launch_fused_g0_qpl<V>(anti, full, blocks, threads, s, tl, delta, T, d_out, nq, K, K_n, \
-                           per_wave, sigma, key, P, Q, loss, g);                            \
+                     hipStream_t s, TimedLaunch tl, const float* delta, int32_t t0,
+                     int32_t T, int32_t d_out, int32_t nq, int32_t K, int32_t K_n,
+                     int32_t per_wave, float sigma, NoiseKey key, float* P, float* Q,
+                     float* loss, float* g32, uint16_t* g_hi, uint16_t* g_lo) {
+#define DUST_FUSED_CASE(V)                                                                   \
+  case V:                                                                                    \
+    launch_fused_g0_qpl<V>(anti, full, blocks, threads, s, tl, delta, t0, T, d_out, nq, K,   \
+                           K_n, per_wave, sigma, key, P, Q, loss, g32, g_hi, g_lo);          \
     break;
   switch (qpl) {
     DUST_FUSED_CASE(1)
@@ -969,7 +992,13 @@ dust_status_t dust_estimate(const void* X, const void* W, const void* target, in
   float* rho_buf = rho ? rho : (float*)(ws + p.off_rho);
   float* mean = (float*)(ws + p.off_mean);
   float* wgt = (float*)(ws + p.off_wgt);
-  float* g_buf = g ? g : (float*)(ws + p.off_g);
+  // g: fp32 for the f32 path (the caller's buffer when requested); for bf16
+  // the outer product reads the bf16 split g_hi + g_lo from the workspace,
+  // and fp32 g is written only when requested
+  const bool bf16 = dtype == DUST_BF16;
+  float* g32 = bf16 ? g : (g ? g : (float*)(ws + p.off_g));
+  uint16_t* g_hi = bf16 ? (uint16_t*)(ws + p.off_g) : nullptr;
+  uint16_t* g_lo = bf16 ? g_hi + T * d_out : nullptr;
   float* gpart = (float*)(ws + p.off_gpart);
   const NoiseKey key = make_key(seed);
   const int32_t Ti = (int32_t)T, di = (int32_t)d_in, dout = (int32_t)d_out;
@@ -998,24 +1027,11 @@ dust_status_t dust_estimate(const void* X, const void* W, const void* target, in
   }
   const int qpl = fused_qpl(p.nq);
   const bool independent = (gamma == 0.0f || seq_len == 1);
+  const bool fused = independent && qpl > 0;
+  const bool want_pq = rho != nullptr || reward != nullptr;
   const TimedLaunch tl = take_timing_events();
-  if (independent && qpl > 0) {
-    // 2'. single-generation estimator: g directly (and P, Q when the loss
-    //     reductions or the credit are requested)
-    const bool want_pq = rho != nullptr || reward != nullptr;
-    const bool full = (p.nq == 64 * qpl) && (d_out % 4 == 0);
-    launch_fused_g0(qpl, p.antithetic != 0, full, (unsigned)T, (unsigned)(64 * p.fz_waves), s,
-                    tl, (const float*)delta, Ti, dout, p.nq, K, p.K_n, p.fz_per_wave, sigma, key,
-                    want_pq ? Pbuf : nullptr, want_pq ? Qbuf : nullptr, loss_clean, g_buf);
-    if (want_pq) {
-      hipLaunchKernelGGL(token_stats_kernel, dim3(grid_for(T, 4)), dim3(256), 0, s,
-                         (const float*)Pbuf, (const float*)Qbuf, Ti, K, p.K_n, p.antithetic,
-                         sigma, rho_buf, mean);
-      hipLaunchKernelGGL(credit_token_kernel, dim3(grid_for(T * p.K_n, 256)), dim3(256), 0, s,
-                         (const float*)rho_buf, (const float*)mean, Ti, K, p.K_n, p.antithetic,
-                         sigma, reward, wgt);
-    }
-  } else {
+
+  if (!fused) {
     // 2. jitter + loss change
     hipExtLaunchKernelGGL(jitter_loss_kernel, dim3(grid_for(T * p.jl_chunks, 4)), dim3(256), 0, s,
                           tl.start, tl.stop, 0, (const float*)delta, Ti, dout, p.nq, p.K_n,
@@ -1045,39 +1061,63 @@ dust_status_t dust_estimate(const void* X, const void* W, const void* target, in
                          (const float*)r_loc, (const float*)carry, Ti, (int32_t)seq_len, K,
                          p.K_n, n_chunks, p.antithetic, sigma, gamma, reward, wgt);
     }
-    // 5. reweight -> g
-    hipLaunchKernelGGL(reweight_kernel, dim3((unsigned)T), dim3(64 * p.rw_waves), 0, s,
-                       (const float*)wgt, Ti, dout, p.nq, p.K_n, p.rw_per_wave, key, g_buf);
   }
-  // 6. outer product -> G_W
-  {
-    float* dst = p.outer_split > 1 ? gpart : G_W;
-    if (dtype == DUST_BF16) {
-      const bool vec = (d_in % 4 == 0) && (d_out % 4 == 0) && ((uintptr_t)X % 8 == 0) &&
-                       ((uintptr_t)g_buf % 16 == 0) && d_in < (1 << 22) && d_out < (1 << 22);
-      const int tiles_m = (int)ceil_div(d_out, 64), tiles_n = (int)ceil_div(d_in, 64);
-      const int per_xcd = (int)ceil_div((int64_t)tiles_m * tiles_n * p.outer_split, 8);
-      const dim3 grid((unsigned)(8 * per_xcd));
-      if (vec)
-        hipLaunchKernelGGL((gemm::tn_outer_kernel<4, true>), grid, dim3(256), 0, s,
-                           (const float*)g_buf, (const uint16_t*)X, Ti, dout, di, tiles_m,
-                           tiles_n, p.outer_split, per_xcd, (int64_t)p.outer_tokens, dst);
-      else
-        hipLaunchKernelGGL((gemm::tn_outer_kernel<4, false>), grid, dim3(256), 0, s,
-                           (const float*)g_buf, (const uint16_t*)X, Ti, dout, di, tiles_m,
-                           tiles_n, p.outer_split, per_xcd, (int64_t)p.outer_tokens, dst);
-    } else {
-      const int tiles_n = (int)ceil_div(d_in, 64);
-      const int64_t tiles = ceil_div(d_out, 64) * tiles_n;
-      hipLaunchKernelGGL(outer_f32_kernel, dim3((unsigned)(tiles * p.outer_split)), dim3(256), 0,
-                         s, (const float*)g_buf, (const float*)X, Ti, di, dout, tiles_n,
-                         (int32_t)p.outer_tokens, dst);
+
+  // 5. g: the fused single-generation kernel (and P, Q when the loss
+  //    reductions or the credit are requested), or the reweight kernel
+  if (fused) {
+    const bool full = (p.nq == 64 * qpl) && (d_out % 4 == 0);
+    launch_fused_g0(qpl, p.antithetic != 0, full, (unsigned)T, (unsigned)(64 * p.fz_waves), s,
+                    tl, (const float*)delta, 0, Ti, dout, p.nq, K, p.K_n, p.fz_per_wave, sigma,
+                    key, want_pq ? Pbuf : nullptr, want_pq ? Qbuf : nullptr, loss_clean, g32,
+                    g_hi, g_lo);
+    if (want_pq) {
+      hipLaunchKernelGGL(token_stats_kernel, dim3(grid_for(T, 4)), dim3(256), 0, s,
+                         (const float*)Pbuf, (const float*)Qbuf, Ti, K, p.K_n, p.antithetic,
+                         sigma, rho_buf, mean);
+      hipLaunchKernelGGL(credit_token_kernel, dim3(grid_for(T * p.K_n, 256)), dim3(256), 0, s,
+                         (const float*)rho_buf, (const float*)mean, Ti, K, p.K_n, p.antithetic,
+                         sigma, reward, wgt);
     }
-    if (p.outer_split > 1) {
-      const int64_t n = d_out * d_in;
-      hipLaunchKernelGGL(split_sum_kernel, dim3(grid_for(ceil_div(n, 4), 256)), dim3(256), 0, s,
-                         (const float*)gpart, p.outer_split, n, G_W);
-    }
+  } else {
+    hipLaunchKernelGGL(reweight_kernel, dim3((unsigned)T), dim3(64 * p.rw_waves), 0, s,
+                       (const float*)wgt, 0, Ti, dout, p.nq, p.K_n, p.rw_per_wave, key, g32,
+                       g_hi, g_lo);
+  }
+
+  // 6. outer product -> the split partials (or G_W itself with one split),
+  //    then their fixed-order sum
+  float* dst = p.outer_split > 1 ? gpart : G_W;
+  if (dtype == DUST_BF16) {
+    const bool vec = (d_in % 8 == 0) && (d_out % 8 == 0) && ((uintptr_t)X % 16 == 0) &&
+                     d_in < (1 << 22) && d_out < (1 << 22);
+    const int tiles_m = (int)ceil_div(d_out, 64), tiles_n = (int)ceil_div(d_in, 64);
+    const int per_xcd = (int)ceil_div((int64_t)tiles_m * tiles_n * p.outer_split, 8);
+    const dim3 grid((unsigned)(8 * per_xcd));
+    const int32_t partial = p.outer_split > 1 ? 1 : 0;
+    if (vec)
+      hipLaunchKernelGGL((gemm::tn_outer_kernel<4, true>), grid, dim3(256), 0, s,
+                         (const uint16_t*)g_hi, (const uint16_t*)g_lo, (const uint16_t*)X, Ti,
+                         dout, di, tiles_m, tiles_n,
+                         p.outer_split, per_xcd, (int64_t)0, (int64_t)p.outer_tokens, partial,
+                         dst);
+    else
+      hipLaunchKernelGGL((gemm::tn_outer_kernel<4, false>), grid, dim3(256), 0, s,
+                         (const uint16_t*)g_hi, (const uint16_t*)g_lo, (const uint16_t*)X, Ti,
+                         dout, di, tiles_m, tiles_n,
+                         p.outer_split, per_xcd, (int64_t)0, (int64_t)p.outer_tokens, partial,
+                         dst);
+  } else {
+    const int tiles_n = (int)ceil_div(d_in, 64);
+    const int64_t tiles = ceil_div(d_out, 64) * tiles_n;
+    hipLaunchKernelGGL(outer_f32_kernel, dim3((unsigned)(tiles * p.outer_split)), dim3(256), 0,
+                       s, (const float*)g32, (const float*)X, Ti, di, dout, tiles_n,
+                       (int32_t)p.outer_tokens, dst);
+  }
+  if (p.outer_split > 1) {
+    const int64_t n = d_out * d_in;
+    hipLaunchKernelGGL(split_sum_kernel, dim3(grid_for(ceil_div(n, 4), 256)), dim3(256), 0, s,
+                       (const float*)gpart, p.outer_split, n, G_W);
   }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(DUST_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));

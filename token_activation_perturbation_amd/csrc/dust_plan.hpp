@@ -22,6 +22,10 @@ constexpr int64_t kTargetWaves = DUST_TARGET_WAVES;
 #ifndef DUST_OUTER_WORKGROUPS
 #define DUST_OUTER_WORKGROUPS 2048
 #endif
+// ... keeping at least this many tokens per split (-DDUST_OUTER_MIN_TOKENS).
+#ifndef DUST_OUTER_MIN_TOKENS
+#define DUST_OUTER_MIN_TOKENS 512
+#endif
 
 struct Plan {
   int64_t T = 0, d_in = 0, d_out = 0;
@@ -100,7 +104,7 @@ inline bool make_plan(int64_t T, int64_t d_in, int64_t d_out, int32_t K,
   // 512-wide and 3072 x 768 layers)
   const int64_t tiles = ceil_div(d_out, 64) * ceil_div(d_in, 64);
   int64_t split = ceil_div(DUST_OUTER_WORKGROUPS, tiles);
-  const int64_t max_split = ceil_div(T, 512);
+  const int64_t max_split = ceil_div(T, DUST_OUTER_MIN_TOKENS);
   if (split > max_split) split = max_split;
   if (split > 64) split = 64;
   if (split < 1) split = 1;
