@@ -37,7 +37,7 @@ def trace_rows(db: str):
 
 
 def trace_markdown(db: str, title: str, command: str) -> str:
-    lines = [f"# {title}", "", "Command (repository root, MI355X box):", "", "```", command,
+    lines = [f"# {title}", "", "Command (repository root, on an MI355X):", "", "```", command,
              "```", "", "| kernel | calls | total us | avg us | % |", "|---|---|---|---|---|"]
     for name, calls, tot, avg, pct in trace_rows(db):
         lines.append(f"| `{short_name(name)}` | {calls} | {tot:.1f} | {avg:.2f} | {pct:.1f} |")
