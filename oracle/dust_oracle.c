@@ -31,6 +31,16 @@
  *      the einsum 'btd,bti->di' of "What the released code actually does",
  *      step 7).  Not divided by the token count.
  *
+ * A second scoring rule replaces the loss of steps 1-2 with a linear score
+ * against a supplied error estimate e_t of the layer's output ("What the
+ * released code actually does", step 4: attention internals are scored as
+ * c_s = -<g_s, Delta o_s> against the estimated output error, keys and
+ * values decayed by gamma = 0.98, queries with their own token's score).
+ * Reading used: the jittered output is the layer's own, Delta o_t^(i) =
+ * s_i sigma a_t^(n(i)), so the score of draw i at token t is
+ * rho_t^(i) = -<e_t, Delta o_t^(i)>, evaluated literally; steps 3-6 then
+ * run unchanged (dust_oracle_estimate_local).
+ *
  * Noise (the pages fix no generator; they name Philox as a counter-based
  * generator whose n-th output is a pure function of (seed, n): "Scaling To
  * Unfathomable Depth", section "MeZO", last paragraphs).  Reading used here:
@@ -149,6 +159,7 @@ void dust_oracle_noise_fill(uint64_t seed, int64_t n0, int64_t n_cnt,
 
 typedef struct {
   const float *X, *W, *target;
+  const float *E;         /* error estimate [T][d_out] (local scoring only) */
   int64_t T, d_in, d_out, seq_len;
   int32_t K;
   double sigma, gamma;
@@ -222,6 +233,37 @@ static void *phase_rho(void *p) {
         perturbed += 0.5 * e * e;
       }
       j->rho[lt * j->K + i] = j->loss[lt] - perturbed;
+    }
+  }
+  free(a);
+  return NULL;
+}
+
+/* Local scoring in place of steps 1-2: the jitter of draw i is the layer's
+ * own output change Delta o = s_i sigma a, scored against the error
+ * estimate e_t: rho_t^(i) = -<e_t, Delta o>. */
+static void *phase_score(void *p) {
+  worker_arg *wa = (worker_arg *)p;
+  oracle_job *j = wa->job;
+  int64_t n_tok = j->t_end - j->t_begin;
+  double *a = (double *)malloc(sizeof(double) * (size_t)j->d_out);
+  for (int64_t lt = wa->tid; lt < n_tok; lt += j->n_threads) {
+    int64_t t = j->t_begin + lt;
+    const float *e = j->E + t * j->d_out;
+    int32_t last_n = -1;
+    for (int32_t i = 0; i < j->K; ++i) {
+      int32_t n = noise_index(j, i);
+      if (n != last_n) {
+        noise_vector(j->seed, (uint32_t)n, (uint32_t)t, j->d_out, a);
+        last_n = n;
+      }
+      double s = draw_sign(j, i);
+      double score = 0.0;
+      for (int64_t c = 0; c < j->d_out; ++c) {
+        double delta_o = s * j->sigma * a[c];
+        score -= (double)e[c] * delta_o;
+      }
+      j->rho[lt * j->K + i] = score;
     }
   }
   free(a);
@@ -397,4 +439,58 @@ void dust_oracle_true_gradient(const float *X, const float *W,
         s += delta[t * d_out + c] * (double)X[t * d_in + k];
       G_true[c * d_in + k] = s;
     }
+}
+
+/*
+ * The estimator with local scoring over the sequences seq_begin..seq_end-1
+ * (0, 0 for all): E [T][d_out] is the supplied error estimate of the layer's
+ * output (fp32, as the GPU receives it); no forward and no loss.  Outputs as
+ * for dust_oracle_estimate, with rho[n_tok][K] holding the scores.  Returns
+ * 0, or -1 on an argument error.
+ */
+int dust_oracle_estimate_local(const float *X, const float *E, int64_t T,
+                               int64_t d_in, int64_t d_out, int64_t seq_len,
+                               int32_t K, float sigma, float gamma,
+                               uint64_t seed, int32_t antithetic,
+                               int64_t seq_begin, int64_t seq_end,
+                               int32_t n_threads, double *G, double *rho,
+                               double *reward, double *g) {
+  if (!X || !E || !G || !rho || !reward || !g) return -1;
+  if (T <= 0 || d_in <= 0 || d_out <= 0 || seq_len <= 0 || T % seq_len != 0)
+    return -1;
+  if (K < 2 || (antithetic && K % 2 != 0)) return -1;
+  int64_t n_seq = T / seq_len;
+  if (seq_end <= seq_begin) {
+    seq_begin = 0;
+    seq_end = n_seq;
+  }
+  if (seq_begin < 0 || seq_end > n_seq) return -1;
+  if (n_threads < 1) n_threads = 1;
+
+  oracle_job j;
+  memset(&j, 0, sizeof(j));
+  j.X = X;
+  j.E = E;
+  j.T = T;
+  j.d_in = d_in;
+  j.d_out = d_out;
+  j.seq_len = seq_len;
+  j.K = K;
+  j.sigma = (double)sigma;
+  j.gamma = (double)gamma;
+  j.seed = seed;
+  j.antithetic = antithetic;
+  j.t_begin = seq_begin * seq_len;
+  j.t_end = seq_end * seq_len;
+  j.n_threads = n_threads;
+  j.rho = rho;
+  j.reward = reward;
+  j.g = g;
+  j.G = G;
+
+  run_phase(&j, phase_score);
+  run_phase(&j, phase_credit);
+  run_phase(&j, phase_error);
+  run_phase(&j, phase_outer);
+  return 0;
 }

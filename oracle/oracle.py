@@ -51,6 +51,10 @@ def _load():
         ctypes.c_float, ctypes.c_uint64, ctypes.c_int32, i64, i64, ctypes.c_int32,
         f64p, f64p, f64p, f64p, f64p]
     lib.dust_oracle_estimate.restype = ctypes.c_int
+    lib.dust_oracle_estimate_local.argtypes = [
+        f32p, f32p, i64, i64, i64, i64, ctypes.c_int32, ctypes.c_float, ctypes.c_float,
+        ctypes.c_uint64, ctypes.c_int32, i64, i64, ctypes.c_int32, f64p, f64p, f64p, f64p]
+    lib.dust_oracle_estimate_local.restype = ctypes.c_int
     lib.dust_oracle_true_gradient.argtypes = [f32p, f32p, f32p, i64, i64, i64, f64p, f64p]
     lib.dust_oracle_true_gradient.restype = None
     _lib = lib
@@ -130,6 +134,37 @@ def estimate(X, W, target, *, K: int, sigma: float, gamma: float, seed: int,
         raise ValueError("oracle rejected its arguments")
     return {"G": G, "loss": loss, "rho": rho, "reward": reward, "g": g,
             "threads": th}
+
+
+def estimate_local(X, E, *, K: int, sigma: float, gamma: float, seed: int,
+                   antithetic: bool, seq_len: int, seq_range=None, threads: int | None = None):
+    """Run the fp64 oracle with local scoring: each draw's jitter of the
+    layer's output is scored against the error estimate E [T,d_out] (fp32)
+    instead of a loss.  X [T,d_in] as for :func:`estimate`.  Returns a dict
+    of fp64 arrays: G [d_out,d_in], rho [n,K] (the scores), reward [n,K],
+    g [n,d_out]."""
+    lib = _load()
+    X = np.ascontiguousarray(X, dtype=np.float32)
+    E = np.ascontiguousarray(E, dtype=np.float32)
+    T, d_in = X.shape
+    d_out = E.shape[1]
+    assert E.shape == (T, d_out) and T % seq_len == 0
+    n_seq = T // seq_len
+    s0, s1 = (0, n_seq) if seq_range is None else seq_range
+    n_tok = (s1 - s0) * seq_len
+    G = np.zeros((d_out, d_in), dtype=np.float64)
+    rho = np.zeros((n_tok, K), dtype=np.float64)
+    reward = np.zeros((n_tok, K), dtype=np.float64)
+    g = np.zeros((n_tok, d_out), dtype=np.float64)
+    th = default_threads() if threads is None else threads
+    rc = lib.dust_oracle_estimate_local(
+        _ptr(X, ctypes.c_float), _ptr(E, ctypes.c_float), T, d_in, d_out, seq_len, K,
+        ctypes.c_float(sigma), ctypes.c_float(gamma), ctypes.c_uint64(seed),
+        int(bool(antithetic)), s0, s1, th, _ptr(G, ctypes.c_double),
+        _ptr(rho, ctypes.c_double), _ptr(reward, ctypes.c_double), _ptr(g, ctypes.c_double))
+    if rc != 0:
+        raise ValueError("oracle rejected its arguments")
+    return {"G": G, "rho": rho, "reward": reward, "g": g, "threads": th}
 
 
 def true_gradient(X, W, target):
