@@ -4,7 +4,8 @@
 
 A step is one whole dust_estimate call (every stage: base GEMM, noise +
 loss change, centring and credit, reweighting, outer product) over one batch
-of synthetic inputs already resident in HBM.  The default workload is the
+of synthetic inputs already resident in HBM; for the local-scoring workloads
+(kv_local_bf16, q_local_bf16) one dust_estimate_local call.  The default workload is the
 "bf16 layer" (T = 4096 tokens in 8 sequences of 512, d_in = d_out = 512,
 K = 64 antithetic draws, sigma = 1e-2, gamma = 0).  Prints one JSON line:
 draw-token-rows per second (K*T per step), the ALU roofline of the dominant
@@ -61,8 +62,14 @@ def cpu_baseline(w, inp, budget_s: float):
     threads = min(16, oracle.default_threads())
     kw = dict(K=w.K, sigma=w.sigma, gamma=w.gamma, seed=w.noise_seed,
               antithetic=w.antithetic, seq_len=w.seq_len, threads=threads)
+    if w.local:
+        def run(seq_range):
+            oracle.estimate_local(inp["X"], inp["E"], seq_range=seq_range, **kw)
+    else:
+        def run(seq_range):
+            oracle.estimate(inp["X"], inp["W"], inp["target"], seq_range=seq_range, **kw)
     t0 = time.perf_counter()
-    oracle.estimate(inp["X"], inp["W"], inp["target"], seq_range=(0, 1), **kw)
+    run((0, 1))
     one = time.perf_counter() - t0
     n_seq = max(1, min(w.n_seq, int(budget_s / max(one, 1e-6))))
     # a whole workload that takes well under the budget is repeated, so the
@@ -72,7 +79,7 @@ def cpu_baseline(w, inp, budget_s: float):
         repeats = max(1, min(50, int(min(budget_s, 10.0) / max(one * n_seq, 1e-6))))
     t0 = time.perf_counter()
     for _ in range(repeats):
-        oracle.estimate(inp["X"], inp["W"], inp["target"], seq_range=(0, n_seq), **kw)
+        run((0, n_seq))
     elapsed = time.perf_counter() - t0
     rows = w.K * w.seq_len * n_seq * repeats
     what = (f"{n_seq} of {w.n_seq} sequences ({n_seq * w.seq_len} tokens x {w.K} draws) "
@@ -105,8 +112,12 @@ def main():
     dev = torch.device("cuda:0")
     inp = synth.make_inputs(w)
     tdt = torch.float32 if w.dtype == "f32" else torch.bfloat16
-    X, W, tg = (torch.from_numpy(inp[k]).to(dev).to(tdt).contiguous()
-                for k in ("X", "W", "target"))
+    X = torch.from_numpy(inp["X"]).to(dev).to(tdt).contiguous()
+    if w.local:
+        # local scoring: the draws are scored against the error estimate E
+        E = torch.from_numpy(inp["E"]).to(dev).contiguous()
+    else:
+        W, tg = (torch.from_numpy(inp[k]).to(dev).to(tdt).contiguous() for k in ("W", "target"))
     dt_code = dust.DUST_F32 if w.dtype == "f32" else dust.DUST_BF16
     ws = torch.empty(dust.dust_workspace_bytes(w.T, w.d_in, w.d_out, w.K, w.antithetic, dt_code),
                      dtype=torch.uint8, device=dev)
@@ -119,9 +130,14 @@ def main():
     cal_dst.copy_(cal_src)
     torch.cuda.synchronize(dev)
     del cal_src, cal_dst
+    def estimate(out):
+        if w.local:
+            return dust.dust_estimate_local(X, E, out=out, workspace=ws, **kw)
+        return dust.dust_estimate(X, W, tg, out=out, workspace=ws, **kw)
+
     out = {}
     for _ in range(args.warmup):
-        out = dust.dust_estimate(X, W, tg, out=out, workspace=ws, **kw)
+        out = estimate(out)
     torch.cuda.synchronize(dev)
     if not bool(torch.isfinite(out["G_W"]).all()):
         sys.exit("bench.py: non-finite G_W")
@@ -142,7 +158,7 @@ def main():
     wall0 = time.perf_counter()
     t_begin.record()
     for _ in range(args.steps):
-        dust.dust_estimate(X, W, tg, out=out, workspace=ws, **kw)
+        estimate(out)
     t_end.record()
     torch.cuda.synchronize(dev)
     wall = time.perf_counter() - wall0
@@ -160,7 +176,7 @@ def main():
     achieved = slots / (kernel_ms * 1e-3) / 1e12
     peak = roofline.PEAK_SLOTS_PER_S / 1e12
     result = {
-        "metric": "draw-token-rows/sec (K*T) for dust_estimate",
+        "metric": "draw-token-rows/sec (K*T) for " + ("dust_estimate_local" if w.local else "dust_estimate"),
         "value": value,
         "unit": "draw-token-rows/s",
         "n_gpus": 1,
@@ -172,7 +188,9 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
-        "data": "synthetic (seeded normal X, W, target; no dataset or trained weights)",
+        "data": ("synthetic (seeded normal X and error estimate E; no dataset or trained weights)"
+                 if w.local else
+                 "synthetic (seeded normal X, W, target; no dataset or trained weights)"),
         "config": {**w.describe(), "input_dtype": w.dtype, "parallelism": "none (1 GPU)"},
         "roofline": {
             "bound": "alu",

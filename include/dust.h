@@ -105,6 +105,46 @@ dust_status_t dust_estimate(const void* X, const void* W, const void* target,
                             void* stream);
 
 /*
+ * Host-side check of dust_estimate_local's arguments: the same rules as
+ * dust_validate, with X, E and G_W the required pointers (E 4-byte
+ * aligned).  No HIP call.
+ */
+dust_status_t dust_validate_local(const void* X, const float* E, int64_t T,
+                                  int64_t d_in, int64_t d_out, int64_t seq_len,
+                                  int32_t dtype, int32_t K, float sigma,
+                                  float gamma, int32_t antithetic,
+                                  const float* G_W, const void* workspace,
+                                  size_t workspace_bytes);
+
+/*
+ * The estimator with local scoring, for sites whose jitter never reaches the
+ * loss ("Dust: every token is a member of the population", section "What the
+ * released code actually does", step 4: attention internals are scored
+ * against the estimated error of their output, c_s = -<g_s, Delta o_s>;
+ * keys, values and gates sum later tokens' scores decayed by gamma = 0.98,
+ * queries keep their own token's score, gamma = 0).  Draw i jitters the
+ * layer's own output by Delta o_t^(i) = s_i sigma a_t^(n(i)) and is scored
+ * rho_t^(i) = -<E_t, Delta o_t^(i)>; centring, credit, g and
+ * G_W = sum_t g_t x_t^T follow as in dust_estimate.  E[g_t] = E_t with
+ * antithetic pairs ((K-1)/K E_t with plain draws); g does not depend on
+ * sigma.  Per-site gamma is this call's gamma.
+ *
+ * Inputs:
+ *   X  [T, d_in]   layer inputs, dtype `dtype`
+ *   E  [T, d_out]  fp32 error estimate of the layer's output
+ * Scalars, noise and workspace (dust_workspace_bytes) as for dust_estimate.
+ * Outputs (fp32, overwritten): G_W [d_out, d_in] required; rho [T, K] (the
+ * scores), reward [T, K] and g [T, d_out] optional (NULL to skip).
+ */
+dust_status_t dust_estimate_local(const void* X, const float* E, int64_t T,
+                                  int64_t d_in, int64_t d_out, int64_t seq_len,
+                                  int32_t dtype, int32_t K, float sigma,
+                                  float gamma, uint64_t seed,
+                                  int32_t antithetic, float* G_W, float* rho,
+                                  float* reward, float* g, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
+/*
  * Test hook: the noise the estimator uses, written out.  For noise indices
  * n0..n0+n_cnt-1 and tokens t0..t0+t_cnt-1:
  *   words [n_cnt, t_cnt, 4*ceil(d_out/4)] uint32  Philox words (optional)
@@ -117,13 +157,14 @@ dust_status_t dust_noise_fill(uint64_t seed, int64_t n0, int64_t n_cnt,
 
 /*
  * Measurement hook (used by the benchmark to time the dominant kernel with
- * HIP events inside its timed region).  After this call, dust_estimate call
- * number i records start[i % n_pairs] and stop[i % n_pairs] (hipEvent_t
- * values passed as void*, created and owned by the caller) on its stream
- * right before and right after its noise kernel: the single-generation
- * kernel when gamma = 0, else the jitter-loss kernel.  n_pairs = 0 turns the
- * hook off.  The pointer arrays are copied; the events must outlive their
- * use.  Process-wide state: not thread-safe.
+ * HIP events inside its timed region).  After this call, estimate call
+ * number i (dust_estimate or dust_estimate_local) has start[i % n_pairs] and
+ * stop[i % n_pairs] (hipEvent_t values passed as void*, created with timing
+ * enabled and owned by the caller) stamped by the dispatch of its noise
+ * kernel, the single-generation kernel when gamma = 0, else the jitter-loss
+ * kernel, at the kernel's start and end (hipExtLaunchKernelGGL's events).
+ * n_pairs = 0 turns the hook off.  The pointer arrays are copied; the events
+ * must outlive their use.  Process-wide state: not thread-safe.
  */
 dust_status_t dust_set_timing_events(void* const* start, void* const* stop,
                                      int32_t n_pairs);

@@ -35,7 +35,7 @@ def declared_entry_points():
 def test_every_declared_symbol_is_exported(lib):
     names = declared_entry_points()
     assert {"dust_estimate", "dust_validate", "dust_workspace_bytes", "dust_noise_fill",
-            "dust_last_error"} <= set(names)
+            "dust_last_error", "dust_estimate_local", "dust_validate_local"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
@@ -105,3 +105,31 @@ def test_python_binding_rejects_bad_tensors():
     with pytest.raises(ValueError):
         dust.dust_estimate(X, X, X, K=4, sigma=0.1, gamma=0.0, seed=0, antithetic=True,
                            seq_len=4)
+
+
+def _validate_local(**over):
+    args = dict(X=16, E=32, T=64, d_in=16, d_out=8, seq_len=16, dtype=dust.DUST_BF16,
+                K=4, sigma=0.2, gamma=0.98, antithetic=1, G=48, ws=64, ws_bytes=None)
+    args.update(over)
+    if args["ws_bytes"] is None:
+        args["ws_bytes"] = dust.dust_workspace_bytes(args["T"], args["d_in"], args["d_out"],
+                                                     args["K"], args["antithetic"],
+                                                     dust.DUST_BF16) or 1
+    return dust.dust_validate_local(args["X"], args["E"], args["T"], args["d_in"],
+                                    args["d_out"], args["seq_len"], args["dtype"], args["K"],
+                                    args["sigma"], args["gamma"], args["antithetic"],
+                                    args["G"], args["ws"], args["ws_bytes"])
+
+
+def test_validate_local_accepts_good_arguments(lib):
+    assert _validate_local() == 0
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(X=None), 1), (dict(E=None), 1), (dict(G=None), 1), (dict(E=34), 1),
+    (dict(T=0), 1), (dict(seq_len=5), 1), (dict(K=1), 1), (dict(K=5), 1),
+    (dict(sigma=0.0), 1), (dict(gamma=1.5), 1), (dict(dtype=7), 2),
+    (dict(T=1 << 24, seq_len=1), 2), (dict(ws=None), 3), (dict(ws_bytes=16), 3)])
+def test_validate_local_rejects(lib, over, status):
+    assert _validate_local(**over) == status
+    assert dust.dust_last_error() != ""

@@ -1,0 +1,150 @@
+"""Parity of the HIP local-scoring estimator (dust_estimate_local, through
+the C ABI) with the fp64 CPU oracle's local scoring.
+
+Local scoring ("What the released code actually does", step 4) jitters the
+layer's own output and scores each draw against a supplied error estimate
+E instead of a loss.  Tolerances as for dust_estimate: every stage (the
+scores rho, the credit r, the error estimate g) and G_W within relative
+Frobenius error 2e-3 for bf16 inputs and 1e-5 for the fp32 path.
+"""
+import numpy as np
+import pytest
+
+from token_activation_perturbation_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "bf16": 2e-3}
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import token_activation_perturbation_amd as dust
+    dust._load()
+    return torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module")
+def threads(oracle_mod):
+    return min(16, oracle_mod.default_threads())
+
+
+def rel(a, b):
+    nb = np.linalg.norm(b)
+    return np.linalg.norm(a - b) / (nb if nb > 0 else 1.0)
+
+
+def local_inputs(T, d_in, d_out, dtype, seed):
+    rng = np.random.default_rng(seed)
+    X = rng.standard_normal((T, d_in)).astype(np.float32)
+    if dtype == "bf16":
+        X = synth.bf16_round(X)
+    E = rng.standard_normal((T, d_out)).astype(np.float32)
+    return X, E
+
+
+def gpu_local(X, E, dtype, dev, E_offset=0, **kw):
+    import torch
+    import token_activation_perturbation_amd as dust
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    Xd = torch.from_numpy(X).to(dev).to(tdt).contiguous()
+    if E_offset:
+        flat = torch.zeros(E.size + E_offset, dtype=torch.float32, device=dev)
+        flat[E_offset:] = torch.from_numpy(E.ravel()).to(dev)
+        Ed = flat[E_offset:].view(E.shape)
+    else:
+        Ed = torch.from_numpy(E).to(dev).contiguous()
+    out = dust.dust_estimate_local(Xd, Ed, want_rho=True, want_reward=True, want_g=True, **kw)
+    torch.cuda.synchronize(dev)
+    return {k: v.cpu().numpy().astype(np.float64) for k, v in out.items()}
+
+
+def compare(got, ref, dtype, label, sl=slice(None)):
+    errs = {"rho": rel(got["rho"][sl], ref["rho"]), "reward": rel(got["reward"][sl], ref["reward"]),
+            "g": rel(got["g"][sl], ref["g"])}
+    if sl == slice(None):
+        errs["G_W"] = rel(got["G_W"], ref["G"])
+    print(label, " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
+    for k, v in errs.items():
+        assert v <= TOL[dtype], (k, v)
+
+
+SMALL = [
+    # T, seq_len, d_in, d_out, K, sigma, gamma, antithetic, dtype
+    (64, 16, 24, 40, 8, 0.2, 0.98, True, "bf16"),        # keys / values
+    (64, 16, 24, 40, 8, 0.2, 0.0, True, "bf16"),         # queries (single generation)
+    (130, 26, 45, 37, 10, 0.1, 0.5, False, "bf16"),      # ragged everything, plain draws
+    (96, 32, 72, 300, 34, 0.2, 0.98, True, "bf16"),      # K_n = 17, wide
+    (64, 64, 64, 64, 16, 1e-2, 0.0, False, "f32"),
+    (99, 33, 16, 24, 4, 0.3, 1.0, False, "f32"),         # suffix sums over 32 + 1 chunks
+    (40, 1, 24, 8, 2, 0.1, 0.98, True, "bf16"),          # one-token sequences, K = 2
+    (256, 128, 128, 1024, 64, 0.2, 0.98, True, "bf16"),  # d_out spans 4 quad rounds
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[f"T{c[0]}_dout{c[3]}_K{c[4]}_g{c[6]}_{c[8]}"
+                                             for c in SMALL])
+def test_local_stage_parity_small(dev, oracle_mod, threads, case):
+    T, seq_len, d_in, d_out, K, sigma, gamma, anti, dtype = case
+    print(f"local stage parity {case}", flush=True)
+    X, E = local_inputs(T, d_in, d_out, dtype, seed=T + d_out)
+    kw = dict(K=K, sigma=sigma, gamma=gamma, seed=T * 3 + 1, antithetic=anti, seq_len=seq_len)
+    got = gpu_local(X, E, dtype, dev, **kw)
+    ref = oracle_mod.estimate_local(X, E, threads=threads, **kw)
+    compare(got, ref, dtype, "  rel err")
+
+
+@pytest.mark.parametrize("name", ["kv_local_bf16", "q_local_bf16"])
+def test_local_workload_full_size_sampled(dev, oracle_mod, threads, name):
+    """Full-size run in the benchmarked launch configuration: the oracle
+    recomputes the last sequence (scores, credit, g); G_W is checked at full
+    size against G_W = sum_t g_t x_t^T formed in fp64 from the GPU's own g."""
+    w = synth.WORKLOADS[name]
+    print(f"local full-size sampled parity {name}", flush=True)
+    inp = synth.make_inputs(w)
+    kw = dict(K=w.K, sigma=w.sigma, gamma=w.gamma, seed=w.noise_seed, antithetic=w.antithetic,
+              seq_len=w.seq_len)
+    got = gpu_local(inp["X"], inp["E"], w.dtype, dev, **kw)
+    s = w.n_seq - 1
+    ref = oracle_mod.estimate_local(inp["X"], inp["E"], seq_range=(s, s + 1), threads=threads,
+                                    **kw)
+    compare(got, ref, w.dtype, f"  {name} (sequence {s})",
+            sl=slice(s * w.seq_len, (s + 1) * w.seq_len))
+    G_from_g = got["g"].T @ inp["X"].astype(np.float64)
+    e = rel(got["G_W"], G_from_g)
+    print(f"  G_W vs g^T X {e:.2e}", flush=True)
+    assert e <= TOL[w.dtype]
+
+
+def test_local_misaligned_error_estimate(dev, oracle_mod, threads):
+    """E starting one float into its storage (4-byte but not 16-byte
+    aligned): the noise kernels take the element-wise loads."""
+    X, E = local_inputs(96, 32, 48, "bf16", seed=17)
+    for gamma in (0.0, 0.98):
+        kw = dict(K=8, sigma=0.2, gamma=gamma, seed=4, antithetic=False, seq_len=32)
+        got = gpu_local(X, E, "bf16", dev, E_offset=1, **kw)
+        ref = oracle_mod.estimate_local(X, E, threads=threads, **kw)
+        compare(got, ref, "bf16", f"  misaligned E, gamma {gamma}")
+
+
+def test_local_does_not_depend_on_sigma(dev):
+    """On the GPU too: the score is linear in the jitter, so sigma cancels
+    up to fp32 rounding."""
+    X, E = local_inputs(128, 64, 96, "bf16", seed=23)
+    kw = dict(K=16, gamma=0.98, seed=9, antithetic=True, seq_len=64)
+    a = gpu_local(X, E, "bf16", dev, sigma=0.01, **kw)
+    b = gpu_local(X, E, "bf16", dev, sigma=0.5, **kw)
+    assert rel(a["G_W"], b["G_W"]) <= 1e-5
+    assert rel(a["g"], b["g"]) <= 1e-5
+
+
+def test_local_bitwise_deterministic(dev):
+    X, E = local_inputs(1024, 128, 256, "bf16", seed=29)
+    kw = dict(K=32, sigma=0.2, gamma=0.98, seed=5, antithetic=True, seq_len=512)
+    a = gpu_local(X, E, "bf16", dev, **kw)
+    b = gpu_local(X, E, "bf16", dev, **kw)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k

@@ -12,8 +12,8 @@ import ctypes
 import os
 
 __all__ = ["DustError", "dust_workspace_bytes", "dust_validate", "dust_estimate",
-           "dust_noise_fill", "dust_set_timing_events", "dust_last_error", "library_path",
-           "DUST_F32", "DUST_BF16"]
+           "dust_validate_local", "dust_estimate_local", "dust_noise_fill",
+           "dust_set_timing_events", "dust_last_error", "library_path", "DUST_F32", "DUST_BF16"]
 
 DUST_F32 = 0
 DUST_BF16 = 1
@@ -52,6 +52,12 @@ def _load():
     lib.dust_estimate.argtypes = [vp, vp, vp, i64, i64, i64, i64, i32, i32, f32, f32,
                                   ctypes.c_uint64, i32, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.dust_estimate.restype = ctypes.c_int
+    lib.dust_validate_local.argtypes = [vp, vp, i64, i64, i64, i64, i32, i32, f32, f32, i32,
+                                        vp, vp, sz]
+    lib.dust_validate_local.restype = ctypes.c_int
+    lib.dust_estimate_local.argtypes = [vp, vp, i64, i64, i64, i64, i32, i32, f32, f32,
+                                        ctypes.c_uint64, i32, vp, vp, vp, vp, vp, sz, vp]
+    lib.dust_estimate_local.restype = ctypes.c_int
     lib.dust_noise_fill.argtypes = [ctypes.c_uint64, i64, i64, i64, i64, i64, vp, vp, vp]
     lib.dust_noise_fill.restype = ctypes.c_int
     vpp = ctypes.POINTER(ctypes.c_void_p)
@@ -83,6 +89,14 @@ def dust_validate(X_ptr, W_ptr, target_ptr, T, d_in, d_out, seq_len, dtype, K, s
     return int(_load().dust_validate(X_ptr, W_ptr, target_ptr, T, d_in, d_out, seq_len, dtype,
                                      K, sigma, gamma, int(bool(antithetic)), G_ptr,
                                      workspace_ptr, workspace_bytes))
+
+
+def dust_validate_local(X_ptr, E_ptr, T, d_in, d_out, seq_len, dtype, K, sigma, gamma,
+                        antithetic, G_ptr, workspace_ptr, workspace_bytes) -> int:
+    """Raw host-side validation of dust_estimate_local's arguments; returns the status."""
+    return int(_load().dust_validate_local(X_ptr, E_ptr, T, d_in, d_out, seq_len, dtype, K,
+                                           sigma, gamma, int(bool(antithetic)), G_ptr,
+                                           workspace_ptr, workspace_bytes))
 
 
 def _dtype_code(t) -> int:
@@ -157,6 +171,60 @@ def dust_estimate(X, W, target, *, K: int, sigma: float, gamma: float, seed: int
     return res
 
 
+def dust_estimate_local(X, E, *, K: int, sigma: float, gamma: float, seed: int,
+                        antithetic: bool, seq_len: int, want_rho: bool = False,
+                        want_reward: bool = False, want_g: bool = False,
+                        out: dict | None = None, workspace=None):
+    """Enqueue dust_estimate_local (local scoring against the error estimate
+    E) on the current stream of X's device.
+
+    X [T,d_in] (bfloat16 or float32) and E [T,d_out] (float32): contiguous
+    device tensors.  Returns a dict of fp32 device tensors: "G_W" [d_out,d_in]
+    and the requested optional outputs "rho" [T,K] (the scores), "reward"
+    [T,K], "g" [T,d_out].  ``out`` and ``workspace`` as for dust_estimate.
+    """
+    import torch
+    for name, t in (("X", X), ("E", E)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    if E.dtype != torch.float32:
+        raise TypeError("E must be float32")
+    if X.dim() != 2 or E.dim() != 2 or X.shape[0] != E.shape[0]:
+        raise ValueError(f"shape mismatch: X {tuple(X.shape)}, E {tuple(E.shape)}")
+    T, d_in = X.shape
+    d_out = E.shape[1]
+    dt = _dtype_code(X)
+    dev = X.device
+    res = dict(out or {})
+
+    def _get(name, shape):
+        t = res.get(name)
+        if t is None:
+            t = torch.empty(shape, dtype=torch.float32, device=dev)
+            res[name] = t
+        elif (tuple(t.shape) != tuple(shape) or t.dtype != torch.float32 or not t.is_contiguous()
+              or t.device != dev):
+            raise ValueError(f"out[{name!r}] must be a contiguous float32 {tuple(shape)} "
+                             f"tensor on {dev}")
+        return t
+
+    G = _get("G_W", (d_out, d_in))
+    rho = _get("rho", (T, K)) if want_rho else None
+    reward = _get("reward", (T, K)) if want_reward else None
+    g = _get("g", (T, d_out)) if want_g else None
+    need = dust_workspace_bytes(T, d_in, d_out, K, antithetic, dt)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    ptr = lambda t: None if t is None else t.data_ptr()  # noqa: E731
+    status = _load().dust_estimate_local(
+        X.data_ptr(), E.data_ptr(), T, d_in, d_out, seq_len, dt, K, sigma, gamma,
+        ctypes.c_uint64(seed & 0xFFFFFFFFFFFFFFFF), int(bool(antithetic)), G.data_ptr(),
+        ptr(rho), ptr(reward), ptr(g), workspace.data_ptr(), workspace.numel(),
+        _stream_ptr(dev))
+    _check(status)
+    return res
+
+
 def dust_noise_fill(seed: int, n0: int, n_cnt: int, t0: int, t_cnt: int, d_out: int, *,
                     words: bool = True, gauss: bool = True, device="cuda"):
     """The estimator's noise written out: words [n_cnt,t_cnt,4*ceil(d_out/4)]
@@ -176,9 +244,9 @@ def dust_noise_fill(seed: int, n0: int, n_cnt: int, t0: int, t_cnt: int, d_out: 
 
 def dust_set_timing_events(starts, stops) -> None:
     """Register event pairs (torch.cuda.Event with enable_timing=True, already
-    recorded once so their HIP events exist) that the next dust_estimate calls
-    record around their noise kernel, pair i on call i.  Pass empty lists to
-    turn the hook off."""
+    recorded once so their HIP events exist) that the dispatch of the next
+    estimate calls' noise kernel stamps at its start and end, pair i on call
+    i.  Pass empty lists to turn the hook off."""
     n = len(starts)
     if len(stops) != n:
         raise ValueError("starts and stops must have the same length")

@@ -40,15 +40,16 @@ size_t dust_workspace_bytes(int64_t T, int64_t d_in, int64_t d_out, int32_t K,
   return p.total;
 }
 
-dust_status_t dust_validate(const void* X, const void* W, const void* target,
-                            int64_t T, int64_t d_in, int64_t d_out,
-                            int64_t seq_len, int32_t dtype, int32_t K,
-                            float sigma, float gamma, int32_t antithetic,
-                            const float* G_W, const void* workspace,
-                            size_t workspace_bytes) {
+}  // extern "C"
+
+namespace {
+
+// The checks both estimators share (everything but their own pointers).
+dust_status_t validate_common(int64_t T, int64_t d_in, int64_t d_out, int64_t seq_len,
+                              int32_t dtype, int32_t K, float sigma, float gamma,
+                              int32_t antithetic, const void* workspace,
+                              size_t workspace_bytes) {
   using dust::fail;
-  if (!X || !W || !target || !G_W)
-    return fail(DUST_ERR_INVALID_ARG, "X, W, target and G_W must not be NULL");
   if (T <= 0 || d_in <= 0 || d_out <= 0)
     return fail(DUST_ERR_INVALID_ARG, "T=%lld, d_in=%lld, d_out=%lld must be positive",
                 (long long)T, (long long)d_in, (long long)d_out);
@@ -76,6 +77,35 @@ dust_status_t dust_validate(const void* X, const void* W, const void* target,
     return fail(DUST_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed",
                 workspace ? workspace_bytes : (size_t)0, p.total);
   return dust::ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+dust_status_t dust_validate(const void* X, const void* W, const void* target,
+                            int64_t T, int64_t d_in, int64_t d_out,
+                            int64_t seq_len, int32_t dtype, int32_t K,
+                            float sigma, float gamma, int32_t antithetic,
+                            const float* G_W, const void* workspace,
+                            size_t workspace_bytes) {
+  if (!X || !W || !target || !G_W)
+    return dust::fail(DUST_ERR_INVALID_ARG, "X, W, target and G_W must not be NULL");
+  return validate_common(T, d_in, d_out, seq_len, dtype, K, sigma, gamma, antithetic,
+                         workspace, workspace_bytes);
+}
+
+dust_status_t dust_validate_local(const void* X, const float* E, int64_t T, int64_t d_in,
+                                  int64_t d_out, int64_t seq_len, int32_t dtype, int32_t K,
+                                  float sigma, float gamma, int32_t antithetic,
+                                  const float* G_W, const void* workspace,
+                                  size_t workspace_bytes) {
+  if (!X || !E || !G_W)
+    return dust::fail(DUST_ERR_INVALID_ARG, "X, E and G_W must not be NULL");
+  if ((uintptr_t)E % 4 != 0)
+    return dust::fail(DUST_ERR_INVALID_ARG, "E must be 4-byte aligned (fp32)");
+  return validate_common(T, d_in, d_out, seq_len, dtype, K, sigma, gamma, antithetic,
+                         workspace, workspace_bytes);
 }
 
 const char* dust_last_error(void) { return g_last_error; }

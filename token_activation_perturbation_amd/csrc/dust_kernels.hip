@@ -201,8 +201,8 @@ __device__ __forceinline__ float wave_sum(float v) {
 // and Q_n = ||a_t^n||^2, then one wave reduction yields the 16 totals.
 
 __global__ __launch_bounds__(256) void jitter_loss_kernel(
-    const float* __restrict__ delta, int32_t T, int32_t d_out, int32_t nq, int32_t K_n,
-    int32_t chunks, int32_t per_chunk, NoiseKey key, float* __restrict__ P,
+    const float* __restrict__ delta, int32_t vec, int32_t T, int32_t d_out, int32_t nq,
+    int32_t K_n, int32_t chunks, int32_t per_chunk, NoiseKey key, float* __restrict__ P,
     float* __restrict__ Q, float* __restrict__ loss_clean) {
   const int lane = threadIdx.x & 63;
   const int64_t task = (int64_t)blockIdx.x * 4 + wave_id();
@@ -212,7 +212,7 @@ __global__ __launch_bounds__(256) void jitter_loss_kernel(
   const int32_t n_begin = chunk * per_chunk;
   const int32_t n_end = min(K_n, n_begin + per_chunk);
   const float* drow = delta + (int64_t)t * d_out;
-  const bool ragged = (d_out & 3) != 0;
+  const bool ragged = !vec;  // vec: d_out % 4 == 0 and delta 16-byte aligned
 
   if (chunk == 0 && loss_clean) {
     float s = 0.f;
@@ -280,16 +280,19 @@ __global__ __launch_bounds__(256) void jitter_loss_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Per-token loss reductions of every draw and their mean over the K draws.
-// One wave per token.
+// Per-token loss reductions of every draw, rho = -s sigma P - curv Q, and
+// their mean over the K draws.  curv = sigma^2 / 2 for the quadratic loss;
+// 0 for local scoring, whose score -<e, s sigma a> = -s sigma P is linear in
+// the jitter.  One wave per token.
 
 __global__ __launch_bounds__(256) void token_stats_kernel(
     const float* __restrict__ P, const float* __restrict__ Q, int32_t T, int32_t K, int32_t K_n,
-    int32_t antithetic, float sigma, float* __restrict__ rho, float* __restrict__ mean) {
+    int32_t antithetic, float sigma, float curv_coef, float* __restrict__ rho,
+    float* __restrict__ mean) {
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + wave_id();
   if (t >= T) return;
-  const float half_s2 = 0.5f * sigma * sigma;
+  const float half_s2 = curv_coef;
   float sum = 0.f;
   for (int32_t n = lane; n < K_n; n += 64) {
     const float pn = P[t * K_n + n];
@@ -624,7 +627,9 @@ __global__ __launch_bounds__(256) void split_sum_kernel(const float* __restrict_
 //       = -1/(K sigma) (sum_n rho_n a^n - mean(rho) sum_n a^n)     plain draws
 //       = (2/K) sum_n P_n a^n                                       antithetic
 // (in an antithetic pair rho_(2n) - rho_(2n+1) = -2 sigma P_n: the curvature
-// term and the centring cancel exactly).  So each noise vector is generated
+// term and the centring cancel exactly), with rho_n = -sigma P_n - curv Q_n,
+// curv = sigma^2 / 2 for the quadratic loss and 0 for local scoring (delta
+// is then the supplied error estimate).  So each noise vector is generated
 // once: a batch of NB noise vectors stays in registers while the wave
 // reduces their P_n = <delta_t, a^n> and Q_n = ||a^n||^2, and is then
 // weighted at once.  One workgroup per token; its waves split the noise
@@ -712,7 +717,7 @@ __device__ __forceinline__ void wave_reduce_to_scalars(float (&v)[M], int lane, 
 template <int QPL, bool ANTI, bool FULL>
 __global__ __launch_bounds__(256) void fused_g0_kernel(
     const float* __restrict__ delta, int32_t t0, int32_t T, int32_t d_out, int32_t nq,
-    int32_t K, int32_t K_n, int32_t per_wave, float sigma, NoiseKey key,
+    int32_t K, int32_t K_n, int32_t per_wave, float sigma, float curv_coef, NoiseKey key,
     float* __restrict__ Pout, float* __restrict__ Qout, float* __restrict__ loss_clean,
     float* __restrict__ g32, uint16_t* __restrict__ g_hi, uint16_t* __restrict__ g_lo) {
   constexpr int NB = QPL <= 2 ? DUST_FUSED_NB_SMALL : (QPL <= 4 ? 2 : 1);
@@ -760,7 +765,7 @@ __global__ __launch_bounds__(256) void fused_g0_kernel(
     if (lane == 0) loss_clean[t] = 0.5f * s;
   }
 
-  const float half_s2 = 0.5f * sigma * sigma;
+  const float half_s2 = curv_coef;
   float rsum = 0.f;
   for (int32_t nb = n_begin; nb < n_end; nb += NB) {
     float4 a[NB][QPL];
@@ -908,12 +913,12 @@ template <int QPL>
 void launch_fused_g0_qpl(bool anti, bool full, unsigned blocks, unsigned threads,
                          hipStream_t s, TimedLaunch tl, const float* delta, int32_t t0,
                          int32_t T, int32_t d_out, int32_t nq, int32_t K, int32_t K_n,
-                         int32_t per_wave, float sigma, NoiseKey key, float* P, float* Q,
-                         float* loss, float* g32, uint16_t* g_hi, uint16_t* g_lo) {
+                         int32_t per_wave, float sigma, float curv, NoiseKey key, float* P,
+                         float* Q, float* loss, float* g32, uint16_t* g_hi, uint16_t* g_lo) {
 #define DUST_FUSED_LAUNCH(A, F)                                                               \
   hipExtLaunchKernelGGL((fused_g0_kernel<QPL, A, F>), dim3(blocks), dim3(threads), 0, s,      \
                         tl.start, tl.stop, 0, delta, t0, T, d_out, nq, K, K_n, per_wave, sigma, \
-                        key, P, Q, loss, g32, g_hi, g_lo)
+                        curv, key, P, Q, loss, g32, g_hi, g_lo)
   if (anti && full)
     DUST_FUSED_LAUNCH(true, true);
   else if (anti)
@@ -937,12 +942,12 @@ inline int fused_qpl(int32_t nq) {
 void launch_fused_g0(int qpl, bool anti, bool full, unsigned blocks, unsigned threads,
                      hipStream_t s, TimedLaunch tl, const float* delta, int32_t t0,
                      int32_t T, int32_t d_out, int32_t nq, int32_t K, int32_t K_n,
-                     int32_t per_wave, float sigma, NoiseKey key, float* P, float* Q,
-                     float* loss, float* g32, uint16_t* g_hi, uint16_t* g_lo) {
+                     int32_t per_wave, float sigma, float curv, NoiseKey key, float* P,
+                     float* Q, float* loss, float* g32, uint16_t* g_hi, uint16_t* g_lo) {
 #define DUST_FUSED_CASE(V)                                                                   \
   case V:                                                                                    \
     launch_fused_g0_qpl<V>(anti, full, blocks, threads, s, tl, delta, t0, T, d_out, nq, K,   \
-                           K_n, per_wave, sigma, key, P, Q, loss, g32, g_hi, g_lo);          \
+                           K_n, per_wave, sigma, curv, key, P, Q, loss, g32, g_hi, g_lo);    \
     break;
   switch (qpl) {
     DUST_FUSED_CASE(1)
@@ -959,6 +964,12 @@ void launch_fused_g0(int qpl, bool anti, bool full, unsigned blocks, unsigned th
 #undef DUST_FUSED_CASE
 }
 
+// Register stages of the outer product's load pipeline (even; a build may
+// override it with -DDUST_TN_STAGES=n).
+#ifndef DUST_TN_STAGES
+#define DUST_TN_STAGES 4
+#endif
+
 inline NoiseKey make_key(uint64_t seed) {
   return NoiseKey{(uint32_t)(seed & 0xFFFFFFFFull), (uint32_t)(seed >> 32)};
 }
@@ -967,26 +978,26 @@ inline unsigned grid_for(int64_t items, int64_t per_block) {
   return (unsigned)ceil_div(items, per_block);
 }
 
-}  // namespace
-}  // namespace dust
-
-extern "C" {
-
-dust_status_t dust_estimate(const void* X, const void* W, const void* target, int64_t T,
-                            int64_t d_in, int64_t d_out, int64_t seq_len, int32_t dtype,
-                            int32_t K, float sigma, float gamma, uint64_t seed,
-                            int32_t antithetic, float* G_W, float* loss_clean, float* rho,
-                            float* reward, float* g, void* workspace, size_t workspace_bytes,
-                            void* stream) {
-  using namespace dust;
-  dust_status_t st = dust_validate(X, W, target, T, d_in, d_out, seq_len, dtype, K, sigma,
-                                   gamma, antithetic, G_W, workspace, workspace_bytes);
-  if (st != DUST_OK) return st;
+// Both estimators after validation.  E == nullptr: the layer-local loss
+// (delta = W x - target from the base GEMM, rho the loss reductions).
+// E != nullptr: local scoring (delta = E, the supplied error estimate; no
+// base GEMM; rho the linear scores, no curvature term; no clean loss).
+dust_status_t run_estimate(const void* X, const void* W, const void* target, const float* E,
+                           int64_t T, int64_t d_in, int64_t d_out, int64_t seq_len,
+                           int32_t dtype, int32_t K, float sigma, float gamma, uint64_t seed,
+                           int32_t antithetic, float* G_W, float* loss_clean, float* rho,
+                           float* reward, float* g, void* workspace, void* stream) {
+  const bool local = E != nullptr;
   Plan p;
   make_plan(T, d_in, d_out, K, antithetic, dtype, &p);
   hipStream_t s = (hipStream_t)stream;
   char* ws = (char*)workspace;
-  float* delta = (float*)(ws + p.off_delta);
+  float* delta = local ? const_cast<float*>(E) : (float*)(ws + p.off_delta);
+  if (local) loss_clean = nullptr;
+  // rho's curvature term: sigma^2 / 2 for the quadratic loss, none for the
+  // linear local score
+  const float curv = local ? 0.0f : 0.5f * sigma * sigma;
+  const bool delta_vec = (d_out % 4 == 0) && ((uintptr_t)delta % 16 == 0);
   float* Pbuf = (float*)(ws + p.off_P);
   float* Qbuf = (float*)(ws + p.off_Q);
   float* rho_buf = rho ? rho : (float*)(ws + p.off_rho);
@@ -1004,7 +1015,9 @@ dust_status_t dust_estimate(const void* X, const void* W, const void* target, in
   const int32_t Ti = (int32_t)T, di = (int32_t)d_in, dout = (int32_t)d_out;
 
   // 1. base GEMM -> delta
-  if (dtype == DUST_BF16) {
+  if (local) {
+    // delta is the caller's error estimate
+  } else if (dtype == DUST_BF16) {
     const bool vec = (d_in % 8 == 0) && ((uintptr_t)X % 16 == 0) && ((uintptr_t)W % 16 == 0);
     const int tiles_m = (int)ceil_div(T, 64), tiles_n = (int)ceil_div(d_out, 64);
     const int per_xcd = (int)ceil_div((int64_t)tiles_m * tiles_n, 8);
@@ -1034,12 +1047,13 @@ dust_status_t dust_estimate(const void* X, const void* W, const void* target, in
   if (!fused) {
     // 2. jitter + loss change
     hipExtLaunchKernelGGL(jitter_loss_kernel, dim3(grid_for(T * p.jl_chunks, 4)), dim3(256), 0, s,
-                          tl.start, tl.stop, 0, (const float*)delta, Ti, dout, p.nq, p.K_n,
-                          p.jl_chunks, p.jl_per_chunk, key, Pbuf, Qbuf, loss_clean);
+                          tl.start, tl.stop, 0, (const float*)delta, (int32_t)delta_vec, Ti,
+                          dout, p.nq, p.K_n, p.jl_chunks, p.jl_per_chunk, key, Pbuf, Qbuf,
+                          loss_clean);
     // 3. loss reductions and their mean over draws
     hipLaunchKernelGGL(token_stats_kernel, dim3(grid_for(T, 4)), dim3(256), 0, s,
                        (const float*)Pbuf, (const float*)Qbuf, Ti, K, p.K_n, p.antithetic, sigma,
-                       rho_buf, mean);
+                       curv, rho_buf, mean);
     // 4. centring + discounted credit -> per-(t, n) weights
     if (independent) {
       hipLaunchKernelGGL(credit_token_kernel, dim3(grid_for(T * p.K_n, 256)), dim3(256), 0, s,
@@ -1066,15 +1080,15 @@ dust_status_t dust_estimate(const void* X, const void* W, const void* target, in
   // 5. g: the fused single-generation kernel (and P, Q when the loss
   //    reductions or the credit are requested), or the reweight kernel
   if (fused) {
-    const bool full = (p.nq == 64 * qpl) && (d_out % 4 == 0);
+    const bool full = (p.nq == 64 * qpl) && delta_vec;
     launch_fused_g0(qpl, p.antithetic != 0, full, (unsigned)T, (unsigned)(64 * p.fz_waves), s,
                     tl, (const float*)delta, 0, Ti, dout, p.nq, K, p.K_n, p.fz_per_wave, sigma,
-                    key, want_pq ? Pbuf : nullptr, want_pq ? Qbuf : nullptr, loss_clean, g32,
+                    curv, key, want_pq ? Pbuf : nullptr, want_pq ? Qbuf : nullptr, loss_clean, g32,
                     g_hi, g_lo);
     if (want_pq) {
       hipLaunchKernelGGL(token_stats_kernel, dim3(grid_for(T, 4)), dim3(256), 0, s,
                          (const float*)Pbuf, (const float*)Qbuf, Ti, K, p.K_n, p.antithetic,
-                         sigma, rho_buf, mean);
+                         sigma, curv, rho_buf, mean);
       hipLaunchKernelGGL(credit_token_kernel, dim3(grid_for(T * p.K_n, 256)), dim3(256), 0, s,
                          (const float*)rho_buf, (const float*)mean, Ti, K, p.K_n, p.antithetic,
                          sigma, reward, wgt);
@@ -1096,13 +1110,13 @@ dust_status_t dust_estimate(const void* X, const void* W, const void* target, in
     const dim3 grid((unsigned)(8 * per_xcd));
     const int32_t partial = p.outer_split > 1 ? 1 : 0;
     if (vec)
-      hipLaunchKernelGGL((gemm::tn_outer_kernel<4, true>), grid, dim3(256), 0, s,
+      hipLaunchKernelGGL((gemm::tn_outer_kernel<DUST_TN_STAGES, true>), grid, dim3(256), 0, s,
                          (const uint16_t*)g_hi, (const uint16_t*)g_lo, (const uint16_t*)X, Ti,
                          dout, di, tiles_m, tiles_n,
                          p.outer_split, per_xcd, (int64_t)0, (int64_t)p.outer_tokens, partial,
                          dst);
     else
-      hipLaunchKernelGGL((gemm::tn_outer_kernel<4, false>), grid, dim3(256), 0, s,
+      hipLaunchKernelGGL((gemm::tn_outer_kernel<DUST_TN_STAGES, false>), grid, dim3(256), 0, s,
                          (const uint16_t*)g_hi, (const uint16_t*)g_lo, (const uint16_t*)X, Ti,
                          dout, di, tiles_m, tiles_n,
                          p.outer_split, per_xcd, (int64_t)0, (int64_t)p.outer_tokens, partial,
@@ -1122,6 +1136,41 @@ dust_status_t dust_estimate(const void* X, const void* W, const void* target, in
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(DUST_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return ok();
+}
+
+}  // namespace
+}  // namespace dust
+
+extern "C" {
+
+
+dust_status_t dust_estimate(const void* X, const void* W, const void* target, int64_t T,
+                            int64_t d_in, int64_t d_out, int64_t seq_len, int32_t dtype,
+                            int32_t K, float sigma, float gamma, uint64_t seed,
+                            int32_t antithetic, float* G_W, float* loss_clean, float* rho,
+                            float* reward, float* g, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  const dust_status_t st = dust_validate(X, W, target, T, d_in, d_out, seq_len, dtype, K,
+                                         sigma, gamma, antithetic, G_W, workspace,
+                                         workspace_bytes);
+  if (st != DUST_OK) return st;
+  return dust::run_estimate(X, W, target, nullptr, T, d_in, d_out, seq_len, dtype, K, sigma,
+                            gamma, seed, antithetic, G_W, loss_clean, rho, reward, g, workspace,
+                            stream);
+}
+
+dust_status_t dust_estimate_local(const void* X, const float* E, int64_t T, int64_t d_in,
+                                  int64_t d_out, int64_t seq_len, int32_t dtype, int32_t K,
+                                  float sigma, float gamma, uint64_t seed, int32_t antithetic,
+                                  float* G_W, float* rho, float* reward, float* g,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  const dust_status_t st = dust_validate_local(X, E, T, d_in, d_out, seq_len, dtype, K, sigma,
+                                               gamma, antithetic, G_W, workspace,
+                                               workspace_bytes);
+  if (st != DUST_OK) return st;
+  return dust::run_estimate(X, nullptr, nullptr, E, T, d_in, d_out, seq_len, dtype, K, sigma,
+                            gamma, seed, antithetic, G_W, nullptr, rho, reward, g, workspace,
+                            stream);
 }
 
 dust_status_t dust_set_timing_events(void* const* start, void* const* stop, int32_t n_pairs) {

@@ -1,13 +1,14 @@
 """Seeded synthetic inputs for the Dust estimator of one linear layer.
 
 This module holds no arithmetic of the estimator: it only draws X, W and
-target with the shapes and distributions of the five workloads below, and
-rounds them to the input dtype.  The pages train on FineWeb with a 37.7M
-parameter GPT whose layers are 512 wide ("Dust: every token is a member of the
-population", sections "What the released code actually does" and "The results,
-checked against the tables"); neither the data nor the weights are available,
-so these draws stand in for that layer's inputs, and the layer-local squared
-error stands in for the network.
+target (or, for local scoring, X and an error estimate E) with the shapes and
+distributions of the workloads below, and rounds them to the input dtype.
+The pages train on FineWeb with a 37.7M parameter GPT whose layers are 512
+wide ("Dust: every token is a member of the population", sections "What the
+released code actually does" and "The results, checked against the tables");
+neither the data nor the weights are available, so these draws stand in for
+that layer's inputs, and the layer-local squared error (or the supplied error
+estimate) stands in for the network.
 
 Recipe: numpy ``default_rng(data_seed)`` (PCG64) standard normals in fp64,
 scaled, cast to fp32 (round to nearest even) and, for bf16 workloads, rounded
@@ -35,7 +36,13 @@ class Workload:
     dtype: str          # "f32" or "bf16"
     data_seed: int
     noise_seed: int
-    target_kind: str    # "iid" (target ~ N(0,1)) or "teacher" (bf16(X W'^T))
+    target_kind: str    # "iid" (target ~ N(0,1)), "teacher" (bf16(X W'^T)),
+                        # or "local": scored against an error estimate
+                        # E ~ N(0,1) (fp32) instead of a loss
+
+    @property
+    def local(self) -> bool:
+        return self.target_kind == "local"
 
     @property
     def n_seq(self) -> int:
@@ -60,10 +67,16 @@ WORKLOADS = {
         Workload("mlp_up_bf16", 16384, 512, 768, 3072, 256, 5e-3, 0.0, True, "bf16", 1003, 0, "teacher"),
         Workload("qkv_credit_bf16", 8192, 1024, 1024, 3072, 128, 1e-2, 0.9, False, "bf16", 1004, 0, "iid"),
         Workload("large_population_bf16", 2048, 1024, 1024, 1024, 4096, 1e-2, 0.5, True, "bf16", 1005, 0, "iid"),
+        # Local scoring of attention internals ("What the released code
+        # actually does", step 4) in the pages' 512-wide model and batches of
+        # 8 sequences x 2048 tokens: keys / values (credit decay 0.98) and
+        # queries (own token's score only).
+        Workload("kv_local_bf16", 16384, 2048, 512, 512, 64, 0.2, 0.98, True, "bf16", 1006, 0, "local"),
+        Workload("q_local_bf16", 16384, 2048, 512, 512, 64, 0.2, 0.0, True, "bf16", 1007, 0, "local"),
     ]
 }
 WORKLOAD_ORDER = ["tiny_f32", "bf16_layer", "mlp_up_bf16", "qkv_credit_bf16",
-                  "large_population_bf16"]
+                  "large_population_bf16", "kv_local_bf16", "q_local_bf16"]
 
 
 def bf16_round(x: np.ndarray) -> np.ndarray:
@@ -91,12 +104,15 @@ def _round(x64: np.ndarray, dtype: str) -> np.ndarray:
 def make_inputs(w: Workload, T: int | None = None, d_in: int | None = None,
                 d_out: int | None = None, data_seed: int | None = None) -> dict:
     """X [T,d_in], W [d_out,d_in], target [T,d_out] as fp32 arrays holding the
-    exact input values.  Sizes and seed default to the workload's."""
+    exact input values; for a local-scoring workload X and E [T,d_out] (fp32)
+    instead.  Sizes and seed default to the workload's."""
     T = w.T if T is None else T
     d_in = w.d_in if d_in is None else d_in
     d_out = w.d_out if d_out is None else d_out
     rng = np.random.default_rng(w.data_seed if data_seed is None else data_seed)
     X = _round(rng.standard_normal((T, d_in)), w.dtype)
+    if w.local:
+        return {"X": X, "E": rng.standard_normal((T, d_out)).astype(np.float32)}
     W = _round(rng.standard_normal((d_out, d_in)) / np.sqrt(d_in), w.dtype)
     if w.target_kind == "teacher":
         # W' = W + E with E ~ N(0, 0.01) read as variance 0.01 (std 0.1).
