@@ -2,12 +2,18 @@
 
     python -m token_activation_perturbation_amd.profiling trace <results.db> <title> <command>
     python -m token_activation_perturbation_amd.profiling pmc <fetch.db> <write.db> <kernel> <copy_bytes>
+    python -m token_activation_perturbation_amd.profiling counters <results.db> <title> <command>
 
 `trace` prints a markdown table of per-kernel calls and durations from a
 `--kernel-trace --stats` run.  `pmc` turns two counter runs (FETCH_SIZE,
 then WRITE_SIZE, in KiB per dispatch) into HBM bytes per launch of `kernel`,
 scaled by what the same counters read for the largest plain copy kernel in
 the run (whose true traffic is copy_bytes read + copy_bytes written).
+`counters` turns one SQ counter run into per-kernel unit utilisation on the
+MI355X (1024 SIMDs in 8 XCDs): VALU busy = SQ_ACTIVE_INST_VALU x 4 (it counts
+quad-cycles, summed over SIMDs) / 1024 / (GRBM_GUI_ACTIVE / 8) (the GPU-busy
+clock, summed over the 8 XCDs); MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / 1024 /
+(GRBM_GUI_ACTIVE / 8); VALU and MFMA instructions per wave.
 """
 from __future__ import annotations
 
@@ -90,9 +96,42 @@ def pmc_traffic(fetch_db: str, write_db: str, kernel: str, copy_bytes: int) -> d
             "bytes_per_launch": fetch_kib * 1024.0 * f_scale + write_kib * 1024.0 * w_scale}
 
 
+N_SIMD = 1024
+N_XCD = 8
+
+
+def counter_table(db: str, title: str, command: str) -> str:
+    con = sqlite3.connect(db)
+    rows = con.execute("select kernel_name, dispatch_id, counter_name, value "
+                       "from counters_collection").fetchall()
+    acc, disp = {}, {}
+    for name, did, cname, val in rows:
+        if "dust" not in name:
+            continue
+        k = short_name(name)
+        acc.setdefault(k, {}).setdefault(cname, 0.0)
+        acc[k][cname] += float(val)
+        disp.setdefault(k, set()).add(did)
+    lines = [f"# {title}", "", "Command (repository root, on an MI355X):", "", "```", command,
+             "```", "", "| kernel | dispatches | VALU busy | MFMA busy | VALU insts / wave | "
+             "MFMA insts / wave | transcendental insts / wave |", "|---|---|---|---|---|---|---|"]
+    for k, c in acc.items():
+        n = len(disp[k])
+        gui = c.get("GRBM_GUI_ACTIVE", 0.0) / n / N_XCD
+        waves = c.get("SQ_WAVES", 0.0) / n
+        valu = c.get("SQ_ACTIVE_INST_VALU", 0.0) / n * 4 / N_SIMD / gui if gui else float("nan")
+        mfma = c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / n / N_SIMD / gui if gui else float("nan")
+        per = lambda name: c.get(name, 0.0) / n / waves if waves else float("nan")  # noqa: E731
+        lines.append(f"| `{k}` | {n} | {valu:.2f} | {mfma:.2f} | {per('SQ_INSTS_VALU'):.0f} | "
+                     f"{per('SQ_INSTS_MFMA'):.0f} | {per('SQ_INSTS_VALU_TRANS_F32'):.0f} |")
+    return "\n".join(lines) + "\n"
+
+
 if __name__ == "__main__":
     if len(sys.argv) >= 5 and sys.argv[1] == "trace":
         print(trace_markdown(sys.argv[2], sys.argv[3], sys.argv[4]), end="")
+    elif len(sys.argv) >= 5 and sys.argv[1] == "counters":
+        print(counter_table(sys.argv[2], sys.argv[3], sys.argv[4]), end="")
     elif len(sys.argv) >= 6 and sys.argv[1] == "pmc":
         print(json.dumps(pmc_traffic(sys.argv[2], sys.argv[3], sys.argv[4], int(sys.argv[5])),
                          indent=1))
