@@ -41,6 +41,17 @@
  * rho_t^(i) = -<e_t, Delta o_t^(i)>, evaluated literally; steps 3-6 then
  * run unchanged (dust_oracle_estimate_local).
  *
+ * A third scoring rule is the model's head: cross-entropy of the logits
+ * z_t = W x_t against a label y_t, jittered "one 256-column slab of the
+ * vocabulary at a time" ("What the released code actually does", step 5).
+ * Reading used: every slab j is its own site with K draws; draw i of slab j
+ * adds s_i sigma a_t^(n(i))[c] to the logits of the slab's columns c only
+ * (the same noise values as the full-width jitter, restricted to the slab),
+ * rho = CE(z_t) - CE(z_t + jitter), evaluated literally with a full
+ * log-sum-exp over all columns; the centring is over the K draws of the same
+ * slab and token; gamma = 0 (the loss is per token); g_t's columns of slab j
+ * come from slab j's draws (dust_oracle_estimate_head).
+ *
  * Noise (the pages fix no generator; they name Philox as a counter-based
  * generator whose n-th output is a pure function of (seed, n): "Scaling To
  * Unfathomable Depth", section "MeZO", last paragraphs).  Reading used here:
@@ -492,5 +503,183 @@ int dust_oracle_estimate_local(const float *X, const float *E, int64_t T,
   run_phase(&j, phase_credit);
   run_phase(&j, phase_error);
   run_phase(&j, phase_outer);
+  return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Cross-entropy head. */
+
+typedef struct {
+  const float *X, *W;
+  const int32_t *labels;
+  int64_t T, d_in, V, slab;
+  int32_t K;
+  double sigma;
+  uint64_t seed;
+  int32_t antithetic;
+  int64_t t_begin, t_end;
+  double *loss, *rho, *g; /* [n_tok], [n_tok][n_slab][K], [n_tok][V] */
+  double *G;              /* [V][d_in] */
+  int n_threads;
+} head_job;
+
+typedef struct {
+  head_job *job;
+  int tid;
+} head_arg;
+
+/* log sum_c exp(z_c), with the maximum taken out first. */
+static double log_sum_exp(const double *z, int64_t n) {
+  double m = z[0];
+  for (int64_t c = 1; c < n; ++c)
+    if (z[c] > m) m = z[c];
+  double s = 0.0;
+  for (int64_t c = 0; c < n; ++c) s += exp(z[c] - m);
+  return m + log(s);
+}
+
+/* Per token: logits, the clean cross-entropy, then for every slab and draw
+ * the literal perturbed cross-entropy, the centring over the slab's draws
+ * and the slab's columns of g. */
+static void *head_token(void *p) {
+  head_arg *ha = (head_arg *)p;
+  head_job *j = ha->job;
+  int64_t n_tok = j->t_end - j->t_begin, n_slab = j->V / j->slab;
+  double *z = (double *)malloc(sizeof(double) * (size_t)j->V);
+  double *zp = (double *)malloc(sizeof(double) * (size_t)j->V);
+  double *a = (double *)malloc(sizeof(double) * (size_t)j->V);
+  double *rho = (double *)malloc(sizeof(double) * (size_t)j->K);
+  double scale = -1.0 / ((double)j->K * j->sigma);
+  for (int64_t lt = ha->tid; lt < n_tok; lt += j->n_threads) {
+    int64_t t = j->t_begin + lt;
+    for (int64_t c = 0; c < j->V; ++c) {
+      double y = 0.0;
+      for (int64_t k = 0; k < j->d_in; ++k)
+        y += (double)j->W[c * j->d_in + k] * (double)j->X[t * j->d_in + k];
+      z[c] = y;
+    }
+    int32_t label = j->labels[t];
+    double ce = log_sum_exp(z, j->V) - z[label];
+    j->loss[lt] = ce;
+    double *g = j->g + lt * j->V;
+    for (int64_t c = 0; c < j->V; ++c) g[c] = 0.0;
+    for (int64_t sl = 0; sl < n_slab; ++sl) {
+      int64_t c0 = sl * j->slab, c1 = c0 + j->slab;
+      double mean = 0.0;
+      int32_t last_n = -1;
+      for (int32_t i = 0; i < j->K; ++i) {
+        int32_t n = j->antithetic ? i / 2 : i;
+        double s = (j->antithetic && (i % 2 == 1)) ? -1.0 : 1.0;
+        if (n != last_n) {
+          noise_vector(j->seed, (uint32_t)n, (uint32_t)t, j->V, a);
+          last_n = n;
+        }
+        memcpy(zp, z, sizeof(double) * (size_t)j->V);
+        for (int64_t c = c0; c < c1; ++c) zp[c] += s * j->sigma * a[c];
+        double ce_p = log_sum_exp(zp, j->V) - zp[label];
+        rho[i] = ce - ce_p;
+        mean += rho[i];
+      }
+      mean /= (double)j->K;
+      double *rho_out = j->rho + (lt * n_slab + sl) * j->K;
+      last_n = -1;
+      for (int32_t i = 0; i < j->K; ++i) {
+        int32_t n = j->antithetic ? i / 2 : i;
+        double s = (j->antithetic && (i % 2 == 1)) ? -1.0 : 1.0;
+        if (n != last_n) {
+          noise_vector(j->seed, (uint32_t)n, (uint32_t)t, j->V, a);
+          last_n = n;
+        }
+        rho_out[i] = rho[i];
+        double coef = (rho[i] - mean) * s;
+        for (int64_t c = c0; c < c1; ++c) g[c] += coef * a[c];
+      }
+      for (int64_t c = c0; c < c1; ++c) g[c] *= scale;
+    }
+  }
+  free(z);
+  free(zp);
+  free(a);
+  free(rho);
+  return NULL;
+}
+
+/* G_W[c][k] = sum_t g_t[c] x_t[k] over the handled tokens, in token order. */
+static void *head_outer(void *p) {
+  head_arg *ha = (head_arg *)p;
+  head_job *j = ha->job;
+  int64_t n_tok = j->t_end - j->t_begin;
+  for (int64_t c = ha->tid; c < j->V; c += j->n_threads) {
+    double *row = j->G + c * j->d_in;
+    for (int64_t k = 0; k < j->d_in; ++k) row[k] = 0.0;
+    for (int64_t lt = 0; lt < n_tok; ++lt) {
+      double gc = j->g[lt * j->V + c];
+      const float *x = j->X + (j->t_begin + lt) * j->d_in;
+      for (int64_t k = 0; k < j->d_in; ++k) row[k] += gc * (double)x[k];
+    }
+  }
+  return NULL;
+}
+
+static void run_head_phase(head_job *j, void *(*fn)(void *)) {
+  int nt = j->n_threads;
+  pthread_t *th = (pthread_t *)malloc(sizeof(pthread_t) * (size_t)nt);
+  head_arg *args = (head_arg *)malloc(sizeof(head_arg) * (size_t)nt);
+  for (int i = 0; i < nt; ++i) {
+    args[i].job = j;
+    args[i].tid = i;
+    pthread_create(&th[i], NULL, fn, &args[i]);
+  }
+  for (int i = 0; i < nt; ++i) pthread_join(th[i], NULL);
+  free(th);
+  free(args);
+}
+
+/*
+ * The cross-entropy head estimator over tokens t_begin..t_end-1 (0, 0 for
+ * all): X [T][d_in], W [V][d_in] (fp32 holding the exact input values),
+ * labels [T] in [0, V); V a multiple of slab.  Outputs for the handled
+ * tokens: loss[n] (clean cross-entropy), rho[n][V/slab][K] (loss reductions
+ * per slab and draw), g[n][V], and G[V][d_in] (their contribution).
+ * Returns 0, or -1 on an argument error.
+ */
+int dust_oracle_estimate_head(const float *X, const float *W, const int32_t *labels,
+                              int64_t T, int64_t d_in, int64_t V, int64_t slab,
+                              int32_t K, float sigma, uint64_t seed, int32_t antithetic,
+                              int64_t t_begin, int64_t t_end, int32_t n_threads,
+                              double *G, double *loss, double *rho, double *g) {
+  if (!X || !W || !labels || !G || !loss || !rho || !g) return -1;
+  if (T <= 0 || d_in <= 0 || V <= 0 || slab <= 0 || V % slab != 0) return -1;
+  if (K < 2 || (antithetic && K % 2 != 0)) return -1;
+  if (t_end <= t_begin) {
+    t_begin = 0;
+    t_end = T;
+  }
+  if (t_begin < 0 || t_end > T) return -1;
+  for (int64_t t = t_begin; t < t_end; ++t)
+    if (labels[t] < 0 || labels[t] >= V) return -1;
+  if (n_threads < 1) n_threads = 1;
+  head_job j;
+  memset(&j, 0, sizeof(j));
+  j.X = X;
+  j.W = W;
+  j.labels = labels;
+  j.T = T;
+  j.d_in = d_in;
+  j.V = V;
+  j.slab = slab;
+  j.K = K;
+  j.sigma = (double)sigma;
+  j.seed = seed;
+  j.antithetic = antithetic;
+  j.t_begin = t_begin;
+  j.t_end = t_end;
+  j.loss = loss;
+  j.rho = rho;
+  j.g = g;
+  j.G = G;
+  j.n_threads = n_threads;
+  run_head_phase(&j, head_token);
+  run_head_phase(&j, head_outer);
   return 0;
 }

@@ -55,6 +55,11 @@ def _load():
         f32p, f32p, i64, i64, i64, i64, ctypes.c_int32, ctypes.c_float, ctypes.c_float,
         ctypes.c_uint64, ctypes.c_int32, i64, i64, ctypes.c_int32, f64p, f64p, f64p, f64p]
     lib.dust_oracle_estimate_local.restype = ctypes.c_int
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    lib.dust_oracle_estimate_head.argtypes = [
+        f32p, f32p, i32p, i64, i64, i64, i64, ctypes.c_int32, ctypes.c_float, ctypes.c_uint64,
+        ctypes.c_int32, i64, i64, ctypes.c_int32, f64p, f64p, f64p, f64p]
+    lib.dust_oracle_estimate_head.restype = ctypes.c_int
     lib.dust_oracle_true_gradient.argtypes = [f32p, f32p, f32p, i64, i64, i64, f64p, f64p]
     lib.dust_oracle_true_gradient.restype = None
     _lib = lib
@@ -165,6 +170,37 @@ def estimate_local(X, E, *, K: int, sigma: float, gamma: float, seed: int,
     if rc != 0:
         raise ValueError("oracle rejected its arguments")
     return {"G": G, "rho": rho, "reward": reward, "g": g, "threads": th}
+
+
+def estimate_head(X, W, labels, *, K: int, sigma: float, seed: int, antithetic: bool,
+                  slab: int = 256, token_range=None, threads: int | None = None):
+    """Run the fp64 oracle of the cross-entropy head: logits z = W x, labels
+    [T] (int), every slab of `slab` columns jittered by its own K draws.
+    ``token_range=(t0, t1)`` restricts the work to those tokens.  Returns a
+    dict of fp64 arrays: G [V,d_in] (those tokens' contribution), loss [n]
+    (clean cross-entropy), rho [n, V/slab, K], g [n, V]."""
+    lib = _load()
+    X = np.ascontiguousarray(X, dtype=np.float32)
+    W = np.ascontiguousarray(W, dtype=np.float32)
+    labels = np.ascontiguousarray(labels, dtype=np.int32)
+    T, d_in = X.shape
+    V = W.shape[0]
+    assert W.shape == (V, d_in) and labels.shape == (T,) and V % slab == 0
+    t0, t1 = (0, T) if token_range is None else token_range
+    n = t1 - t0
+    G = np.zeros((V, d_in), dtype=np.float64)
+    loss = np.zeros(n, dtype=np.float64)
+    rho = np.zeros((n, V // slab, K), dtype=np.float64)
+    g = np.zeros((n, V), dtype=np.float64)
+    th = default_threads() if threads is None else threads
+    rc = lib.dust_oracle_estimate_head(
+        _ptr(X, ctypes.c_float), _ptr(W, ctypes.c_float), _ptr(labels, ctypes.c_int32), T, d_in,
+        V, slab, K, ctypes.c_float(sigma), ctypes.c_uint64(seed), int(bool(antithetic)), t0, t1,
+        th, _ptr(G, ctypes.c_double), _ptr(loss, ctypes.c_double), _ptr(rho, ctypes.c_double),
+        _ptr(g, ctypes.c_double))
+    if rc != 0:
+        raise ValueError("oracle rejected its arguments")
+    return {"G": G, "loss": loss, "rho": rho, "g": g, "threads": th}
 
 
 def true_gradient(X, W, target):
