@@ -5,10 +5,12 @@
 A step is one whole dust_estimate call (every stage: base GEMM, noise +
 loss change, centring and credit, reweighting, outer product) over one batch
 of synthetic inputs already resident in HBM; for the local-scoring workloads
-(kv_local_bf16, q_local_bf16) one dust_estimate_local call.  The default workload is the
+(kv_local_bf16, q_local_bf16) one dust_estimate_local call, and for the
+cross-entropy head (head_ce_bf16) one dust_estimate_head call, whose rows
+are counted per 256-column slab (K*T*V/256).  The default workload is the
 "bf16 layer" (T = 4096 tokens in 8 sequences of 512, d_in = d_out = 512,
 K = 64 antithetic draws, sigma = 1e-2, gamma = 0).  Prints one JSON line:
-draw-token-rows per second (K*T per step), the ALU roofline of the dominant
+draw-token-rows per second (K*T per step; K*T*V/256 for the head), the ALU roofline of the dominant
 kernel timed with HIP events inside the timed region, and the fp64 CPU
 oracle timed on a bounded sample on this machine's host cores.
 """
@@ -57,35 +59,48 @@ def read_traffic(workload: str, kernel: str):
 
 def cpu_baseline(w, inp, budget_s: float):
     """The fp64 oracle, as it stands, on a bounded sample: whole sequences of
-    the same workload, as many as fit the time budget (at least one)."""
+    the same workload (blocks of 16 tokens for the head), as many as fit the
+    time budget (at least one)."""
     from oracle import oracle
     threads = min(16, oracle.default_threads())
     kw = dict(K=w.K, sigma=w.sigma, gamma=w.gamma, seed=w.noise_seed,
               antithetic=w.antithetic, seq_len=w.seq_len, threads=threads)
-    if w.local:
-        def run(seq_range):
-            oracle.estimate_local(inp["X"], inp["E"], seq_range=seq_range, **kw)
+    # the sample is whole units: sequences, or blocks of 16 tokens for the
+    # head (whose loss is per token)
+    if w.head:
+        unit, n_units = 16, w.T // 16
+        kw = dict(K=w.K, sigma=w.sigma, seed=w.noise_seed, antithetic=w.antithetic,
+                  threads=threads)
+
+        def run(lo, hi):
+            oracle.estimate_head(inp["X"], inp["W"], inp["labels"],
+                                 token_range=(lo * unit, hi * unit), **kw)
     else:
-        def run(seq_range):
-            oracle.estimate(inp["X"], inp["W"], inp["target"], seq_range=seq_range, **kw)
+        unit, n_units = w.seq_len, w.n_seq
+        if w.local:
+            def run(lo, hi):
+                oracle.estimate_local(inp["X"], inp["E"], seq_range=(lo, hi), **kw)
+        else:
+            def run(lo, hi):
+                oracle.estimate(inp["X"], inp["W"], inp["target"], seq_range=(lo, hi), **kw)
     t0 = time.perf_counter()
-    run((0, 1))
+    run(0, 1)
     one = time.perf_counter() - t0
-    n_seq = max(1, min(w.n_seq, int(budget_s / max(one, 1e-6))))
+    n = max(1, min(n_units, int(budget_s / max(one, 1e-6))))
     # a whole workload that takes well under the budget is repeated, so the
     # figure is not a sub-second measurement
     repeats = 1
-    if n_seq == w.n_seq:
-        repeats = max(1, min(50, int(min(budget_s, 10.0) / max(one * n_seq, 1e-6))))
+    if n == n_units:
+        repeats = max(1, min(50, int(min(budget_s, 10.0) / max(one * n, 1e-6))))
     t0 = time.perf_counter()
     for _ in range(repeats):
-        run((0, n_seq))
+        run(0, n)
     elapsed = time.perf_counter() - t0
-    rows = w.K * w.seq_len * n_seq * repeats
-    what = (f"{n_seq} of {w.n_seq} sequences ({n_seq * w.seq_len} tokens x {w.K} draws) "
-            f"of the benchmarked workload")
+    rows = w.K * w.n_slab * unit * n * repeats
+    draws = f"{w.K} draws x {w.n_slab} slabs" if w.head else f"{w.K} draws"
+    what = (f"{n * unit} of {w.T} tokens ({draws}) of the benchmarked workload")
     if repeats > 1:
-        what = f"the whole benchmarked workload ({w.T} tokens x {w.K} draws) {repeats} times"
+        what = f"the whole benchmarked workload ({w.T} tokens x {draws}) {repeats} times"
     return {"value": rows / elapsed, "unit": "draw-token-rows/s", "cores": threads,
             "kind": "oracle", "sample": f"{what}, fp64, {elapsed:.1f} s"}
 
@@ -116,6 +131,9 @@ def main():
     if w.local:
         # local scoring: the draws are scored against the error estimate E
         E = torch.from_numpy(inp["E"]).to(dev).contiguous()
+    elif w.head:
+        W = torch.from_numpy(inp["W"]).to(dev).to(tdt).contiguous()
+        labels = torch.from_numpy(inp["labels"]).to(dev).contiguous()
     else:
         W, tg = (torch.from_numpy(inp[k]).to(dev).to(tdt).contiguous() for k in ("W", "target"))
     dt_code = dust.DUST_F32 if w.dtype == "f32" else dust.DUST_BF16
@@ -123,6 +141,8 @@ def main():
                      dtype=torch.uint8, device=dev)
     kw = dict(K=w.K, sigma=w.sigma, gamma=w.gamma, seed=w.noise_seed, antithetic=w.antithetic,
               seq_len=w.seq_len)
+    if w.head:
+        kw = dict(K=w.K, sigma=w.sigma, seed=w.noise_seed, antithetic=w.antithetic)
     # an untimed plain copy of known size: rocprofv3's FETCH_SIZE / WRITE_SIZE
     # counters read on it calibrate the HBM bytes reported for our kernels
     cal_src = torch.ones(CAL_COPY_BYTES // 4, dtype=torch.float32, device=dev)
@@ -130,9 +150,12 @@ def main():
     cal_dst.copy_(cal_src)
     torch.cuda.synchronize(dev)
     del cal_src, cal_dst
+
     def estimate(out):
         if w.local:
             return dust.dust_estimate_local(X, E, out=out, workspace=ws, **kw)
+        if w.head:
+            return dust.dust_estimate_head(X, W, labels, out=out, workspace=ws, **kw)
         return dust.dust_estimate(X, W, tg, out=out, workspace=ws, **kw)
 
     out = {}
@@ -167,16 +190,24 @@ def main():
     kernel_ms = sum(s.elapsed_time(e) for s, e in zip(starts, stops)) / args.steps
 
     value = w.rows / (ms_per_step * 1e-3)
-    if fused:
+    if w.head:
+        kernel = "head_ce_kernel"
+        slots = roofline.head_kernel_slots(w.T, w.d_out, w.K, w.antithetic)
+        min_s = roofline.head_min_seconds(w.T, w.d_out, w.K, w.antithetic)
+    elif fused:
         kernel = "fused_g0_kernel"
         slots = roofline.fused_kernel_slots(w.T, w.d_out, w.K, w.antithetic)
     else:
         kernel = "jitter_loss_kernel"
         slots = roofline.jitter_kernel_slots(w.T, w.d_out, w.K, w.antithetic)
+    if not w.head:
+        min_s = roofline.estimate_min_seconds(w.T, w.d_out, w.K, w.antithetic)
     achieved = slots / (kernel_ms * 1e-3) / 1e12
     peak = roofline.PEAK_SLOTS_PER_S / 1e12
     result = {
-        "metric": "draw-token-rows/sec (K*T) for " + ("dust_estimate_local" if w.local else "dust_estimate"),
+        "metric": ("slab-draw-token-rows/sec (K*T*V/256) for dust_estimate_head" if w.head else
+                   "draw-token-rows/sec (K*T) for " +
+                   ("dust_estimate_local" if w.local else "dust_estimate")),
         "value": value,
         "unit": "draw-token-rows/s",
         "n_gpus": 1,
@@ -190,6 +221,8 @@ def main():
         "dtype": "f32",
         "data": ("synthetic (seeded normal X and error estimate E; no dataset or trained weights)"
                  if w.local else
+                 "synthetic (seeded normal X, W and uniform labels; no dataset or trained weights)"
+                 if w.head else
                  "synthetic (seeded normal X, W, target; no dataset or trained weights)"),
         "config": {**w.describe(), "input_dtype": w.dtype, "parallelism": "none (1 GPU)"},
         "roofline": {
@@ -201,8 +234,7 @@ def main():
             "unit": "T lane-slot/s",
             "frac": achieved / peak,
             "traffic": read_traffic(w.name, kernel),
-            "end_to_end_frac": roofline.estimate_min_seconds(
-                w.T, w.d_out, w.K, w.antithetic) / (ms_per_step * 1e-3),
+            "end_to_end_frac": min_s / (ms_per_step * 1e-3),
         },
     }
     if args.cpu_budget > 0:

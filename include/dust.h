@@ -145,6 +145,55 @@ dust_status_t dust_estimate_local(const void* X, const float* E, int64_t T,
                                   size_t workspace_bytes, void* stream);
 
 /*
+ * Host-side check of dust_estimate_head's arguments: the rules of
+ * dust_validate for T, d_in, K, sigma, dtype and the workspace (sized by
+ * dust_workspace_bytes(T, d_in, V, K, antithetic, dtype)); X, W, labels and
+ * G_W must not be NULL, labels 4-byte aligned, V a positive multiple of 256.
+ * Label values live in device memory and are not checked here.  No HIP call.
+ */
+dust_status_t dust_validate_head(const void* X, const void* W, const int32_t* labels,
+                                 int64_t T, int64_t d_in, int64_t V, int32_t dtype,
+                                 int32_t K, float sigma, int32_t antithetic,
+                                 const float* G_W, const void* workspace,
+                                 size_t workspace_bytes);
+
+/*
+ * The estimator for a cross-entropy head ("Dust: every token is a member of
+ * the population", section "What the released code actually does", step 5:
+ * the head is jittered on its logits one 256-column slab of the vocabulary
+ * at a time, and only the cross-entropy is recomputed from cached sums).
+ * Logits z_t = W x_t; loss CE_t = logsumexp(z_t) - z_t[labels[t]].  Each
+ * slab j (columns 256 j .. 256 j + 255) is its own site with K draws: draw i
+ * adds s_i sigma a_t^(n(i))[c] to the slab's columns only (the noise of
+ * dust_estimate with the vocabulary column as channel), its loss reduction
+ * rho = CE(z) - CE(z + jitter) is centred over the slab's K draws (no credit
+ * scan: the loss is per token), and g_t on the slab's columns is
+ * -1/(K sigma) sum_i c_i s_i a_i over that slab's draws;
+ * G_W = sum_t g_t x_t^T.
+ *
+ * Inputs (device):
+ *   X      [T, d_in]   layer inputs, dtype `dtype`, row-major
+ *   W      [V, d_in]   head weights (nn.Linear layout), dtype `dtype`
+ *   labels [T]         int32 targets in [0, V) (a value outside is clamped to
+ *                      the range: memory-safe, result unspecified)
+ * V must be a multiple of 256.  K, sigma, seed, antithetic as for
+ * dust_estimate (gamma and seq_len do not apply).
+ * Outputs (device fp32, overwritten; the caller owns them):
+ *   G_W        [V, d_in]       required
+ *   loss_clean [T]             optional (NULL skips)
+ *   rho        [T, V/256, K]   optional: loss reductions per slab and draw
+ *   g          [T, V]          optional: the estimated logit gradient
+ * Workspace: dust_workspace_bytes(T, d_in, V, K, antithetic, dtype) bytes.
+ * Errors as for dust_estimate (validation first, nothing enqueued on error).
+ */
+dust_status_t dust_estimate_head(const void* X, const void* W, const int32_t* labels,
+                                 int64_t T, int64_t d_in, int64_t V, int32_t dtype,
+                                 int32_t K, float sigma, uint64_t seed,
+                                 int32_t antithetic, float* G_W, float* loss_clean,
+                                 float* rho, float* g, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
+/*
  * Test hook: the noise the estimator uses, written out.  For noise indices
  * n0..n0+n_cnt-1 and tokens t0..t0+t_cnt-1:
  *   words [n_cnt, t_cnt, 4*ceil(d_out/4)] uint32  Philox words (optional)
@@ -158,11 +207,12 @@ dust_status_t dust_noise_fill(uint64_t seed, int64_t n0, int64_t n_cnt,
 /*
  * Measurement hook (used by the benchmark to time the dominant kernel with
  * HIP events inside its timed region).  After this call, estimate call
- * number i (dust_estimate or dust_estimate_local) has start[i % n_pairs] and
- * stop[i % n_pairs] (hipEvent_t values passed as void*, created with timing
- * enabled and owned by the caller) stamped by the dispatch of its noise
- * kernel, the single-generation kernel when gamma = 0, else the jitter-loss
- * kernel, at the kernel's start and end (hipExtLaunchKernelGGL's events).
+ * number i (dust_estimate, dust_estimate_local or dust_estimate_head) has
+ * start[i % n_pairs] and stop[i % n_pairs] (hipEvent_t values passed as
+ * void*, created with timing enabled and owned by the caller) stamped by the
+ * dispatch of its noise kernel (the single-generation kernel when gamma = 0,
+ * else the jitter-loss kernel; the slab kernel of dust_estimate_head), at the
+ * kernel's start and end (hipExtLaunchKernelGGL's events).
  * n_pairs = 0 turns the hook off.  The pointer arrays are copied; the events
  * must outlive their use.  Process-wide state: not thread-safe.
  */

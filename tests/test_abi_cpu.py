@@ -35,7 +35,8 @@ def declared_entry_points():
 def test_every_declared_symbol_is_exported(lib):
     names = declared_entry_points()
     assert {"dust_estimate", "dust_validate", "dust_workspace_bytes", "dust_noise_fill",
-            "dust_last_error", "dust_estimate_local", "dust_validate_local"} <= set(names)
+            "dust_last_error", "dust_estimate_local", "dust_validate_local",
+            "dust_estimate_head", "dust_validate_head"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
@@ -133,3 +134,42 @@ def test_validate_local_accepts_good_arguments(lib):
 def test_validate_local_rejects(lib, over, status):
     assert _validate_local(**over) == status
     assert dust.dust_last_error() != ""
+
+
+def _validate_head(**over):
+    args = dict(X=16, W=32, labels=48, T=64, d_in=16, V=512, dtype=dust.DUST_BF16,
+                K=4, sigma=0.05, antithetic=1, G=64, ws=80, ws_bytes=None)
+    args.update(over)
+    if args["ws_bytes"] is None:
+        args["ws_bytes"] = dust.dust_workspace_bytes(args["T"], args["d_in"], args["V"],
+                                                     args["K"], args["antithetic"],
+                                                     dust.DUST_BF16) or 1
+    return dust.dust_validate_head(args["X"], args["W"], args["labels"], args["T"],
+                                   args["d_in"], args["V"], args["dtype"], args["K"],
+                                   args["sigma"], args["antithetic"], args["G"], args["ws"],
+                                   args["ws_bytes"])
+
+
+def test_validate_head_accepts_good_arguments(lib):
+    assert _validate_head() == 0
+    assert _validate_head(V=256, K=3, antithetic=0) == 0
+    assert _validate_head(T=1, K=2) == 0
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(X=None), 1), (dict(W=None), 1), (dict(labels=None), 1), (dict(G=None), 1),
+    (dict(labels=50), 1), (dict(V=0), 1), (dict(V=300), 1), (dict(V=128), 1),
+    (dict(T=0), 1), (dict(K=1), 1), (dict(K=5), 1), (dict(sigma=0.0), 1),
+    (dict(sigma=math.nan), 1), (dict(dtype=7), 2), (dict(T=1 << 24), 2), (dict(ws=None), 3),
+    (dict(ws_bytes=16), 3)])
+def test_validate_head_rejects(lib, over, status):
+    assert _validate_head(**over) == status
+    assert dust.dust_last_error() != ""
+
+
+def test_head_binding_rejects_bad_tensors():
+    import torch
+    X = torch.zeros(4, 4)
+    with pytest.raises(ValueError):
+        dust.dust_estimate_head(X, X, torch.zeros(4, dtype=torch.int32), K=4, sigma=0.1, seed=0,
+                                antithetic=True)

@@ -12,7 +12,8 @@ import ctypes
 import os
 
 __all__ = ["DustError", "dust_workspace_bytes", "dust_validate", "dust_estimate",
-           "dust_validate_local", "dust_estimate_local", "dust_noise_fill",
+           "dust_validate_local", "dust_estimate_local", "dust_validate_head",
+           "dust_estimate_head", "dust_noise_fill",
            "dust_set_timing_events", "dust_last_error", "library_path", "DUST_F32", "DUST_BF16"]
 
 DUST_F32 = 0
@@ -58,6 +59,12 @@ def _load():
     lib.dust_estimate_local.argtypes = [vp, vp, i64, i64, i64, i64, i32, i32, f32, f32,
                                         ctypes.c_uint64, i32, vp, vp, vp, vp, vp, sz, vp]
     lib.dust_estimate_local.restype = ctypes.c_int
+    lib.dust_validate_head.argtypes = [vp, vp, vp, i64, i64, i64, i32, i32, f32, i32, vp, vp,
+                                       sz]
+    lib.dust_validate_head.restype = ctypes.c_int
+    lib.dust_estimate_head.argtypes = [vp, vp, vp, i64, i64, i64, i32, i32, f32,
+                                       ctypes.c_uint64, i32, vp, vp, vp, vp, vp, sz, vp]
+    lib.dust_estimate_head.restype = ctypes.c_int
     lib.dust_noise_fill.argtypes = [ctypes.c_uint64, i64, i64, i64, i64, i64, vp, vp, vp]
     lib.dust_noise_fill.restype = ctypes.c_int
     vpp = ctypes.POINTER(ctypes.c_void_p)
@@ -97,6 +104,14 @@ def dust_validate_local(X_ptr, E_ptr, T, d_in, d_out, seq_len, dtype, K, sigma, 
     return int(_load().dust_validate_local(X_ptr, E_ptr, T, d_in, d_out, seq_len, dtype, K,
                                            sigma, gamma, int(bool(antithetic)), G_ptr,
                                            workspace_ptr, workspace_bytes))
+
+
+def dust_validate_head(X_ptr, W_ptr, labels_ptr, T, d_in, V, dtype, K, sigma, antithetic,
+                       G_ptr, workspace_ptr, workspace_bytes) -> int:
+    """Raw host-side validation of dust_estimate_head's arguments; returns the status."""
+    return int(_load().dust_validate_head(X_ptr, W_ptr, labels_ptr, T, d_in, V, dtype, K, sigma,
+                                          int(bool(antithetic)), G_ptr, workspace_ptr,
+                                          workspace_bytes))
 
 
 def _dtype_code(t) -> int:
@@ -221,6 +236,65 @@ def dust_estimate_local(X, E, *, K: int, sigma: float, gamma: float, seed: int,
         ctypes.c_uint64(seed & 0xFFFFFFFFFFFFFFFF), int(bool(antithetic)), G.data_ptr(),
         ptr(rho), ptr(reward), ptr(g), workspace.data_ptr(), workspace.numel(),
         _stream_ptr(dev))
+    _check(status)
+    return res
+
+
+def dust_estimate_head(X, W, labels, *, K: int, sigma: float, seed: int, antithetic: bool,
+                       want_loss: bool = False, want_rho: bool = False, want_g: bool = False,
+                       out: dict | None = None, workspace=None):
+    """Enqueue dust_estimate_head (the cross-entropy head, jittered one
+    256-column slab of the vocabulary at a time) on the current stream of
+    X's device.
+
+    X [T,d_in] and W [V,d_in] (both bfloat16 or both float32) and labels [T]
+    (int32): contiguous device tensors; V a multiple of 256.  Returns a dict
+    of fp32 device tensors: "G_W" [V,d_in] and the requested optional outputs
+    "loss" [T] (clean cross-entropy), "rho" [T,V//256,K] (loss reductions per
+    slab and draw), "g" [T,V].  ``out`` and ``workspace`` as for
+    dust_estimate.
+    """
+    import torch
+    for name, t in (("X", X), ("W", W), ("labels", labels)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    if X.dtype != W.dtype:
+        raise TypeError("X and W must share a dtype")
+    if labels.dtype != torch.int32:
+        raise TypeError("labels must be int32")
+    if X.dim() != 2 or W.dim() != 2 or labels.dim() != 1 or X.shape[1] != W.shape[1] \
+            or labels.shape[0] != X.shape[0]:
+        raise ValueError(f"shape mismatch: X {tuple(X.shape)}, W {tuple(W.shape)}, "
+                         f"labels {tuple(labels.shape)}")
+    T, d_in = X.shape
+    V = W.shape[0]
+    dt = _dtype_code(X)
+    dev = X.device
+    res = dict(out or {})
+
+    def _get(name, shape):
+        t = res.get(name)
+        if t is None:
+            t = torch.empty(shape, dtype=torch.float32, device=dev)
+            res[name] = t
+        elif (tuple(t.shape) != tuple(shape) or t.dtype != torch.float32 or not t.is_contiguous()
+              or t.device != dev):
+            raise ValueError(f"out[{name!r}] must be a contiguous float32 {tuple(shape)} "
+                             f"tensor on {dev}")
+        return t
+
+    G = _get("G_W", (V, d_in))
+    loss = _get("loss", (T,)) if want_loss else None
+    rho = _get("rho", (T, V // 256, K)) if want_rho else None
+    g = _get("g", (T, V)) if want_g else None
+    need = dust_workspace_bytes(T, d_in, V, K, antithetic, dt)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    ptr = lambda t: None if t is None else t.data_ptr()  # noqa: E731
+    status = _load().dust_estimate_head(
+        X.data_ptr(), W.data_ptr(), labels.data_ptr(), T, d_in, V, dt, K, sigma,
+        ctypes.c_uint64(seed & 0xFFFFFFFFFFFFFFFF), int(bool(antithetic)), G.data_ptr(),
+        ptr(loss), ptr(rho), ptr(g), workspace.data_ptr(), workspace.numel(), _stream_ptr(dev))
     _check(status)
     return res
 

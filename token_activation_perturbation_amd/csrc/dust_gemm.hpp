@@ -167,15 +167,15 @@ __device__ __forceinline__ u16x8_t frag_tr(const uint16_t* tile, int ch0, int k0
 
 // ---------------------------------------------------------------------------
 // Base GEMM: delta[m][n] = sum_k A[m][k] B[n][k] - target[m][n] (target bf16,
-// delta fp32), A = X [M = T][K = d_in], B = W [N = d_out][K].  64 x 64 tiles,
-// BK = 64.
+// delta fp32), A = X [M = T][K = d_in], B = W [N = d_out][K]; without TARGET
+// the plain product (the logits of a head).  64 x 64 tiles, BK = 64.
 //
 // Software pipeline: S register stages hold the next S k-tiles in flight
 // from HBM.  Step kt multiplies tile kt from LDS buffer kt & 1, writes tile
 // kt+1 from its register stage into the other LDS buffer, refills that stage
 // with tile kt+1+S, and ends with one barrier.  The k loop is unrolled by S so
 // every stage index is a compile-time constant.
-template <int S, bool VEC>
+template <int S, bool VEC, bool TARGET = true>
 __global__ __launch_bounds__(256) void nt_gemm_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, int64_t lda, int64_t ldb,
     int32_t M, int32_t N, int64_t K, int32_t tiles_m, int32_t tiles_n, int32_t per_xcd,
@@ -215,18 +215,20 @@ __global__ __launch_bounds__(256) void nt_gemm_kernel(
   // fetch the epilogue's target values now, so their latency hides behind
   // the k loop: unconditional loads from a clamped address (no branch, no
   // wait); entries outside the matrix are never stored
-  uint16_t tgt[2][2][4];
+  uint16_t tgt[2][2][4] = {};
+  if constexpr (TARGET) {
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int64_t row = m0 + wm * WM + i * 16 + 4 * (lane >> 4) + e;
-        const int64_t col = n0 + wn * WN + j * 16 + (lane & 15);
-        const int64_t rr = row < M ? row : M - 1, cc = col < N ? col : N - 1;
-        tgt[i][j][e] = target[rr * N + cc];
-      }
+        for (int e = 0; e < 4; ++e) {
+          const int64_t row = m0 + wm * WM + i * 16 + 4 * (lane >> 4) + e;
+          const int64_t col = n0 + wn * WN + j * 16 + (lane & 15);
+          const int64_t rr = row < M ? row : M - 1, cc = col < N ? col : N - 1;
+          tgt[i][j][e] = target[rr * N + cc];
+        }
+  }
 
   // Branch-free pipeline: the tile count is padded to a multiple of S (the
   // padding tiles lie past K, so they load from a clamped address and store
@@ -262,7 +264,8 @@ __global__ __launch_bounds__(256) void nt_gemm_kernel(
         const int64_t row = m0 + wm * WM + i * 16 + 4 * (lane >> 4) + e;
         const int64_t col = n0 + wn * WN + j * 16 + (lane & 15);
         if (row < M && col < N)
-          out[row * N + col] = acc[i][j][e] - bf16_bits_to_f32(tgt[i][j][e]);
+          out[row * N + col] = TARGET ? acc[i][j][e] - bf16_bits_to_f32(tgt[i][j][e])
+                                      : acc[i][j][e];
       }
 }
 

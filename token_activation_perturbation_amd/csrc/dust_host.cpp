@@ -108,6 +108,22 @@ dust_status_t dust_validate_local(const void* X, const float* E, int64_t T, int6
                          workspace, workspace_bytes);
 }
 
+dust_status_t dust_validate_head(const void* X, const void* W, const int32_t* labels,
+                                 int64_t T, int64_t d_in, int64_t V, int32_t dtype, int32_t K,
+                                 float sigma, int32_t antithetic, const float* G_W,
+                                 const void* workspace, size_t workspace_bytes) {
+  if (!X || !W || !labels || !G_W)
+    return dust::fail(DUST_ERR_INVALID_ARG, "X, W, labels and G_W must not be NULL");
+  if ((uintptr_t)labels % 4 != 0)
+    return dust::fail(DUST_ERR_INVALID_ARG, "labels must be 4-byte aligned (int32)");
+  if (V <= 0 || V % 256 != 0)
+    return dust::fail(DUST_ERR_INVALID_ARG, "V=%lld must be a positive multiple of 256",
+                      (long long)V);
+  // the loss is per token: every token is its own sequence, gamma = 0
+  return validate_common(T, d_in, V, 1, dtype, K, sigma, 0.0f, antithetic, workspace,
+                         workspace_bytes);
+}
+
 const char* dust_last_error(void) { return g_last_error; }
 
 }  // extern "C"

@@ -140,7 +140,7 @@ __global__ __launch_bounds__(256) void base_gemm_f32_kernel(
         const int col = n0 + 16 * j + (lane & 15);
         if (row < T && col < d_out) {
           const int64_t o = (int64_t)row * d_out + col;
-          delta[o] = acc[i][j][e] - target[o];
+          delta[o] = target ? acc[i][j][e] - target[o] : acc[i][j][e];
         }
       }
 }
@@ -676,12 +676,12 @@ __device__ __forceinline__ float sum_quad(float x) {
   return x;
 }
 
-// Wave reduction of M values per lane, fixed order; the M totals are
-// returned in scalar registers.  After the halving steps (masks 32, 16, 8 as
-// needed) lane l holds the partial total of value l / (64 / M); the rest is
-// summed inside rows with DPP.
+// Wave reduction of M values per lane, fixed order.  After the halving steps
+// (masks 32, 16, 8 as needed) lane l holds the partial total of value
+// l / (64 / M); the rest is summed inside rows with DPP, so on return every
+// lane l holds the total of value l / (64 / M).
 template <int M>
-__device__ __forceinline__ void wave_reduce_to_scalars(float (&v)[M], int lane, float (&tot)[M]) {
+__device__ __forceinline__ float wave_reduce_to_lanes(float (&v)[M], int lane) {
   static_assert(M == 2 || M == 4 || M == 8, "M");
   float x;
   if constexpr (M == 8) {
@@ -703,6 +703,13 @@ __device__ __forceinline__ void wave_reduce_to_scalars(float (&v)[M], int lane, 
     x += dpp_move<kDppRor8>(x);
     x += __shfl_xor(x, 16);  // groups of 32
   }
+  return x;
+}
+
+// The same reduction with the M totals returned in scalar registers.
+template <int M>
+__device__ __forceinline__ void wave_reduce_to_scalars(float (&v)[M], int lane, float (&tot)[M]) {
+  const float x = wave_reduce_to_lanes<M>(v, lane);
 #pragma unroll
   for (int k = 0; k < M; ++k)
     tot[k] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), k * (64 / M)));
@@ -885,6 +892,244 @@ __global__ __launch_bounds__(256) void fused_g0_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Cross-entropy head ("What the released code actually does", step 5): the
+// logits z_t = W x_t are jittered one slab of 256 columns at a time, every
+// slab its own site with K draws, and only the cross-entropy is recomputed.
+// With m = max_c z_c, e_c = exp(z_c - m) and S = sum_c e_c, the jitter
+// s sigma a on slab j changes the sum by u_s = sum_{c in j} e_c expm1(s sigma a_c),
+// so the loss reduction rho = CE(z) - CE(z + jitter) is
+//   y outside j:  rho = -log1p(u_s / S)
+//   y inside j:   rho = s sigma a_y - log1p(u_s / S)
+//                     = -log1p(q expm1(-s sigma a_y) + exp(-s sigma a_y) u'_s / S)
+// with u'_s the same sum without the label's column and q = 1 - p_y formed as
+// (S - e_y) / S from a sum that leaves e_y out.  Only the slab's partial sum
+// is recomputed, and rho is formed at its own scale: no difference of two
+// O(log V) losses, and no cancellation when the head is confident (p_y near
+// 1).  The loss is per token (gamma = 0), so g is formed in the same pass,
+// as in fused_g0_kernel:
+//   antithetic  g = -1/(K sigma) sum_p (rho_(2p) - rho_(2p+1)) a_p
+//   plain       g = -1/(K sigma) (sum_n rho_n a_n - mean(rho) sum_n a_n)
+// (centring over the slab's draws cancels inside a pair).  One workgroup per
+// token; wave w takes slabs w, w + waves, ...; lane l owns columns 4 l .. + 3
+// of the slab (noise quad 64 j + l of the token).  Every wave forms m and S
+// over the whole row itself (same order, so identical values).
+// expm1 of the jitter: SMALL (sigma sqrt(48 ln 2) < 0.5, all |x| < 0.5) uses
+// the even and odd Taylor parts to x^8, E(x) and O(x), accurate to ~1e-8
+// relative and giving both signs at once, expm1(+-x) = E +- O; otherwise
+// exp(x) - 1 where |x| >= 0.5.  Per-row and per-draw scalars (the row's
+// exponentials, the label's expm1, log1p) use the accurate library routines.
+
+__device__ __forceinline__ void expm1_parts(float x, float& even, float& odd) {
+  const float q = x * x;
+  odd = x * __builtin_fmaf(
+                q, __builtin_fmaf(q, __builtin_fmaf(q, 1.0f / 5040.0f, 1.0f / 120.0f), 1.0f / 6.0f),
+                1.0f);
+  even = q * __builtin_fmaf(
+                 q, __builtin_fmaf(q, __builtin_fmaf(q, 1.0f / 40320.0f, 1.0f / 720.0f),
+                                   1.0f / 24.0f),
+                 0.5f);
+}
+
+// expm1(x) and expm1(-x)
+template <bool SMALL>
+__device__ __forceinline__ void expm1_pm(float x, float& plus, float& minus) {
+  float even, odd;
+  expm1_parts(x, even, odd);
+  plus = even + odd;
+  minus = even - odd;
+  if (!SMALL) {
+    const float ex = __expf(x);
+    if (__builtin_fabsf(x) >= 0.5f) {
+      plus = ex - 1.0f;
+      minus = 1.0f / ex - 1.0f;
+    }
+  }
+}
+
+// expm1(x) alone (plain draws): x (1 + x/2! + ... + x^7/8!) by Horner where
+// |x| < 0.5 (always, when SMALL), else exp(x) - 1
+template <bool SMALL>
+__device__ __forceinline__ float expm1_one(float x) {
+  float p = __builtin_fmaf(x, 1.0f / 40320.0f, 1.0f / 5040.0f);
+  p = __builtin_fmaf(x, p, 1.0f / 720.0f);
+  p = __builtin_fmaf(x, p, 1.0f / 120.0f);
+  p = __builtin_fmaf(x, p, 1.0f / 24.0f);
+  p = __builtin_fmaf(x, p, 1.0f / 6.0f);
+  p = __builtin_fmaf(x, p, 0.5f);
+  p = __builtin_fmaf(x, p, 1.0f);
+  float r = x * p;
+  if (!SMALL) {
+    if (__builtin_fabsf(x) >= 0.5f) r = __expf(x) - 1.0f;
+  }
+  return r;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, m));
+  return v;
+}
+
+__device__ __forceinline__ float quad_comp(float4 a, int c) {
+  return c == 0 ? a.x : (c == 1 ? a.y : (c == 2 ? a.z : a.w));
+}
+
+// exp(z - m) of a quad starting at column c, with column y (if present) zeroed
+__device__ __forceinline__ float4 exp_quad_without(float4 z, float m, int32_t c, int32_t y) {
+  return make_float4(c == y ? 0.f : expf(z.x - m), c + 1 == y ? 0.f : expf(z.y - m),
+                     c + 2 == y ? 0.f : expf(z.z - m), c + 3 == y ? 0.f : expf(z.w - m));
+}
+
+// One draw's loss reduction for the slab: u the reduced partial sum (without
+// the label's column when y_in), ey = expm1(-s sigma a_y)
+__device__ __forceinline__ float head_rho(float u, float inv_s, bool y_in, float q, float ey) {
+  const float r = u * inv_s;
+  return -log1pf(y_in ? __builtin_fmaf(q, ey, (1.0f + ey) * r) : r);
+}
+
+template <bool ANTI, bool SMALL>
+__global__ __launch_bounds__(256) void head_ce_kernel(
+    const float* __restrict__ logits, const int32_t* __restrict__ labels, int32_t V, int32_t K,
+    int32_t K_n, float sigma, NoiseKey key, float* __restrict__ loss_clean,
+    float* __restrict__ rho, float* __restrict__ g32, uint16_t* __restrict__ g_hi,
+    uint16_t* __restrict__ g_lo) {
+  constexpr int M = 8, NB = ANTI ? 4 : 8;
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int waves = blockDim.x >> 6;
+  const int32_t t = blockIdx.x;
+  const float* zrow = logits + (int64_t)t * V;
+  const int32_t n_slab = V >> 8;
+  // labels outside [0, V) are clamped: memory-safe, the result is unspecified
+  int32_t y = labels[t];
+  y = y < 0 ? 0 : (y >= V ? V - 1 : y);
+
+  float zmax = -INFINITY;
+  for (int32_t c = 4 * lane; c < V; c += 256) {
+    const float4 z = *(const float4*)(zrow + c);
+    zmax = __builtin_fmaxf(zmax, __builtin_fmaxf(__builtin_fmaxf(z.x, z.y), __builtin_fmaxf(z.z, z.w)));
+  }
+  zmax = wave_max(zmax);
+  // the row's sum without the label's column, then with it
+  float s_ex = 0.f;
+  for (int32_t c = 4 * lane; c < V; c += 256) {
+    const float4 e = exp_quad_without(*(const float4*)(zrow + c), zmax, c, y);
+    s_ex += (e.x + e.y) + (e.z + e.w);
+  }
+  s_ex = wave_sum(s_ex);
+  const float z_y = zrow[y];
+  const float e_y = expf(z_y - zmax);
+  const float ssum = s_ex + e_y;
+  const float inv_s = 1.0f / ssum;
+  // CE = log(S) - (z_y - m); with p_y > 1/2 as log1p((S - e_y) / e_y), which
+  // keeps its relative accuracy as the loss goes to zero (both forms have
+  // no cancellation where they are used)
+  if (wave == 0 && lane == 0 && loss_clean)
+    loss_clean[t] = (e_y * inv_s > 0.5f) ? log1pf(s_ex / e_y) : (zmax - z_y) + logf(ssum);
+  const float q_y = s_ex * inv_s;  // 1 - p_y
+  const float scale = -1.0f / ((float)K * sigma);
+  const int y_slab = y >> 8, y_lane = (y & 255) >> 2, y_comp = y & 3;
+
+  for (int32_t j = wave; j < n_slab; j += waves) {
+    const int32_t c0 = j * 256 + 4 * lane;
+    const float4 e = exp_quad_without(*(const float4*)(zrow + c0), zmax, c0, y);
+    const bool y_in = (y_slab == j);  // uniform
+    float4 A = make_float4(0.f, 0.f, 0.f, 0.f), Sa = A;
+    float rsum = 0.f;
+    for (int32_t nb = 0; nb < K_n; nb += NB) {
+      float4 a[NB];
+      float v[M], ay[NB];
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        const int32_t n = nb + i;
+        a[i] = (n < K_n) ? noise_quad((uint32_t)(j * 64 + lane), (uint32_t)t, (uint32_t)n, key)
+                         : make_float4(0.f, 0.f, 0.f, 0.f);
+        if (ANTI) {
+          float p0, m0, p1, m1, p2, m2, p3, m3;
+          expm1_pm<SMALL>(sigma * a[i].x, p0, m0);
+          expm1_pm<SMALL>(sigma * a[i].y, p1, m1);
+          expm1_pm<SMALL>(sigma * a[i].z, p2, m2);
+          expm1_pm<SMALL>(sigma * a[i].w, p3, m3);
+          v[i] = __builtin_fmaf(e.x, p0, __builtin_fmaf(e.y, p1, __builtin_fmaf(e.z, p2, e.w * p3)));
+          v[NB + i] =
+              __builtin_fmaf(e.x, m0, __builtin_fmaf(e.y, m1, __builtin_fmaf(e.z, m2, e.w * m3)));
+        } else {
+          v[i] = __builtin_fmaf(
+              e.x, expm1_one<SMALL>(sigma * a[i].x),
+              __builtin_fmaf(e.y, expm1_one<SMALL>(sigma * a[i].y),
+                             __builtin_fmaf(e.z, expm1_one<SMALL>(sigma * a[i].z),
+                                            e.w * expm1_one<SMALL>(sigma * a[i].w))));
+        }
+        ay[i] = y_in ? __int_as_float(__builtin_amdgcn_readlane(
+                           __float_as_int(quad_comp(a[i], y_comp)), y_lane))
+                     : 0.f;
+      }
+      // lane l holds the partial sum of total k = l / 8: draw nb + k % NB,
+      // jitter sign - for k >= NB (antithetic); its loss reduction is formed
+      // there, all eight at once, then broadcast
+      const float x = wave_reduce_to_lanes<M>(v, lane);
+      const int k = lane >> 3;
+      float r;
+      if (y_in) {
+        float ayk = ay[0];
+#pragma unroll
+        for (int i = 1; i < NB; ++i) ayk = (k % NB == i) ? ay[i] : ayk;
+        // expm1(-s sigma a_y) for this lane's draw and sign
+        const float ey = expm1f((ANTI && k >= NB) ? sigma * ayk : -sigma * ayk);
+        r = head_rho(x, inv_s, true, q_y, ey);
+      } else {
+        r = head_rho(x, inv_s, false, 0.f, 0.f);
+      }
+      float rk[M];
+#pragma unroll
+      for (int kk = 0; kk < M; ++kk)
+        rk[kk] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(r), kk * (64 / M)));
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        const int32_t n = nb + i;
+        if (n < K_n) {
+          const float rp = rk[i];
+          float w;
+          if (ANTI) {
+            const float rm = rk[NB + i];
+            w = rp - rm;
+            if (rho && lane == 0) {
+              float* rr = rho + ((int64_t)t * n_slab + j) * K + 2 * n;
+              rr[0] = rp;
+              rr[1] = rm;
+            }
+          } else {
+            w = rp;
+            rsum += rp;
+            if (rho && lane == 0) rho[((int64_t)t * n_slab + j) * K + n] = rp;
+          }
+          A.x = __builtin_fmaf(w, a[i].x, A.x);
+          A.y = __builtin_fmaf(w, a[i].y, A.y);
+          A.z = __builtin_fmaf(w, a[i].z, A.z);
+          A.w = __builtin_fmaf(w, a[i].w, A.w);
+          if (!ANTI) {
+            Sa.x += a[i].x;
+            Sa.y += a[i].y;
+            Sa.z += a[i].z;
+            Sa.w += a[i].w;
+          }
+        }
+      }
+    }
+    float4 gq;
+    if (ANTI) {
+      gq = make_float4(scale * A.x, scale * A.y, scale * A.z, scale * A.w);
+    } else {
+      const float mean = rsum / (float)K;
+      gq = make_float4(scale * __builtin_fmaf(-mean, Sa.x, A.x),
+                       scale * __builtin_fmaf(-mean, Sa.y, A.y),
+                       scale * __builtin_fmaf(-mean, Sa.z, A.z),
+                       scale * __builtin_fmaf(-mean, Sa.w, A.w));
+    }
+    store_g_quad(gq, (int64_t)t * V, c0, V, true, g32, g_hi, g_lo);
+  }
+}
+
 // Bench hook state: event pairs stamped by the dispatch of the noise kernel
 // of the next dust_estimate calls (hipExtLaunchKernelGGL's start and stop
 // events, so they time the kernel itself, not the gap before it), pair i on
@@ -978,6 +1223,74 @@ inline unsigned grid_for(int64_t items, int64_t per_block) {
   return (unsigned)ceil_div(items, per_block);
 }
 
+// y = X W^T (- target when target != nullptr) -> out [T][d_out] fp32.
+void launch_base_gemm(const void* X, const void* W, const void* target, int64_t T, int64_t d_in,
+                      int64_t d_out, int32_t dtype, float* out, hipStream_t s) {
+  const int32_t Ti = (int32_t)T, di = (int32_t)d_in, dout = (int32_t)d_out;
+  if (dtype == DUST_BF16) {
+    const bool vec = (d_in % 8 == 0) && ((uintptr_t)X % 16 == 0) && ((uintptr_t)W % 16 == 0);
+    const int tiles_m = (int)ceil_div(T, 64), tiles_n = (int)ceil_div(d_out, 64);
+    const int per_xcd = (int)ceil_div((int64_t)tiles_m * tiles_n, 8);
+    const dim3 grid((unsigned)(8 * per_xcd));
+#define DUST_BASE_GEMM(V, TG)                                                                \
+  hipLaunchKernelGGL((gemm::nt_gemm_kernel<4, V, TG>), grid, dim3(256), 0, s,               \
+                     (const uint16_t*)X, (const uint16_t*)W, (int64_t)d_in, (int64_t)d_in, \
+                     Ti, dout, (int64_t)d_in, tiles_m, tiles_n, per_xcd,                    \
+                     (const uint16_t*)target, out)
+    if (target) {
+      if (vec) DUST_BASE_GEMM(true, true); else DUST_BASE_GEMM(false, true);
+    } else {
+      if (vec) DUST_BASE_GEMM(true, false); else DUST_BASE_GEMM(false, false);
+    }
+#undef DUST_BASE_GEMM
+  } else {
+    const int tiles_n = (int)ceil_div(d_out, 64);
+    const unsigned blocks = (unsigned)(ceil_div(T, 64) * tiles_n);
+    hipLaunchKernelGGL(base_gemm_f32_kernel, dim3(blocks), dim3(256), 0, s, (const float*)X,
+                       (const float*)W, (const float*)target, Ti, di, dout, tiles_n, out);
+  }
+}
+
+// G_W = sum_t g_t x_t^T: the split partials (or G_W itself with one split),
+// then their fixed-order sum.  bf16: from the split g_hi + g_lo; f32: from g32.
+void launch_outer(const Plan& p, const void* X, const float* g32, const uint16_t* g_hi,
+                  const uint16_t* g_lo, float* gpart, float* G_W, int64_t T, int64_t d_in,
+                  int64_t d_out, int32_t dtype, hipStream_t s) {
+  const int32_t Ti = (int32_t)T, di = (int32_t)d_in, dout = (int32_t)d_out;
+  float* dst = p.outer_split > 1 ? gpart : G_W;
+  if (dtype == DUST_BF16) {
+    const bool vec = (d_in % 8 == 0) && (d_out % 8 == 0) && ((uintptr_t)X % 16 == 0) &&
+                     d_in < (1 << 22) && d_out < (1 << 22);
+    const int tiles_m = (int)ceil_div(d_out, 64), tiles_n = (int)ceil_div(d_in, 64);
+    const int per_xcd = (int)ceil_div((int64_t)tiles_m * tiles_n * p.outer_split, 8);
+    const dim3 grid((unsigned)(8 * per_xcd));
+    const int32_t partial = p.outer_split > 1 ? 1 : 0;
+    if (vec)
+      hipLaunchKernelGGL((gemm::tn_outer_kernel<DUST_TN_STAGES, true>), grid, dim3(256), 0, s,
+                         (const uint16_t*)g_hi, (const uint16_t*)g_lo, (const uint16_t*)X, Ti,
+                         dout, di, tiles_m, tiles_n,
+                         p.outer_split, per_xcd, (int64_t)0, (int64_t)p.outer_tokens, partial,
+                         dst);
+    else
+      hipLaunchKernelGGL((gemm::tn_outer_kernel<DUST_TN_STAGES, false>), grid, dim3(256), 0, s,
+                         (const uint16_t*)g_hi, (const uint16_t*)g_lo, (const uint16_t*)X, Ti,
+                         dout, di, tiles_m, tiles_n,
+                         p.outer_split, per_xcd, (int64_t)0, (int64_t)p.outer_tokens, partial,
+                         dst);
+  } else {
+    const int tiles_n = (int)ceil_div(d_in, 64);
+    const int64_t tiles = ceil_div(d_out, 64) * tiles_n;
+    hipLaunchKernelGGL(outer_f32_kernel, dim3((unsigned)(tiles * p.outer_split)), dim3(256), 0,
+                       s, (const float*)g32, (const float*)X, Ti, di, dout, tiles_n,
+                       (int32_t)p.outer_tokens, dst);
+  }
+  if (p.outer_split > 1) {
+    const int64_t n = d_out * d_in;
+    hipLaunchKernelGGL(split_sum_kernel, dim3(grid_for(ceil_div(n, 4), 256)), dim3(256), 0, s,
+                       (const float*)gpart, p.outer_split, n, G_W);
+  }
+}
+
 // Both estimators after validation.  E == nullptr: the layer-local loss
 // (delta = W x - target from the base GEMM, rho the loss reductions).
 // E != nullptr: local scoring (delta = E, the supplied error estimate; no
@@ -1014,30 +1327,8 @@ dust_status_t run_estimate(const void* X, const void* W, const void* target, con
   const NoiseKey key = make_key(seed);
   const int32_t Ti = (int32_t)T, di = (int32_t)d_in, dout = (int32_t)d_out;
 
-  // 1. base GEMM -> delta
-  if (local) {
-    // delta is the caller's error estimate
-  } else if (dtype == DUST_BF16) {
-    const bool vec = (d_in % 8 == 0) && ((uintptr_t)X % 16 == 0) && ((uintptr_t)W % 16 == 0);
-    const int tiles_m = (int)ceil_div(T, 64), tiles_n = (int)ceil_div(d_out, 64);
-    const int per_xcd = (int)ceil_div((int64_t)tiles_m * tiles_n, 8);
-    const dim3 grid((unsigned)(8 * per_xcd));
-    if (vec)
-      hipLaunchKernelGGL((gemm::nt_gemm_kernel<4, true>), grid, dim3(256), 0, s,
-                         (const uint16_t*)X, (const uint16_t*)W, (int64_t)d_in, (int64_t)d_in,
-                         Ti, dout, (int64_t)d_in, tiles_m, tiles_n, per_xcd,
-                         (const uint16_t*)target, delta);
-    else
-      hipLaunchKernelGGL((gemm::nt_gemm_kernel<4, false>), grid, dim3(256), 0, s,
-                         (const uint16_t*)X, (const uint16_t*)W, (int64_t)d_in, (int64_t)d_in,
-                         Ti, dout, (int64_t)d_in, tiles_m, tiles_n, per_xcd,
-                         (const uint16_t*)target, delta);
-  } else {
-    const int tiles_n = (int)ceil_div(d_out, 64);
-    const unsigned blocks = (unsigned)(ceil_div(T, 64) * tiles_n);
-    hipLaunchKernelGGL(base_gemm_f32_kernel, dim3(blocks), dim3(256), 0, s, (const float*)X,
-                       (const float*)W, (const float*)target, Ti, di, dout, tiles_n, delta);
-  }
+  // 1. base GEMM -> delta (the caller's error estimate itself when local)
+  if (!local) launch_base_gemm(X, W, target, T, d_in, d_out, dtype, delta, s);
   const int qpl = fused_qpl(p.nq);
   const bool independent = (gamma == 0.0f || seq_len == 1);
   const bool fused = independent && qpl > 0;
@@ -1101,38 +1392,47 @@ dust_status_t run_estimate(const void* X, const void* W, const void* target, con
 
   // 6. outer product -> the split partials (or G_W itself with one split),
   //    then their fixed-order sum
-  float* dst = p.outer_split > 1 ? gpart : G_W;
-  if (dtype == DUST_BF16) {
-    const bool vec = (d_in % 8 == 0) && (d_out % 8 == 0) && ((uintptr_t)X % 16 == 0) &&
-                     d_in < (1 << 22) && d_out < (1 << 22);
-    const int tiles_m = (int)ceil_div(d_out, 64), tiles_n = (int)ceil_div(d_in, 64);
-    const int per_xcd = (int)ceil_div((int64_t)tiles_m * tiles_n * p.outer_split, 8);
-    const dim3 grid((unsigned)(8 * per_xcd));
-    const int32_t partial = p.outer_split > 1 ? 1 : 0;
-    if (vec)
-      hipLaunchKernelGGL((gemm::tn_outer_kernel<DUST_TN_STAGES, true>), grid, dim3(256), 0, s,
-                         (const uint16_t*)g_hi, (const uint16_t*)g_lo, (const uint16_t*)X, Ti,
-                         dout, di, tiles_m, tiles_n,
-                         p.outer_split, per_xcd, (int64_t)0, (int64_t)p.outer_tokens, partial,
-                         dst);
-    else
-      hipLaunchKernelGGL((gemm::tn_outer_kernel<DUST_TN_STAGES, false>), grid, dim3(256), 0, s,
-                         (const uint16_t*)g_hi, (const uint16_t*)g_lo, (const uint16_t*)X, Ti,
-                         dout, di, tiles_m, tiles_n,
-                         p.outer_split, per_xcd, (int64_t)0, (int64_t)p.outer_tokens, partial,
-                         dst);
+  launch_outer(p, X, g32, g_hi, g_lo, gpart, G_W, T, d_in, d_out, dtype, s);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(DUST_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+// The cross-entropy head after validation: logits = X W^T, then the slab
+// draws with g in the same pass, then G_W.
+dust_status_t run_head(const void* X, const void* W, const int32_t* labels, int64_t T,
+                       int64_t d_in, int64_t V, int32_t dtype, int32_t K, float sigma,
+                       uint64_t seed, int32_t antithetic, float* G_W, float* loss_clean,
+                       float* rho, float* g, void* workspace, void* stream) {
+  Plan p;
+  make_plan(T, d_in, V, K, antithetic, dtype, &p);
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  float* logits = (float*)(ws + p.off_delta);
+  const bool bf16 = dtype == DUST_BF16;
+  float* g32 = bf16 ? g : (g ? g : (float*)(ws + p.off_g));
+  uint16_t* g_hi = bf16 ? (uint16_t*)(ws + p.off_g) : nullptr;
+  uint16_t* g_lo = bf16 ? g_hi + T * V : nullptr;
+  float* gpart = (float*)(ws + p.off_gpart);
+  const NoiseKey key = make_key(seed);
+
+  launch_base_gemm(X, W, nullptr, T, d_in, V, dtype, logits, s);
+  const TimedLaunch tl = take_timing_events();
+  const int64_t n_slab = V / 256;
+  const unsigned waves = (unsigned)(n_slab < 4 ? n_slab : 4);
+  // every noise value has |a| <= sqrt(48 ln 2) < 5.78, so |sigma a| < 0.5
+  const bool small = sigma * 5.78f < 0.5f;
+#define DUST_HEAD(A, SM)                                                                    \
+  hipExtLaunchKernelGGL((head_ce_kernel<A, SM>), dim3((unsigned)T), dim3(64 * waves), 0, s, \
+                        tl.start, tl.stop, 0, (const float*)logits, labels, (int32_t)V, K,  \
+                        p.K_n, sigma, key, loss_clean, rho, g32, g_hi, g_lo)
+  if (antithetic) {
+    if (small) DUST_HEAD(true, true); else DUST_HEAD(true, false);
   } else {
-    const int tiles_n = (int)ceil_div(d_in, 64);
-    const int64_t tiles = ceil_div(d_out, 64) * tiles_n;
-    hipLaunchKernelGGL(outer_f32_kernel, dim3((unsigned)(tiles * p.outer_split)), dim3(256), 0,
-                       s, (const float*)g32, (const float*)X, Ti, di, dout, tiles_n,
-                       (int32_t)p.outer_tokens, dst);
+    if (small) DUST_HEAD(false, true); else DUST_HEAD(false, false);
   }
-  if (p.outer_split > 1) {
-    const int64_t n = d_out * d_in;
-    hipLaunchKernelGGL(split_sum_kernel, dim3(grid_for(ceil_div(n, 4), 256)), dim3(256), 0, s,
-                       (const float*)gpart, p.outer_split, n, G_W);
-  }
+#undef DUST_HEAD
+  launch_outer(p, X, g32, g_hi, g_lo, gpart, G_W, T, d_in, V, dtype, s);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(DUST_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return ok();
@@ -1142,7 +1442,6 @@ dust_status_t run_estimate(const void* X, const void* W, const void* target, con
 }  // namespace dust
 
 extern "C" {
-
 
 dust_status_t dust_estimate(const void* X, const void* W, const void* target, int64_t T,
                             int64_t d_in, int64_t d_out, int64_t seq_len, int32_t dtype,
@@ -1171,6 +1470,18 @@ dust_status_t dust_estimate_local(const void* X, const float* E, int64_t T, int6
   return dust::run_estimate(X, nullptr, nullptr, E, T, d_in, d_out, seq_len, dtype, K, sigma,
                             gamma, seed, antithetic, G_W, nullptr, rho, reward, g, workspace,
                             stream);
+}
+
+dust_status_t dust_estimate_head(const void* X, const void* W, const int32_t* labels, int64_t T,
+                                 int64_t d_in, int64_t V, int32_t dtype, int32_t K, float sigma,
+                                 uint64_t seed, int32_t antithetic, float* G_W, float* loss_clean,
+                                 float* rho, float* g, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  const dust_status_t st = dust_validate_head(X, W, labels, T, d_in, V, dtype, K, sigma,
+                                              antithetic, G_W, workspace, workspace_bytes);
+  if (st != DUST_OK) return st;
+  return dust::run_head(X, W, labels, T, d_in, V, dtype, K, sigma, seed, antithetic, G_W,
+                        loss_clean, rho, g, workspace, stream);
 }
 
 dust_status_t dust_set_timing_events(void* const* start, void* const* stop, int32_t n_pairs) {

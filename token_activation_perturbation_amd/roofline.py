@@ -19,6 +19,12 @@ at once.  Their bound is the vector ALU issue rate, counted in lane-slots:
   change), 1 FMA for the reweighted sum g, and 1 add for the plain-draw
   noise sum used by the centring.
 
+The cross-entropy head's slab kernel consumes each value as: 1 multiply
+(sigma a), the jitter's expm1 (antithetic: both signs from the even and odd
+Taylor parts, 9 + 2 slots; plain draws: 8 slots of Horner), the slab's
+partial sums (one FMA per sign), 1 FMA for g and, for plain draws, 1 add for
+the noise sum: 57.5 slots per value with antithetic pairs, 54.5 without.
+
 Counted this way a two-pass pipeline (generate for the loss change, then
 regenerate for g) is capped at about half of the roofline; a single
 generation can reach all of it.
@@ -54,3 +60,19 @@ def jitter_kernel_slots(T: int, d_out: int, K: int, antithetic: bool) -> float:
 def estimate_min_seconds(T: int, d_out: int, K: int, antithetic: bool) -> float:
     """Lower bound on one estimate: one generation of every noise value."""
     return fused_kernel_slots(T, d_out, K, antithetic) / PEAK_SLOTS_PER_S
+
+
+def head_slots_per_value(antithetic: bool) -> float:
+    if antithetic:
+        return GEN_SLOTS_PER_VALUE + 1.0 + 11.0 + 2.0 + 1.0
+    return GEN_SLOTS_PER_VALUE + 1.0 + 8.0 + 1.0 + 1.0 + 1.0
+
+
+def head_kernel_slots(T: int, V: int, K: int, antithetic: bool) -> float:
+    """Algorithmic lane-slots of the cross-entropy head's slab kernel: every
+    slab's K draws on every token, i.e. K_n * T * V noise values."""
+    return distinct_noise_values(T, V, K, antithetic) * head_slots_per_value(antithetic)
+
+
+def head_min_seconds(T: int, V: int, K: int, antithetic: bool) -> float:
+    return head_kernel_slots(T, V, K, antithetic) / PEAK_SLOTS_PER_S

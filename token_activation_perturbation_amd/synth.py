@@ -1,8 +1,9 @@
 """Seeded synthetic inputs for the Dust estimator of one linear layer.
 
 This module holds no arithmetic of the estimator: it only draws X, W and
-target (or, for local scoring, X and an error estimate E) with the shapes and
-distributions of the workloads below, and rounds them to the input dtype.
+target (for local scoring X and an error estimate E; for a cross-entropy head
+X, W and labels) with the shapes and distributions of the workloads below,
+and rounds them to the input dtype.
 The pages train on FineWeb with a 37.7M parameter GPT whose layers are 512
 wide ("Dust: every token is a member of the population", sections "What the
 released code actually does" and "The results, checked against the tables");
@@ -37,21 +38,34 @@ class Workload:
     data_seed: int
     noise_seed: int
     target_kind: str    # "iid" (target ~ N(0,1)), "teacher" (bf16(X W'^T)),
-                        # or "local": scored against an error estimate
-                        # E ~ N(0,1) (fp32) instead of a loss
+                        # "local": scored against an error estimate
+                        # E ~ N(0,1) (fp32) instead of a loss, or
+                        # "head": a cross-entropy head, d_out = the vocabulary,
+                        # labels uniform in [0, d_out)
 
     @property
     def local(self) -> bool:
         return self.target_kind == "local"
 
     @property
+    def head(self) -> bool:
+        return self.target_kind == "head"
+
+    @property
     def n_seq(self) -> int:
         return self.T // self.seq_len
 
     @property
+    def n_slab(self) -> int:
+        """256-column vocabulary slabs of a head (each its own site with K
+        draws); 1 for the other layers."""
+        return self.d_out // 256 if self.head else 1
+
+    @property
     def rows(self) -> int:
-        """Draw-token rows K*T of one estimate."""
-        return self.K * self.T
+        """Draw-token rows of one estimate: K*T, and K*T per slab for a
+        head (K*T*V/256 slab-draw-token rows of 256 columns)."""
+        return self.K * self.T * self.n_slab
 
     def describe(self) -> dict:
         return {"workload": self.name, "T": self.T, "seq_len": self.seq_len,
@@ -73,10 +87,15 @@ WORKLOADS = {
         # queries (own token's score only).
         Workload("kv_local_bf16", 16384, 2048, 512, 512, 64, 0.2, 0.98, True, "bf16", 1006, 0, "local"),
         Workload("q_local_bf16", 16384, 2048, 512, 512, 64, 0.2, 0.0, True, "bf16", 1007, 0, "local"),
+        # The untied head of the same model ("What the released code actually
+        # does", step 5): a 4,096-token vocabulary jittered one 256-column
+        # slab at a time, sigma = 0.05, 256 antithetic draws per slab
+        # (4,096 slab draws per token), 8 sequences x 2048 tokens.
+        Workload("head_ce_bf16", 16384, 2048, 512, 4096, 256, 0.05, 0.0, True, "bf16", 1008, 0, "head"),
     ]
 }
 WORKLOAD_ORDER = ["tiny_f32", "bf16_layer", "mlp_up_bf16", "qkv_credit_bf16",
-                  "large_population_bf16", "kv_local_bf16", "q_local_bf16"]
+                  "large_population_bf16", "kv_local_bf16", "q_local_bf16", "head_ce_bf16"]
 
 
 def bf16_round(x: np.ndarray) -> np.ndarray:
@@ -105,7 +124,8 @@ def make_inputs(w: Workload, T: int | None = None, d_in: int | None = None,
                 d_out: int | None = None, data_seed: int | None = None) -> dict:
     """X [T,d_in], W [d_out,d_in], target [T,d_out] as fp32 arrays holding the
     exact input values; for a local-scoring workload X and E [T,d_out] (fp32)
-    instead.  Sizes and seed default to the workload's."""
+    instead, and for a head X, W and int32 labels [T].  Sizes and seed
+    default to the workload's."""
     T = w.T if T is None else T
     d_in = w.d_in if d_in is None else d_in
     d_out = w.d_out if d_out is None else d_out
@@ -114,6 +134,8 @@ def make_inputs(w: Workload, T: int | None = None, d_in: int | None = None,
     if w.local:
         return {"X": X, "E": rng.standard_normal((T, d_out)).astype(np.float32)}
     W = _round(rng.standard_normal((d_out, d_in)) / np.sqrt(d_in), w.dtype)
+    if w.head:
+        return {"X": X, "W": W, "labels": rng.integers(0, d_out, size=T).astype(np.int32)}
     if w.target_kind == "teacher":
         # W' = W + E with E ~ N(0, 0.01) read as variance 0.01 (std 0.1).
         W_teacher = W.astype(np.float64) + 0.1 * rng.standard_normal((d_out, d_in))
