@@ -52,6 +52,16 @@
  * slab and token; gamma = 0 (the loss is per token); g_t's columns of slab j
  * come from slab j's draws (dust_oracle_estimate_head).
  *
+ * A fourth site is a token embedding o_t = E[id_t] ("What the released code
+ * actually does", step 7: an embedding's error becomes its weight gradient
+ * by a scatter-add, and every estimate is divided by the token count before
+ * it is written to .grad).  Reading used: the layer-local loss of step 1
+ * with y_t = E[id_t] (a gather in place of W x_t), steps 2-5 unchanged, and
+ * step 6 replaced by G_E[v] = scale sum_{t: id_t = v} g_t, summed in token
+ * order, rows of ids that do not occur being zero; scale = 1/T writes what
+ * the page writes to .grad, scale = 1 the plain sum
+ * (dust_oracle_estimate_embedding, dust_oracle_reassemble_embedding).
+ *
  * Noise (the pages fix no generator; they name Philox as a counter-based
  * generator whose n-th output is a pure function of (seed, n): "Scaling To
  * Unfathomable Depth", section "MeZO", last paragraphs).  Reading used here:
@@ -171,6 +181,7 @@ void dust_oracle_noise_fill(uint64_t seed, int64_t n0, int64_t n_cnt,
 typedef struct {
   const float *X, *W, *target;
   const float *E;         /* error estimate [T][d_out] (local scoring only) */
+  const int32_t *ids;     /* token ids [T] (embedding only; W is the table) */
   int64_t T, d_in, d_out, seq_len;
   int32_t K;
   double sigma, gamma;
@@ -211,6 +222,26 @@ static void *phase_forward(void *p) {
       for (int64_t k = 0; k < j->d_in; ++k)
         y += (double)j->W[c * j->d_in + k] * (double)j->X[t * j->d_in + k];
       double d = y - (double)j->target[t * j->d_out + c];
+      j->delta[lt * j->d_out + c] = d;
+      loss += 0.5 * d * d;
+    }
+    j->loss[lt] = loss;
+  }
+  return NULL;
+}
+
+/* Step 1 for an embedding: y_t = E[id_t] (row id_t of the table, held in
+ * W as [V][d_out]), delta_t and L_t. */
+static void *phase_gather(void *p) {
+  worker_arg *wa = (worker_arg *)p;
+  oracle_job *j = wa->job;
+  int64_t n_tok = j->t_end - j->t_begin;
+  for (int64_t lt = wa->tid; lt < n_tok; lt += j->n_threads) {
+    int64_t t = j->t_begin + lt;
+    const float *row = j->W + (int64_t)j->ids[t] * j->d_out;
+    double loss = 0.0;
+    for (int64_t c = 0; c < j->d_out; ++c) {
+      double d = (double)row[c] - (double)j->target[t * j->d_out + c];
       j->delta[lt * j->d_out + c] = d;
       loss += 0.5 * d * d;
     }
@@ -504,6 +535,86 @@ int dust_oracle_estimate_local(const float *X, const float *E, int64_t T,
   run_phase(&j, phase_error);
   run_phase(&j, phase_outer);
   return 0;
+}
+
+/*
+ * The embedding's weight gradient from per-token errors: G_E[v][c] =
+ * scale sum_{t: ids[t] = v} g[t][c], the tokens added in order, every row
+ * written (zero for ids that do not occur).  g [T][d] fp64, G_E [V][d] fp64.
+ * Returns 0, or -1 on an argument error (an id outside [0, V) included).
+ */
+int dust_oracle_reassemble_embedding(const int32_t *ids, const double *g, int64_t T,
+                                     int64_t V, int64_t d, double scale, double *G_E) {
+  if (!ids || !g || !G_E || T < 0 || V <= 0 || d <= 0) return -1;
+  for (int64_t t = 0; t < T; ++t)
+    if (ids[t] < 0 || ids[t] >= V) return -1;
+  for (int64_t i = 0; i < V * d; ++i) G_E[i] = 0.0;
+  for (int64_t t = 0; t < T; ++t) {
+    double *row = G_E + (int64_t)ids[t] * d;
+    for (int64_t c = 0; c < d; ++c) row[c] += g[t * d + c];
+  }
+  for (int64_t i = 0; i < V * d; ++i) G_E[i] *= scale;
+  return 0;
+}
+
+/*
+ * The estimator for a token embedding over the sequences
+ * seq_begin..seq_end-1 (0, 0 for all): table [V][d] and target [T][d] (fp32
+ * holding the exact input values), ids [T] in [0, V).  Outputs for the
+ * handled tokens as for dust_oracle_estimate (loss, rho, reward, g with
+ * d_out = d), and G_E [V][d] = scale x (their scatter-added g).  Returns 0,
+ * or -1 on an argument error.
+ */
+int dust_oracle_estimate_embedding(const float *table, const int32_t *ids,
+                                   const float *target, int64_t T, int64_t V, int64_t d,
+                                   int64_t seq_len, int32_t K, float sigma, float gamma,
+                                   uint64_t seed, int32_t antithetic, double scale,
+                                   int64_t seq_begin, int64_t seq_end, int32_t n_threads,
+                                   double *G_E, double *loss, double *rho, double *reward,
+                                   double *g) {
+  if (!table || !ids || !target || !G_E || !loss || !rho || !reward || !g) return -1;
+  if (T <= 0 || V <= 0 || d <= 0 || seq_len <= 0 || T % seq_len != 0) return -1;
+  if (K < 2 || (antithetic && K % 2 != 0)) return -1;
+  for (int64_t t = 0; t < T; ++t)
+    if (ids[t] < 0 || ids[t] >= V) return -1;
+  int64_t n_seq = T / seq_len;
+  if (seq_end <= seq_begin) {
+    seq_begin = 0;
+    seq_end = n_seq;
+  }
+  if (seq_begin < 0 || seq_end > n_seq) return -1;
+  if (n_threads < 1) n_threads = 1;
+
+  oracle_job j;
+  memset(&j, 0, sizeof(j));
+  j.W = table;
+  j.ids = ids;
+  j.target = target;
+  j.T = T;
+  j.d_out = d;
+  j.seq_len = seq_len;
+  j.K = K;
+  j.sigma = (double)sigma;
+  j.gamma = (double)gamma;
+  j.seed = seed;
+  j.antithetic = antithetic;
+  j.t_begin = seq_begin * seq_len;
+  j.t_end = seq_end * seq_len;
+  j.n_threads = n_threads;
+  int64_t n_tok = j.t_end - j.t_begin;
+  j.delta = (double *)malloc(sizeof(double) * (size_t)(n_tok * d));
+  if (!j.delta) return -1;
+  j.loss = loss;
+  j.rho = rho;
+  j.reward = reward;
+  j.g = g;
+
+  run_phase(&j, phase_gather);
+  run_phase(&j, phase_rho);
+  run_phase(&j, phase_credit);
+  run_phase(&j, phase_error);
+  free(j.delta);
+  return dust_oracle_reassemble_embedding(ids + j.t_begin, g, n_tok, V, d, scale, G_E);
 }
 
 /* ------------------------------------------------------------------------ */

@@ -60,6 +60,14 @@ def _load():
         f32p, f32p, i32p, i64, i64, i64, i64, ctypes.c_int32, ctypes.c_float, ctypes.c_uint64,
         ctypes.c_int32, i64, i64, ctypes.c_int32, f64p, f64p, f64p, f64p]
     lib.dust_oracle_estimate_head.restype = ctypes.c_int
+    lib.dust_oracle_reassemble_embedding.argtypes = [i32p, f64p, i64, i64, i64,
+                                                     ctypes.c_double, f64p]
+    lib.dust_oracle_reassemble_embedding.restype = ctypes.c_int
+    lib.dust_oracle_estimate_embedding.argtypes = [
+        f32p, i32p, f32p, i64, i64, i64, i64, ctypes.c_int32, ctypes.c_float, ctypes.c_float,
+        ctypes.c_uint64, ctypes.c_int32, ctypes.c_double, i64, i64, ctypes.c_int32, f64p, f64p,
+        f64p, f64p, f64p]
+    lib.dust_oracle_estimate_embedding.restype = ctypes.c_int
     lib.dust_oracle_true_gradient.argtypes = [f32p, f32p, f32p, i64, i64, i64, f64p, f64p]
     lib.dust_oracle_true_gradient.restype = None
     _lib = lib
@@ -201,6 +209,55 @@ def estimate_head(X, W, labels, *, K: int, sigma: float, seed: int, antithetic: 
     if rc != 0:
         raise ValueError("oracle rejected its arguments")
     return {"G": G, "loss": loss, "rho": rho, "g": g, "threads": th}
+
+
+def reassemble_embedding(ids, g, V: int, scale: float = 1.0) -> np.ndarray:
+    """G_E [V, d] = scale * sum over tokens t with ids[t] = v of g[t] (fp64,
+    tokens added in order; rows of absent ids zero)."""
+    lib = _load()
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    g = np.ascontiguousarray(g, dtype=np.float64)
+    T, d = g.shape
+    assert ids.shape == (T,)
+    G = np.zeros((V, d), dtype=np.float64)
+    rc = lib.dust_oracle_reassemble_embedding(_ptr(ids, ctypes.c_int32), _ptr(g, ctypes.c_double),
+                                              T, V, d, float(scale), _ptr(G, ctypes.c_double))
+    if rc != 0:
+        raise ValueError("oracle rejected its arguments")
+    return G
+
+
+def estimate_embedding(table, ids, target, *, K: int, sigma: float, gamma: float, seed: int,
+                       antithetic: bool, seq_len: int, scale: float = 1.0, seq_range=None,
+                       threads: int | None = None):
+    """Run the fp64 oracle for a token embedding: table [V, d], ids [T],
+    target [T, d]; ``seq_range=(s0, s1)`` restricts the work to those
+    sequences.  Returns a dict of fp64 arrays: G [V, d] (scale x those
+    tokens' scatter-added g), loss [n], rho [n, K], reward [n, K], g [n, d]."""
+    lib = _load()
+    table = np.ascontiguousarray(table, dtype=np.float32)
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    target = np.ascontiguousarray(target, dtype=np.float32)
+    V, d = table.shape
+    T = ids.shape[0]
+    assert target.shape == (T, d)
+    s0, s1 = (0, 0) if seq_range is None else seq_range
+    n = (T if seq_range is None else (s1 - s0) * seq_len)
+    G = np.zeros((V, d), dtype=np.float64)
+    loss = np.zeros(n, dtype=np.float64)
+    rho = np.zeros((n, K), dtype=np.float64)
+    reward = np.zeros((n, K), dtype=np.float64)
+    g = np.zeros((n, d), dtype=np.float64)
+    th = default_threads() if threads is None else threads
+    rc = lib.dust_oracle_estimate_embedding(
+        _ptr(table, ctypes.c_float), _ptr(ids, ctypes.c_int32), _ptr(target, ctypes.c_float), T,
+        V, d, seq_len, K, ctypes.c_float(sigma), ctypes.c_float(gamma), ctypes.c_uint64(seed),
+        int(bool(antithetic)), float(scale), s0, s1, th, _ptr(G, ctypes.c_double),
+        _ptr(loss, ctypes.c_double), _ptr(rho, ctypes.c_double), _ptr(reward, ctypes.c_double),
+        _ptr(g, ctypes.c_double))
+    if rc != 0:
+        raise ValueError("oracle rejected its arguments")
+    return {"G": G, "loss": loss, "rho": rho, "reward": reward, "g": g, "threads": th}
 
 
 def true_gradient(X, W, target):

@@ -2,7 +2,7 @@
 
 This module holds no arithmetic of the estimator: it only draws X, W and
 target (for local scoring X and an error estimate E; for a cross-entropy head
-X, W and labels) with the shapes and distributions of the workloads below,
+X, W and labels; for a token embedding its table, Zipfian ids and target) with the shapes and distributions of the workloads below,
 and rounds them to the input dtype.
 The pages train on FineWeb with a 37.7M parameter GPT whose layers are 512
 wide ("Dust: every token is a member of the population", sections "What the
@@ -41,7 +41,9 @@ class Workload:
                         # "local": scored against an error estimate
                         # E ~ N(0,1) (fp32) instead of a loss, or
                         # "head": a cross-entropy head, d_out = the vocabulary,
-                        # labels uniform in [0, d_out)
+                        # labels uniform in [0, d_out); or "embedding": a token
+                        # embedding table [d_in = vocabulary, d_out], Zipfian
+                        # ids, target ~ N(0,1)
 
     @property
     def local(self) -> bool:
@@ -50,6 +52,15 @@ class Workload:
     @property
     def head(self) -> bool:
         return self.target_kind == "head"
+
+    @property
+    def embedding(self) -> bool:
+        return self.target_kind == "embedding"
+
+    @property
+    def V(self) -> int:
+        """Vocabulary size of a head (d_out) or an embedding (d_in)."""
+        return self.d_out if self.head else (self.d_in if self.embedding else 0)
 
     @property
     def n_seq(self) -> int:
@@ -92,10 +103,15 @@ WORKLOADS = {
         # slab at a time, sigma = 0.05, 256 antithetic draws per slab
         # (4,096 slab draws per token), 8 sequences x 2048 tokens.
         Workload("head_ce_bf16", 16384, 2048, 512, 4096, 256, 0.05, 0.0, True, "bf16", 1008, 0, "head"),
+        # The token embedding of the same model (step 7's scatter-add): a
+        # 4,096 x 512 table, Zipfian token ids, the embedding's sigma 0.4,
+        # own-token losses (gamma = 0), 8 sequences x 2048 tokens.
+        Workload("embed_bf16", 16384, 2048, 4096, 512, 64, 0.4, 0.0, True, "bf16", 1009, 0, "embedding"),
     ]
 }
 WORKLOAD_ORDER = ["tiny_f32", "bf16_layer", "mlp_up_bf16", "qkv_credit_bf16",
-                  "large_population_bf16", "kv_local_bf16", "q_local_bf16", "head_ce_bf16"]
+                  "large_population_bf16", "kv_local_bf16", "q_local_bf16", "head_ce_bf16",
+                  "embed_bf16"]
 
 
 def bf16_round(x: np.ndarray) -> np.ndarray:
@@ -120,16 +136,31 @@ def _round(x64: np.ndarray, dtype: str) -> np.ndarray:
     return bf16_round(x32) if dtype == "bf16" else x32
 
 
+def zipf_ids(rng: np.random.Generator, T: int, V: int) -> np.ndarray:
+    """T token ids with Zipf-Mandelbrot frequencies p(rank r) ~ 1/(r + 2.7),
+    the ranks assigned to ids by a random permutation."""
+    p = 1.0 / (np.arange(1, V + 1, dtype=np.float64) + 2.7)
+    p /= p.sum()
+    ranked = rng.choice(V, size=T, p=p)
+    return rng.permutation(V)[ranked].astype(np.int32)
+
+
 def make_inputs(w: Workload, T: int | None = None, d_in: int | None = None,
                 d_out: int | None = None, data_seed: int | None = None) -> dict:
     """X [T,d_in], W [d_out,d_in], target [T,d_out] as fp32 arrays holding the
     exact input values; for a local-scoring workload X and E [T,d_out] (fp32)
-    instead, and for a head X, W and int32 labels [T].  Sizes and seed
+    instead, for a head X, W and int32 labels [T], and for an embedding the
+    table [d_in, d_out], int32 ids [T] and target [T, d_out].  Sizes and seed
     default to the workload's."""
     T = w.T if T is None else T
     d_in = w.d_in if d_in is None else d_in
     d_out = w.d_out if d_out is None else d_out
     rng = np.random.default_rng(w.data_seed if data_seed is None else data_seed)
+    if w.embedding:
+        table = _round(rng.standard_normal((d_in, d_out)), w.dtype)
+        ids = zipf_ids(rng, T, d_in)
+        target = _round(rng.standard_normal((T, d_out)), w.dtype)
+        return {"table": table, "ids": ids, "target": target}
     X = _round(rng.standard_normal((T, d_in)), w.dtype)
     if w.local:
         return {"X": X, "E": rng.standard_normal((T, d_out)).astype(np.float32)}
