@@ -7,7 +7,9 @@ loss change, centring and credit, reweighting, outer product) over one batch
 of synthetic inputs already resident in HBM; for the local-scoring workloads
 (kv_local_bf16, q_local_bf16) one dust_estimate_local call, and for the
 cross-entropy head (head_ce_bf16) one dust_estimate_head call, whose rows
-are counted per 256-column slab (K*T*V/256).  The default workload is the
+are counted per 256-column slab (K*T*V/256), and for the token embedding
+(embed_bf16) one dust_estimate_embedding call (gather, estimator, and the
+reassembly of G_E divided by the token count).  The default workload is the
 "bf16 layer" (T = 4096 tokens in 8 sequences of 512, d_in = d_out = 512,
 K = 64 antithetic draws, sigma = 1e-2, gamma = 0).  Prints one JSON line:
 draw-token-rows per second (K*T per step; K*T*V/256 for the head), the ALU roofline of the dominant
@@ -77,7 +79,11 @@ def cpu_baseline(w, inp, budget_s: float):
                                  token_range=(lo * unit, hi * unit), **kw)
     else:
         unit, n_units = w.seq_len, w.n_seq
-        if w.local:
+        if w.embedding:
+            def run(lo, hi):
+                oracle.estimate_embedding(inp["table"], inp["ids"], inp["target"],
+                                          seq_range=(lo, hi), scale=1.0 / w.T, **kw)
+        elif w.local:
             def run(lo, hi):
                 oracle.estimate_local(inp["X"], inp["E"], seq_range=(lo, hi), **kw)
         else:
@@ -127,18 +133,24 @@ def main():
     dev = torch.device("cuda:0")
     inp = synth.make_inputs(w)
     tdt = torch.float32 if w.dtype == "f32" else torch.bfloat16
-    X = torch.from_numpy(inp["X"]).to(dev).to(tdt).contiguous()
-    if w.local:
+    def to_dev(name, cast=True):
+        t = torch.from_numpy(inp[name]).to(dev)
+        return (t.to(tdt) if cast else t).contiguous()
+
+    if w.embedding:
+        table, tg, ids = to_dev("table"), to_dev("target"), to_dev("ids", cast=False)
+    elif w.local:
         # local scoring: the draws are scored against the error estimate E
-        E = torch.from_numpy(inp["E"]).to(dev).contiguous()
+        X, E = to_dev("X"), to_dev("E", cast=False)
     elif w.head:
-        W = torch.from_numpy(inp["W"]).to(dev).to(tdt).contiguous()
-        labels = torch.from_numpy(inp["labels"]).to(dev).contiguous()
+        X, W, labels = to_dev("X"), to_dev("W"), to_dev("labels", cast=False)
     else:
-        W, tg = (torch.from_numpy(inp[k]).to(dev).to(tdt).contiguous() for k in ("W", "target"))
+        X, W, tg = to_dev("X"), to_dev("W"), to_dev("target")
     dt_code = dust.DUST_F32 if w.dtype == "f32" else dust.DUST_BF16
-    ws = torch.empty(dust.dust_workspace_bytes(w.T, w.d_in, w.d_out, w.K, w.antithetic, dt_code),
-                     dtype=torch.uint8, device=dev)
+    ws_bytes = (dust.dust_embedding_workspace_bytes(w.T, w.V, w.d_out, w.K, w.antithetic, dt_code)
+                if w.embedding else
+                dust.dust_workspace_bytes(w.T, w.d_in, w.d_out, w.K, w.antithetic, dt_code))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     kw = dict(K=w.K, sigma=w.sigma, gamma=w.gamma, seed=w.noise_seed, antithetic=w.antithetic,
               seq_len=w.seq_len)
     if w.head:
@@ -152,6 +164,9 @@ def main():
     del cal_src, cal_dst
 
     def estimate(out):
+        if w.embedding:
+            return dust.dust_estimate_embedding(table, ids, tg, out=out, workspace=ws,
+                                                scale=1.0 / w.T, **kw)
         if w.local:
             return dust.dust_estimate_local(X, E, out=out, workspace=ws, **kw)
         if w.head:
@@ -162,8 +177,8 @@ def main():
     for _ in range(args.warmup):
         out = estimate(out)
     torch.cuda.synchronize(dev)
-    if not bool(torch.isfinite(out["G_W"]).all()):
-        sys.exit("bench.py: non-finite G_W")
+    if not bool(torch.isfinite(out["G_E" if w.embedding else "G_W"]).all()):
+        sys.exit("bench.py: non-finite weight gradient")
 
     # event pairs stamped by the dispatch of the dominant kernel of every
     # timed step (the library launches it with hipExtLaunchKernelGGL)
@@ -207,7 +222,8 @@ def main():
     result = {
         "metric": ("slab-draw-token-rows/sec (K*T*V/256) for dust_estimate_head" if w.head else
                    "draw-token-rows/sec (K*T) for " +
-                   ("dust_estimate_local" if w.local else "dust_estimate")),
+                   ("dust_estimate_local" if w.local else
+                    "dust_estimate_embedding" if w.embedding else "dust_estimate")),
         "value": value,
         "unit": "draw-token-rows/s",
         "n_gpus": 1,
@@ -223,6 +239,9 @@ def main():
                  if w.local else
                  "synthetic (seeded normal X, W and uniform labels; no dataset or trained weights)"
                  if w.head else
+                 "synthetic (seeded normal table and target, Zipfian token ids; no dataset or "
+                 "trained weights)"
+                 if w.embedding else
                  "synthetic (seeded normal X, W, target; no dataset or trained weights)"),
         "config": {**w.describe(), "input_dtype": w.dtype, "parallelism": "none (1 GPU)"},
         "roofline": {

@@ -194,6 +194,87 @@ dust_status_t dust_estimate_head(const void* X, const void* W, const int32_t* la
                                  size_t workspace_bytes, void* stream);
 
 /*
+ * Workspace bytes dust_estimate_embedding needs (0 for sizes it cannot
+ * plan, an unknown dtype included), and the bytes dust_reassemble_embedding
+ * needs (0 for sizes it cannot plan).  Host-only, no HIP call.
+ */
+size_t dust_embedding_workspace_bytes(int64_t T, int64_t V, int64_t d, int32_t K,
+                                      int32_t antithetic, int32_t dtype);
+size_t dust_reassemble_workspace_bytes(int64_t T, int64_t V, int64_t d);
+
+/*
+ * Host-side check of dust_estimate_embedding's arguments: the rules of
+ * dust_validate for T, K, sigma, gamma, seq_len and dtype with d_out = d;
+ * table, ids, target and G_E must not be NULL, ids 4-byte aligned,
+ * 1 <= V < 2^31, scale finite, the workspace at least
+ * dust_embedding_workspace_bytes(T, V, d, K, antithetic, dtype) bytes.  Id
+ * values live in device memory and are not checked here.  No HIP call.
+ */
+dust_status_t dust_validate_embedding(const void* table, const int32_t* ids,
+                                      const void* target, int64_t T, int64_t V, int64_t d,
+                                      int64_t seq_len, int32_t dtype, int32_t K,
+                                      float sigma, float gamma, int32_t antithetic,
+                                      float scale, const float* G_E,
+                                      const void* workspace, size_t workspace_bytes);
+
+/*
+ * The estimator for a token embedding o_t = E[ids[t]] ("Dust: every token
+ * is a member of the population", section "What the released code actually
+ * does", step 7: an embedding's per-token error becomes its weight gradient
+ * by a scatter-add, and every estimate is divided by the token count before
+ * it is written to .grad).  Step 1 of dust_estimate becomes the gather
+ * delta_t = E[ids[t]] - target_t (layer-local loss); the jitter, loss
+ * reductions, centring, credit scan and g are dust_estimate's with
+ * d_out = d; the outer product becomes
+ *   G_E[v] = scale * sum_{t: ids[t] = v} g_t,
+ * every row written (zero for ids absent from the batch), summed in a fixed
+ * order (bitwise reproducible).  scale = 1/T writes what the page writes to
+ * .grad; scale = 1 gives the plain sum of the other entry points.
+ *
+ * Inputs (device): table [V, d] and target [T, d] in dtype `dtype`;
+ * ids [T] int32 in [0, V) (a value outside is clamped into the range:
+ * memory-safe, result unspecified).  K, sigma, gamma, seed, antithetic,
+ * seq_len as for dust_estimate.
+ * Outputs (device fp32, overwritten; the caller owns them): G_E [V, d]
+ * required; loss_clean [T], rho [T, K], reward [T, K], g [T, d] optional.
+ * Workspace: dust_embedding_workspace_bytes(T, V, d, K, antithetic, dtype).
+ */
+dust_status_t dust_estimate_embedding(const void* table, const int32_t* ids,
+                                      const void* target, int64_t T, int64_t V, int64_t d,
+                                      int64_t seq_len, int32_t dtype, int32_t K,
+                                      float sigma, float gamma, uint64_t seed,
+                                      int32_t antithetic, float scale, float* G_E,
+                                      float* loss_clean, float* rho, float* reward,
+                                      float* g, void* workspace, size_t workspace_bytes,
+                                      void* stream);
+
+/*
+ * Host-side check of dust_reassemble_embedding's arguments: ids, g and G_E
+ * not NULL and 4-byte aligned, T, V, d positive (T < 2^24, V < 2^31), scale
+ * finite, the workspace at least dust_reassemble_workspace_bytes(T, V, d)
+ * bytes.  No HIP call.
+ */
+dust_status_t dust_validate_reassemble(const int32_t* ids, const float* g, int64_t T,
+                                       int64_t V, int64_t d, float scale, const float* G_E,
+                                       const void* workspace, size_t workspace_bytes);
+
+/*
+ * The embedding's weight gradient from per-token errors alone (the
+ * scatter-add of the same passage, step 7), for an error g that comes from
+ * elsewhere (dust_estimate_local's g for value embeddings, for instance):
+ *   G_E[v] = scale * sum_{t: ids[t] = v} g_t   for every v in [0, V),
+ * zero rows for absent ids, a fixed summation order (a stable counting sort
+ * of the tokens by id, then a tiled reduce-by-key).
+ * Inputs (device): ids [T] int32 (clamped into [0, V) as above), g [T, d]
+ * fp32.  Output: G_E [V, d] fp32, overwritten.  Workspace:
+ * dust_reassemble_workspace_bytes(T, V, d).
+ */
+dust_status_t dust_reassemble_embedding(const int32_t* ids, const float* g, int64_t T,
+                                        int64_t V, int64_t d, float scale, float* G_E,
+                                        void* workspace, size_t workspace_bytes,
+                                        void* stream);
+
+/*
  * Test hook: the noise the estimator uses, written out.  For noise indices
  * n0..n0+n_cnt-1 and tokens t0..t0+t_cnt-1:
  *   words [n_cnt, t_cnt, 4*ceil(d_out/4)] uint32  Philox words (optional)
@@ -207,7 +288,8 @@ dust_status_t dust_noise_fill(uint64_t seed, int64_t n0, int64_t n_cnt,
 /*
  * Measurement hook (used by the benchmark to time the dominant kernel with
  * HIP events inside its timed region).  After this call, estimate call
- * number i (dust_estimate, dust_estimate_local or dust_estimate_head) has
+ * number i (dust_estimate, dust_estimate_local, dust_estimate_head or
+ * dust_estimate_embedding) has
  * start[i % n_pairs] and stop[i % n_pairs] (hipEvent_t values passed as
  * void*, created with timing enabled and owned by the caller) stamped by the
  * dispatch of its noise kernel (the single-generation kernel when gamma = 0,

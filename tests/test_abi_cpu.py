@@ -36,7 +36,9 @@ def test_every_declared_symbol_is_exported(lib):
     names = declared_entry_points()
     assert {"dust_estimate", "dust_validate", "dust_workspace_bytes", "dust_noise_fill",
             "dust_last_error", "dust_estimate_local", "dust_validate_local",
-            "dust_estimate_head", "dust_validate_head"} <= set(names)
+            "dust_estimate_head", "dust_validate_head", "dust_estimate_embedding",
+            "dust_validate_embedding", "dust_reassemble_embedding", "dust_validate_reassemble",
+            "dust_embedding_workspace_bytes", "dust_reassemble_workspace_bytes"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
@@ -173,3 +175,82 @@ def test_head_binding_rejects_bad_tensors():
     with pytest.raises(ValueError):
         dust.dust_estimate_head(X, X, torch.zeros(4, dtype=torch.int32), K=4, sigma=0.1, seed=0,
                                 antithetic=True)
+
+
+def _validate_embedding(**over):
+    args = dict(table=16, ids=32, target=48, T=64, V=100, d=24, seq_len=16,
+                dtype=dust.DUST_BF16, K=4, sigma=0.4, gamma=0.0, antithetic=1, scale=1 / 64,
+                G=64, ws=80, ws_bytes=None)
+    args.update(over)
+    if args["ws_bytes"] is None:
+        args["ws_bytes"] = dust.dust_embedding_workspace_bytes(
+            args["T"], args["V"], args["d"], args["K"], args["antithetic"], dust.DUST_BF16) or 1
+    return dust.dust_validate_embedding(args["table"], args["ids"], args["target"], args["T"],
+                                        args["V"], args["d"], args["seq_len"], args["dtype"],
+                                        args["K"], args["sigma"], args["gamma"],
+                                        args["antithetic"], args["scale"], args["G"],
+                                        args["ws"], args["ws_bytes"])
+
+
+def test_validate_embedding_accepts_good_arguments(lib):
+    assert _validate_embedding() == 0
+    assert _validate_embedding(V=1, T=1, seq_len=1, K=2) == 0
+    assert _validate_embedding(gamma=0.98, antithetic=0, K=3) == 0
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(table=None), 1), (dict(ids=None), 1), (dict(target=None), 1), (dict(G=None), 1),
+    (dict(ids=34), 1), (dict(V=0), 1), (dict(V=2**31), 1), (dict(scale=math.inf), 1),
+    (dict(scale=math.nan), 1), (dict(T=0), 1), (dict(seq_len=5), 1), (dict(K=1), 1),
+    (dict(K=5), 1), (dict(sigma=0.0), 1), (dict(gamma=2.0), 1), (dict(d=0), 1),
+    (dict(dtype=7), 2), (dict(T=1 << 24, seq_len=1), 2), (dict(ws=None), 3),
+    (dict(ws_bytes=16), 3)])
+def test_validate_embedding_rejects(lib, over, status):
+    assert _validate_embedding(**over) == status
+    assert dust.dust_last_error() != ""
+
+
+def test_embedding_workspace_covers_the_estimator_and_the_reassembly(lib):
+    T, V, d, K = 4096, 1000, 64, 16
+    e = dust.dust_embedding_workspace_bytes(T, V, d, K, True, dust.DUST_BF16)
+    r = dust.dust_reassemble_workspace_bytes(T, V, d)
+    w = dust.dust_workspace_bytes(T, 1, d, K, True, dust.DUST_BF16)
+    assert r > 0 and w > 0 and e >= w + r
+    # histograms, run starts, the sorted order and two partial rows per tile
+    assert r >= 4 * (V + 1) + 8 * T + 2 * 4 * d * (T // 32)
+    assert dust.dust_reassemble_workspace_bytes(0, V, d) == 0
+    assert dust.dust_reassemble_workspace_bytes(T, 0, d) == 0
+    assert dust.dust_reassemble_workspace_bytes(1 << 24, V, d) == 0
+    assert dust.dust_embedding_workspace_bytes(T, V, d, K, True, 9) == 0
+
+
+def _validate_reassemble(**over):
+    args = dict(ids=16, g=32, T=64, V=100, d=24, scale=1.0, G=48, ws=64, ws_bytes=None)
+    args.update(over)
+    if args["ws_bytes"] is None:
+        args["ws_bytes"] = dust.dust_reassemble_workspace_bytes(args["T"], args["V"],
+                                                                args["d"]) or 1
+    return dust.dust_validate_reassemble(args["ids"], args["g"], args["T"], args["V"],
+                                         args["d"], args["scale"], args["G"], args["ws"],
+                                         args["ws_bytes"])
+
+
+def test_validate_reassemble(lib):
+    assert _validate_reassemble() == 0
+    for over, status in [(dict(ids=None), 1), (dict(g=None), 1), (dict(G=None), 1),
+                         (dict(g=34), 1), (dict(T=0), 1), (dict(V=-1), 1), (dict(d=0), 1),
+                         (dict(scale=math.nan), 1), (dict(T=1 << 24), 2), (dict(ws=None), 3),
+                         (dict(ws_bytes=8), 3)]:
+        assert _validate_reassemble(**over) == status, over
+        assert dust.dust_last_error() != ""
+
+
+def test_embedding_binding_rejects_bad_tensors():
+    import torch
+    t = torch.zeros(4, 4)
+    ids = torch.zeros(4, dtype=torch.int32)
+    with pytest.raises(ValueError):
+        dust.dust_estimate_embedding(t, ids, t, K=4, sigma=0.1, gamma=0.0, seed=0,
+                                     antithetic=True, seq_len=4)
+    with pytest.raises(ValueError):
+        dust.dust_reassemble_embedding(ids, t, 4)

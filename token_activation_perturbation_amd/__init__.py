@@ -13,7 +13,9 @@ import os
 
 __all__ = ["DustError", "dust_workspace_bytes", "dust_validate", "dust_estimate",
            "dust_validate_local", "dust_estimate_local", "dust_validate_head",
-           "dust_estimate_head", "dust_noise_fill",
+           "dust_estimate_head", "dust_embedding_workspace_bytes",
+           "dust_reassemble_workspace_bytes", "dust_validate_embedding", "dust_estimate_embedding",
+           "dust_validate_reassemble", "dust_reassemble_embedding", "dust_noise_fill",
            "dust_set_timing_events", "dust_last_error", "library_path", "DUST_F32", "DUST_BF16"]
 
 DUST_F32 = 0
@@ -65,6 +67,21 @@ def _load():
     lib.dust_estimate_head.argtypes = [vp, vp, vp, i64, i64, i64, i32, i32, f32,
                                        ctypes.c_uint64, i32, vp, vp, vp, vp, vp, sz, vp]
     lib.dust_estimate_head.restype = ctypes.c_int
+    lib.dust_embedding_workspace_bytes.argtypes = [i64, i64, i64, i32, i32, i32]
+    lib.dust_embedding_workspace_bytes.restype = sz
+    lib.dust_reassemble_workspace_bytes.argtypes = [i64, i64, i64]
+    lib.dust_reassemble_workspace_bytes.restype = sz
+    lib.dust_validate_embedding.argtypes = [vp, vp, vp, i64, i64, i64, i64, i32, i32, f32, f32,
+                                            i32, f32, vp, vp, sz]
+    lib.dust_validate_embedding.restype = ctypes.c_int
+    lib.dust_estimate_embedding.argtypes = [vp, vp, vp, i64, i64, i64, i64, i32, i32, f32, f32,
+                                            ctypes.c_uint64, i32, f32, vp, vp, vp, vp, vp, vp,
+                                            sz, vp]
+    lib.dust_estimate_embedding.restype = ctypes.c_int
+    lib.dust_validate_reassemble.argtypes = [vp, vp, i64, i64, i64, f32, vp, vp, sz]
+    lib.dust_validate_reassemble.restype = ctypes.c_int
+    lib.dust_reassemble_embedding.argtypes = [vp, vp, i64, i64, i64, f32, vp, vp, sz, vp]
+    lib.dust_reassemble_embedding.restype = ctypes.c_int
     lib.dust_noise_fill.argtypes = [ctypes.c_uint64, i64, i64, i64, i64, i64, vp, vp, vp]
     lib.dust_noise_fill.restype = ctypes.c_int
     vpp = ctypes.POINTER(ctypes.c_void_p)
@@ -114,6 +131,24 @@ def dust_validate_head(X_ptr, W_ptr, labels_ptr, T, d_in, V, dtype, K, sigma, an
                                           workspace_bytes))
 
 
+def _output_getter(res: dict, dev):
+    """A function (name, shape) -> the fp32 output tensor res[name], created
+    on `dev` when absent, else checked (contiguous float32 of that shape)."""
+    import torch
+
+    def _get(name, shape):
+        t = res.get(name)
+        if t is None:
+            t = torch.empty(shape, dtype=torch.float32, device=dev)
+            res[name] = t
+        elif (tuple(t.shape) != tuple(shape) or t.dtype != torch.float32 or not t.is_contiguous()
+              or t.device != dev):
+            raise ValueError(f"out[{name!r}] must be a contiguous float32 {tuple(shape)} "
+                             f"tensor on {dev}")
+        return t
+    return _get
+
+
 def _dtype_code(t) -> int:
     import torch
     if t.dtype == torch.bfloat16:
@@ -156,17 +191,7 @@ def dust_estimate(X, W, target, *, K: int, sigma: float, gamma: float, seed: int
     dt = _dtype_code(X)
     dev = X.device
     res = dict(out or {})
-
-    def _get(name, shape):
-        t = res.get(name)
-        if t is None:
-            t = torch.empty(shape, dtype=torch.float32, device=dev)
-            res[name] = t
-        elif (tuple(t.shape) != tuple(shape) or t.dtype != torch.float32 or not t.is_contiguous()
-              or t.device != dev):
-            raise ValueError(f"out[{name!r}] must be a contiguous float32 {tuple(shape)} "
-                             f"tensor on {dev}")
-        return t
+    _get = _output_getter(res, dev)
 
     G = _get("G_W", (d_out, d_in))
     loss = _get("loss", (T,)) if want_loss else None
@@ -211,17 +236,7 @@ def dust_estimate_local(X, E, *, K: int, sigma: float, gamma: float, seed: int,
     dt = _dtype_code(X)
     dev = X.device
     res = dict(out or {})
-
-    def _get(name, shape):
-        t = res.get(name)
-        if t is None:
-            t = torch.empty(shape, dtype=torch.float32, device=dev)
-            res[name] = t
-        elif (tuple(t.shape) != tuple(shape) or t.dtype != torch.float32 or not t.is_contiguous()
-              or t.device != dev):
-            raise ValueError(f"out[{name!r}] must be a contiguous float32 {tuple(shape)} "
-                             f"tensor on {dev}")
-        return t
+    _get = _output_getter(res, dev)
 
     G = _get("G_W", (d_out, d_in))
     rho = _get("rho", (T, K)) if want_rho else None
@@ -271,17 +286,7 @@ def dust_estimate_head(X, W, labels, *, K: int, sigma: float, seed: int, antithe
     dt = _dtype_code(X)
     dev = X.device
     res = dict(out or {})
-
-    def _get(name, shape):
-        t = res.get(name)
-        if t is None:
-            t = torch.empty(shape, dtype=torch.float32, device=dev)
-            res[name] = t
-        elif (tuple(t.shape) != tuple(shape) or t.dtype != torch.float32 or not t.is_contiguous()
-              or t.device != dev):
-            raise ValueError(f"out[{name!r}] must be a contiguous float32 {tuple(shape)} "
-                             f"tensor on {dev}")
-        return t
+    _get = _output_getter(res, dev)
 
     G = _get("G_W", (V, d_in))
     loss = _get("loss", (T,)) if want_loss else None
@@ -297,6 +302,107 @@ def dust_estimate_head(X, W, labels, *, K: int, sigma: float, seed: int, antithe
         ptr(loss), ptr(rho), ptr(g), workspace.data_ptr(), workspace.numel(), _stream_ptr(dev))
     _check(status)
     return res
+
+
+def dust_embedding_workspace_bytes(T: int, V: int, d: int, K: int, antithetic: bool,
+                                   dtype: int) -> int:
+    return int(_load().dust_embedding_workspace_bytes(T, V, d, K, int(bool(antithetic)), dtype))
+
+
+def dust_reassemble_workspace_bytes(T: int, V: int, d: int) -> int:
+    return int(_load().dust_reassemble_workspace_bytes(T, V, d))
+
+
+def dust_validate_embedding(table_ptr, ids_ptr, target_ptr, T, V, d, seq_len, dtype, K, sigma,
+                            gamma, antithetic, scale, G_ptr, workspace_ptr,
+                            workspace_bytes) -> int:
+    """Raw host-side validation of dust_estimate_embedding's arguments; returns the status."""
+    return int(_load().dust_validate_embedding(table_ptr, ids_ptr, target_ptr, T, V, d, seq_len,
+                                               dtype, K, sigma, gamma, int(bool(antithetic)),
+                                               scale, G_ptr, workspace_ptr, workspace_bytes))
+
+
+def dust_validate_reassemble(ids_ptr, g_ptr, T, V, d, scale, G_ptr, workspace_ptr,
+                             workspace_bytes) -> int:
+    """Raw host-side validation of dust_reassemble_embedding's arguments; returns the status."""
+    return int(_load().dust_validate_reassemble(ids_ptr, g_ptr, T, V, d, scale, G_ptr,
+                                                workspace_ptr, workspace_bytes))
+
+
+def dust_estimate_embedding(table, ids, target, *, K: int, sigma: float, gamma: float, seed: int,
+                            antithetic: bool, seq_len: int, scale: float = 1.0,
+                            want_loss: bool = False, want_rho: bool = False,
+                            want_reward: bool = False, want_g: bool = False,
+                            out: dict | None = None, workspace=None):
+    """Enqueue dust_estimate_embedding (a token embedding: the gather of
+    table rows, the estimator, the scatter-add of g by id times `scale`) on
+    the current stream of the table's device.
+
+    table [V,d] and target [T,d] (both bfloat16 or both float32), ids [T]
+    (int32): contiguous device tensors.  Returns a dict of fp32 device
+    tensors: "G_E" [V,d] and the requested optional outputs "loss" [T],
+    "rho" [T,K], "reward" [T,K], "g" [T,d].  ``workspace``: a uint8 device
+    tensor of dust_embedding_workspace_bytes.
+    """
+    import torch
+    for name, t in (("table", table), ("ids", ids), ("target", target)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    if table.dtype != target.dtype:
+        raise TypeError("table and target must share one dtype")
+    if ids.dtype != torch.int32:
+        raise TypeError("ids must be int32")
+    if table.dim() != 2 or ids.dim() != 1 or target.dim() != 2 \
+            or tuple(target.shape) != (ids.shape[0], table.shape[1]):
+        raise ValueError(f"shape mismatch: table {tuple(table.shape)}, ids {tuple(ids.shape)}, "
+                         f"target {tuple(target.shape)}")
+    V, d = table.shape
+    T = ids.shape[0]
+    dt = _dtype_code(table)
+    dev = table.device
+    res = dict(out or {})
+    _get = _output_getter(res, dev)
+    G = _get("G_E", (V, d))
+    loss = _get("loss", (T,)) if want_loss else None
+    rho = _get("rho", (T, K)) if want_rho else None
+    reward = _get("reward", (T, K)) if want_reward else None
+    g = _get("g", (T, d)) if want_g else None
+    need = dust_embedding_workspace_bytes(T, V, d, K, antithetic, dt)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    ptr = lambda t: None if t is None else t.data_ptr()  # noqa: E731
+    status = _load().dust_estimate_embedding(
+        table.data_ptr(), ids.data_ptr(), target.data_ptr(), T, V, d, seq_len, dt, K, sigma,
+        gamma, ctypes.c_uint64(seed & 0xFFFFFFFFFFFFFFFF), int(bool(antithetic)), scale,
+        G.data_ptr(), ptr(loss), ptr(rho), ptr(reward), ptr(g), workspace.data_ptr(),
+        workspace.numel(), _stream_ptr(dev))
+    _check(status)
+    return res
+
+
+def dust_reassemble_embedding(ids, g, V: int, *, scale: float = 1.0, out=None, workspace=None):
+    """Enqueue dust_reassemble_embedding: G_E [V,d] = scale * the sum of the
+    rows of g [T,d] (float32) whose ids [T] (int32) select row v, in a fixed
+    order.  Returns G_E (``out`` if given: a contiguous float32 [V,d] tensor)."""
+    import torch
+    for name, t in (("ids", ids), ("g", g)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    if ids.dtype != torch.int32 or g.dtype != torch.float32:
+        raise TypeError("ids must be int32 and g float32")
+    if ids.dim() != 1 or g.dim() != 2 or g.shape[0] != ids.shape[0]:
+        raise ValueError(f"shape mismatch: ids {tuple(ids.shape)}, g {tuple(g.shape)}")
+    T, d = g.shape
+    dev = g.device
+    G = _output_getter({} if out is None else {"G_E": out}, dev)("G_E", (V, d))
+    need = dust_reassemble_workspace_bytes(T, V, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    status = _load().dust_reassemble_embedding(ids.data_ptr(), g.data_ptr(), T, V, d, scale,
+                                               G.data_ptr(), workspace.data_ptr(),
+                                               workspace.numel(), _stream_ptr(dev))
+    _check(status)
+    return G
 
 
 def dust_noise_fill(seed: int, n0: int, n_cnt: int, t0: int, t_cnt: int, d_out: int, *,

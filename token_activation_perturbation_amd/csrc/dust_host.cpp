@@ -124,6 +124,72 @@ dust_status_t dust_validate_head(const void* X, const void* W, const int32_t* la
                          workspace_bytes);
 }
 
+size_t dust_embedding_workspace_bytes(int64_t T, int64_t V, int64_t d, int32_t K,
+                                      int32_t antithetic, int32_t dtype) {
+  if (dtype != DUST_F32 && dtype != DUST_BF16) return 0;
+  dust::Plan p;
+  dust::ReassemblyPlan r;
+  size_t base = 0, total = 0;
+  if (!dust::make_embedding_plan(T, V, d, K, antithetic, dtype, &p, &r, &base, &total)) return 0;
+  return total;
+}
+
+size_t dust_reassemble_workspace_bytes(int64_t T, int64_t V, int64_t d) {
+  dust::ReassemblyPlan r;
+  if (!dust::make_reassembly_plan(T, V, d, &r)) return 0;
+  return r.total;
+}
+
+dust_status_t dust_validate_embedding(const void* table, const int32_t* ids,
+                                      const void* target, int64_t T, int64_t V, int64_t d,
+                                      int64_t seq_len, int32_t dtype, int32_t K, float sigma,
+                                      float gamma, int32_t antithetic, float scale,
+                                      const float* G_E, const void* workspace,
+                                      size_t workspace_bytes) {
+  if (!table || !ids || !target || !G_E)
+    return dust::fail(DUST_ERR_INVALID_ARG, "table, ids, target and G_E must not be NULL");
+  if ((uintptr_t)ids % 4 != 0)
+    return dust::fail(DUST_ERR_INVALID_ARG, "ids must be 4-byte aligned (int32)");
+  if (V <= 0 || V >= (int64_t(1) << 31))
+    return dust::fail(DUST_ERR_INVALID_ARG, "V=%lld must lie in [1, 2^31)", (long long)V);
+  if (!std::isfinite(scale))
+    return dust::fail(DUST_ERR_INVALID_ARG, "scale must be finite");
+  // the estimator's own checks, on a workspace of the estimator's size
+  const dust_status_t st = validate_common(T, 1, d, seq_len, dtype, K, sigma, gamma, antithetic,
+                                           workspace, (size_t)-1);
+  if (st != DUST_OK) return st;
+  dust::Plan p;
+  dust::ReassemblyPlan r;
+  size_t base = 0, total = 0;
+  if (!dust::make_embedding_plan(T, V, d, K, antithetic, dtype, &p, &r, &base, &total))
+    return dust::fail(DUST_ERR_UNSUPPORTED, "sizes exceed the kernels' index range");
+  if (!workspace || workspace_bytes < total)
+    return dust::fail(DUST_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed",
+                      workspace ? workspace_bytes : (size_t)0, total);
+  return dust::ok();
+}
+
+dust_status_t dust_validate_reassemble(const int32_t* ids, const float* g, int64_t T,
+                                       int64_t V, int64_t d, float scale, const float* G_E,
+                                       const void* workspace, size_t workspace_bytes) {
+  using dust::fail;
+  if (!ids || !g || !G_E) return fail(DUST_ERR_INVALID_ARG, "ids, g and G_E must not be NULL");
+  if ((uintptr_t)ids % 4 != 0 || (uintptr_t)g % 4 != 0 || (uintptr_t)G_E % 4 != 0)
+    return fail(DUST_ERR_INVALID_ARG, "ids, g and G_E must be 4-byte aligned");
+  if (T <= 0 || V <= 0 || d <= 0)
+    return fail(DUST_ERR_INVALID_ARG, "T=%lld, V=%lld, d=%lld must be positive", (long long)T,
+                (long long)V, (long long)d);
+  if (!std::isfinite(scale)) return fail(DUST_ERR_INVALID_ARG, "scale must be finite");
+  dust::ReassemblyPlan r;
+  if (!dust::make_reassembly_plan(T, V, d, &r))
+    return fail(DUST_ERR_UNSUPPORTED, "T=%lld, V=%lld, d=%lld exceed the kernels' index range",
+                (long long)T, (long long)V, (long long)d);
+  if (!workspace || workspace_bytes < r.total)
+    return fail(DUST_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed",
+                workspace ? workspace_bytes : (size_t)0, r.total);
+  return dust::ok();
+}
+
 const char* dust_last_error(void) { return g_last_error; }
 
 }  // extern "C"

@@ -27,6 +27,7 @@
 #include "dust_gemm.hpp"
 #include "dust_noise.hpp"
 #include "dust_plan.hpp"
+#include "dust_reassemble.hpp"
 
 namespace dust {
 namespace {
@@ -1130,6 +1131,47 @@ __global__ __launch_bounds__(256) void head_ce_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Token embedding, step 1: delta_t = E[id_t] - target_t (fp32), the gather
+// that takes the base GEMM's place.  One workgroup per token; VEC: four
+// consecutive columns per thread (d % 4 == 0, rows aligned).  Ids outside
+// [0, V) are clamped (memory-safe; the result is then unspecified).
+template <bool BF16, bool VEC>
+__global__ __launch_bounds__(256) void gather_delta_kernel(const void* __restrict__ table,
+                                                           const int32_t* __restrict__ ids,
+                                                           const void* __restrict__ target,
+                                                           int32_t V, int32_t d,
+                                                           float* __restrict__ delta) {
+  const int32_t t = blockIdx.x;
+  const int64_t row = (int64_t)reassemble::clamp_id(ids[t], V) * d;
+  const int64_t trow = (int64_t)t * d;
+  if (VEC) {
+    for (int32_t c = 4 * (int32_t)threadIdx.x; c < d; c += 1024) {
+      float4 a, b;
+      if (BF16) {
+        const uint2 ua = *(const uint2*)((const uint16_t*)table + row + c);
+        const uint2 ub = *(const uint2*)((const uint16_t*)target + trow + c);
+        a = make_float4(__uint_as_float(ua.x << 16), __uint_as_float(ua.x & 0xFFFF0000u),
+                        __uint_as_float(ua.y << 16), __uint_as_float(ua.y & 0xFFFF0000u));
+        b = make_float4(__uint_as_float(ub.x << 16), __uint_as_float(ub.x & 0xFFFF0000u),
+                        __uint_as_float(ub.y << 16), __uint_as_float(ub.y & 0xFFFF0000u));
+      } else {
+        a = *(const float4*)((const float*)table + row + c);
+        b = *(const float4*)((const float*)target + trow + c);
+      }
+      *(float4*)(delta + trow + c) = make_float4(a.x - b.x, a.y - b.y, a.z - b.z, a.w - b.w);
+    }
+  } else {
+    for (int32_t c = threadIdx.x; c < d; c += 256) {
+      const float a = BF16 ? bf16_to_f32(((const uint16_t*)table)[row + c])
+                           : ((const float*)table)[row + c];
+      const float b = BF16 ? bf16_to_f32(((const uint16_t*)target)[trow + c])
+                           : ((const float*)target)[trow + c];
+      delta[trow + c] = a - b;
+    }
+  }
+}
+
 // Bench hook state: event pairs stamped by the dispatch of the noise kernel
 // of the next dust_estimate calls (hipExtLaunchKernelGGL's start and stop
 // events, so they time the kernel itself, not the gap before it), pair i on
@@ -1291,21 +1333,115 @@ void launch_outer(const Plan& p, const void* X, const float* g32, const uint16_t
   }
 }
 
-// Both estimators after validation.  E == nullptr: the layer-local loss
-// (delta = W x - target from the base GEMM, rho the loss reductions).
-// E != nullptr: local scoring (delta = E, the supplied error estimate; no
-// base GEMM; rho the linear scores, no curvature term; no clean loss).
-dust_status_t run_estimate(const void* X, const void* W, const void* target, const float* E,
-                           int64_t T, int64_t d_in, int64_t d_out, int64_t seq_len,
-                           int32_t dtype, int32_t K, float sigma, float gamma, uint64_t seed,
-                           int32_t antithetic, float* G_W, float* loss_clean, float* rho,
-                           float* reward, float* g, void* workspace, void* stream) {
-  const bool local = E != nullptr;
+// delta = table[ids] - target -> [T][d] fp32
+void launch_gather(const void* table, const int32_t* ids, const void* target, int64_t T,
+                   int64_t V, int64_t d, int32_t dtype, float* delta, hipStream_t s) {
+  const bool bf16 = dtype == DUST_BF16;
+  const uintptr_t align = bf16 ? 8 : 16;
+  const bool vec = d % 4 == 0 && (uintptr_t)table % align == 0 && (uintptr_t)target % align == 0;
+#define DUST_GATHER(B, VC)                                                                 \
+  hipLaunchKernelGGL((gather_delta_kernel<B, VC>), dim3((unsigned)T), dim3(256), 0, s, table, \
+                     ids, target, (int32_t)V, (int32_t)d, delta)
+  if (bf16) {
+    if (vec) DUST_GATHER(true, true); else DUST_GATHER(true, false);
+  } else {
+    if (vec) DUST_GATHER(false, true); else DUST_GATHER(false, false);
+  }
+#undef DUST_GATHER
+}
+
+// G_E = scale x the scatter-add of g [T][d] by ids, in a fixed order, with
+// the reassembly's workspace at `base`.
+void launch_reassemble(const ReassemblyPlan& r, char* base, const int32_t* ids, const float* g,
+                       float scale, float* G_E, hipStream_t s) {
+  int32_t* hist = (int32_t*)(base + r.off_hist);
+  int32_t* count = (int32_t*)(base + r.off_count);
+  int32_t* start = (int32_t*)(base + r.off_start);
+  int32_t* perm = (int32_t*)(base + r.off_perm);
+  int32_t* sid = (int32_t*)(base + r.off_sid);
+  float* part = (float*)(base + r.off_part);
+  const int32_t T = (int32_t)r.T, V = (int32_t)r.V, d = (int32_t)r.d;
+  const unsigned chunks = (unsigned)r.n_chunks;
+  const bool small_v = r.V <= kLdsHistMaxV;
+  if (small_v) {
+    hipLaunchKernelGGL(reassemble::hist_kernel<true>, dim3(chunks), dim3(256),
+                       sizeof(int32_t) * (size_t)V, s, ids, T, V, r.chunk_tokens, r.n_chunks,
+                       hist);
+  } else {
+    const int64_t n = r.V * (int64_t)r.n_chunks;
+    hipLaunchKernelGGL(reassemble::zero_kernel, dim3(grid_for(n < 262144 ? n : 262144, 256)),
+                       dim3(256), 0, s, hist, n);
+    hipLaunchKernelGGL(reassemble::hist_kernel<false>, dim3(chunks), dim3(256), 0, s, ids, T, V,
+                       r.chunk_tokens, r.n_chunks, hist);
+  }
+  const bool vec = d % 4 == 0 && (uintptr_t)g % 16 == 0 && (uintptr_t)G_E % 16 == 0;
+  if (vec)
+    hipLaunchKernelGGL(reassemble::colscan_kernel<true>, dim3(grid_for(V, 4)), dim3(256), 0, s,
+                       hist, r.n_chunks, V, d, count, G_E);
+  else
+    hipLaunchKernelGGL(reassemble::colscan_kernel<false>, dim3(grid_for(V, 4)), dim3(256), 0, s,
+                       hist, r.n_chunks, V, d, count, G_E);
+  if (small_v) {
+    hipLaunchKernelGGL(reassemble::place_kernel<true>, dim3(chunks), dim3(256),
+                       sizeof(int32_t) * (size_t)(V + 1), s, ids, T, V, r.chunk_tokens,
+                       r.n_chunks, hist, (const int32_t*)count, start, perm, sid);
+  } else {
+    hipLaunchKernelGGL(reassemble::start_scan_kernel, dim3(1), dim3(1024), 0, s,
+                       (const int32_t*)count, V, start);
+    hipLaunchKernelGGL(reassemble::place_kernel<false>, dim3(chunks), dim3(256), 0, s, ids, T, V,
+                       r.chunk_tokens, r.n_chunks, hist, (const int32_t*)count, start, perm, sid);
+  }
+  const int64_t tile_units = r.n_tiles * r.col_chunks;
+#define DUST_REASSEMBLE(VC)                                                                    \
+  hipLaunchKernelGGL((reassemble::tile_kernel<VC>), dim3(grid_for(tile_units, 4)), dim3(256), 0,  \
+                     s, g, (const int32_t*)perm, (const int32_t*)sid, T, d, r.col_chunks,        \
+                     tile_units, scale, part, G_E);                                             \
+  hipLaunchKernelGGL((reassemble::fixup_kernel<VC>), dim3(grid_for(tile_units, 4)), dim3(256), 0, \
+                     s, (const int32_t*)sid, (const int32_t*)start, T, (const float*)part, d,   \
+                     r.col_chunks, tile_units, scale, G_E)
+  if (vec) {
+    DUST_REASSEMBLE(true);
+  } else {
+    DUST_REASSEMBLE(false);
+  }
+#undef DUST_REASSEMBLE
+}
+
+// What one estimate is about: a layer (X, W, target), local scoring of a
+// layer (X, E), or a token embedding (the table in W, ids, target; its
+// reassembled gradient, times `scale`, goes where G_W goes).
+struct Site {
+  const void* X = nullptr;
+  const void* W = nullptr;
+  const void* target = nullptr;
+  const float* E = nullptr;
+  const int32_t* ids = nullptr;
+  int64_t V = 0;
+  float scale = 1.0f;
+};
+
+// Every estimator but the head's, after validation: the layer-local loss
+// (delta = W x - target from the base GEMM, rho the loss reductions); local
+// scoring (st.E: delta = E, the supplied error estimate; no base GEMM; rho
+// the linear scores, no curvature term; no clean loss); or a token embedding
+// (st.ids: delta = table[ids] - target from a gather; G_W <- scale x the
+// reassembled G_E).
+dust_status_t run_estimate(const Site& st, int64_t T, int64_t d_in, int64_t d_out,
+                           int64_t seq_len, int32_t dtype, int32_t K, float sigma, float gamma,
+                           uint64_t seed, int32_t antithetic, float* G_W, float* loss_clean,
+                           float* rho, float* reward, float* g, void* workspace, void* stream) {
+  const bool local = st.E != nullptr;
+  const bool embed = st.ids != nullptr;
   Plan p;
-  make_plan(T, d_in, d_out, K, antithetic, dtype, &p);
+  ReassemblyPlan rp;
+  size_t r_base = 0, total = 0;
+  if (embed)
+    make_embedding_plan(T, st.V, d_out, K, antithetic, dtype, &p, &rp, &r_base, &total);
+  else
+    make_plan(T, d_in, d_out, K, antithetic, dtype, &p);
   hipStream_t s = (hipStream_t)stream;
   char* ws = (char*)workspace;
-  float* delta = local ? const_cast<float*>(E) : (float*)(ws + p.off_delta);
+  float* delta = local ? const_cast<float*>(st.E) : (float*)(ws + p.off_delta);
   if (local) loss_clean = nullptr;
   // rho's curvature term: sigma^2 / 2 for the quadratic loss, none for the
   // linear local score
@@ -1318,17 +1454,22 @@ dust_status_t run_estimate(const void* X, const void* W, const void* target, con
   float* wgt = (float*)(ws + p.off_wgt);
   // g: fp32 for the f32 path (the caller's buffer when requested); for bf16
   // the outer product reads the bf16 split g_hi + g_lo from the workspace,
-  // and fp32 g is written only when requested
-  const bool bf16 = dtype == DUST_BF16;
-  float* g32 = bf16 ? g : (g ? g : (float*)(ws + p.off_g));
-  uint16_t* g_hi = bf16 ? (uint16_t*)(ws + p.off_g) : nullptr;
-  uint16_t* g_lo = bf16 ? g_hi + T * d_out : nullptr;
+  // and fp32 g is written only when requested; the embedding's reassembly
+  // reads fp32 g
+  const bool split = dtype == DUST_BF16 && !embed;
+  float* g32 = split ? g : (g ? g : (float*)(ws + p.off_g));
+  uint16_t* g_hi = split ? (uint16_t*)(ws + p.off_g) : nullptr;
+  uint16_t* g_lo = split ? g_hi + T * d_out : nullptr;
   float* gpart = (float*)(ws + p.off_gpart);
   const NoiseKey key = make_key(seed);
   const int32_t Ti = (int32_t)T, di = (int32_t)d_in, dout = (int32_t)d_out;
 
-  // 1. base GEMM -> delta (the caller's error estimate itself when local)
-  if (!local) launch_base_gemm(X, W, target, T, d_in, d_out, dtype, delta, s);
+  // 1. base GEMM -> delta (the caller's error estimate itself when local;
+  //    the gather of table rows for an embedding)
+  if (embed)
+    launch_gather(st.W, st.ids, st.target, T, st.V, d_out, dtype, delta, s);
+  else if (!local)
+    launch_base_gemm(st.X, st.W, st.target, T, d_in, d_out, dtype, delta, s);
   const int qpl = fused_qpl(p.nq);
   const bool independent = (gamma == 0.0f || seq_len == 1);
   const bool fused = independent && qpl > 0;
@@ -1391,8 +1532,11 @@ dust_status_t run_estimate(const void* X, const void* W, const void* target, con
   }
 
   // 6. outer product -> the split partials (or G_W itself with one split),
-  //    then their fixed-order sum
-  launch_outer(p, X, g32, g_hi, g_lo, gpart, G_W, T, d_in, d_out, dtype, s);
+  //    then their fixed-order sum; for an embedding the reassembly
+  if (embed)
+    launch_reassemble(rp, ws + r_base, st.ids, g32, st.scale, G_W, s);
+  else
+    launch_outer(p, st.X, g32, g_hi, g_lo, gpart, G_W, T, d_in, d_out, dtype, s);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(DUST_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return ok();
@@ -1453,7 +1597,11 @@ dust_status_t dust_estimate(const void* X, const void* W, const void* target, in
                                          sigma, gamma, antithetic, G_W, workspace,
                                          workspace_bytes);
   if (st != DUST_OK) return st;
-  return dust::run_estimate(X, W, target, nullptr, T, d_in, d_out, seq_len, dtype, K, sigma,
+  dust::Site site;
+  site.X = X;
+  site.W = W;
+  site.target = target;
+  return dust::run_estimate(site, T, d_in, d_out, seq_len, dtype, K, sigma,
                             gamma, seed, antithetic, G_W, loss_clean, rho, reward, g, workspace,
                             stream);
 }
@@ -1467,7 +1615,10 @@ dust_status_t dust_estimate_local(const void* X, const float* E, int64_t T, int6
                                                gamma, antithetic, G_W, workspace,
                                                workspace_bytes);
   if (st != DUST_OK) return st;
-  return dust::run_estimate(X, nullptr, nullptr, E, T, d_in, d_out, seq_len, dtype, K, sigma,
+  dust::Site site;
+  site.X = X;
+  site.E = E;
+  return dust::run_estimate(site, T, d_in, d_out, seq_len, dtype, K, sigma,
                             gamma, seed, antithetic, G_W, nullptr, rho, reward, g, workspace,
                             stream);
 }
@@ -1482,6 +1633,42 @@ dust_status_t dust_estimate_head(const void* X, const void* W, const int32_t* la
   if (st != DUST_OK) return st;
   return dust::run_head(X, W, labels, T, d_in, V, dtype, K, sigma, seed, antithetic, G_W,
                         loss_clean, rho, g, workspace, stream);
+}
+
+dust_status_t dust_estimate_embedding(const void* table, const int32_t* ids, const void* target,
+                                      int64_t T, int64_t V, int64_t d, int64_t seq_len,
+                                      int32_t dtype, int32_t K, float sigma, float gamma,
+                                      uint64_t seed, int32_t antithetic, float scale, float* G_E,
+                                      float* loss_clean, float* rho, float* reward, float* g,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+  const dust_status_t st =
+      dust_validate_embedding(table, ids, target, T, V, d, seq_len, dtype, K, sigma, gamma,
+                              antithetic, scale, G_E, workspace, workspace_bytes);
+  if (st != DUST_OK) return st;
+  dust::Site site;
+  site.W = table;
+  site.ids = ids;
+  site.target = target;
+  site.V = V;
+  site.scale = scale;
+  return dust::run_estimate(site, T, 1, d, seq_len, dtype, K, sigma, gamma, seed, antithetic,
+                            G_E, loss_clean, rho, reward, g, workspace, stream);
+}
+
+dust_status_t dust_reassemble_embedding(const int32_t* ids, const float* g, int64_t T,
+                                        int64_t V, int64_t d, float scale, float* G_E,
+                                        void* workspace, size_t workspace_bytes,
+                                        void* stream) {
+  const dust_status_t st =
+      dust_validate_reassemble(ids, g, T, V, d, scale, G_E, workspace, workspace_bytes);
+  if (st != DUST_OK) return st;
+  dust::ReassemblyPlan r;
+  dust::make_reassembly_plan(T, V, d, &r);
+  dust::launch_reassemble(r, (char*)workspace, ids, g, scale, G_E, (hipStream_t)stream);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess)
+    return dust::fail(DUST_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return dust::ok();
 }
 
 dust_status_t dust_set_timing_events(void* const* start, void* const* stop, int32_t n_pairs) {

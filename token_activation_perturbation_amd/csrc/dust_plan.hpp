@@ -139,4 +139,81 @@ inline bool make_plan(int64_t T, int64_t d_in, int64_t d_out, int32_t K,
   return true;
 }
 
+// ---------------------------------------------------------------------------
+// Embedding reassembly: G_E[v] = scale sum_{t: ids[t] = v} g[t], by a stable
+// counting sort of the token positions by id (per-chunk histograms, their
+// prefix sums over chunks, a scan of the totals, a placement pass), then a
+// reduce-by-key over fixed tiles of the sorted order and a fix-up that sums
+// the partials of the ids whose rows cross tiles.
+
+// Sorted rows per reduce tile, histogram entries (chunks x V) allowed, and
+// the largest V whose per-chunk histogram and run starts are kept in LDS
+// (V + 1 ints and the kernels' static LDS within 64 KiB).
+constexpr int32_t kReassembleTile = 32;
+constexpr int64_t kHistCap = int64_t(1) << 22;
+constexpr int64_t kLdsHistMaxV = 15360;
+
+struct ReassemblyPlan {
+  int64_t T = 0, V = 0, d = 0;
+  int32_t n_chunks = 1;      // token chunks, one workgroup each (hist, place)
+  int64_t chunk_tokens = 0;  // tokens per chunk (multiple of 256)
+  int64_t n_tiles = 0;       // reduce tiles of kReassembleTile sorted rows
+  int32_t col_chunks = 0;    // 256-column chunks of a row (64 lanes x 4)
+  // byte offsets (each 256-byte aligned), relative to the plan's base, and
+  // total: hist [V][n_chunks], count [V], start [V + 1], perm and sid [T],
+  // the partial rows [n_tiles][2][d]
+  size_t off_hist = 0, off_count = 0, off_start = 0, off_perm = 0, off_sid = 0, off_part = 0,
+         total = 0;
+};
+
+// Returns false when the sizes cannot be planned (T <= 0, V <= 0, d <= 0, or
+// past the kernels' index range).
+inline bool make_reassembly_plan(int64_t T, int64_t V, int64_t d, ReassemblyPlan* r) {
+  if (T <= 0 || V <= 0 || d <= 0) return false;
+  if (T >= (int64_t(1) << 24) || V >= (int64_t(1) << 31) || d >= (int64_t(1) << 31)) return false;
+  ReassemblyPlan q;
+  q.T = T;
+  q.V = V;
+  q.d = d;
+  int64_t chunks = ceil_div(T, 256);
+  if (chunks > 1024) chunks = 1024;
+  const int64_t cap = kHistCap / V;
+  if (chunks > cap) chunks = cap;
+  if (chunks < 1) chunks = 1;
+  q.chunk_tokens = ceil_div(ceil_div(T, chunks), 256) * 256;
+  q.n_chunks = (int32_t)ceil_div(T, q.chunk_tokens);
+  q.n_tiles = ceil_div(T, kReassembleTile);
+  const int64_t col_chunks = ceil_div(d, 256);
+  if (col_chunks * q.n_tiles >= (int64_t(1) << 31) || col_chunks * V >= (int64_t(1) << 31))
+    return false;
+  q.col_chunks = (int32_t)col_chunks;
+  size_t off = 0;
+  auto take = [&off](size_t bytes) {
+    size_t at = off;
+    off = align256(off + bytes);
+    return at;
+  };
+  q.off_hist = take(sizeof(int32_t) * size_t(q.n_chunks) * size_t(V));
+  q.off_count = take(sizeof(int32_t) * size_t(V));
+  q.off_start = take(sizeof(int32_t) * size_t(V + 1));
+  q.off_perm = take(sizeof(int32_t) * size_t(T));
+  q.off_sid = take(sizeof(int32_t) * size_t(T));
+  q.off_part = take(sizeof(float) * size_t(q.n_tiles) * 2 * size_t(d));
+  q.total = off;
+  *r = q;
+  return true;
+}
+
+// The embedding estimator's workspace: the estimator's own regions (as for a
+// layer with d_out = d; no outer product, so d_in = 1), then the reassembly's.
+inline bool make_embedding_plan(int64_t T, int64_t V, int64_t d, int32_t K, int32_t antithetic,
+                                int32_t dtype, Plan* p, ReassemblyPlan* r, size_t* r_base,
+                                size_t* total) {
+  if (!make_plan(T, 1, d, K, antithetic, dtype, p)) return false;
+  if (!make_reassembly_plan(T, V, d, r)) return false;
+  *r_base = align256(p->total);
+  *total = *r_base + r->total;
+  return true;
+}
+
 }  // namespace dust
