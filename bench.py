@@ -31,8 +31,10 @@ if ROOT not in sys.path:
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 CAL_COPY_BYTES = 256 << 20
-KERNEL_SOURCES = ["token_activation_perturbation_amd/csrc/dust_kernels.hip",
-                  "token_activation_perturbation_amd/csrc/dust_noise.hpp"]
+# every source the kernels and their launch configuration are built from
+KERNEL_SOURCES = ["token_activation_perturbation_amd/csrc/" + f for f in (
+    "dust_kernels.hip", "dust_noise.hpp", "dust_gemm.hpp", "dust_reassemble.hpp",
+    "dust_plan.hpp")]
 
 
 def kernel_source_hash() -> str:
