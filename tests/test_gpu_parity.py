@@ -291,6 +291,28 @@ def test_misaligned_inputs_take_the_guarded_loads(dev, oracle_mod, threads):
     assert rel(out["G_W"].cpu().numpy().astype(np.float64), ref["G"]) <= TOL["bf16"]
 
 
+def test_misaligned_target_takes_the_guarded_epilogue(dev, oracle_mod, threads):
+    """X and W aligned (the direct-to-LDS base GEMM runs) but target a view
+    starting one element into its storage: the epilogue must fall back from
+    its 16-byte target loads to element-wise ones."""
+    import torch
+    import token_activation_perturbation_amd as dust
+    T, d_in, d_out = 128, 64, 64
+    inp = synth.random_inputs(T, d_in, d_out, "bf16", seed=6)
+    kw = dict(K=8, sigma=1e-2, gamma=0.0, seed=5, antithetic=True, seq_len=64)
+    Xd, Wd = (torch.from_numpy(inp[k]).to(dev).to(torch.bfloat16).contiguous() for k in ("X", "W"))
+    flat = torch.zeros(inp["target"].size + 1, dtype=torch.bfloat16, device=dev)
+    flat[1:] = torch.from_numpy(inp["target"].ravel()).to(dev).to(torch.bfloat16)
+    td = flat[1:].view(inp["target"].shape)
+    assert td.data_ptr() % 16 != 0 and Xd.data_ptr() % 16 == 0
+    out = dust.dust_estimate(Xd, Wd, td, want_loss=True, want_g=True, **kw)
+    torch.cuda.synchronize(dev)
+    ref = oracle_mod.estimate(inp["X"], inp["W"], inp["target"], threads=threads, **kw)
+    assert rel(out["loss"].cpu().numpy().astype(np.float64), ref["loss"]) <= TOL["bf16"]
+    assert rel(out["g"].cpu().numpy().astype(np.float64), ref["g"]) <= TOL["bf16"]
+    assert rel(out["G_W"].cpu().numpy().astype(np.float64), ref["G"]) <= TOL["bf16"]
+
+
 def test_small_workspace_is_an_error(dev):
     import torch
     import token_activation_perturbation_amd as dust

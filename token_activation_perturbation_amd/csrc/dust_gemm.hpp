@@ -454,5 +454,310 @@ __global__ __launch_bounds__(256) void tn_outer_kernel(
       }
 }
 
+// ---------------------------------------------------------------------------
+// The outer product fed by gfx950's direct-to-LDS loads
+// (global_load_lds_dwordx4: lane l's 16 bytes land at the instruction's LDS
+// base + 16 l, measured on MI355X), for the aligned case (M and N multiples of
+// 8, g_hi, g_lo and X 16-byte aligned).  Same work split, contraction order
+// and results (bitwise) as tn_outer_kernel; no registers stage the tiles and
+// no LDS store instructions run, so three workgroups fit a CU (48 KiB of LDS
+// each) and the loads overlap the MFMAs of the other workgroups.
+//
+// A tile is 64 tokens x 64 channels bf16, a token per 128-byte LDS row whose
+// eight 16-byte slots hold the channel chunks permuted: chunk c of row r sits
+// in slot c ^ tr_swz(r).  Each DMA instruction fills 8 rows (1 KiB): lane l
+// fetches row 8 i + l / 8, chunk (l % 8) ^ tr_swz(row), so its 16 bytes land
+// in the right slot.  tr_swz was chosen by an exhaustive search over XOR maps
+// of the row bits so that the transposing fragment reads (frag_sw) are free
+// of bank conflicts per half-wave on 64 banks.  Two LDS stages: the loads of
+// k-block kt + 1 are issued right after the barrier that opens step kt.
+// Token rows past T re-read row T - 1, channel chunks past the edge re-read
+// the last full chunk (their outputs are never stored); g rows past the
+// split's end are zeroed in LDS before the MFMAs read them.
+
+__device__ __forceinline__ int tr_swz(int r) { return (r & 2) | ((r >> 1) & 4); }
+
+// s_waitcnt vmcnt(N) (gfx9 encoding: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8],
+// vmcnt[15:14]; the other counters left unconstrained)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
+
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+
+// frag_tr's fragment from a slot-permuted tile (rows of 128 bytes)
+__device__ __forceinline__ u16x8_t frag_sw(const uint8_t* tile, int ch0, int k0, int lane) {
+  const int tok = k0 + 8 * (lane >> 4) + ((lane & 15) >> 2);
+  const int ch = ch0 + 4 * (lane & 3);
+  const int c = ch >> 3, eb = (ch & 7) * 2;
+  typedef __attribute__((address_space(3))) v4i16_t* lds_v4_ptr;
+  const uint8_t* p0 = tile + tok * 128 + 16 * (c ^ tr_swz(tok)) + eb;
+  const uint8_t* p1 = tile + (tok + 4) * 128 + 16 * (c ^ tr_swz(tok + 4)) + eb;
+  const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4_ptr)p0);
+  const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4_ptr)p1);
+  return __builtin_bit_cast(u16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+__global__ __launch_bounds__(256) void tn_outer_dma_kernel(
+    const uint16_t* __restrict__ g_hi, const uint16_t* __restrict__ g_lo,
+    const uint16_t* __restrict__ X, int32_t T, int32_t M, int32_t N, int32_t tiles_m,
+    int32_t tiles_n, int32_t splits, int32_t per_xcd, int64_t t_first, int64_t t_per_split,
+    int32_t partial, float* __restrict__ out) {
+  constexpr int BK = 64, TB = BK * 128, NS = 2;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[NS * 3 * TB];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const TileWork work = map_tile(tiles_m, tiles_n, splits, per_xcd);
+  if (!work.valid) return;
+  const int64_t m0 = (int64_t)work.m_tile * 64;
+  const int64_t n0 = (int64_t)work.n_tile * 64;
+  const int64_t t_begin = t_first + (int64_t)work.split * t_per_split;
+  const int64_t t_end = min((int64_t)T, t_begin + t_per_split);
+  const int nk = (int)((t_end - t_begin + BK - 1) / BK);
+
+  // this lane's two DMA rows (instructions 2 wave and 2 wave + 1 of a tile)
+  // and the chunks it fetches for them
+  int rq[2];
+  int64_t a_ch[2], b_ch[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int r = 8 * (2 * wave + q) + (lane >> 3);
+    const int c = (lane & 7) ^ tr_swz(r);
+    rq[q] = r;
+    const int64_t am = m0 + 8 * c, bn = n0 + 8 * c;
+    a_ch[q] = am < M ? am : M - 8;
+    b_ch[q] = bn < N ? bn : N - 8;
+  }
+  auto issue = [&](int buf, int kt) {
+    const int64_t tb = t_begin + (int64_t)kt * BK;
+    uint8_t* base = lds + buf * 3 * TB;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      int64_t t = tb + rq[q];
+      t = t < T ? t : (int64_t)T - 1;
+      const int dst = (2 * wave + q) * 1024;
+      __builtin_amdgcn_global_load_lds(g_hi + t * M + a_ch[q], (lds_void_ptr)(base + dst), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(g_lo + t * M + a_ch[q], (lds_void_ptr)(base + TB + dst), 16,
+                                       0, 0);
+      __builtin_amdgcn_global_load_lds(X + t * N + b_ch[q], (lds_void_ptr)(base + 2 * TB + dst),
+                                       16, 0, 0);
+    }
+  };
+
+  f32x4_t acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  if (nk > 0) issue(0, 0);
+  for (int kt = 0; kt < nk; ++kt) {
+    wait_vmcnt<0>();  // this wave's loads of block kt have landed
+    __syncthreads();  // ... and every wave's; block kt - 1 is no longer read
+    const int buf = kt & 1;
+    uint8_t* base = lds + buf * 3 * TB;
+    const int64_t left = t_end - (t_begin + (int64_t)kt * BK);
+    if (left < BK) {
+      // g rows past the split's end (rows keep their place; slots permute
+      // within a row)
+      const int from = (int)(left < 0 ? 0 : left) * 128;
+      for (int o = from + 16 * tid; o < TB; o += 16 * 256) {
+        *(u32x4_t*)(base + o) = u32x4_t{0u, 0u, 0u, 0u};
+        *(u32x4_t*)(base + TB + o) = u32x4_t{0u, 0u, 0u, 0u};
+      }
+      __syncthreads();
+    }
+    if (kt + 1 < nk) issue(buf ^ 1, kt + 1);
+#pragma unroll
+    for (int ks = 0; ks < BK; ks += 32) {
+      u16x8_t ah[2], al[2], bf[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        ah[i] = frag_sw(base, wm * 32 + i * 16, ks, lane);
+        al[i] = frag_sw(base + TB, wm * 32 + i * 16, ks, lane);
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) bf[j] = frag_sw(base + 2 * TB, wn * 32 + j * 16, ks, lane);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          acc[i][j] = mfma16(ah[i], bf[j], acc[i][j]);
+          acc[i][j] = mfma16(al[i], bf[j], acc[i][j]);
+        }
+    }
+  }
+  float* dst = partial ? out + (int64_t)work.split * M * N : out;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t row = m0 + wm * 32 + i * 16 + 4 * (lane >> 4) + e;
+        const int64_t col = n0 + wn * 32 + j * 16 + (lane & 15);
+        if (row < M && col < N) dst[row * N + col] = acc[i][j][e];
+      }
+}
+
+// ---------------------------------------------------------------------------
+// The base GEMM fed by direct-to-LDS loads, for the aligned case (K a
+// multiple of 8; A, B 16-byte aligned; lda, ldb multiples of 8).  Same tiles,
+// contraction order and results (bitwise) as nt_gemm_kernel; two LDS stages
+// of 16 KiB.  An operand tile is 64 rows x 64 contraction values bf16, a row
+// per 128 bytes, chunk c of row r in slot c ^ nt_swz(r): the 16-byte fragment
+// reads (16 rows of one chunk per quarter-wave) then hit every bank once
+// (nt_swz found by the same exhaustive search as tr_swz).  Rows past M or N
+// re-read the last row (their outputs are never stored); chunks past K
+// re-read the last chunk, and A's are zeroed in LDS so they add nothing.
+// With a target, the epilogue goes through LDS so that target is read and
+// delta written in 16-byte pieces along rows; the plain product (a head's
+// logits) is stored straight from the MFMA layout, which measured faster.
+
+__device__ __forceinline__ int nt_swz(int r) { return (r >> 1) & 7; }
+
+template <bool TARGET>
+__global__ __launch_bounds__(256) void nt_gemm_dma_kernel(
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, int64_t lda, int64_t ldb,
+    int32_t M, int32_t N, int64_t K, int32_t tiles_m, int32_t tiles_n, int32_t per_xcd,
+    const uint16_t* __restrict__ target, float* __restrict__ out) {
+  constexpr int BK = 64, TB = 64 * 128, NS = 2;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[NS * 2 * TB];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const TileWork work = map_tile(tiles_m, tiles_n, 1, per_xcd);
+  if (!work.valid) return;
+  const int64_t m0 = (int64_t)work.m_tile * 64;
+  const int64_t n0 = (int64_t)work.n_tile * 64;
+  const int nk = (int)((K + BK - 1) / BK);
+
+  // this lane's two DMA rows and the chunk it fetches for them
+  int ck[2];
+  int64_t a_row[2], b_row[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int r = 8 * (2 * wave + q) + (lane >> 3);
+    ck[q] = (lane & 7) ^ nt_swz(r);
+    a_row[q] = m0 + r < M ? m0 + r : M - 1;
+    b_row[q] = n0 + r < N ? n0 + r : N - 1;
+  }
+  auto issue = [&](int buf, int kt) {
+    uint8_t* base = lds + buf * 2 * TB;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      int64_t k = (int64_t)kt * BK + 8 * ck[q];
+      k = k < K ? k : K - 8;
+      const int dst = (2 * wave + q) * 1024;
+      __builtin_amdgcn_global_load_lds(A + a_row[q] * lda + k, (lds_void_ptr)(base + dst), 16, 0,
+                                       0);
+      __builtin_amdgcn_global_load_lds(B + b_row[q] * ldb + k, (lds_void_ptr)(base + TB + dst), 16,
+                                       0, 0);
+    }
+  };
+
+  f32x4_t acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  if (nk > 0) issue(0, 0);
+  for (int kt = 0; kt < nk; ++kt) {
+    wait_vmcnt<0>();  // this wave's loads of block kt have landed
+    __syncthreads();  // ... and every wave's; block kt - 1 is no longer read
+    const int buf = kt & 1;
+    uint8_t* base = lds + buf * 2 * TB;
+    const int64_t left = K - (int64_t)kt * BK;
+    if (left < BK) {
+      const int row = tid >> 2;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int slot = 2 * (tid & 3) + h;
+        if (8 * (slot ^ nt_swz(row)) >= left)
+          *(u32x4_t*)(base + row * 128 + 16 * slot) = u32x4_t{0u, 0u, 0u, 0u};
+      }
+      __syncthreads();
+    }
+    if (kt + 1 < nk) issue(buf ^ 1, kt + 1);
+#pragma unroll
+    for (int ks = 0; ks < BK; ks += 32) {
+      u16x8_t af[2], bfr[2];
+      const int ch = ks / 8 + (lane >> 4);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int r = wm * 32 + i * 16 + (lane & 15);
+        af[i] = *(const u16x8_t*)(base + r * 128 + 16 * (ch ^ nt_swz(r)));
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int r = wn * 32 + j * 16 + (lane & 15);
+        bfr[j] = *(const u16x8_t*)(base + TB + r * 128 + 16 * (ch ^ nt_swz(r)));
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma16(af[i], bfr[j], acc[i][j]);
+    }
+  }
+  if constexpr (!TARGET) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int64_t row = m0 + wm * 32 + i * 16 + 4 * (lane >> 4) + e;
+          const int64_t col = n0 + wn * 32 + j * 16 + (lane & 15);
+          if (row < M && col < N) out[row * N + col] = acc[i][j][e];
+        }
+  } else {
+    // the 64 x 64 fp32 tile through LDS (row pitch 68 floats), then a row
+    // segment of 16 per thread
+    constexpr int CP = 68;
+    float* ct = (float*)lds;
+    __syncthreads();  // every wave is done with the operand tiles
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          ct[(wm * 32 + i * 16 + 4 * (lane >> 4) + e) * CP + wn * 32 + j * 16 + (lane & 15)] =
+              acc[i][j][e];
+    __syncthreads();
+    const int r = tid >> 2, c0 = (tid & 3) * 16;
+    const int64_t row = m0 + r;
+    if (row < M) {
+      const float* src = ct + r * CP + c0;
+      float* dst = out + row * N + n0 + c0;
+      const uint16_t* tp = target + row * N + n0 + c0;
+      const int64_t ncols = N - (n0 + c0);  // columns left in this row
+      // 16-byte pieces need whole rows of 8-element multiples and aligned bases
+      const bool aligned = ((N & 7) == 0) && (((uintptr_t)target | (uintptr_t)out) & 15) == 0;
+      if (ncols >= 16 && aligned) {
+        float4 v[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = *(const float4*)(src + 4 * q);
+        const u32x4_t t0 = *(const u32x4_t*)tp, t1 = *(const u32x4_t*)(tp + 8);
+        const uint32_t tw[8] = {t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          v[q].x -= __uint_as_float(tw[2 * q] << 16);
+          v[q].y -= __uint_as_float(tw[2 * q] & 0xFFFF0000u);
+          v[q].z -= __uint_as_float(tw[2 * q + 1] << 16);
+          v[q].w -= __uint_as_float(tw[2 * q + 1] & 0xFFFF0000u);
+          *(float4*)(dst + 4 * q) = v[q];
+        }
+      } else {
+        for (int q = 0; q < 16 && q < ncols; ++q) dst[q] = src[q] - bf16_bits_to_f32(tp[q]);
+      }
+    }
+  }
+}
+
 }  // namespace gemm
 }  // namespace dust

@@ -1279,11 +1279,17 @@ void launch_base_gemm(const void* X, const void* W, const void* target, int64_t 
                      (const uint16_t*)X, (const uint16_t*)W, (int64_t)d_in, (int64_t)d_in, \
                      Ti, dout, (int64_t)d_in, tiles_m, tiles_n, per_xcd,                    \
                      (const uint16_t*)target, out)
+#define DUST_BASE_DMA(TG)                                                                   \
+  hipLaunchKernelGGL((gemm::nt_gemm_dma_kernel<TG>), grid, dim3(256), 0, s, (const uint16_t*)X, \
+                     (const uint16_t*)W, (int64_t)d_in, (int64_t)d_in, Ti, dout, (int64_t)d_in,  \
+                     tiles_m, tiles_n, per_xcd, (const uint16_t*)target, out)
+    // aligned operands: the direct-to-LDS kernel
     if (target) {
-      if (vec) DUST_BASE_GEMM(true, true); else DUST_BASE_GEMM(false, true);
+      if (vec) DUST_BASE_DMA(true); else DUST_BASE_GEMM(false, true);
     } else {
-      if (vec) DUST_BASE_GEMM(true, false); else DUST_BASE_GEMM(false, false);
+      if (vec) DUST_BASE_DMA(false); else DUST_BASE_GEMM(false, false);
     }
+#undef DUST_BASE_DMA
 #undef DUST_BASE_GEMM
   } else {
     const int tiles_n = (int)ceil_div(d_out, 64);
@@ -1301,18 +1307,19 @@ void launch_outer(const Plan& p, const void* X, const float* g32, const uint16_t
   const int32_t Ti = (int32_t)T, di = (int32_t)d_in, dout = (int32_t)d_out;
   float* dst = p.outer_split > 1 ? gpart : G_W;
   if (dtype == DUST_BF16) {
+    // aligned operands: the direct-to-LDS kernel (the workspace keeps g_hi
+    // and g_lo 16-byte aligned when d_out is a multiple of 8)
     const bool vec = (d_in % 8 == 0) && (d_out % 8 == 0) && ((uintptr_t)X % 16 == 0) &&
-                     d_in < (1 << 22) && d_out < (1 << 22);
+                     ((uintptr_t)g_hi % 16 == 0) && ((uintptr_t)g_lo % 16 == 0);
     const int tiles_m = (int)ceil_div(d_out, 64), tiles_n = (int)ceil_div(d_in, 64);
     const int per_xcd = (int)ceil_div((int64_t)tiles_m * tiles_n * p.outer_split, 8);
     const dim3 grid((unsigned)(8 * per_xcd));
     const int32_t partial = p.outer_split > 1 ? 1 : 0;
     if (vec)
-      hipLaunchKernelGGL((gemm::tn_outer_kernel<DUST_TN_STAGES, true>), grid, dim3(256), 0, s,
-                         (const uint16_t*)g_hi, (const uint16_t*)g_lo, (const uint16_t*)X, Ti,
-                         dout, di, tiles_m, tiles_n,
-                         p.outer_split, per_xcd, (int64_t)0, (int64_t)p.outer_tokens, partial,
-                         dst);
+      hipLaunchKernelGGL(gemm::tn_outer_dma_kernel, grid, dim3(256), 0, s, (const uint16_t*)g_hi,
+                         (const uint16_t*)g_lo, (const uint16_t*)X, Ti, dout, di, tiles_m,
+                         tiles_n, p.outer_split, per_xcd, (int64_t)0, (int64_t)p.outer_tokens,
+                         partial, dst);
     else
       hipLaunchKernelGGL((gemm::tn_outer_kernel<DUST_TN_STAGES, false>), grid, dim3(256), 0, s,
                          (const uint16_t*)g_hi, (const uint16_t*)g_lo, (const uint16_t*)X, Ti,
