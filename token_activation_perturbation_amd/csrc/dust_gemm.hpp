@@ -6,17 +6,18 @@
 //          along the output axes, the token axis t strided), g fp32 split
 //          into bf16 hi + lo on the way into LDS.
 //
-// A workgroup of 256 threads (4 waves in a 2x2 grid) computes a BM x BN tile;
-// each wave a (BM/2) x (BN/2) block of 16x16 MFMA tiles
+// A workgroup of 256 threads (4 waves in a 2x2 grid) computes a 64 x 64
+// tile; each wave a 32 x 32 block of 16x16 MFMA tiles
 // (v_mfma_f32_16x16x32_bf16: lane l supplies row l % 16 of A and column
 // l % 16 of B with the 8 contraction values of group l / 16, and holds D rows
-// 4 (l / 16) + 0..3 of column l % 16).  Both kernels stage operand tiles in
-// LDS "k-major" (a padded row of contraction values per output row or
-// column), so every MFMA fragment is one ds_read_b128; the TN kernel
-// transposes in registers before its LDS stores.  LDS is double buffered and
-// several k-tiles are in flight from HBM in registers, so each step needs a
-// single barrier and the load latency is hidden behind the MFMAs of the tiles
-// before it.
+// 4 (l / 16) + 0..3 of column l % 16).  Two designs per contraction:
+//  - for aligned operands (the usual case), tiles go straight from HBM to LDS
+//    with gfx950's direct-to-LDS loads into XOR-slot-permuted rows
+//    (nt_gemm_dma_kernel, tn_outer_dma_kernel);
+//  - for any other shape or alignment, element-wise guarded loads staged
+//    through registers (nt_gemm_kernel, tn_outer_kernel).
+// Both give the same results bit for bit (same tiles, same contraction
+// order).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -41,23 +42,18 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 
 // A (rows x BK) tile of a row-major bf16 matrix whose rows are contiguous
 // along k: element (r, k) at src[r * ld + k].  Each thread moves
-// rows * BK / 8 / 256 chunks of 8 values.  VEC (ld and kmax multiples of 8,
-// 16-byte aligned rows): every chunk is wholly inside or outside the matrix,
-// so it is one unconditional 16-byte load from a clamped address, with no
-// branch; the out-of-range chunks are zeroed when written to LDS, so nothing
-// waits for a load before the store that needs it.  Otherwise element-wise
-// guarded loads.
+// rows * BK / 8 / 256 chunks of 8 values with element-wise guarded loads
+// (any ld, any alignment); values outside the matrix are zero.
 // LDS row padding in bf16 elements (-DDUST_LDS_PAD=n at build time).
 #ifndef DUST_LDS_PAD
 #define DUST_LDS_PAD 16
 #endif
 
-template <int ROWS, int BK, bool VEC>
+template <int ROWS, int BK>
 struct KMajorTile {
   static constexpr int LDK = BK + DUST_LDS_PAD;  // padded LDS row, in bf16 elements
   static constexpr int kChunks = ROWS * BK / 8 / 256;
   u16x8_t reg[kChunks];
-  bool in_range[kChunks];
 
   __device__ __forceinline__ void load(const uint16_t* __restrict__ src, int64_t ld,
                                        int64_t rows, int64_t kmax, int tid, int64_t r0,
@@ -67,30 +63,22 @@ struct KMajorTile {
       const int c = tid + 256 * i;
       const int row = c / (BK / 8), kc = (c % (BK / 8)) * 8;
       const int64_t r = r0 + row, k = k0 + kc;
-      if (VEC) {
-        const bool ok = (r < rows) && (k < kmax);
-        reg[i] = *(const u16x8_t*)(src + (ok ? r * ld + k : 0));
-        in_range[i] = ok;
-      } else {
-        u16x8_t v = {0, 0, 0, 0, 0, 0, 0, 0};
-        if (r < rows) {
-          const uint16_t* p = src + r * ld + k;
+      u16x8_t v = {0, 0, 0, 0, 0, 0, 0, 0};
+      if (r < rows) {
+        const uint16_t* p = src + r * ld + k;
 #pragma unroll
-          for (int j = 0; j < 8; ++j)
-            if (k + j < kmax) v[j] = p[j];
-        }
-        reg[i] = v;
-        in_range[i] = true;
+        for (int j = 0; j < 8; ++j)
+          if (k + j < kmax) v[j] = p[j];
       }
+      reg[i] = v;
     }
   }
   __device__ __forceinline__ void store(uint16_t* lds, int tid) const {
-    const u16x8_t zero = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
     for (int i = 0; i < kChunks; ++i) {
       const int c = tid + 256 * i;
       const int row = c / (BK / 8), kc = (c % (BK / 8)) * 8;
-      *(u16x8_t*)(lds + row * LDK + kc) = in_range[i] ? reg[i] : zero;
+      *(u16x8_t*)(lds + row * LDK + kc) = reg[i];
     }
   }
 };
@@ -175,7 +163,7 @@ __device__ __forceinline__ u16x8_t frag_tr(const uint16_t* tile, int ch0, int k0
 // kt+1 from its register stage into the other LDS buffer, refills that stage
 // with tile kt+1+S, and ends with one barrier.  The k loop is unrolled by S so
 // every stage index is a compile-time constant.
-template <int S, bool VEC, bool TARGET = true>
+template <int S, bool TARGET>
 __global__ __launch_bounds__(256) void nt_gemm_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, int64_t lda, int64_t ldb,
     int32_t M, int32_t N, int64_t K, int32_t tiles_m, int32_t tiles_n, int32_t per_xcd,
@@ -194,8 +182,8 @@ __global__ __launch_bounds__(256) void nt_gemm_kernel(
   const int nk = (int)((K + BK - 1) / BK);
   static_assert(S % 2 == 0, "the LDS double buffer is indexed by the stage parity");
 
-  KMajorTile<BM, BK, VEC> ta[S];
-  KMajorTile<BN, BK, VEC> tb[S];
+  KMajorTile<BM, BK> ta[S];
+  KMajorTile<BN, BK> tb[S];
   auto load_stage = [&](int st, int kt) {
     const int64_t k0 = (int64_t)kt * BK;
     ta[st].load(A, lda, M, K, tid, m0, k0);
@@ -282,14 +270,12 @@ __global__ __launch_bounds__(256) void nt_gemm_kernel(
 // tiles are staged as they lie in HBM, 64 tokens x 64 channels with a row
 // pitch of 72 bf16 (144 bytes; nearly free of bank conflicts for the reads
 // below), and the transposition happens in the LDS read (frag_tr).  Loads:
-// thread t moves 16-byte chunks t and t + 256 of each tile (token c / 8,
-// channels 8 (c % 8) .. + 7), a token row per 8 lanes.  Rows past T re-read
-// row T - 1 and chunks past the channel edge re-read the last full chunk;
+// thread t moves chunks t and t + 256 of each tile (token c / 8, channels
+// 8 (c % 8) .. + 7) element by element, so any M, N and alignment work.  Rows
+// past T re-read row T - 1 and channels past the edge re-read the last one;
 // g rows of tokens outside the split are zeroed at the LDS store (X rows need
-// not be: their products with zero g vanish).  VEC: M and N multiples of 8,
-// g_hi, g_lo and X 16-byte aligned (else element-wise loads with the same
-// clamping).  M, N < 2^22 keep the lane offsets in 32 bits.
-// Pipeline as in nt_gemm_kernel.
+// not be: their products with zero g vanish).  Pipeline as in
+// nt_gemm_kernel.
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
@@ -303,7 +289,7 @@ __device__ __forceinline__ void split_pair(float a, float b, uint32_t& hi, uint3
   lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(v - h, bf16x2_t));
 }
 
-template <int S, bool VEC>
+template <int S>
 __global__ __launch_bounds__(256) void tn_outer_kernel(
     const uint16_t* __restrict__ g_hi, const uint16_t* __restrict__ g_lo,
     const uint16_t* __restrict__ X, int32_t T, int32_t M, int32_t N, int32_t tiles_m,
@@ -333,49 +319,21 @@ __global__ __launch_bounds__(256) void tn_outer_kernel(
     trow[h] = c >> 3;
     cc[h] = (c & 7) * 8;
   }
-  // VEC lane offsets (bytes) of the chunks: columns clamped to the last full
-  // chunk, rows relative to the tile's first token
-  uint32_t a_col[2], b_col[2], a_row[2], b_row[2];
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int64_t am = m0 + cc[h], bn = n0 + cc[h];
-    a_col[h] = (uint32_t)((am < M ? am : M - 8) * 2);
-    b_col[h] = (uint32_t)((bn < N ? bn : N - 8) * 2);
-    a_row[h] = (uint32_t)trow[h] * (uint32_t)M * 2u;
-    b_row[h] = (uint32_t)trow[h] * (uint32_t)N * 2u;
-  }
-
   u16x8_t rh[S][2], rl[S][2], rb[S][2];
   auto load_stage = [&](int st, int kt) {
     const int64_t tb = t_begin + (int64_t)kt * BK;
     const int64_t tbc = tb < T ? tb : (int64_t)T - 1;   // uniform
-    const int64_t rows_left = (int64_t)T - 1 - tbc;      // valid rows after the first
-    const uint32_t last = (uint32_t)(rows_left < 63 ? rows_left : 63);
-    if (VEC) {
-      const char* hbase = (const char*)(g_hi + tbc * M);
-      const char* lbase = (const char*)(g_lo + tbc * M);
-      const char* bbase = (const char*)(X + tbc * N);
-      const uint32_t a_lim = last * (uint32_t)M * 2u, b_lim = last * (uint32_t)N * 2u;
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const uint32_t a_off = (a_row[h] < a_lim ? a_row[h] : a_lim) + a_col[h];
-        rh[st][h] = *(const u16x8_t*)(hbase + a_off);
-        rl[st][h] = *(const u16x8_t*)(lbase + a_off);
-        rb[st][h] = *(const u16x8_t*)(bbase + ((b_row[h] < b_lim ? b_row[h] : b_lim) + b_col[h]));
-      }
-    } else {
+    for (int h = 0; h < 2; ++h) {
+      int64_t t = tbc + trow[h];
+      t = t < T ? t : (int64_t)T - 1;
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        int64_t t = tbc + trow[h];
-        t = t < T ? t : (int64_t)T - 1;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int64_t ca = m0 + cc[h] + e < M ? m0 + cc[h] + e : (int64_t)M - 1;
-          const int64_t cb = n0 + cc[h] + e < N ? n0 + cc[h] + e : (int64_t)N - 1;
-          rh[st][h][e] = g_hi[t * M + ca];
-          rl[st][h][e] = g_lo[t * M + ca];
-          rb[st][h][e] = X[t * N + cb];
-        }
+      for (int e = 0; e < 8; ++e) {
+        const int64_t ca = m0 + cc[h] + e < M ? m0 + cc[h] + e : (int64_t)M - 1;
+        const int64_t cb = n0 + cc[h] + e < N ? n0 + cc[h] + e : (int64_t)N - 1;
+        rh[st][h][e] = g_hi[t * M + ca];
+        rl[st][h][e] = g_lo[t * M + ca];
+        rb[st][h][e] = X[t * N + cb];
       }
     }
   };

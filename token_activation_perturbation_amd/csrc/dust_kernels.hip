@@ -1274,22 +1274,18 @@ void launch_base_gemm(const void* X, const void* W, const void* target, int64_t 
     const int tiles_m = (int)ceil_div(T, 64), tiles_n = (int)ceil_div(d_out, 64);
     const int per_xcd = (int)ceil_div((int64_t)tiles_m * tiles_n, 8);
     const dim3 grid((unsigned)(8 * per_xcd));
-#define DUST_BASE_GEMM(V, TG)                                                                \
-  hipLaunchKernelGGL((gemm::nt_gemm_kernel<4, V, TG>), grid, dim3(256), 0, s,               \
-                     (const uint16_t*)X, (const uint16_t*)W, (int64_t)d_in, (int64_t)d_in, \
-                     Ti, dout, (int64_t)d_in, tiles_m, tiles_n, per_xcd,                    \
-                     (const uint16_t*)target, out)
-#define DUST_BASE_DMA(TG)                                                                   \
-  hipLaunchKernelGGL((gemm::nt_gemm_dma_kernel<TG>), grid, dim3(256), 0, s, (const uint16_t*)X, \
-                     (const uint16_t*)W, (int64_t)d_in, (int64_t)d_in, Ti, dout, (int64_t)d_in,  \
-                     tiles_m, tiles_n, per_xcd, (const uint16_t*)target, out)
-    // aligned operands: the direct-to-LDS kernel
+    // aligned operands: the direct-to-LDS kernel; else guarded loads
+#define DUST_BASE_GEMM(KERNEL)                                                                \
+  hipLaunchKernelGGL(KERNEL, grid, dim3(256), 0, s, (const uint16_t*)X, (const uint16_t*)W,     \
+                     (int64_t)d_in, (int64_t)d_in, Ti, dout, (int64_t)d_in, tiles_m, tiles_n,  \
+                     per_xcd, (const uint16_t*)target, out)
     if (target) {
-      if (vec) DUST_BASE_DMA(true); else DUST_BASE_GEMM(false, true);
+      if (vec) DUST_BASE_GEMM((gemm::nt_gemm_dma_kernel<true>));
+      else DUST_BASE_GEMM((gemm::nt_gemm_kernel<4, true>));
     } else {
-      if (vec) DUST_BASE_DMA(false); else DUST_BASE_GEMM(false, false);
+      if (vec) DUST_BASE_GEMM((gemm::nt_gemm_dma_kernel<false>));
+      else DUST_BASE_GEMM((gemm::nt_gemm_kernel<4, false>));
     }
-#undef DUST_BASE_DMA
 #undef DUST_BASE_GEMM
   } else {
     const int tiles_n = (int)ceil_div(d_out, 64);
@@ -1321,7 +1317,7 @@ void launch_outer(const Plan& p, const void* X, const float* g32, const uint16_t
                          tiles_n, p.outer_split, per_xcd, (int64_t)0, (int64_t)p.outer_tokens,
                          partial, dst);
     else
-      hipLaunchKernelGGL((gemm::tn_outer_kernel<DUST_TN_STAGES, false>), grid, dim3(256), 0, s,
+      hipLaunchKernelGGL((gemm::tn_outer_kernel<DUST_TN_STAGES>), grid, dim3(256), 0, s,
                          (const uint16_t*)g_hi, (const uint16_t*)g_lo, (const uint16_t*)X, Ti,
                          dout, di, tiles_m, tiles_n,
                          p.outer_split, per_xcd, (int64_t)0, (int64_t)p.outer_tokens, partial,
