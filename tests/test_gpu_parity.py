@@ -120,6 +120,8 @@ SMALL = [
     (256, 128, 128, 1024, 64, 1e-2, 0.5, True, "bf16"),  # d_out spans 4 quad rounds
     (140, 70, 40, 52, 8, 1e-2, 0.95, True, "bf16"),      # credit chunks 32 + 32 + 6
     (99, 33, 16, 24, 4, 1e-2, 1.0, False, "f32"),        # chunks 32 + 1, suffix sums
+    (1000, 500, 64, 72, 8, 1e-2, 0.0, True, "bf16"),     # aligned: 2 token splits, ragged tail
+    (64, 64, 8, 16, 4, 1e-2, 0.0, False, "bf16"),        # d_in = 8: one k-block, 7 chunks zeroed
 ]
 
 

@@ -603,8 +603,23 @@ __global__ __launch_bounds__(256) void split_sum_kernel(const float* __restrict_
   const int64_t i = 4 * ((int64_t)blockIdx.x * blockDim.x + threadIdx.x);
   if (i >= n) return;
   if (i + 4 <= n && (n % 4) == 0) {
+    // eight partials loaded at a time, then added in split order (the same
+    // order as one at a time)
     float4 s = *(const float4*)(part + i);
-    for (int k = 1; k < splits; ++k) {
+    int k = 1;
+    for (; k + 8 <= splits; k += 8) {
+      float4 o[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) o[u] = *(const float4*)(part + (int64_t)(k + u) * n + i);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        s.x += o[u].x;
+        s.y += o[u].y;
+        s.z += o[u].z;
+        s.w += o[u].w;
+      }
+    }
+    for (; k < splits; ++k) {
       const float4 o = *(const float4*)(part + (int64_t)k * n + i);
       s.x += o.x;
       s.y += o.y;
