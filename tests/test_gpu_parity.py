@@ -315,6 +315,48 @@ def test_misaligned_target_takes_the_guarded_epilogue(dev, oracle_mod, threads):
     assert rel(out["G_W"].cpu().numpy().astype(np.float64), ref["G"]) <= TOL["bf16"]
 
 
+@pytest.fixture(scope="module")
+def max_tokens_inputs():
+    """The largest token count the library accepts, T = 2^24 - 1 = 4095 x 4097
+    (4097 sequences of 4095 tokens), on a narrow layer so the inputs stay a
+    few hundred MB."""
+    T, d = (1 << 24) - 1, 8
+    return synth.random_inputs(T, d, d, "bf16", seed=24), 4095
+
+
+@pytest.mark.parametrize("gamma", [0.0, 0.9])
+def test_maximum_token_count(dev, oracle_mod, threads, max_tokens_inputs, gamma):
+    """T = 2^24 - 1 through every stage (the single-generation kernel at
+    gamma = 0; the jitter-loss pass, the chunked scan over 4097 sequences and
+    the reweight pass at gamma = 0.9): the oracle recomputes the first and the
+    last sequence, and G_W is checked at full size against g^T X formed in
+    fp64 from the GPU's own g."""
+    import torch
+    import token_activation_perturbation_amd as dust
+    inp, seq_len = max_tokens_inputs
+    T = inp["X"].shape[0]
+    print(f"maximum token count T={T} gamma={gamma}", flush=True)
+    Xd, Wd, td = (torch.from_numpy(inp[k]).to(dev).to(torch.bfloat16).contiguous()
+                  for k in ("X", "W", "target"))
+    kw = dict(K=2, sigma=1e-2, gamma=gamma, seed=77, antithetic=True, seq_len=seq_len)
+    out = dust.dust_estimate(Xd, Wd, td, want_reward=True, want_g=True, **kw)
+    torch.cuda.synchronize(dev)
+    g = out["g"].cpu().numpy().astype(np.float64)
+    reward = out["reward"].cpu().numpy().astype(np.float64)
+    n_seq = T // seq_len
+    for sq in (0, n_seq - 1):
+        ref = oracle_mod.estimate(inp["X"], inp["W"], inp["target"], seq_range=(sq, sq + 1),
+                                  threads=threads, **kw)
+        sl = slice(sq * seq_len, (sq + 1) * seq_len)
+        eg, er = rel(g[sl], ref["g"]), rel(reward[sl], ref["reward"])
+        print(f"  sequence {sq}: g {eg:.2e} reward {er:.2e}", flush=True)
+        assert eg <= TOL["bf16"] and er <= TOL["bf16"]
+    G_ref = g.T @ inp["X"].astype(np.float64)
+    e = rel(out["G_W"].cpu().numpy().astype(np.float64), G_ref)
+    print(f"  G_W vs g^T X {e:.2e}", flush=True)
+    assert e <= TOL["bf16"]
+
+
 def test_small_workspace_is_an_error(dev):
     import torch
     import token_activation_perturbation_amd as dust
