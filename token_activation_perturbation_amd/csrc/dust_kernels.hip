@@ -40,23 +40,12 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float((uint32_t)b << 16);
 }
 
-// Round to nearest even; inputs are finite.
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  const uint32_t u = __float_as_uint(f);
-  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
-}
-
 // The wave's index in its workgroup, as a wave-uniform (scalar) value: the
 // compiler cannot prove threadIdx.x / 64 uniform, and everything derived
 // from it (token, noise range) would otherwise live in vector registers and
 // turn uniform loop tests into divergent branches.
 __device__ __forceinline__ int wave_id() {
   return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-}
-
-__device__ __forceinline__ f32x4_t mfma_bf16(u16x8_t a, u16x8_t b, f32x4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
 __device__ __forceinline__ f32x4_t mfma_f32(float a, float b, f32x4_t c) {
@@ -493,7 +482,7 @@ __device__ __forceinline__ void store_g_quad(float4 r, int64_t row, int c, int d
 // quads l + 64 j, and the waves' partial sums are added in wave order.
 
 __global__ __launch_bounds__(256) void reweight_kernel(
-    const float* __restrict__ wgt, int32_t t0, int32_t T, int32_t d_out, int32_t nq,
+    const float* __restrict__ wgt, int32_t t0, int32_t d_out, int32_t nq,
     int32_t K_n, int32_t per_wave, NoiseKey key, float* __restrict__ g32,
     uint16_t* __restrict__ g_hi, uint16_t* __restrict__ g_lo) {
   __shared__ float4 part[4][64];
@@ -739,8 +728,7 @@ __device__ __forceinline__ void wave_reduce_to_scalars(float (&v)[M], int lane, 
 
 template <int QPL, bool ANTI, bool FULL>
 __global__ __launch_bounds__(256) void fused_g0_kernel(
-    const float* __restrict__ delta, int32_t t0, int32_t T, int32_t d_out, int32_t nq,
-    int32_t K, int32_t K_n, int32_t per_wave, float sigma, float curv_coef, NoiseKey key,
+    const float* __restrict__ delta, int32_t t0, int32_t d_out, int32_t K, int32_t K_n, int32_t per_wave, float sigma, float curv_coef, NoiseKey key,
     float* __restrict__ Pout, float* __restrict__ Qout, float* __restrict__ loss_clean,
     float* __restrict__ g32, uint16_t* __restrict__ g_hi, uint16_t* __restrict__ g_lo) {
   constexpr int NB = QPL <= 2 ? DUST_FUSED_NB_SMALL : (QPL <= 4 ? 2 : 1);
@@ -1214,13 +1202,13 @@ inline TimedLaunch take_timing_events() {
 template <int QPL>
 void launch_fused_g0_qpl(bool anti, bool full, unsigned blocks, unsigned threads,
                          hipStream_t s, TimedLaunch tl, const float* delta, int32_t t0,
-                         int32_t T, int32_t d_out, int32_t nq, int32_t K, int32_t K_n,
-                         int32_t per_wave, float sigma, float curv, NoiseKey key, float* P,
-                         float* Q, float* loss, float* g32, uint16_t* g_hi, uint16_t* g_lo) {
+                         int32_t d_out, int32_t K, int32_t K_n, int32_t per_wave, float sigma,
+                         float curv, NoiseKey key, float* P, float* Q, float* loss, float* g32,
+                         uint16_t* g_hi, uint16_t* g_lo) {
 #define DUST_FUSED_LAUNCH(A, F)                                                               \
   hipExtLaunchKernelGGL((fused_g0_kernel<QPL, A, F>), dim3(blocks), dim3(threads), 0, s,      \
-                        tl.start, tl.stop, 0, delta, t0, T, d_out, nq, K, K_n, per_wave, sigma, \
-                        curv, key, P, Q, loss, g32, g_hi, g_lo)
+                        tl.start, tl.stop, 0, delta, t0, d_out, K, K_n, per_wave, sigma, curv, \
+                        key, P, Q, loss, g32, g_hi, g_lo)
   if (anti && full)
     DUST_FUSED_LAUNCH(true, true);
   else if (anti)
@@ -1243,13 +1231,13 @@ inline int fused_qpl(int32_t nq) {
 
 void launch_fused_g0(int qpl, bool anti, bool full, unsigned blocks, unsigned threads,
                      hipStream_t s, TimedLaunch tl, const float* delta, int32_t t0,
-                     int32_t T, int32_t d_out, int32_t nq, int32_t K, int32_t K_n,
-                     int32_t per_wave, float sigma, float curv, NoiseKey key, float* P,
-                     float* Q, float* loss, float* g32, uint16_t* g_hi, uint16_t* g_lo) {
+                     int32_t d_out, int32_t K, int32_t K_n, int32_t per_wave, float sigma,
+                     float curv, NoiseKey key, float* P, float* Q, float* loss, float* g32,
+                     uint16_t* g_hi, uint16_t* g_lo) {
 #define DUST_FUSED_CASE(V)                                                                   \
   case V:                                                                                    \
-    launch_fused_g0_qpl<V>(anti, full, blocks, threads, s, tl, delta, t0, T, d_out, nq, K,   \
-                           K_n, per_wave, sigma, curv, key, P, Q, loss, g32, g_hi, g_lo);    \
+    launch_fused_g0_qpl<V>(anti, full, blocks, threads, s, tl, delta, t0, d_out, K, K_n,     \
+                           per_wave, sigma, curv, key, P, Q, loss, g32, g_hi, g_lo);         \
     break;
   switch (qpl) {
     DUST_FUSED_CASE(1)
@@ -1480,7 +1468,7 @@ dust_status_t run_estimate(const Site& st, int64_t T, int64_t d_in, int64_t d_ou
   uint16_t* g_lo = split ? g_hi + T * d_out : nullptr;
   float* gpart = (float*)(ws + p.off_gpart);
   const NoiseKey key = make_key(seed);
-  const int32_t Ti = (int32_t)T, di = (int32_t)d_in, dout = (int32_t)d_out;
+  const int32_t Ti = (int32_t)T, dout = (int32_t)d_out;
 
   // 1. base GEMM -> delta (the caller's error estimate itself when local;
   //    the gather of table rows for an embedding)
@@ -1532,7 +1520,7 @@ dust_status_t run_estimate(const Site& st, int64_t T, int64_t d_in, int64_t d_ou
   if (fused) {
     const bool full = (p.nq == 64 * qpl) && delta_vec;
     launch_fused_g0(qpl, p.antithetic != 0, full, (unsigned)T, (unsigned)(64 * p.fz_waves), s,
-                    tl, (const float*)delta, 0, Ti, dout, p.nq, K, p.K_n, p.fz_per_wave, sigma,
+                    tl, (const float*)delta, 0, dout, K, p.K_n, p.fz_per_wave, sigma,
                     curv, key, want_pq ? Pbuf : nullptr, want_pq ? Qbuf : nullptr, loss_clean, g32,
                     g_hi, g_lo);
     if (want_pq) {
@@ -1545,7 +1533,7 @@ dust_status_t run_estimate(const Site& st, int64_t T, int64_t d_in, int64_t d_ou
     }
   } else {
     hipLaunchKernelGGL(reweight_kernel, dim3((unsigned)T), dim3(64 * p.rw_waves), 0, s,
-                       (const float*)wgt, 0, Ti, dout, p.nq, p.K_n, p.rw_per_wave, key, g32,
+                       (const float*)wgt, 0, dout, p.nq, p.K_n, p.rw_per_wave, key, g32,
                        g_hi, g_lo);
   }
 
