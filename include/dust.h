@@ -106,8 +106,8 @@ dust_status_t dust_estimate(const void* X, const void* W, const void* target,
 
 /*
  * Host-side check of dust_estimate_local's arguments: the same rules as
- * dust_validate, with X, E and G_W the required pointers (E 4-byte
- * aligned).  No HIP call.
+ * dust_validate, with E required (4-byte aligned) and X and G_W either both
+ * given or both NULL.  No HIP call.
  */
 dust_status_t dust_validate_local(const void* X, const float* E, int64_t T,
                                   int64_t d_in, int64_t d_out, int64_t seq_len,
@@ -130,10 +130,14 @@ dust_status_t dust_validate_local(const void* X, const float* E, int64_t T,
  * sigma.  Per-site gamma is this call's gamma.
  *
  * Inputs:
- *   X  [T, d_in]   layer inputs, dtype `dtype`
+ *   X  [T, d_in]   layer inputs, dtype `dtype`; or NULL together with G_W
+ *                  for a site with no input matrix (a value embedding, whose
+ *                  gradient is then dust_reassemble_embedding of g): the
+ *                  outer product is skipped, d_in only sizes the workspace
+ *                  (pass 1) and dtype must still be a valid code
  *   E  [T, d_out]  fp32 error estimate of the layer's output
  * Scalars, noise and workspace (dust_workspace_bytes) as for dust_estimate.
- * Outputs (fp32, overwritten): G_W [d_out, d_in] required; rho [T, K] (the
+ * Outputs (fp32, overwritten): G_W [d_out, d_in] (with X); rho [T, K] (the
  * scores), reward [T, K] and g [T, d_out] optional (NULL to skip).
  */
 dust_status_t dust_estimate_local(const void* X, const float* E, int64_t T,

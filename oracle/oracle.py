@@ -24,10 +24,11 @@ _lib = None
 
 def build() -> str:
     """Compile the oracle with gcc (no fast-math; plain fp64)."""
+    tmp = f"{_LIB}.{os.getpid()}.tmp"  # concurrent builds each write their own
     cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-Wall", "-Wextra",
-           "-o", _LIB + ".tmp", _SRC, "-lm", "-lpthread"]
+           "-o", tmp, _SRC, "-lm", "-lpthread"]
     subprocess.run(cmd, check=True)
-    os.replace(_LIB + ".tmp", _LIB)
+    os.replace(tmp, _LIB)
     return _LIB
 
 

@@ -110,6 +110,14 @@ def test_python_binding_rejects_bad_tensors():
                            seq_len=4)
 
 
+def test_python_local_binding_rejects_bad_tensors():
+    import torch
+    E = torch.zeros(4, 4)
+    with pytest.raises(ValueError):  # a host tensor, with or without X
+        dust.dust_estimate_local(None, E, K=4, sigma=0.1, gamma=0.0, seed=0, antithetic=True,
+                                 seq_len=4)
+
+
 def _validate_local(**over):
     args = dict(X=16, E=32, T=64, d_in=16, d_out=8, seq_len=16, dtype=dust.DUST_BF16,
                 K=4, sigma=0.2, gamma=0.98, antithetic=1, G=48, ws=64, ws_bytes=None)
@@ -126,6 +134,8 @@ def _validate_local(**over):
 
 def test_validate_local_accepts_good_arguments(lib):
     assert _validate_local() == 0
+    # no input matrix (a value embedding): X and G_W omitted together
+    assert _validate_local(X=None, G=None, d_in=1) == 0
 
 
 @pytest.mark.parametrize("over,status", [

@@ -148,3 +148,37 @@ def test_local_bitwise_deterministic(dev):
     b = gpu_local(X, E, "bf16", dev, **kw)
     for k in a:
         assert np.array_equal(a[k], b[k]), k
+
+
+@pytest.mark.parametrize("gamma", [0.98, 0.0])
+def test_value_embedding_g_only_then_reassembly(dev, oracle_mod, threads, gamma):
+    """A value embedding has no input matrix: local scoring with X and G_W
+    omitted gives g alone, and its weight gradient is the scatter of g into
+    the rows the token ids select (dust_reassemble_embedding).  Checked
+    against the oracle's local scoring (whose g does not involve X) and its
+    fp64 reassembly of that g; the g-only g equals, bit for bit, the g of the
+    same call with an input matrix."""
+    import torch
+    import token_activation_perturbation_amd as dust
+    T, seq_len, d, K, V = 512, 128, 96, 16, 300
+    print(f"value embedding g-only gamma {gamma}", flush=True)
+    rng = np.random.default_rng(41)
+    E = rng.standard_normal((T, d)).astype(np.float32)
+    ids = synth.zipf_ids(rng, T, V)
+    kw = dict(K=K, sigma=0.2, gamma=gamma, seed=12, antithetic=True, seq_len=seq_len)
+    Ed = torch.from_numpy(E).to(dev)
+    out = dust.dust_estimate_local(None, Ed, want_rho=True, want_reward=True, want_g=True, **kw)
+    assert "G_W" not in out
+    G = dust.dust_reassemble_embedding(torch.from_numpy(ids).to(dev), out["g"], V, scale=1.0 / T)
+    torch.cuda.synchronize(dev)
+    got = {k: v.cpu().numpy().astype(np.float64) for k, v in out.items()}
+    ref = oracle_mod.estimate_local(np.zeros((T, 1), np.float32), E, threads=threads, **kw)
+    errs = {k: rel(got[k], ref[k]) for k in ("rho", "reward", "g")}
+    errs["G_V"] = rel(G.cpu().numpy().astype(np.float64),
+                      oracle_mod.reassemble_embedding(ids, ref["g"], V, scale=1.0 / T))
+    print("  rel err", " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
+    for k, v in errs.items():
+        assert v <= TOL["f32"], (k, v)
+    X, _ = local_inputs(T, 32, d, "bf16", seed=43)
+    full = gpu_local(X, E, "bf16", dev, **kw)
+    assert np.array_equal(full["g"], got["g"])

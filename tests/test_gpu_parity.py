@@ -122,6 +122,8 @@ SMALL = [
     (99, 33, 16, 24, 4, 1e-2, 1.0, False, "f32"),        # chunks 32 + 1, suffix sums
     (1000, 500, 64, 72, 8, 1e-2, 0.0, True, "bf16"),     # aligned: 2 token splits, ragged tail
     (64, 64, 8, 16, 4, 1e-2, 0.0, False, "bf16"),        # d_in = 8: one k-block, 7 chunks zeroed
+    (300, 100, 392, 520, 8, 1e-2, 0.0, True, "bf16"),    # 8-wide edge tiles, 44-token tail
+    (1000, 250, 1024, 200, 8, 1e-2, 0.5, False, "bf16"), # wide input, 104-token tail, two passes
 ]
 
 

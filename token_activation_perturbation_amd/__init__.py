@@ -216,29 +216,31 @@ def dust_estimate_local(X, E, *, K: int, sigma: float, gamma: float, seed: int,
                         want_reward: bool = False, want_g: bool = False,
                         out: dict | None = None, workspace=None):
     """Enqueue dust_estimate_local (local scoring against the error estimate
-    E) on the current stream of X's device.
+    E) on the current stream of E's device.
 
     X [T,d_in] (bfloat16 or float32) and E [T,d_out] (float32): contiguous
-    device tensors.  Returns a dict of fp32 device tensors: "G_W" [d_out,d_in]
-    and the requested optional outputs "rho" [T,K] (the scores), "reward"
-    [T,K], "g" [T,d_out].  ``out`` and ``workspace`` as for dust_estimate.
+    device tensors; X may be None for a site with no input matrix (a value
+    embedding): then no G_W is formed, and g (want_g) is the result.  Returns
+    a dict of fp32 device tensors: "G_W" [d_out,d_in] (with X) and the
+    requested optional outputs "rho" [T,K] (the scores), "reward" [T,K],
+    "g" [T,d_out].  ``out`` and ``workspace`` as for dust_estimate.
     """
     import torch
     for name, t in (("X", X), ("E", E)):
-        if not t.is_cuda or not t.is_contiguous():
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
             raise ValueError(f"{name} must be a contiguous device tensor")
     if E.dtype != torch.float32:
         raise TypeError("E must be float32")
-    if X.dim() != 2 or E.dim() != 2 or X.shape[0] != E.shape[0]:
-        raise ValueError(f"shape mismatch: X {tuple(X.shape)}, E {tuple(E.shape)}")
-    T, d_in = X.shape
-    d_out = E.shape[1]
-    dt = _dtype_code(X)
-    dev = X.device
+    if E.dim() != 2 or (X is not None and (X.dim() != 2 or X.shape[0] != E.shape[0])):
+        raise ValueError(f"shape mismatch: X {None if X is None else tuple(X.shape)}, "
+                         f"E {tuple(E.shape)}")
+    T, d_out = E.shape
+    d_in = 1 if X is None else X.shape[1]
+    dt = DUST_F32 if X is None else _dtype_code(X)
+    dev = E.device
     res = dict(out or {})
     _get = _output_getter(res, dev)
-
-    G = _get("G_W", (d_out, d_in))
+    G = None if X is None else _get("G_W", (d_out, d_in))
     rho = _get("rho", (T, K)) if want_rho else None
     reward = _get("reward", (T, K)) if want_reward else None
     g = _get("g", (T, d_out)) if want_g else None
@@ -247,8 +249,8 @@ def dust_estimate_local(X, E, *, K: int, sigma: float, gamma: float, seed: int,
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     ptr = lambda t: None if t is None else t.data_ptr()  # noqa: E731
     status = _load().dust_estimate_local(
-        X.data_ptr(), E.data_ptr(), T, d_in, d_out, seq_len, dt, K, sigma, gamma,
-        ctypes.c_uint64(seed & 0xFFFFFFFFFFFFFFFF), int(bool(antithetic)), G.data_ptr(),
+        ptr(X), E.data_ptr(), T, d_in, d_out, seq_len, dt, K, sigma, gamma,
+        ctypes.c_uint64(seed & 0xFFFFFFFFFFFFFFFF), int(bool(antithetic)), ptr(G),
         ptr(rho), ptr(reward), ptr(g), workspace.data_ptr(), workspace.numel(),
         _stream_ptr(dev))
     _check(status)

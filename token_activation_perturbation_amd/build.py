@@ -19,7 +19,7 @@ HIPCC_FLAGS = [
 
 def build_library(verbose: bool = False) -> str:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    tmp = LIB + ".tmp"
+    tmp = f"{LIB}.{os.getpid()}.tmp"  # concurrent builds each write their own
     cmd = [hipcc, *HIPCC_FLAGS, "-o", tmp, *SOURCES]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:

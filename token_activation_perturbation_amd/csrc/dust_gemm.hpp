@@ -427,8 +427,9 @@ __global__ __launch_bounds__(256) void tn_outer_kernel(
 // fetches row 8 i + l / 8, chunk (l % 8) ^ tr_swz(row), so its 16 bytes land
 // in the right slot.  tr_swz was chosen by an exhaustive search over XOR maps
 // of the row bits so that the transposing fragment reads (frag_sw) are free
-// of bank conflicts per half-wave on 64 banks.  Two LDS stages: the loads of
-// k-block kt + 1 are issued right after the barrier that opens step kt.
+// of bank conflicts per half-wave on 64 banks.  NS LDS stages of 24 KiB: the
+// loads of k-block kt + NS - 1 are issued right after the barrier that opens
+// step kt.
 // Token rows past T re-read row T - 1, channel chunks past the edge re-read
 // the last full chunk (their outputs are never stored); g rows past the
 // split's end are zeroed in LDS before the MFMAs read them.
@@ -444,6 +445,45 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
+
+// LDS stages of the direct-to-LDS kernels (-DDUST_NT_DMA_STAGES=n,
+// -DDUST_TN_DMA_STAGES=n at build time): block kt + NS - 1 is in flight while
+// block kt is multiplied.
+#ifndef DUST_NT_DMA_STAGES
+#define DUST_NT_DMA_STAGES 2
+#endif
+#ifndef DUST_TN_DMA_STAGES
+#define DUST_TN_DMA_STAGES 2
+#endif
+
+// Wait until this wave's loads of the oldest block in flight have landed,
+// with `ahead` (0 .. NS - 2, uniform) later blocks allowed to stay in
+// flight; each block is LOADS load instructions per lane, and vector-memory
+// loads complete in issue order for vmcnt.
+//
+// The barrier that follows is stage_barrier, not __syncthreads: the latter's
+// workgroup fence makes the compiler wait for every load in flight (vmcnt 0,
+// since a direct-to-LDS load counts as an LDS write), which would drain the
+// later stages too.  stage_barrier waits only for this wave's LDS reads
+// (lgkmcnt 0: the buffer about to be refilled is no longer read) and keeps
+// every memory access on its side of the barrier.
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <int NS, int LOADS>
+__device__ __forceinline__ void wait_blocks(int ahead) {
+  static_assert(NS >= 2 && NS <= 4, "stages");
+  if constexpr (NS == 2) {
+    wait_vmcnt<0>();
+  } else if constexpr (NS == 3) {
+    if (ahead >= 1) wait_vmcnt<LOADS>(); else wait_vmcnt<0>();
+  } else {
+    if (ahead >= 2) wait_vmcnt<2 * LOADS>();
+    else if (ahead == 1) wait_vmcnt<LOADS>();
+    else wait_vmcnt<0>();
+  }
+}
 
 // frag_tr's fragment from a slot-permuted tile (rows of 128 bytes)
 __device__ __forceinline__ u16x8_t frag_sw(const uint8_t* tile, int ch0, int k0, int lane) {
@@ -463,7 +503,7 @@ __global__ __launch_bounds__(256) void tn_outer_dma_kernel(
     const uint16_t* __restrict__ X, int32_t T, int32_t M, int32_t N, int32_t tiles_m,
     int32_t tiles_n, int32_t splits, int32_t per_xcd, int64_t t_first, int64_t t_per_split,
     int32_t partial, float* __restrict__ out) {
-  constexpr int BK = 64, TB = BK * 128, NS = 2;
+  constexpr int BK = 64, TB = BK * 128, NS = DUST_TN_DMA_STAGES;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[NS * 3 * TB];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -511,11 +551,12 @@ __global__ __launch_bounds__(256) void tn_outer_dma_kernel(
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  if (nk > 0) issue(0, 0);
+  for (int b = 0; b < NS - 1 && b < nk; ++b) issue(b, b);
   for (int kt = 0; kt < nk; ++kt) {
-    wait_vmcnt<0>();  // this wave's loads of block kt have landed
-    __syncthreads();  // ... and every wave's; block kt - 1 is no longer read
-    const int buf = kt & 1;
+    // this wave's loads of block kt have landed ...
+    wait_blocks<NS, 6>(min(nk - 1 - kt, NS - 2));
+    stage_barrier();  // ... and every wave's; block kt - 1 is no longer read
+    const int buf = kt % NS;
     uint8_t* base = lds + buf * 3 * TB;
     const int64_t left = t_end - (t_begin + (int64_t)kt * BK);
     if (left < BK) {
@@ -528,7 +569,7 @@ __global__ __launch_bounds__(256) void tn_outer_dma_kernel(
       }
       __syncthreads();
     }
-    if (kt + 1 < nk) issue(buf ^ 1, kt + 1);
+    if (kt + NS - 1 < nk) issue((kt + NS - 1) % NS, kt + NS - 1);
 #pragma unroll
     for (int ks = 0; ks < BK; ks += 32) {
       u16x8_t ah[2], al[2], bf[2];
@@ -564,8 +605,8 @@ __global__ __launch_bounds__(256) void tn_outer_dma_kernel(
 // ---------------------------------------------------------------------------
 // The base GEMM fed by direct-to-LDS loads, for the aligned case (K a
 // multiple of 8; A, B 16-byte aligned; lda, ldb multiples of 8).  Same tiles,
-// contraction order and results (bitwise) as nt_gemm_kernel; two LDS stages
-// of 16 KiB.  An operand tile is 64 rows x 64 contraction values bf16, a row
+// contraction order and results (bitwise) as nt_gemm_kernel; NS LDS stages
+// of 16 KiB, block kt + NS - 1 in flight while block kt is multiplied.  An operand tile is 64 rows x 64 contraction values bf16, a row
 // per 128 bytes, chunk c of row r in slot c ^ nt_swz(r): the 16-byte fragment
 // reads (16 rows of one chunk per quarter-wave) then hit every bank once
 // (nt_swz found by the same exhaustive search as tr_swz).  Rows past M or N
@@ -582,7 +623,7 @@ __global__ __launch_bounds__(256) void nt_gemm_dma_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, int64_t lda, int64_t ldb,
     int32_t M, int32_t N, int64_t K, int32_t tiles_m, int32_t tiles_n, int32_t per_xcd,
     const uint16_t* __restrict__ target, float* __restrict__ out) {
-  constexpr int BK = 64, TB = 64 * 128, NS = 2;
+  constexpr int BK = 64, TB = 64 * 128, NS = DUST_NT_DMA_STAGES;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[NS * 2 * TB];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -623,11 +664,26 @@ __global__ __launch_bounds__(256) void nt_gemm_dma_kernel(
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  if (nk > 0) issue(0, 0);
+  // with a target: this thread's 16-column piece of it (the epilogue's row
+  // segment) is fetched before the k loop, so its latency hides behind the
+  // loop; the loads are older than every block's, so the block waits below
+  // cover them too
+  const int er = tid >> 2, ec0 = (tid & 3) * 16;
+  const bool e_vec = TARGET && m0 + er < M && N - (n0 + ec0) >= 16 && (N & 7) == 0 &&
+                     (((uintptr_t)target | (uintptr_t)out) & 15) == 0;
+  u32x4_t tv0 = u32x4_t{0u, 0u, 0u, 0u}, tv1 = tv0;
+  if (e_vec) {
+    const uint16_t* tp = target + (m0 + er) * N + n0 + ec0;
+    tv0 = *(const u32x4_t*)tp;
+    tv1 = *(const u32x4_t*)(tp + 8);
+  }
+
+  for (int b = 0; b < NS - 1 && b < nk; ++b) issue(b, b);
   for (int kt = 0; kt < nk; ++kt) {
-    wait_vmcnt<0>();  // this wave's loads of block kt have landed
-    __syncthreads();  // ... and every wave's; block kt - 1 is no longer read
-    const int buf = kt & 1;
+    // this wave's loads of block kt have landed ...
+    wait_blocks<NS, 4>(min(nk - 1 - kt, NS - 2));
+    stage_barrier();  // ... and every wave's; block kt - 1 is no longer read
+    const int buf = kt % NS;
     uint8_t* base = lds + buf * 2 * TB;
     const int64_t left = K - (int64_t)kt * BK;
     if (left < BK) {
@@ -640,7 +696,7 @@ __global__ __launch_bounds__(256) void nt_gemm_dma_kernel(
       }
       __syncthreads();
     }
-    if (kt + 1 < nk) issue(buf ^ 1, kt + 1);
+    if (kt + NS - 1 < nk) issue((kt + NS - 1) % NS, kt + NS - 1);
 #pragma unroll
     for (int ks = 0; ks < BK; ks += 32) {
       u16x8_t af[2], bfr[2];
@@ -687,7 +743,7 @@ __global__ __launch_bounds__(256) void nt_gemm_dma_kernel(
           ct[(wm * 32 + i * 16 + 4 * (lane >> 4) + e) * CP + wn * 32 + j * 16 + (lane & 15)] =
               acc[i][j][e];
     __syncthreads();
-    const int r = tid >> 2, c0 = (tid & 3) * 16;
+    const int r = er, c0 = ec0;
     const int64_t row = m0 + r;
     if (row < M) {
       const float* src = ct + r * CP + c0;
@@ -695,13 +751,11 @@ __global__ __launch_bounds__(256) void nt_gemm_dma_kernel(
       const uint16_t* tp = target + row * N + n0 + c0;
       const int64_t ncols = N - (n0 + c0);  // columns left in this row
       // 16-byte pieces need whole rows of 8-element multiples and aligned bases
-      const bool aligned = ((N & 7) == 0) && (((uintptr_t)target | (uintptr_t)out) & 15) == 0;
-      if (ncols >= 16 && aligned) {
+      if (e_vec) {
         float4 v[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) v[q] = *(const float4*)(src + 4 * q);
-        const u32x4_t t0 = *(const u32x4_t*)tp, t1 = *(const u32x4_t*)(tp + 8);
-        const uint32_t tw[8] = {t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]};
+        const uint32_t tw[8] = {tv0[0], tv0[1], tv0[2], tv0[3], tv1[0], tv1[1], tv1[2], tv1[3]};
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           v[q].x -= __uint_as_float(tw[2 * q] << 16);

@@ -100,8 +100,10 @@ dust_status_t dust_validate_local(const void* X, const float* E, int64_t T, int6
                                   float sigma, float gamma, int32_t antithetic,
                                   const float* G_W, const void* workspace,
                                   size_t workspace_bytes) {
-  if (!X || !E || !G_W)
-    return dust::fail(DUST_ERR_INVALID_ARG, "X, E and G_W must not be NULL");
+  if (!E) return dust::fail(DUST_ERR_INVALID_ARG, "E must not be NULL");
+  // without X there is no outer product: X and G_W are given or omitted together
+  if ((X == nullptr) != (G_W == nullptr))
+    return dust::fail(DUST_ERR_INVALID_ARG, "X and G_W must both be given or both be NULL");
   if ((uintptr_t)E % 4 != 0)
     return dust::fail(DUST_ERR_INVALID_ARG, "E must be 4-byte aligned (fp32)");
   return validate_common(T, d_in, d_out, seq_len, dtype, K, sigma, gamma, antithetic,

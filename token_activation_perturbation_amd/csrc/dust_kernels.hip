@@ -1438,6 +1438,8 @@ dust_status_t run_estimate(const Site& st, int64_t T, int64_t d_in, int64_t d_ou
                            float* rho, float* reward, float* g, void* workspace, void* stream) {
   const bool local = st.E != nullptr;
   const bool embed = st.ids != nullptr;
+  // local scoring without an input matrix: g only, no outer product
+  const bool outer = !embed && st.X != nullptr;
   Plan p;
   ReassemblyPlan rp;
   size_t r_base = 0, total = 0;
@@ -1461,8 +1463,8 @@ dust_status_t run_estimate(const Site& st, int64_t T, int64_t d_in, int64_t d_ou
   // g: fp32 for the f32 path (the caller's buffer when requested); for bf16
   // the outer product reads the bf16 split g_hi + g_lo from the workspace,
   // and fp32 g is written only when requested; the embedding's reassembly
-  // reads fp32 g
-  const bool split = dtype == DUST_BF16 && !embed;
+  // reads fp32 g, and so does a caller of the g-only local scoring
+  const bool split = dtype == DUST_BF16 && outer;
   float* g32 = split ? g : (g ? g : (float*)(ws + p.off_g));
   uint16_t* g_hi = split ? (uint16_t*)(ws + p.off_g) : nullptr;
   uint16_t* g_lo = split ? g_hi + T * d_out : nullptr;
@@ -1541,7 +1543,7 @@ dust_status_t run_estimate(const Site& st, int64_t T, int64_t d_in, int64_t d_ou
   //    then their fixed-order sum; for an embedding the reassembly
   if (embed)
     launch_reassemble(rp, ws + r_base, st.ids, g32, st.scale, G_W, s);
-  else
+  else if (outer)
     launch_outer(p, st.X, g32, g_hi, g_lo, gpart, G_W, T, d_in, d_out, dtype, s);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(DUST_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
