@@ -317,6 +317,38 @@ def test_misaligned_target_takes_the_guarded_epilogue(dev, oracle_mod, threads):
     assert rel(out["G_W"].cpu().numpy().astype(np.float64), ref["G"]) <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("gamma", [0.0, 0.5])
+def test_direct_to_lds_and_register_staged_paths_agree_bitwise(dev, gamma):
+    """The same aligned-size problem three ways: every operand 16-byte
+    aligned (the direct-to-LDS GEMMs), X and W one element into their
+    storage (the register-staged GEMMs), and target alone shifted (the
+    element-wise epilogue).  The kernels share tiles, token split and
+    contraction order, so every output is bitwise equal."""
+    import torch
+    import token_activation_perturbation_amd as dust
+    T, d_in, d_out = 1000, 136, 200  # ragged 64-wide tiles, 8-element multiples
+    print(f"aligned vs staged, gamma {gamma}", flush=True)
+    inp = synth.random_inputs(T, d_in, d_out, "bf16", seed=8)
+    kw = dict(K=8, sigma=1e-2, gamma=gamma, seed=6, antithetic=True, seq_len=250,
+              want_loss=True, want_rho=True, want_reward=True, want_g=True)
+
+    def place(a, shift):
+        flat = torch.zeros(a.size + 8, dtype=torch.bfloat16, device=dev)
+        flat[shift:shift + a.size] = torch.from_numpy(a.ravel()).to(dev).to(torch.bfloat16)
+        return flat[shift:shift + a.size].view(a.shape)
+
+    runs = {}
+    for name, (sx, st) in {"aligned": (0, 0), "staged": (1, 0), "epilogue": (0, 1)}.items():
+        Xd, Wd, td = place(inp["X"], sx), place(inp["W"], sx), place(inp["target"], st)
+        assert (Xd.data_ptr() % 16 == 0) == (sx == 0) and (td.data_ptr() % 16 == 0) == (st == 0)
+        out = dust.dust_estimate(Xd, Wd, td, **kw)
+        torch.cuda.synchronize(dev)
+        runs[name] = {k: v.cpu().numpy() for k, v in out.items()}
+    for name in ("staged", "epilogue"):
+        for k, v in runs["aligned"].items():
+            assert np.array_equal(v, runs[name][k]), (name, k)
+
+
 @pytest.fixture(scope="module")
 def max_tokens_inputs():
     """The largest token count the library accepts, T = 2^24 - 1 = 4095 x 4097
