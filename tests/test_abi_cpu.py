@@ -264,3 +264,36 @@ def test_embedding_binding_rejects_bad_tensors():
                                      antithetic=True, seq_len=4)
     with pytest.raises(ValueError):
         dust.dust_reassemble_embedding(ids, t, 4)
+
+
+def test_header_is_plain_c_and_links(tmp_path):
+    """include/dust.h compiles as C99 with every warning on, and a C program
+    built against it links libdust.so and gets the same sizing and
+    validation answers as the Python binding (no compute call)."""
+    import shutil
+    import subprocess
+    if shutil.which("gcc") is None:
+        pytest.skip("no gcc")
+    src = tmp_path / "abi.c"
+    src.write_text(r'''
+#include <stdio.h>
+#include "dust.h"
+int main(void) {
+  char a, b, c, ws; float G;
+  size_t need = dust_workspace_bytes(4096, 512, 512, 64, 1, DUST_BF16);
+  dust_status_t ok = dust_validate(&a, &b, &c, 4096, 512, 512, 512, DUST_BF16, 64, 0.01f,
+                                   0.0f, 1, &G, &ws, need);
+  dust_status_t bad = dust_validate(&a, &b, &c, 4096, 512, 512, 512, DUST_BF16, 63, 0.01f,
+                                    0.0f, 1, &G, &ws, need);
+  printf("%zu %d %d %d\n", need, (int)ok, (int)bad, dust_last_error()[0] != 0);
+  return 0;
+}
+''')
+    lib_dir = os.path.dirname(dust.library_path())
+    exe = tmp_path / "abi"
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic",
+                    "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe),
+                    "-L", lib_dir, "-ldust", f"-Wl,-rpath,{lib_dir}"], check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split()
+    need = dust.dust_workspace_bytes(4096, 512, 512, 64, True, dust.DUST_BF16)
+    assert out == [str(need), "0", "1", "1"]  # DUST_OK, DUST_ERR_INVALID_ARG, a message
