@@ -118,6 +118,17 @@ def test_python_local_binding_rejects_bad_tensors():
                                  seq_len=4)
 
 
+def test_python_binding_checks_devices_and_workspace():
+    """Operands on different devices, or a workspace that is not a device
+    tensor, are rejected before the library is called."""
+    import torch
+    X = torch.zeros(4, 4)
+    with pytest.raises(ValueError):
+        dust._check_tensors(None, X=X)
+    with pytest.raises(ValueError):
+        dust._workspace(torch.zeros(16, dtype=torch.uint8), 16, torch.device("cuda:0"))
+
+
 def _validate_local(**over):
     args = dict(X=16, E=32, T=64, d_in=16, d_out=8, seq_len=16, dtype=dust.DUST_BF16,
                 K=4, sigma=0.2, gamma=0.98, antithetic=1, G=48, ws=64, ws_bytes=None)

@@ -149,6 +149,33 @@ def _output_getter(res: dict, dev):
     return _get
 
 
+def _check_tensors(dev, **tensors):
+    """Each given tensor (None skipped) must be a contiguous device tensor on
+    `dev` (the first tensor's device when `dev` is None); returns the device."""
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, the other operands on {dev}")
+    return dev
+
+
+def _workspace(workspace, need: int, dev):
+    """The caller's workspace (a contiguous device tensor on `dev`; its byte
+    size is checked by the library) or a new uint8 tensor of `need` bytes;
+    returns (tensor, its size in bytes)."""
+    import torch
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    else:
+        _check_tensors(dev, workspace=workspace)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
 def _dtype_code(t) -> int:
     import torch
     if t.dtype == torch.bfloat16:
@@ -175,10 +202,7 @@ def dust_estimate(X, W, target, *, K: int, sigma: float, gamma: float, seed: int
     "reward" [T,K], "g" [T,d_out].  ``out`` may supply preallocated output
     tensors and ``workspace`` a uint8 device tensor of dust_workspace_bytes.
     """
-    import torch
-    for name, t in (("X", X), ("W", W), ("target", target)):
-        if not t.is_cuda or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous device tensor")
+    dev = _check_tensors(None, X=X, W=W, target=target)
     if not (X.dtype == W.dtype == target.dtype):
         raise TypeError("X, W and target must share one dtype")
     if X.dim() != 2 or W.dim() != 2 or target.dim() != 2:
@@ -189,7 +213,6 @@ def dust_estimate(X, W, target, *, K: int, sigma: float, gamma: float, seed: int
         raise ValueError(f"shape mismatch: X {tuple(X.shape)}, W {tuple(W.shape)}, "
                          f"target {tuple(target.shape)}")
     dt = _dtype_code(X)
-    dev = X.device
     res = dict(out or {})
     _get = _output_getter(res, dev)
 
@@ -198,15 +221,14 @@ def dust_estimate(X, W, target, *, K: int, sigma: float, gamma: float, seed: int
     rho = _get("rho", (T, K)) if want_rho else None
     reward = _get("reward", (T, K)) if want_reward else None
     g = _get("g", (T, d_out)) if want_g else None
-    need = dust_workspace_bytes(T, d_in, d_out, K, antithetic, dt)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    ws, ws_bytes = _workspace(workspace, dust_workspace_bytes(T, d_in, d_out, K, antithetic, dt),
+                              dev)
     ptr = lambda t: None if t is None else t.data_ptr()  # noqa: E731
     status = _load().dust_estimate(
         X.data_ptr(), W.data_ptr(), target.data_ptr(), T, d_in, d_out, seq_len, dt, K,
         sigma, gamma, ctypes.c_uint64(seed & 0xFFFFFFFFFFFFFFFF), int(bool(antithetic)),
-        G.data_ptr(), ptr(loss), ptr(rho), ptr(reward), ptr(g), workspace.data_ptr(),
-        workspace.numel(), _stream_ptr(dev))
+        G.data_ptr(), ptr(loss), ptr(rho), ptr(reward), ptr(g), ws.data_ptr(), ws_bytes,
+        _stream_ptr(dev))
     _check(status)
     return res
 
@@ -226,9 +248,7 @@ def dust_estimate_local(X, E, *, K: int, sigma: float, gamma: float, seed: int,
     "g" [T,d_out].  ``out`` and ``workspace`` as for dust_estimate.
     """
     import torch
-    for name, t in (("X", X), ("E", E)):
-        if t is not None and (not t.is_cuda or not t.is_contiguous()):
-            raise ValueError(f"{name} must be a contiguous device tensor")
+    dev = _check_tensors(None, E=E, X=X)
     if E.dtype != torch.float32:
         raise TypeError("E must be float32")
     if E.dim() != 2 or (X is not None and (X.dim() != 2 or X.shape[0] != E.shape[0])):
@@ -237,22 +257,19 @@ def dust_estimate_local(X, E, *, K: int, sigma: float, gamma: float, seed: int,
     T, d_out = E.shape
     d_in = 1 if X is None else X.shape[1]
     dt = DUST_F32 if X is None else _dtype_code(X)
-    dev = E.device
     res = dict(out or {})
     _get = _output_getter(res, dev)
     G = None if X is None else _get("G_W", (d_out, d_in))
     rho = _get("rho", (T, K)) if want_rho else None
     reward = _get("reward", (T, K)) if want_reward else None
     g = _get("g", (T, d_out)) if want_g else None
-    need = dust_workspace_bytes(T, d_in, d_out, K, antithetic, dt)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    ws, ws_bytes = _workspace(workspace, dust_workspace_bytes(T, d_in, d_out, K, antithetic, dt),
+                              dev)
     ptr = lambda t: None if t is None else t.data_ptr()  # noqa: E731
     status = _load().dust_estimate_local(
         ptr(X), E.data_ptr(), T, d_in, d_out, seq_len, dt, K, sigma, gamma,
         ctypes.c_uint64(seed & 0xFFFFFFFFFFFFFFFF), int(bool(antithetic)), ptr(G),
-        ptr(rho), ptr(reward), ptr(g), workspace.data_ptr(), workspace.numel(),
-        _stream_ptr(dev))
+        ptr(rho), ptr(reward), ptr(g), ws.data_ptr(), ws_bytes, _stream_ptr(dev))
     _check(status)
     return res
 
@@ -272,9 +289,7 @@ def dust_estimate_head(X, W, labels, *, K: int, sigma: float, seed: int, antithe
     dust_estimate.
     """
     import torch
-    for name, t in (("X", X), ("W", W), ("labels", labels)):
-        if not t.is_cuda or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous device tensor")
+    dev = _check_tensors(None, X=X, W=W, labels=labels)
     if X.dtype != W.dtype:
         raise TypeError("X and W must share a dtype")
     if labels.dtype != torch.int32:
@@ -286,7 +301,6 @@ def dust_estimate_head(X, W, labels, *, K: int, sigma: float, seed: int, antithe
     T, d_in = X.shape
     V = W.shape[0]
     dt = _dtype_code(X)
-    dev = X.device
     res = dict(out or {})
     _get = _output_getter(res, dev)
 
@@ -294,14 +308,12 @@ def dust_estimate_head(X, W, labels, *, K: int, sigma: float, seed: int, antithe
     loss = _get("loss", (T,)) if want_loss else None
     rho = _get("rho", (T, V // 256, K)) if want_rho else None
     g = _get("g", (T, V)) if want_g else None
-    need = dust_workspace_bytes(T, d_in, V, K, antithetic, dt)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    ws, ws_bytes = _workspace(workspace, dust_workspace_bytes(T, d_in, V, K, antithetic, dt), dev)
     ptr = lambda t: None if t is None else t.data_ptr()  # noqa: E731
     status = _load().dust_estimate_head(
         X.data_ptr(), W.data_ptr(), labels.data_ptr(), T, d_in, V, dt, K, sigma,
         ctypes.c_uint64(seed & 0xFFFFFFFFFFFFFFFF), int(bool(antithetic)), G.data_ptr(),
-        ptr(loss), ptr(rho), ptr(g), workspace.data_ptr(), workspace.numel(), _stream_ptr(dev))
+        ptr(loss), ptr(rho), ptr(g), ws.data_ptr(), ws_bytes, _stream_ptr(dev))
     _check(status)
     return res
 
@@ -347,9 +359,7 @@ def dust_estimate_embedding(table, ids, target, *, K: int, sigma: float, gamma: 
     tensor of dust_embedding_workspace_bytes.
     """
     import torch
-    for name, t in (("table", table), ("ids", ids), ("target", target)):
-        if not t.is_cuda or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous device tensor")
+    dev = _check_tensors(None, table=table, ids=ids, target=target)
     if table.dtype != target.dtype:
         raise TypeError("table and target must share one dtype")
     if ids.dtype != torch.int32:
@@ -361,7 +371,6 @@ def dust_estimate_embedding(table, ids, target, *, K: int, sigma: float, gamma: 
     V, d = table.shape
     T = ids.shape[0]
     dt = _dtype_code(table)
-    dev = table.device
     res = dict(out or {})
     _get = _output_getter(res, dev)
     G = _get("G_E", (V, d))
@@ -369,15 +378,14 @@ def dust_estimate_embedding(table, ids, target, *, K: int, sigma: float, gamma: 
     rho = _get("rho", (T, K)) if want_rho else None
     reward = _get("reward", (T, K)) if want_reward else None
     g = _get("g", (T, d)) if want_g else None
-    need = dust_embedding_workspace_bytes(T, V, d, K, antithetic, dt)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    ws, ws_bytes = _workspace(workspace,
+                              dust_embedding_workspace_bytes(T, V, d, K, antithetic, dt), dev)
     ptr = lambda t: None if t is None else t.data_ptr()  # noqa: E731
     status = _load().dust_estimate_embedding(
         table.data_ptr(), ids.data_ptr(), target.data_ptr(), T, V, d, seq_len, dt, K, sigma,
         gamma, ctypes.c_uint64(seed & 0xFFFFFFFFFFFFFFFF), int(bool(antithetic)), scale,
-        G.data_ptr(), ptr(loss), ptr(rho), ptr(reward), ptr(g), workspace.data_ptr(),
-        workspace.numel(), _stream_ptr(dev))
+        G.data_ptr(), ptr(loss), ptr(rho), ptr(reward), ptr(g), ws.data_ptr(), ws_bytes,
+        _stream_ptr(dev))
     _check(status)
     return res
 
@@ -387,22 +395,17 @@ def dust_reassemble_embedding(ids, g, V: int, *, scale: float = 1.0, out=None, w
     rows of g [T,d] (float32) whose ids [T] (int32) select row v, in a fixed
     order.  Returns G_E (``out`` if given: a contiguous float32 [V,d] tensor)."""
     import torch
-    for name, t in (("ids", ids), ("g", g)):
-        if not t.is_cuda or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous device tensor")
+    dev = _check_tensors(None, g=g, ids=ids)
     if ids.dtype != torch.int32 or g.dtype != torch.float32:
         raise TypeError("ids must be int32 and g float32")
     if ids.dim() != 1 or g.dim() != 2 or g.shape[0] != ids.shape[0]:
         raise ValueError(f"shape mismatch: ids {tuple(ids.shape)}, g {tuple(g.shape)}")
     T, d = g.shape
-    dev = g.device
     G = _output_getter({} if out is None else {"G_E": out}, dev)("G_E", (V, d))
-    need = dust_reassemble_workspace_bytes(T, V, d)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    ws, ws_bytes = _workspace(workspace, dust_reassemble_workspace_bytes(T, V, d), dev)
     status = _load().dust_reassemble_embedding(ids.data_ptr(), g.data_ptr(), T, V, d, scale,
-                                               G.data_ptr(), workspace.data_ptr(),
-                                               workspace.numel(), _stream_ptr(dev))
+                                               G.data_ptr(), ws.data_ptr(), ws_bytes,
+                                               _stream_ptr(dev))
     _check(status)
     return G
 
