@@ -687,9 +687,15 @@ __device__ __forceinline__ float sum_quad(float x) {
 // lane l holds the total of value l / (64 / M).
 template <int M>
 __device__ __forceinline__ float wave_reduce_to_lanes(float (&v)[M], int lane) {
-  static_assert(M == 2 || M == 4 || M == 8, "M");
+  static_assert(M == 2 || M == 4 || M == 8 || M == 16, "M");
   float x;
-  if constexpr (M == 8) {
+  if constexpr (M == 16) {
+    halve<8, 32>(v, lane);
+    halve<4, 16>(v, lane);
+    halve<2, 8>(v, lane);
+    halve<1, 4>(v, lane);
+    x = sum_quad(v[0]);
+  } else if constexpr (M == 8) {
     halve<4, 32>(v, lane);
     halve<2, 16>(v, lane);
     halve<1, 8>(v, lane);
@@ -992,13 +998,19 @@ __device__ __forceinline__ float head_rho(float u, float inv_s, bool y_in, float
   return -log1pf(y_in ? __builtin_fmaf(q, ey, (1.0f + ey) * r) : r);
 }
 
+// Antithetic pairs per register batch of the head kernel (-DDUST_HEAD_NB=4
+// or 8 at build time).
+#ifndef DUST_HEAD_NB
+#define DUST_HEAD_NB 8
+#endif
+
 template <bool ANTI, bool SMALL>
 __global__ __launch_bounds__(256) void head_ce_kernel(
     const float* __restrict__ logits, const int32_t* __restrict__ labels, int32_t V, int32_t K,
     int32_t K_n, float sigma, NoiseKey key, float* __restrict__ loss_clean,
     float* __restrict__ rho, float* __restrict__ g32, uint16_t* __restrict__ g_hi,
     uint16_t* __restrict__ g_lo) {
-  constexpr int M = 8, NB = ANTI ? 4 : 8;
+  constexpr int NB = ANTI ? DUST_HEAD_NB : 8, M = ANTI ? 2 * NB : 8;
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int waves = blockDim.x >> 6;
   const int32_t t = blockIdx.x;
@@ -1068,11 +1080,11 @@ __global__ __launch_bounds__(256) void head_ce_kernel(
                            __float_as_int(quad_comp(a[i], y_comp)), y_lane))
                      : 0.f;
       }
-      // lane l holds the partial sum of total k = l / 8: draw nb + k % NB,
-      // jitter sign - for k >= NB (antithetic); its loss reduction is formed
-      // there, all eight at once, then broadcast
+      // lane l holds the partial sum of total k = l / (64 / M): draw
+      // nb + k % NB, jitter sign - for k >= NB (antithetic); its loss
+      // reduction is formed there, all M at once, then broadcast
       const float x = wave_reduce_to_lanes<M>(v, lane);
-      const int k = lane >> 3;
+      const int k = lane / (64 / M);
       float r;
       if (y_in) {
         float ayk = ay[0];
