@@ -90,11 +90,14 @@ __device__ __forceinline__ f32x4_t mfma16(u16x8_t a, u16x8_t b, f32x4_t c) {
 
 // Work mapping.  The dispatcher deals workgroups to the 8 XCDs round-robin
 // (workgroup b runs on XCD b % 8), and each XCD has its own L2.  So the work
-// items (split, m-tile, n-tile) are linearised with n fastest, then m, then
-// split, and XCD x takes the contiguous range [x * per_xcd, (x+1) * per_xcd):
-// the workgroups resident on one XCD at a time share their A row-blocks
-// (reused across n) and the B blocks of their split (few enough to stay in
-// that L2).  grid = 8 * per_xcd; items past the end exit at once.
+// items (split, m-tile, n-tile) are linearised split-major and XCD x takes
+// the contiguous range [x * per_xcd, (x+1) * per_xcd).  Within a split the
+// items run in groups of kTileGroupM m-tiles: m fastest inside a group,
+// then n, then the next group, so the workgroups resident on one XCD at a
+// time cover a compact block of about kTileGroupM A row-blocks and a dozen
+// B blocks, which stays in that L2 even when all of B (a 3072 x 768 weight,
+// 4.7 MB) would not.  grid = 8 * per_xcd; items past the end exit at once.
+constexpr int kTileGroupM = 8;
 struct TileWork {
   int split, m_tile, n_tile;
   bool valid;
@@ -102,11 +105,16 @@ struct TileWork {
 __device__ __forceinline__ TileWork map_tile(int tiles_m, int tiles_n, int splits, int per_xcd) {
   const int b = blockIdx.x;
   const int wid = (b % 8) * per_xcd + b / 8;
+  const int per_split = tiles_m * tiles_n;
   TileWork w;
-  w.valid = wid < tiles_m * tiles_n * splits;
-  w.n_tile = wid % tiles_n;
-  w.m_tile = (wid / tiles_n) % tiles_m;
-  w.split = wid / (tiles_n * tiles_m);
+  w.valid = wid < per_split * splits;
+  w.split = wid / per_split;
+  const int r = wid % per_split;
+  const int first_m = (r / (kTileGroupM * tiles_n)) * kTileGroupM;
+  const int size_m = min(tiles_m - first_m, kTileGroupM);
+  const int in_group = r % (kTileGroupM * tiles_n);
+  w.m_tile = first_m + in_group % size_m;
+  w.n_tile = in_group / size_m;
   return w;
 }
 
