@@ -92,16 +92,20 @@ __device__ __forceinline__ f32x4_t mfma16(u16x8_t a, u16x8_t b, f32x4_t c) {
 // (workgroup b runs on XCD b % 8), and each XCD has its own L2.  So the work
 // items (split, m-tile, n-tile) are linearised split-major and XCD x takes
 // the contiguous range [x * per_xcd, (x+1) * per_xcd).  Within a split the
-// items run in groups of kTileGroupM m-tiles: m fastest inside a group,
-// then n, then the next group, so the workgroups resident on one XCD at a
-// time cover a compact block of about kTileGroupM A row-blocks and a dozen
-// B blocks, which stays in that L2 even when all of B (a 3072 x 768 weight,
-// 4.7 MB) would not.  grid = 8 * per_xcd; items past the end exit at once.
-constexpr int kTileGroupM = 8;
+// items run in groups of GM m-tiles: m fastest inside a group, then n, then
+// the next group.  The base GEMM takes GM = 8, so the workgroups resident on
+// one XCD at a time cover a compact block of about 8 A row-blocks and a
+// dozen B blocks, which stays in that L2 even when all of B (a 3072 x 768
+// weight, 4.7 MB) would not; the outer product, whose B (the layer input's
+// columns) has few tiles, takes GM = 1 (n fastest: consecutive workgroups
+// share their A row-block), which measured half the L2 misses of GM = 8 at
+// the same speed.  grid = 8 * per_xcd; items past the end exit at once.
+constexpr int kNtGroupM = 8, kTnGroupM = 1;
 struct TileWork {
   int split, m_tile, n_tile;
   bool valid;
 };
+template <int GM>
 __device__ __forceinline__ TileWork map_tile(int tiles_m, int tiles_n, int splits, int per_xcd) {
   const int b = blockIdx.x;
   const int wid = (b % 8) * per_xcd + b / 8;
@@ -110,9 +114,9 @@ __device__ __forceinline__ TileWork map_tile(int tiles_m, int tiles_n, int split
   w.valid = wid < per_split * splits;
   w.split = wid / per_split;
   const int r = wid % per_split;
-  const int first_m = (r / (kTileGroupM * tiles_n)) * kTileGroupM;
-  const int size_m = min(tiles_m - first_m, kTileGroupM);
-  const int in_group = r % (kTileGroupM * tiles_n);
+  const int first_m = (r / (GM * tiles_n)) * GM;
+  const int size_m = min(tiles_m - first_m, GM);
+  const int in_group = r % (GM * tiles_n);
   w.m_tile = first_m + in_group % size_m;
   w.n_tile = in_group / size_m;
   return w;
@@ -183,7 +187,7 @@ __global__ __launch_bounds__(256) void nt_gemm_kernel(
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  const TileWork work = map_tile(tiles_m, tiles_n, 1, per_xcd);
+  const TileWork work = map_tile<kNtGroupM>(tiles_m, tiles_n, 1, per_xcd);
   if (!work.valid) return;
   const int64_t m0 = (int64_t)work.m_tile * BM;
   const int64_t n0 = (int64_t)work.n_tile * BN;
@@ -310,7 +314,7 @@ __global__ __launch_bounds__(256) void tn_outer_kernel(
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  const TileWork work = map_tile(tiles_m, tiles_n, splits, per_xcd);
+  const TileWork work = map_tile<kTnGroupM>(tiles_m, tiles_n, splits, per_xcd);
   if (!work.valid) return;
   const int64_t m0 = (int64_t)work.m_tile * BM;
   const int64_t n0 = (int64_t)work.n_tile * BN;
@@ -458,10 +462,14 @@ typedef __attribute__((address_space(3))) void* lds_void_ptr;
 // -DDUST_TN_DMA_STAGES=n at build time): block kt + NS - 1 is in flight while
 // block kt is multiplied.
 #ifndef DUST_NT_DMA_STAGES
-#define DUST_NT_DMA_STAGES 2
+#define DUST_NT_DMA_STAGES 3
 #endif
 #ifndef DUST_TN_DMA_STAGES
 #define DUST_TN_DMA_STAGES 2
+#endif
+// tokens per k-block of the direct-to-LDS outer product (32 or 64)
+#ifndef DUST_TN_BK
+#define DUST_TN_BK 64
 #endif
 
 // Wait until this wave's loads of the oldest block in flight have landed,
@@ -506,17 +514,49 @@ __device__ __forceinline__ u16x8_t frag_sw(const uint8_t* tile, int ch0, int k0,
   return __builtin_bit_cast(u16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
+// frag_sw's fragment read through inline assembly.  The compiler treats the
+// transposing-read builtin as touching any LDS address, so before each one
+// it waits for every direct-to-LDS load in flight (vmcnt 0), draining the
+// next block's loads before the current block is multiplied.  Issued as
+// assembly the reads carry no such wait; the caller orders them with the
+// block waits and barriers of its pipeline and waits for their results with
+// frag_wait before the MFMAs read them.
+__device__ __forceinline__ v4i16_t ds_read_tr_asm(const uint8_t* p) {
+  v4i16_t r;
+  const uint32_t a = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
+  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(a));
+  return r;
+}
+
+__device__ __forceinline__ u16x8_t frag_sw_asm(const uint8_t* tile, int ch0, int k0, int lane) {
+  const int tok = k0 + 8 * (lane >> 4) + ((lane & 15) >> 2);
+  const int ch = ch0 + 4 * (lane & 3);
+  const int c = ch >> 3, eb = (ch & 7) * 2;
+  const v4i16_t lo = ds_read_tr_asm(tile + tok * 128 + 16 * (c ^ tr_swz(tok)) + eb);
+  const v4i16_t hi = ds_read_tr_asm(tile + (tok + 4) * 128 + 16 * (c ^ tr_swz(tok + 4)) + eb);
+  return __builtin_bit_cast(u16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Wait for this wave's LDS reads; the fragments pass through the statement,
+// so no use of them can be scheduled before it.
+__device__ __forceinline__ void frag_wait(u16x8_t& a0, u16x8_t& a1, u16x8_t& a2, u16x8_t& a3,
+                                          u16x8_t& b0, u16x8_t& b1) {
+  asm volatile("s_waitcnt lgkmcnt(0)"
+               : "+v"(a0), "+v"(a1), "+v"(a2), "+v"(a3), "+v"(b0), "+v"(b1));
+}
+
 __global__ __launch_bounds__(256) void tn_outer_dma_kernel(
     const uint16_t* __restrict__ g_hi, const uint16_t* __restrict__ g_lo,
     const uint16_t* __restrict__ X, int32_t T, int32_t M, int32_t N, int32_t tiles_m,
     int32_t tiles_n, int32_t splits, int32_t per_xcd, int64_t t_first, int64_t t_per_split,
     int32_t partial, float* __restrict__ out) {
-  constexpr int BK = 64, TB = BK * 128, NS = DUST_TN_DMA_STAGES;
+  constexpr int BK = DUST_TN_BK, TB = BK * 128, NS = DUST_TN_DMA_STAGES, QN = BK / 32;
+  static_assert(BK == 32 || BK == 64, "k-block");
   __shared__ __attribute__((aligned(1024))) uint8_t lds[NS * 3 * TB];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  const TileWork work = map_tile(tiles_m, tiles_n, splits, per_xcd);
+  const TileWork work = map_tile<kTnGroupM>(tiles_m, tiles_n, splits, per_xcd);
   if (!work.valid) return;
   const int64_t m0 = (int64_t)work.m_tile * 64;
   const int64_t n0 = (int64_t)work.n_tile * 64;
@@ -524,13 +564,13 @@ __global__ __launch_bounds__(256) void tn_outer_dma_kernel(
   const int64_t t_end = min((int64_t)T, t_begin + t_per_split);
   const int nk = (int)((t_end - t_begin + BK - 1) / BK);
 
-  // this lane's two DMA rows (instructions 2 wave and 2 wave + 1 of a tile)
-  // and the chunks it fetches for them
-  int rq[2];
-  int64_t a_ch[2], b_ch[2];
+  // this lane's QN DMA rows (instructions QN wave + q of a tile) and the
+  // chunks it fetches for them
+  int rq[QN];
+  int64_t a_ch[QN], b_ch[QN];
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int r = 8 * (2 * wave + q) + (lane >> 3);
+  for (int q = 0; q < QN; ++q) {
+    const int r = 8 * (QN * wave + q) + (lane >> 3);
     const int c = (lane & 7) ^ tr_swz(r);
     rq[q] = r;
     const int64_t am = m0 + 8 * c, bn = n0 + 8 * c;
@@ -541,10 +581,10 @@ __global__ __launch_bounds__(256) void tn_outer_dma_kernel(
     const int64_t tb = t_begin + (int64_t)kt * BK;
     uint8_t* base = lds + buf * 3 * TB;
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
+    for (int q = 0; q < QN; ++q) {
       int64_t t = tb + rq[q];
       t = t < T ? t : (int64_t)T - 1;
-      const int dst = (2 * wave + q) * 1024;
+      const int dst = (QN * wave + q) * 1024;
       __builtin_amdgcn_global_load_lds(g_hi + t * M + a_ch[q], (lds_void_ptr)(base + dst), 16, 0, 0);
       __builtin_amdgcn_global_load_lds(g_lo + t * M + a_ch[q], (lds_void_ptr)(base + TB + dst), 16,
                                        0, 0);
@@ -562,7 +602,7 @@ __global__ __launch_bounds__(256) void tn_outer_dma_kernel(
   for (int b = 0; b < NS - 1 && b < nk; ++b) issue(b, b);
   for (int kt = 0; kt < nk; ++kt) {
     // this wave's loads of block kt have landed ...
-    wait_blocks<NS, 6>(min(nk - 1 - kt, NS - 2));
+    wait_blocks<NS, 3 * QN>(min(nk - 1 - kt, NS - 2));
     stage_barrier();  // ... and every wave's; block kt - 1 is no longer read
     const int buf = kt % NS;
     uint8_t* base = lds + buf * 3 * TB;
@@ -583,11 +623,12 @@ __global__ __launch_bounds__(256) void tn_outer_dma_kernel(
       u16x8_t ah[2], al[2], bf[2];
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        ah[i] = frag_sw(base, wm * 32 + i * 16, ks, lane);
-        al[i] = frag_sw(base + TB, wm * 32 + i * 16, ks, lane);
+        ah[i] = frag_sw_asm(base, wm * 32 + i * 16, ks, lane);
+        al[i] = frag_sw_asm(base + TB, wm * 32 + i * 16, ks, lane);
       }
 #pragma unroll
-      for (int j = 0; j < 2; ++j) bf[j] = frag_sw(base + 2 * TB, wn * 32 + j * 16, ks, lane);
+      for (int j = 0; j < 2; ++j) bf[j] = frag_sw_asm(base + 2 * TB, wn * 32 + j * 16, ks, lane);
+      frag_wait(ah[0], ah[1], al[0], al[1], bf[0], bf[1]);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -614,8 +655,10 @@ __global__ __launch_bounds__(256) void tn_outer_dma_kernel(
 // The base GEMM fed by direct-to-LDS loads, for the aligned case (K a
 // multiple of 8; A, B 16-byte aligned; lda, ldb multiples of 8).  Same tiles,
 // contraction order and results (bitwise) as nt_gemm_kernel; NS LDS stages
-// of 16 KiB, block kt + NS - 1 in flight while block kt is multiplied.  An operand tile is 64 rows x 64 contraction values bf16, a row
-// per 128 bytes, chunk c of row r in slot c ^ nt_swz(r): the 16-byte fragment
+// of 16 KiB, blocks up to kt + NS - 1 in flight while block kt is
+// multiplied (3 stages: 48 KiB, three workgroups per CU).  An operand tile is
+// 64 rows x 64 contraction values bf16, a row per 128 bytes, chunk c of row
+// r in slot c ^ nt_swz(r): the 16-byte fragment
 // reads (16 rows of one chunk per quarter-wave) then hit every bank once
 // (nt_swz found by the same exhaustive search as tr_swz).  Rows past M or N
 // re-read the last row (their outputs are never stored); chunks past K
@@ -636,7 +679,7 @@ __global__ __launch_bounds__(256) void nt_gemm_dma_kernel(
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  const TileWork work = map_tile(tiles_m, tiles_n, 1, per_xcd);
+  const TileWork work = map_tile<kNtGroupM>(tiles_m, tiles_n, 1, per_xcd);
   if (!work.valid) return;
   const int64_t m0 = (int64_t)work.m_tile * 64;
   const int64_t n0 = (int64_t)work.n_tile * 64;
