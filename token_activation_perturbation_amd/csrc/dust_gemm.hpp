@@ -3,8 +3,9 @@
 //   base   delta[t][c] = sum_k X[t][k] W[c][k] - target[t][c]  ("NT": both
 //          operands contiguous along the contraction axis k)
 //   outer  G[c][i] = sum_t g[t][c] X[t][i]  ("TN": both operands contiguous
-//          along the output axes, the token axis t strided), g fp32 split
-//          into bf16 hi + lo on the way into LDS.
+//          along the output axes, the token axis t strided), g as its bf16
+//          split hi = rn(g), lo = rn(g - hi) (written by the noise kernels),
+//          each half an MFMA A operand, fp32 accumulation.
 //
 // A workgroup of 256 threads (4 waves in a 2x2 grid) computes a 64 x 64
 // tile; each wave a 32 x 32 block of 16x16 MFMA tiles

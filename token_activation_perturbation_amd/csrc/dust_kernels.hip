@@ -1,23 +1,36 @@
 // dust_kernels.hip -- gfx950 kernels and the device-side entry points of
-// libdust.so (dust_estimate, dust_noise_fill).
+// libdust.so (dust_estimate, dust_estimate_local, dust_estimate_head,
+// dust_estimate_embedding, dust_reassemble_embedding, dust_noise_fill,
+// dust_set_timing_events).
 //
 // The estimator ("Dust: every token is a member of the population", section
-// "Perturb the activations, not the weights") runs as six stages on the
-// caller's stream:
-//   base_gemm      y_t = W x_t on MFMA, delta_t = y_t - target_t     (fp32)
-//   jitter_loss    P = <delta_t, a_t^n>, Q = ||a_t^n||^2 per (t, n), and the
-//                  clean loss L_t; the noise is generated inline
+// "Perturb the activations, not the weights") runs on the caller's stream as
+//   base_gemm      y_t = W x_t on MFMA, delta_t = y_t - target_t (fp32)
+//                  (an embedding gathers table rows instead; local scoring
+//                  takes the caller's error estimate E as delta)
+// then, when every token's loss stands alone (gamma = 0 or one-token
+// sequences), one noise pass:
+//   fused_g0       per token, each batch of draws generated once in
+//                  registers: P = <delta_t, a_t^n>, Q = ||a_t^n||^2 reduced
+//                  across the wave, the draw's weight, and g_t accumulated
+//                  (antithetic: g = 2/K sum_n P_n a^n; plain draws: the
+//                  centred form); rho, the credit and L_t when asked for
+// or, when later tokens' losses feed the credit (gamma > 0), two passes:
+//   jitter_loss    P, Q per (t, n) and the clean loss L_t
 //   token_stats    rho_t^(i) = -s_i sigma P - 1/2 sigma^2 Q (the exact loss
-//                  reduction of the quadratic loss, computed at its own
-//                  scale instead of as a difference of two large losses) and
+//                  reduction of the quadratic loss, at its own scale) and
 //                  its mean over the K draws of the token
 //   credit         c = rho - mean, r_t = c_t + gamma r_{t+1} per sequence
-//                  (a chunked scan for gamma > 0), and the per-(t, n) weight
+//                  (a chunked scan), and the per-(t, n) weight
 //                  -1/(K sigma) (r^(2n) - r^(2n+1)) (antithetic) or
 //                  -1/(K sigma) r^(n)
-//   reweight       g_t = sum_n weight_(t,n) a_t^n; the noise regenerated inline
+//   reweight       g_t = sum_n weight_(t,n) a_t^n, the noise regenerated
+// and last
 //   outer          G_W = sum_t g_t x_t^T on MFMA (bf16 hi/lo split of g),
 //                  split over tokens, partials summed in a fixed order
+//                  (an embedding scatters g by token id instead).
+// The cross-entropy head has its own slab kernel (head_ce_kernel) between
+// the logits GEMM and the outer product.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
