@@ -745,7 +745,11 @@ __device__ __forceinline__ void wave_reduce_to_scalars(float (&v)[M], int lane, 
 #define DUST_FUSED_NB_SMALL 4
 #endif
 
-template <int QPL, bool ANTI, bool FULL>
+// QN: Q_n = ||a^n||^2 is formed (plain draws, whose weight needs it, or when
+// the caller asks for rho or the credit).  Antithetic pairs that only feed
+// g skip it; its slot in the reduction then carries zeros, so P, g and G_W
+// are bit for bit those of the QN = true kernel.
+template <int QPL, bool ANTI, bool FULL, bool QN = true>
 __global__ __launch_bounds__(256) void fused_g0_kernel(
     const float* __restrict__ delta, int32_t t0, int32_t d_out, int32_t K, int32_t K_n, int32_t per_wave, float sigma, float curv_coef, NoiseKey key,
     float* __restrict__ Pout, float* __restrict__ Qout, float* __restrict__ loss_clean,
@@ -818,17 +822,20 @@ __global__ __launch_bounds__(256) void fused_g0_kernel(
         } else {
           a[i][j] = make_float4(0.f, 0.f, 0.f, 0.f);
         }
-        float p = v[i], s = v[NB + i];
+        float p = v[i];
         p = __builtin_fmaf(d[j].x, a[i][j].x, p);
         p = __builtin_fmaf(d[j].y, a[i][j].y, p);
         p = __builtin_fmaf(d[j].z, a[i][j].z, p);
         p = __builtin_fmaf(d[j].w, a[i][j].w, p);
-        s = __builtin_fmaf(a[i][j].x, a[i][j].x, s);
-        s = __builtin_fmaf(a[i][j].y, a[i][j].y, s);
-        s = __builtin_fmaf(a[i][j].z, a[i][j].z, s);
-        s = __builtin_fmaf(a[i][j].w, a[i][j].w, s);
         v[i] = p;
-        v[NB + i] = s;
+        if (QN) {
+          float s = v[NB + i];
+          s = __builtin_fmaf(a[i][j].x, a[i][j].x, s);
+          s = __builtin_fmaf(a[i][j].y, a[i][j].y, s);
+          s = __builtin_fmaf(a[i][j].z, a[i][j].z, s);
+          s = __builtin_fmaf(a[i][j].w, a[i][j].w, s);
+          v[NB + i] = s;
+        }
       }
     }
     float tot[M];
@@ -838,7 +845,7 @@ __global__ __launch_bounds__(256) void fused_g0_kernel(
       const int32_t n = nb + i;
       if (n < n_end) {
         const float P = tot[i], Q = tot[NB + i];
-        if (Pout && lane == 0) {
+        if (QN && Pout && lane == 0) {
           Pout[(int64_t)t * K_n + n] = P;
           Qout[(int64_t)t * K_n + n] = Q;
         }
@@ -1230,18 +1237,20 @@ void launch_fused_g0_qpl(bool anti, bool full, unsigned blocks, unsigned threads
                          int32_t d_out, int32_t K, int32_t K_n, int32_t per_wave, float sigma,
                          float curv, NoiseKey key, float* P, float* Q, float* loss, float* g32,
                          uint16_t* g_hi, uint16_t* g_lo) {
-#define DUST_FUSED_LAUNCH(A, F)                                                               \
-  hipExtLaunchKernelGGL((fused_g0_kernel<QPL, A, F>), dim3(blocks), dim3(threads), 0, s,      \
+#define DUST_FUSED_LAUNCH(A, F, QN)                                                           \
+  hipExtLaunchKernelGGL((fused_g0_kernel<QPL, A, F, QN>), dim3(blocks), dim3(threads), 0, s,  \
                         tl.start, tl.stop, 0, delta, t0, d_out, K, K_n, per_wave, sigma, curv, \
                         key, P, Q, loss, g32, g_hi, g_lo)
+  // Q is needed by plain draws and by the per-draw outputs (P != nullptr)
+  const bool need_q = !anti || P != nullptr;
   if (anti && full)
-    DUST_FUSED_LAUNCH(true, true);
+    need_q ? DUST_FUSED_LAUNCH(true, true, true) : DUST_FUSED_LAUNCH(true, true, false);
   else if (anti)
-    DUST_FUSED_LAUNCH(true, false);
+    need_q ? DUST_FUSED_LAUNCH(true, false, true) : DUST_FUSED_LAUNCH(true, false, false);
   else if (full)
-    DUST_FUSED_LAUNCH(false, true);
+    DUST_FUSED_LAUNCH(false, true, true);
   else
-    DUST_FUSED_LAUNCH(false, false);
+    DUST_FUSED_LAUNCH(false, false, true);
 #undef DUST_FUSED_LAUNCH
 }
 

@@ -15,9 +15,11 @@ at once.  Their bound is the vector ALU issue rate, counted in lane-slots:
   pairs, else K).  Per quad of four values:
     Philox4x32-10   10 rounds x (2 multiplies x 4 + 4 xor)      = 120 slots
     Box-Muller      8 transcendentals x 4 + 18 simple ops        =  50 slots
-  i.e. 42.5 slots per value, plus the consumers: 2 FMA for P and Q (loss
-  change), 1 FMA for the reweighted sum g, and 1 add for the plain-draw
-  noise sum used by the centring.
+  i.e. 42.5 slots per value, plus the consumers: 1 FMA for P = <delta, a>,
+  1 FMA for Q = ||a||^2 (needed by plain draws and by the per-draw outputs;
+  with antithetic pairs the curvature cancels inside each pair, so a call
+  that asks only for g and G_W does without it), 1 FMA for the reweighted
+  sum g, and 1 add for the plain-draw noise sum used by the centring.
 
 The cross-entropy head's slab kernel consumes each value as: 1 multiply
 (sigma a), the jitter's expm1 (antithetic: both signs from the even and odd
@@ -46,9 +48,13 @@ def distinct_noise_values(T: int, d_out: int, K: int, antithetic: bool) -> int:
     return K_n * T * d_out
 
 
-def fused_kernel_slots(T: int, d_out: int, K: int, antithetic: bool) -> float:
-    """Algorithmic lane-slots of the single-generation kernel (gamma = 0)."""
-    per_value = GEN_SLOTS_PER_VALUE + 3.0 + (0.0 if antithetic else 1.0)
+def fused_kernel_slots(T: int, d_out: int, K: int, antithetic: bool,
+                       per_draw_outputs: bool = False) -> float:
+    """Algorithmic lane-slots of the single-generation kernel (gamma = 0);
+    `per_draw_outputs`: the call asks for rho or the credit."""
+    need_q = per_draw_outputs or not antithetic
+    per_value = GEN_SLOTS_PER_VALUE + 2.0 + (1.0 if need_q else 0.0) + \
+        (0.0 if antithetic else 1.0)
     return distinct_noise_values(T, d_out, K, antithetic) * per_value
 
 
