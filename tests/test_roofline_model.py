@@ -1,8 +1,10 @@
 """The ALU cost model the bench line's roofline fraction uses, against the
 counts it states: Philox4x32-10 is 10 rounds of 2 quarter-rate 32x32->64
-multiplies and 4 xors per word pair (120 slots per quad), Box-Muller 8
-quarter-rate transcendentals and 18 simple ops per quad (50 slots), and the
-consumers one slot each."""
+multiplies and 4 xors per quad, of which the first round's draw-independent
+half (the quad index's product and the xor with the zero word and the key)
+is shared by all draws (113 slots per quad); Box-Muller 8 quarter-rate
+transcendentals and 18 simple ops per quad (50 slots); the consumers one
+slot each."""
 import pytest
 
 from token_activation_perturbation_amd import roofline
@@ -14,16 +16,16 @@ def test_peak_is_the_fp32_vector_rate():
 
 
 def test_generation_slots_per_value():
-    assert roofline.PHILOX_SLOTS_PER_QUAD == 120
+    assert roofline.PHILOX_SLOTS_PER_QUAD == 9 * 12 + 5
     assert roofline.BOX_MULLER_SLOTS_PER_QUAD == 50
-    assert roofline.GEN_SLOTS_PER_VALUE == 42.5
+    assert roofline.GEN_SLOTS_PER_VALUE == 40.75
 
 
 @pytest.mark.parametrize("anti,outputs,per_value", [
-    (True, False, 44.5),   # P and g; the pair cancels the curvature: no Q
-    (True, True, 45.5),    # rho or the credit asked for: Q too
-    (False, False, 46.5),  # plain draws: Q in the weight, the noise sum for centring
-    (False, True, 46.5),
+    (True, False, 42.75),   # P and g; the pair cancels the curvature: no Q
+    (True, True, 43.75),    # rho or the credit asked for: Q too
+    (False, False, 44.75),  # plain draws: Q in the weight, the noise sum for centring
+    (False, True, 44.75),
 ])
 def test_fused_kernel_slots(anti, outputs, per_value):
     T, d_out, K = 8, 12, 6
@@ -33,7 +35,7 @@ def test_fused_kernel_slots(anti, outputs, per_value):
 
 
 def test_two_pass_and_head_slots():
-    assert roofline.jitter_kernel_slots(2, 4, 4, True) == pytest.approx(2 * 2 * 4 * 44.5)
-    assert roofline.head_slots_per_value(True) == 57.5
-    assert roofline.head_slots_per_value(False) == 54.5
-    assert roofline.head_kernel_slots(1, 256, 4, True) == pytest.approx(2 * 256 * 57.5)
+    assert roofline.jitter_kernel_slots(2, 4, 4, True) == pytest.approx(2 * 2 * 4 * 42.75)
+    assert roofline.head_slots_per_value(True) == 55.75
+    assert roofline.head_slots_per_value(False) == 52.75
+    assert roofline.head_kernel_slots(1, 256, 4, True) == pytest.approx(2 * 256 * 55.75)

@@ -13,9 +13,14 @@ at once.  Their bound is the vector ALU issue rate, counted in lane-slots:
 * Work per distinct noise value (the minimum the method needs: each of the
   K_n * T * d_out values generated once, where K_n = K/2 with antithetic
   pairs, else K).  Per quad of four values:
-    Philox4x32-10   10 rounds x (2 multiplies x 4 + 4 xor)      = 120 slots
+    Philox4x32-10   9 rounds x (2 multiplies x 4 + 4 xor)
+                    + first round 1 multiply x 4 + 1 xor         = 113 slots
     Box-Muller      8 transcendentals x 4 + 18 simple ops        =  50 slots
-  i.e. 42.5 slots per value, plus the consumers: 1 FMA for P = <delta, a>,
+  The counter is (quad, token, noise index, 0), so the first round's product
+  of the quad index and its xor with the zero word and the key are the same
+  for every noise index of a (token, quad): only the product of the noise
+  index and one xor depend on the draw.  That gives 40.75 slots per value,
+  plus the consumers: 1 FMA for P = <delta, a>,
   1 FMA for Q = ||a||^2 (needed by plain draws and by the per-draw outputs;
   with antithetic pairs the curvature cancels inside each pair, so a call
   that asks only for g and G_W does without it), 1 FMA for the reweighted
@@ -25,7 +30,7 @@ The cross-entropy head's slab kernel consumes each value as: 1 multiply
 (sigma a), the jitter's expm1 (antithetic: both signs from the even and odd
 Taylor parts, 9 + 2 slots; plain draws: 8 slots of Horner), the slab's
 partial sums (one FMA per sign), 1 FMA for g and, for plain draws, 1 add for
-the noise sum: 57.5 slots per value with antithetic pairs, 54.5 without.
+the noise sum: 55.75 slots per value with antithetic pairs, 52.75 without.
 
 Counted this way a two-pass pipeline (generate for the loss change, then
 regenerate for g) is capped at about half of the roofline; a single
@@ -38,9 +43,9 @@ CLOCK_HZ = 2.4e9
 LANES_PER_CU_CLOCK = 128
 PEAK_SLOTS_PER_S = CUS * LANES_PER_CU_CLOCK * CLOCK_HZ  # 7.864e13
 
-PHILOX_SLOTS_PER_QUAD = 10 * (2 * 4 + 4)           # 120
+PHILOX_SLOTS_PER_QUAD = 9 * (2 * 4 + 4) + (4 + 1)  # 113
 BOX_MULLER_SLOTS_PER_QUAD = 8 * 4 + 18             # 50
-GEN_SLOTS_PER_VALUE = (PHILOX_SLOTS_PER_QUAD + BOX_MULLER_SLOTS_PER_QUAD) / 4.0  # 42.5
+GEN_SLOTS_PER_VALUE = (PHILOX_SLOTS_PER_QUAD + BOX_MULLER_SLOTS_PER_QUAD) / 4.0  # 40.75
 
 
 def distinct_noise_values(T: int, d_out: int, K: int, antithetic: bool) -> int:
