@@ -213,12 +213,12 @@ def main():
         min_s = roofline.head_min_seconds(w.T, w.d_out, w.K, w.antithetic)
     elif fused:
         kernel = "fused_g0_kernel"
-        slots = roofline.fused_kernel_slots(w.T, w.d_out, w.K, w.antithetic)
+        slots = roofline.fused_kernel_slots(w.T, w.d_out, w.K, w.antithetic, local=w.local)
     else:
         kernel = "jitter_loss_kernel"
-        slots = roofline.jitter_kernel_slots(w.T, w.d_out, w.K, w.antithetic)
+        slots = roofline.jitter_kernel_slots(w.T, w.d_out, w.K, w.antithetic, local=w.local)
     if not w.head:
-        min_s = roofline.estimate_min_seconds(w.T, w.d_out, w.K, w.antithetic)
+        min_s = roofline.estimate_min_seconds(w.T, w.d_out, w.K, w.antithetic, local=w.local)
     achieved = slots / (kernel_ms * 1e-3) / 1e12
     peak = roofline.PEAK_SLOTS_PER_S / 1e12
     result = {

@@ -34,6 +34,16 @@ def test_fused_kernel_slots(anti, outputs, per_value):
     assert got == pytest.approx(K_n * T * d_out * per_value)
 
 
+def test_local_scoring_has_no_curvature_term():
+    # P and g (antithetic) or P, g and the noise sum (plain): never Q
+    assert roofline.fused_kernel_slots(2, 4, 4, True, per_draw_outputs=True, local=True) == \
+        pytest.approx(2 * 2 * 4 * 42.75)
+    assert roofline.fused_kernel_slots(2, 4, 4, False, local=True) == \
+        pytest.approx(4 * 2 * 4 * 43.75)
+    assert roofline.jitter_kernel_slots(2, 4, 4, True, local=True) == \
+        pytest.approx(2 * 2 * 4 * 41.75)
+
+
 def test_two_pass_and_head_slots():
     assert roofline.jitter_kernel_slots(2, 4, 4, True) == pytest.approx(2 * 2 * 4 * 42.75)
     assert roofline.head_slots_per_value(True) == 55.75

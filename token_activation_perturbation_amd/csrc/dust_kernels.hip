@@ -201,8 +201,10 @@ __device__ __forceinline__ float wave_sum(float v) {
 // Jitter + loss change.  One wave per (token t, chunk of noise indices).
 // Lane l owns the channel quads q = l + 64 j of the token.  For a batch of 16
 // noise indices each lane accumulates its share of P_n = <delta_t, a_t^n>
-// and Q_n = ||a_t^n||^2, then one wave reduction yields the 16 totals.
+// and Q_n = ||a_t^n||^2, then one wave reduction yields the 16 totals.  QN
+// false (local scoring, whose score is linear in the jitter): no Q.
 
+template <bool QN>
 __global__ __launch_bounds__(256) void jitter_loss_kernel(
     const float* __restrict__ delta, int32_t vec, int32_t T, int32_t d_out, int32_t nq,
     int32_t K_n, int32_t chunks, int32_t per_chunk, NoiseKey key, float* __restrict__ P,
@@ -257,27 +259,30 @@ __global__ __launch_bounds__(256) void jitter_loss_kernel(
             a.z *= m.z;
             a.w *= m.w;
           }
-          float pj = p[j], sj = s[j];
+          float pj = p[j];
           pj = __builtin_fmaf(d.x, a.x, pj);
           pj = __builtin_fmaf(d.y, a.y, pj);
           pj = __builtin_fmaf(d.z, a.z, pj);
           pj = __builtin_fmaf(d.w, a.w, pj);
-          sj = __builtin_fmaf(a.x, a.x, sj);
-          sj = __builtin_fmaf(a.y, a.y, sj);
-          sj = __builtin_fmaf(a.z, a.z, sj);
-          sj = __builtin_fmaf(a.w, a.w, sj);
           p[j] = pj;
-          s[j] = sj;
+          if (QN) {
+            float sj = s[j];
+            sj = __builtin_fmaf(a.x, a.x, sj);
+            sj = __builtin_fmaf(a.y, a.y, sj);
+            sj = __builtin_fmaf(a.z, a.z, sj);
+            sj = __builtin_fmaf(a.w, a.w, sj);
+            s[j] = sj;
+          }
         }
       }
     }
     wave_reduce16(p, lane);
-    wave_reduce16(s, lane);
+    if (QN) wave_reduce16(s, lane);
     const int32_t n = nb + ((lane >> 2) & 15);
     if ((lane & 3) == 0 && n < n_end) {
       const int64_t o = (int64_t)t * K_n + n;
       P[o] = p[0];
-      Q[o] = s[0];
+      if (QN && Q) Q[o] = s[0];
     }
   }
 }
@@ -299,7 +304,7 @@ __global__ __launch_bounds__(256) void token_stats_kernel(
   float sum = 0.f;
   for (int32_t n = lane; n < K_n; n += 64) {
     const float pn = P[t * K_n + n];
-    const float curv = half_s2 * Q[t * K_n + n];
+    const float curv = Q ? half_s2 * Q[t * K_n + n] : 0.f;  // no Q: no curvature
     if (antithetic) {
       const float r0 = -__builtin_fmaf(sigma, pn, curv);
       const float r1 = __builtin_fmaf(sigma, pn, -curv);
@@ -745,10 +750,11 @@ __device__ __forceinline__ void wave_reduce_to_scalars(float (&v)[M], int lane, 
 #define DUST_FUSED_NB_SMALL 4
 #endif
 
-// QN: Q_n = ||a^n||^2 is formed (plain draws, whose weight needs it, or when
-// the caller asks for rho or the credit).  Antithetic pairs that only feed
-// g skip it; its slot in the reduction then carries zeros, so P, g and G_W
-// are bit for bit those of the QN = true kernel.
+// QN: Q_n = ||a^n||^2 is formed (the quadratic loss with plain draws, whose
+// weight needs it, or when the caller asks for rho or the credit).  Local
+// scoring (no curvature term) and antithetic pairs that only feed g skip it;
+// its slot in the reduction then carries zeros, so P, g and G_W are bit for
+// bit those of the QN = true kernel.
 template <int QPL, bool ANTI, bool FULL, bool QN = true>
 __global__ __launch_bounds__(256) void fused_g0_kernel(
     const float* __restrict__ delta, int32_t t0, int32_t d_out, int32_t K, int32_t K_n, int32_t per_wave, float sigma, float curv_coef, NoiseKey key,
@@ -845,9 +851,9 @@ __global__ __launch_bounds__(256) void fused_g0_kernel(
       const int32_t n = nb + i;
       if (n < n_end) {
         const float P = tot[i], Q = tot[NB + i];
-        if (QN && Pout && lane == 0) {
+        if (Pout && lane == 0) {
           Pout[(int64_t)t * K_n + n] = P;
-          Qout[(int64_t)t * K_n + n] = Q;
+          if (QN && Qout) Qout[(int64_t)t * K_n + n] = Q;
         }
         const float w = ANTI ? P : -__builtin_fmaf(sigma, P, half_s2 * Q);
         if (!ANTI) rsum += w;
@@ -1241,16 +1247,17 @@ void launch_fused_g0_qpl(bool anti, bool full, unsigned blocks, unsigned threads
   hipExtLaunchKernelGGL((fused_g0_kernel<QPL, A, F, QN>), dim3(blocks), dim3(threads), 0, s,  \
                         tl.start, tl.stop, 0, delta, t0, d_out, K, K_n, per_wave, sigma, curv, \
                         key, P, Q, loss, g32, g_hi, g_lo)
-  // Q is needed by plain draws and by the per-draw outputs (P != nullptr)
-  const bool need_q = !anti || P != nullptr;
+  // Q is needed when the loss has a curvature term, by plain draws and by the
+  // per-draw outputs (P != nullptr)
+  const bool need_q = curv != 0.0f && (!anti || P != nullptr);
   if (anti && full)
     need_q ? DUST_FUSED_LAUNCH(true, true, true) : DUST_FUSED_LAUNCH(true, true, false);
   else if (anti)
     need_q ? DUST_FUSED_LAUNCH(true, false, true) : DUST_FUSED_LAUNCH(true, false, false);
   else if (full)
-    DUST_FUSED_LAUNCH(false, true, true);
+    need_q ? DUST_FUSED_LAUNCH(false, true, true) : DUST_FUSED_LAUNCH(false, true, false);
   else
-    DUST_FUSED_LAUNCH(false, false, true);
+    need_q ? DUST_FUSED_LAUNCH(false, false, true) : DUST_FUSED_LAUNCH(false, false, false);
 #undef DUST_FUSED_LAUNCH
 }
 
@@ -1516,18 +1523,26 @@ dust_status_t run_estimate(const Site& st, int64_t T, int64_t d_in, int64_t d_ou
   const bool independent = (gamma == 0.0f || seq_len == 1);
   const bool fused = independent && qpl > 0;
   const bool want_pq = rho != nullptr || reward != nullptr;
+  // Q = ||a||^2 only where the loss has a curvature term (not local scoring)
+  float* const Qused = curv != 0.0f ? Qbuf : nullptr;
   const TimedLaunch tl = take_timing_events();
 
   if (!fused) {
     // 2. jitter + loss change
-    hipExtLaunchKernelGGL(jitter_loss_kernel, dim3(grid_for(T * p.jl_chunks, 4)), dim3(256), 0, s,
-                          tl.start, tl.stop, 0, (const float*)delta, (int32_t)delta_vec, Ti,
-                          dout, p.nq, p.K_n, p.jl_chunks, p.jl_per_chunk, key, Pbuf, Qbuf,
-                          loss_clean);
+    if (Qused)
+      hipExtLaunchKernelGGL(jitter_loss_kernel<true>, dim3(grid_for(T * p.jl_chunks, 4)),
+                            dim3(256), 0, s, tl.start, tl.stop, 0, (const float*)delta,
+                            (int32_t)delta_vec, Ti, dout, p.nq, p.K_n, p.jl_chunks,
+                            p.jl_per_chunk, key, Pbuf, Qused, loss_clean);
+    else
+      hipExtLaunchKernelGGL(jitter_loss_kernel<false>, dim3(grid_for(T * p.jl_chunks, 4)),
+                            dim3(256), 0, s, tl.start, tl.stop, 0, (const float*)delta,
+                            (int32_t)delta_vec, Ti, dout, p.nq, p.K_n, p.jl_chunks,
+                            p.jl_per_chunk, key, Pbuf, Qused, loss_clean);
     // 3. loss reductions and their mean over draws
     hipLaunchKernelGGL(token_stats_kernel, dim3(grid_for(T, 4)), dim3(256), 0, s,
-                       (const float*)Pbuf, (const float*)Qbuf, Ti, K, p.K_n, p.antithetic, sigma,
-                       curv, rho_buf, mean);
+                       (const float*)Pbuf, (const float*)Qused, Ti, K, p.K_n, p.antithetic,
+                       sigma, curv, rho_buf, mean);
     // 4. centring + discounted credit -> per-(t, n) weights
     if (independent) {
       hipLaunchKernelGGL(credit_token_kernel, dim3(grid_for(T * p.K_n, 256)), dim3(256), 0, s,
@@ -1557,11 +1572,11 @@ dust_status_t run_estimate(const Site& st, int64_t T, int64_t d_in, int64_t d_ou
     const bool full = (p.nq == 64 * qpl) && delta_vec;
     launch_fused_g0(qpl, p.antithetic != 0, full, (unsigned)T, (unsigned)(64 * p.fz_waves), s,
                     tl, (const float*)delta, 0, dout, K, p.K_n, p.fz_per_wave, sigma,
-                    curv, key, want_pq ? Pbuf : nullptr, want_pq ? Qbuf : nullptr, loss_clean, g32,
-                    g_hi, g_lo);
+                    curv, key, want_pq ? Pbuf : nullptr, want_pq ? Qused : nullptr, loss_clean,
+                    g32, g_hi, g_lo);
     if (want_pq) {
       hipLaunchKernelGGL(token_stats_kernel, dim3(grid_for(T, 4)), dim3(256), 0, s,
-                         (const float*)Pbuf, (const float*)Qbuf, Ti, K, p.K_n, p.antithetic,
+                         (const float*)Pbuf, (const float*)Qused, Ti, K, p.K_n, p.antithetic,
                          sigma, curv, rho_buf, mean);
       hipLaunchKernelGGL(credit_token_kernel, dim3(grid_for(T * p.K_n, 256)), dim3(256), 0, s,
                          (const float*)rho_buf, (const float*)mean, Ti, K, p.K_n, p.antithetic,

@@ -21,10 +21,12 @@ at once.  Their bound is the vector ALU issue rate, counted in lane-slots:
   for every noise index of a (token, quad): only the product of the noise
   index and one xor depend on the draw.  That gives 40.75 slots per value,
   plus the consumers: 1 FMA for P = <delta, a>,
-  1 FMA for Q = ||a||^2 (needed by plain draws and by the per-draw outputs;
-  with antithetic pairs the curvature cancels inside each pair, so a call
-  that asks only for g and G_W does without it), 1 FMA for the reweighted
-  sum g, and 1 add for the plain-draw noise sum used by the centring.
+  1 FMA for Q = ||a||^2 (the quadratic loss's curvature term: needed by
+  plain draws and by the per-draw outputs; with antithetic pairs it cancels
+  inside each pair, so a call that asks only for g and G_W does without it,
+  and local scoring, linear in the jitter, never needs it), 1 FMA for the
+  reweighted sum g, and 1 add for the plain-draw noise sum used by the
+  centring.
 
 The cross-entropy head's slab kernel consumes each value as: 1 multiply
 (sigma a), the jitter's expm1 (antithetic: both signs from the even and odd
@@ -54,23 +56,28 @@ def distinct_noise_values(T: int, d_out: int, K: int, antithetic: bool) -> int:
 
 
 def fused_kernel_slots(T: int, d_out: int, K: int, antithetic: bool,
-                       per_draw_outputs: bool = False) -> float:
+                       per_draw_outputs: bool = False, local: bool = False) -> float:
     """Algorithmic lane-slots of the single-generation kernel (gamma = 0);
-    `per_draw_outputs`: the call asks for rho or the credit."""
-    need_q = per_draw_outputs or not antithetic
+    `per_draw_outputs`: the call asks for rho or the credit; `local`: local
+    scoring (no curvature term)."""
+    need_q = not local and (per_draw_outputs or not antithetic)
     per_value = GEN_SLOTS_PER_VALUE + 2.0 + (1.0 if need_q else 0.0) + \
         (0.0 if antithetic else 1.0)
     return distinct_noise_values(T, d_out, K, antithetic) * per_value
 
 
-def jitter_kernel_slots(T: int, d_out: int, K: int, antithetic: bool) -> float:
-    """Algorithmic lane-slots of the jitter-loss kernel of the two-pass path."""
-    return distinct_noise_values(T, d_out, K, antithetic) * (GEN_SLOTS_PER_VALUE + 2.0)
+def jitter_kernel_slots(T: int, d_out: int, K: int, antithetic: bool,
+                        local: bool = False) -> float:
+    """Algorithmic lane-slots of the jitter-loss kernel of the two-pass path
+    (P and, for the quadratic loss, Q)."""
+    per_value = GEN_SLOTS_PER_VALUE + (1.0 if local else 2.0)
+    return distinct_noise_values(T, d_out, K, antithetic) * per_value
 
 
-def estimate_min_seconds(T: int, d_out: int, K: int, antithetic: bool) -> float:
+def estimate_min_seconds(T: int, d_out: int, K: int, antithetic: bool,
+                         local: bool = False) -> float:
     """Lower bound on one estimate: one generation of every noise value."""
-    return fused_kernel_slots(T, d_out, K, antithetic) / PEAK_SLOTS_PER_S
+    return fused_kernel_slots(T, d_out, K, antithetic, local=local) / PEAK_SLOTS_PER_S
 
 
 def head_slots_per_value(antithetic: bool) -> float:
