@@ -300,7 +300,8 @@ dust_status_t dust_noise_fill(uint64_t seed, int64_t n0, int64_t n_cnt,
  * else the jitter-loss kernel; the slab kernel of dust_estimate_head), at the
  * kernel's start and end (hipExtLaunchKernelGGL's events).
  * n_pairs = 0 turns the hook off.  The pointer arrays are copied; the events
- * must outlive their use.  Process-wide state: not thread-safe.
+ * must outlive their use.  The hook belongs to the calling thread: it times
+ * the estimate calls that thread makes.
  */
 dust_status_t dust_set_timing_events(void* const* start, void* const* stop,
                                      int32_t n_pairs);

@@ -35,6 +35,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <vector>
+
 #include "dust.h"
 #include "dust_internal.hpp"
 #include "dust_gemm.hpp"
@@ -1213,15 +1215,12 @@ __global__ __launch_bounds__(256) void gather_delta_kernel(const void* __restric
   }
 }
 
-// Bench hook state: event pairs stamped by the dispatch of the noise kernel
-// of the next dust_estimate calls (hipExtLaunchKernelGGL's start and stop
-// events, so they time the kernel itself, not the gap before it), pair i on
-// call i (cycling).  Process-wide, not synchronized: set it from one thread
-// while no estimate is being enqueued.
-hipEvent_t* g_ev_start = nullptr;
-hipEvent_t* g_ev_stop = nullptr;
-int32_t g_ev_count = 0;
-int64_t g_ev_next = 0;
+// Bench hook state, per calling thread: event pairs stamped by the dispatch
+// of the noise kernel of this thread's next estimate calls
+// (hipExtLaunchKernelGGL's start and stop events, so they time the kernel
+// itself, not the gap before it), pair i on call i (cycling).
+thread_local std::vector<hipEvent_t> g_ev_start, g_ev_stop;
+thread_local int64_t g_ev_next = 0;
 
 struct TimedLaunch {
   hipEvent_t start = nullptr, stop = nullptr;
@@ -1230,8 +1229,8 @@ struct TimedLaunch {
 // the cursor moved on to the next pair.
 inline TimedLaunch take_timing_events() {
   TimedLaunch t;
-  if (g_ev_count <= 0) return t;
-  const int64_t i = g_ev_next++ % g_ev_count;
+  if (g_ev_start.empty()) return t;
+  const size_t i = (size_t)(g_ev_next++ % (int64_t)g_ev_start.size());
   t.start = g_ev_start[i];
   t.stop = g_ev_stop[i];
   return t;
@@ -1732,24 +1731,13 @@ dust_status_t dust_set_timing_events(void* const* start, void* const* stop, int3
   using namespace dust;
   if (n_pairs < 0 || (n_pairs > 0 && (!start || !stop)))
     return fail(DUST_ERR_INVALID_ARG, "set_timing_events: need two arrays of n_pairs events");
-  static hipEvent_t* owned_start = nullptr;
-  static hipEvent_t* owned_stop = nullptr;
-  delete[] owned_start;
-  delete[] owned_stop;
-  owned_start = owned_stop = nullptr;
-  g_ev_count = 0;
+  g_ev_start.clear();
+  g_ev_stop.clear();
   g_ev_next = 0;
-  if (n_pairs > 0) {
-    owned_start = new hipEvent_t[n_pairs];
-    owned_stop = new hipEvent_t[n_pairs];
-    for (int32_t i = 0; i < n_pairs; ++i) {
-      owned_start[i] = (hipEvent_t)start[i];
-      owned_stop[i] = (hipEvent_t)stop[i];
-    }
+  for (int32_t i = 0; i < n_pairs; ++i) {
+    g_ev_start.push_back((hipEvent_t)start[i]);
+    g_ev_stop.push_back((hipEvent_t)stop[i]);
   }
-  g_ev_start = owned_start;
-  g_ev_stop = owned_stop;
-  g_ev_count = n_pairs;
   return ok();
 }
 
