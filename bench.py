@@ -118,7 +118,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="bf16_layer")
+    ap.add_argument("--workload", default="bf16_layer",
+                    help="one of the synthetic workloads of synth.py")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for the CPU baseline (0 to skip)")
     args = ap.parse_args()
@@ -126,10 +127,15 @@ def main():
         sys.exit(f"bench.py: this estimator is measured on one GPU; --gpus {args.gpus} is not "
                  "supported (sharding over sequences is a design note, not built)")
 
+    from token_activation_perturbation_amd import synth
+    if args.workload not in synth.WORKLOADS:
+        sys.exit(f"bench.py: unknown workload {args.workload!r}; one of "
+                 f"{', '.join(synth.WORKLOAD_ORDER)}")
+
     import torch
 
     import token_activation_perturbation_amd as dust
-    from token_activation_perturbation_amd import roofline, synth
+    from token_activation_perturbation_amd import roofline
 
     w = synth.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
