@@ -1,10 +1,12 @@
 """The ALU cost model the bench line's roofline fraction uses, against the
-counts it states: Philox4x32-10 is 10 rounds of 2 quarter-rate 32x32->64
-multiplies and 4 xors per quad, of which the first round's draw-independent
-half (the quad index's product and the xor with the zero word and the key)
-is shared by all draws (113 slots per quad); Box-Muller 8 quarter-rate
-transcendentals and 18 simple ops per quad (50 slots); the consumers one
-slot each."""
+counts it states.  Issue classes (measured rate classes on gfx950):
+single-pass 1 slot, integer products and integer-to-float conversion 2,
+transcendentals 4.  Philox4x32-10 per quad and draw: the second round's two
+xors, the third round's two products, three-input xor and xor, then seven
+rounds of two products and two three-input xors (50 slots); Box-Muller per
+pair 2 shifts, 2 conversions, the u and v scalings, 4 transcendentals, the
+-2 ln 2 multiply and two multiplies by the radius (27 slots, 54 per quad);
+the consumers one slot each."""
 import pytest
 
 from token_activation_perturbation_amd import roofline
@@ -16,16 +18,16 @@ def test_peak_is_the_fp32_vector_rate():
 
 
 def test_generation_slots_per_value():
-    assert roofline.PHILOX_SLOTS_PER_QUAD == 9 * 12 + 5
-    assert roofline.BOX_MULLER_SLOTS_PER_QUAD == 50
-    assert roofline.GEN_SLOTS_PER_VALUE == 40.75
+    assert roofline.PHILOX_SLOTS_PER_QUAD == 2 + (4 + 2) + 7 * (4 + 2)
+    assert roofline.BOX_MULLER_SLOTS_PER_QUAD == 2 * (2 + 4 + 2 + 16 + 3)
+    assert roofline.GEN_SLOTS_PER_VALUE == 26.0
 
 
 @pytest.mark.parametrize("anti,outputs,per_value", [
-    (True, False, 42.75),   # P and g; the pair cancels the curvature: no Q
-    (True, True, 43.75),    # rho or the credit asked for: Q too
-    (False, False, 44.75),  # plain draws: Q in the weight, the noise sum for centring
-    (False, True, 44.75),
+    (True, False, 28.0),   # P and g; the pair cancels the curvature: no Q
+    (True, True, 29.0),    # rho or the credit asked for: Q too
+    (False, False, 30.0),  # plain draws: Q in the weight, the noise sum for centring
+    (False, True, 30.0),
 ])
 def test_fused_kernel_slots(anti, outputs, per_value):
     T, d_out, K = 8, 12, 6
@@ -37,15 +39,21 @@ def test_fused_kernel_slots(anti, outputs, per_value):
 def test_local_scoring_has_no_curvature_term():
     # P and g (antithetic) or P, g and the noise sum (plain): never Q
     assert roofline.fused_kernel_slots(2, 4, 4, True, per_draw_outputs=True, local=True) == \
-        pytest.approx(2 * 2 * 4 * 42.75)
+        pytest.approx(2 * 2 * 4 * 28.0)
     assert roofline.fused_kernel_slots(2, 4, 4, False, local=True) == \
-        pytest.approx(4 * 2 * 4 * 43.75)
+        pytest.approx(4 * 2 * 4 * 29.0)
     assert roofline.jitter_kernel_slots(2, 4, 4, True, local=True) == \
-        pytest.approx(2 * 2 * 4 * 41.75)
+        pytest.approx(2 * 2 * 4 * 27.0)
 
 
 def test_two_pass_and_head_slots():
-    assert roofline.jitter_kernel_slots(2, 4, 4, True) == pytest.approx(2 * 2 * 4 * 42.75)
-    assert roofline.head_slots_per_value(True) == 55.75
-    assert roofline.head_slots_per_value(False) == 52.75
-    assert roofline.head_kernel_slots(1, 256, 4, True) == pytest.approx(2 * 256 * 55.75)
+    assert roofline.jitter_kernel_slots(2, 4, 4, True) == pytest.approx(2 * 2 * 4 * 28.0)
+    assert roofline.head_slots_per_value(True) == 41.0
+    assert roofline.head_slots_per_value(False) == 38.0
+    assert roofline.head_kernel_slots(1, 256, 4, True) == pytest.approx(2 * 256 * 41.0)
+
+
+def test_minimum_time_is_one_generation_at_peak():
+    T, d_out, K = 4096, 512, 64
+    assert roofline.estimate_min_seconds(T, d_out, K, True) == pytest.approx(
+        32 * T * d_out * 28.0 / roofline.PEAK_SLOTS_PER_S)

@@ -1,4 +1,5 @@
-"""Builds libdust.so (HIP, gfx950) in-tree with hipcc."""
+"""Builds libdust.so (HIP, gfx950) in-tree with hipcc, and the valu_rates
+measurement program (the issue rates the ALU cost model is weighted by)."""
 from __future__ import annotations
 
 import os
@@ -9,12 +10,15 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libdust.so")
 SOURCES = [os.path.join(CSRC, "dust_kernels.hip"), os.path.join(CSRC, "dust_host.cpp")]
-HIPCC_FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+RATES_SRC = os.path.join(CSRC, "valu_rates.hip")
+RATES_BIN = os.path.join(PKG, "valu_rates")
+COMMON_FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17",
     # keep the compiler from emitting packed fp32 ops
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]
+HIPCC_FLAGS = COMMON_FLAGS + ["-fPIC", "-shared"]
 
 
 def build_library(verbose: bool = False) -> str:
@@ -30,5 +34,19 @@ def build_library(verbose: bool = False) -> str:
     return LIB
 
 
+def build_rates(verbose: bool = False) -> str:
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    tmp = f"{RATES_BIN}.{os.getpid()}.tmp"
+    cmd = [hipcc, *COMMON_FLAGS, "-o", tmp, RATES_SRC]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + res.stdout + res.stderr)
+    if verbose:
+        print(" ".join(cmd))
+    os.replace(tmp, RATES_BIN)
+    return RATES_BIN
+
+
 if __name__ == "__main__":
     print(build_library(verbose=True))
+    print(build_rates(verbose=True))

@@ -41,6 +41,13 @@ __device__ __forceinline__ void mul_wide(uint32_t m, uint32_t x, uint32_t& hi, u
   lo = (uint32_t)prod;
 }
 
+// a ^ b ^ c as one VALU instruction: gfx950's three-input bitwise operation
+// with truth table 0x96 (odd parity).  The compiler does not form it from a
+// chain of XORs.
+__device__ __forceinline__ uint32_t xor3(uint32_t a, uint32_t b, uint32_t c) {
+  return __builtin_amdgcn_bitop3_b32(a, b, c, 0x96);
+}
+
 __device__ __forceinline__ uint4 philox4x32_10(uint32_t x0, uint32_t x1, uint32_t x2,
                                                uint32_t x3, NoiseKey key) {
   uint32_t k0 = key.k0, k1 = key.k1;
@@ -49,8 +56,13 @@ __device__ __forceinline__ uint4 philox4x32_10(uint32_t x0, uint32_t x1, uint32_
     uint32_t hi0, lo0, hi1, lo1;
     mul_wide(kPhiloxM0, x0, hi0, lo0);
     mul_wide(kPhiloxM1, x2, hi1, lo1);
-    const uint32_t y0 = hi1 ^ x1 ^ k0;
-    const uint32_t y2 = hi0 ^ x3 ^ k1;
+    // With the counter (quad, token, noise index, 0) only the quad differs
+    // per lane, so early rounds XOR a per-lane word with two wave-uniform
+    // ones: plain XORs let the compiler fold those two on the scalar unit
+    // (the first two rounds of y0, the first three of y2).  Later, two of
+    // the three operands differ per lane.
+    const uint32_t y0 = round < 2 ? hi1 ^ x1 ^ k0 : xor3(hi1, x1, k0);
+    const uint32_t y2 = round < 3 ? hi0 ^ x3 ^ k1 : xor3(hi0, x3, k1);
     x0 = y0;
     x1 = lo1;
     x2 = y2;

@@ -5,35 +5,56 @@ of (seed, noise index, token, channel), generated in registers and consumed
 at once.  Their bound is the vector ALU issue rate, counted in lane-slots:
 
 * Peak.  MI355X: 256 compute units at 2.4 GHz; its fp32 vector peak of
-  157.3 TFLOP/s is 2 flops x 128 lanes per clock per CU, so a full-rate
+  157.3 TFLOP/s is 2 flops x 128 lanes per clock per CU, so a single-pass
   32-bit VALU operation occupies one of 256 x 128 x 2.4e9 = 7.864e13
-  lane-slots per second.  Quarter-rate operations (32x32->64 integer
-  multiply, and the transcendentals log2, sqrt, sin, cos) occupy 4 slots.
+  lane-slots per second.
+
+* Issue cost of each instruction, by the rate class measured on an MI355X
+  with the `valu_rates` program built beside this module (each instruction
+  alone, operands in vector registers, lanes per CU per clock at the clock
+  measured during the run): single-pass operations (xor, shifts, fp32
+  add / mul / fma, the three-input bitwise op) 1 slot (107-118 lanes per
+  clock for the two-operand forms; the three-operand forms alone reach ~80,
+  a register-read limit that a mixed stream does not hit, so they count 1);
+  32x32->64 integer multiply-add, 32-bit high/low products and the
+  integer-to-float conversion 2 slots (~61 lanes per clock); the
+  transcendentals log2, sqrt, sin, cos 4 slots (~30.5).  Under-weighting a
+  class only lowers the fraction, so the model stays a lower bound on time.
 
 * Work per distinct noise value (the minimum the method needs: each of the
   K_n * T * d_out values generated once, where K_n = K/2 with antithetic
-  pairs, else K).  Per quad of four values:
-    Philox4x32-10   9 rounds x (2 multiplies x 4 + 4 xor)
-                    + first round 1 multiply x 4 + 1 xor         = 113 slots
-    Box-Muller      8 transcendentals x 4 + 18 simple ops        =  50 slots
-  The counter is (quad, token, noise index, 0), so the first round's product
-  of the quad index and its xor with the zero word and the key are the same
-  for every noise index of a (token, quad): only the product of the noise
-  index and one xor depend on the draw.  That gives 40.75 slots per value,
-  plus the consumers: 1 FMA for P = <delta, a>,
-  1 FMA for Q = ||a||^2 (the quadratic loss's curvature term: needed by
-  plain draws and by the per-draw outputs; with antithetic pairs it cancels
-  inside each pair, so a call that asks only for g and G_W does without it,
-  and local scoring, linear in the jitter, never needs it), 1 FMA for the
-  reweighted sum g, and 1 add for the plain-draw noise sum used by the
-  centring.
+  pairs, else K).  The counter is (quad, token, noise index, 0): only the
+  quad index differs per lane, and the first round's products are either
+  wave-uniform (the noise index's, on the scalar unit) or the same for
+  every noise index of a (token, quad) (the quad index's, computed once per
+  lane), as is the second round's product of the first round's per-lane
+  word.  Per quad of four values and draw:
+    Philox4x32-10   second round: 2 xors                          =  2 slots
+                    third round: 2 products x 2 + 1 three-input xor
+                    + 1 xor (its other two words are wave-uniform) =  6
+                    rounds 4-10: 7 x (2 products x 2 + 2 three-input
+                    xors)                                          = 42
+                                                                   = 50 slots
+    Box-Muller      per pair: 2 shifts, 2 conversions x 2, 1 FMA for u,
+                    1 multiply for v, log2, sqrt, sin, cos x 4, 1 multiply
+                    by -2 ln 2, 2 multiplies by the radius = 27;  = 54 slots
+  That gives 26 slots per value, plus the consumers: 1 FMA for
+  P = <delta, a>, 1 FMA for Q = ||a||^2 (the quadratic loss's curvature
+  term: needed by plain draws and by the per-draw outputs; with antithetic
+  pairs it cancels inside each pair, so a call that asks only for g and G_W
+  does without it, and local scoring, linear in the jitter, never needs
+  it), 1 FMA for the reweighted sum g, and 1 add for the plain-draw noise
+  sum used by the centring.
 
 The cross-entropy head's slab kernel consumes each value as: 1 multiply
 (sigma a), the jitter's expm1 (antithetic: both signs from the even and odd
 Taylor parts, 9 + 2 slots; plain draws: 8 slots of Horner), the slab's
 partial sums (one FMA per sign), 1 FMA for g and, for plain draws, 1 add for
-the noise sum: 55.75 slots per value with antithetic pairs, 52.75 without.
+the noise sum: 41 slots per value with antithetic pairs, 38 without.
 
+The generation alone (noise_quad in a loop, the `valu_rates` program's last
+row) runs at ~0.84 of this model's peak with the clock at 2.4 GHz: the
+practical ceiling the noise kernels are measured against in the text.
 Counted this way a two-pass pipeline (generate for the loss change, then
 regenerate for g) is capped at about half of the roofline; a single
 generation can reach all of it.
@@ -45,9 +66,19 @@ CLOCK_HZ = 2.4e9
 LANES_PER_CU_CLOCK = 128
 PEAK_SLOTS_PER_S = CUS * LANES_PER_CU_CLOCK * CLOCK_HZ  # 7.864e13
 
-PHILOX_SLOTS_PER_QUAD = 9 * (2 * 4 + 4) + (4 + 1)  # 113
-BOX_MULLER_SLOTS_PER_QUAD = 8 * 4 + 18             # 50
-GEN_SLOTS_PER_VALUE = (PHILOX_SLOTS_PER_QUAD + BOX_MULLER_SLOTS_PER_QUAD) / 4.0  # 40.75
+# issue cost classes, in lane-slots per lane: single-pass, half-rate
+# (integer products, integer-to-float conversion), quarter-rate
+# (transcendentals)
+SINGLE, HALF, QUARTER = 1, 2, 4
+
+PHILOX_SLOTS_PER_QUAD = (2 * SINGLE                         # second round
+                         + 2 * HALF + 2 * SINGLE            # third round
+                         + 7 * (2 * HALF + 2 * SINGLE))     # rounds 4-10: 50
+BOX_MULLER_SLOTS_PER_QUAD = 2 * (2 * SINGLE + 2 * HALF      # shifts, conversions
+                                 + 2 * SINGLE               # u, v scaling
+                                 + 4 * QUARTER              # log2, sqrt, sin, cos
+                                 + 3 * SINGLE)              # -2 ln 2, radius x 2: 54
+GEN_SLOTS_PER_VALUE = (PHILOX_SLOTS_PER_QUAD + BOX_MULLER_SLOTS_PER_QUAD) / 4.0  # 26
 
 
 def distinct_noise_values(T: int, d_out: int, K: int, antithetic: bool) -> int:
