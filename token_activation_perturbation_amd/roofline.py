@@ -13,7 +13,7 @@ at once.  Their bound is the vector ALU issue rate, counted in lane-slots:
   with the `valu_rates` program built beside this module (each instruction
   alone, operands in vector registers, lanes per CU per clock at the clock
   measured during the run): single-pass operations (xor, shifts, fp32
-  add / mul / fma, the three-input bitwise op) 1 slot (107-118 lanes per
+  add / mul / fma, the three-input bitwise op) 1 slot (107-122 lanes per
   clock for the two-operand forms; the three-operand forms alone reach ~80,
   a register-read limit that a mixed stream does not hit, so they count 1);
   32x32->64 integer multiply-add, 32-bit high/low products and the
