@@ -156,9 +156,14 @@ def main():
     else:
         X, W, tg = to_dev("X"), to_dev("W"), to_dev("target")
     dt_code = dust.DUST_F32 if w.dtype == "f32" else dust.DUST_BF16
+    # the estimator's workspace sized for single generation where it applies
+    # (gamma > 0 with antithetic pairs and enough sequence-pair chains)
+    base_bytes = dust.dust_workspace_bytes(w.T, w.d_in, w.d_out, w.K, w.antithetic, dt_code)
     ws_bytes = (dust.dust_embedding_workspace_bytes(w.T, w.V, w.d_out, w.K, w.antithetic, dt_code)
-                if w.embedding else
-                dust.dust_workspace_bytes(w.T, w.d_in, w.d_out, w.K, w.antithetic, dt_code))
+                if w.embedding else base_bytes if w.head else
+                dust.dust_workspace_bytes_seq(w.T, w.d_in, w.d_out, w.seq_len, w.K, w.gamma,
+                                              w.antithetic, dt_code))
+    chain = not w.embedding and not w.head and ws_bytes > base_bytes
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     kw = dict(K=w.K, sigma=w.sigma, gamma=w.gamma, seed=w.noise_seed, antithetic=w.antithetic,
               seq_len=w.seq_len)
@@ -218,8 +223,9 @@ def main():
         kernel = "head_ce_kernel"
         slots = roofline.head_kernel_slots(w.T, w.d_out, w.K, w.antithetic)
         min_s = roofline.head_min_seconds(w.T, w.d_out, w.K, w.antithetic)
-    elif fused:
-        kernel = "fused_g0_kernel"
+    elif fused or chain:
+        # both generate each noise value once and add P's and g's FMAs
+        kernel = "fused_g0_kernel" if fused else "chain_g_kernel"
         slots = roofline.fused_kernel_slots(w.T, w.d_out, w.K, w.antithetic, local=w.local)
     else:
         kernel = "jitter_loss_kernel"

@@ -54,6 +54,28 @@ size_t dust_workspace_bytes(int64_t T, int64_t d_in, int64_t d_out, int32_t K,
                             int32_t antithetic, int32_t dtype);
 
 /*
+ * Bytes of device workspace that let dust_estimate and dust_estimate_local
+ * generate each noise value once for gamma > 0 ("Dust: every token is a
+ * member of the population", section "Perturb the activations, not the
+ * weights": the credit r_t = c_t + gamma r_(t+1); for an antithetic pair
+ * centring and curvature cancel, so r+ - r- = -2 sigma R_t with
+ * R_t = P_t + gamma R_(t+1), P_t = <delta_t, a_t>, and one walk over each
+ * sequence in reverse token order forms P, R and g_t = (2/K) sum_p R_t^p a_t^p
+ * from the same noise values).  Larger than dust_workspace_bytes exactly
+ * when that path applies to these sizes: antithetic != 0, gamma > 0,
+ * seq_len >= 2 dividing T, d_out <= 1024, and (T / seq_len) * K / 2 >= 2048
+ * pair chains; it adds ceil(K / 32) partial g arrays of T x d_out fp32.
+ * A call takes that path when its workspace is at least this size and it
+ * asks for neither rho nor reward (which need every draw's centred credit);
+ * otherwise it regenerates the noise in a second pass.  The two paths agree
+ * within fp32 rounding (different summation orders); each is bitwise
+ * reproducible.  0 when the sizes are invalid.  Pure host function.
+ */
+size_t dust_workspace_bytes_seq(int64_t T, int64_t d_in, int64_t d_out,
+                                int64_t seq_len, int32_t K, float gamma,
+                                int32_t antithetic, int32_t dtype);
+
+/*
  * Host-side check of dust_estimate's arguments, the same check dust_estimate
  * runs first.  Touches no device memory and makes no HIP call.  Rejects: a
  * NULL X, W, target or G_W; T, d_in, d_out <= 0; seq_len <= 0 or T not a
@@ -93,7 +115,9 @@ dust_status_t dust_validate(const void* X, const void* W, const void* target,
  *   g          [T, d_out]     per-token error estimate g_t; optional
  *   (optional outputs may be NULL)
  * Workspace: device memory of at least dust_workspace_bytes(...) bytes,
- * owned by the caller, contents undefined on return.
+ * owned by the caller, contents undefined on return; with
+ * dust_workspace_bytes_seq(...) bytes a gamma > 0 call with antithetic pairs
+ * generates each noise value once (see there).
  */
 dust_status_t dust_estimate(const void* X, const void* W, const void* target,
                             int64_t T, int64_t d_in, int64_t d_out,

@@ -1,0 +1,156 @@
+"""Single generation for gamma > 0 with antithetic pairs (the chain path).
+
+With a workspace of dust_workspace_bytes_seq bytes and no per-draw output
+asked for, dust_estimate and dust_estimate_local walk each sequence in
+reverse token order, one pair per wave, and generate every noise value
+once: for a pair, centring and curvature cancel and
+g_t = (2/K) sum_p R_t^p a_t^p with R_t = P_t + gamma R_(t+1) ("Dust: every
+token is a member of the population", section "Perturb the activations,
+not the weights": the credit recursion).  Checked: parity with the fp64
+oracle at the estimate's bars (2e-3 for bf16 inputs, 1e-5 for the fp32
+path) on G_W, g and the clean loss; agreement with the two-pass path of the
+same call (given only dust_workspace_bytes), which adds the draws in another
+order, so the two differ by rounding only and are not bitwise equal (which
+also shows that the chain path ran); bitwise reproducibility; the full
+large-population workload in the benchmarked configuration.
+"""
+import numpy as np
+import pytest
+
+from token_activation_perturbation_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "bf16": 2e-3}
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import token_activation_perturbation_amd as dust
+    dust._load()
+    return torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module")
+def threads(oracle_mod):
+    return min(16, oracle_mod.default_threads())
+
+
+def rel(a, b):
+    nb = np.linalg.norm(b)
+    return np.linalg.norm(a - b) / (nb if nb > 0 else 1.0)
+
+
+def dtype_code(dtype):
+    import token_activation_perturbation_amd as dust
+    return dust.DUST_F32 if dtype == "f32" else dust.DUST_BF16
+
+
+def run(inp, dtype, dev, two_pass=False, local=False, **kw):
+    """dust_estimate (or _local with E) with the chain path's workspace, or
+    with exactly the two-pass workspace."""
+    import torch
+    import token_activation_perturbation_amd as dust
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    X = torch.from_numpy(inp["X"]).to(dev).to(tdt).contiguous()
+    T, d_in = inp["X"].shape
+    d_out = inp["E" if local else "W"].shape[1 if local else 0]
+    ws = None
+    if two_pass:
+        nbytes = dust.dust_workspace_bytes(T, d_in, d_out, kw["K"], kw["antithetic"],
+                                           dtype_code(dtype))
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    if local:
+        E = torch.from_numpy(inp["E"]).to(dev).contiguous()
+        out = dust.dust_estimate_local(X, E, want_g=True, workspace=ws, **kw)
+    else:
+        W = torch.from_numpy(inp["W"]).to(dev).to(tdt).contiguous()
+        tg = torch.from_numpy(inp["target"]).to(dev).to(tdt).contiguous()
+        out = dust.dust_estimate(X, W, tg, want_loss=True, want_g=True, workspace=ws, **kw)
+    torch.cuda.synchronize(dev)
+    return {k: v.cpu().numpy().astype(np.float64) for k, v in out.items()}
+
+
+CASES = [
+    # T, seq_len, d_in, d_out, K, sigma, gamma, dtype
+    (16, 8, 32, 64, 4096, 1e-2, 0.5, "bf16"),    # 2 sequences x 2048 pairs
+    (12, 6, 24, 70, 4096, 1e-2, 0.9, "bf16"),    # ragged width: quads past d_out
+    (16, 4, 16, 32, 1024, 1e-2, 1.0, "f32"),     # 4 x 512 pairs, gamma = 1
+    (8, 2, 20, 1024, 4096, 5e-3, 0.3, "bf16"),   # the widest layer the path takes
+    (16, 8, 32, 64, 4100, 1e-2, 0.7, "bf16"),    # 2050 pairs: a partial last group
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"T{c[0]}_L{c[1]}_dout{c[3]}_K{c[4]}_g{c[6]}_{c[7]}"
+                                             for c in CASES])
+def test_chain_parity_with_oracle_and_two_pass(dev, oracle_mod, threads, case):
+    import token_activation_perturbation_amd as dust
+    T, seq_len, d_in, d_out, K, sigma, gamma, dtype = case
+    print(f"chain parity {case}", flush=True)
+    code = dtype_code(dtype)
+    assert dust.dust_workspace_bytes_seq(T, d_in, d_out, seq_len, K, gamma, True, code) > \
+        dust.dust_workspace_bytes(T, d_in, d_out, K, True, code)
+    inp = synth.random_inputs(T, d_in, d_out, dtype, seed=T * 13 + d_out + K)
+    kw = dict(K=K, sigma=sigma, gamma=gamma, seed=K + 3, antithetic=True, seq_len=seq_len)
+    chain = run(inp, dtype, dev, **kw)
+    two = run(inp, dtype, dev, two_pass=True, **kw)
+    ref = oracle_mod.estimate(inp["X"], inp["W"], inp["target"], threads=threads, **kw)
+    errs = {"G_W": rel(chain["G_W"], ref["G"]), "g": rel(chain["g"], ref["g"]),
+            "loss": rel(chain["loss"], ref["loss"]), "vs_two_pass": rel(chain["G_W"], two["G_W"])}
+    print("  rel err " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
+    for k, v in errs.items():
+        assert v <= TOL[dtype], (k, v)
+    assert rel(two["G_W"], ref["G"]) <= TOL[dtype]
+    assert not np.array_equal(chain["g"], two["g"])
+
+
+def test_chain_local_scoring(dev, oracle_mod, threads):
+    """dust_estimate_local: keys/values-style scoring with gamma = 0.98."""
+    T, seq_len, d_in, d_out, K = 16, 8, 32, 64, 4096
+    rng = np.random.default_rng(41)
+    inp = synth.random_inputs(T, d_in, d_out, "bf16", seed=41)
+    inp["E"] = rng.standard_normal((T, d_out)).astype(np.float32)
+    kw = dict(K=K, sigma=0.2, gamma=0.98, seed=9, antithetic=True, seq_len=seq_len)
+    chain = run(inp, "bf16", dev, local=True, **kw)
+    two = run(inp, "bf16", dev, local=True, two_pass=True, **kw)
+    ref = oracle_mod.estimate_local(inp["X"], inp["E"], threads=threads, **kw)
+    errs = {"G_W": rel(chain["G_W"], ref["G"]), "g": rel(chain["g"], ref["g"]),
+            "vs_two_pass": rel(chain["g"], two["g"])}
+    print("  local rel err " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
+    for k, v in errs.items():
+        assert v <= TOL["bf16"], (k, v)
+    assert not np.array_equal(chain["g"], two["g"])
+
+
+def test_chain_bitwise_deterministic(dev):
+    inp = synth.random_inputs(16, 32, 64, "bf16", seed=5)
+    kw = dict(K=4096, sigma=1e-2, gamma=0.5, seed=1, antithetic=True, seq_len=8)
+    a = run(inp, "bf16", dev, **kw)
+    b = run(inp, "bf16", dev, **kw)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
+
+
+def test_chain_large_population_full_size(dev, oracle_mod, threads):
+    """The large-population workload (2 sequences x 2048 pairs, d_out 1024)
+    in the benchmarked configuration: the oracle recomputes the last
+    sequence (g, loss); G_W at full size against the fp64 outer product of
+    the GPU's own g."""
+    w = synth.WORKLOADS["large_population_bf16"]
+    print("chain full-size large_population_bf16", flush=True)
+    inp = synth.make_inputs(w)
+    kw = dict(K=w.K, sigma=w.sigma, gamma=w.gamma, seed=w.noise_seed, antithetic=w.antithetic,
+              seq_len=w.seq_len)
+    got = run(inp, w.dtype, dev, **kw)
+    s = w.n_seq - 1
+    ref = oracle_mod.estimate(inp["X"], inp["W"], inp["target"], seq_range=(s, s + 1),
+                              threads=threads, **kw)
+    sl = slice(s * w.seq_len, (s + 1) * w.seq_len)
+    errs = {"g": rel(got["g"][sl], ref["g"]), "loss": rel(got["loss"][sl], ref["loss"]),
+            "G_W_vs_gTX": rel(got["G_W"], got["g"].T @ inp["X"].astype(np.float64))}
+    print("  rel err " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
+    for k, v in errs.items():
+        assert v <= TOL[w.dtype], (k, v)

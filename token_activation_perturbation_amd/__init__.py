@@ -11,7 +11,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["DustError", "dust_workspace_bytes", "dust_validate", "dust_estimate",
+__all__ = ["DustError", "dust_workspace_bytes", "dust_workspace_bytes_seq", "dust_validate", "dust_estimate",
            "dust_validate_local", "dust_estimate_local", "dust_validate_head",
            "dust_estimate_head", "dust_embedding_workspace_bytes",
            "dust_reassemble_workspace_bytes", "dust_validate_embedding", "dust_estimate_embedding",
@@ -49,6 +49,8 @@ def _load():
                              ctypes.c_float, ctypes.c_size_t)
     lib.dust_workspace_bytes.argtypes = [i64, i64, i64, i32, i32, i32]
     lib.dust_workspace_bytes.restype = sz
+    lib.dust_workspace_bytes_seq.argtypes = [i64, i64, i64, i64, i32, f32, i32, i32]
+    lib.dust_workspace_bytes_seq.restype = sz
     lib.dust_validate.argtypes = [vp, vp, vp, i64, i64, i64, i64, i32, i32, f32, f32, i32,
                                   vp, vp, sz]
     lib.dust_validate.restype = ctypes.c_int
@@ -105,6 +107,15 @@ def _check(status: int):
 def dust_workspace_bytes(T: int, d_in: int, d_out: int, K: int, antithetic: bool,
                          dtype: int) -> int:
     return int(_load().dust_workspace_bytes(T, d_in, d_out, K, int(bool(antithetic)), dtype))
+
+
+def dust_workspace_bytes_seq(T: int, d_in: int, d_out: int, seq_len: int, K: int, gamma: float,
+                             antithetic: bool, dtype: int) -> int:
+    """Workspace bytes with which a gamma > 0 call with antithetic pairs
+    generates each noise value once (equal to dust_workspace_bytes where
+    that path does not apply to these sizes)."""
+    return int(_load().dust_workspace_bytes_seq(T, d_in, d_out, seq_len, K, gamma,
+                                                int(bool(antithetic)), dtype))
 
 
 def dust_validate(X_ptr, W_ptr, target_ptr, T, d_in, d_out, seq_len, dtype, K, sigma, gamma,
@@ -221,8 +232,10 @@ def dust_estimate(X, W, target, *, K: int, sigma: float, gamma: float, seed: int
     rho = _get("rho", (T, K)) if want_rho else None
     reward = _get("reward", (T, K)) if want_reward else None
     g = _get("g", (T, d_out)) if want_g else None
-    ws, ws_bytes = _workspace(workspace, dust_workspace_bytes(T, d_in, d_out, K, antithetic, dt),
-                              dev)
+    # per-draw outputs need the two-pass path: its workspace suffices then
+    need = (dust_workspace_bytes(T, d_in, d_out, K, antithetic, dt) if want_rho or want_reward
+            else dust_workspace_bytes_seq(T, d_in, d_out, seq_len, K, gamma, antithetic, dt))
+    ws, ws_bytes = _workspace(workspace, need, dev)
     ptr = lambda t: None if t is None else t.data_ptr()  # noqa: E731
     status = _load().dust_estimate(
         X.data_ptr(), W.data_ptr(), target.data_ptr(), T, d_in, d_out, seq_len, dt, K,
@@ -263,8 +276,9 @@ def dust_estimate_local(X, E, *, K: int, sigma: float, gamma: float, seed: int,
     rho = _get("rho", (T, K)) if want_rho else None
     reward = _get("reward", (T, K)) if want_reward else None
     g = _get("g", (T, d_out)) if want_g else None
-    ws, ws_bytes = _workspace(workspace, dust_workspace_bytes(T, d_in, d_out, K, antithetic, dt),
-                              dev)
+    need = (dust_workspace_bytes(T, d_in, d_out, K, antithetic, dt) if want_rho or want_reward
+            else dust_workspace_bytes_seq(T, d_in, d_out, seq_len, K, gamma, antithetic, dt))
+    ws, ws_bytes = _workspace(workspace, need, dev)
     ptr = lambda t: None if t is None else t.data_ptr()  # noqa: E731
     status = _load().dust_estimate_local(
         ptr(X), E.data_ptr(), T, d_in, d_out, seq_len, dt, K, sigma, gamma,

@@ -40,6 +40,15 @@ size_t dust_workspace_bytes(int64_t T, int64_t d_in, int64_t d_out, int32_t K,
   return p.total;
 }
 
+size_t dust_workspace_bytes_seq(int64_t T, int64_t d_in, int64_t d_out, int64_t seq_len,
+                                int32_t K, float gamma, int32_t antithetic, int32_t dtype) {
+  if (dtype != DUST_F32 && dtype != DUST_BF16) return 0;
+  dust::Plan p;
+  if (!dust::make_plan(T, d_in, d_out, K, antithetic, dtype, &p)) return 0;
+  const dust::ChainPlan c = dust::make_chain_plan(p, seq_len, gamma);
+  return c.ok ? c.total : p.total;
+}
+
 }  // extern "C"
 
 namespace {

@@ -931,6 +931,128 @@ __global__ __launch_bounds__(256) void fused_g0_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Single generation for gamma > 0 with antithetic pairs.  Within a pair the
+// centring and the curvature cancel: r_t^+ - r_t^- = -2 sigma R_t with
+// R_t = P_t + gamma R_(t+1) inside a sequence and P_t = <delta_t, a_t>, so
+//   g_t = -1/(K sigma) sum_p (r_t^+ - r_t^-) a_t^p = (2/K) sum_p R_t^p a_t^p,
+// and a walk over a sequence in reverse token order generates each noise
+// value once: a_t^p, then P_t^p (a wave reduction), R_t^p, and R_t^p a_t^p.
+// One workgroup of kChainWaves waves per (sequence, group of pairs), one
+// pair per wave (waves past K_n run with weight 0 so every wave reaches the
+// barriers); the waves' R a are added in LDS in wave order and the group's
+// sum is its partial g_t, [group][T][d_out]; chain_sum_kernel adds the
+// groups in group order.  Lane l owns channel quads l + 64 j; channels past
+// d_out have delta 0 (P ignores them) and are never stored.
+
+template <int QPL, bool FULL>
+__global__ __launch_bounds__(1024) void chain_g_kernel(
+    const float* __restrict__ delta, int32_t T, int32_t d_out, int32_t seq_len, int32_t K_n,
+    int32_t groups, float gamma, NoiseKey key, float* __restrict__ loss_clean,
+    float* __restrict__ part) {
+  constexpr int NQ = 64 * QPL;
+  extern __shared__ float4 chain_red[];  // [waves][NQ]
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int waves = blockDim.x >> 6;
+  const int32_t seq = (int32_t)blockIdx.x / groups;
+  const int32_t group = (int32_t)blockIdx.x % groups;
+  const int32_t n = group * waves + wave;
+  const float live = n < K_n ? 1.0f : 0.0f;
+  const int32_t t_first = seq * seq_len;
+  float R = 0.f;
+  for (int32_t tt = seq_len - 1; tt >= 0; --tt) {
+    const int32_t t = t_first + tt;
+    const float* drow = delta + (int64_t)t * d_out;
+    float4 d[QPL], a[QPL];
+    float p = 0.f;
+#pragma unroll
+    for (int j = 0; j < QPL; ++j) {
+      const int c = 4 * (lane + 64 * j);
+      if (FULL) {
+        d[j] = *(const float4*)(drow + c);
+      } else {
+        d[j].x = (c < d_out) ? drow[c] : 0.f;
+        d[j].y = (c + 1 < d_out) ? drow[c + 1] : 0.f;
+        d[j].z = (c + 2 < d_out) ? drow[c + 2] : 0.f;
+        d[j].w = (c + 3 < d_out) ? drow[c + 3] : 0.f;
+      }
+      a[j] = noise_quad((uint32_t)(lane + 64 * j), (uint32_t)t, (uint32_t)n, key);
+      p = __builtin_fmaf(d[j].x, a[j].x, p);
+      p = __builtin_fmaf(d[j].y, a[j].y, p);
+      p = __builtin_fmaf(d[j].z, a[j].z, p);
+      p = __builtin_fmaf(d[j].w, a[j].w, p);
+    }
+    p = wave_sum(p);
+    R = __builtin_fmaf(gamma, R, p);
+    const float w = live * R;
+#pragma unroll
+    for (int j = 0; j < QPL; ++j)
+      chain_red[wave * NQ + 64 * j + lane] =
+          make_float4(w * a[j].x, w * a[j].y, w * a[j].z, w * a[j].w);
+    if (loss_clean && group == 0 && wave == 0) {
+      float s = 0.f;
+#pragma unroll
+      for (int j = 0; j < QPL; ++j) {
+        s = __builtin_fmaf(d[j].x, d[j].x, s);
+        s = __builtin_fmaf(d[j].y, d[j].y, s);
+        s = __builtin_fmaf(d[j].z, d[j].z, s);
+        s = __builtin_fmaf(d[j].w, d[j].w, s);
+      }
+      s = wave_sum(s);
+      if (lane == 0) loss_clean[t] = 0.5f * s;
+    }
+    __syncthreads();
+    // every thread sums whole channels over the waves (channel c is float c
+    // of a wave's row), so all the workgroup's lanes share the reduction
+    const float* red = (const float*)chain_red;
+    float* dst = part + ((int64_t)group * T + t) * d_out;
+    for (int c = (int)threadIdx.x; c < 4 * NQ; c += (int)blockDim.x) {
+      float acc = red[c];
+      for (int w2 = 1; w2 < waves; ++w2) acc += red[w2 * 4 * NQ + c];
+      if (FULL || c < d_out) dst[c] = acc;
+    }
+    __syncthreads();
+  }
+}
+
+// g_t = scale x the sum of the groups' partial g_t in group order, written
+// as fp32 and / or its bf16 split.  One lane per (token, channel quad).
+template <bool FULL>
+__global__ __launch_bounds__(256) void chain_sum_kernel(const float* __restrict__ part, int32_t T,
+                                                        int32_t d_out, int32_t nq, int32_t groups,
+                                                        float scale, float* __restrict__ g32,
+                                                        uint16_t* __restrict__ g_hi,
+                                                        uint16_t* __restrict__ g_lo) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)T * nq) return;
+  const int64_t t = i / nq;
+  const int c = 4 * (int)(i % nq);
+  const int64_t stride = (int64_t)T * d_out;
+  const float* src = part + t * d_out + c;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (FULL) {
+    acc = *(const float4*)src;
+    for (int32_t gr = 1; gr < groups; ++gr) {
+      const float4 o = *(const float4*)(src + gr * stride);
+      acc.x += o.x;
+      acc.y += o.y;
+      acc.z += o.z;
+      acc.w += o.w;
+    }
+  } else {
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int e = 0; e < 4; ++e)
+      if (c + e < d_out) {
+        float sum = src[e];
+        for (int32_t gr = 1; gr < groups; ++gr) sum += src[gr * stride + e];
+        v[e] = sum;
+      }
+    acc = make_float4(v[0], v[1], v[2], v[3]);
+  }
+  acc = make_float4(scale * acc.x, scale * acc.y, scale * acc.z, scale * acc.w);
+  store_g_quad(acc, t * d_out, c, d_out, FULL, g32, g_hi, g_lo);
+}
+
+// ---------------------------------------------------------------------------
 // Cross-entropy head ("What the released code actually does", step 5): the
 // logits z_t = W x_t are jittered one slab of 256 columns at a time, every
 // slab its own site with K draws, and only the cross-entropy is recomputed.
@@ -1338,6 +1460,46 @@ void launch_base_gemm(const void* X, const void* W, const void* target, int64_t 
   }
 }
 
+// The chain path's two kernels (single generation, gamma > 0, antithetic
+// pairs): partial g per pair group, then their sum scaled by 2 / K.
+void launch_chain(const Plan& p, const ChainPlan& cp, int64_t seq_len, float gamma,
+                  NoiseKey key, const float* delta, bool delta_vec, float* loss_clean,
+                  float* part, float* g32, uint16_t* g_hi, uint16_t* g_lo, hipStream_t s,
+                  TimedLaunch tl) {
+  const int qpl = fused_qpl(p.nq);
+  const bool part_vec = ((uintptr_t)part % 16) == 0;
+  const bool full = (p.nq == 64 * qpl) && delta_vec && part_vec;
+  const dim3 grid((unsigned)(cp.n_seq * cp.groups)), block(64 * kChainWaves);
+  const size_t lds = sizeof(float4) * 64 * (size_t)qpl * kChainWaves;
+  const int32_t Ti = (int32_t)p.T, dout = (int32_t)p.d_out, sl = (int32_t)seq_len;
+#define DUST_CHAIN(Q, F)                                                                        \
+  hipExtLaunchKernelGGL((chain_g_kernel<Q, F>), grid, block, lds, s, tl.start, tl.stop, 0, delta, \
+                        Ti, dout, sl, p.K_n, cp.groups, gamma, key, loss_clean, part)
+#define DUST_CHAIN_Q(Q)               \
+  case Q:                             \
+    if (full) DUST_CHAIN(Q, true);    \
+    else DUST_CHAIN(Q, false);        \
+    break;
+  switch (qpl) {
+    DUST_CHAIN_Q(1)
+    DUST_CHAIN_Q(2)
+    DUST_CHAIN_Q(3)
+    DUST_CHAIN_Q(4)
+    default: break;
+  }
+#undef DUST_CHAIN_Q
+#undef DUST_CHAIN
+  const bool sum_full = (p.d_out % 4 == 0) && part_vec;
+  const unsigned blocks = (unsigned)ceil_div(p.T * p.nq, 256);
+  const float scale = 2.0f / (float)p.K;
+  if (sum_full)
+    hipLaunchKernelGGL(chain_sum_kernel<true>, dim3(blocks), dim3(256), 0, s, (const float*)part,
+                       Ti, dout, p.nq, cp.groups, scale, g32, g_hi, g_lo);
+  else
+    hipLaunchKernelGGL(chain_sum_kernel<false>, dim3(blocks), dim3(256), 0, s,
+                       (const float*)part, Ti, dout, p.nq, cp.groups, scale, g32, g_hi, g_lo);
+}
+
 // G_W = sum_t g_t x_t^T: the split partials (or G_W itself with one split),
 // then their fixed-order sum.  bf16: from the split g_hi + g_lo; f32: from g32.
 void launch_outer(const Plan& p, const void* X, const float* g32, const uint16_t* g_hi,
@@ -1475,7 +1637,8 @@ struct Site {
 dust_status_t run_estimate(const Site& st, int64_t T, int64_t d_in, int64_t d_out,
                            int64_t seq_len, int32_t dtype, int32_t K, float sigma, float gamma,
                            uint64_t seed, int32_t antithetic, float* G_W, float* loss_clean,
-                           float* rho, float* reward, float* g, void* workspace, void* stream) {
+                           float* rho, float* reward, float* g, void* workspace,
+                           size_t workspace_bytes, void* stream) {
   const bool local = st.E != nullptr;
   const bool embed = st.ids != nullptr;
   // local scoring without an input matrix: g only, no outer product
@@ -1525,8 +1688,15 @@ dust_status_t run_estimate(const Site& st, int64_t T, int64_t d_in, int64_t d_ou
   // Q = ||a||^2 only where the loss has a curvature term (not local scoring)
   float* const Qused = curv != 0.0f ? Qbuf : nullptr;
   const TimedLaunch tl = take_timing_events();
+  // single generation for gamma > 0 with antithetic pairs, when the caller's
+  // workspace holds the groups' partial g and no per-draw output is asked for
+  const ChainPlan cp = embed ? ChainPlan{} : make_chain_plan(p, seq_len, gamma);
+  const bool chain = !fused && cp.ok && !want_pq && workspace_bytes >= cp.total;
 
-  if (!fused) {
+  if (chain) {
+    launch_chain(p, cp, seq_len, gamma, key, (const float*)delta, delta_vec, loss_clean,
+                 (float*)(ws + cp.off_part), g32, g_hi, g_lo, s, tl);
+  } else if (!fused) {
     // 2. jitter + loss change
     if (Qused)
       hipExtLaunchKernelGGL(jitter_loss_kernel<true>, dim3(grid_for(T * p.jl_chunks, 4)),
@@ -1567,7 +1737,9 @@ dust_status_t run_estimate(const Site& st, int64_t T, int64_t d_in, int64_t d_ou
 
   // 5. g: the fused single-generation kernel (and P, Q when the loss
   //    reductions or the credit are requested), or the reweight kernel
-  if (fused) {
+  //    (the chain path has formed g already)
+  if (chain) {
+  } else if (fused) {
     const bool full = (p.nq == 64 * qpl) && delta_vec;
     launch_fused_g0(qpl, p.antithetic != 0, full, (unsigned)T, (unsigned)(64 * p.fz_waves), s,
                     tl, (const float*)delta, 0, dout, K, p.K_n, p.fz_per_wave, sigma,
@@ -1659,7 +1831,7 @@ dust_status_t dust_estimate(const void* X, const void* W, const void* target, in
   site.target = target;
   return dust::run_estimate(site, T, d_in, d_out, seq_len, dtype, K, sigma,
                             gamma, seed, antithetic, G_W, loss_clean, rho, reward, g, workspace,
-                            stream);
+                            workspace_bytes, stream);
 }
 
 dust_status_t dust_estimate_local(const void* X, const float* E, int64_t T, int64_t d_in,
@@ -1676,7 +1848,7 @@ dust_status_t dust_estimate_local(const void* X, const float* E, int64_t T, int6
   site.E = E;
   return dust::run_estimate(site, T, d_in, d_out, seq_len, dtype, K, sigma,
                             gamma, seed, antithetic, G_W, nullptr, rho, reward, g, workspace,
-                            stream);
+                            workspace_bytes, stream);
 }
 
 dust_status_t dust_estimate_head(const void* X, const void* W, const int32_t* labels, int64_t T,
@@ -1708,7 +1880,7 @@ dust_status_t dust_estimate_embedding(const void* table, const int32_t* ids, con
   site.V = V;
   site.scale = scale;
   return dust::run_estimate(site, T, 1, d, seq_len, dtype, K, sigma, gamma, seed, antithetic,
-                            G_E, loss_clean, rho, reward, g, workspace, stream);
+                            G_E, loss_clean, rho, reward, g, workspace, workspace_bytes, stream);
 }
 
 dust_status_t dust_reassemble_embedding(const int32_t* ids, const float* g, int64_t T,

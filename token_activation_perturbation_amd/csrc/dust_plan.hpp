@@ -140,6 +140,44 @@ inline bool make_plan(int64_t T, int64_t d_in, int64_t d_out, int32_t K,
 }
 
 // ---------------------------------------------------------------------------
+// Single generation for gamma > 0 with antithetic pairs (the "chain" path):
+// one workgroup of kChainWaves waves per (sequence, group of kChainWaves
+// pairs), one pair per wave, each wave walking its sequence's tokens in
+// reverse order; every group writes a partial g per token, [groups][T][d_out]
+// fp32, placed after the two-pass layout, so the chain path needs a larger
+// workspace (dust_workspace_bytes_seq) and a call given only
+// dust_workspace_bytes takes the two-pass path.  It is planned only where
+// the chains fill the chip (sequences x pairs >= kChainMinChains) and the
+// waves' partial sums fit the 64 KiB of LDS a workgroup is given
+// (kChainWaves x d_out x 4 bytes: d_out <= kChainMaxDout).
+constexpr int32_t kChainWaves = 16;
+constexpr int64_t kChainMinChains = 2048;
+constexpr int64_t kChainMaxDout = 1024;
+
+struct ChainPlan {
+  bool ok = false;
+  int32_t groups = 0;   // pair groups per sequence, ceil(K_n / kChainWaves)
+  int64_t n_seq = 0;    // sequences, T / seq_len
+  size_t off_part = 0;  // partial g [groups][T][d_out] fp32
+  size_t total = 0;     // workspace bytes of the chain path
+};
+
+inline ChainPlan make_chain_plan(const Plan& p, int64_t seq_len, float gamma) {
+  ChainPlan c;
+  if (!p.antithetic || !(gamma > 0.0f) || seq_len < 2 || p.T % seq_len != 0) return c;
+  if (p.d_out > kChainMaxDout) return c;
+  c.n_seq = p.T / seq_len;
+  if (c.n_seq * p.K_n < kChainMinChains) return c;
+  c.groups = (int32_t)ceil_div(p.K_n, kChainWaves);
+  if (c.n_seq * c.groups >= (int64_t(1) << 31)) return c;
+  c.off_part = align256(p.total);
+  c.total = align256(c.off_part + sizeof(float) * size_t(c.groups) * size_t(p.T) *
+                                      size_t(p.d_out));
+  c.ok = true;
+  return c;
+}
+
+// ---------------------------------------------------------------------------
 // Embedding reassembly: G_E[v] = scale sum_{t: ids[t] = v} g[t], by a stable
 // counting sort of the token positions by id (per-chunk histograms, their
 // prefix sums over chunks, a scan of the totals, a placement pass), then a

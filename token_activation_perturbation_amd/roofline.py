@@ -88,9 +88,10 @@ def distinct_noise_values(T: int, d_out: int, K: int, antithetic: bool) -> int:
 
 def fused_kernel_slots(T: int, d_out: int, K: int, antithetic: bool,
                        per_draw_outputs: bool = False, local: bool = False) -> float:
-    """Algorithmic lane-slots of the single-generation kernel (gamma = 0);
-    `per_draw_outputs`: the call asks for rho or the credit; `local`: local
-    scoring (no curvature term)."""
+    """Algorithmic lane-slots of the single-generation kernels (gamma = 0;
+    and the gamma > 0 chain kernel of antithetic pairs, which also adds P's
+    and g's FMAs per value); `per_draw_outputs`: the call asks for rho or
+    the credit; `local`: local scoring (no curvature term)."""
     need_q = not local and (per_draw_outputs or not antithetic)
     per_value = GEN_SLOTS_PER_VALUE + 2.0 + (1.0 if need_q else 0.0) + \
         (0.0 if antithetic else 1.0)
