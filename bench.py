@@ -97,10 +97,12 @@ def cpu_baseline(w, inp, budget_s: float):
     one = time.perf_counter() - t0
     n = max(1, min(n_units, int(budget_s / max(one, 1e-6))))
     # a whole workload that takes well under the budget is repeated, so the
-    # figure is not a sub-second measurement (about 12 s of CPU work)
+    # figure is not a sub-second measurement (the repeats are planned from one
+    # sequence's time, which overstates a whole run's: ~10 s of CPU work for
+    # the default 15 s budget)
     repeats = 1
     if n == n_units:
-        repeats = max(1, min(200, int(min(budget_s, 12.0) / max(one * n, 1e-6))))
+        repeats = max(1, min(400, int(budget_s / max(one * n, 1e-6))))
     t0 = time.perf_counter()
     for _ in range(repeats):
         run(0, n)
