@@ -25,6 +25,13 @@
 //                  -1/(K sigma) (r^(2n) - r^(2n+1)) (antithetic) or
 //                  -1/(K sigma) r^(n)
 //   reweight       g_t = sum_n weight_(t,n) a_t^n, the noise regenerated
+// unless the pairs are antithetic, the chains fill the chip and the caller's
+// workspace holds the partials (dust_workspace_bytes_seq), when one pass
+// walks each sequence backwards:
+//   chain_g        per (sequence, group of 16 pairs), one pair per wave:
+//                  a_t generated once, P_t, R_t = P_t + gamma R_(t+1), and
+//                  the group's partial g_t = sum_p R_t^p a_t^p
+//   chain_sum      g_t = 2/K x the groups' partials, added in group order
 // and last
 //   outer          G_W = sum_t g_t x_t^T on MFMA (bf16 hi/lo split of g),
 //                  split over tokens, partials summed in a fixed order
