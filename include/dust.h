@@ -48,7 +48,15 @@ typedef enum {
 
 /*
  * Bytes of device workspace dust_estimate needs for these sizes (0 when the
- * sizes are invalid).  Pure host function.
+ * sizes are invalid).  Pure host function.  The workspace holds what the
+ * stages of the estimate hand to each other ("Dust: every token is a member
+ * of the population", section "Perturb the activations, not the weights",
+ * the three estimator equations): delta_t = W x_t - target_t, the per-draw
+ * loss reductions and their centred, discounted credit, g_t (for bf16 as
+ * its hi/lo split), and the token-split partial sums of G_W.  The noise is
+ * never part of it: a counter-based generator regenerates it where needed
+ * ("Scaling To Unfathomable Depth", section "MeZO": store the seed, not the
+ * perturbation).
  */
 size_t dust_workspace_bytes(int64_t T, int64_t d_in, int64_t d_out, int32_t K,
                             int32_t antithetic, int32_t dtype);
@@ -77,7 +85,12 @@ size_t dust_workspace_bytes_seq(int64_t T, int64_t d_in, int64_t d_out,
 
 /*
  * Host-side check of dust_estimate's arguments, the same check dust_estimate
- * runs first.  Touches no device memory and makes no HIP call.  Rejects: a
+ * runs first.  Touches no device memory and makes no HIP call.  The rules
+ * follow from the estimator ("Dust: every token is a member of the
+ * population", section "Perturb the activations, not the weights": K draws
+ * per token centred across the draws of one forward, the credit summed
+ * within a sequence with decay gamma; section "What a zeroth-order gradient
+ * is" on antithetic pairs, two evaluations of one noise vector).  Rejects: a
  * NULL X, W, target or G_W; T, d_in, d_out <= 0; seq_len <= 0 or T not a
  * multiple of seq_len; T >= 2^31 or d_out >= 2^31 (the noise counter words
  * are 32-bit); K < 2 (centring over one draw leaves nothing); odd K with
@@ -188,8 +201,8 @@ dust_status_t dust_validate_head(const void* X, const void* W, const int32_t* la
 /*
  * The estimator for a cross-entropy head ("Dust: every token is a member of
  * the population", section "What the released code actually does", step 5:
- * the head is jittered on its logits one 256-column slab of the vocabulary
- * at a time, and only the cross-entropy is recomputed from cached sums).
+ * the head's logits are perturbed in 256-column slabs of the vocabulary,
+ * and for each only the cross-entropy is formed again from cached sums).
  * Logits z_t = W x_t; loss CE_t = logsumexp(z_t) - z_t[labels[t]].  Each
  * slab j (columns 256 j .. 256 j + 255) is its own site with K draws: draw i
  * adds s_i sigma a_t^(n(i))[c] to the slab's columns only (the noise of
@@ -303,8 +316,13 @@ dust_status_t dust_reassemble_embedding(const int32_t* ids, const float* g, int6
                                         void* stream);
 
 /*
- * Test hook: the noise the estimator uses, written out.  For noise indices
- * n0..n0+n_cnt-1 and tokens t0..t0+t_cnt-1:
+ * Test hook: the noise the estimator uses, written out.  The estimator's
+ * noise is a pure function of (seed, noise index, token, channel) from a
+ * counter-based generator, so any value can be produced on its own and none
+ * is stored ("Scaling To Unfathomable Depth", section "MeZO": counter-based
+ * generators such as Philox give the n-th value from the seed and n alone;
+ * the layout and transform are those of dust_estimate's `seed` argument).
+ * For noise indices n0..n0+n_cnt-1 and tokens t0..t0+t_cnt-1:
  *   words [n_cnt, t_cnt, 4*ceil(d_out/4)] uint32  Philox words (optional)
  *   gauss [n_cnt, t_cnt, d_out]           fp32    Gaussians    (optional)
  * Sizes must be positive and n0+n_cnt, t0+t_cnt, d_out below 2^31.
@@ -329,6 +347,29 @@ dust_status_t dust_noise_fill(uint64_t seed, int64_t n0, int64_t n_cnt,
  */
 dust_status_t dust_set_timing_events(void* const* start, void* const* stop,
                                      int32_t n_pairs);
+
+/*
+ * Measurement hook: per-kernel durations and algorithmic work of this
+ * thread's library calls (used by the benchmark to report every stage
+ * against its roofline).  dust_profile_begin creates 2 * max_launches HIP
+ * events owned by the library (1 <= max_launches <= 2^20) and turns the
+ * profile on for the calling thread; from then on each kernel launch of the
+ * thread's library calls, up to max_launches of them, is stamped by its own
+ * event pair at the dispatch's start and end (hipExtLaunchKernelGGL's
+ * events; while the profile is on it takes the place of the
+ * dust_set_timing_events pair).  dust_profile_end turns it off, waits for
+ * the recorded launches, and writes for the first `cap` of them, in launch
+ * order: the stage name (a static string: "base_gemm", "fused_g0_kernel",
+ * "outer_gemm", "split_sum_kernel", ...), the duration in milliseconds, the
+ * method's MFMA flops of the launch (2 x the contraction's multiply-adds;
+ * 0 for kernels without a contraction), and the least HBM bytes the launch
+ * must move (its inputs read once, its outputs written once); *count gets
+ * the number of launches recorded.  It then destroys the events.  A HIP
+ * error returns DUST_ERR_HIP (the profile is released either way).
+ */
+dust_status_t dust_profile_begin(int32_t max_launches);
+dust_status_t dust_profile_end(const char** kernel, float* ms, double* flops, double* bytes,
+                               int32_t cap, int32_t* count);
 
 /* Message for the last non-OK status on this thread ("" if none). */
 const char* dust_last_error(void);

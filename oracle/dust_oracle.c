@@ -42,8 +42,8 @@
  * run unchanged (dust_oracle_estimate_local).
  *
  * A third scoring rule is the model's head: cross-entropy of the logits
- * z_t = W x_t against a label y_t, jittered "one 256-column slab of the
- * vocabulary at a time" ("What the released code actually does", step 5).
+ * z_t = W x_t against a label y_t, its logits perturbed in 256-column
+ * slabs of the vocabulary ("What the released code actually does", step 5).
  * Reading used: every slab j is its own site with K draws; draw i of slab j
  * adds s_i sigma a_t^(n(i))[c] to the logits of the slab's columns c only
  * (the same noise values as the full-width jitter, restricted to the slab),

@@ -1,0 +1,68 @@
+"""Error measures the GPU parity tests share.
+
+The estimate's bar (the tolerance stated for the method's output): G_W
+within relative Frobenius error 2e-3 for bf16 inputs with fp32 accumulation
+and 1e-5 for the fp32 path.  The parity tests hold every stage output (the
+clean loss L_t, the loss reductions rho, the credit r, the error estimate g)
+to the same relative level twice over:
+
+  * whole tensor:  ||got - ref||_F / ||ref||_F <= bar
+  * per row:       max over tokens t of ||got_t - ref_t|| / ||ref_t|| <= bar
+                   (rows of G_W: max over output channels c)
+
+The per-row form is the one that catches a single wrong token, a wrong tail
+quad or a wrong sequence, which the whole-tensor norm dilutes.  A row whose
+reference is exactly zero is compared in absolute terms.
+"""
+import numpy as np
+
+TOL = {"f32": 1e-5, "bf16": 2e-3}
+
+
+def rel(a, b):
+    nb = np.linalg.norm(b)
+    return float(np.linalg.norm(a - b) / (nb if nb > 0 else 1.0))
+
+
+def rows_rel(a, b):
+    """Largest per-row relative error (rows along the first axis) and the
+    row where it occurs."""
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, (a.shape, b.shape)
+    if a.ndim == 1:
+        a, b = a[:, None], b[:, None]
+    a = a.reshape(a.shape[0], -1)
+    b = b.reshape(b.shape[0], -1)
+    num = np.linalg.norm(a - b, axis=1)
+    den = np.linalg.norm(b, axis=1)
+    err = num / np.where(den > 0, den, 1.0)
+    i = int(np.argmax(err)) if err.size else 0
+    return (float(err[i]) if err.size else 0.0), i
+
+
+def stage_errors(got, ref, keys=("loss", "rho", "reward", "g"), g_key="G_W", ref_g_key="G",
+                 token_slice=None):
+    """Whole and per-row errors of the stage outputs present in `got` (the
+    GPU's, fp64 arrays) against the oracle's `ref`; `token_slice` selects the
+    tokens of `got` that `ref` covers."""
+    errs = {}
+    for k in keys:
+        if k not in got or k not in ref:
+            continue
+        a = got[k] if token_slice is None else got[k][token_slice]
+        errs[k] = rel(a, ref[k])
+        errs[k + "_row"], _ = rows_rel(a, ref[k])
+    if g_key in got and ref_g_key in ref:
+        errs[g_key] = rel(got[g_key], ref[ref_g_key])
+        errs[g_key + "_row"], _ = rows_rel(got[g_key], ref[ref_g_key])
+    return errs
+
+
+def report(name, errs):
+    print(name, " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
+
+
+def assert_within(errs, tol):
+    bad = {k: v for k, v in errs.items() if not v <= tol}
+    assert not bad, (bad, tol)

@@ -27,7 +27,22 @@ def test_unknown_workload_is_refused():
     assert "unknown workload" in res.stderr and "bf16_layer" in res.stderr
 
 
-def test_default_workload_is_the_benchmarked_layer():
-    assert "bf16_layer" in synth.WORKLOADS
+def test_default_workload_is_the_largest_reference_configuration():
+    """The headline is the MLP up-projection: the reference configuration
+    with the most noise values and MFMA work per call; the five reference
+    configurations are all measured by default."""
+    assert "mlp_up_bf16" in synth.WORKLOADS
     src = open(os.path.join(ROOT, "bench.py")).read()
-    assert 'default="bf16_layer"' in src or "default='bf16_layer'" in src
+    assert 'HEADLINE = "mlp_up_bf16"' in src
+    ref = ["tiny_f32", "bf16_layer", "mlp_up_bf16", "qkv_credit_bf16", "large_population_bf16"]
+    assert all(r in src for r in ref)
+    big = max(ref, key=lambda n: (synth.WORKLOADS[n].K // (2 if synth.WORKLOADS[n].antithetic
+                                                          else 1)) * synth.WORKLOADS[n].T
+              * synth.WORKLOADS[n].d_out)
+    assert big == "mlp_up_bf16"
+
+
+def test_unknown_config_is_refused():
+    res = run("--configs", "bf16_layer,nope", "--cpu-budget", "0")
+    assert res.returncode != 0
+    assert "unknown workload" in res.stderr

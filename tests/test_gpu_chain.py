@@ -11,17 +11,20 @@ oracle at the estimate's bars (2e-3 for bf16 inputs, 1e-5 for the fp32
 path) on G_W, g and the clean loss; agreement with the two-pass path of the
 same call (given only dust_workspace_bytes), which adds the draws in another
 order, so the two differ by rounding only and are not bitwise equal (which
-also shows that the chain path ran); bitwise reproducibility; the full
-large-population workload in the benchmarked configuration.
+also shows that the chain path ran); every register layout the path has
+(1 to 4 channel quads per lane, whole and ragged widths); the path switch a
+request for per-draw outputs makes; bitwise reproducibility.  The
+large-population workload at full size, in the benchmarked configuration,
+is checked against the oracle over every sequence in test_gpu_parity.py.
+Errors are measured over whole tensors and token by token (parity_util.py).
 """
 import numpy as np
 import pytest
 
+from parity_util import TOL, assert_within, rel, report, stage_errors
 from token_activation_perturbation_amd import synth
 
 pytestmark = pytest.mark.gpu
-
-TOL = {"f32": 1e-5, "bf16": 2e-3}
 
 
 @pytest.fixture(scope="module")
@@ -37,11 +40,6 @@ def dev():
 @pytest.fixture(scope="module")
 def threads(oracle_mod):
     return min(16, oracle_mod.default_threads())
-
-
-def rel(a, b):
-    nb = np.linalg.norm(b)
-    return np.linalg.norm(a - b) / (nb if nb > 0 else 1.0)
 
 
 def dtype_code(dtype):
@@ -81,6 +79,10 @@ CASES = [
     (16, 4, 16, 32, 1024, 1e-2, 1.0, "f32"),     # 4 x 512 pairs, gamma = 1
     (8, 2, 20, 1024, 4096, 5e-3, 0.3, "bf16"),   # the widest layer the path takes
     (16, 8, 32, 64, 4100, 1e-2, 0.7, "bf16"),    # 2050 pairs: a partial last group
+    (8, 4, 24, 300, 2048, 1e-2, 0.6, "bf16"),    # 2 quads per lane, ragged quads
+    (8, 4, 24, 512, 2048, 1e-2, 0.8, "bf16"),    # 2 quads per lane, whole
+    (8, 4, 24, 700, 2048, 1e-2, 0.5, "bf16"),    # 3 quads per lane
+    (8, 4, 24, 1022, 2048, 1e-2, 0.9, "bf16"),   # 4 quads per lane, d_out % 4 != 0
 ]
 
 
@@ -98,13 +100,37 @@ def test_chain_parity_with_oracle_and_two_pass(dev, oracle_mod, threads, case):
     chain = run(inp, dtype, dev, **kw)
     two = run(inp, dtype, dev, two_pass=True, **kw)
     ref = oracle_mod.estimate(inp["X"], inp["W"], inp["target"], threads=threads, **kw)
-    errs = {"G_W": rel(chain["G_W"], ref["G"]), "g": rel(chain["g"], ref["g"]),
-            "loss": rel(chain["loss"], ref["loss"]), "vs_two_pass": rel(chain["G_W"], two["G_W"])}
-    print("  rel err " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
-    for k, v in errs.items():
-        assert v <= TOL[dtype], (k, v)
-    assert rel(two["G_W"], ref["G"]) <= TOL[dtype]
+    errs = stage_errors(chain, ref, keys=("loss", "g"))
+    errs["vs_two_pass"] = rel(chain["G_W"], two["G_W"])
+    report("  rel err", errs)
+    assert_within(errs, TOL[dtype])
+    assert_within(stage_errors(two, ref, keys=("loss", "g")), TOL[dtype])
     assert not np.array_equal(chain["g"], two["g"])
+
+
+def test_asking_for_per_draw_outputs_keeps_G_within_the_bar(dev, oracle_mod, threads):
+    """On a chain-eligible call, asking for rho or the credit switches to the
+    two-pass path (every draw's centred credit is then formed): G_W changes
+    by rounding only, and the per-draw outputs match the oracle token by
+    token."""
+    import torch
+    import token_activation_perturbation_amd as dust
+    T, seq_len, d_in, d_out, K = 8, 4, 40, 256, 2048
+    inp = synth.random_inputs(T, d_in, d_out, "bf16", seed=77)
+    kw = dict(K=K, sigma=1e-2, gamma=0.7, seed=5, antithetic=True, seq_len=seq_len)
+    X, W, tg = (torch.from_numpy(inp[k]).to(dev).to(torch.bfloat16).contiguous()
+                for k in ("X", "W", "target"))
+    bare = dust.dust_estimate(X, W, tg, **kw)["G_W"].cpu().numpy().astype(np.float64)
+    full = dust.dust_estimate(X, W, tg, want_rho=True, want_reward=True, want_g=True, **kw)
+    torch.cuda.synchronize(dev)
+    full = {k: v.cpu().numpy().astype(np.float64) for k, v in full.items()}
+    ref = oracle_mod.estimate(inp["X"], inp["W"], inp["target"], threads=threads, **kw)
+    errs = stage_errors(full, ref, keys=("rho", "reward", "g"))
+    errs["bare_G_W"] = rel(bare, ref["G"])
+    errs["full_vs_bare"] = rel(full["G_W"], bare)
+    report("  path switch", errs)
+    assert_within(errs, TOL["bf16"])
+    assert not np.array_equal(full["G_W"], bare)  # the two paths really differ
 
 
 def test_chain_local_scoring(dev, oracle_mod, threads):
@@ -117,11 +143,10 @@ def test_chain_local_scoring(dev, oracle_mod, threads):
     chain = run(inp, "bf16", dev, local=True, **kw)
     two = run(inp, "bf16", dev, local=True, two_pass=True, **kw)
     ref = oracle_mod.estimate_local(inp["X"], inp["E"], threads=threads, **kw)
-    errs = {"G_W": rel(chain["G_W"], ref["G"]), "g": rel(chain["g"], ref["g"]),
-            "vs_two_pass": rel(chain["g"], two["g"])}
-    print("  local rel err " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
-    for k, v in errs.items():
-        assert v <= TOL["bf16"], (k, v)
+    errs = stage_errors(chain, ref, keys=("g",))
+    errs["vs_two_pass"] = rel(chain["g"], two["g"])
+    report("  local rel err", errs)
+    assert_within(errs, TOL["bf16"])
     assert not np.array_equal(chain["g"], two["g"])
 
 
@@ -132,25 +157,3 @@ def test_chain_bitwise_deterministic(dev):
     b = run(inp, "bf16", dev, **kw)
     for k in a:
         assert np.array_equal(a[k], b[k]), k
-
-
-def test_chain_large_population_full_size(dev, oracle_mod, threads):
-    """The large-population workload (2 sequences x 2048 pairs, d_out 1024)
-    in the benchmarked configuration: the oracle recomputes the last
-    sequence (g, loss); G_W at full size against the fp64 outer product of
-    the GPU's own g."""
-    w = synth.WORKLOADS["large_population_bf16"]
-    print("chain full-size large_population_bf16", flush=True)
-    inp = synth.make_inputs(w)
-    kw = dict(K=w.K, sigma=w.sigma, gamma=w.gamma, seed=w.noise_seed, antithetic=w.antithetic,
-              seq_len=w.seq_len)
-    got = run(inp, w.dtype, dev, **kw)
-    s = w.n_seq - 1
-    ref = oracle_mod.estimate(inp["X"], inp["W"], inp["target"], seq_range=(s, s + 1),
-                              threads=threads, **kw)
-    sl = slice(s * w.seq_len, (s + 1) * w.seq_len)
-    errs = {"g": rel(got["g"][sl], ref["g"]), "loss": rel(got["loss"][sl], ref["loss"]),
-            "G_W_vs_gTX": rel(got["G_W"], got["g"].T @ inp["X"].astype(np.float64))}
-    print("  rel err " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
-    for k, v in errs.items():
-        assert v <= TOL[w.dtype], (k, v)

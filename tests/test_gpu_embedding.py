@@ -14,6 +14,7 @@ G_E within 2e-3 for bf16 inputs and 1e-5 for the fp32 path.
 import numpy as np
 import pytest
 
+from parity_util import assert_within, report, stage_errors
 from token_activation_perturbation_amd import synth
 
 pytestmark = pytest.mark.gpu
@@ -155,12 +156,13 @@ def gpu_embedding(table, ids, target, dtype, dev, **kw):
 
 
 def compare(got, ref, dtype, label, sl=slice(None)):
-    errs = {k: rel(got[k][sl], ref[k]) for k in ("loss", "rho", "reward", "g")}
-    if isinstance(sl, slice) and sl == slice(None):
-        errs["G_E"] = rel(got["G_E"], ref["G"])
-    print(label, " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
-    for k, v in errs.items():
-        assert v <= TOL[dtype], (k, v)
+    """Whole-tensor and per-token errors (rows of G_E too when every token is
+    compared) at the estimate's bar."""
+    whole = isinstance(sl, slice) and sl == slice(None)
+    errs = stage_errors(got, ref, keys=("loss", "rho", "reward", "g"),
+                        g_key="G_E" if whole else "none", token_slice=sl)
+    report(label, errs)
+    assert_within(errs, TOL[dtype])
 
 
 EMBED = [

@@ -12,6 +12,7 @@ for bf16 inputs and 1e-5 for the fp32 path.
 import numpy as np
 import pytest
 
+from parity_util import assert_within, report, stage_errors
 from token_activation_perturbation_amd import synth
 
 pytestmark = pytest.mark.gpu
@@ -62,13 +63,14 @@ def gpu_head(X, W, y, dtype, dev, **kw):
 
 
 def compare(got, ref, dtype, label, sl=slice(None)):
-    errs = {"loss": rel(got["loss"][sl], ref["loss"]), "rho": rel(got["rho"][sl], ref["rho"]),
-            "g": rel(got["g"][sl], ref["g"])}
-    if isinstance(sl, slice) and sl == slice(None):
-        errs["G_W"] = rel(got["G_W"], ref["G"])
-    print(label, " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
-    for k, v in errs.items():
-        assert v <= TOL[dtype], (k, v)
+    """Whole-tensor and per-token errors (rho per token over all its slabs
+    and draws; rows of G_W too when every token is compared) at the
+    estimate's bar."""
+    whole = isinstance(sl, slice) and sl == slice(None)
+    errs = stage_errors(got, ref, keys=("loss", "rho", "g"),
+                        g_key="G_W" if whole else "none", token_slice=sl)
+    report(label, errs)
+    assert_within(errs, TOL[dtype])
 
 
 SMALL = [

@@ -10,6 +10,7 @@ Frobenius error 2e-3 for bf16 inputs and 1e-5 for the fp32 path.
 import numpy as np
 import pytest
 
+from parity_util import assert_within, report, stage_errors
 from token_activation_perturbation_amd import synth
 
 pytestmark = pytest.mark.gpu
@@ -63,13 +64,13 @@ def gpu_local(X, E, dtype, dev, E_offset=0, **kw):
 
 
 def compare(got, ref, dtype, label, sl=slice(None)):
-    errs = {"rho": rel(got["rho"][sl], ref["rho"]), "reward": rel(got["reward"][sl], ref["reward"]),
-            "g": rel(got["g"][sl], ref["g"])}
-    if sl == slice(None):
-        errs["G_W"] = rel(got["G_W"], ref["G"])
-    print(label, " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
-    for k, v in errs.items():
-        assert v <= TOL[dtype], (k, v)
+    """Whole-tensor and per-token errors (rows of G_W too when every token is
+    compared) at the estimate's bar."""
+    whole = isinstance(sl, slice) and sl == slice(None)
+    errs = stage_errors(got, ref, keys=("rho", "reward", "g"),
+                        g_key="G_W" if whole else "none", token_slice=sl)
+    report(label, errs)
+    assert_within(errs, TOL[dtype])
 
 
 SMALL = [
@@ -173,12 +174,13 @@ def test_value_embedding_g_only_then_reassembly(dev, oracle_mod, threads, gamma)
     torch.cuda.synchronize(dev)
     got = {k: v.cpu().numpy().astype(np.float64) for k, v in out.items()}
     ref = oracle_mod.estimate_local(np.zeros((T, 1), np.float32), E, threads=threads, **kw)
-    errs = {k: rel(got[k], ref[k]) for k in ("rho", "reward", "g")}
-    errs["G_V"] = rel(G.cpu().numpy().astype(np.float64),
-                      oracle_mod.reassemble_embedding(ids, ref["g"], V, scale=1.0 / T))
-    print("  rel err", " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
-    for k, v in errs.items():
-        assert v <= TOL["f32"], (k, v)
+    errs = stage_errors(got, ref, keys=("rho", "reward", "g"), g_key="none")
+    errs.update(stage_errors({"G_V": G.cpu().numpy().astype(np.float64)},
+                             {"G": oracle_mod.reassemble_embedding(ids, ref["g"], V,
+                                                                   scale=1.0 / T)},
+                             keys=(), g_key="G_V"))
+    report("  rel err", errs)
+    assert_within(errs, TOL["f32"])
     X, _ = local_inputs(T, 32, d, "bf16", seed=43)
     full = gpu_local(X, E, "bf16", dev, **kw)
     assert np.array_equal(full["g"], got["g"])

@@ -57,3 +57,30 @@ def test_minimum_time_is_one_generation_at_peak():
     T, d_out, K = 4096, 512, 64
     assert roofline.estimate_min_seconds(T, d_out, K, True) == pytest.approx(
         32 * T * d_out * 28.0 / roofline.PEAK_SLOTS_PER_S)
+
+
+def test_stage_roofline_picks_the_bound_of_each_kind():
+    # a contraction: MFMA flops against the operand type's peak
+    s = roofline.stage_roofline("base_gemm", 1.0, 2.5e12, 8.0e9, "bf16")
+    assert s["bound"] == "mfma" and s["frac"] == pytest.approx(1.0)
+    assert s["hbm_frac"] == pytest.approx(1.0)
+    assert s["bound_ms"] == pytest.approx(1.0)
+    s = roofline.stage_roofline("outer_gemm", 2.0, 157.3e9, 0.0, "f32")
+    assert s["bound"] == "mfma" and s["frac"] == pytest.approx(0.5)
+    # a noise stage: the slot model
+    s = roofline.stage_roofline("fused_g0_kernel", 1.0, 0.0, 1e6, "bf16",
+                                slots=roofline.PEAK_SLOTS_PER_S * 0.5e-3)
+    assert s["bound"] == "alu" and s["frac"] == pytest.approx(0.5)
+    assert s["bound_ms"] == pytest.approx(0.5)
+    # anything else: HBM bytes against 8 TB/s
+    s = roofline.stage_roofline("split_sum_kernel", 1.0, 0.0, 4.0e9, "bf16")
+    assert s["bound"] == "hbm" and s["frac"] == pytest.approx(0.5)
+
+
+@pytest.mark.parametrize("kernel,per_value", [
+    ("fused_g0_kernel", 28.0), ("chain_g_kernel", 28.0), ("jitter_loss_kernel", 28.0),
+    ("reweight_kernel", 27.0)])
+def test_noise_stage_slots(kernel, per_value):
+    T, d_out, K = 4, 8, 6
+    assert roofline.noise_stage_slots(kernel, T, d_out, K, True) == \
+        pytest.approx(K // 2 * T * d_out * per_value)

@@ -16,7 +16,8 @@ __all__ = ["DustError", "dust_workspace_bytes", "dust_workspace_bytes_seq", "dus
            "dust_estimate_head", "dust_embedding_workspace_bytes",
            "dust_reassemble_workspace_bytes", "dust_validate_embedding", "dust_estimate_embedding",
            "dust_validate_reassemble", "dust_reassemble_embedding", "dust_noise_fill",
-           "dust_set_timing_events", "dust_last_error", "library_path", "DUST_F32", "DUST_BF16"]
+           "dust_set_timing_events", "dust_profile_begin", "dust_profile_end", "dust_last_error",
+           "library_path", "DUST_F32", "DUST_BF16"]
 
 DUST_F32 = 0
 DUST_BF16 = 1
@@ -89,6 +90,13 @@ def _load():
     vpp = ctypes.POINTER(ctypes.c_void_p)
     lib.dust_set_timing_events.argtypes = [vpp, vpp, i32]
     lib.dust_set_timing_events.restype = ctypes.c_int
+    lib.dust_profile_begin.argtypes = [i32]
+    lib.dust_profile_begin.restype = ctypes.c_int
+    lib.dust_profile_end.argtypes = [ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(f32),
+                                     ctypes.POINTER(ctypes.c_double),
+                                     ctypes.POINTER(ctypes.c_double), i32,
+                                     ctypes.POINTER(i32)]
+    lib.dust_profile_end.restype = ctypes.c_int
     lib.dust_last_error.argtypes = []
     lib.dust_last_error.restype = ctypes.c_char_p
     _lib = lib
@@ -458,3 +466,34 @@ def dust_set_timing_events(starts, stops) -> None:
     if not all(handles_s) or not all(handles_e):
         raise ValueError("record every event once before registering it")
     _check(_load().dust_set_timing_events(arr(*handles_s), arr(*handles_e), n))
+
+
+_profile_cap = 0
+
+
+def dust_profile_begin(max_launches: int) -> None:
+    """Turn on the per-launch profile for this thread: each kernel launch of
+    the next library calls (up to max_launches) is stamped by its own pair
+    of library-owned events."""
+    global _profile_cap
+    _check(_load().dust_profile_begin(int(max_launches)))
+    _profile_cap = int(max_launches)
+
+
+def dust_profile_end() -> list:
+    """Turn the profile off (waiting for the recorded launches) and return
+    one dict per recorded launch, in launch order: kernel (stage name), ms,
+    flops (the method's MFMA flops), bytes (least HBM bytes it must move)."""
+    global _profile_cap
+    cap = max(_profile_cap, 1)
+    _profile_cap = 0
+    lib = _load()
+    names = (ctypes.c_char_p * cap)()
+    ms = (ctypes.c_float * cap)()
+    flops = (ctypes.c_double * cap)()
+    nbytes = (ctypes.c_double * cap)()
+    count = ctypes.c_int32(0)
+    _check(lib.dust_profile_end(names, ms, flops, nbytes, cap, ctypes.byref(count)))
+    n = min(cap, count.value)
+    return [{"kernel": names[i].decode(), "ms": float(ms[i]), "flops": float(flops[i]),
+             "bytes": float(nbytes[i])} for i in range(n)]

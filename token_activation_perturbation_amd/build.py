@@ -1,5 +1,4 @@
-"""Builds libdust.so (HIP, gfx950) in-tree with hipcc, and the valu_rates
-measurement program (the issue rates the ALU cost model is weighted by)."""
+"""Builds libdust.so (HIP, gfx950) in-tree with hipcc."""
 from __future__ import annotations
 
 import os
@@ -10,8 +9,6 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libdust.so")
 SOURCES = [os.path.join(CSRC, "dust_kernels.hip"), os.path.join(CSRC, "dust_host.cpp")]
-RATES_SRC = os.path.join(CSRC, "valu_rates.hip")
-RATES_BIN = os.path.join(PKG, "valu_rates")
 COMMON_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17",
     # keep the compiler from emitting packed fp32 ops
@@ -34,19 +31,5 @@ def build_library(verbose: bool = False) -> str:
     return LIB
 
 
-def build_rates(verbose: bool = False) -> str:
-    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    tmp = f"{RATES_BIN}.{os.getpid()}.tmp"
-    cmd = [hipcc, *COMMON_FLAGS, "-o", tmp, RATES_SRC]
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + res.stdout + res.stderr)
-    if verbose:
-        print(" ".join(cmd))
-    os.replace(tmp, RATES_BIN)
-    return RATES_BIN
-
-
 if __name__ == "__main__":
     print(build_library(verbose=True))
-    print(build_rates(verbose=True))

@@ -1365,6 +1365,42 @@ inline TimedLaunch take_timing_events() {
   return t;
 }
 
+// Per-launch profile, per calling thread (dust_profile_begin / _end): while
+// it is on, every kernel launch of this thread's library calls is stamped by
+// the next pair of library-owned events and recorded with its kernel name
+// and its algorithmic work (MFMA flops of the method's contraction, and the
+// HBM bytes the launch must move at least).
+struct LaunchRecord {
+  const char* name;
+  double flops, bytes;
+  hipEvent_t start, stop;
+};
+thread_local bool g_prof_on = false;
+thread_local std::vector<hipEvent_t> g_prof_events;  // 2 per recordable launch
+thread_local std::vector<LaunchRecord> g_prof;
+
+// The events one launch is stamped with: the profile's next pair while the
+// profile is on (the launch is recorded; launches past its capacity are not
+// stamped), else `tl` (the dominant-kernel hook's pair, or none).
+inline TimedLaunch stamp(const char* name, double flops, double bytes,
+                         TimedLaunch tl = TimedLaunch{}) {
+  if (!g_prof_on) return tl;
+  const size_t i = g_prof.size();
+  if (2 * i + 1 >= g_prof_events.size()) return TimedLaunch{};
+  g_prof.push_back(LaunchRecord{name, flops, bytes, g_prof_events[2 * i],
+                                g_prof_events[2 * i + 1]});
+  return TimedLaunch{g_prof_events[2 * i], g_prof_events[2 * i + 1]};
+}
+
+// Every kernel of the library is launched through this, with the events of
+// `ev` (a TimedLaunch; null events launch unstamped).
+#define DUST_LAUNCH(EV, KERNEL, GRID, BLOCK, LDS, STREAM, ...)                             \
+  do {                                                                                    \
+    const TimedLaunch ev_ = (EV);                                                         \
+    hipExtLaunchKernelGGL(KERNEL, GRID, BLOCK, LDS, STREAM, ev_.start, ev_.stop, 0,       \
+                          __VA_ARGS__);                                                   \
+  } while (0)
+
 template <int QPL>
 void launch_fused_g0_qpl(bool anti, bool full, unsigned blocks, unsigned threads,
                          hipStream_t s, TimedLaunch tl, const float* delta, int32_t t0,
@@ -1441,6 +1477,11 @@ inline unsigned grid_for(int64_t items, int64_t per_block) {
 void launch_base_gemm(const void* X, const void* W, const void* target, int64_t T, int64_t d_in,
                       int64_t d_out, int32_t dtype, float* out, hipStream_t s) {
   const int32_t Ti = (int32_t)T, di = (int32_t)d_in, dout = (int32_t)d_out;
+  const double es = dtype == DUST_BF16 ? 2.0 : 4.0;
+  const TimedLaunch ev =
+      stamp("base_gemm", 2.0 * T * d_in * d_out,
+            es * ((double)T * d_in + (double)d_out * d_in + (target ? (double)T * d_out : 0.0)) +
+                4.0 * T * d_out);
   if (dtype == DUST_BF16) {
     const bool vec = (d_in % 8 == 0) && ((uintptr_t)X % 16 == 0) && ((uintptr_t)W % 16 == 0);
     const int tiles_m = (int)ceil_div(T, 64), tiles_n = (int)ceil_div(d_out, 64);
@@ -1448,9 +1489,9 @@ void launch_base_gemm(const void* X, const void* W, const void* target, int64_t 
     const dim3 grid((unsigned)(8 * per_xcd));
     // aligned operands: the direct-to-LDS kernel; else guarded loads
 #define DUST_BASE_GEMM(KERNEL)                                                                \
-  hipLaunchKernelGGL(KERNEL, grid, dim3(256), 0, s, (const uint16_t*)X, (const uint16_t*)W,     \
-                     (int64_t)d_in, (int64_t)d_in, Ti, dout, (int64_t)d_in, tiles_m, tiles_n,  \
-                     per_xcd, (const uint16_t*)target, out)
+  DUST_LAUNCH(ev, KERNEL, grid, dim3(256), 0, s, (const uint16_t*)X, (const uint16_t*)W,        \
+              (int64_t)d_in, (int64_t)d_in, Ti, dout, (int64_t)d_in, tiles_m, tiles_n, per_xcd, \
+              (const uint16_t*)target, out)
     if (target) {
       if (vec) DUST_BASE_GEMM((gemm::nt_gemm_dma_kernel<true>));
       else DUST_BASE_GEMM((gemm::nt_gemm_kernel<4, true>));
@@ -1462,8 +1503,8 @@ void launch_base_gemm(const void* X, const void* W, const void* target, int64_t 
   } else {
     const int tiles_n = (int)ceil_div(d_out, 64);
     const unsigned blocks = (unsigned)(ceil_div(T, 64) * tiles_n);
-    hipLaunchKernelGGL(base_gemm_f32_kernel, dim3(blocks), dim3(256), 0, s, (const float*)X,
-                       (const float*)W, (const float*)target, Ti, di, dout, tiles_n, out);
+    DUST_LAUNCH(ev, base_gemm_f32_kernel, dim3(blocks), dim3(256), 0, s, (const float*)X,
+                (const float*)W, (const float*)target, Ti, di, dout, tiles_n, out);
   }
 }
 
@@ -1479,9 +1520,12 @@ void launch_chain(const Plan& p, const ChainPlan& cp, int64_t seq_len, float gam
   const dim3 grid((unsigned)(cp.n_seq * cp.groups)), block(64 * kChainWaves);
   const size_t lds = sizeof(float4) * 64 * (size_t)qpl * kChainWaves;
   const int32_t Ti = (int32_t)p.T, dout = (int32_t)p.d_out, sl = (int32_t)seq_len;
+  const double td = (double)p.T * p.d_out;
+  const TimedLaunch ev = stamp("chain_g_kernel", 0.0,
+                               4.0 * td * (1.0 + cp.groups) + (loss_clean ? 4.0 * p.T : 0.0), tl);
 #define DUST_CHAIN(Q, F)                                                                        \
-  hipExtLaunchKernelGGL((chain_g_kernel<Q, F>), grid, block, lds, s, tl.start, tl.stop, 0, delta, \
-                        Ti, dout, sl, p.K_n, cp.groups, gamma, key, loss_clean, part)
+  DUST_LAUNCH(ev, (chain_g_kernel<Q, F>), grid, block, lds, s, delta, Ti, dout, sl, p.K_n,      \
+              cp.groups, gamma, key, loss_clean, part)
 #define DUST_CHAIN_Q(Q)               \
   case Q:                             \
     if (full) DUST_CHAIN(Q, true);    \
@@ -1499,12 +1543,14 @@ void launch_chain(const Plan& p, const ChainPlan& cp, int64_t seq_len, float gam
   const bool sum_full = (p.d_out % 4 == 0) && part_vec;
   const unsigned blocks = (unsigned)ceil_div(p.T * p.nq, 256);
   const float scale = 2.0f / (float)p.K;
+  const TimedLaunch evs = stamp(
+      "chain_sum_kernel", 0.0, 4.0 * td * cp.groups + (g32 ? 4.0 * td : 0.0) + (g_hi ? 4.0 * td : 0.0));
   if (sum_full)
-    hipLaunchKernelGGL(chain_sum_kernel<true>, dim3(blocks), dim3(256), 0, s, (const float*)part,
-                       Ti, dout, p.nq, cp.groups, scale, g32, g_hi, g_lo);
+    DUST_LAUNCH(evs, chain_sum_kernel<true>, dim3(blocks), dim3(256), 0, s, (const float*)part,
+                Ti, dout, p.nq, cp.groups, scale, g32, g_hi, g_lo);
   else
-    hipLaunchKernelGGL(chain_sum_kernel<false>, dim3(blocks), dim3(256), 0, s,
-                       (const float*)part, Ti, dout, p.nq, cp.groups, scale, g32, g_hi, g_lo);
+    DUST_LAUNCH(evs, chain_sum_kernel<false>, dim3(blocks), dim3(256), 0, s, (const float*)part,
+                Ti, dout, p.nq, cp.groups, scale, g32, g_hi, g_lo);
 }
 
 // G_W = sum_t g_t x_t^T: the split partials (or G_W itself with one split),
@@ -1514,6 +1560,12 @@ void launch_outer(const Plan& p, const void* X, const float* g32, const uint16_t
                   int64_t d_out, int32_t dtype, hipStream_t s) {
   const int32_t Ti = (int32_t)T, di = (int32_t)d_in, dout = (int32_t)d_out;
   float* dst = p.outer_split > 1 ? gpart : G_W;
+  // the method's contraction (the bf16 path runs it twice, on g's hi and lo
+  // halves); bytes: g (split or fp32) and X in, the partials or G_W out
+  const double gn = (double)d_out * d_in;
+  const TimedLaunch ev = stamp(
+      "outer_gemm", 2.0 * T * d_in * d_out,
+      4.0 * T * d_out + (dtype == DUST_BF16 ? 2.0 : 4.0) * T * d_in + 4.0 * gn * p.outer_split);
   if (dtype == DUST_BF16) {
     // aligned operands: the direct-to-LDS kernel (the workspace keeps g_hi
     // and g_lo 16-byte aligned when d_out is a multiple of 8)
@@ -1524,27 +1576,26 @@ void launch_outer(const Plan& p, const void* X, const float* g32, const uint16_t
     const dim3 grid((unsigned)(8 * per_xcd));
     const int32_t partial = p.outer_split > 1 ? 1 : 0;
     if (vec)
-      hipLaunchKernelGGL(gemm::tn_outer_dma_kernel, grid, dim3(256), 0, s, (const uint16_t*)g_hi,
-                         (const uint16_t*)g_lo, (const uint16_t*)X, Ti, dout, di, tiles_m,
-                         tiles_n, p.outer_split, per_xcd, (int64_t)0, (int64_t)p.outer_tokens,
-                         partial, dst);
+      DUST_LAUNCH(ev, gemm::tn_outer_dma_kernel, grid, dim3(256), 0, s, (const uint16_t*)g_hi,
+                  (const uint16_t*)g_lo, (const uint16_t*)X, Ti, dout, di, tiles_m, tiles_n,
+                  p.outer_split, per_xcd, (int64_t)0, (int64_t)p.outer_tokens, partial, dst);
     else
-      hipLaunchKernelGGL((gemm::tn_outer_kernel<DUST_TN_STAGES>), grid, dim3(256), 0, s,
-                         (const uint16_t*)g_hi, (const uint16_t*)g_lo, (const uint16_t*)X, Ti,
-                         dout, di, tiles_m, tiles_n,
-                         p.outer_split, per_xcd, (int64_t)0, (int64_t)p.outer_tokens, partial,
-                         dst);
+      DUST_LAUNCH(ev, (gemm::tn_outer_kernel<DUST_TN_STAGES>), grid, dim3(256), 0, s,
+                  (const uint16_t*)g_hi, (const uint16_t*)g_lo, (const uint16_t*)X, Ti, dout, di,
+                  tiles_m, tiles_n, p.outer_split, per_xcd, (int64_t)0, (int64_t)p.outer_tokens,
+                  partial, dst);
   } else {
     const int tiles_n = (int)ceil_div(d_in, 64);
     const int64_t tiles = ceil_div(d_out, 64) * tiles_n;
-    hipLaunchKernelGGL(outer_f32_kernel, dim3((unsigned)(tiles * p.outer_split)), dim3(256), 0,
-                       s, (const float*)g32, (const float*)X, Ti, di, dout, tiles_n,
-                       (int32_t)p.outer_tokens, dst);
+    DUST_LAUNCH(ev, outer_f32_kernel, dim3((unsigned)(tiles * p.outer_split)), dim3(256), 0, s,
+                (const float*)g32, (const float*)X, Ti, di, dout, tiles_n,
+                (int32_t)p.outer_tokens, dst);
   }
   if (p.outer_split > 1) {
     const int64_t n = d_out * d_in;
-    hipLaunchKernelGGL(split_sum_kernel, dim3(grid_for(ceil_div(n, 4), 256)), dim3(256), 0, s,
-                       (const float*)gpart, p.outer_split, n, G_W);
+    DUST_LAUNCH(stamp("split_sum_kernel", 0.0, 4.0 * gn * (p.outer_split + 1)), split_sum_kernel,
+                dim3(grid_for(ceil_div(n, 4), 256)), dim3(256), 0, s, (const float*)gpart,
+                p.outer_split, n, G_W);
   }
 }
 
@@ -1554,9 +1605,11 @@ void launch_gather(const void* table, const int32_t* ids, const void* target, in
   const bool bf16 = dtype == DUST_BF16;
   const uintptr_t align = bf16 ? 8 : 16;
   const bool vec = d % 4 == 0 && (uintptr_t)table % align == 0 && (uintptr_t)target % align == 0;
-#define DUST_GATHER(B, VC)                                                                 \
-  hipLaunchKernelGGL((gather_delta_kernel<B, VC>), dim3((unsigned)T), dim3(256), 0, s, table, \
-                     ids, target, (int32_t)V, (int32_t)d, delta)
+  const TimedLaunch ev =
+      stamp("gather_delta_kernel", 0.0, (bf16 ? 4.0 : 8.0) * T * d + 4.0 * T * d + 4.0 * T);
+#define DUST_GATHER(B, VC)                                                                   \
+  DUST_LAUNCH(ev, (gather_delta_kernel<B, VC>), dim3((unsigned)T), dim3(256), 0, s, table, ids, \
+              target, (int32_t)V, (int32_t)d, delta)
   if (bf16) {
     if (vec) DUST_GATHER(true, true); else DUST_GATHER(true, false);
   } else {
@@ -1578,42 +1631,51 @@ void launch_reassemble(const ReassemblyPlan& r, char* base, const int32_t* ids, 
   const int32_t T = (int32_t)r.T, V = (int32_t)r.V, d = (int32_t)r.d;
   const unsigned chunks = (unsigned)r.n_chunks;
   const bool small_v = r.V <= kLdsHistMaxV;
+  // bytes: ids in and the per-chunk histograms out (and back), the sorted
+  // order, then g in and G_E out once
+  const double hist_b = 4.0 * r.V * (double)r.n_chunks;
   if (small_v) {
-    hipLaunchKernelGGL(reassemble::hist_kernel<true>, dim3(chunks), dim3(256),
-                       sizeof(int32_t) * (size_t)V, s, ids, T, V, r.chunk_tokens, r.n_chunks,
-                       hist);
+    DUST_LAUNCH(stamp("reassemble_hist", 0.0, 4.0 * T + hist_b), reassemble::hist_kernel<true>,
+                dim3(chunks), dim3(256), sizeof(int32_t) * (size_t)V, s, ids, T, V,
+                r.chunk_tokens, r.n_chunks, hist);
   } else {
     const int64_t n = r.V * (int64_t)r.n_chunks;
-    hipLaunchKernelGGL(reassemble::zero_kernel, dim3(grid_for(n < 262144 ? n : 262144, 256)),
-                       dim3(256), 0, s, hist, n);
-    hipLaunchKernelGGL(reassemble::hist_kernel<false>, dim3(chunks), dim3(256), 0, s, ids, T, V,
-                       r.chunk_tokens, r.n_chunks, hist);
+    DUST_LAUNCH(stamp("reassemble_zero", 0.0, hist_b), reassemble::zero_kernel,
+                dim3(grid_for(n < 262144 ? n : 262144, 256)), dim3(256), 0, s, hist, n);
+    DUST_LAUNCH(stamp("reassemble_hist", 0.0, 4.0 * T + hist_b), reassemble::hist_kernel<false>,
+                dim3(chunks), dim3(256), 0, s, ids, T, V, r.chunk_tokens, r.n_chunks, hist);
   }
   const bool vec = d % 4 == 0 && (uintptr_t)g % 16 == 0 && (uintptr_t)G_E % 16 == 0;
+  const TimedLaunch evc = stamp("reassemble_colscan", 0.0, 2.0 * hist_b + 4.0 * V);
   if (vec)
-    hipLaunchKernelGGL(reassemble::colscan_kernel<true>, dim3(grid_for(V, 4)), dim3(256), 0, s,
-                       hist, r.n_chunks, V, d, count, G_E);
+    DUST_LAUNCH(evc, reassemble::colscan_kernel<true>, dim3(grid_for(V, 4)), dim3(256), 0, s,
+                hist, r.n_chunks, V, d, count, G_E);
   else
-    hipLaunchKernelGGL(reassemble::colscan_kernel<false>, dim3(grid_for(V, 4)), dim3(256), 0, s,
-                       hist, r.n_chunks, V, d, count, G_E);
+    DUST_LAUNCH(evc, reassemble::colscan_kernel<false>, dim3(grid_for(V, 4)), dim3(256), 0, s,
+                hist, r.n_chunks, V, d, count, G_E);
+  const double place_b = 4.0 * T + hist_b + 8.0 * T;
   if (small_v) {
-    hipLaunchKernelGGL(reassemble::place_kernel<true>, dim3(chunks), dim3(256),
-                       sizeof(int32_t) * (size_t)(V + 1), s, ids, T, V, r.chunk_tokens,
-                       r.n_chunks, hist, (const int32_t*)count, start, perm, sid);
+    DUST_LAUNCH(stamp("reassemble_place", 0.0, place_b), reassemble::place_kernel<true>,
+                dim3(chunks), dim3(256), sizeof(int32_t) * (size_t)(V + 1), s, ids, T, V,
+                r.chunk_tokens, r.n_chunks, hist, (const int32_t*)count, start, perm, sid);
   } else {
-    hipLaunchKernelGGL(reassemble::start_scan_kernel, dim3(1), dim3(1024), 0, s,
-                       (const int32_t*)count, V, start);
-    hipLaunchKernelGGL(reassemble::place_kernel<false>, dim3(chunks), dim3(256), 0, s, ids, T, V,
-                       r.chunk_tokens, r.n_chunks, hist, (const int32_t*)count, start, perm, sid);
+    DUST_LAUNCH(stamp("reassemble_start_scan", 0.0, 8.0 * V), reassemble::start_scan_kernel,
+                dim3(1), dim3(1024), 0, s, (const int32_t*)count, V, start);
+    DUST_LAUNCH(stamp("reassemble_place", 0.0, place_b), reassemble::place_kernel<false>,
+                dim3(chunks), dim3(256), 0, s, ids, T, V, r.chunk_tokens, r.n_chunks, hist,
+                (const int32_t*)count, start, perm, sid);
   }
   const int64_t tile_units = r.n_tiles * r.col_chunks;
+  const double gb = 4.0 * T * d, pb = 8.0 * r.n_tiles * d;
 #define DUST_REASSEMBLE(VC)                                                                    \
-  hipLaunchKernelGGL((reassemble::tile_kernel<VC>), dim3(grid_for(tile_units, 4)), dim3(256), 0,  \
-                     s, g, (const int32_t*)perm, (const int32_t*)sid, T, d, r.col_chunks,        \
-                     tile_units, scale, part, G_E);                                             \
-  hipLaunchKernelGGL((reassemble::fixup_kernel<VC>), dim3(grid_for(tile_units, 4)), dim3(256), 0, \
-                     s, (const int32_t*)sid, (const int32_t*)start, T, (const float*)part, d,   \
-                     r.col_chunks, tile_units, scale, G_E)
+  DUST_LAUNCH(stamp("reassemble_tile", 0.0, gb + 8.0 * T + pb + 4.0 * V * d),                  \
+              (reassemble::tile_kernel<VC>), dim3(grid_for(tile_units, 4)), dim3(256), 0, s, g, \
+              (const int32_t*)perm, (const int32_t*)sid, T, d, r.col_chunks, tile_units, scale, \
+              part, G_E);                                                                      \
+  DUST_LAUNCH(stamp("reassemble_fixup", 0.0, pb), (reassemble::fixup_kernel<VC>),              \
+              dim3(grid_for(tile_units, 4)), dim3(256), 0, s, (const int32_t*)sid,              \
+              (const int32_t*)start, T, (const float*)part, d, r.col_chunks, tile_units, scale,  \
+              G_E)
   if (vec) {
     DUST_REASSEMBLE(true);
   } else {
@@ -1700,30 +1762,37 @@ dust_status_t run_estimate(const Site& st, int64_t T, int64_t d_in, int64_t d_ou
   const ChainPlan cp = embed ? ChainPlan{} : make_chain_plan(p, seq_len, gamma);
   const bool chain = !fused && cp.ok && !want_pq && workspace_bytes >= cp.total;
 
+  // algorithmic bytes of the per-draw stages: P (and Q) per (t, n), rho
+  // and the credit per (t, i), the weights per (t, n)
+  const double tkn = (double)T * p.K_n, tk = (double)T * K, td = (double)T * d_out;
+  const double pq_b = 4.0 * tkn * (Qused ? 2.0 : 1.0);
+  const double g_out_b = (g32 ? 4.0 * td : 0.0) + (g_hi ? 4.0 * td : 0.0);
+  const double stats_b = pq_b + 4.0 * tk + 4.0 * T;
+  const double credit_b = 4.0 * tk + 4.0 * T + (reward ? 4.0 * tk : 0.0) + 4.0 * tkn;
   if (chain) {
     launch_chain(p, cp, seq_len, gamma, key, (const float*)delta, delta_vec, loss_clean,
                  (float*)(ws + cp.off_part), g32, g_hi, g_lo, s, tl);
   } else if (!fused) {
     // 2. jitter + loss change
+    const TimedLaunch evj =
+        stamp("jitter_loss_kernel", 0.0, 4.0 * td + pq_b + (loss_clean ? 4.0 * T : 0.0), tl);
     if (Qused)
-      hipExtLaunchKernelGGL(jitter_loss_kernel<true>, dim3(grid_for(T * p.jl_chunks, 4)),
-                            dim3(256), 0, s, tl.start, tl.stop, 0, (const float*)delta,
-                            (int32_t)delta_vec, Ti, dout, p.nq, p.K_n, p.jl_chunks,
-                            p.jl_per_chunk, key, Pbuf, Qused, loss_clean);
+      DUST_LAUNCH(evj, jitter_loss_kernel<true>, dim3(grid_for(T * p.jl_chunks, 4)), dim3(256), 0,
+                  s, (const float*)delta, (int32_t)delta_vec, Ti, dout, p.nq, p.K_n, p.jl_chunks,
+                  p.jl_per_chunk, key, Pbuf, Qused, loss_clean);
     else
-      hipExtLaunchKernelGGL(jitter_loss_kernel<false>, dim3(grid_for(T * p.jl_chunks, 4)),
-                            dim3(256), 0, s, tl.start, tl.stop, 0, (const float*)delta,
-                            (int32_t)delta_vec, Ti, dout, p.nq, p.K_n, p.jl_chunks,
-                            p.jl_per_chunk, key, Pbuf, Qused, loss_clean);
+      DUST_LAUNCH(evj, jitter_loss_kernel<false>, dim3(grid_for(T * p.jl_chunks, 4)), dim3(256),
+                  0, s, (const float*)delta, (int32_t)delta_vec, Ti, dout, p.nq, p.K_n,
+                  p.jl_chunks, p.jl_per_chunk, key, Pbuf, Qused, loss_clean);
     // 3. loss reductions and their mean over draws
-    hipLaunchKernelGGL(token_stats_kernel, dim3(grid_for(T, 4)), dim3(256), 0, s,
-                       (const float*)Pbuf, (const float*)Qused, Ti, K, p.K_n, p.antithetic,
-                       sigma, curv, rho_buf, mean);
+    DUST_LAUNCH(stamp("token_stats_kernel", 0.0, stats_b), token_stats_kernel,
+                dim3(grid_for(T, 4)), dim3(256), 0, s, (const float*)Pbuf, (const float*)Qused,
+                Ti, K, p.K_n, p.antithetic, sigma, curv, rho_buf, mean);
     // 4. centring + discounted credit -> per-(t, n) weights
     if (independent) {
-      hipLaunchKernelGGL(credit_token_kernel, dim3(grid_for(T * p.K_n, 256)), dim3(256), 0, s,
-                         (const float*)rho_buf, (const float*)mean, Ti, K, p.K_n, p.antithetic,
-                         sigma, reward, wgt);
+      DUST_LAUNCH(stamp("credit_token_kernel", 0.0, credit_b), credit_token_kernel,
+                  dim3(grid_for(T * p.K_n, 256)), dim3(256), 0, s, (const float*)rho_buf,
+                  (const float*)mean, Ti, K, p.K_n, p.antithetic, sigma, reward, wgt);
     } else {
       const int64_t n_seq = T / seq_len;
       const int32_t n_chunks = (int32_t)ceil_div(seq_len, kScanChunk);
@@ -1731,14 +1800,19 @@ dust_status_t run_estimate(const Site& st, int64_t T, int64_t d_in, int64_t d_ou
       float* carry = (float*)(ws + p.off_carry);
       float gamma_chunk = 1.f;
       for (int k = 0; k < kScanChunk; ++k) gamma_chunk *= gamma;
-      hipLaunchKernelGGL(scan_local_kernel, dim3(grid_for(n_seq * n_chunks * K, 256)), dim3(256),
-                         0, s, (const float*)rho_buf, (const float*)mean, Ti, (int32_t)seq_len,
-                         K, n_chunks, gamma, r_loc, carry);
-      hipLaunchKernelGGL(scan_carry_kernel, dim3(grid_for(n_seq * K, 256)), dim3(256), 0, s,
-                         carry, (int32_t)n_seq, n_chunks, K, gamma_chunk);
-      hipLaunchKernelGGL(scan_apply_kernel, dim3(grid_for(T * p.K_n, 256)), dim3(256), 0, s,
-                         (const float*)r_loc, (const float*)carry, Ti, (int32_t)seq_len, K,
-                         p.K_n, n_chunks, p.antithetic, sigma, gamma, reward, wgt);
+      const double heads_b = 4.0 * n_seq * n_chunks * (double)K;
+      DUST_LAUNCH(stamp("scan_local_kernel", 0.0, 8.0 * tk + 4.0 * T + heads_b),
+                  scan_local_kernel, dim3(grid_for(n_seq * n_chunks * K, 256)), dim3(256), 0, s,
+                  (const float*)rho_buf, (const float*)mean, Ti, (int32_t)seq_len, K, n_chunks,
+                  gamma, r_loc, carry);
+      DUST_LAUNCH(stamp("scan_carry_kernel", 0.0, 2.0 * heads_b), scan_carry_kernel,
+                  dim3(grid_for(n_seq * K, 256)), dim3(256), 0, s, carry, (int32_t)n_seq,
+                  n_chunks, K, gamma_chunk);
+      DUST_LAUNCH(stamp("scan_apply_kernel", 0.0,
+                        4.0 * tk + heads_b + (reward ? 4.0 * tk : 0.0) + 4.0 * tkn),
+                  scan_apply_kernel, dim3(grid_for(T * p.K_n, 256)), dim3(256), 0, s,
+                  (const float*)r_loc, (const float*)carry, Ti, (int32_t)seq_len, K, p.K_n,
+                  n_chunks, p.antithetic, sigma, gamma, reward, wgt);
     }
   }
 
@@ -1748,22 +1822,25 @@ dust_status_t run_estimate(const Site& st, int64_t T, int64_t d_in, int64_t d_ou
   if (chain) {
   } else if (fused) {
     const bool full = (p.nq == 64 * qpl) && delta_vec;
+    const TimedLaunch evf = stamp(
+        "fused_g0_kernel", 0.0,
+        4.0 * td + g_out_b + (loss_clean ? 4.0 * T : 0.0) + (want_pq ? pq_b : 0.0), tl);
     launch_fused_g0(qpl, p.antithetic != 0, full, (unsigned)T, (unsigned)(64 * p.fz_waves), s,
-                    tl, (const float*)delta, 0, dout, K, p.K_n, p.fz_per_wave, sigma,
+                    evf, (const float*)delta, 0, dout, K, p.K_n, p.fz_per_wave, sigma,
                     curv, key, want_pq ? Pbuf : nullptr, want_pq ? Qused : nullptr, loss_clean,
                     g32, g_hi, g_lo);
     if (want_pq) {
-      hipLaunchKernelGGL(token_stats_kernel, dim3(grid_for(T, 4)), dim3(256), 0, s,
-                         (const float*)Pbuf, (const float*)Qused, Ti, K, p.K_n, p.antithetic,
-                         sigma, curv, rho_buf, mean);
-      hipLaunchKernelGGL(credit_token_kernel, dim3(grid_for(T * p.K_n, 256)), dim3(256), 0, s,
-                         (const float*)rho_buf, (const float*)mean, Ti, K, p.K_n, p.antithetic,
-                         sigma, reward, wgt);
+      DUST_LAUNCH(stamp("token_stats_kernel", 0.0, stats_b), token_stats_kernel,
+                  dim3(grid_for(T, 4)), dim3(256), 0, s, (const float*)Pbuf, (const float*)Qused,
+                  Ti, K, p.K_n, p.antithetic, sigma, curv, rho_buf, mean);
+      DUST_LAUNCH(stamp("credit_token_kernel", 0.0, credit_b), credit_token_kernel,
+                  dim3(grid_for(T * p.K_n, 256)), dim3(256), 0, s, (const float*)rho_buf,
+                  (const float*)mean, Ti, K, p.K_n, p.antithetic, sigma, reward, wgt);
     }
   } else {
-    hipLaunchKernelGGL(reweight_kernel, dim3((unsigned)T), dim3(64 * p.rw_waves), 0, s,
-                       (const float*)wgt, 0, dout, p.nq, p.K_n, p.rw_per_wave, key, g32,
-                       g_hi, g_lo);
+    DUST_LAUNCH(stamp("reweight_kernel", 0.0, 4.0 * tkn + g_out_b), reweight_kernel,
+                dim3((unsigned)T), dim3(64 * p.rw_waves), 0, s, (const float*)wgt, 0, dout, p.nq,
+                p.K_n, p.rw_per_wave, key, g32, g_hi, g_lo);
   }
 
   // 6. outer product -> the split partials (or G_W itself with one split),
@@ -1801,10 +1878,16 @@ dust_status_t run_head(const void* X, const void* W, const int32_t* labels, int6
   const unsigned waves = (unsigned)(n_slab < 4 ? n_slab : 4);
   // every noise value has |a| <= sqrt(48 ln 2) < 5.78, so |sigma a| < 0.5
   const bool small = sigma * 5.78f < 0.5f;
-#define DUST_HEAD(A, SM)                                                                    \
-  hipExtLaunchKernelGGL((head_ce_kernel<A, SM>), dim3((unsigned)T), dim3(64 * waves), 0, s, \
-                        tl.start, tl.stop, 0, (const float*)logits, labels, (int32_t)V, K,  \
-                        p.K_n, sigma, key, loss_clean, rho, g32, g_hi, g_lo)
+  const double tv = (double)T * V;
+  const TimedLaunch evh =
+      stamp("head_ce_kernel", 0.0,
+            4.0 * tv + 4.0 * T + (g32 ? 4.0 * tv : 0.0) + (g_hi ? 4.0 * tv : 0.0) +
+                (loss_clean ? 4.0 * T : 0.0) + (rho ? 4.0 * T * (double)(V / 256) * K : 0.0),
+            tl);
+#define DUST_HEAD(A, SM)                                                                       \
+  DUST_LAUNCH(evh, (head_ce_kernel<A, SM>), dim3((unsigned)T), dim3(64 * waves), 0, s,          \
+              (const float*)logits, labels, (int32_t)V, K, p.K_n, sigma, key, loss_clean, rho,  \
+              g32, g_hi, g_lo)
   if (antithetic) {
     if (small) DUST_HEAD(true, true); else DUST_HEAD(true, false);
   } else {
@@ -1920,6 +2003,66 @@ dust_status_t dust_set_timing_events(void* const* start, void* const* stop, int3
   return ok();
 }
 
+namespace {
+void release_profile() {
+  for (hipEvent_t e : dust::g_prof_events) (void)hipEventDestroy(e);
+  dust::g_prof_events.clear();
+  dust::g_prof.clear();
+  dust::g_prof_on = false;
+}
+}  // namespace
+
+dust_status_t dust_profile_begin(int32_t max_launches) {
+  using namespace dust;
+  if (max_launches <= 0 || max_launches > (1 << 20))
+    return fail(DUST_ERR_INVALID_ARG, "profile_begin: max_launches=%d must lie in [1, 2^20]",
+                max_launches);
+  release_profile();
+  g_prof_events.reserve(2 * (size_t)max_launches);
+  g_prof.reserve((size_t)max_launches);
+  for (int32_t i = 0; i < 2 * max_launches; ++i) {
+    hipEvent_t e = nullptr;
+    const hipError_t r = hipEventCreate(&e);
+    if (r != hipSuccess) {
+      release_profile();
+      return fail(DUST_ERR_HIP, "profile_begin: hipEventCreate failed: %s", hipGetErrorString(r));
+    }
+    g_prof_events.push_back(e);
+  }
+  g_prof_on = true;
+  return ok();
+}
+
+dust_status_t dust_profile_end(const char** kernel, float* ms, double* flops, double* bytes,
+                               int32_t cap, int32_t* count) {
+  using namespace dust;
+  if (cap < 0 || (cap > 0 && (!kernel || !ms || !flops || !bytes)) || !count) {
+    release_profile();
+    return fail(DUST_ERR_INVALID_ARG, "profile_end: need cap >= 0, output arrays and count");
+  }
+  g_prof_on = false;
+  int32_t n = 0;
+  for (const LaunchRecord& r : g_prof) {
+    hipError_t e = hipEventSynchronize(r.stop);
+    float t = 0.f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&t, r.start, r.stop);
+    if (e != hipSuccess) {
+      release_profile();
+      return fail(DUST_ERR_HIP, "profile_end: event query failed: %s", hipGetErrorString(e));
+    }
+    if (n < cap) {
+      kernel[n] = r.name;
+      ms[n] = t;
+      flops[n] = r.flops;
+      bytes[n] = r.bytes;
+    }
+    ++n;
+  }
+  *count = n;
+  release_profile();
+  return ok();
+}
+
 dust_status_t dust_noise_fill(uint64_t seed, int64_t n0, int64_t n_cnt, int64_t t0,
                               int64_t t_cnt, int64_t d_out, uint32_t* words, float* gauss,
                               void* stream) {
@@ -1933,9 +2076,11 @@ dust_status_t dust_noise_fill(uint64_t seed, int64_t n0, int64_t n_cnt, int64_t 
   const int64_t total = n_cnt * t_cnt * nq;
   if (total >= (int64_t(1) << 40))
     return fail(DUST_ERR_INVALID_ARG, "noise_fill: too many values");
-  hipLaunchKernelGGL(noise_fill_kernel, dim3(grid_for(total, 256)), dim3(256), 0,
-                     (hipStream_t)stream, make_key(seed), (int32_t)n0, (int32_t)n_cnt,
-                     (int32_t)t0, (int32_t)t_cnt, (int32_t)d_out, (int32_t)nq, words, gauss);
+  DUST_LAUNCH(stamp("noise_fill_kernel", 0.0,
+                    (double)n_cnt * t_cnt * ((words ? 16.0 * nq : 0.0) + (gauss ? 4.0 * d_out : 0.0))),
+              noise_fill_kernel, dim3(grid_for(total, 256)), dim3(256), 0, (hipStream_t)stream,
+              make_key(seed), (int32_t)n0, (int32_t)n_cnt, (int32_t)t0, (int32_t)t_cnt,
+              (int32_t)d_out, (int32_t)nq, words, gauss);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(DUST_ERR_HIP, "noise_fill launch failed: %s", hipGetErrorString(e));
   return ok();

@@ -10,9 +10,9 @@ at once.  Their bound is the vector ALU issue rate, counted in lane-slots:
   lane-slots per second.
 
 * Issue cost of each instruction, by the rate class measured on an MI355X
-  with the `valu_rates` program built beside this module (each instruction
-  alone, operands in vector registers, lanes per CU per clock at the clock
-  measured during the run): single-pass operations (xor, shifts, fp32
+  with a one-off instruction-rate probe (each instruction alone, operands
+  in vector registers, lanes per CU per clock at the clock measured during
+  the run): single-pass operations (xor, shifts, fp32
   add / mul / fma, the three-input bitwise op) 1 slot (107-122 lanes per
   clock for the two-operand forms; the three-operand forms alone reach ~80,
   a register-read limit that a mixed stream does not hit, so they count 1);
@@ -52,8 +52,8 @@ Taylor parts, 9 + 2 slots; plain draws: 8 slots of Horner), the slab's
 partial sums (one FMA per sign), 1 FMA for g and, for plain draws, 1 add for
 the noise sum: 41 slots per value with antithetic pairs, 38 without.
 
-The generation alone (noise_quad in a loop, the `valu_rates` program's last
-row) runs at ~0.84 of this model's peak with the clock at 2.4 GHz: the
+The generation alone (noise_quad in a loop, the probe's last row) runs at
+~0.84 of this model's peak with the clock at 2.4 GHz: the
 practical ceiling the noise kernels are measured against in the text.
 Counted this way a two-pass pipeline (generate for the loss change, then
 regenerate for g) is capped at about half of the roofline; a single
@@ -126,3 +126,68 @@ def head_kernel_slots(T: int, V: int, K: int, antithetic: bool) -> float:
 
 def head_min_seconds(T: int, V: int, K: int, antithetic: bool) -> float:
     return head_kernel_slots(T, V, K, antithetic) / PEAK_SLOTS_PER_S
+
+
+def reweight_kernel_slots(T: int, d_out: int, K: int, antithetic: bool) -> float:
+    """The reweight pass of the two-pass path: the noise generated again and
+    one FMA per value into g."""
+    return distinct_noise_values(T, d_out, K, antithetic) * (GEN_SLOTS_PER_VALUE + 1.0)
+
+
+# ---------------------------------------------------------------------------
+# Every stage against its own roofline.  The other units' peaks on MI355X:
+# dense MFMA (bf16 operands, fp32 accumulation) 2.5 PFLOP/s, fp32 MFMA
+# 157.3 TFLOP/s, HBM3E 8 TB/s.
+
+MFMA_PEAK_FLOPS = {"bf16": 2.5e15, "f32": 157.3e12}
+HBM_PEAK_BYTES = 8.0e12
+
+# stages whose bound is the vector ALU (each generates noise values)
+NOISE_STAGES = ("fused_g0_kernel", "chain_g_kernel", "jitter_loss_kernel", "reweight_kernel",
+                "head_ce_kernel")
+
+
+def noise_stage_slots(kernel: str, T: int, d_out: int, K: int, antithetic: bool,
+                      per_draw_outputs: bool = False, local: bool = False) -> float:
+    """Algorithmic lane-slots of one launch of a noise stage (d_out is the
+    vocabulary for the head)."""
+    if kernel == "fused_g0_kernel":
+        return fused_kernel_slots(T, d_out, K, antithetic, per_draw_outputs, local)
+    if kernel == "chain_g_kernel":
+        return fused_kernel_slots(T, d_out, K, antithetic, False, local)
+    if kernel == "jitter_loss_kernel":
+        return jitter_kernel_slots(T, d_out, K, antithetic, local)
+    if kernel == "reweight_kernel":
+        return reweight_kernel_slots(T, d_out, K, antithetic)
+    if kernel == "head_ce_kernel":
+        return head_kernel_slots(T, d_out, K, antithetic)
+    raise KeyError(kernel)
+
+
+def stage_roofline(kernel: str, ms: float, flops: float, nbytes: float, dtype: str,
+                   slots: float | None = None) -> dict:
+    """One stage's time against the bound of its kind: the ALU slot model for
+    the noise stages (`slots`), the MFMA peak of the operand type for a
+    contraction (`flops` > 0), HBM for the rest.  Every stage also carries its
+    HBM rate (algorithmic bytes / time) and `bound_ms`, the time its slowest
+    unit needs at peak (the larger of its ALU, MFMA and HBM times)."""
+    t = ms * 1e-3
+    hbm = nbytes / t if t > 0 else float("nan")
+    alu_s = (slots or 0.0) / PEAK_SLOTS_PER_S
+    mfma_s = flops / MFMA_PEAK_FLOPS[dtype] if flops > 0 else 0.0
+    hbm_s = nbytes / HBM_PEAK_BYTES
+    out = {"kernel": kernel, "ms": ms, "hbm_GBps": hbm / 1e9, "hbm_frac": hbm / HBM_PEAK_BYTES,
+           "bound_ms": max(alu_s, mfma_s, hbm_s) * 1e3}
+    if slots is not None:
+        achieved = slots / t / 1e12
+        out.update(bound="alu", achieved=achieved, peak=PEAK_SLOTS_PER_S / 1e12,
+                   unit="T lane-slot/s", frac=achieved / (PEAK_SLOTS_PER_S / 1e12))
+    elif flops > 0:
+        achieved = flops / t / 1e12
+        peak = MFMA_PEAK_FLOPS[dtype] / 1e12
+        out.update(bound="mfma", achieved=achieved, peak=peak, unit="TFLOP/s",
+                   frac=achieved / peak)
+    else:
+        out.update(bound="hbm", achieved=hbm / 1e9, peak=HBM_PEAK_BYTES / 1e9, unit="GB/s",
+                   frac=hbm / HBM_PEAK_BYTES)
+    return out
