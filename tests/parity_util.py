@@ -4,19 +4,34 @@ The estimate's bar (the tolerance stated for the method's output): G_W
 within relative Frobenius error 2e-3 for bf16 inputs with fp32 accumulation
 and 1e-5 for the fp32 path.  The parity tests hold every stage output (the
 clean loss L_t, the loss reductions rho, the credit r, the error estimate g)
-to the same relative level twice over:
+to that relative level over the whole tensor, and each token on its own
+(each row of G_W likewise):
 
-  * whole tensor:  ||got - ref||_F / ||ref||_F <= bar
-  * per row:       max over tokens t of ||got_t - ref_t|| / ||ref_t|| <= bar
-                   (rows of G_W: max over output channels c)
+  * whole tensor:  ||got - ref||_F / ||ref||_F <= TOL[dtype]
+  * per row:       max over tokens t of ||got_t - ref_t|| / ||ref_t||
+                   <= ROW_TOL[dtype]   (rows of G_W: max over channels c)
 
 The per-row form is the one that catches a single wrong token, a wrong tail
 quad or a wrong sequence, which the whole-tensor norm dilutes.  A row whose
 reference is exactly zero is compared in absolute terms.
+
+The per-row bar of the fp32 path is not the whole-tensor 1e-5: one token's
+value is a handful of fp32 sums, and an fp32 sum of n terms can be off by up
+to about n u relative to the sum of the terms' magnitudes (u = 2^-24, the
+unit roundoff); over a whole tensor those per-token rounding errors average
+out, token by token they do not.  A token whose value is small next to its
+terms (a near-zero cross-entropy of a confident head, whose logits carry
+absolute rounding of d_in u |x w|; a loss reduction that nearly cancels)
+shows its terms' rounding at full size.  ROW_TOL["f32"] = 1e-4 is n u for
+n of about 1,700 terms, the length of the longest fp32 sums the fp32 test
+shapes form per token (vocabulary columns plus draws, or channels plus
+draws).  The bf16 path's bar, 2e-3, already exceeds that bound at every
+size tested and is used for rows unchanged.
 """
 import numpy as np
 
 TOL = {"f32": 1e-5, "bf16": 2e-3}
+ROW_TOL = {"f32": 1e-4, "bf16": 2e-3}
 
 
 def rel(a, b):
@@ -63,6 +78,9 @@ def report(name, errs):
     print(name, " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
 
 
-def assert_within(errs, tol):
-    bad = {k: v for k, v in errs.items() if not v <= tol}
-    assert not bad, (bad, tol)
+def assert_within(errs, dtype):
+    """Every error of `errs` within its bar: ROW_TOL for the per-row entries
+    (keys ending in "_row"), TOL for the rest."""
+    bad = {k: v for k, v in errs.items()
+           if not v <= (ROW_TOL if k.endswith("_row") else TOL)[dtype]}
+    assert not bad, (bad, dtype, TOL[dtype], ROW_TOL[dtype])

@@ -21,7 +21,7 @@ Errors are measured over whole tensors and token by token (parity_util.py).
 import numpy as np
 import pytest
 
-from parity_util import TOL, assert_within, rel, report, stage_errors
+from parity_util import assert_within, rel, report, stage_errors
 from token_activation_perturbation_amd import synth
 
 pytestmark = pytest.mark.gpu
@@ -103,8 +103,8 @@ def test_chain_parity_with_oracle_and_two_pass(dev, oracle_mod, threads, case):
     errs = stage_errors(chain, ref, keys=("loss", "g"))
     errs["vs_two_pass"] = rel(chain["G_W"], two["G_W"])
     report("  rel err", errs)
-    assert_within(errs, TOL[dtype])
-    assert_within(stage_errors(two, ref, keys=("loss", "g")), TOL[dtype])
+    assert_within(errs, dtype)
+    assert_within(stage_errors(two, ref, keys=("loss", "g")), dtype)
     assert not np.array_equal(chain["g"], two["g"])
 
 
@@ -129,7 +129,7 @@ def test_asking_for_per_draw_outputs_keeps_G_within_the_bar(dev, oracle_mod, thr
     errs["bare_G_W"] = rel(bare, ref["G"])
     errs["full_vs_bare"] = rel(full["G_W"], bare)
     report("  path switch", errs)
-    assert_within(errs, TOL["bf16"])
+    assert_within(errs, "bf16")
     assert not np.array_equal(full["G_W"], bare)  # the two paths really differ
 
 
@@ -146,7 +146,7 @@ def test_chain_local_scoring(dev, oracle_mod, threads):
     errs = stage_errors(chain, ref, keys=("g",))
     errs["vs_two_pass"] = rel(chain["g"], two["g"])
     report("  local rel err", errs)
-    assert_within(errs, TOL["bf16"])
+    assert_within(errs, "bf16")
     assert not np.array_equal(chain["g"], two["g"])
 
 

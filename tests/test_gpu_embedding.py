@@ -162,7 +162,7 @@ def compare(got, ref, dtype, label, sl=slice(None)):
     errs = stage_errors(got, ref, keys=("loss", "rho", "reward", "g"),
                         g_key="G_E" if whole else "none", token_slice=sl)
     report(label, errs)
-    assert_within(errs, TOL[dtype])
+    assert_within(errs, dtype)
 
 
 EMBED = [

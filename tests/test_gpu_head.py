@@ -70,7 +70,7 @@ def compare(got, ref, dtype, label, sl=slice(None)):
     errs = stage_errors(got, ref, keys=("loss", "rho", "g"),
                         g_key="G_W" if whole else "none", token_slice=sl)
     report(label, errs)
-    assert_within(errs, TOL[dtype])
+    assert_within(errs, dtype)
 
 
 SMALL = [

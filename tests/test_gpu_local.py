@@ -70,7 +70,7 @@ def compare(got, ref, dtype, label, sl=slice(None)):
     errs = stage_errors(got, ref, keys=("rho", "reward", "g"),
                         g_key="G_W" if whole else "none", token_slice=sl)
     report(label, errs)
-    assert_within(errs, TOL[dtype])
+    assert_within(errs, dtype)
 
 
 SMALL = [
@@ -180,7 +180,7 @@ def test_value_embedding_g_only_then_reassembly(dev, oracle_mod, threads, gamma)
                                                                    scale=1.0 / T)},
                              keys=(), g_key="G_V"))
     report("  rel err", errs)
-    assert_within(errs, TOL["f32"])
+    assert_within(errs, "f32")
     X, _ = local_inputs(T, 32, d, "bf16", seed=43)
     full = gpu_local(X, E, "bf16", dev, **kw)
     assert np.array_equal(full["g"], got["g"])
