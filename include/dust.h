@@ -142,6 +142,34 @@ dust_status_t dust_estimate(const void* X, const void* W, const void* target,
                             void* stream);
 
 /*
+ * dust_estimate for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * It takes no workspace argument: its workspace is a file-scope device array
+ * of DUST_NOALLOC_WORKSPACE_BYTES (64 MiB) inside the library, one copy per
+ * GPU, placed when the library's code is first loaded on that GPU and held
+ * until the process ends.  The call makes no hipMalloc, hipFree or other
+ * allocating call (its first call on a GPU looks up that copy's address).
+ * Sizes whose dust_workspace_bytes(...) exceeds the array are rejected with
+ * DUST_ERR_UNSUPPORTED before anything is enqueued; the other argument
+ * checks, the outputs and the errors are dust_estimate's.  The estimate is
+ * the one dust_estimate computes with a workspace of that many bytes
+ * (single generation for gamma > 0 where dust_workspace_bytes_seq(...) fits
+ * in it).  Nothing in the array needs to start at zero: every stage writes
+ * what the next one reads.  Every call on one GPU shares that GPU's array and
+ * it keeps the last call's contents: calls that overlap on one GPU (on
+ * different streams, or from threads without ordering between them) race
+ * and give undefined results; calls ordered on one stream are safe.
+ */
+#define DUST_NOALLOC_WORKSPACE_BYTES ((size_t)64 << 20)
+size_t dust_noalloc_workspace_capacity(void);
+dust_status_t dust_estimate_noalloc(const void* X, const void* W, const void* target,
+                                    int64_t T, int64_t d_in, int64_t d_out,
+                                    int64_t seq_len, int32_t dtype, int32_t K,
+                                    float sigma, float gamma, uint64_t seed,
+                                    int32_t antithetic, float* G_W, float* loss_clean,
+                                    float* rho, float* reward, float* g, void* stream);
+
+/*
  * Host-side check of dust_estimate_local's arguments: the same rules as
  * dust_validate, with E required (4-byte aligned) and X and G_W either both
  * given or both NULL.  No HIP call.

@@ -16,6 +16,7 @@ __all__ = ["DustError", "dust_workspace_bytes", "dust_workspace_bytes_seq", "dus
            "dust_estimate_head", "dust_embedding_workspace_bytes",
            "dust_reassemble_workspace_bytes", "dust_validate_embedding", "dust_estimate_embedding",
            "dust_validate_reassemble", "dust_reassemble_embedding", "dust_noise_fill",
+           "dust_estimate_noalloc", "dust_noalloc_workspace_capacity",
            "dust_set_timing_events", "dust_profile_begin", "dust_profile_end", "dust_last_error",
            "library_path", "DUST_F32", "DUST_BF16"]
 
@@ -58,6 +59,11 @@ def _load():
     lib.dust_estimate.argtypes = [vp, vp, vp, i64, i64, i64, i64, i32, i32, f32, f32,
                                   ctypes.c_uint64, i32, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.dust_estimate.restype = ctypes.c_int
+    lib.dust_estimate_noalloc.argtypes = [vp, vp, vp, i64, i64, i64, i64, i32, i32, f32, f32,
+                                          ctypes.c_uint64, i32, vp, vp, vp, vp, vp, vp]
+    lib.dust_estimate_noalloc.restype = ctypes.c_int
+    lib.dust_noalloc_workspace_capacity.argtypes = []
+    lib.dust_noalloc_workspace_capacity.restype = sz
     lib.dust_validate_local.argtypes = [vp, vp, i64, i64, i64, i64, i32, i32, f32, f32, i32,
                                         vp, vp, sz]
     lib.dust_validate_local.restype = ctypes.c_int
@@ -250,6 +256,47 @@ def dust_estimate(X, W, target, *, K: int, sigma: float, gamma: float, seed: int
         sigma, gamma, ctypes.c_uint64(seed & 0xFFFFFFFFFFFFFFFF), int(bool(antithetic)),
         G.data_ptr(), ptr(loss), ptr(rho), ptr(reward), ptr(g), ws.data_ptr(), ws_bytes,
         _stream_ptr(dev))
+    _check(status)
+    return res
+
+
+def dust_noalloc_workspace_capacity() -> int:
+    """Bytes of the static workspace dust_estimate_noalloc runs in."""
+    return int(_load().dust_noalloc_workspace_capacity())
+
+
+def dust_estimate_noalloc(X, W, target, *, K: int, sigma: float, gamma: float, seed: int,
+                          antithetic: bool, seq_len: int, want_loss: bool = False,
+                          want_rho: bool = False, want_reward: bool = False,
+                          want_g: bool = False, out: dict | None = None):
+    """Enqueue dust_estimate_noalloc (dust_estimate in the library's static
+    workspace: the library allocates nothing) on the current stream of X's
+    device.  Arguments and outputs as for dust_estimate, without a
+    workspace; pass every output in ``out`` for a call that allocates
+    nothing at all (missing ones are created here, before the call)."""
+    dev = _check_tensors(None, X=X, W=W, target=target)
+    if not (X.dtype == W.dtype == target.dtype):
+        raise TypeError("X, W and target must share one dtype")
+    if X.dim() != 2 or W.dim() != 2 or target.dim() != 2:
+        raise ValueError("X, W and target must be 2-D")
+    T, d_in = X.shape
+    d_out = W.shape[0]
+    if W.shape[1] != d_in or tuple(target.shape) != (T, d_out):
+        raise ValueError(f"shape mismatch: X {tuple(X.shape)}, W {tuple(W.shape)}, "
+                         f"target {tuple(target.shape)}")
+    dt = _dtype_code(X)
+    res = dict(out or {})
+    _get = _output_getter(res, dev)
+    G = _get("G_W", (d_out, d_in))
+    loss = _get("loss", (T,)) if want_loss else None
+    rho = _get("rho", (T, K)) if want_rho else None
+    reward = _get("reward", (T, K)) if want_reward else None
+    g = _get("g", (T, d_out)) if want_g else None
+    ptr = lambda t: None if t is None else t.data_ptr()  # noqa: E731
+    status = _load().dust_estimate_noalloc(
+        X.data_ptr(), W.data_ptr(), target.data_ptr(), T, d_in, d_out, seq_len, dt, K,
+        sigma, gamma, ctypes.c_uint64(seed & 0xFFFFFFFFFFFFFFFF), int(bool(antithetic)),
+        G.data_ptr(), ptr(loss), ptr(rho), ptr(reward), ptr(g), _stream_ptr(dev))
     _check(status)
     return res
 

@@ -42,6 +42,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <vector>
 
 #include "dust.h"
@@ -1900,10 +1901,75 @@ dust_status_t run_head(const void* X, const void* W, const int32_t* labels, int6
   return ok();
 }
 
+// ---------------------------------------------------------------------------
+// The workspace of dust_estimate_noalloc: a file-scope device array, one copy
+// per GPU the library runs on (the runtime places it when the code object
+// is loaded on that GPU and keeps it until the process ends).  In host code
+// `scratch` names a host-side stand-in, not a device address: the device
+// address of the current GPU's copy comes from hipGetSymbolAddress, once per
+// device, and only that address is ever handed to kernels.
+constexpr size_t kScratchBytes = size_t(DUST_NOALLOC_WORKSPACE_BYTES);
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+std::vector<void*> g_scratch_ptr;  // indexed by device ordinal; null until looked up
+
+// The device address of `scratch` on the current device (looked up on the
+// first call on that device, with it current).
+dust_status_t scratch_on_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0)
+    return fail(DUST_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr.size() <= (size_t)dev) g_scratch_ptr.resize((size_t)dev + 1, nullptr);
+  if (!g_scratch_ptr[(size_t)dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(DUST_ERR_HIP, "hipGetSymbolAddress of the static workspace failed: %s",
+                  hipGetErrorString(e));
+    g_scratch_ptr[(size_t)dev] = p;
+  }
+  *out = g_scratch_ptr[(size_t)dev];
+  return ok();
+}
+
 }  // namespace
 }  // namespace dust
 
 extern "C" {
+
+size_t dust_noalloc_workspace_capacity(void) { return dust::kScratchBytes; }
+
+dust_status_t dust_estimate_noalloc(const void* X, const void* W, const void* target, int64_t T,
+                                    int64_t d_in, int64_t d_out, int64_t seq_len, int32_t dtype,
+                                    int32_t K, float sigma, float gamma, uint64_t seed,
+                                    int32_t antithetic, float* G_W, float* loss_clean,
+                                    float* rho, float* reward, float* g, void* stream) {
+  using namespace dust;
+  // the argument checks of dust_estimate, the workspace aside (a non-null
+  // stand-in of unbounded size: the static workspace is checked next)
+  const dust_status_t st = dust_validate(X, W, target, T, d_in, d_out, seq_len, dtype, K, sigma,
+                                         gamma, antithetic, G_W, (const void*)&kScratchBytes,
+                                         (size_t)-1);
+  if (st != DUST_OK) return st;
+  const size_t need = dust_workspace_bytes(T, d_in, d_out, K, antithetic, dtype);
+  if (need > kScratchBytes)
+    return fail(DUST_ERR_UNSUPPORTED,
+                "estimate_noalloc: these sizes need %zu bytes of workspace; the static "
+                "workspace holds %zu (call dust_estimate with a workspace instead)",
+                need, kScratchBytes);
+  void* ws = nullptr;
+  const dust_status_t sp = scratch_on_current_device(&ws);
+  if (sp != DUST_OK) return sp;
+  Site site;
+  site.X = X;
+  site.W = W;
+  site.target = target;
+  return run_estimate(site, T, d_in, d_out, seq_len, dtype, K, sigma, gamma, seed, antithetic,
+                      G_W, loss_clean, rho, reward, g, ws, kScratchBytes, stream);
+}
 
 dust_status_t dust_estimate(const void* X, const void* W, const void* target, int64_t T,
                             int64_t d_in, int64_t d_out, int64_t seq_len, int32_t dtype,
