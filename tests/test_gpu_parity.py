@@ -372,6 +372,48 @@ def test_direct_to_lds_and_register_staged_paths_agree_bitwise(dev, gamma):
             assert np.array_equal(v, runs[name][k]), (name, k)
 
 
+@pytest.mark.parametrize("gamma", [0.0, 0.5])
+def test_big_tile_and_register_staged_paths_agree_bitwise(dev, gamma):
+    """A shape with enough 128 x 128 tiles for both GEMMs to take their
+    large-tile kernels (T 12010: a partial last row tile and a last token
+    split of 746 tokens, 23 whole 32-token blocks and a 10-token tail; d_in
+    1016 and d_out 1000: ragged 128-wide edge tiles and a partial last
+    64-wide k-block).  There the base GEMM writes y = W x and the noise
+    kernels (the single-generation kernel at gamma 0, the jitter-loss pass
+    at gamma 0.5) subtract the target.  Against it: the same problem with X
+    and W one element into their storage (the register-staged 64 x 64
+    kernels), and with the target one element into its storage (the noise
+    kernels' element-wise target loads).  Every output element is
+    contracted over the same k-steps in the same order, the tokens are split
+    alike and delta is the same fp32 subtraction, so every output is bitwise
+    equal."""
+    import torch
+    import token_activation_perturbation_amd as dust
+    T, d_in, d_out = 12010, 1016, 1000
+    print(f"big tiles vs staged, gamma {gamma}", flush=True)
+    inp = synth.random_inputs(T, d_in, d_out, "bf16", seed=12)
+    kw = dict(K=4, sigma=1e-2, gamma=gamma, seed=3, antithetic=True, seq_len=1201,
+              want_loss=True, want_g=True)
+
+    def place(a, shift):
+        flat = torch.zeros(a.size + 8, dtype=torch.bfloat16, device=dev)
+        flat[shift:shift + a.size] = torch.from_numpy(a.ravel()).to(dev).to(torch.bfloat16)
+        return flat[shift:shift + a.size].view(a.shape)
+
+    runs = {}
+    for name, (sx, st) in {"aligned": (0, 0), "staged": (1, 0), "target": (0, 1)}.items():
+        Xd, Wd, td = place(inp["X"], sx), place(inp["W"], sx), place(inp["target"], st)
+        out = dust.dust_estimate(Xd, Wd, td, **kw)
+        torch.cuda.synchronize(dev)
+        runs[name] = {k: v.cpu().numpy() for k, v in out.items()}
+    for name in ("staged", "target"):
+        for k, v in runs["aligned"].items():
+            assert np.array_equal(v, runs[name][k]), (name, k)
+    # and G_W is the outer product of the GPU's own g
+    G = runs["aligned"]["g"].astype(np.float64).T @ inp["X"].astype(np.float64)
+    assert rel(runs["aligned"]["G_W"].astype(np.float64), G) <= TOL["bf16"]
+
+
 @pytest.fixture(scope="module")
 def max_tokens_inputs():
     """The largest token count the library accepts, T = 2^24 - 1 = 4095 x 4097

@@ -24,6 +24,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace dust {
 namespace gemm {
 
@@ -818,6 +820,356 @@ __global__ __launch_bounds__(256) void nt_gemm_dma_kernel(
         }
       } else {
         for (int q = 0; q < 16 && q < ncols; ++q) dst[q] = src[q] - bf16_bits_to_f32(tp[q]);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// The outer product on 128 x 128 tiles (the aligned case of
+// tn_outer_dma_kernel, for problems with enough tiles per token split).
+// Each wave multiplies a 64 x 64 block: per 32-token k-block it reads 4 hi,
+// 4 lo and 4 X fragments and issues 32 MFMAs, twice the MFMAs per fragment
+// of the 64 x 64 kernel.  A 128-channel tile is held as two 64-channel
+// sub-tiles in the layout of tn_outer_dma_kernel (a token per 128-byte row,
+// chunk c of row r in slot c ^ tr_swz(r)), so wave (wm, wn) reads hi / lo
+// sub-tile wm and X sub-tile wn.  k-blocks of 32 tokens, two LDS stages of
+// 24 KiB (48 KiB: three workgroups per CU).  Per output element the
+// contraction runs over the same 32-token steps in the same order (hi, then
+// lo) as in tn_outer_dma_kernel, so for the same token split the results are
+// bitwise equal.  Edges as there: token rows past T re-read row T - 1, chunks
+// past M or N re-read the last full chunk (never stored), g rows past the
+// split's end are zeroed in LDS.
+
+// Wait for this wave's LDS reads: 12 fragments pass through the statement.
+__device__ __forceinline__ void frag_wait12(u16x8_t (&a)[4], u16x8_t (&b)[4], u16x8_t (&c)[4]) {
+  asm volatile("s_waitcnt lgkmcnt(0)"
+               : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(b[0]), "+v"(b[1]),
+                 "+v"(b[2]), "+v"(b[3]), "+v"(c[0]), "+v"(c[1]), "+v"(c[2]), "+v"(c[3]));
+}
+
+constexpr int kTnBigStage = 6 * 32 * 128;  // bytes of one LDS stage of tn_outer_big_kernel
+
+template <int NS>
+__global__ __launch_bounds__(256) void tn_outer_big_kernel(
+    const uint16_t* __restrict__ g_hi, const uint16_t* __restrict__ g_lo,
+    const uint16_t* __restrict__ X, int32_t T, int32_t M, int32_t N, int32_t tiles_m,
+    int32_t tiles_n, int32_t splits, int32_t per_xcd, int64_t t_first, int64_t t_per_split,
+    int32_t partial, float* __restrict__ out) {
+  constexpr int BK = 32, SUB = BK * 128;  // a 32-token x 64-channel sub-tile
+  constexpr int STAGE = 6 * SUB;          // hi (2), lo (2), X (2) sub-tiles
+  static_assert(STAGE == kTnBigStage, "stage size");
+  extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];  // NS * STAGE bytes
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const TileWork work = map_tile<kTnGroupM>(tiles_m, tiles_n, splits, per_xcd);
+  if (!work.valid) return;
+  const int64_t m0 = (int64_t)work.m_tile * 128;
+  const int64_t n0 = (int64_t)work.n_tile * 128;
+  const int64_t t_begin = t_first + (int64_t)work.split * t_per_split;
+  const int64_t t_end = min((int64_t)T, t_begin + t_per_split);
+  const int nk = (int)((t_end - t_begin + BK - 1) / BK);
+
+  // this lane's DMA row of every sub-tile (rows 8 wave .. + 7) and the
+  // channel offsets it fetches for each half
+  const int rq = 8 * wave + (lane >> 3);
+  const int cq = (lane & 7) ^ tr_swz(rq);
+  int64_t a_ch[2], b_ch[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int64_t am = m0 + 64 * h + 8 * cq, bn = n0 + 64 * h + 8 * cq;
+    a_ch[h] = am < M ? am : M - 8;
+    b_ch[h] = bn < N ? bn : N - 8;
+  }
+  auto issue = [&](int buf, int kt) {
+    int64_t t = t_begin + (int64_t)kt * BK + rq;
+    t = t < T ? t : (int64_t)T - 1;
+    uint8_t* base = lds + buf * STAGE + wave * 1024;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      __builtin_amdgcn_global_load_lds(g_hi + t * M + a_ch[h], (lds_void_ptr)(base + h * SUB),
+                                       16, 0, 0);
+      __builtin_amdgcn_global_load_lds(g_lo + t * M + a_ch[h],
+                                       (lds_void_ptr)(base + (2 + h) * SUB), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(X + t * N + b_ch[h], (lds_void_ptr)(base + (4 + h) * SUB),
+                                       16, 0, 0);
+    }
+  };
+
+  f32x4_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  for (int b = 0; b < NS - 1 && b < nk; ++b) issue(b, b);
+  for (int kt = 0; kt < nk; ++kt) {
+    wait_blocks<NS, 6>(min(nk - 1 - kt, NS - 2));
+    stage_barrier();
+    const int buf = kt % NS;
+    uint8_t* base = lds + buf * STAGE;
+    const int64_t left = t_end - (t_begin + (int64_t)kt * BK);
+    if (left < BK) {
+      // g rows past the split's end, in the four hi / lo sub-tiles
+      const int from = (int)(left < 0 ? 0 : left) * 128;
+      for (int o = from + 16 * tid; o < SUB; o += 16 * 256) {
+#pragma unroll
+        for (int st = 0; st < 4; ++st) *(u32x4_t*)(base + st * SUB + o) = u32x4_t{0u, 0u, 0u, 0u};
+      }
+      __syncthreads();
+    }
+    if (kt + NS - 1 < nk) issue((kt + NS - 1) % NS, kt + NS - 1);
+    u16x8_t ah[4], al[4], bf[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ah[i] = frag_sw_asm(base + wm * SUB, i * 16, 0, lane);
+      al[i] = frag_sw_asm(base + (2 + wm) * SUB, i * 16, 0, lane);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bf[j] = frag_sw_asm(base + (4 + wn) * SUB, j * 16, 0, lane);
+    frag_wait12(ah, al, bf);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc[i][j] = mfma16(ah[i], bf[j], acc[i][j]);
+        acc[i][j] = mfma16(al[i], bf[j], acc[i][j]);
+      }
+  }
+  float* dst = partial ? out + (int64_t)work.split * M * N : out;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t row = m0 + wm * 64 + i * 16 + 4 * (lane >> 4) + e;
+        const int64_t col = n0 + wn * 64 + j * 16 + (lane & 15);
+        if (row < M && col < N) dst[row * N + col] = acc[i][j][e];
+      }
+}
+
+// ---------------------------------------------------------------------------
+// The base GEMM on 128 x 128 tiles (the aligned case of nt_gemm_dma_kernel,
+// for problems with enough tiles to fill the chip twice over).  Each wave
+// multiplies a 64 x 64 block (4 x 4 MFMA tiles), so every operand fragment
+// read from LDS feeds four MFMAs instead of two: half the LDS and L2 bytes
+// per flop of the 64 x 64 kernel.  Two LDS stages of 32 KiB (64 KiB): two
+// workgroups share a CU, so one's epilogue overlaps the other's k loop
+// (NS stages: the LDS is dynamic, NS x 32 KiB).
+// Same per-element contraction order as nt_gemm_dma_kernel (k-blocks of 64
+// in order, two MFMA k-steps each), so the results are bitwise equal.  With a
+// target, the epilogue stages the tile through LDS one 64-row half at a
+// time (row pitch 132 floats), then each thread subtracts the target from
+// 32 consecutive columns of one row and stores them in 16-byte pieces.
+constexpr int kNtBigStage = 2 * 128 * 128;  // bytes of one LDS stage of nt_gemm_big_kernel
+
+template <bool TARGET, int NS>
+__global__ __launch_bounds__(256) void nt_gemm_big_kernel(
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, int64_t lda, int64_t ldb,
+    int32_t M, int32_t N, int64_t K, int32_t tiles_m, int32_t tiles_n, int32_t per_xcd,
+    const uint16_t* __restrict__ target, float* __restrict__ out) {
+  constexpr int BM = 128, BN = 128, BK = 64;
+  constexpr int TBA = BM * 128, TBB = BN * 128, STAGE = TBA + TBB;
+  static_assert(STAGE == kNtBigStage, "stage size");
+  constexpr int QA = BM / 32, QB = BN / 32;  // DMA instructions per wave and block
+  constexpr int FI = BM / 32, FJ = BN / 32;  // MFMA tiles per wave (64 x 64 block)
+  extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];  // NS * STAGE bytes
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const TileWork work = map_tile<kNtGroupM>(tiles_m, tiles_n, 1, per_xcd);
+  if (!work.valid) return;
+  const int64_t m0 = (int64_t)work.m_tile * BM;
+  const int64_t n0 = (int64_t)work.n_tile * BN;
+  const int nk = (int)((K + BK - 1) / BK);
+
+  // this lane's DMA rows and the chunk it fetches for them
+  int cka[QA], ckb[QB];
+  int64_t a_row[QA], b_row[QB];
+#pragma unroll
+  for (int q = 0; q < QA; ++q) {
+    const int r = 8 * (QA * wave + q) + (lane >> 3);
+    cka[q] = (lane & 7) ^ nt_swz(r);
+    a_row[q] = m0 + r < M ? m0 + r : M - 1;
+  }
+#pragma unroll
+  for (int q = 0; q < QB; ++q) {
+    const int r = 8 * (QB * wave + q) + (lane >> 3);
+    ckb[q] = (lane & 7) ^ nt_swz(r);
+    b_row[q] = n0 + r < N ? n0 + r : N - 1;
+  }
+  auto issue = [&](int buf, int kt) {
+    uint8_t* base = lds + buf * STAGE;
+#pragma unroll
+    for (int q = 0; q < QA; ++q) {
+      int64_t k = (int64_t)kt * BK + 8 * cka[q];
+      k = k < K ? k : K - 8;
+      __builtin_amdgcn_global_load_lds(A + a_row[q] * lda + k,
+                                       (lds_void_ptr)(base + (QA * wave + q) * 1024), 16, 0, 0);
+    }
+#pragma unroll
+    for (int q = 0; q < QB; ++q) {
+      int64_t k = (int64_t)kt * BK + 8 * ckb[q];
+      k = k < K ? k : K - 8;
+      __builtin_amdgcn_global_load_lds(B + b_row[q] * ldb + k,
+                                       (lds_void_ptr)(base + TBA + (QB * wave + q) * 1024), 16,
+                                       0, 0);
+    }
+  };
+
+  f32x4_t acc[FI][FJ];
+#pragma unroll
+  for (int i = 0; i < FI; ++i)
+#pragma unroll
+    for (int j = 0; j < FJ; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // A's chunks past K re-read the last chunk: zero them in the block at
+  // `base` (the last one, when K is not a multiple of 64)
+  auto zero_tail = [&](uint8_t* base, int64_t left) {
+#pragma unroll
+    for (int h = 0; h < BM / 64; ++h) {
+      const int row = (tid >> 2) + 64 * h;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int slot = 2 * (tid & 3) + e;
+        if (8 * (slot ^ nt_swz(row)) >= left)
+          *(u32x4_t*)(base + row * 128 + 16 * slot) = u32x4_t{0u, 0u, 0u, 0u};
+      }
+    }
+    __syncthreads();
+  };
+  // the operand fragments of k-step ks (0 or 32) of the block at `base`
+  auto read_frags = [&](const uint8_t* base, int ks, u16x8_t (&af)[FI], u16x8_t (&bf)[FJ]) {
+    const int ch = ks / 8 + (lane >> 4);
+#pragma unroll
+    for (int i = 0; i < FI; ++i) {
+      const int r = wm * 64 + i * 16 + (lane & 15);
+      af[i] = *(const u16x8_t*)(base + r * 128 + 16 * (ch ^ nt_swz(r)));
+    }
+#pragma unroll
+    for (int j = 0; j < FJ; ++j) {
+      const int r = wn * 64 + j * 16 + (lane & 15);
+      bf[j] = *(const u16x8_t*)(base + TBA + r * 128 + 16 * (ch ^ nt_swz(r)));
+    }
+  };
+  auto mma = [&](const u16x8_t (&af)[FI], const u16x8_t (&bf)[FJ]) {
+#pragma unroll
+    for (int i = 0; i < FI; ++i)
+#pragma unroll
+      for (int j = 0; j < FJ; ++j) acc[i][j] = mfma16(af[i], bf[j], acc[i][j]);
+  };
+  // the scheduler is asked to alternate two MFMAs with one LDS read, so the
+  // next k-step's fragments arrive while this one's MFMAs run
+  auto interleave = [&]() {
+#pragma unroll
+    for (int u = 0; u < FI + FJ; ++u) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+    }
+  };
+
+  // Software pipeline over k-steps of 32: the fragments of the next k-step
+  // are read while the MFMAs of the current one run.  Per block kt: read
+  // (kt, 32) while multiplying (kt, 0); then wait for block kt + 1, meet at
+  // the barrier (block kt is no longer read: its buffer takes block kt + NS),
+  // and read (kt + 1, 0) while multiplying (kt, 32).  Blocks kt + 1 ..
+  // kt + NS - 1 are in flight while block kt is multiplied.
+  for (int b = 0; b < NS - 1 && b < nk; ++b) issue(b, b);
+  wait_blocks<NS, QA + QB>(min(nk - 1, NS - 2));
+  stage_barrier();
+  if (K < BK) zero_tail(lds, K);
+  if (NS - 1 < nk) issue(NS - 1, NS - 1);
+  u16x8_t f0a[FI], f0b[FJ], f1a[FI], f1b[FJ];
+  read_frags(lds, 0, f0a, f0b);
+  // one block; NEXT: block kt + 1 exists (TAIL: it is the last, possibly
+  // partial one); the steady-state body (NEXT, not TAIL) has no branch
+  // between its LDS reads and their MFMAs, so each wait covers only the
+  // fragments it needs
+  auto step = [&](int kt, auto next_c, auto tail_c) {
+    constexpr bool NEXT = decltype(next_c)::value, TAIL = decltype(tail_c)::value;
+    uint8_t* base = lds + (kt % NS) * STAGE;
+    read_frags(base, 32, f1a, f1b);
+    mma(f0a, f0b);
+    interleave();
+    if constexpr (NEXT) {
+      wait_blocks<NS, QA + QB>(min(nk - 2 - kt, NS - 2));
+      stage_barrier();
+      uint8_t* next = lds + ((kt + 1) % NS) * STAGE;
+      if constexpr (TAIL) {
+        const int64_t left = K - (int64_t)(kt + 1) * BK;
+        if (left < BK) zero_tail(next, left);
+      }
+      if (kt + NS < nk) issue(kt % NS, kt + NS);
+      read_frags(next, 0, f0a, f0b);
+    }
+    mma(f1a, f1b);
+    interleave();
+  };
+  using yes = std::true_type;
+  using no = std::false_type;
+  int kt = 0;
+  for (; kt + 2 < nk; ++kt) step(kt, yes{}, no{});
+  if (kt + 1 < nk) step(kt++, yes{}, yes{});
+  step(kt, no{}, no{});
+  if constexpr (!TARGET) {
+#pragma unroll
+    for (int i = 0; i < FI; ++i)
+#pragma unroll
+      for (int j = 0; j < FJ; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int64_t row = m0 + wm * 64 + i * 16 + 4 * (lane >> 4) + e;
+          const int64_t col = n0 + wn * 64 + j * 16 + (lane & 15);
+          if (row < M && col < N) out[row * N + col] = acc[i][j][e];
+        }
+  } else {
+    constexpr int CP = BN + 4;  // 64 rows x 132 floats = 33 KiB of the NS x 32 KiB
+    float* ct = (float*)lds;
+    const int er = tid >> 2, ec0 = (tid & 3) * 32;
+    const bool vec_ok =
+        (N & 7) == 0 && (((uintptr_t)target | (uintptr_t)out) & 15) == 0;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      __syncthreads();  // the operand tiles (h = 0) or the last half are no longer read
+      if (wm == h) {
+#pragma unroll
+        for (int i = 0; i < FI; ++i)
+#pragma unroll
+          for (int j = 0; j < FJ; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              ct[(i * 16 + 4 * (lane >> 4) + e) * CP + wn * 64 + j * 16 + (lane & 15)] =
+                  acc[i][j][e];
+      }
+      __syncthreads();
+      const int64_t row = m0 + 64 * h + er;
+      if (row < M) {
+        const float* src = ct + er * CP + ec0;
+        float* dst = out + row * N + n0 + ec0;
+        const uint16_t* tp = target + row * N + n0 + ec0;
+        const int64_t ncols = N - (n0 + ec0);
+        if (vec_ok && ncols >= 32) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const u32x4_t tw = *(const u32x4_t*)(tp + 8 * q);
+            float4 v0 = *(const float4*)(src + 8 * q);
+            float4 v1 = *(const float4*)(src + 8 * q + 4);
+            v0.x -= __uint_as_float(tw[0] << 16);
+            v0.y -= __uint_as_float(tw[0] & 0xFFFF0000u);
+            v0.z -= __uint_as_float(tw[1] << 16);
+            v0.w -= __uint_as_float(tw[1] & 0xFFFF0000u);
+            v1.x -= __uint_as_float(tw[2] << 16);
+            v1.y -= __uint_as_float(tw[2] & 0xFFFF0000u);
+            v1.z -= __uint_as_float(tw[3] << 16);
+            v1.w -= __uint_as_float(tw[3] & 0xFFFF0000u);
+            *(float4*)(dst + 8 * q) = v0;
+            *(float4*)(dst + 8 * q + 4) = v1;
+          }
+        } else {
+          for (int q = 0; q < 32 && q < ncols; ++q) dst[q] = src[q] - bf16_bits_to_f32(tp[q]);
+        }
       }
     }
   }

@@ -207,6 +207,36 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// delta_t's channels c .. c + 3 from the row `drow` the base GEMM wrote:
+// that row itself, or, when the bf16 target's row `trow` is given (the GEMM
+// then wrote y = W x alone), y - target formed here, the same fp32
+// subtraction the GEMM's epilogue would have made.  `vec`: all four
+// channels in range, drow 16-byte and trow 8-byte aligned; otherwise
+// channels past d_out read 0.
+__device__ __forceinline__ float4 load_delta4(const float* __restrict__ drow,
+                                              const uint16_t* __restrict__ trow, int c,
+                                              int d_out, bool vec) {
+  float4 d;
+  if (vec) {
+    d = *(const float4*)(drow + c);
+    if (trow) {
+      const uint2 tv = *(const uint2*)(trow + c);
+      d.x -= __uint_as_float(tv.x << 16);
+      d.y -= __uint_as_float(tv.x & 0xFFFF0000u);
+      d.z -= __uint_as_float(tv.y << 16);
+      d.w -= __uint_as_float(tv.y & 0xFFFF0000u);
+    }
+  } else {
+    float v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      v[e] = (c + e < d_out) ? (trow ? drow[c + e] - bf16_to_f32(trow[c + e]) : drow[c + e])
+                             : 0.f;
+    d = make_float4(v[0], v[1], v[2], v[3]);
+  }
+  return d;
+}
+
 // ---------------------------------------------------------------------------
 // Jitter + loss change.  One wave per (token t, chunk of noise indices).
 // Lane l owns the channel quads q = l + 64 j of the token.  For a batch of 16
@@ -216,9 +246,9 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 template <bool QN>
 __global__ __launch_bounds__(256) void jitter_loss_kernel(
-    const float* __restrict__ delta, int32_t vec, int32_t T, int32_t d_out, int32_t nq,
-    int32_t K_n, int32_t chunks, int32_t per_chunk, NoiseKey key, float* __restrict__ P,
-    float* __restrict__ Q, float* __restrict__ loss_clean) {
+    const float* __restrict__ delta, const uint16_t* __restrict__ tgt, int32_t vec, int32_t T,
+    int32_t d_out, int32_t nq, int32_t K_n, int32_t chunks, int32_t per_chunk, NoiseKey key,
+    float* __restrict__ P, float* __restrict__ Q, float* __restrict__ loss_clean) {
   const int lane = threadIdx.x & 63;
   const int64_t task = (int64_t)blockIdx.x * 4 + wave_id();
   if (task >= (int64_t)T * chunks) return;
@@ -227,11 +257,15 @@ __global__ __launch_bounds__(256) void jitter_loss_kernel(
   const int32_t n_begin = chunk * per_chunk;
   const int32_t n_end = min(K_n, n_begin + per_chunk);
   const float* drow = delta + (int64_t)t * d_out;
-  const bool ragged = !vec;  // vec: d_out % 4 == 0 and delta 16-byte aligned
+  const uint16_t* trow = tgt ? tgt + (int64_t)t * d_out : nullptr;
+  const bool ragged = !vec;  // vec: d_out % 4 == 0, delta (and target) aligned
 
   if (chunk == 0 && loss_clean) {
     float s = 0.f;
-    for (int32_t c = lane; c < d_out; c += 64) s = __builtin_fmaf(drow[c], drow[c], s);
+    for (int32_t c = lane; c < d_out; c += 64) {
+      const float dc = trow ? drow[c] - bf16_to_f32(trow[c]) : drow[c];
+      s = __builtin_fmaf(dc, dc, s);
+    }
     s = wave_sum(s);
     if (lane == 0) loss_clean[t] = 0.5f * s;
   }
@@ -244,16 +278,10 @@ __global__ __launch_bounds__(256) void jitter_loss_kernel(
       s[j] = 0.f;
     }
     for (int32_t q = lane; q < nq; q += 64) {
-      float4 d;
+      const float4 d = load_delta4(drow, trow, 4 * q, d_out, !ragged);
       float4 m = make_float4(1.f, 1.f, 1.f, 1.f);
-      if (!ragged) {
-        d = *(const float4*)(drow + 4 * q);
-      } else {
+      if (ragged) {
         const int c = 4 * q;
-        d.x = drow[c];
-        d.y = (c + 1 < d_out) ? drow[c + 1] : 0.f;
-        d.z = (c + 2 < d_out) ? drow[c + 2] : 0.f;
-        d.w = (c + 3 < d_out) ? drow[c + 3] : 0.f;
         m.y = (c + 1 < d_out) ? 1.f : 0.f;
         m.z = (c + 2 < d_out) ? 1.f : 0.f;
         m.w = (c + 3 < d_out) ? 1.f : 0.f;
@@ -767,7 +795,8 @@ __device__ __forceinline__ void wave_reduce_to_scalars(float (&v)[M], int lane, 
 // bit those of the QN = true kernel.
 template <int QPL, bool ANTI, bool FULL, bool QN = true>
 __global__ __launch_bounds__(256) void fused_g0_kernel(
-    const float* __restrict__ delta, int32_t t0, int32_t d_out, int32_t K, int32_t K_n, int32_t per_wave, float sigma, float curv_coef, NoiseKey key,
+    const float* __restrict__ delta, const uint16_t* __restrict__ tgt, int32_t t0, int32_t d_out,
+    int32_t K, int32_t K_n, int32_t per_wave, float sigma, float curv_coef, NoiseKey key,
     float* __restrict__ Pout, float* __restrict__ Qout, float* __restrict__ loss_clean,
     float* __restrict__ g32, uint16_t* __restrict__ g_hi, uint16_t* __restrict__ g_lo) {
   constexpr int NB = QPL <= 2 ? DUST_FUSED_NB_SMALL : (QPL <= 4 ? 2 : 1);
@@ -780,6 +809,7 @@ __global__ __launch_bounds__(256) void fused_g0_kernel(
   const int32_t n_begin = wave * per_wave;
   const int32_t n_end = min(K_n, n_begin + per_wave);
   const float* drow = delta + (int64_t)t * d_out;
+  const uint16_t* trow = tgt ? tgt + (int64_t)t * d_out : nullptr;
 
   float4 d[QPL], msk[QPL], A[QPL], S[QPL];
 #pragma unroll
@@ -788,14 +818,10 @@ __global__ __launch_bounds__(256) void fused_g0_kernel(
     const int c = 4 * q;
     A[j] = make_float4(0.f, 0.f, 0.f, 0.f);
     S[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+    d[j] = load_delta4(drow, trow, c, d_out, FULL);
     if (FULL) {
-      d[j] = *(const float4*)(drow + c);
       msk[j] = make_float4(1.f, 1.f, 1.f, 1.f);
     } else {
-      d[j].x = (c < d_out) ? drow[c] : 0.f;
-      d[j].y = (c + 1 < d_out) ? drow[c + 1] : 0.f;
-      d[j].z = (c + 2 < d_out) ? drow[c + 2] : 0.f;
-      d[j].w = (c + 3 < d_out) ? drow[c + 3] : 0.f;
       msk[j].x = (c < d_out) ? 1.f : 0.f;
       msk[j].y = (c + 1 < d_out) ? 1.f : 0.f;
       msk[j].z = (c + 2 < d_out) ? 1.f : 0.f;
@@ -954,7 +980,8 @@ __global__ __launch_bounds__(256) void fused_g0_kernel(
 
 template <int QPL, bool FULL>
 __global__ __launch_bounds__(1024) void chain_g_kernel(
-    const float* __restrict__ delta, int32_t T, int32_t d_out, int32_t seq_len, int32_t K_n,
+    const float* __restrict__ delta, const uint16_t* __restrict__ tgt, int32_t T, int32_t d_out,
+    int32_t seq_len, int32_t K_n,
     int32_t groups, float gamma, NoiseKey key, float* __restrict__ loss_clean,
     float* __restrict__ part) {
   constexpr int NQ = 64 * QPL;
@@ -970,19 +997,13 @@ __global__ __launch_bounds__(1024) void chain_g_kernel(
   for (int32_t tt = seq_len - 1; tt >= 0; --tt) {
     const int32_t t = t_first + tt;
     const float* drow = delta + (int64_t)t * d_out;
+    const uint16_t* trow = tgt ? tgt + (int64_t)t * d_out : nullptr;
     float4 d[QPL], a[QPL];
     float p = 0.f;
 #pragma unroll
     for (int j = 0; j < QPL; ++j) {
       const int c = 4 * (lane + 64 * j);
-      if (FULL) {
-        d[j] = *(const float4*)(drow + c);
-      } else {
-        d[j].x = (c < d_out) ? drow[c] : 0.f;
-        d[j].y = (c + 1 < d_out) ? drow[c + 1] : 0.f;
-        d[j].z = (c + 2 < d_out) ? drow[c + 2] : 0.f;
-        d[j].w = (c + 3 < d_out) ? drow[c + 3] : 0.f;
-      }
+      d[j] = load_delta4(drow, trow, c, d_out, FULL);
       a[j] = noise_quad((uint32_t)(lane + 64 * j), (uint32_t)t, (uint32_t)n, key);
       p = __builtin_fmaf(d[j].x, a[j].x, p);
       p = __builtin_fmaf(d[j].y, a[j].y, p);
@@ -1404,14 +1425,15 @@ inline TimedLaunch stamp(const char* name, double flops, double bytes,
 
 template <int QPL>
 void launch_fused_g0_qpl(bool anti, bool full, unsigned blocks, unsigned threads,
-                         hipStream_t s, TimedLaunch tl, const float* delta, int32_t t0,
+                         hipStream_t s, TimedLaunch tl, const float* delta, const uint16_t* tgt,
+                         int32_t t0,
                          int32_t d_out, int32_t K, int32_t K_n, int32_t per_wave, float sigma,
                          float curv, NoiseKey key, float* P, float* Q, float* loss, float* g32,
                          uint16_t* g_hi, uint16_t* g_lo) {
 #define DUST_FUSED_LAUNCH(A, F, QN)                                                           \
   hipExtLaunchKernelGGL((fused_g0_kernel<QPL, A, F, QN>), dim3(blocks), dim3(threads), 0, s,  \
-                        tl.start, tl.stop, 0, delta, t0, d_out, K, K_n, per_wave, sigma, curv, \
-                        key, P, Q, loss, g32, g_hi, g_lo)
+                        tl.start, tl.stop, 0, delta, tgt, t0, d_out, K, K_n, per_wave, sigma,   \
+                        curv, key, P, Q, loss, g32, g_hi, g_lo)
   // Q is needed when the loss has a curvature term, by plain draws and by the
   // per-draw outputs (P != nullptr)
   const bool need_q = curv != 0.0f && (!anti || P != nullptr);
@@ -1436,13 +1458,14 @@ inline int fused_qpl(int32_t nq) {
 }
 
 void launch_fused_g0(int qpl, bool anti, bool full, unsigned blocks, unsigned threads,
-                     hipStream_t s, TimedLaunch tl, const float* delta, int32_t t0,
+                     hipStream_t s, TimedLaunch tl, const float* delta, const uint16_t* tgt,
+                     int32_t t0,
                      int32_t d_out, int32_t K, int32_t K_n, int32_t per_wave, float sigma,
                      float curv, NoiseKey key, float* P, float* Q, float* loss, float* g32,
                      uint16_t* g_hi, uint16_t* g_lo) {
 #define DUST_FUSED_CASE(V)                                                                   \
   case V:                                                                                    \
-    launch_fused_g0_qpl<V>(anti, full, blocks, threads, s, tl, delta, t0, d_out, K, K_n,     \
+    launch_fused_g0_qpl<V>(anti, full, blocks, threads, s, tl, delta, tgt, t0, d_out, K, K_n, \
                            per_wave, sigma, curv, key, P, Q, loss, g32, g_hi, g_lo);         \
     break;
   switch (qpl) {
@@ -1460,6 +1483,15 @@ void launch_fused_g0(int qpl, bool anti, bool full, unsigned blocks, unsigned th
 #undef DUST_FUSED_CASE
 }
 
+// LDS stages of the 128 x 128 GEMM kernels (-DDUST_NT_BIG_STAGES=n,
+// -DDUST_TN_BIG_STAGES=n at build time; 2 to 4).
+#ifndef DUST_NT_BIG_STAGES
+#define DUST_NT_BIG_STAGES 2
+#endif
+#ifndef DUST_TN_BIG_STAGES
+#define DUST_TN_BIG_STAGES 2
+#endif
+
 // Register stages of the outer product's load pipeline (even; a build may
 // override it with -DDUST_TN_STAGES=n).
 #ifndef DUST_TN_STAGES
@@ -1475,8 +1507,8 @@ inline unsigned grid_for(int64_t items, int64_t per_block) {
 }
 
 // y = X W^T (- target when target != nullptr) -> out [T][d_out] fp32.
-void launch_base_gemm(const void* X, const void* W, const void* target, int64_t T, int64_t d_in,
-                      int64_t d_out, int32_t dtype, float* out, hipStream_t s) {
+void launch_base_gemm(const Plan& p, const void* X, const void* W, const void* target, int64_t T,
+                      int64_t d_in, int64_t d_out, int32_t dtype, float* out, hipStream_t s) {
   const int32_t Ti = (int32_t)T, di = (int32_t)d_in, dout = (int32_t)d_out;
   const double es = dtype == DUST_BF16 ? 2.0 : 4.0;
   const TimedLaunch ev =
@@ -1485,7 +1517,9 @@ void launch_base_gemm(const void* X, const void* W, const void* target, int64_t 
                 4.0 * T * d_out);
   if (dtype == DUST_BF16) {
     const bool vec = (d_in % 8 == 0) && ((uintptr_t)X % 16 == 0) && ((uintptr_t)W % 16 == 0);
-    const int tiles_m = (int)ceil_div(T, 64), tiles_n = (int)ceil_div(d_out, 64);
+    const bool big = vec && p.base_big;
+    const int tb = big ? 128 : 64;
+    const int tiles_m = (int)ceil_div(T, tb), tiles_n = (int)ceil_div(d_out, tb);
     const int per_xcd = (int)ceil_div((int64_t)tiles_m * tiles_n, 8);
     const dim3 grid((unsigned)(8 * per_xcd));
     // aligned operands: the direct-to-LDS kernel; else guarded loads
@@ -1493,13 +1527,20 @@ void launch_base_gemm(const void* X, const void* W, const void* target, int64_t 
   DUST_LAUNCH(ev, KERNEL, grid, dim3(256), 0, s, (const uint16_t*)X, (const uint16_t*)W,        \
               (int64_t)d_in, (int64_t)d_in, Ti, dout, (int64_t)d_in, tiles_m, tiles_n, per_xcd, \
               (const uint16_t*)target, out)
+#define DUST_BASE_GEMM_BIG(KERNEL)                                                            \
+  DUST_LAUNCH(ev, KERNEL, grid, dim3(256), (size_t)DUST_NT_BIG_STAGES * gemm::kNtBigStage, s,   \
+              (const uint16_t*)X, (const uint16_t*)W, (int64_t)d_in, (int64_t)d_in, Ti, dout,  \
+              (int64_t)d_in, tiles_m, tiles_n, per_xcd, (const uint16_t*)target, out)
     if (target) {
-      if (vec) DUST_BASE_GEMM((gemm::nt_gemm_dma_kernel<true>));
+      if (big) DUST_BASE_GEMM_BIG((gemm::nt_gemm_big_kernel<true, DUST_NT_BIG_STAGES>));
+      else if (vec) DUST_BASE_GEMM((gemm::nt_gemm_dma_kernel<true>));
       else DUST_BASE_GEMM((gemm::nt_gemm_kernel<4, true>));
     } else {
-      if (vec) DUST_BASE_GEMM((gemm::nt_gemm_dma_kernel<false>));
+      if (big) DUST_BASE_GEMM_BIG((gemm::nt_gemm_big_kernel<false, DUST_NT_BIG_STAGES>));
+      else if (vec) DUST_BASE_GEMM((gemm::nt_gemm_dma_kernel<false>));
       else DUST_BASE_GEMM((gemm::nt_gemm_kernel<4, false>));
     }
+#undef DUST_BASE_GEMM_BIG
 #undef DUST_BASE_GEMM
   } else {
     const int tiles_n = (int)ceil_div(d_out, 64);
@@ -1512,7 +1553,8 @@ void launch_base_gemm(const void* X, const void* W, const void* target, int64_t 
 // The chain path's two kernels (single generation, gamma > 0, antithetic
 // pairs): partial g per pair group, then their sum scaled by 2 / K.
 void launch_chain(const Plan& p, const ChainPlan& cp, int64_t seq_len, float gamma,
-                  NoiseKey key, const float* delta, bool delta_vec, float* loss_clean,
+                  NoiseKey key, const float* delta, const uint16_t* tgt, bool delta_vec,
+                  float* loss_clean,
                   float* part, float* g32, uint16_t* g_hi, uint16_t* g_lo, hipStream_t s,
                   TimedLaunch tl) {
   const int qpl = fused_qpl(p.nq);
@@ -1523,9 +1565,11 @@ void launch_chain(const Plan& p, const ChainPlan& cp, int64_t seq_len, float gam
   const int32_t Ti = (int32_t)p.T, dout = (int32_t)p.d_out, sl = (int32_t)seq_len;
   const double td = (double)p.T * p.d_out;
   const TimedLaunch ev = stamp("chain_g_kernel", 0.0,
-                               4.0 * td * (1.0 + cp.groups) + (loss_clean ? 4.0 * p.T : 0.0), tl);
+                               4.0 * td * (1.0 + cp.groups) + (tgt ? 2.0 * td : 0.0) +
+                                   (loss_clean ? 4.0 * p.T : 0.0),
+                               tl);
 #define DUST_CHAIN(Q, F)                                                                        \
-  DUST_LAUNCH(ev, (chain_g_kernel<Q, F>), grid, block, lds, s, delta, Ti, dout, sl, p.K_n,      \
+  DUST_LAUNCH(ev, (chain_g_kernel<Q, F>), grid, block, lds, s, delta, tgt, Ti, dout, sl, p.K_n, \
               cp.groups, gamma, key, loss_clean, part)
 #define DUST_CHAIN_Q(Q)               \
   case Q:                             \
@@ -1572,11 +1616,18 @@ void launch_outer(const Plan& p, const void* X, const float* g32, const uint16_t
     // and g_lo 16-byte aligned when d_out is a multiple of 8)
     const bool vec = (d_in % 8 == 0) && (d_out % 8 == 0) && ((uintptr_t)X % 16 == 0) &&
                      ((uintptr_t)g_hi % 16 == 0) && ((uintptr_t)g_lo % 16 == 0);
-    const int tiles_m = (int)ceil_div(d_out, 64), tiles_n = (int)ceil_div(d_in, 64);
+    const bool big = vec && p.outer_big;
+    const int tb = big ? 128 : 64;
+    const int tiles_m = (int)ceil_div(d_out, tb), tiles_n = (int)ceil_div(d_in, tb);
     const int per_xcd = (int)ceil_div((int64_t)tiles_m * tiles_n * p.outer_split, 8);
     const dim3 grid((unsigned)(8 * per_xcd));
     const int32_t partial = p.outer_split > 1 ? 1 : 0;
-    if (vec)
+    if (big)
+      DUST_LAUNCH(ev, gemm::tn_outer_big_kernel<DUST_TN_BIG_STAGES>, grid, dim3(256),
+                  (size_t)DUST_TN_BIG_STAGES * gemm::kTnBigStage, s, (const uint16_t*)g_hi,
+                  (const uint16_t*)g_lo, (const uint16_t*)X, Ti, dout, di, tiles_m, tiles_n,
+                  p.outer_split, per_xcd, (int64_t)0, (int64_t)p.outer_tokens, partial, dst);
+    else if (vec)
       DUST_LAUNCH(ev, gemm::tn_outer_dma_kernel, grid, dim3(256), 0, s, (const uint16_t*)g_hi,
                   (const uint16_t*)g_lo, (const uint16_t*)X, Ti, dout, di, tiles_m, tiles_n,
                   p.outer_split, per_xcd, (int64_t)0, (int64_t)p.outer_tokens, partial, dst);
@@ -1727,7 +1778,28 @@ dust_status_t run_estimate(const Site& st, int64_t T, int64_t d_in, int64_t d_ou
   // rho's curvature term: sigma^2 / 2 for the quadratic loss, none for the
   // linear local score
   const float curv = local ? 0.0f : 0.5f * sigma * sigma;
-  const bool delta_vec = (d_out % 4 == 0) && ((uintptr_t)delta % 16 == 0);
+  const int qpl = fused_qpl(p.nq);
+  const bool independent = (gamma == 0.0f || seq_len == 1);
+  const bool fused = independent && qpl > 0;
+  const bool want_pq = rho != nullptr || reward != nullptr;
+  // single generation for gamma > 0 with antithetic pairs, when the caller's
+  // workspace holds the groups' partial g and no per-draw output is asked for
+  const ChainPlan cp = embed ? ChainPlan{} : make_chain_plan(p, seq_len, gamma);
+  const bool chain = !fused && cp.ok && !want_pq && workspace_bytes >= cp.total;
+  // Where the bf16 layer's base GEMM runs on 128 x 128 tiles, it writes
+  // y = W x alone and the noise kernels that read delta (the single-
+  // generation kernel, the jitter-loss pass) subtract the target themselves,
+  // the same fp32 subtraction: the GEMM's epilogue then moves a third fewer
+  // bytes, and those kernels, bound by their ALU work, read 2 more bytes per
+  // value at no cost.  The chain path, which walks one token per step behind
+  // a barrier, would pay the extra load's latency at every step, so there
+  // (and on the small layers, the fp32 path, local scoring and embeddings)
+  // delta is formed in the GEMM as before.
+  const uint16_t* tgt16 = (!local && !embed && dtype == DUST_BF16 && p.base_big && !chain)
+                              ? (const uint16_t*)st.target
+                              : nullptr;
+  const bool delta_vec = (d_out % 4 == 0) && ((uintptr_t)delta % 16 == 0) &&
+                         ((uintptr_t)tgt16 % 8 == 0);
   float* Pbuf = (float*)(ws + p.off_P);
   float* Qbuf = (float*)(ws + p.off_Q);
   float* rho_buf = rho ? rho : (float*)(ws + p.off_rho);
@@ -1750,40 +1822,34 @@ dust_status_t run_estimate(const Site& st, int64_t T, int64_t d_in, int64_t d_ou
   if (embed)
     launch_gather(st.W, st.ids, st.target, T, st.V, d_out, dtype, delta, s);
   else if (!local)
-    launch_base_gemm(st.X, st.W, st.target, T, d_in, d_out, dtype, delta, s);
-  const int qpl = fused_qpl(p.nq);
-  const bool independent = (gamma == 0.0f || seq_len == 1);
-  const bool fused = independent && qpl > 0;
-  const bool want_pq = rho != nullptr || reward != nullptr;
+    launch_base_gemm(p, st.X, st.W, tgt16 ? nullptr : st.target, T, d_in, d_out, dtype, delta,
+                     s);
   // Q = ||a||^2 only where the loss has a curvature term (not local scoring)
   float* const Qused = curv != 0.0f ? Qbuf : nullptr;
   const TimedLaunch tl = take_timing_events();
-  // single generation for gamma > 0 with antithetic pairs, when the caller's
-  // workspace holds the groups' partial g and no per-draw output is asked for
-  const ChainPlan cp = embed ? ChainPlan{} : make_chain_plan(p, seq_len, gamma);
-  const bool chain = !fused && cp.ok && !want_pq && workspace_bytes >= cp.total;
 
   // algorithmic bytes of the per-draw stages: P (and Q) per (t, n), rho
   // and the credit per (t, i), the weights per (t, n)
   const double tkn = (double)T * p.K_n, tk = (double)T * K, td = (double)T * d_out;
   const double pq_b = 4.0 * tkn * (Qused ? 2.0 : 1.0);
   const double g_out_b = (g32 ? 4.0 * td : 0.0) + (g_hi ? 4.0 * td : 0.0);
+  const double delta_b = 4.0 * td + (tgt16 ? 2.0 * td : 0.0);  // y (or delta) and the target
   const double stats_b = pq_b + 4.0 * tk + 4.0 * T;
   const double credit_b = 4.0 * tk + 4.0 * T + (reward ? 4.0 * tk : 0.0) + 4.0 * tkn;
   if (chain) {
-    launch_chain(p, cp, seq_len, gamma, key, (const float*)delta, delta_vec, loss_clean,
+    launch_chain(p, cp, seq_len, gamma, key, (const float*)delta, tgt16, delta_vec, loss_clean,
                  (float*)(ws + cp.off_part), g32, g_hi, g_lo, s, tl);
   } else if (!fused) {
     // 2. jitter + loss change
     const TimedLaunch evj =
-        stamp("jitter_loss_kernel", 0.0, 4.0 * td + pq_b + (loss_clean ? 4.0 * T : 0.0), tl);
+        stamp("jitter_loss_kernel", 0.0, delta_b + pq_b + (loss_clean ? 4.0 * T : 0.0), tl);
     if (Qused)
       DUST_LAUNCH(evj, jitter_loss_kernel<true>, dim3(grid_for(T * p.jl_chunks, 4)), dim3(256), 0,
-                  s, (const float*)delta, (int32_t)delta_vec, Ti, dout, p.nq, p.K_n, p.jl_chunks,
-                  p.jl_per_chunk, key, Pbuf, Qused, loss_clean);
+                  s, (const float*)delta, tgt16, (int32_t)delta_vec, Ti, dout, p.nq, p.K_n,
+                  p.jl_chunks, p.jl_per_chunk, key, Pbuf, Qused, loss_clean);
     else
       DUST_LAUNCH(evj, jitter_loss_kernel<false>, dim3(grid_for(T * p.jl_chunks, 4)), dim3(256),
-                  0, s, (const float*)delta, (int32_t)delta_vec, Ti, dout, p.nq, p.K_n,
+                  0, s, (const float*)delta, tgt16, (int32_t)delta_vec, Ti, dout, p.nq, p.K_n,
                   p.jl_chunks, p.jl_per_chunk, key, Pbuf, Qused, loss_clean);
     // 3. loss reductions and their mean over draws
     DUST_LAUNCH(stamp("token_stats_kernel", 0.0, stats_b), token_stats_kernel,
@@ -1825,9 +1891,9 @@ dust_status_t run_estimate(const Site& st, int64_t T, int64_t d_in, int64_t d_ou
     const bool full = (p.nq == 64 * qpl) && delta_vec;
     const TimedLaunch evf = stamp(
         "fused_g0_kernel", 0.0,
-        4.0 * td + g_out_b + (loss_clean ? 4.0 * T : 0.0) + (want_pq ? pq_b : 0.0), tl);
+        delta_b + g_out_b + (loss_clean ? 4.0 * T : 0.0) + (want_pq ? pq_b : 0.0), tl);
     launch_fused_g0(qpl, p.antithetic != 0, full, (unsigned)T, (unsigned)(64 * p.fz_waves), s,
-                    evf, (const float*)delta, 0, dout, K, p.K_n, p.fz_per_wave, sigma,
+                    evf, (const float*)delta, tgt16, 0, dout, K, p.K_n, p.fz_per_wave, sigma,
                     curv, key, want_pq ? Pbuf : nullptr, want_pq ? Qused : nullptr, loss_clean,
                     g32, g_hi, g_lo);
     if (want_pq) {
@@ -1873,7 +1939,7 @@ dust_status_t run_head(const void* X, const void* W, const int32_t* labels, int6
   float* gpart = (float*)(ws + p.off_gpart);
   const NoiseKey key = make_key(seed);
 
-  launch_base_gemm(X, W, nullptr, T, d_in, V, dtype, logits, s);
+  launch_base_gemm(p, X, W, nullptr, T, d_in, V, dtype, logits, s);
   const TimedLaunch tl = take_timing_events();
   const int64_t n_slab = V / 256;
   const unsigned waves = (unsigned)(n_slab < 4 ? n_slab : 4);

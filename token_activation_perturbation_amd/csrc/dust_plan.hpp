@@ -27,6 +27,23 @@ constexpr int64_t kTargetWaves = DUST_TARGET_WAVES;
 #define DUST_OUTER_MIN_TOKENS 512
 #endif
 
+// 128 x 128 GEMM tiles: the base GEMM takes them from this many tiles on
+// (-DDUST_BIG_TILES_MIN); the outer product when its token splits of at
+// least kBigOuterMinTokens give kBigOuterWorkgroups workgroups (three share
+// a CU).
+#ifndef DUST_BIG_TILES_MIN
+#define DUST_BIG_TILES_MIN 512
+#endif
+#ifndef DUST_BIG_OUTER_WORKGROUPS
+#define DUST_BIG_OUTER_WORKGROUPS 768
+#endif
+#ifndef DUST_BIG_OUTER_MIN_TOKENS
+#define DUST_BIG_OUTER_MIN_TOKENS 1024
+#endif
+constexpr int64_t kBigTilesMin = DUST_BIG_TILES_MIN;
+constexpr int64_t kBigOuterWorkgroups = DUST_BIG_OUTER_WORKGROUPS;
+constexpr int64_t kBigOuterMinTokens = DUST_BIG_OUTER_MIN_TOKENS;
+
 struct Plan {
   int64_t T = 0, d_in = 0, d_out = 0;
   int32_t K = 0, K_n = 0, antithetic = 0, dtype = 0;
@@ -40,8 +57,12 @@ struct Plan {
   // fused single-generation kernel (gamma = 0): one workgroup of fz_waves
   // waves per token, the noise indices split into ranges of fz_per_wave
   int32_t fz_waves = 1, fz_per_wave = 0;
-  // outer product (64 x 64 output tiles): split of the token (contraction)
-  // axis into outer_split ranges of outer_tokens
+  // base GEMM: 128 x 128 tiles (base_big) when the problem has enough of
+  // them to fill the chip twice over, else 64 x 64
+  int32_t base_big = 0;
+  // outer product: 128 x 128 output tiles (outer_big) or 64 x 64; split of
+  // the token (contraction) axis into outer_split ranges of outer_tokens
+  int32_t outer_big = 0;
   int32_t outer_split = 1;
   int64_t outer_tokens = 0;  // tokens per split (multiple of 64)
 
@@ -99,12 +120,26 @@ inline bool make_plan(int64_t T, int64_t d_in, int64_t d_out, int32_t K,
   if (fw < 1) fw = 1;
   q.fz_per_wave = (int32_t)(ceil_div(ceil_div(q.K_n, fw), 4) * 4);
   q.fz_waves = (int32_t)ceil_div(q.K_n, q.fz_per_wave);
-  // outer product: 64x64 tiles; split the tokens until ~DUST_OUTER_WORKGROUPS
-  // workgroups, keeping >= 512 tokens per split (measured best on MI355X for
-  // 512-wide and 3072 x 768 layers)
-  const int64_t tiles = ceil_div(d_out, 64) * ceil_div(d_in, 64);
-  int64_t split = ceil_div(DUST_OUTER_WORKGROUPS, tiles);
-  const int64_t max_split = ceil_div(T, DUST_OUTER_MIN_TOKENS);
+  // base GEMM: 128 x 128 tiles once there are at least kBigTilesMin of them
+  // (two workgroups per CU share it; fewer would leave CUs idle)
+  const bool aligned8 = (d_in % 8) == 0 && (d_out % 8) == 0;
+  q.base_big = (aligned8 && ceil_div(T, 128) * ceil_div(d_out, 128) >= kBigTilesMin) ? 1 : 0;
+  // outer product: 128 x 128 tiles when, with splits of at least
+  // kBigOuterMinTokens tokens, there are kBigOuterWorkgroups of them;
+  // else 64 x 64 tiles, split until ~DUST_OUTER_WORKGROUPS workgroups with
+  // >= DUST_OUTER_MIN_TOKENS tokens per split (measured best on MI355X for
+  // 512-wide layers)
+  const int64_t tiles128 = ceil_div(d_out, 128) * ceil_div(d_in, 128);
+  q.outer_big =
+      (aligned8 && tiles128 * ceil_div(T, kBigOuterMinTokens) >= kBigOuterWorkgroups) ? 1 : 0;
+  const int64_t tiles = q.outer_big ? tiles128 : ceil_div(d_out, 64) * ceil_div(d_in, 64);
+  // the large tiles' grid is sized to fit one round of resident workgroups
+  // (a second round that holds only a few would take nearly as long as the
+  // first); the small tiles run many rounds
+  int64_t split = q.outer_big ? kBigOuterWorkgroups / tiles
+                              : ceil_div(DUST_OUTER_WORKGROUPS, tiles);
+  const int64_t max_split =
+      ceil_div(T, q.outer_big ? kBigOuterMinTokens : DUST_OUTER_MIN_TOKENS);
   if (split > max_split) split = max_split;
   if (split > 64) split = 64;
   if (split < 1) split = 1;
