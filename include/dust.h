@@ -65,19 +65,27 @@ size_t dust_workspace_bytes(int64_t T, int64_t d_in, int64_t d_out, int32_t K,
  * Bytes of device workspace that let dust_estimate and dust_estimate_local
  * generate each noise value once for gamma > 0 ("Dust: every token is a
  * member of the population", section "Perturb the activations, not the
- * weights": the credit r_t = c_t + gamma r_(t+1); for an antithetic pair
- * centring and curvature cancel, so r+ - r- = -2 sigma R_t with
- * R_t = P_t + gamma R_(t+1), P_t = <delta_t, a_t>, and one walk over each
- * sequence in reverse token order forms P, R and g_t = (2/K) sum_p R_t^p a_t^p
- * from the same noise values).  Larger than dust_workspace_bytes exactly
- * when that path applies to these sizes: antithetic != 0, gamma > 0,
- * seq_len >= 2 dividing T, d_out <= 1024, and (T / seq_len) * K / 2 >= 2048
- * pair chains; it adds ceil(K / 32) partial g arrays of T x d_out fp32.
- * A call takes that path when its workspace is at least this size and it
- * asks for neither rho nor reward (which need every draw's centred credit);
- * otherwise it regenerates the noise in a second pass.  The two paths agree
- * within fp32 rounding (different summation orders); each is bitwise
- * reproducible.  0 when the sizes are invalid.  Pure host function.
+ * weights": the credit r_t = c_t + gamma r_(t+1)).  One walk over each
+ * sequence in reverse token order per chain forms the chain's R_t from the
+ * same noise values it reweights:
+ *  - antithetic pairs: centring and curvature cancel within a pair, so
+ *    r+ - r- = -2 sigma R_t with R_t = P_t + gamma R_(t+1), P_t = <delta_t,
+ *    a_t>, and g_t = (2/K) sum_p R_t^p a_t^p;
+ *  - plain draws: r_t^(i) = R_t^(i) - M_t with R_t^(i) = rho_t^(i) +
+ *    gamma R_(t+1)^(i) and M_t = m_t + gamma M_(t+1) (m_t the mean of rho_t
+ *    over the draws, the same for every draw), so
+ *    g_t = -1/(K sigma) (sum_i R_t^(i) a_t^(i) - M_t sum_i a_t^(i)).
+ * Larger than dust_workspace_bytes exactly when that path applies to these
+ * sizes: gamma > 0, seq_len >= 2 dividing T, d_out <= 1024, (T / seq_len)
+ * chains >= 2048 (a chain is a pair, K / 2 per sequence, or a plain draw,
+ * K), and seq_len <= 8192 for plain draws; it adds, per group of 16 chains,
+ * the partial sum of R a (T x d_out fp32) and for plain draws those of a
+ * (T x d_out) and of rho (T), plus M (T).  A call takes that path when its
+ * workspace is at least this size and it asks for neither rho nor reward
+ * (which need every draw's centred credit); otherwise it regenerates the
+ * noise in a second pass.  The two paths agree within fp32 rounding
+ * (different summation orders); each is bitwise reproducible.  0 when the
+ * sizes are invalid.  Pure host function.
  */
 size_t dust_workspace_bytes_seq(int64_t T, int64_t d_in, int64_t d_out,
                                 int64_t seq_len, int32_t K, float gamma,

@@ -1,12 +1,15 @@
-"""Single generation for gamma > 0 with antithetic pairs (the chain path).
+"""Single generation for gamma > 0 (the chain path).
 
 With a workspace of dust_workspace_bytes_seq bytes and no per-draw output
 asked for, dust_estimate and dust_estimate_local walk each sequence in
-reverse token order, one pair per wave, and generate every noise value
-once: for a pair, centring and curvature cancel and
-g_t = (2/K) sum_p R_t^p a_t^p with R_t = P_t + gamma R_(t+1) ("Dust: every
-token is a member of the population", section "Perturb the activations,
-not the weights": the credit recursion).  Checked: parity with the fp64
+reverse token order, two chains per wave, and generate every noise value
+once ("Dust: every token is a member of the population", section "Perturb
+the activations, not the weights": the credit recursion).  For an
+antithetic pair centring and curvature cancel and
+g_t = (2/K) sum_p R_t^p a_t^p with R_t = P_t + gamma R_(t+1); for plain
+draws r_t^(i) = R_t^(i) - M_t with R_t^(i) = rho_t^(i) + gamma R_(t+1)^(i)
+and M_t the same recursion over the draws' mean loss reduction, so
+g_t = -1/(K sigma) (sum_i R_t^(i) a_t^(i) - M_t sum_i a_t^(i)).  Checked: parity with the fp64
 oracle at the estimate's bars (2e-3 for bf16 inputs, 1e-5 for the fp32
 path) on G_W, g and the clean loss; agreement with the two-pass path of the
 same call (given only dust_workspace_bytes), which adds the draws in another
@@ -73,7 +76,7 @@ def run(inp, dtype, dev, two_pass=False, local=False, **kw):
 
 
 CASES = [
-    # T, seq_len, d_in, d_out, K, sigma, gamma, dtype
+    # T, seq_len, d_in, d_out, K, sigma, gamma, dtype (antithetic pairs)
     (16, 8, 32, 64, 4096, 1e-2, 0.5, "bf16"),    # 2 sequences x 2048 pairs
     (12, 6, 24, 70, 4096, 1e-2, 0.9, "bf16"),    # ragged width: quads past d_out
     (16, 4, 16, 32, 1024, 1e-2, 1.0, "f32"),     # 4 x 512 pairs, gamma = 1
@@ -84,19 +87,31 @@ CASES = [
     (8, 4, 24, 700, 2048, 1e-2, 0.5, "bf16"),    # 3 quads per lane
     (8, 4, 24, 1022, 2048, 1e-2, 0.9, "bf16"),   # 4 quads per lane, d_out % 4 != 0
 ]
+PLAIN_CASES = [
+    # T, seq_len, d_in, d_out, K, sigma, gamma, dtype (plain draws: K chains per sequence)
+    (8, 4, 24, 300, 1024, 1e-2, 0.6, "bf16"),    # 2 sequences x 1024 draws, ragged quads
+    (16, 8, 32, 64, 1030, 1e-2, 0.7, "bf16"),    # 1030 draws: a partial last group
+    (8, 4, 16, 1022, 1024, 5e-3, 0.9, "f32"),    # 4 quads per lane, ragged, fp32
+    (8, 2, 20, 512, 512, 1e-2, 1.0, "bf16"),     # 4 x 512 draws, gamma = 1: suffix sums
+    (12, 6, 24, 700, 1024, 1e-2, 0.5, "bf16"),   # 3 quads per lane
+]
 
 
-@pytest.mark.parametrize("case", CASES, ids=[f"T{c[0]}_L{c[1]}_dout{c[3]}_K{c[4]}_g{c[6]}_{c[7]}"
-                                             for c in CASES])
+ALL_CASES = [c + (True,) for c in CASES] + [c + (False,) for c in PLAIN_CASES]
+
+
+@pytest.mark.parametrize("case", ALL_CASES,
+                         ids=[f"T{c[0]}_L{c[1]}_dout{c[3]}_K{c[4]}_g{c[6]}_{c[7]}_"
+                              f"{'pairs' if c[8] else 'plain'}" for c in ALL_CASES])
 def test_chain_parity_with_oracle_and_two_pass(dev, oracle_mod, threads, case):
     import token_activation_perturbation_amd as dust
-    T, seq_len, d_in, d_out, K, sigma, gamma, dtype = case
+    T, seq_len, d_in, d_out, K, sigma, gamma, dtype, anti = case
     print(f"chain parity {case}", flush=True)
     code = dtype_code(dtype)
-    assert dust.dust_workspace_bytes_seq(T, d_in, d_out, seq_len, K, gamma, True, code) > \
-        dust.dust_workspace_bytes(T, d_in, d_out, K, True, code)
+    assert dust.dust_workspace_bytes_seq(T, d_in, d_out, seq_len, K, gamma, anti, code) > \
+        dust.dust_workspace_bytes(T, d_in, d_out, K, anti, code)
     inp = synth.random_inputs(T, d_in, d_out, dtype, seed=T * 13 + d_out + K)
-    kw = dict(K=K, sigma=sigma, gamma=gamma, seed=K + 3, antithetic=True, seq_len=seq_len)
+    kw = dict(K=K, sigma=sigma, gamma=gamma, seed=K + 3, antithetic=anti, seq_len=seq_len)
     chain = run(inp, dtype, dev, **kw)
     two = run(inp, dtype, dev, two_pass=True, **kw)
     ref = oracle_mod.estimate(inp["X"], inp["W"], inp["target"], threads=threads, **kw)
@@ -133,13 +148,15 @@ def test_asking_for_per_draw_outputs_keeps_G_within_the_bar(dev, oracle_mod, thr
     assert not np.array_equal(full["G_W"], bare)  # the two paths really differ
 
 
-def test_chain_local_scoring(dev, oracle_mod, threads):
-    """dust_estimate_local: keys/values-style scoring with gamma = 0.98."""
-    T, seq_len, d_in, d_out, K = 16, 8, 32, 64, 4096
+@pytest.mark.parametrize("anti", [True, False], ids=["pairs", "plain"])
+def test_chain_local_scoring(dev, oracle_mod, threads, anti):
+    """dust_estimate_local: keys/values-style scoring with gamma = 0.98 (no
+    curvature term: the score is linear in the jitter)."""
+    T, seq_len, d_in, d_out, K = 16, 8, 32, 64, 4096 if anti else 2048
     rng = np.random.default_rng(41)
     inp = synth.random_inputs(T, d_in, d_out, "bf16", seed=41)
     inp["E"] = rng.standard_normal((T, d_out)).astype(np.float32)
-    kw = dict(K=K, sigma=0.2, gamma=0.98, seed=9, antithetic=True, seq_len=seq_len)
+    kw = dict(K=K, sigma=0.2, gamma=0.98, seed=9, antithetic=anti, seq_len=seq_len)
     chain = run(inp, "bf16", dev, local=True, **kw)
     two = run(inp, "bf16", dev, local=True, two_pass=True, **kw)
     ref = oracle_mod.estimate_local(inp["X"], inp["E"], threads=threads, **kw)
@@ -150,9 +167,11 @@ def test_chain_local_scoring(dev, oracle_mod, threads):
     assert not np.array_equal(chain["g"], two["g"])
 
 
-def test_chain_bitwise_deterministic(dev):
+@pytest.mark.parametrize("anti", [True, False], ids=["pairs", "plain"])
+def test_chain_bitwise_deterministic(dev, anti):
     inp = synth.random_inputs(16, 32, 64, "bf16", seed=5)
-    kw = dict(K=4096, sigma=1e-2, gamma=0.5, seed=1, antithetic=True, seq_len=8)
+    kw = dict(K=4096 if anti else 2048, sigma=1e-2, gamma=0.5, seed=1, antithetic=anti,
+              seq_len=8)
     a = run(inp, "bf16", dev, **kw)
     b = run(inp, "bf16", dev, **kw)
     for k in a:

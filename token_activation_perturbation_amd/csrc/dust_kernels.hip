@@ -965,82 +965,302 @@ __global__ __launch_bounds__(256) void fused_g0_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Single generation for gamma > 0 with antithetic pairs.  Within a pair the
-// centring and the curvature cancel: r_t^+ - r_t^- = -2 sigma R_t with
-// R_t = P_t + gamma R_(t+1) inside a sequence and P_t = <delta_t, a_t>, so
-//   g_t = -1/(K sigma) sum_p (r_t^+ - r_t^-) a_t^p = (2/K) sum_p R_t^p a_t^p,
-// and a walk over a sequence in reverse token order generates each noise
-// value once: a_t^p, then P_t^p (a wave reduction), R_t^p, and R_t^p a_t^p.
-// One workgroup of kChainWaves waves per (sequence, group of pairs), one
-// pair per wave (waves past K_n run with weight 0 so every wave reaches the
-// barriers); the waves' R a are added in LDS in wave order and the group's
-// sum is its partial g_t, [group][T][d_out]; chain_sum_kernel adds the
-// groups in group order.  Lane l owns channel quads l + 64 j; channels past
-// d_out have delta 0 (P ignores them) and are never stored.
+// Single generation for gamma > 0: one walk over each sequence in reverse
+// token order generates every noise value once.
+//
+// Antithetic pairs: within a pair the centring and the curvature cancel,
+// r_t^+ - r_t^- = -2 sigma R_t with R_t = P_t + gamma R_(t+1) inside a
+// sequence and P_t = <delta_t, a_t>, so
+//   g_t = -1/(K sigma) sum_p (r_t^+ - r_t^-) a_t^p = (2/K) sum_p R_t^p a_t^p.
+// Plain draws: with rho_t^(i) = -sigma P_t - curv Q_t (Q_t = ||a_t||^2; curv
+// is sigma^2 / 2 for the quadratic loss, 0 for local scoring) and the mean
+// over draws m_t, the credit is r_t^(i) = R_t^(i) - M_t with
+// R_t^(i) = rho_t^(i) + gamma R_(t+1)^(i) and M_t = m_t + gamma M_(t+1) (M_t
+// is the same for every draw), so
+//   g_t = -1/(K sigma) (sum_i R_t^(i) a_t^(i) - M_t sum_i a_t^(i)).
+// The walk forms R per chain (a pair, or a draw) and, per group of chains,
+// the partial sums of R a (and for plain draws of a and of rho); fixed-order
+// kernels then add the groups (and scan m into M).
+//
+// One workgroup of kChainWaves waves per (sequence, group of kChainGroup
+// chains), kChainPerWave chains per wave (chains past K_n run with weight 0,
+// so every wave reaches the barriers).  Lane l owns channel quads l + 64 j;
+// channels past d_out have delta 0 and are never stored.  Per token a wave
+// adds its chains' R a (and a) in registers, the waves' rows are added in
+// LDS in wave order, and the group's sums go to part[group][t][:] (and
+// part_s[group][t][:], rsum_part[t][group]: token-major, so one wave per
+// token adds the groups' loss reductions).
 
-template <int QPL, bool FULL>
-__global__ __launch_bounds__(1024) void chain_g_kernel(
-    const float* __restrict__ delta, const uint16_t* __restrict__ tgt, int32_t T, int32_t d_out,
-    int32_t seq_len, int32_t K_n,
-    int32_t groups, float gamma, NoiseKey key, float* __restrict__ loss_clean,
-    float* __restrict__ part) {
-  constexpr int NQ = 64 * QPL;
-  extern __shared__ float4 chain_red[];  // [waves][NQ]
+template <int QPL, bool FULL, bool PLAIN>
+__global__ __launch_bounds__(64 * kChainWaves) void chain_g_kernel(
+    const float* __restrict__ delta, int32_t T, int32_t d_out, int32_t seq_len, int32_t K_n,
+    int32_t groups, float gamma, float sigma, float curv, NoiseKey key,
+    float* __restrict__ loss_clean, float* __restrict__ part, float* __restrict__ part_s,
+    float* __restrict__ rsum_part) {
+  constexpr int NQ = 64 * QPL, CPW = kChainPerWave, W = kChainWaves;
+  constexpr int M = PLAIN ? 2 * CPW : CPW;  // totals per wave reduction: P (and Q) per chain
+  constexpr int ROWS = PLAIN ? 2 * W : W;   // LDS rows per buffer: R a (then a) per wave
+  // two buffers of [ROWS][NQ] float4, then (plain) two of [W] floats
+  extern __shared__ float4 chain_red[];
   const int lane = threadIdx.x & 63, wave = wave_id();
-  const int waves = blockDim.x >> 6;
   const int32_t seq = (int32_t)blockIdx.x / groups;
   const int32_t group = (int32_t)blockIdx.x % groups;
-  const int32_t n = group * waves + wave;
-  const float live = n < K_n ? 1.0f : 0.0f;
+  const int32_t n0 = (group * W + wave) * CPW;
+  float live[CPW], R[CPW];
+#pragma unroll
+  for (int c = 0; c < CPW; ++c) {
+    live[c] = n0 + c < K_n ? 1.0f : 0.0f;
+    R[c] = 0.f;
+  }
   const int32_t t_first = seq * seq_len;
-  float R = 0.f;
   for (int32_t tt = seq_len - 1; tt >= 0; --tt) {
     const int32_t t = t_first + tt;
+    // buffer tt & 1: a wave writes it only after the barrier of step tt + 1,
+    // which every wave reaches after finishing its share of step tt + 2's
+    // reduction (the last reader of this buffer), so one barrier per step
+    float4* red = chain_red + (tt & 1) * ROWS * NQ;
+    float* rs_red = (float*)(chain_red + 2 * ROWS * NQ) + (tt & 1) * W;
     const float* drow = delta + (int64_t)t * d_out;
-    const uint16_t* trow = tgt ? tgt + (int64_t)t * d_out : nullptr;
-    float4 d[QPL], a[QPL];
-    float p = 0.f;
+    float4 d[QPL], a[CPW][QPL];
+    float v[M];
+#pragma unroll
+    for (int k = 0; k < M; ++k) v[k] = 0.f;
 #pragma unroll
     for (int j = 0; j < QPL; ++j) {
       const int c = 4 * (lane + 64 * j);
-      d[j] = load_delta4(drow, trow, c, d_out, FULL);
-      a[j] = noise_quad((uint32_t)(lane + 64 * j), (uint32_t)t, (uint32_t)n, key);
-      p = __builtin_fmaf(d[j].x, a[j].x, p);
-      p = __builtin_fmaf(d[j].y, a[j].y, p);
-      p = __builtin_fmaf(d[j].z, a[j].z, p);
-      p = __builtin_fmaf(d[j].w, a[j].w, p);
-    }
-    p = wave_sum(p);
-    R = __builtin_fmaf(gamma, R, p);
-    const float w = live * R;
+      d[j] = load_delta4(drow, nullptr, c, d_out, FULL);
 #pragma unroll
-    for (int j = 0; j < QPL; ++j)
-      chain_red[wave * NQ + 64 * j + lane] =
-          make_float4(w * a[j].x, w * a[j].y, w * a[j].z, w * a[j].w);
+      for (int ch = 0; ch < CPW; ++ch) {
+        a[ch][j] = noise_quad((uint32_t)(lane + 64 * j), (uint32_t)t, (uint32_t)(n0 + ch), key);
+        float p = v[ch];
+        p = __builtin_fmaf(d[j].x, a[ch][j].x, p);
+        p = __builtin_fmaf(d[j].y, a[ch][j].y, p);
+        p = __builtin_fmaf(d[j].z, a[ch][j].z, p);
+        p = __builtin_fmaf(d[j].w, a[ch][j].w, p);
+        v[ch] = p;
+        if (PLAIN) {
+          // channels past d_out: the noise is generated but must not enter Q
+          float4 am = a[ch][j];
+          if (!FULL) {
+            am.x = c < d_out ? am.x : 0.f;
+            am.y = c + 1 < d_out ? am.y : 0.f;
+            am.z = c + 2 < d_out ? am.z : 0.f;
+            am.w = c + 3 < d_out ? am.w : 0.f;
+            a[ch][j] = am;
+          }
+          float q = v[CPW + ch];
+          q = __builtin_fmaf(am.x, am.x, q);
+          q = __builtin_fmaf(am.y, am.y, q);
+          q = __builtin_fmaf(am.z, am.z, q);
+          q = __builtin_fmaf(am.w, am.w, q);
+          v[CPW + ch] = q;
+        }
+      }
+    }
+    float tot[M];
+    wave_reduce_to_scalars<M>(v, lane, tot);
+    float w[CPW], rho_w = 0.f;
+#pragma unroll
+    for (int ch = 0; ch < CPW; ++ch) {
+      if (PLAIN) {
+        const float rho = -__builtin_fmaf(sigma, tot[ch], curv * tot[CPW + ch]);
+        R[ch] = __builtin_fmaf(gamma, R[ch], rho);
+        rho_w = __builtin_fmaf(live[ch], rho, rho_w);
+      } else {
+        R[ch] = __builtin_fmaf(gamma, R[ch], tot[ch]);
+      }
+      w[ch] = live[ch] * R[ch];
+    }
+#pragma unroll
+    for (int j = 0; j < QPL; ++j) {
+      float4 r = make_float4(w[0] * a[0][j].x, w[0] * a[0][j].y, w[0] * a[0][j].z,
+                             w[0] * a[0][j].w);
+#pragma unroll
+      for (int ch = 1; ch < CPW; ++ch) {
+        r.x = __builtin_fmaf(w[ch], a[ch][j].x, r.x);
+        r.y = __builtin_fmaf(w[ch], a[ch][j].y, r.y);
+        r.z = __builtin_fmaf(w[ch], a[ch][j].z, r.z);
+        r.w = __builtin_fmaf(w[ch], a[ch][j].w, r.w);
+      }
+      red[wave * NQ + 64 * j + lane] = r;
+      if (PLAIN) {
+        float4 sa = make_float4(live[0] * a[0][j].x, live[0] * a[0][j].y, live[0] * a[0][j].z,
+                                live[0] * a[0][j].w);
+#pragma unroll
+        for (int ch = 1; ch < CPW; ++ch) {
+          sa.x = __builtin_fmaf(live[ch], a[ch][j].x, sa.x);
+          sa.y = __builtin_fmaf(live[ch], a[ch][j].y, sa.y);
+          sa.z = __builtin_fmaf(live[ch], a[ch][j].z, sa.z);
+          sa.w = __builtin_fmaf(live[ch], a[ch][j].w, sa.w);
+        }
+        red[(W + wave) * NQ + 64 * j + lane] = sa;
+      }
+    }
+    if (PLAIN && lane == 0) rs_red[wave] = rho_w;
     if (loss_clean && group == 0 && wave == 0) {
-      float s = 0.f;
+      float sl = 0.f;
 #pragma unroll
       for (int j = 0; j < QPL; ++j) {
-        s = __builtin_fmaf(d[j].x, d[j].x, s);
-        s = __builtin_fmaf(d[j].y, d[j].y, s);
-        s = __builtin_fmaf(d[j].z, d[j].z, s);
-        s = __builtin_fmaf(d[j].w, d[j].w, s);
+        sl = __builtin_fmaf(d[j].x, d[j].x, sl);
+        sl = __builtin_fmaf(d[j].y, d[j].y, sl);
+        sl = __builtin_fmaf(d[j].z, d[j].z, sl);
+        sl = __builtin_fmaf(d[j].w, d[j].w, sl);
       }
-      s = wave_sum(s);
-      if (lane == 0) loss_clean[t] = 0.5f * s;
+      sl = wave_sum(sl);
+      if (lane == 0) loss_clean[t] = 0.5f * sl;
     }
     __syncthreads();
-    // every thread sums whole channels over the waves (channel c is float c
-    // of a wave's row), so all the workgroup's lanes share the reduction
-    const float* red = (const float*)chain_red;
-    float* dst = part + ((int64_t)group * T + t) * d_out;
-    for (int c = (int)threadIdx.x; c < 4 * NQ; c += (int)blockDim.x) {
-      float acc = red[c];
-      for (int w2 = 1; w2 < waves; ++w2) acc += red[w2 * 4 * NQ + c];
-      if (FULL || c < d_out) dst[c] = acc;
+    // the group's sums, one thread per (row kind, channel quad), the waves'
+    // rows added in wave order
+    const int64_t row = ((int64_t)group * T + t) * d_out;
+    for (int i = (int)threadIdx.x; i < (PLAIN ? 2 : 1) * NQ; i += 64 * W) {
+      const int kind = i >= NQ ? 1 : 0, q = i - kind * NQ;
+      const float4* src = red + kind * W * NQ + q;
+      float4 acc = src[0];
+#pragma unroll
+      for (int w2 = 1; w2 < W; ++w2) {
+        const float4 o = src[w2 * NQ];
+        acc.x += o.x;
+        acc.y += o.y;
+        acc.z += o.z;
+        acc.w += o.w;
+      }
+      float* dst = (kind ? part_s : part) + row;
+      const int c = 4 * q;
+      if (FULL) {
+        *(float4*)(dst + c) = acc;
+      } else {
+        const float v4[4] = {acc.x, acc.y, acc.z, acc.w};
+        for (int e = 0; e < 4; ++e)
+          if (c + e < d_out) dst[c + e] = v4[e];
+      }
     }
-    __syncthreads();
+    if (PLAIN && threadIdx.x == 0) {
+      float r = rs_red[0];
+      for (int w2 = 1; w2 < W; ++w2) r += rs_red[w2];
+      rsum_part[(int64_t)t * groups + group] = r;
+    }
   }
+}
+
+// Plain draws: the mean loss reduction over the K draws of every token,
+// m_t = (sum over groups of rsum_part[t][:]) / K, one wave per token (the
+// groups added lane-strided, then across the wave in a fixed order).
+__global__ __launch_bounds__(256) void chain_rho_mean_kernel(const float* __restrict__ rsum_part,
+                                                             int32_t T, int32_t groups,
+                                                             float inv_k, float* __restrict__ m) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + wave_id();
+  if (t >= T) return;
+  const float* row = rsum_part + t * groups;
+  float r = 0.f;
+  for (int32_t gr = lane; gr < groups; gr += 64) r += row[gr];
+  r = wave_sum(r);
+  if (lane == 0) m[t] = r * inv_k;
+}
+
+// Plain draws: M_t = m_t + gamma M_(t+1) per sequence, in place.  One
+// workgroup per sequence; m is staged in LDS ([seq_len] floats), cut into one
+// chunk per thread for a local reverse scan, the chunks' carries chained by
+// one thread from the last chunk to the first, and each token's value
+// completed with gamma^e times its chunk's carry (e the distance from the
+// token to the next chunk's first token).  The scan is associative, so this
+// equals the token-by-token recurrence up to fp32 rounding order.
+__global__ __launch_bounds__(256) void chain_mean_kernel(int32_t seq_len, float gamma,
+                                                         float* __restrict__ Mv) {
+  extern __shared__ float mscan[];  // [seq_len] values, then [256] chunk heads / carries
+  float* heads = mscan + seq_len;
+  const int tid = (int)threadIdx.x, nth = (int)blockDim.x;
+  float* mrow = Mv + (int64_t)blockIdx.x * seq_len;
+  for (int tt = tid; tt < seq_len; tt += nth) mscan[tt] = mrow[tt];
+  __syncthreads();
+  const int L = (seq_len + nth - 1) / nth;  // tokens per chunk
+  const int lo = tid * L, hi = min(seq_len, lo + L);
+  float r = 0.f;
+  for (int tt = hi - 1; tt >= lo; --tt) {
+    r = __builtin_fmaf(gamma, r, mscan[tt]);
+    mscan[tt] = r;
+  }
+  heads[tid] = lo < hi ? r : 0.f;
+  __syncthreads();
+  if (tid == 0) {
+    // carry into chunk k: the value at chunk k + 1's first token
+    float carry = 0.f;
+    for (int k = nth - 1; k >= 0; --k) {
+      const int klo = k * L, khi = min(seq_len, klo + L);
+      const float head = heads[k];
+      heads[k] = carry;
+      if (klo < khi) {
+        float gl = 1.f;
+        for (int e = 0; e < khi - klo; ++e) gl *= gamma;
+        carry = __builtin_fmaf(gl, carry, head);
+      }
+    }
+  }
+  __syncthreads();
+  const float carry = heads[tid];
+  float factor = 1.f;
+  for (int tt = hi - 1; tt >= lo; --tt) {
+    factor *= gamma;  // gamma^(hi - tt)
+    mrow[tt] = __builtin_fmaf(factor, carry, mscan[tt]);
+  }
+}
+
+// Plain draws: g_t = scale (sum_groups A_t - M_t sum_groups S_t), the groups
+// added in group order, scale = -1/(K sigma); written as fp32 and / or its
+// bf16 split.  One lane per (token, channel quad).
+template <bool FULL>
+__global__ __launch_bounds__(256) void chain_sum_plain_kernel(
+    const float* __restrict__ part, const float* __restrict__ part_s,
+    const float* __restrict__ Mv, int32_t T, int32_t d_out, int32_t nq, int32_t groups,
+    float scale, float* __restrict__ g32, uint16_t* __restrict__ g_hi,
+    uint16_t* __restrict__ g_lo) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)T * nq) return;
+  const int64_t t = i / nq;
+  const int c = 4 * (int)(i % nq);
+  const int64_t stride = (int64_t)T * d_out;
+  const float m = Mv[t];
+  float a[4], sv[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    a[e] = 0.f;
+    sv[e] = 0.f;
+  }
+  if (FULL) {
+    float4 acc = *(const float4*)(part + t * d_out + c);
+    float4 sacc = *(const float4*)(part_s + t * d_out + c);
+    for (int32_t gr = 1; gr < groups; ++gr) {
+      const float4 o = *(const float4*)(part + gr * stride + t * d_out + c);
+      const float4 so = *(const float4*)(part_s + gr * stride + t * d_out + c);
+      acc.x += o.x;
+      acc.y += o.y;
+      acc.z += o.z;
+      acc.w += o.w;
+      sacc.x += so.x;
+      sacc.y += so.y;
+      sacc.z += so.z;
+      sacc.w += so.w;
+    }
+    a[0] = acc.x; a[1] = acc.y; a[2] = acc.z; a[3] = acc.w;
+    sv[0] = sacc.x; sv[1] = sacc.y; sv[2] = sacc.z; sv[3] = sacc.w;
+  } else {
+    for (int e = 0; e < 4; ++e)
+      if (c + e < d_out) {
+        float sum = part[t * d_out + c + e], ssum = part_s[t * d_out + c + e];
+        for (int32_t gr = 1; gr < groups; ++gr) {
+          sum += part[gr * stride + t * d_out + c + e];
+          ssum += part_s[gr * stride + t * d_out + c + e];
+        }
+        a[e] = sum;
+        sv[e] = ssum;
+      }
+  }
+  const float4 r = make_float4(scale * __builtin_fmaf(-m, sv[0], a[0]),
+                               scale * __builtin_fmaf(-m, sv[1], a[1]),
+                               scale * __builtin_fmaf(-m, sv[2], a[2]),
+                               scale * __builtin_fmaf(-m, sv[3], a[3]));
+  store_g_quad(r, t * d_out, c, d_out, FULL, g32, g_hi, g_lo);
 }
 
 // g_t = scale x the sum of the groups' partial g_t in group order, written
@@ -1550,31 +1770,44 @@ void launch_base_gemm(const Plan& p, const void* X, const void* W, const void* t
   }
 }
 
-// The chain path's two kernels (single generation, gamma > 0, antithetic
-// pairs): partial g per pair group, then their sum scaled by 2 / K.
-void launch_chain(const Plan& p, const ChainPlan& cp, int64_t seq_len, float gamma,
-                  NoiseKey key, const float* delta, const uint16_t* tgt, bool delta_vec,
-                  float* loss_clean,
-                  float* part, float* g32, uint16_t* g_hi, uint16_t* g_lo, hipStream_t s,
-                  TimedLaunch tl) {
+// The chain path (single generation, gamma > 0): the walk over each
+// sequence, which writes the chain groups' partial sums, then their sum:
+// g = (2/K) sum A for antithetic pairs; for plain draws the per-token credit
+// mean M first, then g = -1/(K sigma) (sum A - M sum S).
+void launch_chain(const Plan& p, const ChainPlan& cp, int64_t seq_len, float gamma, float sigma,
+                  float curv, NoiseKey key, const float* delta, bool delta_vec,
+                  float* loss_clean, char* ws, float* g32, uint16_t* g_hi, uint16_t* g_lo,
+                  hipStream_t s, TimedLaunch tl) {
   const int qpl = fused_qpl(p.nq);
-  const bool part_vec = ((uintptr_t)part % 16) == 0;
+  float* part = (float*)(ws + cp.off_part);
+  float* part_s = cp.plain ? (float*)(ws + cp.off_part_s) : nullptr;
+  float* rsum = cp.plain ? (float*)(ws + cp.off_rsum) : nullptr;
+  float* Mv = cp.plain ? (float*)(ws + cp.off_mean) : nullptr;
+  const bool part_vec = ((uintptr_t)part % 16) == 0 && ((uintptr_t)part_s % 16) == 0;
   const bool full = (p.nq == 64 * qpl) && delta_vec && part_vec;
   const dim3 grid((unsigned)(cp.n_seq * cp.groups)), block(64 * kChainWaves);
-  const size_t lds = sizeof(float4) * 64 * (size_t)qpl * kChainWaves;
+  const size_t lds = 2 * sizeof(float4) * 64 * (size_t)qpl * kChainWaves * (cp.plain ? 2 : 1) +
+                     (cp.plain ? 2 * sizeof(float) * kChainWaves : 0);
   const int32_t Ti = (int32_t)p.T, dout = (int32_t)p.d_out, sl = (int32_t)seq_len;
   const double td = (double)p.T * p.d_out;
-  const TimedLaunch ev = stamp("chain_g_kernel", 0.0,
-                               4.0 * td * (1.0 + cp.groups) + (tgt ? 2.0 * td : 0.0) +
-                                   (loss_clean ? 4.0 * p.T : 0.0),
-                               tl);
-#define DUST_CHAIN(Q, F)                                                                        \
-  DUST_LAUNCH(ev, (chain_g_kernel<Q, F>), grid, block, lds, s, delta, tgt, Ti, dout, sl, p.K_n, \
-              cp.groups, gamma, key, loss_clean, part)
-#define DUST_CHAIN_Q(Q)               \
-  case Q:                             \
-    if (full) DUST_CHAIN(Q, true);    \
-    else DUST_CHAIN(Q, false);        \
+  const double rows_b = 4.0 * td * cp.groups * (cp.plain ? 2.0 : 1.0);
+  const TimedLaunch ev =
+      stamp("chain_g_kernel", 0.0,
+            4.0 * td + rows_b + (cp.plain ? 4.0 * p.T * cp.groups : 0.0) +
+                (loss_clean ? 4.0 * p.T : 0.0),
+            tl);
+#define DUST_CHAIN(Q, F, PL)                                                                     \
+  DUST_LAUNCH(ev, (chain_g_kernel<Q, F, PL>), grid, block, lds, s, delta, Ti, dout, sl, p.K_n,   \
+              cp.groups, gamma, sigma, curv, key, loss_clean, part, part_s, rsum)
+#define DUST_CHAIN_Q(Q)                                              \
+  case Q:                                                            \
+    if (cp.plain) {                                                  \
+      if (full) DUST_CHAIN(Q, true, true);                           \
+      else DUST_CHAIN(Q, false, true);                               \
+    } else {                                                         \
+      if (full) DUST_CHAIN(Q, true, false);                          \
+      else DUST_CHAIN(Q, false, false);                              \
+    }                                                                \
     break;
   switch (qpl) {
     DUST_CHAIN_Q(1)
@@ -1587,15 +1820,34 @@ void launch_chain(const Plan& p, const ChainPlan& cp, int64_t seq_len, float gam
 #undef DUST_CHAIN
   const bool sum_full = (p.d_out % 4 == 0) && part_vec;
   const unsigned blocks = (unsigned)ceil_div(p.T * p.nq, 256);
-  const float scale = 2.0f / (float)p.K;
-  const TimedLaunch evs = stamp(
-      "chain_sum_kernel", 0.0, 4.0 * td * cp.groups + (g32 ? 4.0 * td : 0.0) + (g_hi ? 4.0 * td : 0.0));
-  if (sum_full)
-    DUST_LAUNCH(evs, chain_sum_kernel<true>, dim3(blocks), dim3(256), 0, s, (const float*)part,
-                Ti, dout, p.nq, cp.groups, scale, g32, g_hi, g_lo);
-  else
-    DUST_LAUNCH(evs, chain_sum_kernel<false>, dim3(blocks), dim3(256), 0, s, (const float*)part,
-                Ti, dout, p.nq, cp.groups, scale, g32, g_hi, g_lo);
+  const double g_b = (g32 ? 4.0 * td : 0.0) + (g_hi ? 4.0 * td : 0.0);
+  if (!cp.plain) {
+    const float scale = 2.0f / (float)p.K;
+    const TimedLaunch evs = stamp("chain_sum_kernel", 0.0, rows_b + g_b);
+    if (sum_full)
+      DUST_LAUNCH(evs, chain_sum_kernel<true>, dim3(blocks), dim3(256), 0, s, (const float*)part,
+                  Ti, dout, p.nq, cp.groups, scale, g32, g_hi, g_lo);
+    else
+      DUST_LAUNCH(evs, chain_sum_kernel<false>, dim3(blocks), dim3(256), 0, s,
+                  (const float*)part, Ti, dout, p.nq, cp.groups, scale, g32, g_hi, g_lo);
+  } else {
+    DUST_LAUNCH(stamp("chain_rho_mean_kernel", 0.0, 4.0 * p.T * (cp.groups + 1.0)),
+                chain_rho_mean_kernel, dim3(grid_for(p.T, 4)), dim3(256), 0, s, (const float*)rsum,
+                Ti, cp.groups, 1.0f / (float)p.K, Mv);
+    DUST_LAUNCH(stamp("chain_mean_kernel", 0.0, 8.0 * p.T), chain_mean_kernel,
+                dim3((unsigned)cp.n_seq), dim3(256), sizeof(float) * (size_t)(seq_len + 256), s,
+                sl, gamma, Mv);
+    const float scale = -1.0f / ((float)p.K * sigma);
+    const TimedLaunch evs = stamp("chain_sum_kernel", 0.0, rows_b + 4.0 * p.T + g_b);
+    if (sum_full)
+      DUST_LAUNCH(evs, chain_sum_plain_kernel<true>, dim3(blocks), dim3(256), 0, s,
+                  (const float*)part, (const float*)part_s, (const float*)Mv, Ti, dout, p.nq,
+                  cp.groups, scale, g32, g_hi, g_lo);
+    else
+      DUST_LAUNCH(evs, chain_sum_plain_kernel<false>, dim3(blocks), dim3(256), 0, s,
+                  (const float*)part, (const float*)part_s, (const float*)Mv, Ti, dout, p.nq,
+                  cp.groups, scale, g32, g_hi, g_lo);
+  }
 }
 
 // G_W = sum_t g_t x_t^T: the split partials (or G_W itself with one split),
@@ -1837,8 +2089,8 @@ dust_status_t run_estimate(const Site& st, int64_t T, int64_t d_in, int64_t d_ou
   const double stats_b = pq_b + 4.0 * tk + 4.0 * T;
   const double credit_b = 4.0 * tk + 4.0 * T + (reward ? 4.0 * tk : 0.0) + 4.0 * tkn;
   if (chain) {
-    launch_chain(p, cp, seq_len, gamma, key, (const float*)delta, tgt16, delta_vec, loss_clean,
-                 (float*)(ws + cp.off_part), g32, g_hi, g_lo, s, tl);
+    launch_chain(p, cp, seq_len, gamma, sigma, curv, key, (const float*)delta, delta_vec,
+                 loss_clean, ws, g32, g_hi, g_lo, s, tl);
   } else if (!fused) {
     // 2. jitter + loss change
     const TimedLaunch evj =

@@ -175,39 +175,64 @@ inline bool make_plan(int64_t T, int64_t d_in, int64_t d_out, int32_t K,
 }
 
 // ---------------------------------------------------------------------------
-// Single generation for gamma > 0 with antithetic pairs (the "chain" path):
-// one workgroup of kChainWaves waves per (sequence, group of kChainWaves
-// pairs), one pair per wave, each wave walking its sequence's tokens in
-// reverse order; every group writes a partial g per token, [groups][T][d_out]
-// fp32, placed after the two-pass layout, so the chain path needs a larger
+// Single generation for gamma > 0 (the "chain" path): each sequence is walked
+// in reverse token order once per chain (an antithetic pair, or one plain
+// draw); one workgroup of kChainWaves waves per (sequence, group of
+// kChainGroup chains), kChainPerWave chains per wave.  Every group writes,
+// per token, its partial sum of R a ([groups][T][d_out] fp32) and for plain
+// draws also its partial sums of a ([groups][T][d_out]) and of rho
+// ([T][groups]), with the per-token credit mean M ([T]) after them; all of
+// it is placed after the two-pass layout, so the chain path needs a larger
 // workspace (dust_workspace_bytes_seq) and a call given only
 // dust_workspace_bytes takes the two-pass path.  It is planned only where
-// the chains fill the chip (sequences x pairs >= kChainMinChains) and the
-// waves' partial sums fit the 64 KiB of LDS a workgroup is given
-// (kChainWaves x d_out x 4 bytes: d_out <= kChainMaxDout).
-constexpr int32_t kChainWaves = 16;
+// the chains fill the chip (sequences x chains >= kChainMinChains), the
+// waves' rows fit the workgroup's LDS (d_out <= kChainMaxDout) and, for plain
+// draws, a sequence's mean scan fits LDS (seq_len <= kChainMaxSeqLen).
+#ifndef DUST_CHAIN_WAVES
+#define DUST_CHAIN_WAVES 8
+#endif
+#ifndef DUST_CHAIN_PER_WAVE
+#define DUST_CHAIN_PER_WAVE 2
+#endif
+constexpr int32_t kChainWaves = DUST_CHAIN_WAVES;      // -DDUST_CHAIN_WAVES=n
+constexpr int32_t kChainPerWave = DUST_CHAIN_PER_WAVE;  // -DDUST_CHAIN_PER_WAVE=n (2 or 4)
+constexpr int32_t kChainGroup = kChainWaves * kChainPerWave;
 constexpr int64_t kChainMinChains = 2048;
 constexpr int64_t kChainMaxDout = 1024;
+constexpr int64_t kChainMaxSeqLen = 8192;
 
 struct ChainPlan {
   bool ok = false;
-  int32_t groups = 0;   // pair groups per sequence, ceil(K_n / kChainWaves)
-  int64_t n_seq = 0;    // sequences, T / seq_len
-  size_t off_part = 0;  // partial g [groups][T][d_out] fp32
-  size_t total = 0;     // workspace bytes of the chain path
+  bool plain = false;     // plain draws (else antithetic pairs)
+  int32_t groups = 0;     // chain groups per sequence, ceil(K_n / kChainGroup)
+  int64_t n_seq = 0;      // sequences, T / seq_len
+  size_t off_part = 0;    // partial sum of R a [groups][T][d_out] fp32
+  size_t off_part_s = 0;  // plain: partial sum of a [groups][T][d_out] fp32
+  size_t off_rsum = 0;    // plain: partial sum of rho [T][groups] fp32
+  size_t off_mean = 0;    // plain: M_t [T] fp32
+  size_t total = 0;       // workspace bytes of the chain path
 };
 
 inline ChainPlan make_chain_plan(const Plan& p, int64_t seq_len, float gamma) {
   ChainPlan c;
-  if (!p.antithetic || !(gamma > 0.0f) || seq_len < 2 || p.T % seq_len != 0) return c;
+  if (!(gamma > 0.0f) || seq_len < 2 || p.T % seq_len != 0) return c;
   if (p.d_out > kChainMaxDout) return c;
+  c.plain = !p.antithetic;
+  if (c.plain && seq_len > kChainMaxSeqLen) return c;
   c.n_seq = p.T / seq_len;
   if (c.n_seq * p.K_n < kChainMinChains) return c;
-  c.groups = (int32_t)ceil_div(p.K_n, kChainWaves);
+  c.groups = (int32_t)ceil_div(p.K_n, kChainGroup);
   if (c.n_seq * c.groups >= (int64_t(1) << 31)) return c;
+  const size_t rows = sizeof(float) * size_t(c.groups) * size_t(p.T) * size_t(p.d_out);
   c.off_part = align256(p.total);
-  c.total = align256(c.off_part + sizeof(float) * size_t(c.groups) * size_t(p.T) *
-                                      size_t(p.d_out));
+  size_t end = align256(c.off_part + rows);
+  if (c.plain) {
+    c.off_part_s = end;
+    c.off_rsum = align256(c.off_part_s + rows);
+    c.off_mean = align256(c.off_rsum + sizeof(float) * size_t(c.groups) * size_t(p.T));
+    end = align256(c.off_mean + sizeof(float) * size_t(p.T));
+  }
+  c.total = end;
   c.ok = true;
   return c;
 }

@@ -92,6 +92,11 @@ WORKLOADS = {
         Workload("mlp_up_bf16", 16384, 512, 768, 3072, 256, 5e-3, 0.0, True, "bf16", 1003, 0, "teacher"),
         Workload("qkv_credit_bf16", 8192, 1024, 1024, 3072, 128, 1e-2, 0.9, False, "bf16", 1004, 0, "iid"),
         Workload("large_population_bf16", 2048, 1024, 1024, 1024, 4096, 1e-2, 0.5, True, "bf16", 1005, 0, "iid"),
+        # The large population with plain draws (no antithetic pairs): the
+        # single-generation walk for gamma > 0 then also carries each group's
+        # noise sum and mean loss reduction for the centring.
+        Workload("large_population_plain_bf16", 2048, 1024, 1024, 1024, 4096, 1e-2, 0.5, False,
+                 "bf16", 1010, 0, "iid"),
         # Local scoring of attention internals ("What the released code
         # actually does", step 4) in the pages' 512-wide model and batches of
         # 8 sequences x 2048 tokens: keys / values (credit decay 0.98) and
@@ -110,8 +115,8 @@ WORKLOADS = {
     ]
 }
 WORKLOAD_ORDER = ["tiny_f32", "bf16_layer", "mlp_up_bf16", "qkv_credit_bf16",
-                  "large_population_bf16", "kv_local_bf16", "q_local_bf16", "head_ce_bf16",
-                  "embed_bf16"]
+                  "large_population_bf16", "large_population_plain_bf16", "kv_local_bf16",
+                  "q_local_bf16", "head_ce_bf16", "embed_bf16"]
 
 
 def bf16_round(x: np.ndarray) -> np.ndarray:
