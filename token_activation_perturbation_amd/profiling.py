@@ -10,10 +10,19 @@ then WRITE_SIZE, in KiB per dispatch) into HBM bytes per launch of `kernel`,
 scaled by what the same counters read for the largest plain copy kernel in
 the run (whose true traffic is copy_bytes read + copy_bytes written).
 `counters` turns one SQ counter run into per-kernel unit utilisation on the
-MI355X (1024 SIMDs in 8 XCDs): VALU busy = SQ_ACTIVE_INST_VALU x 4 (it counts
-quad-cycles, summed over SIMDs) / 1024 / (GRBM_GUI_ACTIVE / 8) (the GPU-busy
-clock, summed over the 8 XCDs); MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / 1024 /
-(GRBM_GUI_ACTIVE / 8); VALU and MFMA instructions per wave.
+MI355X (1024 SIMDs in 8 XCDs, GRBM_GUI_ACTIVE counted per XCD):
+  * VALU issue = issue slots / (2 x quad-cycles x 1024): a SIMD issues up to
+    two single-pass VALU instructions per quad-cycle (128 lanes per CU per
+    clock, the fp32 vector peak), and the slots weight every issued VALU
+    instruction by its rate class as the ALU cost model does: 1 for a
+    single-pass instruction, 2 for a 64-bit integer or conversion
+    instruction (SQ_INSTS_VALU_INT64, SQ_INSTS_VALU_CVT: half rate), 4 for
+    a transcendental (SQ_INSTS_VALU_TRANS_F32: quarter rate); quad-cycles
+    = the kernel's GPU-busy clock (GRBM_GUI_ACTIVE averaged over the XCDs)
+    / 4.  It is a fraction of the issue capacity, at most 1;
+  * MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / 1024 / GPU-busy cycles;
+  * VALU and MFMA instructions per wave, and the transcendental, 64-bit
+    integer and conversion instructions per wave.
 """
 from __future__ import annotations
 
@@ -113,17 +122,27 @@ def counter_table(db: str, title: str, command: str) -> str:
         acc[k][cname] += float(val)
         disp.setdefault(k, set()).add(did)
     lines = [f"# {title}", "", "Command (repository root, on an MI355X):", "", "```", command,
-             "```", "", "| kernel | dispatches | VALU busy | MFMA busy | VALU insts / wave | "
-             "MFMA insts / wave | transcendental insts / wave |", "|---|---|---|---|---|---|---|"]
+             "```", "",
+             "VALU issue = (SQ_INSTS_VALU + 3 SQ_INSTS_VALU_TRANS_F32 + SQ_INSTS_VALU_INT64 + "
+             "SQ_INSTS_VALU_CVT) / (2 x GRBM_GUI_ACTIVE / 8 / 4 x 1024): issue slots weighted by "
+             "rate class (single-pass 1, 64-bit integer and conversion 2, transcendental 4) over "
+             "the SIMDs' capacity of two single-pass instructions per quad-cycle; at most 1.  "
+             "MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / 1024 / (GRBM_GUI_ACTIVE / 8).", "",
+             "| kernel | dispatches | VALU issue | MFMA busy | VALU insts / wave | "
+             "MFMA insts / wave | transcendental / wave | 64-bit int / wave | conversion / wave |",
+             "|---|---|---|---|---|---|---|---|---|"]
     for k, c in acc.items():
         n = len(disp[k])
         gui = c.get("GRBM_GUI_ACTIVE", 0.0) / n / N_XCD
         waves = c.get("SQ_WAVES", 0.0) / n
-        valu = c.get("SQ_ACTIVE_INST_VALU", 0.0) / n * 4 / N_SIMD / gui if gui else float("nan")
+        slots = (c.get("SQ_INSTS_VALU", 0.0) + 3 * c.get("SQ_INSTS_VALU_TRANS_F32", 0.0)
+                 + c.get("SQ_INSTS_VALU_INT64", 0.0) + c.get("SQ_INSTS_VALU_CVT", 0.0)) / n
+        valu = slots / (2.0 * gui / 4.0 * N_SIMD) if gui else float("nan")
         mfma = c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / n / N_SIMD / gui if gui else float("nan")
         per = lambda name: c.get(name, 0.0) / n / waves if waves else float("nan")  # noqa: E731
         lines.append(f"| `{k}` | {n} | {valu:.2f} | {mfma:.2f} | {per('SQ_INSTS_VALU'):.0f} | "
-                     f"{per('SQ_INSTS_MFMA'):.0f} | {per('SQ_INSTS_VALU_TRANS_F32'):.0f} |")
+                     f"{per('SQ_INSTS_MFMA'):.0f} | {per('SQ_INSTS_VALU_TRANS_F32'):.0f} | "
+                     f"{per('SQ_INSTS_VALU_INT64'):.0f} | {per('SQ_INSTS_VALU_CVT'):.0f} |")
     return "\n".join(lines) + "\n"
 
 
