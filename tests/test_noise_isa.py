@@ -6,7 +6,10 @@ the loop body's instructions per quad must be the ones the model counts:
 16 32x32->64 multiply-adds, 15 three-input xors and 3 xors for Philox
 (50 slots at 2 per product and 1 per single-pass op), 4 shifts, 4
 integer-to-float conversions, the u scaling FMA x 2 and 8 transcendentals
-for Box-Muller.  Needs hipcc (cross-compiles, no GPU)."""
+for Box-Muller.  The same holds for noise_quad_x2, which the kernels use to
+advance two quads' Philox rounds together (pairs of noise indices here): it
+must not cost a single extra instruction per quad.  Needs hipcc
+(cross-compiles, no GPU)."""
 import os
 import re
 import shutil
@@ -20,7 +23,8 @@ from token_activation_perturbation_amd import build, roofline
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 QUADS_PER_ITER = 4
 
-KERNEL = r"""
+KERNELS = {
+    "single": r"""
 #include <hip/hip_runtime.h>
 #include "dust_noise.hpp"
 __global__ void gen(float* out, unsigned t, int K, dust::NoiseKey key) {
@@ -35,16 +39,35 @@ __global__ void gen(float* out, unsigned t, int K, dust::NoiseKey key) {
   }
   out[blockIdx.x * blockDim.x + threadIdx.x] = r;
 }
-"""
+""",
+    "paired": r"""
+#include <hip/hip_runtime.h>
+#include "dust_noise.hpp"
+__global__ void gen(float* out, unsigned t, int K, dust::NoiseKey key) {
+  const unsigned q = threadIdx.x;
+  float r = 0.f;
+  for (int n = 0; n < K; n += 4) {
+#pragma unroll
+    for (int j = 0; j < 4; j += 2) {
+      float4 a, b;
+      dust::noise_quad_x2(q, (unsigned)(n + j), q, (unsigned)(n + j + 1), t, key, a, b);
+      r += a.x + a.y + a.z + a.w;
+      r += b.x + b.y + b.z + b.w;
+    }
+  }
+  out[blockIdx.x * blockDim.x + threadIdx.x] = r;
+}
+""",
+}
 
 
-@pytest.fixture(scope="module")
-def loop_ops(tmp_path_factory):
+@pytest.fixture(scope="module", params=sorted(KERNELS))
+def loop_ops(request, tmp_path_factory):
     if shutil.which(HIPCC) is None and not os.path.exists(HIPCC):
         pytest.skip("hipcc not available")
     d = tmp_path_factory.mktemp("isa")
     src, asm = d / "gen.hip", d / "gen.s"
-    src.write_text(KERNEL)
+    src.write_text(KERNELS[request.param])
     flags = [f for f in build.COMMON_FLAGS]
     res = subprocess.run([HIPCC, *flags, "--cuda-device-only", "-S", "-o", str(asm), str(src)],
                          capture_output=True, text=True)

@@ -244,6 +244,8 @@ __device__ __forceinline__ float4 load_delta4(const float* __restrict__ drow,
 // and Q_n = ||a_t^n||^2, then one wave reduction yields the 16 totals.  QN
 // false (local scoring, whose score is linear in the jitter): no Q.
 
+static_assert(kNoiseBatch % 2 == 0, "noise indices are generated in pairs");
+
 template <bool QN>
 __global__ __launch_bounds__(256) void jitter_loss_kernel(
     const float* __restrict__ delta, const uint16_t* __restrict__ tgt, int32_t vec, int32_t T,
@@ -287,29 +289,34 @@ __global__ __launch_bounds__(256) void jitter_loss_kernel(
         m.w = (c + 3 < d_out) ? 1.f : 0.f;
       }
 #pragma unroll
-      for (int j = 0; j < kNoiseBatch; ++j) {
-        const int32_t n = nb + j;
-        if (n < n_end) {
-          float4 a = noise_quad((uint32_t)q, (uint32_t)t, (uint32_t)n, key);
-          if (ragged) {
-            a.x *= m.x;
-            a.y *= m.y;
-            a.z *= m.z;
-            a.w *= m.w;
-          }
-          float pj = p[j];
-          pj = __builtin_fmaf(d.x, a.x, pj);
-          pj = __builtin_fmaf(d.y, a.y, pj);
-          pj = __builtin_fmaf(d.z, a.z, pj);
-          pj = __builtin_fmaf(d.w, a.w, pj);
-          p[j] = pj;
-          if (QN) {
-            float sj = s[j];
-            sj = __builtin_fmaf(a.x, a.x, sj);
-            sj = __builtin_fmaf(a.y, a.y, sj);
-            sj = __builtin_fmaf(a.z, a.z, sj);
-            sj = __builtin_fmaf(a.w, a.w, sj);
-            s[j] = sj;
+      for (int j = 0; j < kNoiseBatch; j += 2) {
+        float4 an[2];
+        noise_quad_x2((uint32_t)q, (uint32_t)(nb + j), (uint32_t)q, (uint32_t)(nb + j + 1),
+                      (uint32_t)t, key, an[0], an[1]);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          if (nb + j + h < n_end) {
+            float4 a = an[h];
+            if (ragged) {
+              a.x *= m.x;
+              a.y *= m.y;
+              a.z *= m.z;
+              a.w *= m.w;
+            }
+            float pj = p[j + h];
+            pj = __builtin_fmaf(d.x, a.x, pj);
+            pj = __builtin_fmaf(d.y, a.y, pj);
+            pj = __builtin_fmaf(d.z, a.z, pj);
+            pj = __builtin_fmaf(d.w, a.w, pj);
+            p[j + h] = pj;
+            if (QN) {
+              float sj = s[j + h];
+              sj = __builtin_fmaf(a.x, a.x, sj);
+              sj = __builtin_fmaf(a.y, a.y, sj);
+              sj = __builtin_fmaf(a.z, a.z, sj);
+              sj = __builtin_fmaf(a.w, a.w, sj);
+              s[j + h] = sj;
+            }
           }
         }
       }
@@ -851,10 +858,18 @@ __global__ __launch_bounds__(256) void fused_g0_kernel(
       v[i] = 0.f;
       v[NB + i] = 0.f;
       const int32_t n = nb + i;
+      if (n < n_end) {
+#pragma unroll
+        for (int j = 0; j + 1 < QPL; j += 2)
+          noise_quad_x2((uint32_t)(lane + 64 * j), (uint32_t)n, (uint32_t)(lane + 64 * (j + 1)),
+                        (uint32_t)n, (uint32_t)t, key, a[i][j], a[i][j + 1]);
+        if (QPL & 1)
+          a[i][QPL - 1] =
+              noise_quad((uint32_t)(lane + 64 * (QPL - 1)), (uint32_t)t, (uint32_t)n, key);
+      }
 #pragma unroll
       for (int j = 0; j < QPL; ++j) {
         if (n < n_end) {
-          a[i][j] = noise_quad((uint32_t)(lane + 64 * j), (uint32_t)t, (uint32_t)n, key);
           if (!FULL) {
             a[i][j].x *= msk[j].x;
             a[i][j].y *= msk[j].y;
@@ -1410,6 +1425,7 @@ __global__ __launch_bounds__(256) void head_ce_kernel(
     float* __restrict__ rho, float* __restrict__ g32, uint16_t* __restrict__ g_hi,
     uint16_t* __restrict__ g_lo) {
   constexpr int NB = ANTI ? DUST_HEAD_NB : 8, M = ANTI ? 2 * NB : 8;
+  static_assert(NB % 2 == 0, "noise indices are generated in pairs");
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int waves = blockDim.x >> 6;
   const int32_t t = blockIdx.x;
@@ -1455,10 +1471,13 @@ __global__ __launch_bounds__(256) void head_ce_kernel(
       float4 a[NB];
       float v[M], ay[NB];
 #pragma unroll
+      for (int i = 0; i < NB; i += 2)
+        noise_quad_x2((uint32_t)(j * 64 + lane), (uint32_t)(nb + i), (uint32_t)(j * 64 + lane),
+                      (uint32_t)(nb + i + 1), (uint32_t)t, key, a[i], a[i + 1]);
+#pragma unroll
       for (int i = 0; i < NB; ++i) {
         const int32_t n = nb + i;
-        a[i] = (n < K_n) ? noise_quad((uint32_t)(j * 64 + lane), (uint32_t)t, (uint32_t)n, key)
-                         : make_float4(0.f, 0.f, 0.f, 0.f);
+        if (n >= K_n) a[i] = make_float4(0.f, 0.f, 0.f, 0.f);
         if (ANTI) {
           float p0, m0, p1, m1, p2, m2, p3, m3;
           expm1_pm<SMALL>(sigma * a[i].x, p0, m0);

@@ -91,4 +91,42 @@ __device__ __forceinline__ float4 noise_quad(uint32_t q, uint32_t t, uint32_t n,
   return make_float4(a.x, a.y, b.x, b.y);
 }
 
+// Two noise quads at once, (quad qa, noise index na) and (qb, nb) of token
+// t, their Philox rounds advanced together.  The values are those of two
+// noise_quad calls; interleaving the two dependency chains gives the
+// scheduler independent multiplies to issue while a round's products are in
+// flight (each stream alone has only two per round).
+__device__ __forceinline__ void noise_quad_x2(uint32_t qa, uint32_t na, uint32_t qb, uint32_t nb,
+                                              uint32_t t, NoiseKey key, float4& A, float4& B) {
+  uint32_t k0 = key.k0, k1 = key.k1;
+  uint32_t a0 = qa, a1 = t, a2 = na, a3 = 0u;
+  uint32_t b0 = qb, b1 = t, b2 = nb, b3 = 0u;
+#pragma unroll
+  for (int round = 0; round < 10; ++round) {
+    uint32_t ha0, la0, ha1, la1, hb0, lb0, hb1, lb1;
+    mul_wide(kPhiloxM0, a0, ha0, la0);
+    mul_wide(kPhiloxM0, b0, hb0, lb0);
+    mul_wide(kPhiloxM1, a2, ha1, la1);
+    mul_wide(kPhiloxM1, b2, hb1, lb1);
+    const uint32_t ya0 = round < 2 ? ha1 ^ a1 ^ k0 : xor3(ha1, a1, k0);
+    const uint32_t yb0 = round < 2 ? hb1 ^ b1 ^ k0 : xor3(hb1, b1, k0);
+    const uint32_t ya2 = round < 3 ? ha0 ^ a3 ^ k1 : xor3(ha0, a3, k1);
+    const uint32_t yb2 = round < 3 ? hb0 ^ b3 ^ k1 : xor3(hb0, b3, k1);
+    a0 = ya0;
+    a1 = la1;
+    a2 = ya2;
+    a3 = la0;
+    b0 = yb0;
+    b1 = lb1;
+    b2 = yb2;
+    b3 = lb0;
+    k0 += kPhiloxW0;
+    k1 += kPhiloxW1;
+  }
+  const float2 a_lo = box_muller(a0, a1), b_lo = box_muller(b0, b1);
+  const float2 a_hi = box_muller(a2, a3), b_hi = box_muller(b2, b3);
+  A = make_float4(a_lo.x, a_lo.y, a_hi.x, a_hi.y);
+  B = make_float4(b_lo.x, b_lo.y, b_hi.x, b_hi.y);
+}
+
 }  // namespace dust
