@@ -43,6 +43,7 @@
 #include <stdint.h>
 
 #include <mutex>
+#include <type_traits>
 #include <vector>
 
 #include "dust.h"
@@ -279,48 +280,63 @@ __global__ __launch_bounds__(256) void jitter_loss_kernel(
       p[j] = 0.f;
       s[j] = 0.f;
     }
-    for (int32_t q = lane; q < nq; q += 64) {
-      const float4 d = load_delta4(drow, trow, 4 * q, d_out, !ragged);
-      float4 m = make_float4(1.f, 1.f, 1.f, 1.f);
-      if (ragged) {
-        const int c = 4 * q;
-        m.y = (c + 1 < d_out) ? 1.f : 0.f;
-        m.z = (c + 2 < d_out) ? 1.f : 0.f;
-        m.w = (c + 3 < d_out) ? 1.f : 0.f;
-      }
+    // ALL: every noise index of the batch is in range; RAG: d_out is not a
+    // multiple of 4 (or delta is unaligned).  Both are uniform, and the
+    // common case (ALL, !RAG) runs without a branch between the draws.
+    auto sweep = [&](auto all_c, auto rag_c) {
+      constexpr bool ALL = decltype(all_c)::value, RAG = decltype(rag_c)::value;
+      for (int32_t q = lane; q < nq; q += 64) {
+        const float4 d = load_delta4(drow, trow, 4 * q, d_out, !RAG);
+        float4 m = make_float4(1.f, 1.f, 1.f, 1.f);
+        if (RAG) {
+          const int c = 4 * q;
+          m.y = (c + 1 < d_out) ? 1.f : 0.f;
+          m.z = (c + 2 < d_out) ? 1.f : 0.f;
+          m.w = (c + 3 < d_out) ? 1.f : 0.f;
+        }
 #pragma unroll
-      for (int j = 0; j < kNoiseBatch; j += 2) {
-        float4 an[2];
-        noise_quad_x2((uint32_t)q, (uint32_t)(nb + j), (uint32_t)q, (uint32_t)(nb + j + 1),
-                      (uint32_t)t, key, an[0], an[1]);
+        for (int j = 0; j < kNoiseBatch; j += 2) {
+          float4 an[2];
+          noise_quad_x2((uint32_t)q, (uint32_t)(nb + j), (uint32_t)q, (uint32_t)(nb + j + 1),
+                        (uint32_t)t, key, an[0], an[1]);
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          if (nb + j + h < n_end) {
-            float4 a = an[h];
-            if (ragged) {
-              a.x *= m.x;
-              a.y *= m.y;
-              a.z *= m.z;
-              a.w *= m.w;
-            }
-            float pj = p[j + h];
-            pj = __builtin_fmaf(d.x, a.x, pj);
-            pj = __builtin_fmaf(d.y, a.y, pj);
-            pj = __builtin_fmaf(d.z, a.z, pj);
-            pj = __builtin_fmaf(d.w, a.w, pj);
-            p[j + h] = pj;
-            if (QN) {
-              float sj = s[j + h];
-              sj = __builtin_fmaf(a.x, a.x, sj);
-              sj = __builtin_fmaf(a.y, a.y, sj);
-              sj = __builtin_fmaf(a.z, a.z, sj);
-              sj = __builtin_fmaf(a.w, a.w, sj);
-              s[j + h] = sj;
+          for (int h = 0; h < 2; ++h) {
+            if (ALL || nb + j + h < n_end) {
+              float4 a = an[h];
+              if (RAG) {
+                a.x *= m.x;
+                a.y *= m.y;
+                a.z *= m.z;
+                a.w *= m.w;
+              }
+              float pj = p[j + h];
+              pj = __builtin_fmaf(d.x, a.x, pj);
+              pj = __builtin_fmaf(d.y, a.y, pj);
+              pj = __builtin_fmaf(d.z, a.z, pj);
+              pj = __builtin_fmaf(d.w, a.w, pj);
+              p[j + h] = pj;
+              if (QN) {
+                float sj = s[j + h];
+                sj = __builtin_fmaf(a.x, a.x, sj);
+                sj = __builtin_fmaf(a.y, a.y, sj);
+                sj = __builtin_fmaf(a.z, a.z, sj);
+                sj = __builtin_fmaf(a.w, a.w, sj);
+                s[j + h] = sj;
+              }
             }
           }
         }
       }
-    }
+    };
+    const bool all = nb + kNoiseBatch <= n_end;
+    if (all && !ragged)
+      sweep(std::true_type{}, std::false_type{});
+    else if (all)
+      sweep(std::true_type{}, std::true_type{});
+    else if (!ragged)
+      sweep(std::false_type{}, std::false_type{});
+    else
+      sweep(std::false_type{}, std::true_type{});
     wave_reduce16(p, lane);
     if (QN) wave_reduce16(s, lane);
     const int32_t n = nb + ((lane >> 2) & 15);
