@@ -15,7 +15,8 @@ COMMON_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]
-HIPCC_FLAGS = COMMON_FLAGS + ["-fPIC", "-shared"]
+# -z defs: a symbol the library references but does not define fails the link
+HIPCC_FLAGS = COMMON_FLAGS + ["-fPIC", "-shared", "-Wl,-z,defs"]
 
 
 def build_library(verbose: bool = False) -> str:
