@@ -307,6 +307,8 @@ __global__ __launch_bounds__(256) void tile_kernel(
 // the first run, began before the tile and does not go on past it; that
 // tile's wave (one per tile and 256-column chunk) sums the run's partials in
 // tile order and writes the row (times scale).
+constexpr int32_t kFixupBlock = 64;  // tile sums added per block in the fix-up
+
 template <bool VEC>
 __global__ __launch_bounds__(256) void fixup_kernel(const int32_t* __restrict__ sid,
                                                     const int32_t* __restrict__ start, int32_t T,
@@ -327,8 +329,15 @@ __global__ __launch_bounds__(256) void fixup_kernel(const int32_t* __restrict__ 
   const int32_t s = start[v];
   const int32_t kb = s / P;
   float4 sum = load_cols<VEC>(part + ((int64_t)kb * 2 + (s == kb * P ? 0 : 1)) * d, c, d);
-  for (int32_t kk = kb + 1; kk <= (int32_t)k; ++kk)
-    sum = add4(sum, load_cols<VEC>(part + (int64_t)kk * 2 * d, c, d));
+  // the later tiles' sums in blocks of kFixupBlock, each block added first:
+  // a run over n tiles then rounds like kFixupBlock + n / kFixupBlock terms
+  // instead of n (the heaviest id of a long Zipfian batch spans ~20,000)
+  for (int32_t kk = kb + 1; kk <= (int32_t)k;) {
+    const int32_t kend = min(kk + kFixupBlock - 1, (int32_t)k);
+    float4 blk = load_cols<VEC>(part + (int64_t)kk * 2 * d, c, d);
+    for (++kk; kk <= kend; ++kk) blk = add4(blk, load_cols<VEC>(part + (int64_t)kk * 2 * d, c, d));
+    sum = add4(sum, blk);
+  }
   store_cols<VEC>(G_E + (int64_t)v * d, c, d, mul4(scale, sum));
 }
 
