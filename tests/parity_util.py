@@ -12,7 +12,13 @@ to that relative level over the whole tensor, and each token on its own
                    <= ROW_TOL[dtype]   (rows of G_W: max over channels c)
 
 The per-row form is the one that catches a single wrong token, a wrong tail
-quad or a wrong sequence, which the whole-tensor norm dilutes.  A row whose
+quad or a wrong sequence, which the whole-tensor norm dilutes.  A row's
+error is measured against the larger of its own norm and ROW_FLOOR (1%) of
+the root-mean-square row norm: an fp32 sum rounds in proportion to the
+magnitudes of its terms, not to its value, so a row whose terms nearly
+cancel (a single-element row of G_W when d_in = 1, say) would otherwise
+show its rounding at any relative size, while a wrong row is still off by
+about the typical row norm and fails by a wide margin.  A tensor whose
 reference is exactly zero is compared in absolute terms.
 
 The per-row bar of the fp32 path is not the whole-tensor 1e-5: one token's
@@ -32,6 +38,7 @@ import numpy as np
 
 TOL = {"f32": 1e-5, "bf16": 2e-3}
 ROW_TOL = {"f32": 1e-4, "bf16": 2e-3}
+ROW_FLOOR = 0.01
 
 
 def rel(a, b):
@@ -40,7 +47,8 @@ def rel(a, b):
 
 
 def rows_rel(a, b):
-    """Largest per-row relative error (rows along the first axis) and the
+    """Largest per-row relative error (rows along the first axis; each row
+    against the larger of its norm and ROW_FLOOR of the RMS row norm) and the
     row where it occurs."""
     a = np.asarray(a, dtype=np.float64)
     b = np.asarray(b, dtype=np.float64)
@@ -51,6 +59,8 @@ def rows_rel(a, b):
     b = b.reshape(b.shape[0], -1)
     num = np.linalg.norm(a - b, axis=1)
     den = np.linalg.norm(b, axis=1)
+    floor = ROW_FLOOR * float(np.sqrt(np.mean(den ** 2))) if den.size else 0.0
+    den = np.maximum(den, floor)
     err = num / np.where(den > 0, den, 1.0)
     i = int(np.argmax(err)) if err.size else 0
     return (float(err[i]) if err.size else 0.0), i
