@@ -1,7 +1,7 @@
 // dust_kernels.hip -- gfx950 kernels and the device-side entry points of
-// libdust.so (dust_estimate, dust_estimate_local, dust_estimate_head,
-// dust_estimate_embedding, dust_reassemble_embedding, dust_noise_fill,
-// dust_set_timing_events).
+// libdust.so (dust_estimate, dust_estimate_noalloc, dust_estimate_local,
+// dust_estimate_head, dust_estimate_embedding, dust_reassemble_embedding,
+// dust_noise_fill, dust_set_timing_events, dust_profile_begin / _end).
 //
 // The estimator ("Dust: every token is a member of the population", section
 // "Perturb the activations, not the weights") runs on the caller's stream as
@@ -25,13 +25,16 @@
 //                  -1/(K sigma) (r^(2n) - r^(2n+1)) (antithetic) or
 //                  -1/(K sigma) r^(n)
 //   reweight       g_t = sum_n weight_(t,n) a_t^n, the noise regenerated
-// unless the pairs are antithetic, the chains fill the chip and the caller's
-// workspace holds the partials (dust_workspace_bytes_seq), when one pass
-// walks each sequence backwards:
-//   chain_g        per (sequence, group of 16 pairs), one pair per wave:
-//                  a_t generated once, P_t, R_t = P_t + gamma R_(t+1), and
-//                  the group's partial g_t = sum_p R_t^p a_t^p
+// unless the chains (antithetic pairs, or plain draws) fill the chip and
+// the caller's workspace holds the partials (dust_workspace_bytes_seq), when
+// one pass walks each sequence backwards:
+//   chain_g        per (sequence, group of 16 chains), two chains per wave:
+//                  a_t generated once, P_t (and Q_t), the chain's discounted
+//                  sum R_t = rho_t + gamma R_(t+1), and the group's partial
+//                  sums of R_t a_t (and, for plain draws, of a_t and rho_t)
 //   chain_sum      g_t = 2/K x the groups' partials, added in group order
+//                  (plain draws: the draws' mean scanned into M_t first, then
+//                  g_t = -1/(K sigma) (sum R a - M_t sum a))
 // and last
 //   outer          G_W = sum_t g_t x_t^T on MFMA (bf16 hi/lo split of g),
 //                  split over tokens, partials summed in a fixed order
