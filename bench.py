@@ -30,6 +30,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import re
 import os
 import sys
 import time
@@ -53,11 +54,19 @@ CPU_THREADS_MAX = 16
 PROFILE_STEPS = 3
 
 
+def _code_only(text: str) -> str:
+    """The source without its comments and blank space, so that a change to
+    a comment alone does not count as a change of the kernels."""
+    token = re.compile(r'"(?:\\.|[^"\\\n])*"|/\*.*?\*/|//[^\n]*', re.S)
+    text = token.sub(lambda m: m.group(0) if m.group(0).startswith('"') else " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

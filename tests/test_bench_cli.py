@@ -46,3 +46,15 @@ def test_unknown_config_is_refused():
     res = run("--configs", "bf16_layer,nope", "--cpu-budget", "0")
     assert res.returncode != 0
     assert "unknown workload" in res.stderr
+
+
+def test_kernel_hash_ignores_comments_only():
+    """The committed HBM-traffic figures stay valid across comment edits of
+    the kernel sources but not across code edits."""
+    sys.path.insert(0, ROOT)
+    import bench
+    code = 'int a = 1; // note\n/* block\n comment */ const char* s = "//x"; int b;\n'
+    assert bench._code_only(code) == bench._code_only(
+        'int a = 1; // other note\n/* another */ const char* s = "//x";\n  int b;')
+    assert bench._code_only(code) != bench._code_only(code.replace("int b;", "int c;"))
+    assert bench._code_only(code) != bench._code_only(code.replace('"//x"', '"//y"'))
