@@ -41,6 +41,21 @@
  * rho_t^(i) = -<e_t, Delta o_t^(i)>, evaluated literally; steps 3-6 then
  * run unchanged (dust_oracle_estimate_local).
  *
+ * The same step's own form recomputes the attention: the internals
+ * (queries, keys, values) are jittered, only their block's attention is
+ * recomputed from cached activations, and the change of the attention
+ * output is what the error estimate scores.  Reading used: one block's
+ * causal softmax attention with H heads of width d_head inside each
+ * sequence, o_s = sum_{t <= s} softmax_t(<q_s, k_t> / sqrt(d_head)) v_t per
+ * head; the site (queries, keys or values, a [T][H d_head] array whose head
+ * h holds channels h d_head .. h d_head + d_head - 1) takes draw i's jitter
+ * s_i sigma a_t^(n(i)) over its channels; every output of the sequence is
+ * recomputed literally with the jittered site, and the score of token s is
+ * rho_s^(i) = -sum_h <e_s,h, o'_s,h - o_s,h>, e the supplied error estimate
+ * of the attention output [T][H d_head]; steps 3-6 then run unchanged, the
+ * site's weight gradient being sum_t g_t x_t^T with x the block's input
+ * (dust_oracle_estimate_attention).
+ *
  * A third scoring rule is the model's head: cross-entropy of the logits
  * z_t = W x_t against a label y_t, its logits perturbed in 256-column
  * slabs of the vocabulary ("What the released code actually does", step 5).
@@ -182,6 +197,9 @@ typedef struct {
   const float *X, *W, *target;
   const float *E;         /* error estimate [T][d_out] (local scoring only) */
   const int32_t *ids;     /* token ids [T] (embedding only; W is the table) */
+  const float *Qa, *Ka, *Va; /* cached attention activations [T][H d_head] */
+  int64_t heads, d_head;  /* attention site: heads and head width */
+  int32_t site;           /* 0 queries, 1 keys, 2 values */
   int64_t T, d_in, d_out, seq_len;
   int32_t K;
   double sigma, gamma;
@@ -534,6 +552,171 @@ int dust_oracle_estimate_local(const float *X, const float *E, int64_t T,
   run_phase(&j, phase_credit);
   run_phase(&j, phase_error);
   run_phase(&j, phase_outer);
+  return 0;
+}
+
+/* Causal softmax attention of one head over one sequence of L tokens:
+ * out_s = sum_{t <= s} w_st v_t, w_st = exp(l_st - max) / sum, l_st =
+ * <q_s, k_t> / sqrt(dh).  q, k, v, out are [L][dh]; w is scratch [L]. */
+static void attend(const double *q, const double *k, const double *v, int64_t L,
+                   int64_t dh, double *w, double *out) {
+  const double scale = 1.0 / sqrt((double)dh);
+  for (int64_t s = 0; s < L; ++s) {
+    double m = -INFINITY;
+    for (int64_t t = 0; t <= s; ++t) {
+      double l = 0.0;
+      for (int64_t c = 0; c < dh; ++c) l += q[s * dh + c] * k[t * dh + c];
+      w[t] = l * scale;
+      if (w[t] > m) m = w[t];
+    }
+    double z = 0.0;
+    for (int64_t t = 0; t <= s; ++t) {
+      w[t] = exp(w[t] - m);
+      z += w[t];
+    }
+    for (int64_t c = 0; c < dh; ++c) out[s * dh + c] = 0.0;
+    for (int64_t t = 0; t <= s; ++t)
+      for (int64_t c = 0; c < dh; ++c) out[s * dh + c] += (w[t] / z) * v[t * dh + c];
+  }
+}
+
+/* Scores through a recomputed attention, in place of steps 1-2: for every
+ * sequence, head and draw, the jittered site's attention is recomputed and
+ * its output change scored against the error estimate.  Sequences split
+ * across threads. */
+static void *phase_attn_score(void *p) {
+  worker_arg *wa = (worker_arg *)p;
+  oracle_job *j = wa->job;
+  const int64_t L = j->seq_len, H = j->heads, dh = j->d_head, D = H * dh;
+  const int64_t seq0 = j->t_begin / L, seq1 = j->t_end / L;
+  double *A = (double *)malloc(sizeof(double) * (size_t)(L * D));
+  double *act[3], *jit[3];
+  for (int u = 0; u < 3; ++u) {
+    act[u] = (double *)malloc(sizeof(double) * (size_t)(H * L * dh));
+    jit[u] = (double *)malloc(sizeof(double) * (size_t)(L * dh));
+  }
+  double *clean = (double *)malloc(sizeof(double) * (size_t)(H * L * dh));
+  double *o2 = (double *)malloc(sizeof(double) * (size_t)(L * dh));
+  double *w = (double *)malloc(sizeof(double) * (size_t)L);
+  const float *src[3] = {j->Qa, j->Ka, j->Va};
+  for (int64_t sq = seq0 + wa->tid; sq < seq1; sq += j->n_threads) {
+    const int64_t first = sq * L;
+    /* the cached activations of this sequence, per head, and the clean
+       outputs */
+    for (int u = 0; u < 3; ++u)
+      for (int64_t h = 0; h < H; ++h)
+        for (int64_t t = 0; t < L; ++t)
+          for (int64_t c = 0; c < dh; ++c)
+            act[u][(h * L + t) * dh + c] = (double)src[u][(first + t) * D + h * dh + c];
+    for (int64_t h = 0; h < H; ++h)
+      attend(act[0] + h * L * dh, act[1] + h * L * dh, act[2] + h * L * dh, L, dh, w,
+             clean + h * L * dh);
+    for (int64_t t = 0; t < L; ++t)
+      for (int32_t i = 0; i < j->K; ++i) j->rho[(first + t - j->t_begin) * j->K + i] = 0.0;
+    int32_t last_n = -1;
+    for (int32_t i = 0; i < j->K; ++i) {
+      const int32_t n = noise_index(j, i);
+      if (n != last_n) {
+        for (int64_t t = 0; t < L; ++t)
+          noise_vector(j->seed, (uint32_t)n, (uint32_t)(first + t), D, A + t * D);
+        last_n = n;
+      }
+      const double amp = draw_sign(j, i) * j->sigma;
+      for (int64_t h = 0; h < H; ++h) {
+        const double *in[3];
+        for (int u = 0; u < 3; ++u) in[u] = act[u] + h * L * dh;
+        /* the jittered site of this head */
+        double *site = jit[j->site];
+        for (int64_t t = 0; t < L; ++t)
+          for (int64_t c = 0; c < dh; ++c)
+            site[t * dh + c] = in[j->site][t * dh + c] + amp * A[t * D + h * dh + c];
+        in[j->site] = site;
+        attend(in[0], in[1], in[2], L, dh, w, o2);
+        const double *oc = clean + h * L * dh;
+        for (int64_t s = 0; s < L; ++s) {
+          double score = 0.0;
+          for (int64_t c = 0; c < dh; ++c)
+            score -= (double)j->E[(first + s) * D + h * dh + c] *
+                     (o2[s * dh + c] - oc[s * dh + c]);
+          j->rho[(first + s - j->t_begin) * j->K + i] += score;
+        }
+      }
+    }
+  }
+  free(A);
+  for (int u = 0; u < 3; ++u) {
+    free(act[u]);
+    free(jit[u]);
+  }
+  free(clean);
+  free(o2);
+  free(w);
+  return NULL;
+}
+
+/*
+ * The estimator with scores through a recomputed attention over the
+ * sequences seq_begin..seq_end-1 (0, 0 for all).  Qa, Ka, Va [T][heads
+ * d_head] are the cached queries, keys and values of one block (fp32, as the
+ * GPU receives them); site 0, 1 or 2 jitters the queries, keys or values;
+ * E [T][heads d_head] is the supplied error estimate of the attention
+ * output.  X [T][d_in] (the block's input) gives the site's weight gradient
+ * G [heads d_head][d_in]; with X NULL, G is left untouched.  Outputs as for
+ * dust_oracle_estimate_local.  Returns 0, or -1 on an argument error.
+ */
+int dust_oracle_estimate_attention(const float *X, const float *Qa, const float *Ka,
+                                   const float *Va, const float *E, int64_t T,
+                                   int64_t d_in, int64_t heads, int64_t d_head,
+                                   int64_t seq_len, int32_t site, int32_t K,
+                                   float sigma, float gamma, uint64_t seed,
+                                   int32_t antithetic, int64_t seq_begin,
+                                   int64_t seq_end, int32_t n_threads, double *G,
+                                   double *rho, double *reward, double *g) {
+  if (!Qa || !Ka || !Va || !E || !rho || !reward || !g || (X && !G)) return -1;
+  if (T <= 0 || heads <= 0 || d_head <= 0 || seq_len <= 0 || T % seq_len != 0)
+    return -1;
+  if (X && d_in <= 0) return -1;
+  if (site < 0 || site > 2) return -1;
+  if (K < 2 || (antithetic && K % 2 != 0)) return -1;
+  int64_t n_seq = T / seq_len;
+  if (seq_end <= seq_begin) {
+    seq_begin = 0;
+    seq_end = n_seq;
+  }
+  if (seq_begin < 0 || seq_end > n_seq) return -1;
+  if (n_threads < 1) n_threads = 1;
+
+  oracle_job j;
+  memset(&j, 0, sizeof(j));
+  j.X = X;
+  j.Qa = Qa;
+  j.Ka = Ka;
+  j.Va = Va;
+  j.E = E;
+  j.T = T;
+  j.d_in = d_in;
+  j.d_out = heads * d_head;
+  j.heads = heads;
+  j.d_head = d_head;
+  j.site = site;
+  j.seq_len = seq_len;
+  j.K = K;
+  j.sigma = (double)sigma;
+  j.gamma = (double)gamma;
+  j.seed = seed;
+  j.antithetic = antithetic;
+  j.t_begin = seq_begin * seq_len;
+  j.t_end = seq_end * seq_len;
+  j.n_threads = n_threads;
+  j.rho = rho;
+  j.reward = reward;
+  j.g = g;
+  j.G = G;
+
+  run_phase(&j, phase_attn_score);
+  run_phase(&j, phase_credit);
+  run_phase(&j, phase_error);
+  if (X) run_phase(&j, phase_outer);
   return 0;
 }
 

@@ -69,6 +69,11 @@ def _load():
         ctypes.c_uint64, ctypes.c_int32, ctypes.c_double, i64, i64, ctypes.c_int32, f64p, f64p,
         f64p, f64p, f64p]
     lib.dust_oracle_estimate_embedding.restype = ctypes.c_int
+    lib.dust_oracle_estimate_attention.argtypes = [
+        f32p, f32p, f32p, f32p, f32p, i64, i64, i64, i64, i64, ctypes.c_int32, ctypes.c_int32,
+        ctypes.c_float, ctypes.c_float, ctypes.c_uint64, ctypes.c_int32, i64, i64, ctypes.c_int32,
+        f64p, f64p, f64p, f64p]
+    lib.dust_oracle_estimate_attention.restype = ctypes.c_int
     lib.dust_oracle_true_gradient.argtypes = [f32p, f32p, f32p, i64, i64, i64, f64p, f64p]
     lib.dust_oracle_true_gradient.restype = None
     _lib = lib
@@ -179,6 +184,53 @@ def estimate_local(X, E, *, K: int, sigma: float, gamma: float, seed: int,
     if rc != 0:
         raise ValueError("oracle rejected its arguments")
     return {"G": G, "rho": rho, "reward": reward, "g": g, "threads": th}
+
+
+ATTENTION_SITES = {"query": 0, "key": 1, "value": 2}
+
+
+def estimate_attention(X, q, k, v, E, *, heads: int, site: str, K: int, sigma: float,
+                       gamma: float, seed: int, antithetic: bool, seq_len: int,
+                       seq_range=None, threads: int | None = None):
+    """Run the fp64 oracle with scores through a recomputed attention: the
+    cached queries q, keys k and values v [T, heads*d_head] of one block's
+    causal attention (head h on columns h*d_head .. (h+1)*d_head - 1), the
+    site ("query", "key" or "value") jittered, and every draw's change of
+    the attention output scored against the error estimate E [T,
+    heads*d_head].  X [T,d_in] (or None) is the block's input for the site's
+    weight gradient.  Returns a dict of fp64 arrays: G [heads*d_head,d_in]
+    (absent without X), rho [n,K] (the scores), reward [n,K], g [n,
+    heads*d_head]."""
+    lib = _load()
+    q, k, v, E = (np.ascontiguousarray(a, dtype=np.float32) for a in (q, k, v, E))
+    T, D = q.shape
+    assert k.shape == v.shape == E.shape == (T, D) and D % heads == 0 and T % seq_len == 0
+    d_head = D // heads
+    if X is not None:
+        X = np.ascontiguousarray(X, dtype=np.float32)
+        assert X.shape[0] == T
+    d_in = X.shape[1] if X is not None else 0
+    n_seq = T // seq_len
+    s0, s1 = (0, n_seq) if seq_range is None else seq_range
+    n_tok = (s1 - s0) * seq_len
+    G = np.zeros((D, max(d_in, 1)), dtype=np.float64)
+    rho = np.zeros((n_tok, K), dtype=np.float64)
+    reward = np.zeros((n_tok, K), dtype=np.float64)
+    g = np.zeros((n_tok, D), dtype=np.float64)
+    th = default_threads() if threads is None else threads
+    rc = lib.dust_oracle_estimate_attention(
+        _ptr(X, ctypes.c_float) if X is not None else None, _ptr(q, ctypes.c_float),
+        _ptr(k, ctypes.c_float), _ptr(v, ctypes.c_float), _ptr(E, ctypes.c_float), T, d_in,
+        heads, d_head, seq_len, ATTENTION_SITES[site], K, ctypes.c_float(sigma),
+        ctypes.c_float(gamma), ctypes.c_uint64(seed), int(bool(antithetic)), s0, s1, th,
+        _ptr(G, ctypes.c_double) if X is not None else None, _ptr(rho, ctypes.c_double),
+        _ptr(reward, ctypes.c_double), _ptr(g, ctypes.c_double))
+    if rc != 0:
+        raise ValueError("oracle rejected its arguments")
+    out = {"rho": rho, "reward": reward, "g": g, "threads": th}
+    if X is not None:
+        out["G"] = G
+    return out
 
 
 def estimate_head(X, W, labels, *, K: int, sigma: float, seed: int, antithetic: bool,
