@@ -16,9 +16,10 @@ population of 4096 draws), and under "stages" every kernel of the headline
 step against its own roofline (ALU for the noise stages, MFMA for the two
 contractions, HBM for the rest), from a separate profiled pass.
 
-Other workloads (local scoring, the cross-entropy head, the token embedding)
-run with --workload: dust_estimate_local, dust_estimate_head (rows counted
-per 256-column slab, K*T*V/256) and dust_estimate_embedding calls.
+Other workloads (local scoring, the cross-entropy head, the token embedding,
+scores through a recomputed attention) run with --workload:
+dust_estimate_local, dust_estimate_head (rows counted per 256-column slab,
+K*T*V/256), dust_estimate_embedding and dust_estimate_attention calls.
 
 The JSON line: draw-token-rows per second (K*T per step), the ALU roofline of
 the dominant kernel timed with HIP events inside the timed region, the
@@ -44,7 +45,7 @@ CAL_COPY_BYTES = 256 << 20
 # every source the kernels and their launch configuration are built from
 KERNEL_SOURCES = ["token_activation_perturbation_amd/csrc/" + f for f in (
     "dust_kernels.hip", "dust_noise.hpp", "dust_gemm.hpp", "dust_reassemble.hpp",
-    "dust_plan.hpp")]
+    "dust_plan.hpp", "dust_attention.hpp")]
 # the estimator's five reference configurations, in order
 REFERENCE_CONFIGS = ["tiny_f32", "bf16_layer", "mlp_up_bf16", "qkv_credit_bf16",
                      "large_population_bf16"]
@@ -115,6 +116,19 @@ def cpu_baseline(w, inp, budget_s: float):
         def run(lo, hi):
             oracle.estimate_head(inp["X"], inp["W"], inp["labels"],
                                  token_range=(lo * unit, hi * unit), **kw)
+    elif w.attention:
+        # the oracle recomputes the attention for every draw, ~K L^2 d flops
+        # per sequence and head: the sample is every sequence (one thread
+        # each) with the first 2 of the K draws, whose scores do not depend
+        # on the others, so rows are 2 T per run
+        unit, n_units = w.seq_len, 1
+        threads = min(threads, w.n_seq)
+        kw = dict(K=2, sigma=w.sigma, gamma=w.gamma, seed=w.noise_seed,
+                  antithetic=w.antithetic, seq_len=w.seq_len, threads=threads)
+
+        def run(lo, hi):
+            oracle.estimate_attention(inp["X"], inp["q"], inp["k"], inp["v"], inp["E"],
+                                      heads=w.heads, site=w.site, **kw)
     else:
         unit, n_units = w.seq_len, w.n_seq
         if w.embedding:
@@ -148,6 +162,10 @@ def cpu_baseline(w, inp, budget_s: float):
     what = (f"{n * unit} of {w.T} tokens ({draws}) of the benchmarked workload")
     if repeats > 1:
         what = f"the whole benchmarked workload ({w.T} tokens x {draws}) {repeats} times"
+    if w.attention:
+        rows = 2 * w.T * repeats
+        what = (f"all {w.T} tokens ({w.n_seq} sequences, one thread each) x 2 of the {w.K} "
+                f"draws, {repeats} time(s)")
     return {"value": rows / elapsed, "unit": "draw-token-rows/s", "cores": threads,
             "kind": "oracle", "sample": f"{what}, fp64, {elapsed:.1f} s",
             "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
@@ -158,6 +176,8 @@ def cpu_baseline(w, inp, budget_s: float):
 def dominant_kernel(w, chain: bool) -> str:
     if w.head:
         return "head_ce_kernel"
+    if w.attention:
+        return "attn_score_kernel"
     if w.gamma == 0.0 or w.seq_len == 1:
         return "fused_g0_kernel"
     return "chain_g_kernel" if chain else "jitter_loss_kernel"
@@ -182,6 +202,9 @@ def measure(w, steps: int, warmup: int, want_inputs: bool = False):
 
     if w.embedding:
         table, tg, ids = to_dev("table"), to_dev("target"), to_dev("ids", cast=False)
+    elif w.attention:
+        X, q, k, v = to_dev("X"), to_dev("q"), to_dev("k"), to_dev("v")
+        E = to_dev("E", cast=False)
     elif w.local:
         # local scoring: the draws are scored against the error estimate E
         X, E = to_dev("X"), to_dev("E", cast=False)
@@ -195,9 +218,12 @@ def measure(w, steps: int, warmup: int, want_inputs: bool = False):
     base_bytes = dust.dust_workspace_bytes(w.T, w.d_in, w.d_out, w.K, w.antithetic, dt_code)
     ws_bytes = (dust.dust_embedding_workspace_bytes(w.T, w.V, w.d_out, w.K, w.antithetic, dt_code)
                 if w.embedding else base_bytes if w.head else
+                dust.dust_attention_workspace_bytes(w.T, w.d_in, w.heads, w.d_head, w.seq_len,
+                                                    w.site, w.K, w.antithetic)
+                if w.attention else
                 dust.dust_workspace_bytes_seq(w.T, w.d_in, w.d_out, w.seq_len, w.K, w.gamma,
                                               w.antithetic, dt_code))
-    chain = not w.embedding and not w.head and ws_bytes > base_bytes
+    chain = not w.embedding and not w.head and not w.attention and ws_bytes > base_bytes
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     kw = dict(K=w.K, sigma=w.sigma, gamma=w.gamma, seed=w.noise_seed, antithetic=w.antithetic,
               seq_len=w.seq_len)
@@ -210,6 +236,9 @@ def measure(w, steps: int, warmup: int, want_inputs: bool = False):
                                                 scale=1.0 / w.T, **kw)
         if w.local:
             return dust.dust_estimate_local(X, E, out=out, workspace=ws, **kw)
+        if w.attention:
+            return dust.dust_estimate_attention(X, q, k, v, E, heads=w.heads, site=w.site,
+                                                out=out, workspace=ws, **kw)
         if w.head:
             return dust.dust_estimate_head(X, W, labels, out=out, workspace=ws, **kw)
         return dust.dust_estimate(X, W, tg, out=out, workspace=ws, **kw)
@@ -264,6 +293,14 @@ def measure(w, steps: int, warmup: int, want_inputs: bool = False):
         if name in roofline.NOISE_STAGES:
             slots = roofline.noise_stage_slots(name, w.T, w.d_out, w.K, w.antithetic,
                                                local=w.local) * calls_per_step
+        elif name == "attn_score_kernel":
+            bound, work, _, _ = roofline.attention_score_bound(
+                w.site, w.T, w.seq_len, w.heads, w.d_head, w.K, w.antithetic)
+            if bound == "alu":
+                slots = work * calls_per_step
+        elif name in ("attn_probs_kernel", "attn_bmat_kernel"):
+            # fp32 contractions on the vector ALU: one FMA (2 flops) per slot
+            slots = e["flops"] / PROFILE_STEPS / 2.0
         st = roofline.stage_roofline(name, ms, e["flops"] / PROFILE_STEPS,
                                      e["bytes"] / PROFILE_STEPS, w.dtype, slots)
         st["calls"] = calls_per_step
@@ -271,27 +308,38 @@ def measure(w, steps: int, warmup: int, want_inputs: bool = False):
     stage_ms = sum(s["ms"] for s in stages)
 
     kernel = dominant_kernel(w, chain)
+    bound, unit = "alu", "T lane-slot/s"
     if w.head:
         slots = roofline.head_kernel_slots(w.T, w.d_out, w.K, w.antithetic)
         min_s = roofline.head_min_seconds(w.T, w.d_out, w.K, w.antithetic)
+        peak_per_s = roofline.PEAK_SLOTS_PER_S
+    elif w.attention:
+        # the score kernel's larger of its ALU and MFMA work; end to end,
+        # that kernel at its bound plus the regeneration of every noise
+        # value for g
+        bound, slots, peak_per_s, unit = roofline.attention_score_bound(
+            w.site, w.T, w.seq_len, w.heads, w.d_head, w.K, w.antithetic)
+        min_s = (slots / peak_per_s + roofline.reweight_kernel_slots(
+            w.T, w.d_out, w.K, w.antithetic) / roofline.PEAK_SLOTS_PER_S)
     else:
         slots = roofline.noise_stage_slots(kernel, w.T, w.d_out, w.K, w.antithetic,
                                            local=w.local)
         min_s = roofline.estimate_min_seconds(w.T, w.d_out, w.K, w.antithetic, local=w.local)
+        peak_per_s = roofline.PEAK_SLOTS_PER_S
     achieved = slots / (kernel_ms * 1e-3) / 1e12
-    peak = roofline.PEAK_SLOTS_PER_S / 1e12
+    peak = peak_per_s / 1e12
     res = {
         "workload": w.name,
         "value": w.rows / (ms_per_step * 1e-3),
         "ms_per_step": ms_per_step,
         "wall_ms_per_step": wall * 1e3 / steps,
         "roofline": {
-            "bound": "alu",
+            "bound": bound,
             "kernel": kernel,
             "kernel_ms": kernel_ms,
             "achieved": achieved,
             "peak": peak,
-            "unit": "T lane-slot/s",
+            "unit": unit,
             "frac": achieved / peak,
             "traffic": read_traffic(w.name, kernel),
             # one generation of every noise value at the ALU peak, over the step
@@ -376,7 +424,8 @@ def main():
         "metric": ("slab-draw-token-rows/sec (K*T*V/256) for dust_estimate_head" if w.head else
                    "draw-token-rows/sec (K*T) for " +
                    ("dust_estimate_local" if w.local else
-                    "dust_estimate_embedding" if w.embedding else "dust_estimate")),
+                    "dust_estimate_embedding" if w.embedding else
+                    "dust_estimate_attention" if w.attention else "dust_estimate")),
         "value": head["value"],
         "unit": "draw-token-rows/s",
         "n_gpus": 1,
@@ -391,6 +440,9 @@ def main():
         "accumulation_dtype": "f32",
         "data": ("synthetic (seeded normal X and error estimate E; no dataset or trained weights)"
                  if w.local else
+                 "synthetic (seeded normal X, cached q, k, v and error estimate E; no dataset or "
+                 "trained weights)"
+                 if w.attention else
                  "synthetic (seeded normal X, W and uniform labels; no dataset or trained weights)"
                  if w.head else
                  "synthetic (seeded normal table and target, Zipfian token ids; no dataset or "

@@ -222,6 +222,83 @@ dust_status_t dust_estimate_local(const void* X, const float* E, int64_t T,
                                   size_t workspace_bytes, void* stream);
 
 /*
+ * Local scoring through a recomputed attention ("Dust: every token is a
+ * member of the population", section "What the released code actually
+ * does", step 4: the queries, keys or values of one block are jittered, that
+ * block's attention is recomputed from its cached activations, and the
+ * change of its output is scored against the estimated error of the
+ * attention output, c_s = -<e_s, Delta o_s>).  The attention is causal
+ * softmax attention inside each sequence, heads of width d_head:
+ * o_s,h = sum_{t<=s} softmax_t(<q_s,h, k_t,h> / sqrt(d_head)) v_t,h.  Draw i
+ * jitters the site's token t by s_i sigma a_t^(n(i)) over its heads * d_head
+ * channels (the noise of dust_estimate with d_out = heads * d_head), and the
+ * score of token s is rho_s^(i) = -sum_h <E_s,h, o'_s,h - o_s,h>, o' the
+ * attention with the jittered site.  Centring, credit (per-site gamma is this
+ * call's gamma), g [T, heads * d_head] and G_W = sum_t g_t x_t^T (the site's
+ * projection weight, with x the block's input) follow as in dust_estimate.
+ */
+typedef enum { DUST_ATTN_QUERY = 0, DUST_ATTN_KEY = 1, DUST_ATTN_VALUE = 2 } dust_attn_site_t;
+
+/*
+ * Bytes of device workspace dust_estimate_attention needs (0 when the sizes
+ * are invalid).  Pure host function.  Besides the estimator's own regions
+ * (dust_workspace_bytes with d_out = heads * d_head) it holds, per sequence
+ * and head, the clean probabilities and for keys and queries the clean
+ * weights p_st <e_s, v_t - o_s> as fp32 [Lp][Lp] (Lp = seq_len rounded up to
+ * 64), and the score kernels' partial row sums, fp32 [slots][sums][K][Lp]
+ * (keys and values: one slot per 64 tokens; queries: one; two sums, values
+ * one).
+ */
+size_t dust_attention_workspace_bytes(int64_t T, int64_t d_in, int64_t heads, int64_t d_head,
+                                      int64_t seq_len, int32_t site, int32_t K,
+                                      int32_t antithetic, int32_t dtype);
+
+/*
+ * Host-side check of dust_estimate_attention's arguments: the rules of
+ * dust_validate for T, seq_len, K, sigma, gamma and the workspace, with
+ * d_out = heads * d_head; Qa, Ka, Va and E required and 16-byte aligned; X
+ * and G_W both given or both NULL (without X, d_in only sizes the workspace:
+ * pass 1); site one of dust_attn_site_t; dtype DUST_BF16 only
+ * (DUST_ERR_UNSUPPORTED otherwise: the cached activations and X are bf16);
+ * d_head 64 or 128 and seq_len at most 4096 (DUST_ERR_UNSUPPORTED).  No HIP
+ * call.
+ */
+dust_status_t dust_validate_attention(const void* X, const void* Qa, const void* Ka,
+                                      const void* Va, const float* E, int64_t T, int64_t d_in,
+                                      int64_t heads, int64_t d_head, int64_t seq_len,
+                                      int32_t site, int32_t dtype, int32_t K, float sigma,
+                                      float gamma, int32_t antithetic, const float* G_W,
+                                      const void* workspace, size_t workspace_bytes);
+
+/*
+ * The estimator with scores through a recomputed attention, enqueued on
+ * `stream`.
+ *
+ * Inputs (device, row-major, contiguous):
+ *   X      [T, d_in]             the block's input (bf16), or NULL with G_W
+ *   Qa, Ka, Va [T, heads*d_head] the cached queries, keys and values (bf16);
+ *                                head h on channels h*d_head .. +d_head-1,
+ *                                token t = b*seq_len + pos
+ *   E      [T, heads*d_head]     fp32 error estimate of the attention output
+ * Scalars: site (which of Qa, Ka, Va is jittered); seq_len, K, sigma, gamma,
+ * seed and antithetic as for dust_estimate.
+ * Outputs (fp32, overwritten): G_W [heads*d_head, d_in] (with X); rho [T, K]
+ * (the scores), reward [T, K] and g [T, heads*d_head] optional (NULL to
+ * skip).  Workspace: at least dust_attention_workspace_bytes(...) bytes.
+ * The scores use the closed forms of the recomputed output change (values:
+ * sigma P A; keys and queries: the softmax re-weighted by e^x, with
+ * x = s_i sigma <q_s, a_t> / sqrt(d_head) or s_i sigma <a_s, k_t> /
+ * sqrt(d_head)), the noise entering a bf16 contraction as its hi + lo split.
+ */
+dust_status_t dust_estimate_attention(const void* X, const void* Qa, const void* Ka,
+                                      const void* Va, const float* E, int64_t T, int64_t d_in,
+                                      int64_t heads, int64_t d_head, int64_t seq_len,
+                                      int32_t site, int32_t dtype, int32_t K, float sigma,
+                                      float gamma, uint64_t seed, int32_t antithetic, float* G_W,
+                                      float* rho, float* reward, float* g, void* workspace,
+                                      size_t workspace_bytes, void* stream);
+
+/*
  * Host-side check of dust_estimate_head's arguments: the rules of
  * dust_validate for T, d_in, K, sigma, dtype and the workspace (sized by
  * dust_workspace_bytes(T, d_in, V, K, antithetic, dtype)); X, W, labels and

@@ -17,11 +17,14 @@ __all__ = ["DustError", "dust_workspace_bytes", "dust_workspace_bytes_seq", "dus
            "dust_reassemble_workspace_bytes", "dust_validate_embedding", "dust_estimate_embedding",
            "dust_validate_reassemble", "dust_reassemble_embedding", "dust_noise_fill",
            "dust_estimate_noalloc", "dust_noalloc_workspace_capacity",
+           "dust_attention_workspace_bytes", "dust_validate_attention", "dust_estimate_attention",
            "dust_set_timing_events", "dust_profile_begin", "dust_profile_end", "dust_last_error",
-           "library_path", "DUST_F32", "DUST_BF16"]
+           "library_path", "DUST_F32", "DUST_BF16", "ATTENTION_SITES"]
 
 DUST_F32 = 0
 DUST_BF16 = 1
+# dust_attn_site_t: which of the cached queries, keys and values is jittered
+ATTENTION_SITES = {"query": 0, "key": 1, "value": 2}
 _STATUS = {0: "DUST_OK", 1: "DUST_ERR_INVALID_ARG", 2: "DUST_ERR_UNSUPPORTED",
            3: "DUST_ERR_WORKSPACE", 4: "DUST_ERR_HIP"}
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -91,6 +94,15 @@ def _load():
     lib.dust_validate_reassemble.restype = ctypes.c_int
     lib.dust_reassemble_embedding.argtypes = [vp, vp, i64, i64, i64, f32, vp, vp, sz, vp]
     lib.dust_reassemble_embedding.restype = ctypes.c_int
+    lib.dust_attention_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i32, i32, i32, i32]
+    lib.dust_attention_workspace_bytes.restype = sz
+    lib.dust_validate_attention.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32,
+                                            i32, i32, f32, f32, i32, vp, vp, sz]
+    lib.dust_validate_attention.restype = ctypes.c_int
+    lib.dust_estimate_attention.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32,
+                                            i32, i32, f32, f32, ctypes.c_uint64, i32, vp, vp,
+                                            vp, vp, vp, sz, vp]
+    lib.dust_estimate_attention.restype = ctypes.c_int
     lib.dust_noise_fill.argtypes = [ctypes.c_uint64, i64, i64, i64, i64, i64, vp, vp, vp]
     lib.dust_noise_fill.restype = ctypes.c_int
     vpp = ctypes.POINTER(ctypes.c_void_p)
@@ -339,6 +351,73 @@ def dust_estimate_local(X, E, *, K: int, sigma: float, gamma: float, seed: int,
         ptr(X), E.data_ptr(), T, d_in, d_out, seq_len, dt, K, sigma, gamma,
         ctypes.c_uint64(seed & 0xFFFFFFFFFFFFFFFF), int(bool(antithetic)), ptr(G),
         ptr(rho), ptr(reward), ptr(g), ws.data_ptr(), ws_bytes, _stream_ptr(dev))
+    _check(status)
+    return res
+
+
+def dust_attention_workspace_bytes(T: int, d_in: int, heads: int, d_head: int, seq_len: int,
+                                   site: str, K: int, antithetic: bool) -> int:
+    """Bytes of workspace dust_estimate_attention needs (0 if invalid)."""
+    return int(_load().dust_attention_workspace_bytes(T, d_in, heads, d_head, seq_len,
+                                                      ATTENTION_SITES[site], K,
+                                                      int(bool(antithetic)), DUST_BF16))
+
+
+def dust_validate_attention(X_ptr, Q_ptr, K_ptr, V_ptr, E_ptr, T, d_in, heads, d_head, seq_len,
+                            site, dtype, K, sigma, gamma, antithetic, G_ptr, workspace_ptr,
+                            workspace_bytes) -> int:
+    """Raw host-side validation of dust_estimate_attention's arguments (site
+    as its integer code); returns the status."""
+    return int(_load().dust_validate_attention(X_ptr, Q_ptr, K_ptr, V_ptr, E_ptr, T, d_in, heads,
+                                               d_head, seq_len, site, dtype, K, sigma, gamma,
+                                               int(bool(antithetic)), G_ptr, workspace_ptr,
+                                               workspace_bytes))
+
+
+def dust_estimate_attention(X, q, k, v, E, *, heads: int, site: str, K: int, sigma: float,
+                            gamma: float, seed: int, antithetic: bool, seq_len: int,
+                            want_rho: bool = False, want_reward: bool = False,
+                            want_g: bool = False, out: dict | None = None, workspace=None):
+    """Enqueue dust_estimate_attention (scores through a recomputed causal
+    attention) on the current stream of q's device.
+
+    q, k, v [T, heads*d_head] (bfloat16): the block's cached queries, keys
+    and values; E [T, heads*d_head] (float32): the error estimate of the
+    attention output; site: "query", "key" or "value" (the one jittered); X
+    [T, d_in] (bfloat16) the block's input, or None (no G_W).  Returns a dict
+    of fp32 device tensors: "G_W" [heads*d_head, d_in] (with X) and the
+    requested "rho" [T,K] (the scores), "reward" [T,K], "g" [T,heads*d_head].
+    """
+    import torch
+    dev = _check_tensors(None, q=q, k=k, v=v, E=E, X=X)
+    if not (q.dtype == k.dtype == v.dtype == torch.bfloat16) or (
+            X is not None and X.dtype != torch.bfloat16):
+        raise TypeError("q, k, v and X must be bfloat16")
+    if E.dtype != torch.float32:
+        raise TypeError("E must be float32")
+    if q.dim() != 2 or tuple(k.shape) != tuple(q.shape) or tuple(v.shape) != tuple(q.shape) \
+            or tuple(E.shape) != tuple(q.shape) or q.shape[1] % heads != 0:
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, "
+                         f"v {tuple(v.shape)}, E {tuple(E.shape)}, heads {heads}")
+    T, D = q.shape
+    if X is not None and (X.dim() != 2 or X.shape[0] != T):
+        raise ValueError(f"X {tuple(X.shape)} must be [T={T}, d_in]")
+    d_in = 1 if X is None else X.shape[1]
+    res = dict(out or {})
+    _get = _output_getter(res, dev)
+    G = None if X is None else _get("G_W", (D, d_in))
+    rho = _get("rho", (T, K)) if want_rho else None
+    reward = _get("reward", (T, K)) if want_reward else None
+    g = _get("g", (T, D)) if want_g else None
+    need = dust_attention_workspace_bytes(T, d_in, heads, D // heads, seq_len, site, K,
+                                          antithetic)
+    ws, ws_bytes = _workspace(workspace, need, dev)
+    ptr = lambda t: None if t is None else t.data_ptr()  # noqa: E731
+    status = _load().dust_estimate_attention(
+        ptr(X), q.data_ptr(), k.data_ptr(), v.data_ptr(), E.data_ptr(), T, d_in, heads,
+        D // heads, seq_len, ATTENTION_SITES[site], DUST_BF16, K, sigma, gamma,
+        ctypes.c_uint64(seed & 0xFFFFFFFFFFFFFFFF), int(bool(antithetic)), ptr(G), ptr(rho),
+        ptr(reward), ptr(g), ws.data_ptr(), ws_bytes, _stream_ptr(dev))
     _check(status)
     return res
 

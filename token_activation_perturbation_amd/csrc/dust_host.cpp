@@ -201,6 +201,56 @@ dust_status_t dust_validate_reassemble(const int32_t* ids, const float* g, int64
   return dust::ok();
 }
 
+size_t dust_attention_workspace_bytes(int64_t T, int64_t d_in, int64_t heads, int64_t d_head,
+                                      int64_t seq_len, int32_t site, int32_t K,
+                                      int32_t antithetic, int32_t dtype) {
+  if (dtype != DUST_BF16 || heads <= 0 || d_head <= 0) return 0;
+  dust::Plan p;
+  if (!dust::make_plan(T, d_in, heads * d_head, K, antithetic, dtype, &p)) return 0;
+  dust::AttnPlan a;
+  if (!dust::make_attn_plan(p, seq_len, heads, d_head, site, &a)) return 0;
+  return a.total;
+}
+
+dust_status_t dust_validate_attention(const void* X, const void* Qa, const void* Ka,
+                                      const void* Va, const float* E, int64_t T, int64_t d_in,
+                                      int64_t heads, int64_t d_head, int64_t seq_len,
+                                      int32_t site, int32_t dtype, int32_t K, float sigma,
+                                      float gamma, int32_t antithetic, const float* G_W,
+                                      const void* workspace, size_t workspace_bytes) {
+  using dust::fail;
+  if (!Qa || !Ka || !Va || !E)
+    return fail(DUST_ERR_INVALID_ARG, "Qa, Ka, Va and E must not be NULL");
+  if ((X == nullptr) != (G_W == nullptr))
+    return fail(DUST_ERR_INVALID_ARG, "X and G_W must both be given or both be NULL");
+  if ((uintptr_t)Qa % 16 || (uintptr_t)Ka % 16 || (uintptr_t)Va % 16 || (uintptr_t)E % 16)
+    return fail(DUST_ERR_INVALID_ARG, "Qa, Ka, Va and E must be 16-byte aligned");
+  if (site != DUST_ATTN_QUERY && site != DUST_ATTN_KEY && site != DUST_ATTN_VALUE)
+    return fail(DUST_ERR_INVALID_ARG, "site=%d: DUST_ATTN_QUERY, _KEY or _VALUE", site);
+  if (heads <= 0 || d_head <= 0 || heads * d_head >= (int64_t(1) << 31))
+    return fail(DUST_ERR_INVALID_ARG, "heads=%lld, d_head=%lld must be positive",
+                (long long)heads, (long long)d_head);
+  // the estimator's own checks, on a workspace of unbounded size
+  const dust_status_t st = validate_common(T, X ? d_in : 1, heads * d_head, seq_len, dtype, K,
+                                           sigma, gamma, antithetic, workspace, (size_t)-1);
+  if (st != DUST_OK) return st;
+  if (dtype != DUST_BF16)
+    return fail(DUST_ERR_UNSUPPORTED, "dtype=%d: the attention site takes bf16 activations",
+                dtype);
+  if (d_head != 64 && d_head != 128)
+    return fail(DUST_ERR_UNSUPPORTED, "d_head=%lld: 64 or 128", (long long)d_head);
+  if (seq_len > dust::kAttnMaxSeqLen)
+    return fail(DUST_ERR_UNSUPPORTED, "seq_len=%lld: at most %lld", (long long)seq_len,
+                (long long)dust::kAttnMaxSeqLen);
+  const size_t need = dust_attention_workspace_bytes(T, X ? d_in : 1, heads, d_head, seq_len,
+                                                     site, K, antithetic, dtype);
+  if (need == 0) return fail(DUST_ERR_UNSUPPORTED, "sizes exceed the kernels' index range");
+  if (!workspace || workspace_bytes < need)
+    return fail(DUST_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed",
+                workspace ? workspace_bytes : (size_t)0, need);
+  return dust::ok();
+}
+
 const char* dust_last_error(void) { return g_last_error; }
 
 }  // extern "C"

@@ -1657,6 +1657,9 @@ __global__ __launch_bounds__(256) void gather_delta_kernel(const void* __restric
   }
 }
 
+// The attention site's kernels (local scoring through a recomputed attention).
+#include "dust_attention.hpp"
+
 // Bench hook state, per calling thread: event pairs stamped by the dispatch
 // of the noise kernel of this thread's next estimate calls
 // (hipExtLaunchKernelGGL's start and stop events, so they time the kernel
@@ -2290,6 +2293,160 @@ dust_status_t run_head(const void* X, const void* W, const int32_t* labels, int6
   return ok();
 }
 
+// Local scoring through a recomputed attention, after validation: the clean
+// pass (P, m0, and B for keys and queries), the score kernel of the site,
+// the reduction to rho and its mean, then the credit, g and G_W as for
+// dust_estimate_local.
+struct AttnArgs {
+  const void* X = nullptr;
+  const uint16_t *Q = nullptr, *Kc = nullptr, *V = nullptr;
+  const float* E = nullptr;
+  int64_t heads = 0, d_head = 0;
+  int32_t site = 0;
+};
+
+template <int DH>
+void launch_attn_scores(const AttnPlan& a, const Plan& p, const AttnArgs& at, const float* Pm,
+                        const float* Bm, float xscale, NoiseKey key, float* part, hipStream_t s,
+                        TimedLaunch tl) {
+  const int32_t L = (int32_t)a.L, Lp = (int32_t)a.Lp, H = (int32_t)a.H, D = (int32_t)p.d_out;
+  const int32_t nseq = (int32_t)a.n_seq;
+  const int64_t units = a.n_seq * a.H * a.nb;
+  const dim3 grid((unsigned)(ceil_div(units, 8) * 8 * a.n_groups));
+  // the method's contraction: per (sequence, head, noise vector) every
+  // causal pair (s, t) takes one d_head-long dot product; bytes: the clean
+  // blocks, the site's operand and the partial sums once
+  const double pairs = (double)a.n_seq * a.H * (double)a.L * (a.L + 1) / 2.0;
+  const double flops = 2.0 * pairs * (double)a.dh * p.K_n;
+  const double bytes = 4.0 * pairs * (a.site == kAttnValue ? 1.0 : 2.0) +
+                       (a.site == kAttnValue ? 4.0 : 2.0) * (double)p.T * p.d_out +
+                       4.0 * (double)a.n_seq * a.H * a.n_slots * a.n_sums * p.K * a.Lp;
+  const TimedLaunch ev = stamp("attn_score_kernel", flops, bytes, tl);
+#define DUST_ATTN_T(SITE, ANTI)                                                                \
+  DUST_LAUNCH(ev, (attn_score_t_kernel<SITE, DH, kAttnNV, ANTI>), grid, dim3(256), 0, s, at.Q,  \
+              at.E, Pm, Bm, L, Lp, a.nb, nseq, H, D, p.K, p.K_n, a.n_groups, xscale, key, part)
+#define DUST_ATTN_S(ANTI)                                                                      \
+  DUST_LAUNCH(ev, (attn_score_s_kernel<DH, kAttnNV, ANTI>), grid, dim3(256), 0, s, at.Kc, Pm,   \
+              Bm, L, Lp, a.nb, nseq, H, D, p.K, p.K_n, a.n_groups, xscale, key, part)
+  if (a.site == kAttnKey) {
+    if (p.antithetic) DUST_ATTN_T(kAttnKey, true); else DUST_ATTN_T(kAttnKey, false);
+  } else if (a.site == kAttnValue) {
+    if (p.antithetic) DUST_ATTN_T(kAttnValue, true); else DUST_ATTN_T(kAttnValue, false);
+  } else {
+    if (p.antithetic) DUST_ATTN_S(true); else DUST_ATTN_S(false);
+  }
+#undef DUST_ATTN_S
+#undef DUST_ATTN_T
+}
+
+template <int DH>
+void launch_attn_clean(const AttnPlan& a, const Plan& p, const AttnArgs& at, float* Pm,
+                       float* Bm, float* m0, hipStream_t s) {
+  const int32_t L = (int32_t)a.L, Lp = (int32_t)a.Lp, H = (int32_t)a.H, D = (int32_t)p.d_out;
+  const double pairs = (double)a.n_seq * a.H * (double)a.L * (a.L + 1) / 2.0;
+  const double td = (double)p.T * p.d_out;
+  // the logits twice (statistics, then p) and p V: three causal contractions
+  DUST_LAUNCH(stamp("attn_probs_kernel", 3.0 * 2.0 * pairs * a.dh,
+                    2.0 * 3.0 * td + 4.0 * td + 4.0 * pairs + 4.0 * a.n_seq * a.H * a.Lp),
+              attn_probs_kernel<DH>, dim3((unsigned)(a.n_seq * a.H * a.nb)), dim3(256), 0, s,
+              at.Q, at.Kc, at.V, at.E, L, Lp, a.nb, H, D, 1.0f / sqrtf((float)a.dh), Pm, m0);
+  if (a.site != kAttnValue)
+    DUST_LAUNCH(stamp("attn_bmat_kernel", 2.0 * pairs * a.dh, 4.0 * td + 2.0 * td + 8.0 * pairs),
+                attn_bmat_kernel<DH>, dim3((unsigned)(a.n_seq * a.H * a.nb * a.nb)), dim3(256),
+                0, s, at.E, at.V, (const float*)Pm, (const float*)m0, L, Lp, a.nb, H, D, Bm);
+}
+
+dust_status_t run_attention(const AttnArgs& at, int64_t T, int64_t d_in, int64_t seq_len,
+                            int32_t dtype, int32_t K, float sigma, float gamma, uint64_t seed,
+                            int32_t antithetic, float* G_W, float* rho, float* reward, float* g,
+                            void* workspace, void* stream) {
+  const int64_t D = at.heads * at.d_head;
+  const bool outer = at.X != nullptr;
+  Plan p;
+  AttnPlan a;
+  make_plan(T, outer ? d_in : 1, D, K, antithetic, dtype, &p);
+  make_attn_plan(p, seq_len, at.heads, at.d_head, at.site, &a);
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  float* Pm = (float*)(ws + a.off_P);
+  float* Bm = a.site == kAttnValue ? nullptr : (float*)(ws + a.off_B);
+  float* m0 = (float*)(ws + a.off_m0);
+  float* part = (float*)(ws + a.off_part);
+  float* rho_buf = rho ? rho : (float*)(ws + p.off_rho);
+  float* mean = (float*)(ws + p.off_mean);
+  float* wgt = (float*)(ws + p.off_wgt);
+  const bool split = dtype == DUST_BF16 && outer;
+  float* g32 = split ? g : (g ? g : (float*)(ws + p.off_g));
+  uint16_t* g_hi = split ? (uint16_t*)(ws + p.off_g) : nullptr;
+  uint16_t* g_lo = split ? g_hi + T * D : nullptr;
+  float* gpart = (float*)(ws + p.off_gpart);
+  const NoiseKey key = make_key(seed);
+  const int32_t Ti = (int32_t)T;
+
+  // 1. the clean attention of every (sequence, head)
+  if (at.d_head == 64)
+    launch_attn_clean<64>(a, p, at, Pm, Bm, m0, s);
+  else
+    launch_attn_clean<128>(a, p, at, Pm, Bm, m0, s);
+  // 2. the partial sums of every draw, then rho and its mean
+  const TimedLaunch tl = take_timing_events();
+  const float xscale = sigma / sqrtf((float)at.d_head);
+  if (at.d_head == 64)
+    launch_attn_scores<64>(a, p, at, Pm, Bm, xscale, key, part, s, tl);
+  else
+    launch_attn_scores<128>(a, p, at, Pm, Bm, xscale, key, part, s, tl);
+  const double tk = (double)T * K;
+  const double part_b = 4.0 * (double)a.n_seq * a.H * a.n_sums * K * a.Lp *
+                        (a.site == kAttnQuery ? 1.0 : (a.nb + 1) / 2.0);
+#define DUST_ATTN_RED(SITE)                                                                     \
+  DUST_LAUNCH(stamp("attn_reduce_kernel", 0.0, part_b + 4.0 * tk + 4.0 * T),                   \
+              attn_reduce_kernel<SITE>, dim3((unsigned)(a.n_seq * a.nb)), dim3(256), 0, s,      \
+              (const float*)part, (int32_t)a.L, (int32_t)a.Lp, a.nb, (int32_t)a.H, K, a.n_slots, \
+              sigma, rho_buf, mean)
+  if (a.site == kAttnKey) DUST_ATTN_RED(kAttnKey);
+  else if (a.site == kAttnValue) DUST_ATTN_RED(kAttnValue);
+  else DUST_ATTN_RED(kAttnQuery);
+#undef DUST_ATTN_RED
+
+  // 3. centring + discounted credit -> per-(t, n) weights
+  const double tkn = (double)T * p.K_n, td = (double)T * D;
+  const double credit_b = 4.0 * tk + 4.0 * T + (reward ? 4.0 * tk : 0.0) + 4.0 * tkn;
+  if (gamma == 0.0f || seq_len == 1) {
+    DUST_LAUNCH(stamp("credit_token_kernel", 0.0, credit_b), credit_token_kernel,
+                dim3(grid_for(T * p.K_n, 256)), dim3(256), 0, s, (const float*)rho_buf,
+                (const float*)mean, Ti, K, p.K_n, p.antithetic, sigma, reward, wgt);
+  } else {
+    const int64_t n_seq = T / seq_len;
+    const int32_t n_chunks = (int32_t)ceil_div(seq_len, kScanChunk);
+    float* r_loc = reward ? reward : (float*)(ws + p.off_rloc);
+    float* carry = (float*)(ws + p.off_carry);
+    float gamma_chunk = 1.f;
+    for (int k = 0; k < kScanChunk; ++k) gamma_chunk *= gamma;
+    const double heads_b = 4.0 * n_seq * n_chunks * (double)K;
+    DUST_LAUNCH(stamp("scan_local_kernel", 0.0, 8.0 * tk + 4.0 * T + heads_b), scan_local_kernel,
+                dim3(grid_for(n_seq * n_chunks * K, 256)), dim3(256), 0, s,
+                (const float*)rho_buf, (const float*)mean, Ti, (int32_t)seq_len, K, n_chunks,
+                gamma, r_loc, carry);
+    DUST_LAUNCH(stamp("scan_carry_kernel", 0.0, 2.0 * heads_b), scan_carry_kernel,
+                dim3(grid_for(n_seq * K, 256)), dim3(256), 0, s, carry, (int32_t)n_seq, n_chunks,
+                K, gamma_chunk);
+    DUST_LAUNCH(stamp("scan_apply_kernel", 0.0,
+                      4.0 * tk + heads_b + (reward ? 4.0 * tk : 0.0) + 4.0 * tkn),
+                scan_apply_kernel, dim3(grid_for(T * p.K_n, 256)), dim3(256), 0, s,
+                (const float*)r_loc, (const float*)carry, Ti, (int32_t)seq_len, K, p.K_n,
+                n_chunks, p.antithetic, sigma, gamma, reward, wgt);
+  }
+  // 4. g from the regenerated noise, 5. G_W
+  const double g_out_b = (g32 ? 4.0 * td : 0.0) + (g_hi ? 4.0 * td : 0.0);
+  DUST_LAUNCH(stamp("reweight_kernel", 0.0, 4.0 * tkn + g_out_b), reweight_kernel,
+              dim3((unsigned)T), dim3(64 * p.rw_waves), 0, s, (const float*)wgt, 0,
+              (int32_t)D, p.nq, p.K_n, p.rw_per_wave, key, g32, g_hi, g_lo);
+  if (outer) launch_outer(p, at.X, g32, g_hi, g_lo, gpart, G_W, T, d_in, D, dtype, s);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(DUST_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 // ---------------------------------------------------------------------------
 // The workspace of dust_estimate_noalloc: a file-scope device array, one copy
 // per GPU the library runs on (the runtime places it when the code object
@@ -2394,6 +2551,30 @@ dust_status_t dust_estimate_local(const void* X, const float* E, int64_t T, int6
   return dust::run_estimate(site, T, d_in, d_out, seq_len, dtype, K, sigma,
                             gamma, seed, antithetic, G_W, nullptr, rho, reward, g, workspace,
                             workspace_bytes, stream);
+}
+
+dust_status_t dust_estimate_attention(const void* X, const void* Qa, const void* Ka,
+                                      const void* Va, const float* E, int64_t T, int64_t d_in,
+                                      int64_t heads, int64_t d_head, int64_t seq_len,
+                                      int32_t site, int32_t dtype, int32_t K, float sigma,
+                                      float gamma, uint64_t seed, int32_t antithetic, float* G_W,
+                                      float* rho, float* reward, float* g, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  const dust_status_t st = dust_validate_attention(X, Qa, Ka, Va, E, T, d_in, heads, d_head,
+                                                   seq_len, site, dtype, K, sigma, gamma,
+                                                   antithetic, G_W, workspace, workspace_bytes);
+  if (st != DUST_OK) return st;
+  dust::AttnArgs at;
+  at.X = X;
+  at.Q = (const uint16_t*)Qa;
+  at.Kc = (const uint16_t*)Ka;
+  at.V = (const uint16_t*)Va;
+  at.E = E;
+  at.heads = heads;
+  at.d_head = d_head;
+  at.site = site;
+  return dust::run_attention(at, T, d_in, seq_len, dtype, K, sigma, gamma, seed, antithetic, G_W,
+                             rho, reward, g, workspace, stream);
 }
 
 dust_status_t dust_estimate_head(const void* X, const void* W, const int32_t* labels, int64_t T,

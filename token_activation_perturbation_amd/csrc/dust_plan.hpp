@@ -314,4 +314,72 @@ inline bool make_embedding_plan(int64_t T, int64_t V, int64_t d, int32_t K, int3
   return true;
 }
 
+
+// ---------------------------------------------------------------------------
+// Local scoring through a recomputed attention (dust_estimate_attention): the
+// clean probabilities P and, for keys and queries, the clean weights
+// B_st = p_st <e_s, v_t - o_s> of every (sequence, head) as [Lp][Lp] fp32
+// (Lp = seq_len rounded up to kAttnBlock; entries past the causal edge or
+// the sequence are zero, blocks above the diagonal are never written or
+// read), m0_s = <e_s, o_s> [Lp], and the score kernels' partial row sums
+// [slots][sums][K][Lp] per (sequence, head): keys and values write one slot
+// per block of kAttnBlock jittered tokens, queries one; keys and queries two
+// sums per (token, draw), values one.  These follow the estimator's own
+// regions (make_plan with d_out = heads * d_head).
+constexpr int32_t kAttnBlock = 64;
+constexpr int64_t kAttnMaxSeqLen = 4096;
+enum { kAttnQuery = 0, kAttnKey = 1, kAttnValue = 2 };
+
+struct AttnPlan {
+  int64_t n_seq = 0, L = 0, Lp = 0, H = 0, dh = 0;
+  int32_t nb = 0;       // blocks of kAttnBlock tokens per sequence
+  int32_t site = 0;     // kAttnQuery, kAttnKey or kAttnValue
+  int32_t n_sums = 0;   // partial sums per (token, draw): 2, or 1 for values
+  int32_t n_slots = 0;  // partial slots per token: nb, or 1 for queries
+  int32_t nv = 0;       // noise vectors per score workgroup
+  int32_t n_groups = 0; // score workgroups per (sequence, head, block): ceil(K_n / nv)
+  size_t off_P = 0, off_B = 0, off_m0 = 0, off_part = 0, total = 0;
+};
+
+// Returns false when the sizes cannot be planned (d_head not 64 or 128, a
+// sequence longer than kAttnMaxSeqLen, an unknown site, or grids past the
+// kernels' 32-bit indices).
+inline bool make_attn_plan(const Plan& p, int64_t seq_len, int64_t heads, int64_t d_head,
+                           int32_t site, AttnPlan* a) {
+  if (heads <= 0 || (d_head != 64 && d_head != 128)) return false;
+  if (site != kAttnQuery && site != kAttnKey && site != kAttnValue) return false;
+  if (seq_len <= 0 || seq_len > kAttnMaxSeqLen || p.T % seq_len != 0) return false;
+  if (p.d_out != heads * d_head) return false;
+  AttnPlan q;
+  q.n_seq = p.T / seq_len;
+  q.L = seq_len;
+  q.Lp = ceil_div(seq_len, kAttnBlock) * kAttnBlock;
+  q.H = heads;
+  q.dh = d_head;
+  q.nb = (int32_t)(q.Lp / kAttnBlock);
+  q.site = site;
+  q.n_sums = site == kAttnValue ? 1 : 2;
+  q.n_slots = site == kAttnQuery ? 1 : q.nb;
+  q.nv = 2;
+  q.n_groups = (int32_t)ceil_div(p.K_n, q.nv);
+  const int64_t units = q.n_seq * heads * q.nb;
+  if (ceil_div(units, 8) * 8 * q.n_groups >= (int64_t(1) << 31)) return false;
+  const size_t sq = size_t(q.n_seq) * size_t(heads);
+  const size_t mat = sizeof(float) * sq * size_t(q.Lp) * size_t(q.Lp);
+  size_t off = align256(p.total);
+  auto take = [&off](size_t bytes) {
+    size_t at = off;
+    off = align256(off + bytes);
+    return at;
+  };
+  q.off_P = take(mat);
+  q.off_B = take(site == kAttnValue ? 0 : mat);
+  q.off_m0 = take(sizeof(float) * sq * size_t(q.Lp));
+  q.off_part = take(sizeof(float) * sq * size_t(q.n_slots) * size_t(q.n_sums) * size_t(p.K) *
+                    size_t(q.Lp));
+  q.total = off;
+  *a = q;
+  return true;
+}
+
 }  // namespace dust

@@ -142,6 +142,51 @@ def reweight_kernel_slots(T: int, d_out: int, K: int, antithetic: bool) -> float
 MFMA_PEAK_FLOPS = {"bf16": 2.5e15, "f32": 157.3e12}
 HBM_PEAK_BYTES = 8.0e12
 
+# ---------------------------------------------------------------------------
+# Scores through a recomputed attention (the attention site's score kernel).
+# Per (sequence, head, noise vector) the method computes, for every causal
+# pair s >= t of the sequence, one d_head-long dot product of the jittered
+# operand with the noise (the MFMA contraction, 2 d_head flops per pair,
+# priced as one bf16 contraction although the kernel issues it twice, once
+# per half of the noise's hi + lo split), then per pair: keys and queries
+# 1 multiply (the logit change), e^x - 1 (antithetic: both signs from the
+# even and odd Taylor parts, u = x^2, 4 + 3 slots, 2 adds, 1 compare = 11;
+# plain draws: 9) and one FMA per row sum (S1 and S2, per sign); values one
+# FMA.  Each noise value (K_n T d_out of them) is generated once.
+
+def attention_pairs(T: int, seq_len: int, heads: int) -> float:
+    """Causal (s, t) pairs of every (sequence, head)."""
+    return (T // seq_len) * heads * seq_len * (seq_len + 1) / 2.0
+
+
+def attention_score_flops(T: int, seq_len: int, heads: int, d_head: int, K: int,
+                          antithetic: bool) -> float:
+    K_n = K // 2 if antithetic else K
+    return 2.0 * attention_pairs(T, seq_len, heads) * d_head * K_n
+
+
+def attention_score_slots(site: str, T: int, seq_len: int, heads: int, d_head: int, K: int,
+                          antithetic: bool) -> float:
+    K_n = K // 2 if antithetic else K
+    if site == "value":
+        per_pair = 1.0
+    else:
+        per_pair = 1.0 + (11.0 + 4.0 if antithetic else 9.0 + 2.0)
+    gen = distinct_noise_values(T, heads * d_head, K, antithetic) * GEN_SLOTS_PER_VALUE
+    return K_n * attention_pairs(T, seq_len, heads) * per_pair + gen
+
+
+def attention_score_bound(site: str, T: int, seq_len: int, heads: int, d_head: int, K: int,
+                          antithetic: bool) -> tuple:
+    """(bound, algorithmic work, peak per second, unit) of the score kernel:
+    the unit whose work takes longer at its peak."""
+    slots = attention_score_slots(site, T, seq_len, heads, d_head, K, antithetic)
+    flops = attention_score_flops(T, seq_len, heads, d_head, K, antithetic)
+    if slots / PEAK_SLOTS_PER_S >= flops / MFMA_PEAK_FLOPS["bf16"]:
+        return "alu", slots, PEAK_SLOTS_PER_S, "T lane-slot/s"
+    return "mfma", flops, MFMA_PEAK_FLOPS["bf16"], "TFLOP/s"
+
+
 # stages whose bound is the vector ALU (each generates noise values)
 NOISE_STAGES = ("fused_g0_kernel", "chain_g_kernel", "jitter_loss_kernel", "reweight_kernel",
                 "head_ce_kernel")

@@ -2,7 +2,9 @@
 
 This module holds no arithmetic of the estimator: it only draws X, W and
 target (for local scoring X and an error estimate E; for a cross-entropy head
-X, W and labels; for a token embedding its table, Zipfian ids and target) with the shapes and distributions of the workloads below,
+X, W and labels; for a token embedding its table, Zipfian ids and target;
+for an attention site X, the cached q, k, v and E) with the shapes and
+distributions of the workloads below,
 and rounds them to the input dtype.
 The pages train on FineWeb with a 37.7M parameter GPT whose layers are 512
 wide ("Dust: every token is a member of the population", sections "What the
@@ -43,7 +45,13 @@ class Workload:
                         # "head": a cross-entropy head, d_out = the vocabulary,
                         # labels uniform in [0, d_out); or "embedding": a token
                         # embedding table [d_in = vocabulary, d_out], Zipfian
-                        # ids, target ~ N(0,1)
+                        # ids, target ~ N(0,1); or "attention": a block's
+                        # cached queries, keys and values q, k, v ~ N(0,1)
+                        # [T, d_out = heads * d_head] (bf16), the error
+                        # estimate of its output E ~ N(0,1) (fp32) and the
+                        # block's input X, one of q, k, v jittered (site)
+    heads: int = 0      # attention: heads of width d_out / heads
+    site: str = ""      # attention: "query", "key" or "value"
 
     @property
     def local(self) -> bool:
@@ -56,6 +64,14 @@ class Workload:
     @property
     def embedding(self) -> bool:
         return self.target_kind == "embedding"
+
+    @property
+    def attention(self) -> bool:
+        return self.target_kind == "attention"
+
+    @property
+    def d_head(self) -> int:
+        return self.d_out // self.heads if self.attention else 0
 
     @property
     def V(self) -> int:
@@ -79,10 +95,13 @@ class Workload:
         return self.K * self.T * self.n_slab
 
     def describe(self) -> dict:
-        return {"workload": self.name, "T": self.T, "seq_len": self.seq_len,
-                "d_in": self.d_in, "d_out": self.d_out, "K": self.K,
-                "sigma": self.sigma, "gamma": self.gamma,
-                "antithetic": self.antithetic, "dtype": self.dtype}
+        d = {"workload": self.name, "T": self.T, "seq_len": self.seq_len,
+             "d_in": self.d_in, "d_out": self.d_out, "K": self.K,
+             "sigma": self.sigma, "gamma": self.gamma,
+             "antithetic": self.antithetic, "dtype": self.dtype}
+        if self.attention:
+            d.update(heads=self.heads, d_head=self.d_head, site=self.site)
+        return d
 
 
 WORKLOADS = {
@@ -112,11 +131,24 @@ WORKLOADS = {
         # 4,096 x 512 table, Zipfian token ids, the embedding's sigma 0.4,
         # own-token losses (gamma = 0), 8 sequences x 2048 tokens.
         Workload("embed_bf16", 16384, 2048, 4096, 512, 64, 0.4, 0.0, True, "bf16", 1009, 0, "embedding"),
+        # Local scoring through the recomputed attention of one block of the
+        # same model ("What the released code actually does", step 4): its
+        # 512 channels as 4 heads of width 128 (the pages give no head
+        # count), 8 sequences x 2048 tokens, the attention internals' sigma
+        # 0.05 (SGD recipe), 64 antithetic draws; keys and values with credit
+        # decay 0.98, queries with their own token's score only.
+        Workload("attn_key_bf16", 16384, 2048, 512, 512, 64, 0.05, 0.98, True, "bf16", 1011, 0,
+                 "attention", heads=4, site="key"),
+        Workload("attn_value_bf16", 16384, 2048, 512, 512, 64, 0.05, 0.98, True, "bf16", 1012, 0,
+                 "attention", heads=4, site="value"),
+        Workload("attn_query_bf16", 16384, 2048, 512, 512, 64, 0.05, 0.0, True, "bf16", 1013, 0,
+                 "attention", heads=4, site="query"),
     ]
 }
 WORKLOAD_ORDER = ["tiny_f32", "bf16_layer", "mlp_up_bf16", "qkv_credit_bf16",
                   "large_population_bf16", "large_population_plain_bf16", "kv_local_bf16",
-                  "q_local_bf16", "head_ce_bf16", "embed_bf16"]
+                  "q_local_bf16", "head_ce_bf16", "embed_bf16", "attn_key_bf16",
+                  "attn_value_bf16", "attn_query_bf16"]
 
 
 def bf16_round(x: np.ndarray) -> np.ndarray:
@@ -167,6 +199,10 @@ def make_inputs(w: Workload, T: int | None = None, d_in: int | None = None,
         target = _round(rng.standard_normal((T, d_out)), w.dtype)
         return {"table": table, "ids": ids, "target": target}
     X = _round(rng.standard_normal((T, d_in)), w.dtype)
+    if w.attention:
+        q, k, v = (_round(rng.standard_normal((T, d_out)), w.dtype) for _ in range(3))
+        return {"X": X, "q": q, "k": k, "v": v,
+                "E": rng.standard_normal((T, d_out)).astype(np.float32)}
     if w.local:
         return {"X": X, "E": rng.standard_normal((T, d_out)).astype(np.float32)}
     W = _round(rng.standard_normal((d_out, d_in)) / np.sqrt(d_in), w.dtype)
@@ -179,6 +215,17 @@ def make_inputs(w: Workload, T: int | None = None, d_in: int | None = None,
     else:
         target = _round(rng.standard_normal((T, d_out)), w.dtype)
     return {"X": X, "W": W, "target": target}
+
+
+def attention_inputs(T: int, d_in: int, d_out: int, seed: int) -> dict:
+    """Attention-site inputs of any shape with the recipe of the attention
+    workloads: X [T,d_in], q, k, v [T,d_out] ~ N(0,1) rounded to bf16, E
+    [T,d_out] ~ N(0,1) in fp32."""
+    rng = np.random.default_rng(seed)
+    X = _round(rng.standard_normal((T, d_in)), "bf16")
+    q, k, v = (_round(rng.standard_normal((T, d_out)), "bf16") for _ in range(3))
+    return {"X": X, "q": q, "k": k, "v": v,
+            "E": rng.standard_normal((T, d_out)).astype(np.float32)}
 
 
 def random_inputs(T: int, d_in: int, d_out: int, dtype: str, seed: int) -> dict:
