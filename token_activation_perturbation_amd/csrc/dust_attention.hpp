@@ -27,8 +27,8 @@
 // pass over the T x T block and two row sums.
 //
 // Kernels, in launch order:
-//   attn_probs_kernel   clean P and m0 (fp32 VALU, once per call)
-//   attn_bmat_kernel    clean B (keys and queries)
+//   attn_clean_kernel   clean P and, for keys and queries, B (bf16 MFMA, once
+//                       per call)
 //   attn_score_t_kernel keys and values: one workgroup per (sequence, head,
 //                       block of 64 jittered tokens t, pair of noise
 //                       vectors); the noise of its tokens is generated once,
@@ -41,275 +41,9 @@
 //                       keys t <= s streams past it, the row sums staying in
 //                       registers
 //   attn_reduce_kernel  the partial sums added per (token, draw), the closed
-//                       forms, the sum over heads, rho [T][K] and its mean
-//                       over the draws
+//                       forms and the sum over heads: rho [T][K]
+//   attn_row_mean_kernel  the mean of rho over the draws
 #pragma once
-
-// ---------------------------------------------------------------------------
-// Clean pass.  One workgroup per (sequence, head, block b of 64 rows s);
-// thread (ty, tx) = (tid / 16, tid % 16) owns rows 4 ty + r (r < 4) and, of
-// each 64-token key block, columns 4 tx + c (c < 4).  The contraction runs in
-// chunks of 32 channels staged through LDS, in fp32.
-
-constexpr int kAttnChunk = 32;
-
-// Loads a [64][32] chunk of a bf16 [rows][D] array (rows r0 .., channels
-// c0 ..) transposed into dst[k][row] as fp32; rows at or past `valid` are 0.
-__device__ __forceinline__ void attn_load_chunk_t(const uint16_t* __restrict__ src, int64_t r0,
-                                                  int valid, int D, int c0,
-                                                  float (*dst)[64]) {
-  const int row = threadIdx.x >> 2, k8 = (threadIdx.x & 3) * 8;
-  u16x8_t v = {0, 0, 0, 0, 0, 0, 0, 0};
-  if (row < valid) v = *(const u16x8_t*)(src + (r0 + row) * D + c0 + k8);
-#pragma unroll
-  for (int e = 0; e < 8; ++e) dst[k8 + e][row] = bf16_to_f32(v[e]);
-}
-
-// The same for a fp32 source.
-__device__ __forceinline__ void attn_load_chunk_t(const float* __restrict__ src, int64_t r0,
-                                                  int valid, int D, int c0,
-                                                  float (*dst)[64]) {
-  const int row = threadIdx.x >> 2, k8 = (threadIdx.x & 3) * 8;
-  float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
-  if (row < valid) {
-    a = *(const float4*)(src + (r0 + row) * D + c0 + k8);
-    b = *(const float4*)(src + (r0 + row) * D + c0 + k8 + 4);
-  }
-  const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-  for (int e = 0; e < 8; ++e) dst[k8 + e][row] = v[e];
-}
-
-// acc[r][c] += sum_k A[k][4 ty + r] B[k][4 tx + c] over one staged chunk.
-__device__ __forceinline__ void attn_chunk_fma(const float (*A)[64], const float (*B)[64],
-                                               int ty, int tx, float (&acc)[4][4]) {
-#pragma unroll 8
-  for (int k = 0; k < kAttnChunk; ++k) {
-    const float4 a = *(const float4*)&A[k][4 * ty];
-    const float4 b = *(const float4*)&B[k][4 * tx];
-    const float av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) acc[r][c] = __builtin_fmaf(av[r], bv[c], acc[r][c]);
-  }
-}
-
-// The same with A held as bf16 (the block's queries, exact in bf16).
-__device__ __forceinline__ void attn_chunk_fma(const uint16_t (*A)[64], const float (*B)[64],
-                                               int ty, int tx, float (&acc)[4][4]) {
-#pragma unroll 8
-  for (int k = 0; k < kAttnChunk; ++k) {
-    const uint2 a = *(const uint2*)&A[k][4 * ty];
-    const float4 b = *(const float4*)&B[k][4 * tx];
-    const float av[4] = {__uint_as_float(a.x << 16), __uint_as_float(a.x & 0xFFFF0000u),
-                         __uint_as_float(a.y << 16), __uint_as_float(a.y & 0xFFFF0000u)};
-    const float bv[4] = {b.x, b.y, b.z, b.w};
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) acc[r][c] = __builtin_fmaf(av[r], bv[c], acc[r][c]);
-  }
-}
-
-// The logits <q_s, k_t> of the thread's 4 x 4 entries of the (b, j) block,
-// q held transposed in qT (bf16), keys staged chunk by chunk through kT.
-// Ends with a barrier (kT is free again).
-template <int DH>
-__device__ __forceinline__ void attn_logits(const uint16_t (*qT)[64], float (*kT)[64],
-                                            const uint16_t* __restrict__ Ka, int64_t krow0,
-                                            int kvalid, int D, int hc, int ty, int tx,
-                                            float (&acc)[4][4]) {
-#pragma unroll
-  for (int r = 0; r < 4; ++r)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) acc[r][c] = 0.f;
-  for (int kc = 0; kc < DH; kc += kAttnChunk) {
-    attn_load_chunk_t(Ka, krow0, kvalid, D, hc + kc, kT);
-    __syncthreads();
-    attn_chunk_fma(qT + kc, kT, ty, tx, acc);
-    __syncthreads();
-  }
-}
-
-// Clean probabilities, written to Pm, and m0_s = <e_s, o_s>.  LDS: the
-// block's queries transposed (bf16), a staged key chunk (fp32), p of one
-// key block transposed (fp32) and that block's values (bf16): 56 KB for
-// d_head = 128.
-template <int DH>
-__global__ __launch_bounds__(256) void attn_probs_kernel(
-    const uint16_t* __restrict__ Qa, const uint16_t* __restrict__ Ka,
-    const uint16_t* __restrict__ Va, const float* __restrict__ E, int32_t L, int32_t Lp,
-    int32_t nb, int32_t H, int32_t D, float scale, float* __restrict__ Pm,
-    float* __restrict__ m0) {
-  __shared__ __attribute__((aligned(16))) uint16_t qT[DH][64];
-  __shared__ __attribute__((aligned(16))) float kT[kAttnChunk][64];
-  __shared__ __attribute__((aligned(16))) float pT[64][64];  // p of one block, [t][s]
-  __shared__ __attribute__((aligned(16))) uint16_t vt[64][DH];
-  const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
-  const int b = blockIdx.x % nb, sh = blockIdx.x / nb, h = sh % H, seq = sh / H;
-  const int s0 = 64 * b, hc = h * DH;
-  const int64_t row0 = (int64_t)seq * L;  // the sequence's first token
-  const int svalid = min(64, L - s0);
-  {
-    // queries of the block, transposed: thread moves 8 channels of a row
-    for (int c = tid; c < 64 * (DH / 8); c += 256) {
-      const int row = c / (DH / 8), k8 = (c % (DH / 8)) * 8;
-      u16x8_t v = {0, 0, 0, 0, 0, 0, 0, 0};
-      if (row < svalid) v = *(const u16x8_t*)(Qa + (row0 + s0 + row) * D + hc + k8);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qT[k8 + e][row] = v[e];
-    }
-  }
-  __syncthreads();
-
-  // 1. row maxima and sums of exp, online over the key blocks
-  float mx[4], z[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    mx[r] = -INFINITY;
-    z[r] = 0.f;
-  }
-  float acc[4][4];
-  for (int j = 0; j <= b; ++j) {
-    const int t0 = 64 * j;
-    attn_logits<DH>(qT, kT, Ka, row0 + t0, min(64, L - t0), D, hc, ty, tx, acc);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int s = s0 + 4 * ty + r;
-      float m_new = mx[r];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int t = t0 + 4 * tx + c;
-        if (t <= s && t < L && s < L) m_new = fmaxf(m_new, acc[r][c] * scale);
-      }
-      if (m_new == -INFINITY) continue;
-      float zr = mx[r] == -INFINITY ? 0.f : z[r] * expf(mx[r] - m_new);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int t = t0 + 4 * tx + c;
-        if (t <= s && t < L && s < L) zr += expf(acc[r][c] * scale - m_new);
-      }
-      mx[r] = m_new;
-      z[r] = zr;
-    }
-  }
-  // combine over the 16 threads of a row group (lanes tx of one wave); the
-  // butterfly leaves every lane with the same value
-#pragma unroll
-  for (int d = 1; d < 16; d <<= 1) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float mo = __shfl_xor(mx[r], d), zo = __shfl_xor(z[r], d);
-      const float mn = fmaxf(mx[r], mo);
-      const float a = mx[r] == -INFINITY ? 0.f : z[r] * expf(mx[r] - mn);
-      const float c = mo == -INFINITY ? 0.f : zo * expf(mo - mn);
-      mx[r] = mn;
-      z[r] = a + c;
-    }
-  }
-  float rz[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) rz[r] = z[r] > 0.f ? 1.f / z[r] : 0.f;
-
-  // 2. p written out, and o_s = sum_t p_st v_t (thread: rows 4 ty + r,
-  //    channels tx + 16 q)
-  constexpr int NO = DH / 16;
-  float o[4][NO];
-#pragma unroll
-  for (int r = 0; r < 4; ++r)
-#pragma unroll
-    for (int q = 0; q < NO; ++q) o[r][q] = 0.f;
-  const int64_t pbase = (int64_t)sh * Lp * Lp;
-  for (int j = 0; j <= b; ++j) {
-    const int t0 = 64 * j, tvalid = min(64, L - t0);
-    attn_logits<DH>(qT, kT, Ka, row0 + t0, tvalid, D, hc, ty, tx, acc);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int s = s0 + 4 * ty + r;
-      float p[4];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int t = t0 + 4 * tx + c;
-        p[c] = (t <= s && t < L && s < L) ? expf(acc[r][c] * scale - mx[r]) * rz[r] : 0.f;
-        pT[4 * tx + c][4 * ty + r] = p[c];
-      }
-      *(float4*)(Pm + pbase + (int64_t)s * Lp + t0 + 4 * tx) = make_float4(p[0], p[1], p[2], p[3]);
-    }
-    for (int c = tid; c < 64 * (DH / 8); c += 256) {
-      const int row = c / (DH / 8), k8 = (c % (DH / 8)) * 8;
-      u16x8_t v = {0, 0, 0, 0, 0, 0, 0, 0};
-      if (row < tvalid) v = *(const u16x8_t*)(Va + (row0 + t0 + row) * D + hc + k8);
-      *(u16x8_t*)&vt[row][k8] = v;
-    }
-    __syncthreads();
-    for (int t = 0; t < 64; ++t) {
-      const float4 pr = *(const float4*)&pT[t][4 * ty];
-      const float pv[4] = {pr.x, pr.y, pr.z, pr.w};
-#pragma unroll
-      for (int q = 0; q < NO; ++q) {
-        const float vv = bf16_to_f32(vt[t][tx + 16 * q]);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) o[r][q] = __builtin_fmaf(pv[r], vv, o[r][q]);
-      }
-    }
-    __syncthreads();
-  }
-
-  // 3. m0_s = <e_s, o_s>, summed over the 16 threads of the row group
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int s = s0 + 4 * ty + r;
-    float d = 0.f;
-    if (s < L) {
-      const float* er = E + (row0 + s) * D + hc;
-#pragma unroll
-      for (int q = 0; q < NO; ++q) d = __builtin_fmaf(er[tx + 16 * q], o[r][q], d);
-    }
-#pragma unroll
-    for (int dd = 1; dd < 16; dd <<= 1) d += __shfl_xor(d, dd);
-    if (tx == 0) m0[(int64_t)sh * Lp + s] = d;
-  }
-}
-
-// B_st = p_st (<e_s, v_t> - m0_s) of one (s block b, t block j <= b); one
-// workgroup per (sequence, head, b, j), the blocks above the diagonal exit.
-template <int DH>
-__global__ __launch_bounds__(256) void attn_bmat_kernel(
-    const float* __restrict__ E, const uint16_t* __restrict__ Va, const float* __restrict__ Pm,
-    const float* __restrict__ m0, int32_t L, int32_t Lp, int32_t nb, int32_t H, int32_t D,
-    float* __restrict__ Bm) {
-  __shared__ __attribute__((aligned(16))) float eT[kAttnChunk][64];
-  __shared__ __attribute__((aligned(16))) float vT[kAttnChunk][64];
-  const int j = blockIdx.x % nb, b = (blockIdx.x / nb) % nb, sh = blockIdx.x / (nb * nb);
-  if (j > b) return;
-  const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
-  const int h = sh % H, seq = sh / H, hc = h * DH;
-  const int s0 = 64 * b, t0 = 64 * j;
-  const int64_t row0 = (int64_t)seq * L;
-  float acc[4][4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) acc[r][c] = 0.f;
-  for (int kc = 0; kc < DH; kc += kAttnChunk) {
-    attn_load_chunk_t(E, row0 + s0, min(64, L - s0), D, hc + kc, eT);
-    attn_load_chunk_t(Va, row0 + t0, min(64, L - t0), D, hc + kc, vT);
-    __syncthreads();
-    attn_chunk_fma(eT, vT, ty, tx, acc);
-    __syncthreads();
-  }
-  const int64_t pbase = (int64_t)sh * Lp * Lp;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int s = s0 + 4 * ty + r;
-    const int64_t at = pbase + (int64_t)s * Lp + t0 + 4 * tx;
-    const float4 p = *(const float4*)(Pm + at);
-    const float mm = m0[(int64_t)sh * Lp + s];
-    *(float4*)(Bm + at) = make_float4(p.x * (acc[r][0] - mm), p.y * (acc[r][1] - mm),
-                                      p.z * (acc[r][2] - mm), p.w * (acc[r][3] - mm));
-  }
-}
 
 // ---------------------------------------------------------------------------
 // Scores.  Both score kernels hold the noise of 16 tokens per wave as MFMA
@@ -321,12 +55,11 @@ __global__ __launch_bounds__(256) void attn_bmat_kernel(
 
 constexpr int kAttnNV = 2;
 
-// e^x - 1 and e^-x - 1.  Below |x| = 1/4 from the Taylor series of e^x - 1
+// e^x - 1 and e^-x - 1 for |x| < 1/4, from the Taylor series of e^x - 1
 // split into its even part ev and odd part od (e^x - 1 = ev + od,
 // e^-x - 1 = ev - od); the first terms left out, x^8 / 8! and x^9 / 9!, are
-// below 2e-9 |x| there.  Elsewhere from the exponential, where e^x - 1 is
-// at least 0.22 in size and loses no more than a few ulp.
-__device__ __forceinline__ void attn_expm1_pair(float x, float& ep, float& em) {
+// below 2e-9 |x| there.
+__device__ __forceinline__ void attn_expm1_series(float x, float& ep, float& em) {
   const float u = x * x;
   const float od =
       x * __builtin_fmaf(u, __builtin_fmaf(u, __builtin_fmaf(u, 1.f / 5040.f, 1.f / 120.f),
@@ -335,10 +68,31 @@ __device__ __forceinline__ void attn_expm1_pair(float x, float& ep, float& em) {
   const float ev = u * __builtin_fmaf(u, __builtin_fmaf(u, 1.f / 720.f, 1.f / 24.f), 0.5f);
   ep = ev + od;
   em = ev - od;
+}
+
+// The same for any x: the series below 1/4, else the exponential itself
+// (there e^x - 1 is at least 0.22 in size and loses no more than a few ulp).
+__device__ __forceinline__ void attn_expm1_any(float x, float& ep, float& em) {
+  attn_expm1_series(x, ep, em);
   if (fabsf(x) >= 0.25f) {
     ep = expf(x) - 1.f;
     em = expf(-x) - 1.f;
   }
+}
+
+// Whether any lane of the wave holds a logit change of 1/4 or more among
+// the `n` accumulators (scaled by xscale): a wave-uniform choice between the
+// series alone and the general form, so the common case runs no exponential.
+template <int NV>
+__device__ __forceinline__ bool attn_any_large(const f32x4_t (&acc)[NV][4], float xscale) {
+  float m = 0.f;
+#pragma unroll
+  for (int v = 0; v < NV; ++v)
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) m = fmaxf(m, fabsf(acc[v][q][i]));
+  return __ballot(m * fabsf(xscale) >= 0.25f) != 0;
 }
 
 // Eight bf16 values from four dwords (each holding two, the first in the low
@@ -371,6 +125,234 @@ __device__ __forceinline__ void attn_noise_frags(bool valid, uint32_t n, uint32_
   }
 }
 
+// A block of 64 rows (tokens r0 + 0..63, the head's DH channels) of a bf16
+// [T][D] array, staged through LDS: each thread moves DH / 32 chunks of 16
+// bytes (rows at or past `valid` read as 0) into registers, and later into a
+// padded [64][DH + 8] LDS tile (the 16-byte pad staggers the rows across
+// the banks for the fragment reads).
+template <int DH>
+struct AttnRows {
+  static constexpr int LD = DH + 8;
+  static constexpr int NCH = 64 * DH / 8 / 256;
+  u16x8_t r[NCH];
+  __device__ __forceinline__ void load(const uint16_t* __restrict__ src, int64_t r0, int valid,
+                                       int D, int hc) {
+#pragma unroll
+    for (int u = 0; u < NCH; ++u) {
+      const int c = threadIdx.x + 256 * u, row = c / (DH / 8), k8 = (c % (DH / 8)) * 8;
+      u16x8_t v = {0, 0, 0, 0, 0, 0, 0, 0};
+      if (row < valid) v = *(const u16x8_t*)(src + (r0 + row) * D + hc + k8);
+      r[u] = v;
+    }
+  }
+  __device__ __forceinline__ void store(uint16_t* tile) const {
+#pragma unroll
+    for (int u = 0; u < NCH; ++u) {
+      const int c = threadIdx.x + 256 * u, row = c / (DH / 8), k8 = (c % (DH / 8)) * 8;
+      *(u16x8_t*)(tile + row * LD + k8) = r[u];
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Clean pass, on MFMA: one workgroup per (sequence, head, block b of 64 rows
+// s), the longest rows first; wave w owns rows 64 b + 16 w + [0, 16) as the
+// A operand (its queries, and for keys and queries its error estimate rows
+// split hi + lo), every key block j <= b streams through LDS as the B
+// operand, and lane l holds D rows s = 64 b + 16 w + 4 (l / 16) + i, i < 4,
+// of columns t = 64 j + 16 tt + l % 16 for the four t tiles tt.
+//   pass 1: the logits <q_s, k_t> / sqrt(d) (bf16 products, exact, fp32
+//           sums) and, online, each row's maximum and sum of exponentials,
+//           combined over the 16 lanes of the row at the end;
+//   pass 2: p_st written to P, and (WB) M_st = <e_s, v_t> with its row
+//           sums m0_s = sum_t p_st M_st (= <e_s, o_s>);
+//   pass 3 (WB): p_st and M_st again (the same instructions, so the same
+//           bits) and B_st = p_st (M_st - m0_s) written to B.
+// Entries past the causal edge or the sequence are written as 0.
+template <int DH, bool WB>
+__global__ __launch_bounds__(256) void attn_clean_kernel(
+    const uint16_t* __restrict__ Qa, const uint16_t* __restrict__ Ka,
+    const uint16_t* __restrict__ Va, const float* __restrict__ E, int32_t L, int32_t Lp,
+    int32_t nb, int32_t n_seq, int32_t H, int32_t D, float scale, float* __restrict__ Pm,
+    float* __restrict__ Bm) {
+  constexpr int KS = DH / 32;
+  using Rows = AttnRows<DH>;
+  __shared__ __attribute__((aligned(16))) uint16_t kt[64 * Rows::LD];
+  __shared__ __attribute__((aligned(16))) uint16_t vt[WB ? 64 * Rows::LD : 8];
+  const int lane = threadIdx.x & 63, w = wave_id(), g = lane >> 4, r16 = lane & 15;
+  const int shn = n_seq * H;
+  const int b = nb - 1 - (int)blockIdx.x / shn, sh = (int)blockIdx.x % shn;
+  const int seq = sh / H, h = sh % H, hc = h * DH;
+  const int64_t row0 = (int64_t)seq * L;
+  const int arow = 64 * b + 16 * w + r16;  // the A operand row this lane supplies
+  u16x8_t qf[KS], ehi[KS], elo[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const int64_t at = (row0 + arow) * D + hc + 32 * ks + 8 * g;
+    u16x8_t v = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (arow < L) v = *(const u16x8_t*)(Qa + at);
+    qf[ks] = v;
+    if constexpr (WB) {
+      float4 e0 = make_float4(0.f, 0.f, 0.f, 0.f), e1 = e0;
+      if (arow < L) {
+        e0 = *(const float4*)(E + at);
+        e1 = *(const float4*)(E + at + 4);
+      }
+      uint32_t h0, h1, h2, h3, l0, l1, l2, l3;
+      gemm::split_pair(e0.x, e0.y, h0, l0);
+      gemm::split_pair(e0.z, e0.w, h1, l1);
+      gemm::split_pair(e1.x, e1.y, h2, l2);
+      gemm::split_pair(e1.z, e1.w, h3, l3);
+      ehi[ks] = attn_pack(h0, h1, h2, h3);
+      elo[ks] = attn_pack(l0, l1, l2, l3);
+    }
+  }
+  const int srow0 = 64 * b + 16 * w + 4 * g;  // the first of the lane's 4 output rows
+  Rows nk, nv;
+  // key (and value) block j into LDS; the next one's loads start after it
+  auto stage = [&](int j, bool values) {
+    __syncthreads();
+    nk.store(kt);
+    if (values) nv.store(vt);
+    __syncthreads();
+    if (j + 1 <= b) {
+      const int t1 = 64 * (j + 1);
+      nk.load(Ka, row0 + t1, min(64, L - t1), D, hc);
+      if (values) nv.load(Va, row0 + t1, min(64, L - t1), D, hc);
+    }
+  };
+  // the logits (times scale) of block j: acc[tt][i] for (srow0 + i, 64 j + 16 tt + r16)
+  auto logits = [&](f32x4_t (&acc)[4]) {
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) acc[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        const u16x8_t kf = *(const u16x8_t*)(kt + (16 * tt + r16) * Rows::LD + 32 * ks + 8 * g);
+        acc[tt] = gemm::mfma16(qf[ks], kf, acc[tt]);
+      }
+  };
+  auto mvals = [&](f32x4_t (&acc)[4]) {
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) acc[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        const u16x8_t vf = *(const u16x8_t*)(vt + (16 * tt + r16) * Rows::LD + 32 * ks + 8 * g);
+        acc[tt] = gemm::mfma16(ehi[ks], vf, acc[tt]);
+        acc[tt] = gemm::mfma16(elo[ks], vf, acc[tt]);
+      }
+  };
+  auto valid = [&](int i, int t) {
+    const int s = srow0 + i;
+    return t <= s && t < L && s < L;
+  };
+
+  // 1. row maxima and sums of exponentials
+  float mx[4], z[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    mx[i] = -INFINITY;
+    z[i] = 0.f;
+  }
+  nk.load(Ka, row0, min(64, L), D, hc);
+  for (int j = 0; j <= b; ++j) {
+    stage(j, false);
+    f32x4_t acc[4];
+    logits(acc);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float m_new = mx[i];
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt)
+        if (valid(i, 64 * j + 16 * tt + r16)) m_new = fmaxf(m_new, acc[tt][i] * scale);
+      if (m_new == -INFINITY) continue;
+      float zr = mx[i] == -INFINITY ? 0.f : z[i] * expf(mx[i] - m_new);
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt)
+        if (valid(i, 64 * j + 16 * tt + r16)) zr += expf(acc[tt][i] * scale - m_new);
+      mx[i] = m_new;
+      z[i] = zr;
+    }
+  }
+  // combine over the 16 lanes of each row (the butterfly leaves every lane
+  // with the same value)
+#pragma unroll
+  for (int d = 1; d < 16; d <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float mo = __shfl_xor(mx[i], d), zo = __shfl_xor(z[i], d);
+      const float mn = fmaxf(mx[i], mo);
+      const float a = mx[i] == -INFINITY ? 0.f : z[i] * expf(mx[i] - mn);
+      const float c = mo == -INFINITY ? 0.f : zo * expf(mo - mn);
+      mx[i] = mn;
+      z[i] = a + c;
+    }
+  }
+  float rz[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) rz[i] = z[i] > 0.f ? 1.f / z[i] : 0.f;
+  const int64_t pbase = (int64_t)sh * Lp * Lp;
+  auto probs = [&](int j, const f32x4_t (&acc)[4], float (&p)[4][4]) {
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        p[tt][i] = valid(i, 64 * j + 16 * tt + r16) ? expf(acc[tt][i] * scale - mx[i]) * rz[i]
+                                                     : 0.f;
+  };
+
+  // 2. P, and the row sums m0 of P o M
+  float m0[4] = {0.f, 0.f, 0.f, 0.f};
+  nk.load(Ka, row0, min(64, L), D, hc);
+  if constexpr (WB) nv.load(Va, row0, min(64, L), D, hc);
+  for (int j = 0; j <= b; ++j) {
+    stage(j, WB);
+    f32x4_t acc[4];
+    logits(acc);
+    float p[4][4];
+    probs(j, acc, p);
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        Pm[pbase + (int64_t)(srow0 + i) * Lp + 64 * j + 16 * tt + r16] = p[tt][i];
+    if constexpr (WB) {
+      f32x4_t mv[4];
+      mvals(mv);
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) m0[i] = __builtin_fmaf(p[tt][i], mv[tt][i], m0[i]);
+    }
+  }
+  if constexpr (!WB) return;
+#pragma unroll
+  for (int d = 1; d < 16; d <<= 1)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) m0[i] += __shfl_xor(m0[i], d);
+
+  // 3. B = P o (M - m0)
+  nk.load(Ka, row0, min(64, L), D, hc);
+  nv.load(Va, row0, min(64, L), D, hc);
+  for (int j = 0; j <= b; ++j) {
+    stage(j, true);
+    f32x4_t acc[4], mv[4];
+    logits(acc);
+    mvals(mv);
+    float p[4][4];
+    probs(j, acc, p);
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        Bm[pbase + (int64_t)(srow0 + i) * Lp + 64 * j + 16 * tt + r16] =
+            p[tt][i] * (mv[tt][i] - m0[i]);
+  }
+}
+
 // Keys and values: the jittered tokens t are the MFMA rows.  Workgroup
 // (unit, noise group): units are (t block j, sequence, head), j slowest so
 // the longest rows of blocks start first, dealt to the 8 XCDs round-robin;
@@ -381,7 +363,11 @@ __device__ __forceinline__ void attn_noise_frags(bool valid, uint32_t n, uint32_
 // s tiles st; their partial row sums over the lane's t are summed over the
 // lane groups by two halving steps (lane l then holds token s = 64 b + l)
 // and over the waves through LDS, and written to
-// part[sequence, head][j][sum][draw][s].
+// part[sequence, head][j][sum][draw][s].  Keys: the 64 query rows of block b
+// are staged through a double-buffered LDS tile, loaded one block ahead;
+// values: the error estimate's rows are read by each lane and split
+// hi + lo.  One barrier per block: it publishes the staged rows of block b
+// and the previous block's row sums, which are then written out.
 template <int SITE, int DH, int NV, bool ANTI>
 __global__ __launch_bounds__(256) void attn_score_t_kernel(
     const uint16_t* __restrict__ Qa, const float* __restrict__ E, const float* __restrict__ Pm,
@@ -393,7 +379,9 @@ __global__ __launch_bounds__(256) void attn_score_t_kernel(
   constexpr int M = KEY ? (ANTI ? 4 : 2) : 1;  // sums per (token, noise vector)
   constexpr int MM = NV * M;
   constexpr int NS = KEY ? 2 : 1;
-  __shared__ float red[4][MM][64];
+  using Rows = AttnRows<DH>;
+  __shared__ __attribute__((aligned(16))) uint16_t qs[KEY ? 2 : 1][KEY ? 64 * Rows::LD : 8];
+  __shared__ float red[2][4][MM][64];
   const int lane = threadIdx.x & 63, w = wave_id(), g = lane >> 4, r16 = lane & 15;
   const int pos = (int)(blockIdx.x >> 3), xcd = (int)(blockIdx.x & 7);
   const int unit = xcd + 8 * (pos / n_groups), grp = pos % n_groups;
@@ -411,10 +399,35 @@ __global__ __launch_bounds__(256) void attn_score_t_kernel(
                          ahi[v], alo[v]);
   }
 
+  // the row sums of block bb, summed over the waves, to part
+  auto flush = [&](int rb, int bb) {
+    for (int o = threadIdx.x; o < MM * 64; o += 256) {
+      const int mm = o >> 6, sl = o & 63, v = mm / M, m = mm % M;
+      const int n = grp * NV + v;
+      if (n >= K_n) continue;
+      const float tot =
+          red[rb][0][mm][sl] + red[rb][1][mm][sl] + red[rb][2][mm][sl] + red[rb][3][mm][sl];
+      // (sum, draw): keys S1, S2 of draw n, or of draws 2n (+) and 2n+1 (-);
+      // values the signed sum of draw n, or +S for 2n and -S for 2n+1
+      const int type = KEY ? (m & 1) : 0;
+      const int draw = ANTI ? 2 * n + (m >> 1) : n;
+      const int64_t at = ((((int64_t)sh * nb + j) * NS + type) * K + draw) * Lp + 64 * bb + sl;
+      part[at] = tot;
+      if constexpr (!KEY && ANTI) part[at + Lp] = -tot;
+    }
+  };
+
   const int64_t pbase = (int64_t)sh * Lp * Lp;
   const int tcol = 64 * j + 16 * w + 4 * g;
+  Rows nxt;
+  if constexpr (KEY) nxt.load(Qa, row0 + 64 * j, min(64, L - 64 * j), D, hc);
   for (int b = j; b < nb; ++b) {
-    const int s0 = 64 * b;
+    const int s0 = 64 * b, buf = (b - j) & 1;
+    if constexpr (KEY) nxt.store(qs[buf]);
+    __syncthreads();
+    if (b > j) flush(buf ^ 1, b - 1);
+    if constexpr (KEY)
+      if (b + 1 < nb) nxt.load(Qa, row0 + s0 + 64, min(64, L - s0 - 64), D, hc);
     float4 pv[4], bv[4];
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
@@ -431,17 +444,17 @@ __global__ __launch_bounds__(256) void attn_score_t_kernel(
     for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
-        const int sl = s0 + 16 * st + r16;
-        const int64_t ro = (row0 + sl) * D + hc + 32 * ks + 8 * g;
         if constexpr (KEY) {
-          u16x8_t o = {0, 0, 0, 0, 0, 0, 0, 0};
-          if (sl < L) o = *(const u16x8_t*)(Qa + ro);
+          const u16x8_t o =
+              *(const u16x8_t*)(qs[buf] + (16 * st + r16) * Rows::LD + 32 * ks + 8 * g);
 #pragma unroll
           for (int v = 0; v < NV; ++v) {
             acc[v][st] = gemm::mfma16(ahi[v][ks], o, acc[v][st]);
             acc[v][st] = gemm::mfma16(alo[v][ks], o, acc[v][st]);
           }
         } else {
+          const int sl = s0 + 16 * st + r16;
+          const int64_t ro = (row0 + sl) * D + hc + 32 * ks + 8 * g;
           float4 e0 = make_float4(0.f, 0.f, 0.f, 0.f), e1 = e0;
           if (sl < L) {
             e0 = *(const float4*)(E + ro);
@@ -464,18 +477,22 @@ __global__ __launch_bounds__(256) void attn_score_t_kernel(
       }
     }
     float vals[4 * MM];
+    if constexpr (KEY) {
+      const bool large = attn_any_large<NV>(acc, xscale);
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      const float pp[4] = {pv[st].x, pv[st].y, pv[st].z, pv[st].w};
+      for (int st = 0; st < 4; ++st) {
+        const float pp[4] = {pv[st].x, pv[st].y, pv[st].z, pv[st].w};
+        const float bb[4] = {bv[st].x, bv[st].y, bv[st].z, bv[st].w};
 #pragma unroll
-      for (int v = 0; v < NV; ++v) {
-        if constexpr (KEY) {
-          const float bb[4] = {bv[st].x, bv[st].y, bv[st].z, bv[st].w};
+        for (int v = 0; v < NV; ++v) {
           float s1p = 0.f, s2p = 0.f, s1m = 0.f, s2m = 0.f;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             float ep, em;
-            attn_expm1_pair(xscale * acc[v][st][i], ep, em);
+            if (large)
+              attn_expm1_any(xscale * acc[v][st][i], ep, em);
+            else
+              attn_expm1_series(xscale * acc[v][st][i], ep, em);
             s1p = __builtin_fmaf(pp[i], ep, s1p);
             s2p = __builtin_fmaf(bb[i], ep, s2p);
             if constexpr (ANTI) {
@@ -489,7 +506,14 @@ __global__ __launch_bounds__(256) void attn_score_t_kernel(
             vals[st * MM + v * M + 2] = s1m;
             vals[st * MM + v * M + 3] = s2m;
           }
-        } else {
+        }
+      }
+    } else {
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const float pp[4] = {pv[st].x, pv[st].y, pv[st].z, pv[st].w};
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
           float sp = 0.f;
 #pragma unroll
           for (int i = 0; i < 4; ++i) sp = __builtin_fmaf(pp[i], acc[v][st][i], sp);
@@ -500,23 +524,10 @@ __global__ __launch_bounds__(256) void attn_score_t_kernel(
     halve<2 * MM, 32, true>(vals, lane);
     halve<MM, 16, true>(vals, lane);
 #pragma unroll
-    for (int mm = 0; mm < MM; ++mm) red[w][mm][lane] = vals[mm];
-    __syncthreads();
-    for (int o = threadIdx.x; o < MM * 64; o += 256) {
-      const int mm = o >> 6, sl = o & 63, v = mm / M, m = mm % M;
-      const int n = grp * NV + v;
-      if (n >= K_n) continue;
-      const float tot = red[0][mm][sl] + red[1][mm][sl] + red[2][mm][sl] + red[3][mm][sl];
-      // (sum, draw): keys S1, S2 of draw n, or of draws 2n (+) and 2n+1 (-);
-      // values the signed sum of draw n, or +S for 2n and -S for 2n+1
-      const int type = KEY ? (m & 1) : 0;
-      const int draw = ANTI ? 2 * n + (m >> 1) : n;
-      const int64_t at = ((((int64_t)sh * nb + j) * NS + type) * K + draw) * Lp + s0 + sl;
-      part[at] = tot;
-      if constexpr (!KEY && ANTI) part[at + Lp] = -tot;
-    }
-    __syncthreads();
+    for (int mm = 0; mm < MM; ++mm) red[buf][w][mm][lane] = vals[mm];
   }
+  __syncthreads();
+  flush((nb - 1 - j) & 1, nb - 1);
 }
 
 // Queries: the jittered tokens s are the MFMA columns.  Workgroup (unit,
@@ -525,7 +536,8 @@ __global__ __launch_bounds__(256) void attn_score_t_kernel(
 // key block j <= b, lane l's D entries are (t = 64 j + 16 tt + 4 (l / 16) + i,
 // s = 64 b + 16 w + l % 16) for the four t tiles tt; the lane's row sums
 // accumulate over every block and are summed over the lane groups at the
-// end, into part[sequence, head][0][sum][draw][s].
+// end, into part[sequence, head][0][sum][draw][s].  The 64 key rows of block
+// j are staged through a double-buffered LDS tile, loaded one block ahead.
 template <int DH, int NV, bool ANTI>
 __global__ __launch_bounds__(256) void attn_score_s_kernel(
     const uint16_t* __restrict__ Ka, const float* __restrict__ Pm, const float* __restrict__ Bm,
@@ -534,6 +546,8 @@ __global__ __launch_bounds__(256) void attn_score_s_kernel(
   constexpr int KS = DH / 32;
   constexpr int M = ANTI ? 4 : 2;
   constexpr int MM = NV * M;
+  using Rows = AttnRows<DH>;
+  __shared__ __attribute__((aligned(16))) uint16_t kt[2][64 * Rows::LD];
   const int lane = threadIdx.x & 63, w = wave_id(), g = lane >> 4, r16 = lane & 15;
   const int pos = (int)(blockIdx.x >> 3), xcd = (int)(blockIdx.x & 7);
   const int unit = xcd + 8 * (pos / n_groups), grp = pos % n_groups;
@@ -554,8 +568,13 @@ __global__ __launch_bounds__(256) void attn_score_s_kernel(
 #pragma unroll
   for (int mm = 0; mm < MM; ++mm) S[mm] = 0.f;
   const int64_t prow = (int64_t)sh * Lp * Lp + (int64_t)sl * Lp;
+  Rows nxt;
+  nxt.load(Ka, row0, min(64, L), D, hc);
   for (int j = 0; j <= b; ++j) {
-    const int t0 = 64 * j;
+    const int t0 = 64 * j, buf = j & 1;
+    nxt.store(kt[buf]);
+    __syncthreads();
+    if (j + 1 <= b) nxt.load(Ka, row0 + t0 + 64, min(64, L - t0 - 64), D, hc);
     float4 pv[4], bv[4];
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
@@ -572,9 +591,8 @@ __global__ __launch_bounds__(256) void attn_score_s_kernel(
     for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt) {
-        const int t = t0 + 16 * tt + r16;
-        u16x8_t kf = {0, 0, 0, 0, 0, 0, 0, 0};
-        if (t < L) kf = *(const u16x8_t*)(Ka + (row0 + t) * D + hc + 32 * ks + 8 * g);
+        const u16x8_t kf =
+            *(const u16x8_t*)(kt[buf] + (16 * tt + r16) * Rows::LD + 32 * ks + 8 * g);
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
           acc[v][tt] = gemm::mfma16(kf, ahi[v][ks], acc[v][tt]);
@@ -582,6 +600,7 @@ __global__ __launch_bounds__(256) void attn_score_s_kernel(
         }
       }
     }
+    const bool large = attn_any_large<NV>(acc, xscale);
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
       const float pp[4] = {pv[tt].x, pv[tt].y, pv[tt].z, pv[tt].w};
@@ -591,7 +610,10 @@ __global__ __launch_bounds__(256) void attn_score_s_kernel(
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           float ep, em;
-          attn_expm1_pair(xscale * acc[v][tt][i], ep, em);
+          if (large)
+            attn_expm1_any(xscale * acc[v][tt][i], ep, em);
+          else
+            attn_expm1_series(xscale * acc[v][tt][i], ep, em);
           S[v * M + 0] = __builtin_fmaf(pp[i], ep, S[v * M + 0]);
           S[v * M + 1] = __builtin_fmaf(bb[i], ep, S[v * M + 1]);
           if constexpr (ANTI) {
@@ -619,51 +641,73 @@ __global__ __launch_bounds__(256) void attn_score_s_kernel(
 }
 
 // rho[t][i] = sum over heads of the closed form from the partial sums
-// (keys, queries: -S2 / (1 + S1); values: -sigma S) and mean[t] its mean
-// over the draws.  One workgroup per (sequence, block of 64 tokens); thread
-// (s, ig) = (tid % 64, tid / 64) forms draws ig + 4 r of each chunk of 64,
-// which go through LDS to rows of rho; the mean adds the draws in order.
+// (keys, queries: -S2 / (1 + S1); values: -sigma S).  One workgroup per
+// (sequence, block of 64 tokens, group of 4 draws); thread (s, r) =
+// (tid % 64, tid / 64) forms draw 4 group + r of token s: per head, the
+// slots are added four at a time into four running sums (independent loads,
+// each coalesced over the 64 tokens of the wave), which are then added in a
+// fixed order.  The 4 draws of a token go out as one 16-byte row piece
+// through LDS.
 template <int SITE>
 __global__ __launch_bounds__(256) void attn_reduce_kernel(
     const float* __restrict__ part, int32_t L, int32_t Lp, int32_t nb, int32_t H, int32_t K,
-    int32_t n_slots, float sigma, float* __restrict__ rho, float* __restrict__ mean) {
+    int32_t n_slots, float sigma, float* __restrict__ rho) {
   constexpr int NS = SITE == kAttnValue ? 1 : 2;
-  __shared__ float cb[64][65];
-  const int seq = blockIdx.x / nb, b = blockIdx.x % nb;
-  const int sl = threadIdx.x & 63, ig = threadIdx.x >> 6;
-  const int s = 64 * b + sl;
-  const bool sval = s < L;
+  __shared__ float cb[64][5];
+  const int n_dg = (K + 3) >> 2;
+  const int dg = blockIdx.x % n_dg, rest = blockIdx.x / n_dg;
+  const int b = rest % nb, seq = rest / nb;
+  const int sl = threadIdx.x & 63, r = threadIdx.x >> 6;
+  const int s = 64 * b + sl, i = 4 * dg + r;
   const int slots = SITE == kAttnQuery ? 1 : b + 1;
   const int64_t slot_stride = (int64_t)NS * K * Lp, type_stride = (int64_t)K * Lp;
-  float macc = 0.f;
-  for (int i0 = 0; i0 < K; i0 += 64) {
-#pragma unroll 4
-    for (int r = 0; r < 16; ++r) {
-      const int ic = ig + 4 * r, i = i0 + ic;
-      float c = 0.f;
-      if (sval && i < K) {
-        for (int h = 0; h < H; ++h) {
-          const int64_t base =
-              (((int64_t)(seq * H + h) * n_slots) * NS * K + i) * Lp + s;
-          float s1 = 0.f, s2 = 0.f;
-          for (int jj = 0; jj < slots; ++jj) {
-            s1 += part[base + jj * slot_stride];
-            if constexpr (NS == 2) s2 += part[base + jj * slot_stride + type_stride];
-          }
-          c += SITE == kAttnValue ? -sigma * s1 : -s2 / (1.f + s1);
+  float c = 0.f;
+  if (s < L && i < K) {
+    for (int h = 0; h < H; ++h) {
+      const float* pb = part + (((int64_t)(seq * H + h) * n_slots) * NS * K + i) * Lp + s;
+      float a1[4] = {0.f, 0.f, 0.f, 0.f}, a2[4] = {0.f, 0.f, 0.f, 0.f};
+      int jj = 0;
+      for (; jj + 4 <= slots; jj += 4) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          a1[u] += pb[(jj + u) * slot_stride];
+          if constexpr (NS == 2) a2[u] += pb[(jj + u) * slot_stride + type_stride];
         }
       }
-      cb[sl][ic] = c;
+      for (; jj < slots; ++jj) {
+        a1[0] += pb[jj * slot_stride];
+        if constexpr (NS == 2) a2[0] += pb[jj * slot_stride + type_stride];
+      }
+      const float s1 = (a1[0] + a1[1]) + (a1[2] + a1[3]);
+      const float s2 = (a2[0] + a2[1]) + (a2[2] + a2[3]);
+      c += SITE == kAttnValue ? -sigma * s1 : -s2 / (1.f + s1);
     }
-    __syncthreads();
-    for (int e = threadIdx.x; e < 64 * 64; e += 256) {
-      const int row = e >> 6, col = e & 63;
-      if (64 * b + row < L && i0 + col < K)
-        rho[((int64_t)seq * L + 64 * b + row) * K + i0 + col] = cb[row][col];
-    }
-    if (ig == 0)
-      for (int col = 0; col < 64 && i0 + col < K; ++col) macc += cb[sl][col];
-    __syncthreads();
   }
-  if (ig == 0 && sval) mean[(int64_t)seq * L + s] = macc / (float)K;
+  cb[sl][r] = c;
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    const int row = threadIdx.x, srow = 64 * b + row;
+    if (srow < L) {
+      float* dst = rho + ((int64_t)seq * L + srow) * K + 4 * dg;
+      if (4 * dg + 4 <= K && ((uintptr_t)dst & 15) == 0) {
+        *(float4*)dst = make_float4(cb[row][0], cb[row][1], cb[row][2], cb[row][3]);
+      } else {
+        for (int e = 0; e < 4 && 4 * dg + e < K; ++e) dst[e] = cb[row][e];
+      }
+    }
+  }
+}
+
+// mean[t] = (1/K) sum_i rho[t][i], one wave per token (fixed order: the
+// lanes' strided sums, then the wave's reduction).
+__global__ __launch_bounds__(256) void attn_row_mean_kernel(const float* __restrict__ rho,
+                                                            int32_t T, int32_t K,
+                                                            float* __restrict__ mean) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + wave_id();
+  if (t >= T) return;
+  float sum = 0.f;
+  for (int32_t i = lane; i < K; i += 64) sum += rho[t * K + i];
+  sum = wave_sum(sum);
+  if (lane == 0) mean[t] = sum / (float)K;
 }

@@ -2294,8 +2294,8 @@ dust_status_t run_head(const void* X, const void* W, const int32_t* labels, int6
 }
 
 // Local scoring through a recomputed attention, after validation: the clean
-// pass (P, m0, and B for keys and queries), the score kernel of the site,
-// the reduction to rho and its mean, then the credit, g and G_W as for
+// pass (P, and B for keys and queries), the score kernel of the site, the
+// reduction to rho and its mean, then the credit, g and G_W as for
 // dust_estimate_local.
 struct AttnArgs {
   const void* X = nullptr;
@@ -2341,19 +2341,23 @@ void launch_attn_scores(const AttnPlan& a, const Plan& p, const AttnArgs& at, co
 
 template <int DH>
 void launch_attn_clean(const AttnPlan& a, const Plan& p, const AttnArgs& at, float* Pm,
-                       float* Bm, float* m0, hipStream_t s) {
+                       float* Bm, hipStream_t s) {
   const int32_t L = (int32_t)a.L, Lp = (int32_t)a.Lp, H = (int32_t)a.H, D = (int32_t)p.d_out;
   const double pairs = (double)a.n_seq * a.H * (double)a.L * (a.L + 1) / 2.0;
   const double td = (double)p.T * p.d_out;
-  // the logits twice (statistics, then p) and p V: three causal contractions
-  DUST_LAUNCH(stamp("attn_probs_kernel", 3.0 * 2.0 * pairs * a.dh,
-                    2.0 * 3.0 * td + 4.0 * td + 4.0 * pairs + 4.0 * a.n_seq * a.H * a.Lp),
-              attn_probs_kernel<DH>, dim3((unsigned)(a.n_seq * a.H * a.nb)), dim3(256), 0, s,
-              at.Q, at.Kc, at.V, at.E, L, Lp, a.nb, H, D, 1.0f / sqrtf((float)a.dh), Pm, m0);
-  if (a.site != kAttnValue)
-    DUST_LAUNCH(stamp("attn_bmat_kernel", 2.0 * pairs * a.dh, 4.0 * td + 2.0 * td + 8.0 * pairs),
-                attn_bmat_kernel<DH>, dim3((unsigned)(a.n_seq * a.H * a.nb * a.nb)), dim3(256),
-                0, s, at.E, at.V, (const float*)Pm, (const float*)m0, L, Lp, a.nb, H, D, Bm);
+  const bool wb = a.site != kAttnValue;
+  // the method's work: the logits once, and for keys and queries <e_s, v_t>;
+  // bytes: q, k (and v, E) in, P (and B) out over the causal blocks
+  const TimedLaunch ev =
+      stamp("attn_clean_kernel", 2.0 * pairs * a.dh * (wb ? 2.0 : 1.0),
+            2.0 * 2.0 * td + (wb ? 2.0 * td + 4.0 * td : 0.0) + 4.0 * pairs * (wb ? 2.0 : 1.0));
+  const dim3 grid((unsigned)(a.n_seq * a.H * a.nb));
+  if (wb)
+    DUST_LAUNCH(ev, (attn_clean_kernel<DH, true>), grid, dim3(256), 0, s, at.Q, at.Kc, at.V, at.E,
+                L, Lp, a.nb, (int32_t)a.n_seq, H, D, 1.0f / sqrtf((float)a.dh), Pm, Bm);
+  else
+    DUST_LAUNCH(ev, (attn_clean_kernel<DH, false>), grid, dim3(256), 0, s, at.Q, at.Kc, at.V,
+                at.E, L, Lp, a.nb, (int32_t)a.n_seq, H, D, 1.0f / sqrtf((float)a.dh), Pm, Bm);
 }
 
 dust_status_t run_attention(const AttnArgs& at, int64_t T, int64_t d_in, int64_t seq_len,
@@ -2370,7 +2374,6 @@ dust_status_t run_attention(const AttnArgs& at, int64_t T, int64_t d_in, int64_t
   char* ws = (char*)workspace;
   float* Pm = (float*)(ws + a.off_P);
   float* Bm = a.site == kAttnValue ? nullptr : (float*)(ws + a.off_B);
-  float* m0 = (float*)(ws + a.off_m0);
   float* part = (float*)(ws + a.off_part);
   float* rho_buf = rho ? rho : (float*)(ws + p.off_rho);
   float* mean = (float*)(ws + p.off_mean);
@@ -2385,9 +2388,9 @@ dust_status_t run_attention(const AttnArgs& at, int64_t T, int64_t d_in, int64_t
 
   // 1. the clean attention of every (sequence, head)
   if (at.d_head == 64)
-    launch_attn_clean<64>(a, p, at, Pm, Bm, m0, s);
+    launch_attn_clean<64>(a, p, at, Pm, Bm, s);
   else
-    launch_attn_clean<128>(a, p, at, Pm, Bm, m0, s);
+    launch_attn_clean<128>(a, p, at, Pm, Bm, s);
   // 2. the partial sums of every draw, then rho and its mean
   const TimedLaunch tl = take_timing_events();
   const float xscale = sigma / sqrtf((float)at.d_head);
@@ -2398,15 +2401,17 @@ dust_status_t run_attention(const AttnArgs& at, int64_t T, int64_t d_in, int64_t
   const double tk = (double)T * K;
   const double part_b = 4.0 * (double)a.n_seq * a.H * a.n_sums * K * a.Lp *
                         (a.site == kAttnQuery ? 1.0 : (a.nb + 1) / 2.0);
+  const unsigned red_grid = (unsigned)(a.n_seq * a.nb * ceil_div(K, 4));
 #define DUST_ATTN_RED(SITE)                                                                     \
-  DUST_LAUNCH(stamp("attn_reduce_kernel", 0.0, part_b + 4.0 * tk + 4.0 * T),                   \
-              attn_reduce_kernel<SITE>, dim3((unsigned)(a.n_seq * a.nb)), dim3(256), 0, s,      \
-              (const float*)part, (int32_t)a.L, (int32_t)a.Lp, a.nb, (int32_t)a.H, K, a.n_slots, \
-              sigma, rho_buf, mean)
+  DUST_LAUNCH(stamp("attn_reduce_kernel", 0.0, part_b + 4.0 * tk), attn_reduce_kernel<SITE>,    \
+              dim3(red_grid), dim3(256), 0, s, (const float*)part, (int32_t)a.L, (int32_t)a.Lp, \
+              a.nb, (int32_t)a.H, K, a.n_slots, sigma, rho_buf)
   if (a.site == kAttnKey) DUST_ATTN_RED(kAttnKey);
   else if (a.site == kAttnValue) DUST_ATTN_RED(kAttnValue);
   else DUST_ATTN_RED(kAttnQuery);
 #undef DUST_ATTN_RED
+  DUST_LAUNCH(stamp("attn_row_mean_kernel", 0.0, 4.0 * tk + 4.0 * T), attn_row_mean_kernel,
+              dim3(grid_for(T, 4)), dim3(256), 0, s, (const float*)rho_buf, Ti, K, mean);
 
   // 3. centring + discounted credit -> per-(t, n) weights
   const double tkn = (double)T * p.K_n, td = (double)T * D;

@@ -321,7 +321,7 @@ inline bool make_embedding_plan(int64_t T, int64_t V, int64_t d, int32_t K, int3
 // B_st = p_st <e_s, v_t - o_s> of every (sequence, head) as [Lp][Lp] fp32
 // (Lp = seq_len rounded up to kAttnBlock; entries past the causal edge or
 // the sequence are zero, blocks above the diagonal are never written or
-// read), m0_s = <e_s, o_s> [Lp], and the score kernels' partial row sums
+// read), and the score kernels' partial row sums
 // [slots][sums][K][Lp] per (sequence, head): keys and values write one slot
 // per block of kAttnBlock jittered tokens, queries one; keys and queries two
 // sums per (token, draw), values one.  These follow the estimator's own
@@ -338,7 +338,7 @@ struct AttnPlan {
   int32_t n_slots = 0;  // partial slots per token: nb, or 1 for queries
   int32_t nv = 0;       // noise vectors per score workgroup
   int32_t n_groups = 0; // score workgroups per (sequence, head, block): ceil(K_n / nv)
-  size_t off_P = 0, off_B = 0, off_m0 = 0, off_part = 0, total = 0;
+  size_t off_P = 0, off_B = 0, off_part = 0, total = 0;
 };
 
 // Returns false when the sizes cannot be planned (d_head not 64 or 128, a
@@ -374,7 +374,6 @@ inline bool make_attn_plan(const Plan& p, int64_t seq_len, int64_t heads, int64_
   };
   q.off_P = take(mat);
   q.off_B = take(site == kAttnValue ? 0 : mat);
-  q.off_m0 = take(sizeof(float) * sq * size_t(q.Lp));
   q.off_part = take(sizeof(float) * sq * size_t(q.n_slots) * size_t(q.n_sums) * size_t(p.K) *
                     size_t(q.Lp));
   q.total = off;
