@@ -51,9 +51,12 @@
 // with the 8 contraction values of group l / 16, and holds D rows
 // 4 (l / 16) + i, i < 4, of column l % 16): lane l generates, for its token,
 // channels 32 ks + 8 (l / 16) + 0..7 of the head (two noise quads per ks),
-// split hi + lo.  A workgroup takes kAttnNV noise vectors.
-
-constexpr int kAttnNV = 2;
+// split hi + lo.  A workgroup takes kAttnNV noise vectors.  The score
+// kernels are compiled for DUST_ATTN_WAVES waves per SIMD (a build may set
+// -DDUST_ATTN_WAVES=n).
+#ifndef DUST_ATTN_WAVES
+#define DUST_ATTN_WAVES 2
+#endif
 
 // e^x - 1 and e^-x - 1 for |x| < 1/4, from the Taylor series of e^x - 1
 // split into its even part ev and odd part od (e^x - 1 = ev + od,
@@ -81,10 +84,10 @@ __device__ __forceinline__ void attn_expm1_any(float x, float& ep, float& em) {
 }
 
 // Whether any lane of the wave holds a logit change of 1/4 or more among
-// the `n` accumulators (scaled by xscale): a wave-uniform choice between the
-// series alone and the general form, so the common case runs no exponential.
+// its accumulators: a wave-uniform choice between the series alone and the
+// general form, so the common case runs no exponential.
 template <int NV>
-__device__ __forceinline__ bool attn_any_large(const f32x4_t (&acc)[NV][4], float xscale) {
+__device__ __forceinline__ bool attn_any_large(const f32x4_t (&acc)[NV][4]) {
   float m = 0.f;
 #pragma unroll
   for (int v = 0; v < NV; ++v)
@@ -92,7 +95,31 @@ __device__ __forceinline__ bool attn_any_large(const f32x4_t (&acc)[NV][4], floa
     for (int q = 0; q < 4; ++q)
 #pragma unroll
       for (int i = 0; i < 4; ++i) m = fmaxf(m, fabsf(acc[v][q][i]));
-  return __ballot(m * fabsf(xscale) >= 0.25f) != 0;
+  return __ballot(m >= 0.25f) != 0;
+}
+
+// The row sums of one 16 x 16 D tile (acc: the logit changes x of the
+// lane's 4 entries; pp, bb: their p and B): S1 += p E, S2 += B E with
+// E = e^x - 1, and with antithetic pairs the same for e^-x - 1.  LARGE: the
+// general form of e^x - 1, else its series.
+template <bool LARGE, bool ANTI>
+__device__ __forceinline__ void attn_tile_sums(const f32x4_t& acc, const float (&pp)[4],
+                                               const float (&bb)[4], float& s1p, float& s2p,
+                                               float& s1m, float& s2m) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float ep, em;
+    if constexpr (LARGE)
+      attn_expm1_any(acc[i], ep, em);
+    else
+      attn_expm1_series(acc[i], ep, em);
+    s1p = __builtin_fmaf(pp[i], ep, s1p);
+    s2p = __builtin_fmaf(bb[i], ep, s2p);
+    if constexpr (ANTI) {
+      s1m = __builtin_fmaf(pp[i], em, s1m);
+      s2m = __builtin_fmaf(bb[i], em, s2m);
+    }
+  }
 }
 
 // Eight bf16 values from four dwords (each holding two, the first in the low
@@ -103,11 +130,11 @@ __device__ __forceinline__ u16x8_t attn_pack(uint32_t a, uint32_t b, uint32_t c,
 }
 
 // The noise of token tg, channels hc + 32 ks + 8 g + 0..7 under noise index
-// n, as hi and lo MFMA operands (zero when !valid).
+// n, times `scale`, as hi and lo MFMA operands (zero when !valid).
 template <int KS>
 __device__ __forceinline__ void attn_noise_frags(bool valid, uint32_t n, uint32_t tg, int hc,
-                                                 int g, NoiseKey key, u16x8_t (&hi)[KS],
-                                                 u16x8_t (&lo)[KS]) {
+                                                 int g, float scale, NoiseKey key,
+                                                 u16x8_t (&hi)[KS], u16x8_t (&lo)[KS]) {
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     uint32_t h0 = 0u, h1 = 0u, h2 = 0u, h3 = 0u, l0 = 0u, l1 = 0u, l2 = 0u, l3 = 0u;
@@ -115,10 +142,10 @@ __device__ __forceinline__ void attn_noise_frags(bool valid, uint32_t n, uint32_
       const uint32_t q = (uint32_t)(hc + 32 * ks + 8 * g) >> 2;
       float4 a, b;
       noise_quad_x2(q, n, q + 1, n, tg, key, a, b);
-      gemm::split_pair(a.x, a.y, h0, l0);
-      gemm::split_pair(a.z, a.w, h1, l1);
-      gemm::split_pair(b.x, b.y, h2, l2);
-      gemm::split_pair(b.z, b.w, h3, l3);
+      gemm::split_pair(scale * a.x, scale * a.y, h0, l0);
+      gemm::split_pair(scale * a.z, scale * a.w, h1, l1);
+      gemm::split_pair(scale * b.x, scale * b.y, h2, l2);
+      gemm::split_pair(scale * b.z, scale * b.w, h3, l3);
     }
     hi[ks] = attn_pack(h0, h1, h2, h3);
     lo[ks] = attn_pack(l0, l1, l2, l3);
@@ -150,6 +177,38 @@ struct AttnRows {
     for (int u = 0; u < NCH; ++u) {
       const int c = threadIdx.x + 256 * u, row = c / (DH / 8), k8 = (c % (DH / 8)) * 8;
       *(u16x8_t*)(tile + row * LD + k8) = r[u];
+    }
+  }
+};
+
+// A block of 64 rows of a fp32 [T][D] array (the error estimate), staged
+// through LDS as its bf16 split hi = rn(e), lo = rn(e - hi): each thread
+// moves DH / 16 chunks of four values into registers, and later writes the
+// split to two padded [64][DH + 8] tiles.
+template <int DH>
+struct AttnRowsSplit {
+  static constexpr int LD = DH + 8;
+  static constexpr int NCH = 64 * DH / 4 / 256;
+  float4 r[NCH];
+  __device__ __forceinline__ void load(const float* __restrict__ src, int64_t r0, int valid,
+                                       int D, int hc) {
+#pragma unroll
+    for (int u = 0; u < NCH; ++u) {
+      const int c = threadIdx.x + 256 * u, row = c / (DH / 4), k4 = (c % (DH / 4)) * 4;
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (row < valid) v = *(const float4*)(src + (r0 + row) * D + hc + k4);
+      r[u] = v;
+    }
+  }
+  __device__ __forceinline__ void store(uint16_t* hi, uint16_t* lo) const {
+#pragma unroll
+    for (int u = 0; u < NCH; ++u) {
+      const int c = threadIdx.x + 256 * u, row = c / (DH / 4), k4 = (c % (DH / 4)) * 4;
+      uint32_t h0, h1, l0, l1;
+      gemm::split_pair(r[u].x, r[u].y, h0, l0);
+      gemm::split_pair(r[u].z, r[u].w, h1, l1);
+      *(uint2*)(hi + row * LD + k4) = make_uint2(h0, h1);
+      *(uint2*)(lo + row * LD + k4) = make_uint2(l0, l1);
     }
   }
 };
@@ -363,13 +422,15 @@ __global__ __launch_bounds__(256) void attn_clean_kernel(
 // s tiles st; their partial row sums over the lane's t are summed over the
 // lane groups by two halving steps (lane l then holds token s = 64 b + l)
 // and over the waves through LDS, and written to
-// part[sequence, head][j][sum][draw][s].  Keys: the 64 query rows of block b
-// are staged through a double-buffered LDS tile, loaded one block ahead;
-// values: the error estimate's rows are read by each lane and split
-// hi + lo.  One barrier per block: it publishes the staged rows of block b
-// and the previous block's row sums, which are then written out.
+// part[sequence, head][j][sum][draw][s].  The operand rows of block b are
+// staged through LDS, loaded one block ahead: keys, the 64 query rows in a
+// double-buffered tile, one barrier per block (it publishes the staged rows
+// of block b and the previous block's row sums, which are then written
+// out); values, the error estimate's rows split hi + lo into two tiles, a
+// second barrier per block keeping the single buffer free until every wave
+// is done with it.
 template <int SITE, int DH, int NV, bool ANTI>
-__global__ __launch_bounds__(256) void attn_score_t_kernel(
+__global__ __launch_bounds__(256, DUST_ATTN_WAVES) void attn_score_t_kernel(
     const uint16_t* __restrict__ Qa, const float* __restrict__ E, const float* __restrict__ Pm,
     const float* __restrict__ Bm, int32_t L, int32_t Lp, int32_t nb, int32_t n_seq, int32_t H,
     int32_t D, int32_t K, int32_t K_n, int32_t n_groups, float xscale, NoiseKey key,
@@ -380,7 +441,8 @@ __global__ __launch_bounds__(256) void attn_score_t_kernel(
   constexpr int MM = NV * M;
   constexpr int NS = KEY ? 2 : 1;
   using Rows = AttnRows<DH>;
-  __shared__ __attribute__((aligned(16))) uint16_t qs[KEY ? 2 : 1][KEY ? 64 * Rows::LD : 8];
+  // keys: two buffers of query rows; values: the hi and lo tiles of E
+  __shared__ __attribute__((aligned(16))) uint16_t qs[2][64 * Rows::LD];
   __shared__ float red[2][4][MM][64];
   const int lane = threadIdx.x & 63, w = wave_id(), g = lane >> 4, r16 = lane & 15;
   const int pos = (int)(blockIdx.x >> 3), xcd = (int)(blockIdx.x & 7);
@@ -395,8 +457,8 @@ __global__ __launch_bounds__(256) void attn_score_t_kernel(
 #pragma unroll
   for (int v = 0; v < NV; ++v) {
     const int n = grp * NV + v;
-    attn_noise_frags<KS>(tl < L && n < K_n, (uint32_t)n, (uint32_t)(row0 + tl), hc, g, key,
-                         ahi[v], alo[v]);
+    attn_noise_frags<KS>(tl < L && n < K_n, (uint32_t)n, (uint32_t)(row0 + tl), hc, g,
+                         KEY ? xscale : 1.0f, key, ahi[v], alo[v]);
   }
 
   // the row sums of block bb, summed over the waves, to part
@@ -419,15 +481,27 @@ __global__ __launch_bounds__(256) void attn_score_t_kernel(
 
   const int64_t pbase = (int64_t)sh * Lp * Lp;
   const int tcol = 64 * j + 16 * w + 4 * g;
-  Rows nxt;
-  if constexpr (KEY) nxt.load(Qa, row0 + 64 * j, min(64, L - 64 * j), D, hc);
+  std::conditional_t<KEY, Rows, AttnRowsSplit<DH>> nxt;
+  if constexpr (KEY)
+    nxt.load(Qa, row0 + 64 * j, min(64, L - 64 * j), D, hc);
+  else
+    nxt.load(E, row0 + 64 * j, min(64, L - 64 * j), D, hc);
   for (int b = j; b < nb; ++b) {
     const int s0 = 64 * b, buf = (b - j) & 1;
-    if constexpr (KEY) nxt.store(qs[buf]);
+    if constexpr (KEY) {
+      nxt.store(qs[buf]);
+    } else {
+      __syncthreads();
+      nxt.store(qs[0], qs[1]);
+    }
     __syncthreads();
     if (b > j) flush(buf ^ 1, b - 1);
-    if constexpr (KEY)
-      if (b + 1 < nb) nxt.load(Qa, row0 + s0 + 64, min(64, L - s0 - 64), D, hc);
+    if (b + 1 < nb) {
+      if constexpr (KEY)
+        nxt.load(Qa, row0 + s0 + 64, min(64, L - s0 - 64), D, hc);
+      else
+        nxt.load(E, row0 + s0 + 64, min(64, L - s0 - 64), D, hc);
+    }
     float4 pv[4], bv[4];
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
@@ -453,20 +527,9 @@ __global__ __launch_bounds__(256) void attn_score_t_kernel(
             acc[v][st] = gemm::mfma16(alo[v][ks], o, acc[v][st]);
           }
         } else {
-          const int sl = s0 + 16 * st + r16;
-          const int64_t ro = (row0 + sl) * D + hc + 32 * ks + 8 * g;
-          float4 e0 = make_float4(0.f, 0.f, 0.f, 0.f), e1 = e0;
-          if (sl < L) {
-            e0 = *(const float4*)(E + ro);
-            e1 = *(const float4*)(E + ro + 4);
-          }
-          uint32_t h0, h1, h2, h3, l0, l1, l2, l3;
-          gemm::split_pair(e0.x, e0.y, h0, l0);
-          gemm::split_pair(e0.z, e0.w, h1, l1);
-          gemm::split_pair(e1.x, e1.y, h2, l2);
-          gemm::split_pair(e1.z, e1.w, h3, l3);
-          const u16x8_t oh = attn_pack(h0, h1, h2, h3);
-          const u16x8_t ol = attn_pack(l0, l1, l2, l3);
+          const int at = (16 * st + r16) * Rows::LD + 32 * ks + 8 * g;
+          const u16x8_t oh = *(const u16x8_t*)(qs[0] + at);
+          const u16x8_t ol = *(const u16x8_t*)(qs[1] + at);
 #pragma unroll
           for (int v = 0; v < NV; ++v) {
             acc[v][st] = gemm::mfma16(ahi[v][ks], oh, acc[v][st]);
@@ -478,36 +541,30 @@ __global__ __launch_bounds__(256) void attn_score_t_kernel(
     }
     float vals[4 * MM];
     if constexpr (KEY) {
-      const bool large = attn_any_large<NV>(acc, xscale);
+      // the accumulators hold the logit changes x (the noise carries
+      // s sigma / sqrt(d)); one wave-uniform branch picks the form of e^x - 1
+      auto sums = [&](auto large) {
 #pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        const float pp[4] = {pv[st].x, pv[st].y, pv[st].z, pv[st].w};
-        const float bb[4] = {bv[st].x, bv[st].y, bv[st].z, bv[st].w};
+        for (int st = 0; st < 4; ++st) {
+          const float pp[4] = {pv[st].x, pv[st].y, pv[st].z, pv[st].w};
+          const float bb[4] = {bv[st].x, bv[st].y, bv[st].z, bv[st].w};
 #pragma unroll
-        for (int v = 0; v < NV; ++v) {
-          float s1p = 0.f, s2p = 0.f, s1m = 0.f, s2m = 0.f;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float ep, em;
-            if (large)
-              attn_expm1_any(xscale * acc[v][st][i], ep, em);
-            else
-              attn_expm1_series(xscale * acc[v][st][i], ep, em);
-            s1p = __builtin_fmaf(pp[i], ep, s1p);
-            s2p = __builtin_fmaf(bb[i], ep, s2p);
+          for (int v = 0; v < NV; ++v) {
+            float s1p = 0.f, s2p = 0.f, s1m = 0.f, s2m = 0.f;
+            attn_tile_sums<decltype(large)::value, ANTI>(acc[v][st], pp, bb, s1p, s2p, s1m, s2m);
+            vals[st * MM + v * M + 0] = s1p;
+            vals[st * MM + v * M + 1] = s2p;
             if constexpr (ANTI) {
-              s1m = __builtin_fmaf(pp[i], em, s1m);
-              s2m = __builtin_fmaf(bb[i], em, s2m);
+              vals[st * MM + v * M + 2] = s1m;
+              vals[st * MM + v * M + 3] = s2m;
             }
           }
-          vals[st * MM + v * M + 0] = s1p;
-          vals[st * MM + v * M + 1] = s2p;
-          if constexpr (ANTI) {
-            vals[st * MM + v * M + 2] = s1m;
-            vals[st * MM + v * M + 3] = s2m;
-          }
         }
-      }
+      };
+      if (attn_any_large<NV>(acc))
+        sums(std::true_type{});
+      else
+        sums(std::false_type{});
     } else {
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
@@ -539,7 +596,7 @@ __global__ __launch_bounds__(256) void attn_score_t_kernel(
 // end, into part[sequence, head][0][sum][draw][s].  The 64 key rows of block
 // j are staged through a double-buffered LDS tile, loaded one block ahead.
 template <int DH, int NV, bool ANTI>
-__global__ __launch_bounds__(256) void attn_score_s_kernel(
+__global__ __launch_bounds__(256, DUST_ATTN_WAVES) void attn_score_s_kernel(
     const uint16_t* __restrict__ Ka, const float* __restrict__ Pm, const float* __restrict__ Bm,
     int32_t L, int32_t Lp, int32_t nb, int32_t n_seq, int32_t H, int32_t D, int32_t K,
     int32_t K_n, int32_t n_groups, float xscale, NoiseKey key, float* __restrict__ part) {
@@ -561,8 +618,8 @@ __global__ __launch_bounds__(256) void attn_score_s_kernel(
 #pragma unroll
   for (int v = 0; v < NV; ++v) {
     const int n = grp * NV + v;
-    attn_noise_frags<KS>(sl < L && n < K_n, (uint32_t)n, (uint32_t)(row0 + sl), hc, g, key,
-                         ahi[v], alo[v]);
+    attn_noise_frags<KS>(sl < L && n < K_n, (uint32_t)n, (uint32_t)(row0 + sl), hc, g, xscale,
+                         key, ahi[v], alo[v]);
   }
   float S[MM];
 #pragma unroll
@@ -600,28 +657,26 @@ __global__ __launch_bounds__(256) void attn_score_s_kernel(
         }
       }
     }
-    const bool large = attn_any_large<NV>(acc, xscale);
+    // the accumulators hold the logit changes x (the noise carries
+    // s sigma / sqrt(d)); one wave-uniform branch picks the form of e^x - 1
+    auto sums = [&](auto large) {
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-      const float pp[4] = {pv[tt].x, pv[tt].y, pv[tt].z, pv[tt].w};
-      const float bb[4] = {bv[tt].x, bv[tt].y, bv[tt].z, bv[tt].w};
+      for (int tt = 0; tt < 4; ++tt) {
+        const float pp[4] = {pv[tt].x, pv[tt].y, pv[tt].z, pv[tt].w};
+        const float bb[4] = {bv[tt].x, bv[tt].y, bv[tt].z, bv[tt].w};
 #pragma unroll
-      for (int v = 0; v < NV; ++v)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float ep, em;
-          if (large)
-            attn_expm1_any(xscale * acc[v][tt][i], ep, em);
-          else
-            attn_expm1_series(xscale * acc[v][tt][i], ep, em);
-          S[v * M + 0] = __builtin_fmaf(pp[i], ep, S[v * M + 0]);
-          S[v * M + 1] = __builtin_fmaf(bb[i], ep, S[v * M + 1]);
-          if constexpr (ANTI) {
-            S[v * M + 2] = __builtin_fmaf(pp[i], em, S[v * M + 2]);
-            S[v * M + 3] = __builtin_fmaf(bb[i], em, S[v * M + 3]);
-          }
+        for (int v = 0; v < NV; ++v) {
+          float dm1 = 0.f, dm2 = 0.f;
+          attn_tile_sums<decltype(large)::value, ANTI>(acc[v][tt], pp, bb, S[v * M + 0],
+                                                       S[v * M + 1], ANTI ? S[v * M + 2] : dm1,
+                                                       ANTI ? S[v * M + 3] : dm2);
         }
-    }
+      }
+    };
+    if (attn_any_large<NV>(acc))
+      sums(std::true_type{});
+    else
+      sums(std::false_type{});
   }
 #pragma unroll
   for (int mm = 0; mm < MM; ++mm) {

@@ -328,6 +328,12 @@ inline bool make_embedding_plan(int64_t T, int64_t V, int64_t d, int32_t K, int3
 // regions (make_plan with d_out = heads * d_head).
 constexpr int32_t kAttnBlock = 64;
 constexpr int64_t kAttnMaxSeqLen = 4096;
+// Noise vectors per score workgroup (-DDUST_ATTN_NV=n at build time: 1, 2
+// or 4), held in registers as MFMA operands.
+#ifndef DUST_ATTN_NV
+#define DUST_ATTN_NV 2
+#endif
+constexpr int kAttnNV = DUST_ATTN_NV;
 enum { kAttnQuery = 0, kAttnKey = 1, kAttnValue = 2 };
 
 struct AttnPlan {
@@ -360,7 +366,7 @@ inline bool make_attn_plan(const Plan& p, int64_t seq_len, int64_t heads, int64_
   q.site = site;
   q.n_sums = site == kAttnValue ? 1 : 2;
   q.n_slots = site == kAttnQuery ? 1 : q.nb;
-  q.nv = 2;
+  q.nv = kAttnNV;
   q.n_groups = (int32_t)ceil_div(p.K_n, q.nv);
   const int64_t units = q.n_seq * heads * q.nb;
   if (ceil_div(units, 8) * 8 * q.n_groups >= (int64_t(1) << 31)) return false;
