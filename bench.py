@@ -177,7 +177,7 @@ def dominant_kernel(w, chain: bool) -> str:
     if w.head:
         return "head_ce_kernel"
     if w.attention:
-        return "attn_score_kernel"
+        return "attn_score_s_kernel" if w.site == "query" else "attn_score_t_kernel"
     if w.gamma == 0.0 or w.seq_len == 1:
         return "fused_g0_kernel"
     return "chain_g_kernel" if chain else "jitter_loss_kernel"
@@ -293,14 +293,12 @@ def measure(w, steps: int, warmup: int, want_inputs: bool = False):
         if name in roofline.NOISE_STAGES:
             slots = roofline.noise_stage_slots(name, w.T, w.d_out, w.K, w.antithetic,
                                                local=w.local) * calls_per_step
-        elif name == "attn_score_kernel":
+        elif name in ("attn_score_t_kernel", "attn_score_s_kernel"):
             bound, work, _, _ = roofline.attention_score_bound(
                 w.site, w.T, w.seq_len, w.heads, w.d_head, w.K, w.antithetic)
             if bound == "alu":
                 slots = work * calls_per_step
-        elif name in ("attn_probs_kernel", "attn_bmat_kernel"):
-            # fp32 contractions on the vector ALU: one FMA (2 flops) per slot
-            slots = e["flops"] / PROFILE_STEPS / 2.0
+
         st = roofline.stage_roofline(name, ms, e["flops"] / PROFILE_STEPS,
                                      e["bytes"] / PROFILE_STEPS, w.dtype, slots)
         st["calls"] = calls_per_step

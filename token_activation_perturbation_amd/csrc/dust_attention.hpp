@@ -423,12 +423,11 @@ __global__ __launch_bounds__(256) void attn_clean_kernel(
 // lane groups by two halving steps (lane l then holds token s = 64 b + l)
 // and over the waves through LDS, and written to
 // part[sequence, head][j][sum][draw][s].  The operand rows of block b are
-// staged through LDS, loaded one block ahead: keys, the 64 query rows in a
-// double-buffered tile, one barrier per block (it publishes the staged rows
-// of block b and the previous block's row sums, which are then written
-// out); values, the error estimate's rows split hi + lo into two tiles, a
-// second barrier per block keeping the single buffer free until every wave
-// is done with it.
+// staged through double-buffered LDS tiles, loaded one block ahead (keys:
+// the 64 query rows; values: the error estimate's rows split hi + lo, two
+// tiles per buffer, 70 KB in all), with one barrier per block: it publishes
+// the staged rows of block b and the previous block's row sums, which are
+// then written out.
 template <int SITE, int DH, int NV, bool ANTI>
 __global__ __launch_bounds__(256, DUST_ATTN_WAVES) void attn_score_t_kernel(
     const uint16_t* __restrict__ Qa, const float* __restrict__ E, const float* __restrict__ Pm,
@@ -441,8 +440,9 @@ __global__ __launch_bounds__(256, DUST_ATTN_WAVES) void attn_score_t_kernel(
   constexpr int MM = NV * M;
   constexpr int NS = KEY ? 2 : 1;
   using Rows = AttnRows<DH>;
-  // keys: two buffers of query rows; values: the hi and lo tiles of E
-  __shared__ __attribute__((aligned(16))) uint16_t qs[2][64 * Rows::LD];
+  // keys: two buffers of query rows; values: two buffers of the hi and lo
+  // tiles of E (tiles 2 buf and 2 buf + 1)
+  __shared__ __attribute__((aligned(16))) uint16_t qs[KEY ? 2 : 4][64 * Rows::LD];
   __shared__ float red[2][4][MM][64];
   const int lane = threadIdx.x & 63, w = wave_id(), g = lane >> 4, r16 = lane & 15;
   const int pos = (int)(blockIdx.x >> 3), xcd = (int)(blockIdx.x & 7);
@@ -488,12 +488,10 @@ __global__ __launch_bounds__(256, DUST_ATTN_WAVES) void attn_score_t_kernel(
     nxt.load(E, row0 + 64 * j, min(64, L - 64 * j), D, hc);
   for (int b = j; b < nb; ++b) {
     const int s0 = 64 * b, buf = (b - j) & 1;
-    if constexpr (KEY) {
+    if constexpr (KEY)
       nxt.store(qs[buf]);
-    } else {
-      __syncthreads();
-      nxt.store(qs[0], qs[1]);
-    }
+    else
+      nxt.store(qs[2 * buf], qs[2 * buf + 1]);
     __syncthreads();
     if (b > j) flush(buf ^ 1, b - 1);
     if (b + 1 < nb) {
@@ -528,8 +526,8 @@ __global__ __launch_bounds__(256, DUST_ATTN_WAVES) void attn_score_t_kernel(
           }
         } else {
           const int at = (16 * st + r16) * Rows::LD + 32 * ks + 8 * g;
-          const u16x8_t oh = *(const u16x8_t*)(qs[0] + at);
-          const u16x8_t ol = *(const u16x8_t*)(qs[1] + at);
+          const u16x8_t oh = *(const u16x8_t*)(qs[2 * buf] + at);
+          const u16x8_t ol = *(const u16x8_t*)(qs[2 * buf + 1] + at);
 #pragma unroll
           for (int v = 0; v < NV; ++v) {
             acc[v][st] = gemm::mfma16(ahi[v][ks], oh, acc[v][st]);

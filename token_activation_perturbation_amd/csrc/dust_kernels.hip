@@ -2321,7 +2321,8 @@ void launch_attn_scores(const AttnPlan& a, const Plan& p, const AttnArgs& at, co
   const double bytes = 4.0 * pairs * (a.site == kAttnValue ? 1.0 : 2.0) +
                        (a.site == kAttnValue ? 4.0 : 2.0) * (double)p.T * p.d_out +
                        4.0 * (double)a.n_seq * a.H * a.n_slots * a.n_sums * p.K * a.Lp;
-  const TimedLaunch ev = stamp("attn_score_kernel", flops, bytes, tl);
+  const TimedLaunch ev = stamp(a.site == kAttnQuery ? "attn_score_s_kernel" : "attn_score_t_kernel",
+                              flops, bytes, tl);
 #define DUST_ATTN_T(SITE, ANTI)                                                                \
   DUST_LAUNCH(ev, (attn_score_t_kernel<SITE, DH, kAttnNV, ANTI>), grid, dim3(256), 0, s, at.Q,  \
               at.E, Pm, Bm, L, Lp, a.nb, nseq, H, D, p.K, p.K_n, a.n_groups, xscale, key, part)
