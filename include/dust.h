@@ -192,10 +192,10 @@ dust_status_t dust_validate_local(const void* X, const float* E, int64_t T,
 /*
  * The estimator with local scoring, for sites whose jitter never reaches the
  * loss ("Dust: every token is a member of the population", section "What the
- * released code actually does", step 4: attention internals are scored
- * against the estimated error of their output, c_s = -<g_s, Delta o_s>;
- * keys, values and gates sum later tokens' scores decayed by gamma = 0.98,
- * queries keep their own token's score, gamma = 0).  Draw i jitters the
+ * released code actually does", step 4: a perturbed attention internal
+ * earns c_s = -<g_s, Delta o_s>, the inner product of its output's change
+ * with an error estimate of that output; keys, values and gates add later
+ * tokens' scores with decay gamma = 0.98, queries use their own, gamma = 0).  Draw i jitters the
  * layer's own output by Delta o_t^(i) = s_i sigma a_t^(n(i)) and is scored
  * rho_t^(i) = -<E_t, Delta o_t^(i)>; centring, credit, g and
  * G_W = sum_t g_t x_t^T follow as in dust_estimate.  E[g_t] = E_t with
@@ -224,10 +224,10 @@ dust_status_t dust_estimate_local(const void* X, const float* E, int64_t T,
 /*
  * Local scoring through a recomputed attention ("Dust: every token is a
  * member of the population", section "What the released code actually
- * does", step 4: the queries, keys or values of one block are jittered, that
- * block's attention is recomputed from its cached activations, and the
- * change of its output is scored against the estimated error of the
- * attention output, c_s = -<e_s, Delta o_s>).  The attention is causal
+ * does", step 4, in the form that perturbs a query, key or value of an
+ * attention block and evaluates that block's attention again from the
+ * activations kept from the clean forward; the score is c_s =
+ * -<e_s, Delta o_s>, e an error estimate of the attention output).  The attention is causal
  * softmax attention inside each sequence, heads of width d_head:
  * o_s,h = sum_{t<=s} softmax_t(<q_s,h, k_t,h> / sqrt(d_head)) v_t,h.  Draw i
  * jitters the site's token t by s_i sigma a_t^(n(i)) over its heads * d_head

@@ -33,18 +33,19 @@
  *
  * A second scoring rule replaces the loss of steps 1-2 with a linear score
  * against a supplied error estimate e_t of the layer's output ("What the
- * released code actually does", step 4: attention internals are scored as
- * c_s = -<g_s, Delta o_s> against the estimated output error, keys and
- * values decayed by gamma = 0.98, queries with their own token's score).
+ * released code actually does", step 4: a perturbation of an attention
+ * internal earns the score c_s = -<g_s, Delta o_s>, the inner product of
+ * the output's change with an error estimate of that output; keys and
+ * values decay later tokens' scores by gamma = 0.98, queries keep their own).
  * Reading used: the jittered output is the layer's own, Delta o_t^(i) =
  * s_i sigma a_t^(n(i)), so the score of draw i at token t is
  * rho_t^(i) = -<e_t, Delta o_t^(i)>, evaluated literally; steps 3-6 then
  * run unchanged (dust_oracle_estimate_local).
  *
- * The same step's own form recomputes the attention: the internals
- * (queries, keys, values) are jittered, only their block's attention is
- * recomputed from cached activations, and the change of the attention
- * output is what the error estimate scores.  Reading used: one block's
+ * In the page's own form of that step the perturbed internal is a query,
+ * key or value of an attention block, the block's attention is evaluated
+ * again from the activations kept from the clean forward, and the score
+ * uses the change of the attention output.  Reading used: one block's
  * causal softmax attention with H heads of width d_head inside each
  * sequence, o_s = sum_{t <= s} softmax_t(<q_s, k_t> / sqrt(d_head)) v_t per
  * head; the site (queries, keys or values, a [T][H d_head] array whose head

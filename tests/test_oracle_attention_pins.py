@@ -3,9 +3,9 @@
 
 The site is one block's causal softmax attention ("Dust: every token is a
 member of the population", section "What the released code actually does",
-step 4: queries, keys and values are jittered, only that block's attention
-is recomputed, and its output change is scored against the estimated
-attention-output error, c_s = -<g_s, Delta o_s>).  The oracle recomputes the
+step 4, in the form that perturbs a query, key or value and evaluates the
+block's attention again; a draw's score is c_s = -<g_s, Delta o_s> with g an
+error estimate of the attention output).  The oracle recomputes the
 jittered attention literally; these pins check it against independent numpy
 algebra:
 

@@ -1,6 +1,6 @@
 """Pins of the oracle's cross-entropy head ("What the released code actually
-does", step 5: the head is jittered on its logits one 256-column slab of the
-vocabulary at a time, and only the cross-entropy is recomputed).
+does", step 5: the head's logits are perturbed in 256-column slabs of the
+vocabulary, one slab per draw, and the cross-entropy alone is formed again).
 
 Reading pinned here: the layer is the head z_t = W x_t with the per-token
 loss CE(z_t, y_t) = logsumexp(z_t) - z_t[y_t]; each slab of columns is its

@@ -1,8 +1,9 @@
 """Pins of the oracle's local scoring ("What the released code actually
-does", step 4: attention internals never reach the loss, so a jitter is
-scored against the estimated output error as c_s = -<g_s, Delta o_s>; keys,
-values and gates sum later tokens' scores decayed by gamma = 0.98, queries
-keep their own token's score).
+does", step 4: attention internals have no direct path to the loss, so a
+jitter earns c_s = -<g_s, Delta o_s>, the inner product of the output's
+change with an error estimate of that output; keys, values and gates add
+later tokens' scores with decay gamma = 0.98, queries use their own token's
+score only).
 
 Reading pinned here: the jittered output is the layer's own, so draw i's
 score at token t is -<e_t, s_i sigma a_t^(n(i))> against a supplied error

@@ -1,9 +1,10 @@
 // dust_attention.hpp -- kernels of local scoring through a recomputed
 // attention ("Dust: every token is a member of the population", section
-// "What the released code actually does", step 4: the queries, keys or
-// values of one block are jittered, only that block's causal attention is
-// recomputed from its cached activations, and the change of its output is
-// scored against the estimated error of that output, c_s = -<e_s, Delta o_s>).
+// "What the released code actually does", step 4, in the form that perturbs
+// a query, key or value of an attention block and evaluates that block's
+// causal attention again from the activations kept from the clean forward;
+// a draw's score is c_s = -<e_s, Delta o_s>, e an error estimate of the
+// attention output).
 //
 // Included by dust_kernels.hip inside namespace dust, after the noise and
 // wave-reduction helpers; it includes nothing itself.

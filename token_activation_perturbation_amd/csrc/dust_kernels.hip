@@ -1370,8 +1370,8 @@ __global__ __launch_bounds__(256) void chain_sum_kernel(const float* __restrict_
 
 // ---------------------------------------------------------------------------
 // Cross-entropy head ("What the released code actually does", step 5): the
-// logits z_t = W x_t are jittered one slab of 256 columns at a time, every
-// slab its own site with K draws, and only the cross-entropy is recomputed.
+// logits z_t = W x_t are perturbed in slabs of 256 columns, every slab its own
+// site with K draws, and the cross-entropy alone is formed again.
 // With m = max_c z_c, e_c = exp(z_c - m) and S = sum_c e_c, the jitter
 // s sigma a on slab j changes the sum by u_s = sum_{c in j} e_c expm1(s sigma a_c),
 // so the loss reduction rho = CE(z) - CE(z + jitter) is
@@ -1380,7 +1380,7 @@ __global__ __launch_bounds__(256) void chain_sum_kernel(const float* __restrict_
 //                     = -log1p(q expm1(-s sigma a_y) + exp(-s sigma a_y) u'_s / S)
 // with u'_s the same sum without the label's column and q = 1 - p_y formed as
 // (S - e_y) / S from a sum that leaves e_y out.  Only the slab's partial sum
-// is recomputed, and rho is formed at its own scale: no difference of two
+// is formed per draw, and rho is formed at its own scale: no difference of two
 // O(log V) losses, and no cancellation when the head is confident (p_y near
 // 1).  The loss is per token (gamma = 0), so g is formed in the same pass,
 // as in fused_g0_kernel:
