@@ -183,3 +183,32 @@ def test_full_size_sampled(dev, oracle_mod, name):
     e_G = rel(G[rows], G_ref)
     report(f"  {name}", {"rho": e_rho, "rho_row": e_rho_row, "g": e_g, "G_W": e_G})
     assert_within({"rho": e_rho, "rho_row": e_rho_row, "g": e_g, "G_W": e_G}, "bf16")
+
+
+def draw_attention_case(i):
+    rng = np.random.default_rng(9500 + i)
+    anti = bool(rng.integers(0, 2))
+    site = SITES[int(rng.integers(0, 3))]
+    return dict(site=site, n_seq=int(rng.integers(1, 4)), L=int(rng.integers(1, 301)),
+                heads=int(rng.integers(1, 5)), d_head=int(rng.choice([64, 128])),
+                d_in=int(rng.choice([1, 16, 48, 100])),
+                K=int(rng.integers(1, 13)) * 2 if anti else int(rng.integers(2, 25)),
+                sigma=float(10 ** rng.uniform(-3, -0.5)),
+                gamma=float(rng.choice([0.0, 1.0, rng.uniform(0.05, 0.99)])),
+                antithetic=anti, seed=int(rng.integers(0, 2**62)),
+                with_x=bool(rng.integers(0, 4) > 0))
+
+
+RANDOM_CASES = [draw_attention_case(i) for i in range(16)]
+
+
+@pytest.mark.parametrize("c", RANDOM_CASES, ids=[
+    f"{c['site']}_S{c['n_seq']}_L{c['L']}_H{c['heads']}x{c['d_head']}_K{c['K']}"
+    f"{'_pairs' if c['antithetic'] else '_plain'}_g{c['gamma']:.2f}{'' if c['with_x'] else '_nox'}"
+    for c in RANDOM_CASES])
+def test_random_shapes(dev, oracle_mod, threads, c):
+    """Seeded random cases, every parameter at once: sequence count and
+    length (ragged and one-token), heads and width, site, draw kind, K,
+    sigma (1e-3 to 0.3, so some logit changes take the exponential form of
+    e^x - 1), gamma and the block's input present or not."""
+    run_case(dev, oracle_mod, threads, **c)
