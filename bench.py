@@ -42,10 +42,13 @@ if ROOT not in sys.path:
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 CAL_COPY_BYTES = 256 << 20
-# every source the kernels and their launch configuration are built from
+# every source the kernels and their launch configuration are built from; the
+# attention site's kernels are also built from ATTENTION_SOURCES, which no
+# other workload's kernels use
 KERNEL_SOURCES = ["token_activation_perturbation_amd/csrc/" + f for f in (
     "dust_kernels.hip", "dust_noise.hpp", "dust_gemm.hpp", "dust_reassemble.hpp",
-    "dust_plan.hpp", "dust_attention.hpp")]
+    "dust_plan.hpp")]
+ATTENTION_SOURCES = ["token_activation_perturbation_amd/csrc/dust_attention.hpp"]
 # the estimator's five reference configurations, in order
 REFERENCE_CONFIGS = ["tiny_f32", "bf16_layer", "mlp_up_bf16", "qkv_credit_bf16",
                      "large_population_bf16"]
@@ -63,9 +66,12 @@ def _code_only(text: str) -> str:
     return " ".join(text.split())
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(workload: str | None = None) -> str:
+    """Hash of the code (comments dropped) that the workload's kernels are
+    built from: the attention sources count only for attention workloads."""
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    extra = ATTENTION_SOURCES if workload is not None and workload.startswith("attn_") else []
+    for rel in KERNEL_SOURCES + extra:
         with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
             h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
@@ -82,7 +88,7 @@ def read_traffic(workload: str, kernel: str):
     entry = data.get(workload)
     if not entry or entry.get("kernel") != kernel:
         return None
-    if entry.get("source_hash") != kernel_source_hash():
+    if entry.get("source_hash") != kernel_source_hash(workload):
         return None
     return entry.get("bytes_per_launch")
 

@@ -58,3 +58,16 @@ def test_kernel_hash_ignores_comments_only():
         'int a = 1; // other note\n/* another */ const char* s = "//x";\n  int b;')
     assert bench._code_only(code) != bench._code_only(code.replace("int b;", "int c;"))
     assert bench._code_only(code) != bench._code_only(code.replace('"//x"', '"//y"'))
+
+
+def test_kernel_hash_covers_the_attention_sources_only_for_attention_workloads(monkeypatch):
+    import bench
+    base = bench.kernel_source_hash("mlp_up_bf16")
+    attn = bench.kernel_source_hash("attn_key_bf16")
+    assert base != attn
+    assert bench.kernel_source_hash("attn_value_bf16") == attn
+    # another attention source changes the attention hash only
+    monkeypatch.setattr(bench, "ATTENTION_SOURCES",
+                        ["token_activation_perturbation_amd/csrc/dust_noise.hpp"])
+    assert bench.kernel_source_hash("mlp_up_bf16") == base
+    assert bench.kernel_source_hash("attn_key_bf16") != attn

@@ -59,17 +59,21 @@
 #define DUST_ATTN_WAVES 2
 #endif
 
-// e^x - 1 and e^-x - 1 for |x| < 1/4, from the Taylor series of e^x - 1
-// split into its even part ev and odd part od (e^x - 1 = ev + od,
-// e^-x - 1 = ev - od); the first terms left out, x^8 / 8! and x^9 / 9!, are
-// below 2e-9 |x| there.
-__device__ __forceinline__ void attn_expm1_series(float x, float& ep, float& em) {
+// The even and odd parts of e^x - 1 for |x| < 1/4 (e^x - 1 = ev + od,
+// e^-x - 1 = ev - od), from their Taylor series to x^5: the first terms left
+// out, x^6 / 720 and x^7 / 5040, are below 1.4e-6 |x| there (below 4e-10 |x|
+// at the |x| ~ 0.05 of sigma = 0.05), under the 2^-17 relative residual the
+// noise's hi + lo split already puts into x.
+__device__ __forceinline__ void attn_expm1_parts(float x, float& ev, float& od) {
   const float u = x * x;
-  const float od =
-      x * __builtin_fmaf(u, __builtin_fmaf(u, __builtin_fmaf(u, 1.f / 5040.f, 1.f / 120.f),
-                                           1.f / 6.f),
-                         1.f);
-  const float ev = u * __builtin_fmaf(u, __builtin_fmaf(u, 1.f / 720.f, 1.f / 24.f), 0.5f);
+  od = x * __builtin_fmaf(u, __builtin_fmaf(u, 1.f / 120.f, 1.f / 6.f), 1.f);
+  ev = u * __builtin_fmaf(u, 1.f / 24.f, 0.5f);
+}
+
+// e^x - 1 and e^-x - 1 for |x| < 1/4.
+__device__ __forceinline__ void attn_expm1_series(float x, float& ep, float& em) {
+  float ev, od;
+  attn_expm1_parts(x, ev, od);
   ep = ev + od;
   em = ev - od;
 }
@@ -102,11 +106,30 @@ __device__ __forceinline__ bool attn_any_large(const f32x4_t (&acc)[NV][4]) {
 // The row sums of one 16 x 16 D tile (acc: the logit changes x of the
 // lane's 4 entries; pp, bb: their p and B): S1 += p E, S2 += B E with
 // E = e^x - 1, and with antithetic pairs the same for e^-x - 1.  LARGE: the
-// general form of e^x - 1, else its series.
+// general form of e^x - 1, else its series; the series with antithetic
+// pairs sums p ev, p od, B ev and B od and forms the two signs' sums from
+// them (S1 for +x is sum p ev + sum p od, for -x sum p ev - sum p od).
 template <bool LARGE, bool ANTI>
 __device__ __forceinline__ void attn_tile_sums(const f32x4_t& acc, const float (&pp)[4],
                                                const float (&bb)[4], float& s1p, float& s2p,
                                                float& s1m, float& s2m) {
+  if constexpr (!LARGE && ANTI) {
+    float pe = 0.f, po = 0.f, be = 0.f, bo = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float ev, od;
+      attn_expm1_parts(acc[i], ev, od);
+      pe = __builtin_fmaf(pp[i], ev, pe);
+      po = __builtin_fmaf(pp[i], od, po);
+      be = __builtin_fmaf(bb[i], ev, be);
+      bo = __builtin_fmaf(bb[i], od, bo);
+    }
+    s1p += pe + po;
+    s2p += be + bo;
+    s1m += pe - po;
+    s2m += be - bo;
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     float ep, em;
