@@ -245,19 +245,23 @@ struct AttnRowsSplit {
 // operand, and lane l holds D rows s = 64 b + 16 w + 4 (l / 16) + i, i < 4,
 // of columns t = 64 j + 16 tt + l % 16 for the four t tiles tt.
 //   pass 1: the logits <q_s, k_t> / sqrt(d) (bf16 products, exact, fp32
-//           sums) and, online, each row's maximum and sum of exponentials,
-//           combined over the 16 lanes of the row at the end;
+//           sums; carried in base 2, times log2 e, so the exponentials are
+//           the hardware's 2^x, within ~1e-6 relative) and, online, each
+//           row's maximum and sum of exponentials, combined over the 16
+//           lanes of the row at the end;
 //   pass 2: p_st written to P, and (WB) M_st = <e_s, v_t> with its row
 //           sums m0_s = sum_t p_st M_st (= <e_s, o_s>);
 //   pass 3 (WB): p_st and M_st again (the same instructions, so the same
 //           bits) and B_st = p_st (M_st - m0_s) written to B.
-// Entries past the causal edge or the sequence are written as 0.
+// Entries past the causal edge or the sequence are written as 0; blocks
+// wholly below the diagonal and inside the sequence skip the mask.
 template <int DH, bool WB>
 __global__ __launch_bounds__(256) void attn_clean_kernel(
     const uint16_t* __restrict__ Qa, const uint16_t* __restrict__ Ka,
     const uint16_t* __restrict__ Va, const float* __restrict__ E, int32_t L, int32_t Lp,
-    int32_t nb, int32_t n_seq, int32_t H, int32_t D, float scale, float* __restrict__ Pm,
+    int32_t nb, int32_t n_seq, int32_t H, int32_t D, float scale2, float* __restrict__ Pm,
     float* __restrict__ Bm) {
+  // scale2 = log2(e) / sqrt(d): logits in base 2
   constexpr int KS = DH / 32;
   using Rows = AttnRows<DH>;
   __shared__ __attribute__((aligned(16))) uint16_t kt[64 * Rows::LD];
@@ -332,6 +336,8 @@ __global__ __launch_bounds__(256) void attn_clean_kernel(
     const int s = srow0 + i;
     return t <= s && t < L && s < L;
   };
+  // block j lies wholly below the diagonal and inside the sequence
+  auto interior = [&](int j) { return j < b && 64 * (b + 1) <= L; };
 
   // 1. row maxima and sums of exponentials
   float mx[4], z[4];
@@ -345,17 +351,19 @@ __global__ __launch_bounds__(256) void attn_clean_kernel(
     stage(j, false);
     f32x4_t acc[4];
     logits(acc);
+    const bool all = interior(j);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       float m_new = mx[i];
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt)
-        if (valid(i, 64 * j + 16 * tt + r16)) m_new = fmaxf(m_new, acc[tt][i] * scale);
+        if (all || valid(i, 64 * j + 16 * tt + r16)) m_new = fmaxf(m_new, acc[tt][i] * scale2);
       if (m_new == -INFINITY) continue;
-      float zr = mx[i] == -INFINITY ? 0.f : z[i] * expf(mx[i] - m_new);
+      float zr = mx[i] == -INFINITY ? 0.f : z[i] * __builtin_amdgcn_exp2f(mx[i] - m_new);
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt)
-        if (valid(i, 64 * j + 16 * tt + r16)) zr += expf(acc[tt][i] * scale - m_new);
+        if (all || valid(i, 64 * j + 16 * tt + r16))
+          zr += __builtin_amdgcn_exp2f(acc[tt][i] * scale2 - m_new);
       mx[i] = m_new;
       z[i] = zr;
     }
@@ -368,8 +376,8 @@ __global__ __launch_bounds__(256) void attn_clean_kernel(
     for (int i = 0; i < 4; ++i) {
       const float mo = __shfl_xor(mx[i], d), zo = __shfl_xor(z[i], d);
       const float mn = fmaxf(mx[i], mo);
-      const float a = mx[i] == -INFINITY ? 0.f : z[i] * expf(mx[i] - mn);
-      const float c = mo == -INFINITY ? 0.f : zo * expf(mo - mn);
+      const float a = mx[i] == -INFINITY ? 0.f : z[i] * __builtin_amdgcn_exp2f(mx[i] - mn);
+      const float c = mo == -INFINITY ? 0.f : zo * __builtin_amdgcn_exp2f(mo - mn);
       mx[i] = mn;
       z[i] = a + c;
     }
@@ -379,12 +387,14 @@ __global__ __launch_bounds__(256) void attn_clean_kernel(
   for (int i = 0; i < 4; ++i) rz[i] = z[i] > 0.f ? 1.f / z[i] : 0.f;
   const int64_t pbase = (int64_t)sh * Lp * Lp;
   auto probs = [&](int j, const f32x4_t (&acc)[4], float (&p)[4][4]) {
+    const bool all = interior(j);
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        p[tt][i] = valid(i, 64 * j + 16 * tt + r16) ? expf(acc[tt][i] * scale - mx[i]) * rz[i]
-                                                     : 0.f;
+        p[tt][i] = (all || valid(i, 64 * j + 16 * tt + r16))
+                       ? __builtin_amdgcn_exp2f(acc[tt][i] * scale2 - mx[i]) * rz[i]
+                       : 0.f;
   };
 
   // 2. P, and the row sums m0 of P o M

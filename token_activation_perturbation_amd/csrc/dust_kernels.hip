@@ -2353,12 +2353,14 @@ void launch_attn_clean(const AttnPlan& a, const Plan& p, const AttnArgs& at, flo
       stamp("attn_clean_kernel", 2.0 * pairs * a.dh * (wb ? 2.0 : 1.0),
             2.0 * 2.0 * td + (wb ? 2.0 * td + 4.0 * td : 0.0) + 4.0 * pairs * (wb ? 2.0 : 1.0));
   const dim3 grid((unsigned)(a.n_seq * a.H * a.nb));
+  // the logits in base 2: log2(e) / sqrt(d)
+  const float scale2 = (float)(1.4426950408889634 / std::sqrt((double)a.dh));
   if (wb)
     DUST_LAUNCH(ev, (attn_clean_kernel<DH, true>), grid, dim3(256), 0, s, at.Q, at.Kc, at.V, at.E,
-                L, Lp, a.nb, (int32_t)a.n_seq, H, D, 1.0f / sqrtf((float)a.dh), Pm, Bm);
+                L, Lp, a.nb, (int32_t)a.n_seq, H, D, scale2, Pm, Bm);
   else
     DUST_LAUNCH(ev, (attn_clean_kernel<DH, false>), grid, dim3(256), 0, s, at.Q, at.Kc, at.V,
-                at.E, L, Lp, a.nb, (int32_t)a.n_seq, H, D, 1.0f / sqrtf((float)a.dh), Pm, Bm);
+                at.E, L, Lp, a.nb, (int32_t)a.n_seq, H, D, scale2, Pm, Bm);
 }
 
 dust_status_t run_attention(const AttnArgs& at, int64_t T, int64_t d_in, int64_t seq_len,
