@@ -84,3 +84,22 @@ def test_noise_stage_slots(kernel, per_value):
     T, d_out, K = 4, 8, 6
     assert roofline.noise_stage_slots(kernel, T, d_out, K, True) == \
         pytest.approx(K // 2 * T * d_out * per_value)
+
+
+def test_attention_score_bound():
+    from token_activation_perturbation_amd import roofline as r
+    T, L, H, d, K = 16384, 2048, 4, 128, 64
+    pairs = (T // L) * H * L * (L + 1) / 2
+    assert r.attention_pairs(T, L, H) == pairs
+    assert r.attention_score_flops(T, L, H, d, K, True) == 2 * pairs * d * (K // 2)
+    gen = (K // 2) * T * H * d * (r.GEN_SLOTS_PER_VALUE + 1)
+    assert r.attention_score_slots("key", T, L, H, d, K, True) == (K // 2) * pairs * 11 + gen
+    assert r.attention_score_slots("query", T, L, H, d, K, False) == K * pairs * 9 + \
+        K * T * H * d * (r.GEN_SLOTS_PER_VALUE + 1)
+    assert r.attention_score_slots("value", T, L, H, d, K, True) == (K // 2) * pairs + gen
+    # keys and queries spend more time on the ALU than on the MFMA contraction,
+    # values the other way round
+    for site, bound in (("key", "alu"), ("query", "alu"), ("value", "mfma")):
+        b, work, peak, unit = r.attention_score_bound(site, T, L, H, d, K, True)
+        assert b == bound
+        assert unit == ("T lane-slot/s" if bound == "alu" else "TFLOP/s")
