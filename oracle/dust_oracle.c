@@ -87,9 +87,9 @@
  *   words of Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11) with counter
  *   (q, t, n, 0) and key (seed mod 2^32, floor(seed / 2^32));
  *   words (w0,w1) give channels 4q, 4q+1 and (w2,w3) channels 4q+2, 4q+3 by
- *   Box-Muller: u = ((w_even >> 8) + 1) 2^-24 in (0,1],
- *   v = (w_odd >> 8) 2^-24 in [0,1), R = sqrt(-2 ln u),
- *   a_even = R cos(2 pi v), a_odd = R sin(2 pi v).
+ *   Box-Muller on 23-bit uniforms (the top 23 bits of each word):
+ *   u = 1 - (w_even >> 9) 2^-23 in (0,1], v = (w_odd >> 9) 2^-23 in [0,1),
+ *   R = sqrt(-2 ln u), a_even = R cos(2 pi v), a_odd = R sin(2 pi v).
  *
  * Parity is pinned (see tests/): Philox words against an independent library
  * implementation, the Gaussians by distribution tests, each estimator step
@@ -148,8 +148,8 @@ static void quad_words(uint64_t seed, uint32_t n, uint32_t t, uint32_t q,
 /* Box-Muller on one pair of words, in fp64. */
 static void box_muller(uint32_t w_even, uint32_t w_odd, double *a_even,
                        double *a_odd) {
-  double u = ((double)(w_even >> 8) + 1.0) * (1.0 / 16777216.0);
-  double v = (double)(w_odd >> 8) * (1.0 / 16777216.0);
+  double u = 1.0 - (double)(w_even >> 9) * (1.0 / 8388608.0);
+  double v = (double)(w_odd >> 9) * (1.0 / 8388608.0);
   double radius = sqrt(-2.0 * log(u));
   *a_even = radius * cos(ORACLE_TWO_PI * v);
   *a_odd = radius * sin(ORACLE_TWO_PI * v);

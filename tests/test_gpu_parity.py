@@ -18,8 +18,9 @@ pytestmark = pytest.mark.gpu
 
 # fp32 Box-Muller from the hardware transcendentals: v_log_f32, v_sqrt_f32,
 # v_sin_f32 and v_cos_f32 are each accurate to a few ulp over the ranges used
-# (u in [2^-24, 1], v in [0, 1) revolutions); with |a| <= 5.77 a few ulp of
-# the largest values is about 2e-6, so 1e-5 absolute leaves a 5x margin.
+# (u in [2^-23, 1]; the angle in revolutions in [1, 2), whose fraction is
+# v); with |a| <= 5.65 a few ulp of the largest values is about 2e-6, so
+# 1e-5 absolute leaves a 5x margin.
 GAUSS_ABS_TOL = 1e-5
 
 

@@ -4,9 +4,10 @@ loop of noise indices (the noise kernels' own shape: the quad index is the
 only per-lane counter word) is compiled for gfx950 with the library's flags;
 the loop body's instructions per quad must be the ones the model counts:
 16 32x32->64 multiply-adds, 15 three-input xors and 3 xors for Philox
-(50 slots at 2 per product and 1 per single-pass op), 4 shifts, 4
-integer-to-float conversions, the u scaling FMA x 2 and 8 transcendentals
-for Box-Muller.  The same holds for noise_quad_x2, which the kernels use to
+(50 slots at 2 per product and 1 per single-pass op), and for Box-Muller 4
+funnel shifts (each uniform built in a float's bit fields, no
+integer-to-float conversion), 2 subtractions (u = 2 - x) and 8
+transcendentals.  The same holds for noise_quad_x2, which the kernels use to
 advance two quads' Philox rounds together (pairs of noise indices here): it
 must not cost a single extra instruction per quad.  Needs hipcc
 (cross-compiles, no GPU)."""
@@ -104,8 +105,11 @@ def test_philox_stream_is_the_modelled_one(loop_ops):
 def test_box_muller_stream_is_the_modelled_one(loop_ops):
     trans = sum(count(loop_ops, p) for p in ("v_log_f32", "v_sqrt_f32", "v_sin_f32", "v_cos_f32"))
     assert trans == 8
-    assert count(loop_ops, "v_cvt_f32_u32") == 4
-    assert count(loop_ops, "v_lshrrev_b32") == 4
+    assert count(loop_ops, "v_alignbit_b32") == 4
+    assert count(loop_ops, "v_sub_f32") == 2
+    # no integer-to-float conversion and no separate shift
+    assert count(loop_ops, "v_cvt_f32") == 0
+    assert count(loop_ops, "v_lshrrev_b32") == 0
     # no other integer products or transcendentals in the generation
     assert count(loop_ops, "v_mul_hi_u32") == 0 and count(loop_ops, "v_mul_lo_u32") == 0
     assert count(loop_ops, "v_exp_f32") == 0 and count(loop_ops, "v_rcp_f32") == 0

@@ -8,8 +8,8 @@
 //                                        key (seed low, seed high))
 //   (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as easy as 1, 2,
 //   3", SC'11), then Box-Muller on (w0,w1) for channels 4q, 4q+1 and on
-//   (w2,w3) for 4q+2, 4q+3 with 24-bit uniforms
-//   u = ((w_even >> 8) + 1) 2^-24 in (0,1], v = (w_odd >> 8) 2^-24 in [0,1),
+//   (w2,w3) for 4q+2, 4q+3 with 23-bit uniforms (each word's top 23 bits)
+//   u = 1 - (w_even >> 9) 2^-23 in (0,1], v = (w_odd >> 9) 2^-23 in [0,1),
 //   a_even = sqrt(-2 ln u) cos(2 pi v), a_odd = sqrt(-2 ln u) sin(2 pi v).
 //
 // gfx950 notes.  The counter is laid out so that one lane's quad index is the
@@ -17,8 +17,13 @@
 // two rounds largely run on the scalar unit or are loop-invariant, and the
 // key schedule is scalar.  The 32x32->64 products map to v_mad_u64_u32.  The
 // transform uses the hardware transcendental unit directly: v_log_f32 is
-// log2, and v_sin_f32 / v_cos_f32 take their argument in revolutions, so
-// 2 pi v needs no range reduction (v is already in [0,1)).
+// log2, and v_sin_f32 / v_cos_f32 take their argument in revolutions and
+// use only its fraction, so 2 pi v needs no range reduction.  A uniform is
+// built in a float's bit fields, not converted from an integer: the word's
+// top 23 bits under exponent field 127 are the float 1 + m 2^-23 in [1, 2)
+// (one funnel shift, v_alignbit_b32), whose fraction is v itself and whose
+// difference from 2 is u, where a shift, an integer-to-float conversion (a
+// half-rate instruction) and a scaling would cost four issue slots.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -77,10 +82,15 @@ __device__ __forceinline__ uint4 philox4x32_10(uint32_t x0, uint32_t x1, uint32_
 constexpr float kMinusTwoLn2 = -1.38629436111989061883f;
 
 __device__ __forceinline__ float2 box_muller(uint32_t w_even, uint32_t w_odd) {
-  const float u = __builtin_fmaf((float)(w_even >> 8), 0x1p-24f, 0x1p-24f);  // exact
-  const float v = (float)(w_odd >> 8) * 0x1p-24f;                            // exact
+  // the float 1 + (w >> 9) 2^-23 in [1, 2): exponent field 127, the word's
+  // top 23 bits as the mantissa (one funnel shift)
+  const float xu = __uint_as_float(__builtin_amdgcn_alignbit(0x7Fu, w_even, 9u));
+  const float xv = __uint_as_float(__builtin_amdgcn_alignbit(0x7Fu, w_odd, 9u));
+  const float u = 2.0f - xu;  // 1 - (w_even >> 9) 2^-23 in (0, 1], exact
   const float radius = __builtin_amdgcn_sqrtf(kMinusTwoLn2 * __builtin_amdgcn_logf(u));
-  return make_float2(radius * __builtin_amdgcn_cosf(v), radius * __builtin_amdgcn_sinf(v));
+  // v_sin / v_cos take revolutions and keep only the fraction, so xv itself
+  // is the angle v = (w_odd >> 9) 2^-23
+  return make_float2(radius * __builtin_amdgcn_cosf(xv), radius * __builtin_amdgcn_sinf(xv));
 }
 
 // The four Gaussians of channel quad q of token t under noise index n.

@@ -35,10 +35,11 @@ at once.  Their bound is the vector ALU issue rate, counted in lane-slots:
                     rounds 4-10: 7 x (2 products x 2 + 2 three-input
                     xors)                                          = 42
                                                                    = 50 slots
-    Box-Muller      per pair: 2 shifts, 2 conversions x 2, 1 FMA for u,
-                    1 multiply for v, log2, sqrt, sin, cos x 4, 1 multiply
-                    by -2 ln 2, 2 multiplies by the radius = 27;  = 54 slots
-  That gives 26 slots per value, plus the consumers: 1 FMA for
+    Box-Muller      per pair: 2 funnel shifts (each word's top 23 bits
+                    as the mantissa of a float in [1, 2)), 1 subtraction
+                    for u, log2, sqrt, sin, cos x 4, 1 multiply by
+                    -2 ln 2, 2 multiplies by the radius = 22;      = 44 slots
+  That gives 23.5 slots per value, plus the consumers: 1 FMA for
   P = <delta, a>, 1 FMA for Q = ||a||^2 (the quadratic loss's curvature
   term: needed by plain draws and by the per-draw outputs; with antithetic
   pairs it cancels inside each pair, so a call that asks only for g and G_W
@@ -50,7 +51,7 @@ The cross-entropy head's slab kernel consumes each value as: 1 multiply
 (sigma a), the jitter's expm1 (antithetic: both signs from the even and odd
 Taylor parts, 9 + 2 slots; plain draws: 8 slots of Horner), the slab's
 partial sums (one FMA per sign), 1 FMA for g and, for plain draws, 1 add for
-the noise sum: 41 slots per value with antithetic pairs, 38 without.
+the noise sum: 38.5 slots per value with antithetic pairs, 35.5 without.
 
 The generation alone (noise_quad in a loop, the probe's last row) runs at
 ~0.84 of this model's peak with the clock at 2.4 GHz: the
@@ -74,11 +75,11 @@ SINGLE, HALF, QUARTER = 1, 2, 4
 PHILOX_SLOTS_PER_QUAD = (2 * SINGLE                         # second round
                          + 2 * HALF + 2 * SINGLE            # third round
                          + 7 * (2 * HALF + 2 * SINGLE))     # rounds 4-10: 50
-BOX_MULLER_SLOTS_PER_QUAD = 2 * (2 * SINGLE + 2 * HALF      # shifts, conversions
-                                 + 2 * SINGLE               # u, v scaling
+BOX_MULLER_SLOTS_PER_QUAD = 2 * (2 * SINGLE               # funnel shifts: u, v fields
+                                 + 1 * SINGLE               # u = 2 - (1 + m 2^-23)
                                  + 4 * QUARTER              # log2, sqrt, sin, cos
-                                 + 3 * SINGLE)              # -2 ln 2, radius x 2: 54
-GEN_SLOTS_PER_VALUE = (PHILOX_SLOTS_PER_QUAD + BOX_MULLER_SLOTS_PER_QUAD) / 4.0  # 26
+                                 + 3 * SINGLE)              # -2 ln 2, radius x 2: 44
+GEN_SLOTS_PER_VALUE = (PHILOX_SLOTS_PER_QUAD + BOX_MULLER_SLOTS_PER_QUAD) / 4.0  # 23.5
 
 
 def distinct_noise_values(T: int, d_out: int, K: int, antithetic: bool) -> int:
