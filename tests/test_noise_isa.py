@@ -6,8 +6,9 @@ the loop body's instructions per quad must be the ones the model counts:
 16 32x32->64 multiply-adds, 15 three-input xors and 3 xors for Philox
 (50 slots at 2 per product and 1 per single-pass op), and for Box-Muller 4
 funnel shifts (each uniform built in a float's bit fields, no
-integer-to-float conversion), 2 subtractions (u = 2 - x) and 8
-transcendentals.  The same holds for noise_quad_x2, which the kernels use to
+integer-to-float conversion), 2 subtractions (u = 2 - x), 8
+transcendentals and 4 multiplies by the radius (the values come in units of
+sqrt(2 ln 2): no multiply by -2 ln 2).  The same holds for noise_quad_x2, which the kernels use to
 advance two quads' Philox rounds together (pairs of noise indices here): it
 must not cost a single extra instruction per quad.  Needs hipcc
 (cross-compiles, no GPU)."""
@@ -107,9 +108,13 @@ def test_box_muller_stream_is_the_modelled_one(loop_ops):
     assert trans == 8
     assert count(loop_ops, "v_alignbit_b32") == 4
     assert count(loop_ops, "v_sub_f32") == 2
-    # no integer-to-float conversion and no separate shift
+    # no integer-to-float conversion, no separate shift, and the log's
+    # negation rides on the square root as a source modifier
     assert count(loop_ops, "v_cvt_f32") == 0
     assert count(loop_ops, "v_lshrrev_b32") == 0
+    # 4 radius products per quad, of which the test loop's own sum fuses 3
+    # into FMAs
+    assert count(loop_ops, "v_mul_f32") + count(loop_ops, "v_fmac_f32") == 4
     # no other integer products or transcendentals in the generation
     assert count(loop_ops, "v_mul_hi_u32") == 0 and count(loop_ops, "v_mul_lo_u32") == 0
     assert count(loop_ops, "v_exp_f32") == 0 and count(loop_ops, "v_rcp_f32") == 0

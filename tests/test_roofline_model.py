@@ -5,9 +5,10 @@ transcendentals 4.  Philox4x32-10 per quad and draw: the second round's two
 xors, the third round's two products, three-input xor and xor, then seven
 rounds of two products and two three-input xors (50 slots); Box-Muller per
 pair 2 funnel shifts (the uniforms built in a float's bit fields), the
-subtraction that forms u, 4 transcendentals, the -2 ln 2 multiply and two
-multiplies by the radius (22 slots, 44 per quad); the consumers one slot
-each."""
+subtraction that forms u, 4 transcendentals and two multiplies by the
+radius (21 slots, 42 per quad: the values come in units of sqrt(2 ln 2),
+which the consumers apply per total, not per value); the consumers one
+slot each."""
 import pytest
 
 from token_activation_perturbation_amd import roofline
@@ -20,15 +21,15 @@ def test_peak_is_the_fp32_vector_rate():
 
 def test_generation_slots_per_value():
     assert roofline.PHILOX_SLOTS_PER_QUAD == 2 + (4 + 2) + 7 * (4 + 2)
-    assert roofline.BOX_MULLER_SLOTS_PER_QUAD == 2 * (2 + 1 + 16 + 3)
-    assert roofline.GEN_SLOTS_PER_VALUE == 23.5
+    assert roofline.BOX_MULLER_SLOTS_PER_QUAD == 2 * (2 + 1 + 16 + 2)
+    assert roofline.GEN_SLOTS_PER_VALUE == 23.0
 
 
 @pytest.mark.parametrize("anti,outputs,per_value", [
-    (True, False, 25.5),   # P and g; the pair cancels the curvature: no Q
-    (True, True, 26.5),    # rho or the credit asked for: Q too
-    (False, False, 27.5),  # plain draws: Q in the weight, the noise sum for centring
-    (False, True, 27.5),
+    (True, False, 25.0),   # P and g; the pair cancels the curvature: no Q
+    (True, True, 26.0),    # rho or the credit asked for: Q too
+    (False, False, 27.0),  # plain draws: Q in the weight, the noise sum for centring
+    (False, True, 27.0),
 ])
 def test_fused_kernel_slots(anti, outputs, per_value):
     T, d_out, K = 8, 12, 6
@@ -40,24 +41,24 @@ def test_fused_kernel_slots(anti, outputs, per_value):
 def test_local_scoring_has_no_curvature_term():
     # P and g (antithetic) or P, g and the noise sum (plain): never Q
     assert roofline.fused_kernel_slots(2, 4, 4, True, per_draw_outputs=True, local=True) == \
-        pytest.approx(2 * 2 * 4 * 25.5)
+        pytest.approx(2 * 2 * 4 * 25.0)
     assert roofline.fused_kernel_slots(2, 4, 4, False, local=True) == \
-        pytest.approx(4 * 2 * 4 * 26.5)
+        pytest.approx(4 * 2 * 4 * 26.0)
     assert roofline.jitter_kernel_slots(2, 4, 4, True, local=True) == \
-        pytest.approx(2 * 2 * 4 * 24.5)
+        pytest.approx(2 * 2 * 4 * 24.0)
 
 
 def test_two_pass_and_head_slots():
-    assert roofline.jitter_kernel_slots(2, 4, 4, True) == pytest.approx(2 * 2 * 4 * 25.5)
-    assert roofline.head_slots_per_value(True) == 38.5
-    assert roofline.head_slots_per_value(False) == 35.5
-    assert roofline.head_kernel_slots(1, 256, 4, True) == pytest.approx(2 * 256 * 38.5)
+    assert roofline.jitter_kernel_slots(2, 4, 4, True) == pytest.approx(2 * 2 * 4 * 25.0)
+    assert roofline.head_slots_per_value(True) == 38.0
+    assert roofline.head_slots_per_value(False) == 35.0
+    assert roofline.head_kernel_slots(1, 256, 4, True) == pytest.approx(2 * 256 * 38.0)
 
 
 def test_minimum_time_is_one_generation_at_peak():
     T, d_out, K = 4096, 512, 64
     assert roofline.estimate_min_seconds(T, d_out, K, True) == pytest.approx(
-        32 * T * d_out * 25.5 / roofline.PEAK_SLOTS_PER_S)
+        32 * T * d_out * 25.0 / roofline.PEAK_SLOTS_PER_S)
 
 
 def test_stage_roofline_picks_the_bound_of_each_kind():
@@ -79,8 +80,8 @@ def test_stage_roofline_picks_the_bound_of_each_kind():
 
 
 @pytest.mark.parametrize("kernel,per_value", [
-    ("fused_g0_kernel", 25.5), ("chain_g_kernel", 25.5), ("jitter_loss_kernel", 25.5),
-    ("reweight_kernel", 24.5)])
+    ("fused_g0_kernel", 25.0), ("chain_g_kernel", 25.0), ("jitter_loss_kernel", 25.0),
+    ("reweight_kernel", 24.0)])
 def test_noise_stage_slots(kernel, per_value):
     T, d_out, K = 4, 8, 6
     assert roofline.noise_stage_slots(kernel, T, d_out, K, True) == \

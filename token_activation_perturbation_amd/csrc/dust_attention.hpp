@@ -159,6 +159,7 @@ template <int KS>
 __device__ __forceinline__ void attn_noise_frags(bool valid, uint32_t n, uint32_t tg, int hc,
                                                  int g, float scale, NoiseKey key,
                                                  u16x8_t (&hi)[KS], u16x8_t (&lo)[KS]) {
+  scale *= kNoiseUnit;  // the generator's values are in units of kNoiseUnit
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     uint32_t h0 = 0u, h1 = 0u, h2 = 0u, h3 = 0u, l0 = 0u, l1 = 0u, l2 = 0u, l3 = 0u;

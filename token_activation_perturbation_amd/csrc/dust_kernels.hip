@@ -103,7 +103,7 @@ __global__ void noise_fill_kernel(NoiseKey key, int32_t n0, int32_t n_cnt, int32
   if (gauss) {
     const float2 a = box_muller(w.x, w.y);
     const float2 b = box_muller(w.z, w.w);
-    const float v[4] = {a.x, a.y, b.x, b.y};
+    const float v[4] = {kNoiseUnit * a.x, kNoiseUnit * a.y, kNoiseUnit * b.x, kNoiseUnit * b.y};
     float* dst = gauss + nt * d_out;
     for (int j = 0; j < 4; ++j) {
       const int32_t c = 4 * q + j;
@@ -300,8 +300,8 @@ __global__ __launch_bounds__(256) void jitter_loss_kernel(
 #pragma unroll
         for (int j = 0; j < kNoiseBatch; j += 2) {
           float4 an[2];
-          noise_quad_x2((uint32_t)q, (uint32_t)(nb + j), (uint32_t)q, (uint32_t)(nb + j + 1),
-                        (uint32_t)t, key, an[0], an[1]);
+          noise_quad_x2<false>((uint32_t)q, (uint32_t)(nb + j), (uint32_t)q,
+                               (uint32_t)(nb + j + 1), (uint32_t)t, key, an[0], an[1]);
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
             if (ALL || nb + j + h < n_end) {
@@ -610,6 +610,9 @@ __global__ __launch_bounds__(256) void reweight_kernel(
     }
     if (wave == 0 && q < nq) {
       const int c = 4 * q;
+      // the noise came in units of kNoiseUnit
+      acc = make_float4(kNoiseUnit * acc.x, kNoiseUnit * acc.y, kNoiseUnit * acc.z,
+                        kNoiseUnit * acc.w);
       store_g_quad(acc, (int64_t)t * d_out, c, d_out, c + 3 < d_out && (d_out & 3) == 0, g32,
                    g_hi, g_lo);
     }
@@ -900,7 +903,10 @@ __global__ __launch_bounds__(256) void fused_g0_kernel(
     if (lane == 0) loss_clean[t] = 0.5f * s;
   }
 
-  const float half_s2 = curv_coef;
+  // the noise comes in units of kNoiseUnit: P = kNoiseUnit P', Q =
+  // kNoiseUnit^2 Q' for the reduced totals P', Q' of that noise, so the
+  // weight of a plain draw takes the scaled coefficients
+  const float sigma_u = sigma * kNoiseUnit, half_s2 = curv_coef * kNoiseUnit2;
   float rsum = 0.f;
   for (int32_t nb = n_begin; nb < n_end; nb += NB) {
     float4 a[NB][QPL];
@@ -955,10 +961,10 @@ __global__ __launch_bounds__(256) void fused_g0_kernel(
       if (n < n_end) {
         const float P = tot[i], Q = tot[NB + i];
         if (Pout && lane == 0) {
-          Pout[(int64_t)t * K_n + n] = P;
-          if (QN && Qout) Qout[(int64_t)t * K_n + n] = Q;
+          Pout[(int64_t)t * K_n + n] = kNoiseUnit * P;
+          if (QN && Qout) Qout[(int64_t)t * K_n + n] = kNoiseUnit2 * Q;
         }
-        const float w = ANTI ? P : -__builtin_fmaf(sigma, P, half_s2 * Q);
+        const float w = ANTI ? P : -__builtin_fmaf(sigma_u, P, half_s2 * Q);
         if (!ANTI) rsum += w;
 #pragma unroll
         for (int j = 0; j < QPL; ++j) {
@@ -1014,7 +1020,9 @@ __global__ __launch_bounds__(256) void fused_g0_kernel(
   }
   if (wave != 0) return;
   const float mean_rho = rsum / (float)K;
-  const float scale = ANTI ? 2.0f / (float)K : -1.0f / ((float)K * sigma);
+  // antithetic: g = (2/K) sum_n P_n a^n, both factors in noise units;
+  // plain draws: the weights are true loss reductions, the noise is not
+  const float scale = ANTI ? 2.0f * kNoiseUnit2 / (float)K : -kNoiseUnit / ((float)K * sigma);
 #pragma unroll
   for (int j = 0; j < QPL; ++j) {
     const int q = lane + 64 * j;
@@ -1130,7 +1138,9 @@ __global__ __launch_bounds__(64 * kChainWaves) void chain_g_kernel(
 #pragma unroll
     for (int ch = 0; ch < CPW; ++ch) {
       if (PLAIN) {
-        const float rho = -__builtin_fmaf(sigma, tot[ch], curv * tot[CPW + ch]);
+        // noise units: P = kNoiseUnit P', Q = kNoiseUnit^2 Q'
+        const float rho =
+            -__builtin_fmaf(sigma * kNoiseUnit, tot[ch], curv * kNoiseUnit2 * tot[CPW + ch]);
         R[ch] = __builtin_fmaf(gamma, R[ch], rho);
         rho_w = __builtin_fmaf(live[ch], rho, rho_w);
       } else {
@@ -1510,7 +1520,10 @@ __global__ __launch_bounds__(256) void head_ce_kernel(
   if (wave == 0 && lane == 0 && loss_clean)
     loss_clean[t] = (e_y * inv_s > 0.5f) ? log1pf(s_ex / e_y) : (zmax - z_y) + logf(ssum);
   const float q_y = s_ex * inv_s;  // 1 - p_y
-  const float scale = -1.0f / ((float)K * sigma);
+  // the noise comes in units of kNoiseUnit: the jitter is sigma_u a' and g
+  // carries the unit once
+  const float sigma_u = sigma * kNoiseUnit;
+  const float scale = -kNoiseUnit / ((float)K * sigma);
   const int y_slab = y >> 8, y_lane = (y & 255) >> 2, y_comp = y & 3;
 
   for (int32_t j = wave; j < n_slab; j += waves) {
@@ -1532,19 +1545,19 @@ __global__ __launch_bounds__(256) void head_ce_kernel(
         if (n >= K_n) a[i] = make_float4(0.f, 0.f, 0.f, 0.f);
         if (ANTI) {
           float p0, m0, p1, m1, p2, m2, p3, m3;
-          expm1_pm<SMALL>(sigma * a[i].x, p0, m0);
-          expm1_pm<SMALL>(sigma * a[i].y, p1, m1);
-          expm1_pm<SMALL>(sigma * a[i].z, p2, m2);
-          expm1_pm<SMALL>(sigma * a[i].w, p3, m3);
+          expm1_pm<SMALL>(sigma_u * a[i].x, p0, m0);
+          expm1_pm<SMALL>(sigma_u * a[i].y, p1, m1);
+          expm1_pm<SMALL>(sigma_u * a[i].z, p2, m2);
+          expm1_pm<SMALL>(sigma_u * a[i].w, p3, m3);
           v[i] = __builtin_fmaf(e.x, p0, __builtin_fmaf(e.y, p1, __builtin_fmaf(e.z, p2, e.w * p3)));
           v[NB + i] =
               __builtin_fmaf(e.x, m0, __builtin_fmaf(e.y, m1, __builtin_fmaf(e.z, m2, e.w * m3)));
         } else {
           v[i] = __builtin_fmaf(
-              e.x, expm1_one<SMALL>(sigma * a[i].x),
-              __builtin_fmaf(e.y, expm1_one<SMALL>(sigma * a[i].y),
-                             __builtin_fmaf(e.z, expm1_one<SMALL>(sigma * a[i].z),
-                                            e.w * expm1_one<SMALL>(sigma * a[i].w))));
+              e.x, expm1_one<SMALL>(sigma_u * a[i].x),
+              __builtin_fmaf(e.y, expm1_one<SMALL>(sigma_u * a[i].y),
+                             __builtin_fmaf(e.z, expm1_one<SMALL>(sigma_u * a[i].z),
+                                            e.w * expm1_one<SMALL>(sigma_u * a[i].w))));
         }
         ay[i] = y_in ? __int_as_float(__builtin_amdgcn_readlane(
                            __float_as_int(quad_comp(a[i], y_comp)), y_lane))
@@ -1561,7 +1574,7 @@ __global__ __launch_bounds__(256) void head_ce_kernel(
 #pragma unroll
         for (int i = 1; i < NB; ++i) ayk = (k % NB == i) ? ay[i] : ayk;
         // expm1(-s sigma a_y) for this lane's draw and sign
-        const float ey = expm1f((ANTI && k >= NB) ? sigma * ayk : -sigma * ayk);
+        const float ey = expm1f((ANTI && k >= NB) ? sigma_u * ayk : -sigma_u * ayk);
         r = head_rho(x, inv_s, true, q_y, ey);
       } else {
         r = head_rho(x, inv_s, false, 0.f, 0.f);
@@ -1896,7 +1909,8 @@ void launch_chain(const Plan& p, const ChainPlan& cp, int64_t seq_len, float gam
   const unsigned blocks = (unsigned)ceil_div(p.T * p.nq, 256);
   const double g_b = (g32 ? 4.0 * td : 0.0) + (g_hi ? 4.0 * td : 0.0);
   if (!cp.plain) {
-    const float scale = 2.0f / (float)p.K;
+    // the walk's R and noise are both in noise units (kNoiseUnit each)
+    const float scale = 2.0f * kNoiseUnit2 / (float)p.K;
     const TimedLaunch evs = stamp("chain_sum_kernel", 0.0, rows_b + g_b);
     if (sum_full)
       DUST_LAUNCH(evs, chain_sum_kernel<true>, dim3(blocks), dim3(256), 0, s, (const float*)part,
@@ -1911,7 +1925,8 @@ void launch_chain(const Plan& p, const ChainPlan& cp, int64_t seq_len, float gam
     DUST_LAUNCH(stamp("chain_mean_kernel", 0.0, 8.0 * p.T), chain_mean_kernel,
                 dim3((unsigned)cp.n_seq), dim3(256), sizeof(float) * (size_t)(seq_len + 256), s,
                 sl, gamma, Mv);
-    const float scale = -1.0f / ((float)p.K * sigma);
+    // the partial sums of R a and of a carry the noise in units of kNoiseUnit
+    const float scale = -kNoiseUnit / ((float)p.K * sigma);
     const TimedLaunch evs = stamp("chain_sum_kernel", 0.0, rows_b + 4.0 * p.T + g_b);
     if (sum_full)
       DUST_LAUNCH(evs, chain_sum_plain_kernel<true>, dim3(blocks), dim3(256), 0, s,

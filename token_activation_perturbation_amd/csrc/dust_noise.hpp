@@ -78,34 +78,48 @@ __device__ __forceinline__ uint4 philox4x32_10(uint32_t x0, uint32_t x1, uint32_
   return make_uint4(x0, x1, x2, x3);
 }
 
-// -2 ln 2, so that -2 ln u = kMinusTwoLn2 * log2 u.
+// UNIT: the generator returns each Gaussian in units of sqrt(2 ln 2): with
+// log2 u from the hardware, a = sqrt(-2 ln u) cos 2 pi v = kNoiseUnit *
+// sqrt(-log2 u) cos 2 pi v, and the constant factor is left to the
+// consumers, which apply it once per reduced total or per output (a
+// multiply per value saved).  !UNIT: the Gaussians themselves (the
+// two-pass loss kernel keeps this form, which measured faster there).
+constexpr float kNoiseUnit = 1.17741002251547469101f;   // sqrt(2 ln 2)
+constexpr float kNoiseUnit2 = 1.38629436111989061883f;  // 2 ln 2
 constexpr float kMinusTwoLn2 = -1.38629436111989061883f;
 
+// The pair (a_even, a_odd), divided by kNoiseUnit when UNIT.
+template <bool UNIT = true>
 __device__ __forceinline__ float2 box_muller(uint32_t w_even, uint32_t w_odd) {
   // the float 1 + (w >> 9) 2^-23 in [1, 2): exponent field 127, the word's
   // top 23 bits as the mantissa (one funnel shift)
   const float xu = __uint_as_float(__builtin_amdgcn_alignbit(0x7Fu, w_even, 9u));
   const float xv = __uint_as_float(__builtin_amdgcn_alignbit(0x7Fu, w_odd, 9u));
   const float u = 2.0f - xu;  // 1 - (w_even >> 9) 2^-23 in (0, 1], exact
-  const float radius = __builtin_amdgcn_sqrtf(kMinusTwoLn2 * __builtin_amdgcn_logf(u));
+  // log2 u <= 0; its negation is a source modifier of the square root
+  const float radius = UNIT ? __builtin_amdgcn_sqrtf(-__builtin_amdgcn_logf(u))
+                            : __builtin_amdgcn_sqrtf(kMinusTwoLn2 * __builtin_amdgcn_logf(u));
   // v_sin / v_cos take revolutions and keep only the fraction, so xv itself
   // is the angle v = (w_odd >> 9) 2^-23
   return make_float2(radius * __builtin_amdgcn_cosf(xv), radius * __builtin_amdgcn_sinf(xv));
 }
 
-// The four Gaussians of channel quad q of token t under noise index n.
+// The four Gaussians of channel quad q of token t under noise index n (in
+// units of kNoiseUnit when UNIT).
+template <bool UNIT = true>
 __device__ __forceinline__ float4 noise_quad(uint32_t q, uint32_t t, uint32_t n, NoiseKey key) {
   const uint4 w = philox4x32_10(q, t, n, 0u, key);
-  const float2 a = box_muller(w.x, w.y);
-  const float2 b = box_muller(w.z, w.w);
+  const float2 a = box_muller<UNIT>(w.x, w.y);
+  const float2 b = box_muller<UNIT>(w.z, w.w);
   return make_float4(a.x, a.y, b.x, b.y);
 }
 
 // Two noise quads at once, (quad qa, noise index na) and (qb, nb) of token
 // t, their Philox rounds advanced together.  The values are those of two
-// noise_quad calls; interleaving the two dependency chains gives the
+// noise_quad<UNIT> calls; interleaving the two dependency chains gives the
 // scheduler independent multiplies to issue while a round's products are in
 // flight (each stream alone has only two per round).
+template <bool UNIT = true>
 __device__ __forceinline__ void noise_quad_x2(uint32_t qa, uint32_t na, uint32_t qb, uint32_t nb,
                                               uint32_t t, NoiseKey key, float4& A, float4& B) {
   uint32_t k0 = key.k0, k1 = key.k1;
@@ -133,8 +147,8 @@ __device__ __forceinline__ void noise_quad_x2(uint32_t qa, uint32_t na, uint32_t
     k0 += kPhiloxW0;
     k1 += kPhiloxW1;
   }
-  const float2 a_lo = box_muller(a0, a1), b_lo = box_muller(b0, b1);
-  const float2 a_hi = box_muller(a2, a3), b_hi = box_muller(b2, b3);
+  const float2 a_lo = box_muller<UNIT>(a0, a1), b_lo = box_muller<UNIT>(b0, b1);
+  const float2 a_hi = box_muller<UNIT>(a2, a3), b_hi = box_muller<UNIT>(b2, b3);
   A = make_float4(a_lo.x, a_lo.y, a_hi.x, a_hi.y);
   B = make_float4(b_lo.x, b_lo.y, b_hi.x, b_hi.y);
 }

@@ -37,9 +37,11 @@ at once.  Their bound is the vector ALU issue rate, counted in lane-slots:
                                                                    = 50 slots
     Box-Muller      per pair: 2 funnel shifts (each word's top 23 bits
                     as the mantissa of a float in [1, 2)), 1 subtraction
-                    for u, log2, sqrt, sin, cos x 4, 1 multiply by
-                    -2 ln 2, 2 multiplies by the radius = 22;      = 44 slots
-  That gives 23.5 slots per value, plus the consumers: 1 FMA for
+                    for u, log2, sqrt, sin, cos x 4, 2 multiplies by
+                    the radius = 21 (the values come in units of
+                    sqrt(2 ln 2), which the consumers apply once per
+                    reduced total or output, not per value);       = 42 slots
+  That gives 23 slots per value, plus the consumers: 1 FMA for
   P = <delta, a>, 1 FMA for Q = ||a||^2 (the quadratic loss's curvature
   term: needed by plain draws and by the per-draw outputs; with antithetic
   pairs it cancels inside each pair, so a call that asks only for g and G_W
@@ -51,7 +53,7 @@ The cross-entropy head's slab kernel consumes each value as: 1 multiply
 (sigma a), the jitter's expm1 (antithetic: both signs from the even and odd
 Taylor parts, 9 + 2 slots; plain draws: 8 slots of Horner), the slab's
 partial sums (one FMA per sign), 1 FMA for g and, for plain draws, 1 add for
-the noise sum: 38.5 slots per value with antithetic pairs, 35.5 without.
+the noise sum: 38 slots per value with antithetic pairs, 35 without.
 
 The generation alone (noise_quad in a loop, the probe's last row) runs at
 ~0.84 of this model's peak with the clock at 2.4 GHz: the
@@ -78,8 +80,8 @@ PHILOX_SLOTS_PER_QUAD = (2 * SINGLE                         # second round
 BOX_MULLER_SLOTS_PER_QUAD = 2 * (2 * SINGLE               # funnel shifts: u, v fields
                                  + 1 * SINGLE               # u = 2 - (1 + m 2^-23)
                                  + 4 * QUARTER              # log2, sqrt, sin, cos
-                                 + 3 * SINGLE)              # -2 ln 2, radius x 2: 44
-GEN_SLOTS_PER_VALUE = (PHILOX_SLOTS_PER_QUAD + BOX_MULLER_SLOTS_PER_QUAD) / 4.0  # 23.5
+                                 + 2 * SINGLE)              # radius x 2: 42
+GEN_SLOTS_PER_VALUE = (PHILOX_SLOTS_PER_QUAD + BOX_MULLER_SLOTS_PER_QUAD) / 4.0  # 23
 
 
 def distinct_noise_values(T: int, d_out: int, K: int, antithetic: bool) -> int:
