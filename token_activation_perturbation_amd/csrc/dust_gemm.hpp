@@ -951,6 +951,136 @@ __global__ __launch_bounds__(256) void tn_outer_big_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// The outer product on 128 x 256 tiles (128 channels of g, 256 of the layer
+// input): each wave multiplies a 64 x 128 block, reading per 32-token
+// k-block 4 hi, 4 lo and 8 X fragments for 64 MFMAs, a third fewer LDS
+// bytes per MFMA than tn_outer_big_kernel's 64 x 64 blocks.  The tile is held
+// as 64-channel sub-tiles in the layout of tn_outer_dma_kernel (a token per
+// 128-byte row, chunk c of row r in slot c ^ tr_swz(r)): hi 0-1, lo 2-3 and
+// X 4-7; wave (wm, wn) reads hi / lo sub-tile wm and X sub-tiles 2 wn, 2 wn +
+// 1.  Two LDS stages of 32 KiB (two workgroups per CU).  Per output element
+// the contraction runs over the same 32-token steps in the same order (hi,
+// then lo) as tn_outer_big_kernel, so for the same token split the results
+// are bitwise equal; edges as there.
+
+// Wait for this wave's LDS reads: 16 fragments pass through the statement.
+__device__ __forceinline__ void frag_wait16(u16x8_t (&a)[4], u16x8_t (&b)[4], u16x8_t (&c)[8]) {
+  asm volatile("s_waitcnt lgkmcnt(0)"
+               : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(b[0]), "+v"(b[1]),
+                 "+v"(b[2]), "+v"(b[3]), "+v"(c[0]), "+v"(c[1]), "+v"(c[2]), "+v"(c[3]),
+                 "+v"(c[4]), "+v"(c[5]), "+v"(c[6]), "+v"(c[7]));
+}
+
+constexpr int kTnWideStage = 8 * 32 * 128;  // bytes of one LDS stage of tn_outer_wide_kernel
+
+template <int NS>
+__global__ __launch_bounds__(256) void tn_outer_wide_kernel(
+    const uint16_t* __restrict__ g_hi, const uint16_t* __restrict__ g_lo,
+    const uint16_t* __restrict__ X, int32_t T, int32_t M, int32_t N, int32_t tiles_m,
+    int32_t tiles_n, int32_t splits, int32_t per_xcd, int64_t t_first, int64_t t_per_split,
+    int32_t partial, float* __restrict__ out) {
+  constexpr int BK = 32, SUB = BK * 128;  // a 32-token x 64-channel sub-tile
+  constexpr int STAGE = 8 * SUB;          // hi (2), lo (2), X (4) sub-tiles
+  static_assert(STAGE == kTnWideStage, "stage size");
+  extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];  // NS * STAGE bytes
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const TileWork work = map_tile<kTnGroupM>(tiles_m, tiles_n, splits, per_xcd);
+  if (!work.valid) return;
+  const int64_t m0 = (int64_t)work.m_tile * 128;
+  const int64_t n0 = (int64_t)work.n_tile * 256;
+  const int64_t t_begin = t_first + (int64_t)work.split * t_per_split;
+  const int64_t t_end = min((int64_t)T, t_begin + t_per_split);
+  const int nk = (int)((t_end - t_begin + BK - 1) / BK);
+
+  // this lane's DMA row of every sub-tile (rows 8 wave .. + 7) and the
+  // channel offsets it fetches for each 64-channel piece
+  const int rq = 8 * wave + (lane >> 3);
+  const int cq = (lane & 7) ^ tr_swz(rq);
+  int64_t a_ch[2], b_ch[4];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int64_t am = m0 + 64 * h + 8 * cq;
+    a_ch[h] = am < M ? am : M - 8;
+  }
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    const int64_t bn = n0 + 64 * h + 8 * cq;
+    b_ch[h] = bn < N ? bn : N - 8;
+  }
+  auto issue = [&](int buf, int kt) {
+    int64_t t = t_begin + (int64_t)kt * BK + rq;
+    t = t < T ? t : (int64_t)T - 1;
+    uint8_t* base = lds + buf * STAGE + wave * 1024;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      __builtin_amdgcn_global_load_lds(g_hi + t * M + a_ch[h], (lds_void_ptr)(base + h * SUB),
+                                       16, 0, 0);
+      __builtin_amdgcn_global_load_lds(g_lo + t * M + a_ch[h],
+                                       (lds_void_ptr)(base + (2 + h) * SUB), 16, 0, 0);
+    }
+#pragma unroll
+    for (int h = 0; h < 4; ++h)
+      __builtin_amdgcn_global_load_lds(X + t * N + b_ch[h], (lds_void_ptr)(base + (4 + h) * SUB),
+                                       16, 0, 0);
+  };
+
+  f32x4_t acc[4][8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  for (int b = 0; b < NS - 1 && b < nk; ++b) issue(b, b);
+  for (int kt = 0; kt < nk; ++kt) {
+    wait_blocks<NS, 8>(min(nk - 1 - kt, NS - 2));
+    stage_barrier();
+    const int buf = kt % NS;
+    uint8_t* base = lds + buf * STAGE;
+    const int64_t left = t_end - (t_begin + (int64_t)kt * BK);
+    if (left < BK) {
+      // g rows past the split's end, in the four hi / lo sub-tiles
+      const int from = (int)(left < 0 ? 0 : left) * 128;
+      for (int o = from + 16 * tid; o < SUB; o += 16 * 256) {
+#pragma unroll
+        for (int st = 0; st < 4; ++st) *(u32x4_t*)(base + st * SUB + o) = u32x4_t{0u, 0u, 0u, 0u};
+      }
+      __syncthreads();
+    }
+    if (kt + NS - 1 < nk) issue((kt + NS - 1) % NS, kt + NS - 1);
+    u16x8_t ah[4], al[4], bf[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ah[i] = frag_sw_asm(base + wm * SUB, i * 16, 0, lane);
+      al[i] = frag_sw_asm(base + (2 + wm) * SUB, i * 16, 0, lane);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      bf[j] = frag_sw_asm(base + (4 + 2 * wn + (j >> 2)) * SUB, (j & 3) * 16, 0, lane);
+    frag_wait16(ah, al, bf);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        acc[i][j] = mfma16(ah[i], bf[j], acc[i][j]);
+        acc[i][j] = mfma16(al[i], bf[j], acc[i][j]);
+      }
+  }
+  float* dst = partial ? out + (int64_t)work.split * M * N : out;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t row = m0 + wm * 64 + i * 16 + 4 * (lane >> 4) + e;
+        const int64_t col = n0 + wn * 128 + j * 16 + (lane & 15);
+        if (row < M && col < N) dst[row * N + col] = acc[i][j][e];
+      }
+}
+
+// ---------------------------------------------------------------------------
 // The base GEMM on 128 x 128 tiles (the aligned case of nt_gemm_dma_kernel,
 // for problems with enough tiles to fill the chip twice over).  Each wave
 // multiplies a 64 x 64 block (4 x 4 MFMA tiles), so every operand fragment

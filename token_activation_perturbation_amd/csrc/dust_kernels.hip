@@ -1958,12 +1958,19 @@ void launch_outer(const Plan& p, const void* X, const float* g32, const uint16_t
     const bool vec = (d_in % 8 == 0) && (d_out % 8 == 0) && ((uintptr_t)X % 16 == 0) &&
                      ((uintptr_t)g_hi % 16 == 0) && ((uintptr_t)g_lo % 16 == 0);
     const bool big = vec && p.outer_big;
+    const bool wide = big && p.outer_wide;
     const int tb = big ? 128 : 64;
-    const int tiles_m = (int)ceil_div(d_out, tb), tiles_n = (int)ceil_div(d_in, tb);
+    const int tiles_m = (int)ceil_div(d_out, tb);
+    const int tiles_n = (int)ceil_div(d_in, wide ? 256 : tb);
     const int per_xcd = (int)ceil_div((int64_t)tiles_m * tiles_n * p.outer_split, 8);
     const dim3 grid((unsigned)(8 * per_xcd));
     const int32_t partial = p.outer_split > 1 ? 1 : 0;
-    if (big)
+    if (wide)
+      DUST_LAUNCH(ev, gemm::tn_outer_wide_kernel<2>, grid, dim3(256),
+                  (size_t)2 * gemm::kTnWideStage, s, (const uint16_t*)g_hi,
+                  (const uint16_t*)g_lo, (const uint16_t*)X, Ti, dout, di, tiles_m, tiles_n,
+                  p.outer_split, per_xcd, (int64_t)0, (int64_t)p.outer_tokens, partial, dst);
+    else if (big)
       DUST_LAUNCH(ev, gemm::tn_outer_big_kernel<DUST_TN_BIG_STAGES>, grid, dim3(256),
                   (size_t)DUST_TN_BIG_STAGES * gemm::kTnBigStage, s, (const uint16_t*)g_hi,
                   (const uint16_t*)g_lo, (const uint16_t*)X, Ti, dout, di, tiles_m, tiles_n,

@@ -41,6 +41,18 @@ constexpr int64_t kTargetWaves = DUST_TARGET_WAVES;
 #define DUST_BIG_OUTER_MIN_TOKENS 1024
 #endif
 constexpr int64_t kBigTilesMin = DUST_BIG_TILES_MIN;
+// The outer product on 128 x 256 tiles (outer_wide) where it takes 128 x 128
+// tiles and the layer input has at least kWideOuterMinN channels; its token
+// split aims for kWideOuterWorkgroups workgroups (two share a CU).
+// -DDUST_WIDE_OUTER_MIN_N=n at build time (0 switches it off).
+#ifndef DUST_WIDE_OUTER_MIN_N
+#define DUST_WIDE_OUTER_MIN_N 512
+#endif
+#ifndef DUST_WIDE_OUTER_WORKGROUPS
+#define DUST_WIDE_OUTER_WORKGROUPS 512
+#endif
+constexpr int64_t kWideOuterMinN = DUST_WIDE_OUTER_MIN_N;
+constexpr int64_t kWideOuterWorkgroups = DUST_WIDE_OUTER_WORKGROUPS;
 constexpr int64_t kBigOuterWorkgroups = DUST_BIG_OUTER_WORKGROUPS;
 constexpr int64_t kBigOuterMinTokens = DUST_BIG_OUTER_MIN_TOKENS;
 
@@ -63,6 +75,7 @@ struct Plan {
   // outer product: 128 x 128 output tiles (outer_big) or 64 x 64; split of
   // the token (contraction) axis into outer_split ranges of outer_tokens
   int32_t outer_big = 0;
+  int32_t outer_wide = 0;  // 128 x 256 tiles (implies outer_big)
   int32_t outer_split = 1;
   int64_t outer_tokens = 0;  // tokens per split (multiple of 64)
 
@@ -132,12 +145,16 @@ inline bool make_plan(int64_t T, int64_t d_in, int64_t d_out, int32_t K,
   const int64_t tiles128 = ceil_div(d_out, 128) * ceil_div(d_in, 128);
   q.outer_big =
       (aligned8 && tiles128 * ceil_div(T, kBigOuterMinTokens) >= kBigOuterWorkgroups) ? 1 : 0;
-  const int64_t tiles = q.outer_big ? tiles128 : ceil_div(d_out, 64) * ceil_div(d_in, 64);
+  q.outer_wide = (q.outer_big && kWideOuterMinN > 0 && d_in >= kWideOuterMinN) ? 1 : 0;
+  const int64_t tiles = q.outer_wide  ? ceil_div(d_out, 128) * ceil_div(d_in, 256)
+                        : q.outer_big ? tiles128
+                                      : ceil_div(d_out, 64) * ceil_div(d_in, 64);
   // the large tiles' grid is sized to fit one round of resident workgroups
   // (a second round that holds only a few would take nearly as long as the
   // first); the small tiles run many rounds
-  int64_t split = q.outer_big ? kBigOuterWorkgroups / tiles
-                              : ceil_div(DUST_OUTER_WORKGROUPS, tiles);
+  int64_t split = q.outer_wide  ? kWideOuterWorkgroups / tiles
+                  : q.outer_big ? kBigOuterWorkgroups / tiles
+                                : ceil_div(DUST_OUTER_WORKGROUPS, tiles);
   const int64_t max_split =
       ceil_div(T, q.outer_big ? kBigOuterMinTokens : DUST_OUTER_MIN_TOKENS);
   if (split > max_split) split = max_split;
