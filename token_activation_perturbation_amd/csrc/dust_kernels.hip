@@ -1400,7 +1400,7 @@ __global__ __launch_bounds__(256) void chain_sum_kernel(const float* __restrict_
 // token; wave w takes slabs w, w + waves, ...; lane l owns columns 4 l .. + 3
 // of the slab (noise quad 64 j + l of the token).  Every wave forms m and S
 // over the whole row itself (same order, so identical values).
-// expm1 of the jitter: SMALL (sigma sqrt(48 ln 2) < 0.5, all |x| < 0.5) uses
+// expm1 of the jitter: SMALL (sigma 5.78 < 0.5, all |x| < 0.5) uses
 // the even and odd Taylor parts to x^8, E(x) and O(x), accurate to ~1e-8
 // relative and giving both signs at once, expm1(+-x) = E +- O; otherwise
 // exp(x) - 1 where |x| >= 0.5.  Per-row and per-draw scalars (the row's
@@ -2291,7 +2291,8 @@ dust_status_t run_head(const void* X, const void* W, const int32_t* labels, int6
   const TimedLaunch tl = take_timing_events();
   const int64_t n_slab = V / 256;
   const unsigned waves = (unsigned)(n_slab < 4 ? n_slab : 4);
-  // every noise value has |a| <= sqrt(48 ln 2) < 5.78, so |sigma a| < 0.5
+  // every noise value has |a| <= sqrt(46 ln 2) < 5.65 (the smallest uniform u
+  // is 2^-23), so with sigma 5.78 < 0.5 every |sigma a| < 0.5
   const bool small = sigma * 5.78f < 0.5f;
   const double tv = (double)T * V;
   const TimedLaunch evh =
