@@ -127,7 +127,10 @@ dust_status_t dust_validate(const void* X, const void* W, const void* target,
  *   sigma    jitter scale (fp32); gamma credit decay in [0,1] (fp32)
  *   seed     64-bit noise key.  Noise value a_t^(n)[c] is Box-Muller of
  *            Philox4x32-10 words, counter (c/4, t, n, 0), key (seed low,
- *            seed high); it is regenerated where needed, never stored.
+ *            seed high): words (w0, w1) give channels 4q, 4q+1 and (w2, w3)
+ *            4q+2, 4q+3 as sqrt(-2 ln u) (cos 2 pi v, sin 2 pi v) with
+ *            u = 1 - (w_even >> 9) 2^-23, v = (w_odd >> 9) 2^-23; it is
+ *            regenerated where needed, never stored.
  * Outputs (fp32, overwritten, not accumulated):
  *   G_W        [d_out, d_in]  sum_t g_t x_t^T (NOT divided by T); required
  *   loss_clean [T]            L_t = 1/2 ||W x_t - target_t||^2; optional
