@@ -133,19 +133,26 @@ __global__ __launch_bounds__(256) void base_gemm_f32_kernel(
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  for (int k = 0; k < d_in; k += 4) {
-    const int kc = k + kk;
-    float a[2], b[2];
+  // eight k-steps' operands loaded at a time, then their MFMAs in k order
+  constexpr int U = 8;
+  for (int k0 = 0; k0 < d_in; k0 += 4 * U) {
+    float a[U][2], b[U][2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int row = m0 + 16 * i + r, col = n0 + 16 * i + r;
-      a[i] = (row < T && kc < d_in) ? X[(int64_t)row * d_in + kc] : 0.f;
-      b[i] = (col < d_out && kc < d_in) ? W[(int64_t)col * d_in + kc] : 0.f;
+    for (int u = 0; u < U; ++u) {
+      const int kc = k0 + 4 * u + kk;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int row = m0 + 16 * i + r, col = n0 + 16 * i + r;
+        a[u][i] = (row < T && kc < d_in) ? X[(int64_t)row * d_in + kc] : 0.f;
+        b[u][i] = (col < d_out && kc < d_in) ? W[(int64_t)col * d_in + kc] : 0.f;
+      }
     }
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) acc[i][j] = mfma_f32(a[i], b[j], acc[i][j]);
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma_f32(a[u][i], b[u][j], acc[i][j]);
   }
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -642,19 +649,26 @@ __global__ __launch_bounds__(256) void outer_f32_kernel(
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  for (int t0 = t_begin; t0 < t_end; t0 += 4) {
-    const int t = t0 + kk;
-    float a[2], b[2];
+  // eight token steps' operands loaded at a time, then their MFMAs in order
+  constexpr int U = 8;
+  for (int t0 = t_begin; t0 < t_end; t0 += 4 * U) {
+    float a[U][2], b[U][2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = m0 + 16 * i + r, col = n0 + 16 * i + r;
-      a[i] = (t < t_end && c < d_out) ? g[(int64_t)t * d_out + c] : 0.f;
-      b[i] = (t < t_end && col < d_in) ? X[(int64_t)t * d_in + col] : 0.f;
+    for (int u = 0; u < U; ++u) {
+      const int t = t0 + 4 * u + kk;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int c = m0 + 16 * i + r, col = n0 + 16 * i + r;
+        a[u][i] = (t < t_end && c < d_out) ? g[(int64_t)t * d_out + c] : 0.f;
+        b[u][i] = (t < t_end && col < d_in) ? X[(int64_t)t * d_in + col] : 0.f;
+      }
     }
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) acc[i][j] = mfma_f32(a[i], b[j], acc[i][j]);
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma_f32(a[u][i], b[u][j], acc[i][j]);
   }
   float* dst = out + (int64_t)split * d_out * d_in;
 #pragma unroll
