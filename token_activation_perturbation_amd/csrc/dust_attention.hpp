@@ -516,6 +516,7 @@ __global__ __launch_bounds__(256, DUST_ATTN_WAVES) void attn_score_t_kernel(
 
   const int64_t pbase = (int64_t)sh * Lp * Lp;
   const int tcol = 64 * j + 16 * w + 4 * g;
+  float pf_p = 0.f;
   std::conditional_t<KEY, Rows, AttnRowsSplit<DH>> nxt;
   if constexpr (KEY)
     nxt.load(Qa, row0 + 64 * j, min(64, L - 64 * j), D, hc);
@@ -541,6 +542,20 @@ __global__ __launch_bounds__(256, DUST_ATTN_WAVES) void attn_score_t_kernel(
       const int64_t at = pbase + (int64_t)(s0 + 16 * st + r16) * Lp + tcol;
       pv[st] = *(const float4*)(Pm + at);
       if constexpr (KEY) bv[st] = *(const float4*)(Bm + at);
+    }
+    // Values: the next block's P lines brought into L2 now (lane l touches
+    // row s0 + 64 + l of the wave's 16 columns; past the padded length, its
+    // last row), so that their loads a block later hit L2: the 16 noise
+    // groups of a unit reach a block together and would otherwise all wait
+    // for HBM.  The value is only kept alive: the statement below takes the
+    // previous block's (landed long since) as an operand.  Measured on one
+    // box, alternating builds: the value site's kernel 1.65-1.67 ->
+    // 1.61 ms; the same for P and B in the key kernel (255 VGPRs) 1.84-1.86
+    // -> 1.88 ms, so keys go without.
+    if constexpr (!KEY) {
+      asm volatile("" : : "v"(pf_p));
+      const int64_t at = pbase + (int64_t)min(s0 + 64 + lane, Lp - 1) * Lp + 64 * j + 16 * w;
+      pf_p = Pm[at];
     }
     f32x4_t acc[NV][4];
 #pragma unroll
@@ -658,6 +673,7 @@ __global__ __launch_bounds__(256, DUST_ATTN_WAVES) void attn_score_s_kernel(
 #pragma unroll
   for (int mm = 0; mm < MM; ++mm) S[mm] = 0.f;
   const int64_t prow = (int64_t)sh * Lp * Lp + (int64_t)sl * Lp;
+  float pf_p = 0.f, pf_b = 0.f;
   Rows nxt;
   nxt.load(Ka, row0, min(64, L), D, hc);
   for (int j = 0; j <= b; ++j) {
@@ -671,6 +687,17 @@ __global__ __launch_bounds__(256, DUST_ATTN_WAVES) void attn_score_s_kernel(
       const int64_t at = prow + t0 + 16 * tt + 4 * g;
       pv[tt] = *(const float4*)(Pm + at);
       bv[tt] = *(const float4*)(Bm + at);
+    }
+    // the next key block's P and B lines into L2 (lane l: row 16 w + l % 16
+    // of the wave, the line of columns t0 + 64 + 32 ((l / 16) % 2); past the
+    // padded length, its last line), as for the value site in
+    // attn_score_t_kernel (1.68-1.71 -> 1.65-1.67 ms)
+    asm volatile("" : : "v"(pf_p), "v"(pf_b));
+    {
+      const int64_t at = (int64_t)sh * Lp * Lp + (int64_t)(64 * b + 16 * w + r16) * Lp +
+                         min(t0 + 64 + 32 * (g & 1), Lp - 32);
+      pf_p = Pm[at];
+      pf_b = Bm[at];
     }
     f32x4_t acc[NV][4];
 #pragma unroll
