@@ -543,16 +543,16 @@ __global__ __launch_bounds__(256, DUST_ATTN_WAVES) void attn_score_t_kernel(
       pv[st] = *(const float4*)(Pm + at);
       if constexpr (KEY) bv[st] = *(const float4*)(Bm + at);
     }
-    // Values: the next block's P lines brought into L2 now (lane l touches
-    // row s0 + 64 + l of the wave's 16 columns; past the padded length, its
-    // last row), so that their loads a block later hit L2: the 16 noise
-    // groups of a unit reach a block together and would otherwise all wait
-    // for HBM.  The value is only kept alive: the statement below takes the
-    // previous block's (landed long since) as an operand.  Measured on one
-    // box, alternating builds: the value site's kernel 1.65-1.67 ->
-    // 1.61 ms; the same for P and B in the key kernel (255 VGPRs) 1.84-1.86
-    // -> 1.88 ms, so keys go without.
-    if constexpr (!KEY) {
+    // The next block's P lines brought into L2 now (lane l touches row
+    // s0 + 64 + l of the wave's 16 columns; past the padded length, its last
+    // row), so that their loads a block later hit L2: the 16 noise groups of
+    // a unit reach a block together and would otherwise all wait for HBM.
+    // The value is only kept alive: the statement below takes the previous
+    // block's (landed long since) as an operand.  Measured on one box,
+    // alternating builds: the value site's kernel 1.65-1.67 -> 1.61 ms, the
+    // key site's step 2.70 -> 2.67 ms; B's lines too, for keys (255 VGPRs),
+    // measured slower (1.84-1.86 -> 1.88 ms).
+    {
       asm volatile("" : : "v"(pf_p));
       const int64_t at = pbase + (int64_t)min(s0 + 64 + lane, Lp - 1) * Lp + 64 * j + 16 * w;
       pf_p = Pm[at];
